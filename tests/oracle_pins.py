@@ -1,0 +1,380 @@
+"""Pins of the CPU oracle against facts it does not compute itself.
+
+Each ``pin_*`` takes an oracle module and raises AssertionError when the
+module disagrees with a closed form, a brute-force count on a tiny input, an
+independent library routine, a printed value of the pages, or an invariant
+the pages state. ``test_oracle_pins.py`` runs them on the real oracle and on
+copies of it with planted mistakes (each planted mistake must trip a pin).
+"""
+
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _bf16_vals(rng, shape, scale=1.0):
+    """Random bf16-representable float64 values (truncated float32)."""
+    x = (scale * rng.standard_normal(shape)).astype(np.float32)
+    bits = x.view(np.uint32) & np.uint32(0xFFFF0000)
+    return bits.view(np.float32).astype(np.float64)
+
+
+def read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append(line.split())
+    return rows
+
+
+# ------------------------------------------------------------------ bf16
+
+def pin_bf16_golden(o):
+    """Hand-derived roundings (bf16 = 1 sign, 8 exponent, 7 fraction bits)."""
+    for expr, bits in read_golden("bf16_rne.txt"):
+        x = float(eval(expr, {"__builtins__": {}}, {}))  # arithmetic only
+        got = int(o.bf16_bits(o.bf16_round(np.array([x])))[0])
+        assert got == int(bits, 16), (expr, hex(got), bits)
+
+
+def pin_bf16_vs_torch(o):
+    """Library routine: torch's float32 -> bfloat16 conversion rounds to
+    nearest even; on float32 inputs direct rounding must agree with it."""
+    import torch
+    rng = _rng(1)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),  # subnormal
+        (rng.standard_normal(2000) * 1e37).astype(np.float32),
+    ])
+    # exact halfway points between neighbouring bf16 values
+    base = x.view(np.uint32) & np.uint32(0xFFFF0000)
+    half = (base | np.uint32(0x8000)).view(np.float32)
+    x = np.concatenate([x, half[np.isfinite(half)]])
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16)
+    ref = ref.numpy().view(np.uint16)
+    got = o.bf16_bits(o.bf16_round(x.astype(np.float64)))
+    assert np.array_equal(got, ref)
+
+
+def pin_bf16_exact_path(o):
+    """The rational-input rounding agrees with the float64 one."""
+    rng = _rng(2)
+    for v in rng.standard_normal(300) * 10.0 ** rng.integers(-30, 30, 300):
+        assert o.bf16_round_exact(Fraction(float(v))) == float(
+            o.bf16_round(np.array([v]))[0])
+
+
+# ------------------------------------------------------------------ CompressK
+
+def pin_chunk_count(o):
+    """Chunk i covers tokens [16i, 16i+32): brute-force count of complete
+    windows."""
+    for L in range(0, 300):
+        brute = sum(1 for i in range(L) if 16 * i + 32 <= L)
+        assert o.n_chunks(L) == brute, L
+
+
+def pin_compress_exact_means(o):
+    """Keys that are small integers: the chunk mean is an exact dyadic value
+    with at most 8 significant bits, so CompressK must return it exactly."""
+    rng = _rng(3)
+    K = rng.integers(-4, 5, size=(96, 8)).astype(np.float64)
+    c = o.compress_keys(K)
+    assert c.shape == (5, 8)
+    for i in range(5):
+        for d in range(8):
+            exact = Fraction(int(K[16 * i:16 * i + 32, d].sum()), 32)
+            assert Fraction(c[i, d]) == exact, (i, d)
+
+
+def pin_compress_single_rounding(o):
+    """The mean is rounded once, directly: 31 ones and one 1.125 average to
+    1 + 2^-8, an exact tie between 1 and 1 + 2^-7 that rounds to even (1)."""
+    rows = np.ones((32, 2))
+    rows[5, 0] = 1.125
+    rows[7, 1] = 1.125 + 2.0 ** -4   # mean 1 + 2^-8 + 2^-9: rounds up
+    c = o.compress_chunk(rows)
+    assert c[0] == 1.0
+    assert c[1] == 1.0 + 2.0 ** -7
+
+
+def pin_compress_wide_range(o):
+    """Exact sum even when float64 accumulation would lose a term:
+    2^60 + 2^-60 - 2^60 averages to 2^-65, a bf16 value."""
+    rows = np.zeros((32, 1))
+    rows[0, 0], rows[1, 0], rows[2, 0] = 2.0 ** 60, 2.0 ** -60, -(2.0 ** 60)
+    assert o.compress_chunk(rows)[0] == 2.0 ** -65
+
+
+def pin_pool_identity(o):
+    """Mean pooling commutes with the dot product: for keys whose chunk means
+    are bf16-exact, q . c_i equals the mean of q . k_j over chunk i."""
+    rng = _rng(4)
+    K = rng.integers(-3, 4, size=(160, 16)).astype(np.float64)
+    q = rng.standard_normal(16)
+    c = o.compress_keys(K)
+    tok = K @ q
+    for i in range(c.shape[0]):
+        assert math.isclose(c[i] @ q, tok[16 * i:16 * i + 32].mean(),
+                            rel_tol=1e-12, abs_tol=1e-12)
+
+
+# ------------------------------------------------------------------ eviction
+
+def pin_eviction_closed_form(o):
+    """softplus(0) = ln 2 and softplus(ln(e - 1)) = 1; W1 is input-major, so a
+    one-hot value vector at input e reads row e of W1."""
+    d = 4
+    W1 = np.zeros((d, d))
+    W1[0, 0] = math.log(math.e - 1.0)      # row 0 -> hidden 0 gets 1
+    W1[1, 2] = 50.0                          # row 1 -> hidden 2 ~ linear
+    W2 = np.array([2.0, 3.0, 5.0, 0.0])
+    V = np.eye(d)[:2]
+    s = o.eviction_scores(V, W1, W2)
+    ln2 = math.log(2.0)
+    assert math.isclose(s[0], 2.0 * 1.0 + 3.0 * ln2 + 5.0 * ln2, rel_tol=1e-13)
+    assert math.isclose(s[1], 2.0 * ln2 + 3.0 * ln2 + 5.0 * 50.0,
+                        rel_tol=1e-13)
+    # very negative pre-activations contribute nothing
+    W1n = np.full((d, d), -800.0)
+    assert abs(o.eviction_scores(V, W1n, W2)[0]) < 1e-300
+
+
+def pin_chunk_means_closed_form(o):
+    """Mean of s_j = j over chunk i is 16i + 15.5."""
+    s = np.arange(200, dtype=np.float64)
+    m = o.chunk_means(s)
+    assert len(m) == o.n_chunks(200)
+    assert np.allclose(m, 16 * np.arange(len(m)) + 15.5, rtol=0, atol=0)
+
+
+def pin_block_pool_brute(o):
+    """Brute force over tokens: block b takes the max over every chunk that
+    shares at least one token with it."""
+    rng = _rng(5)
+    for L in (32, 47, 64, 100, 128, 200, 511, 640):
+        C = o.n_chunks(L)
+        nb = -(-L // 64)
+        x = rng.standard_normal(C)
+        got = o.block_max_pool(x, nb)
+        for b in range(nb):
+            members = [i for i in range(C)
+                       if set(range(16 * i, 16 * i + 32))
+                       & set(range(64 * b, 64 * b + 64))]
+            want = max(x[i] for i in members) if members else -np.inf
+            assert got[b] == want, (L, b)
+
+
+# ------------------------------------------------------------------ query-aware
+
+def pin_query_scores_closed_form(o):
+    """Two chunks whose scaled logits differ by ln 3 get softmax weights 1/4
+    and 3/4; the scale is 1/sqrt(d)."""
+    d = 128
+    c = np.zeros((2, d))
+    c[1, 0] = 1.0
+    q = np.zeros((1, d))
+    q[0, 0] = math.log(3.0) * math.sqrt(d)
+    a = o.query_chunk_scores(q, c)
+    assert np.allclose(a, [0.25, 0.75], rtol=1e-14, atol=0)
+
+
+def pin_query_scores_scipy(o):
+    """Library routine: scipy's softmax per head, summed over the group."""
+    from scipy.special import softmax
+    rng = _rng(6)
+    for G, C in ((1, 7), (4, 33), (8, 100)):
+        q = _bf16_vals(rng, (G, 128), 3.0)
+        c = _bf16_vals(rng, (C, 128))
+        want = softmax((q @ c.T) / math.sqrt(128), axis=1).sum(axis=0)
+        got = o.query_chunk_scores(q, c)
+        assert np.allclose(got, want, rtol=1e-12, atol=0)
+        assert math.isclose(got.sum(), G, rel_tol=1e-12)
+
+
+# ------------------------------------------------------------------ selection
+
+def pin_roles(o):
+    """Sink, window and candidates partition the blocks, by brute force."""
+    for L in range(1, 1200, 7):
+        for n_s, n_w in ((1, 2), (1, 4), (2, 3), (0, 2)):
+            r = o.block_roles(L, n_s, n_w)
+            nb = -(-L // 64)
+            assert r.nb == nb
+            allb = sorted(r.sink + r.window + r.candidates)
+            assert allb == list(range(nb)), (L, n_s, n_w)
+            assert r.sink == [b for b in range(nb) if b < n_s]
+            assert r.window == [b for b in range(nb)
+                                if b >= n_s and b >= nb - n_w]
+            for b in r.candidates:                     # complete blocks only
+                assert 64 * (b + 1) <= L
+
+
+def pin_topk_lexsort(o):
+    """Library routine: numpy's lexsort on (score descending, id ascending),
+    with many exact ties."""
+    rng = _rng(7)
+    for n, k in ((1, 1), (10, 3), (50, 50), (300, 16), (300, 0), (40, 64)):
+        scores = rng.integers(0, 6, size=n).astype(np.float64)
+        ids = list(range(n))
+        want = list(np.lexsort((np.arange(n), -scores))[:max(0, k)])
+        assert o.top_by_score(ids, scores, k) == want
+
+
+def pin_select_reduces_to_plain_topk(o):
+    """With k_e' = 0 the selection is sink + window + top-k_q (InfLLM-V2's
+    plain selection)."""
+    rng = _rng(8)
+    r = o.block_roles(64 * 40 + 5, 1, 4)
+    Qb = rng.standard_normal(r.nb)
+    Eb = rng.standard_normal(r.nb)
+    sel = o.select_blocks(Qb, Eb, set(r.candidates), r, 6, 0)
+    top = sorted(r.candidates, key=lambda b: -Qb[b])[:6]
+    assert sel.blocks == sorted(set(r.sink) | set(r.window) | set(top))
+    assert sel.agnostic == []
+
+
+def _run_pair(o, rng, L0, steps, n_s, n_w, k_q, k_e_dyn, G=2, d=8,
+              hot=False):
+    cap = L0 + steps
+    K = _bf16_vals(rng, (cap, d))
+    V = _bf16_vals(rng, (cap, d))
+    W1 = _bf16_vals(rng, (d, d), 0.5)
+    W2 = _bf16_vals(rng, (d,), 0.5)
+    if hot:
+        u = rng.standard_normal(d)
+        for b in rng.choice(np.arange(n_s, max(n_s + 1, L0 // 64 - n_w)),
+                            size=2):
+            K[64 * b:64 * b + 64] += u
+    p = o.PairOracle(K.copy(), V.copy(), W1, W2, L0, n_s, n_w, k_q, k_e_dyn,
+                     1.0)
+    out = []
+    for t in range(steps):
+        qg = _bf16_vals(rng, (G, d), 2.0)
+        out.append(p.step(K[L0 + t], V[L0 + t], qg))
+    return out
+
+
+def pin_agnostic_only_is_streaming_topk(o):
+    """With k_q = 0 the agnostic part is a streaming top-k over a fixed
+    score: A(t) = top-k_e' of A(t-1) plus the blocks that just left the
+    window (closed form of the never-reselect rule)."""
+    rng = _rng(9)
+    res = _run_pair(o, rng, 64 * 30, 140, 1, 3, 0, 5)
+    for t in range(1, len(res)):
+        prev, cur = res[t - 1], res[t]
+        fresh = set(cur.roles.candidates) - set(prev.roles.candidates)
+        pool = set(prev.sel.agnostic) | fresh
+        want = sorted(sorted(pool, key=lambda b: (-cur.Eb[b], b))[:5])
+        assert cur.sel.agnostic == want, t
+
+
+def pin_invariants(o, seed=10, cases=12):
+    """Theorem 2's bound gamma(t) >= k_e / k, the eligible set only shrinking
+    or extending forward in time ([W] How NOSA works), and the bookkeeping
+    facts that follow from the construction."""
+    rng = _rng(seed)
+    for case in range(cases):
+        n_s = int(rng.integers(0, 3))
+        n_w = int(rng.integers(2, 5))
+        k_q = int(rng.integers(0, 5))
+        k_e_dyn = int(rng.integers(0, 6))
+        L0 = 64 * int(rng.integers(1, 25)) + int(rng.integers(0, 64))
+        res = _run_pair(o, rng, L0, 150, n_s, n_w, k_q, k_e_dyn,
+                        hot=bool(case % 2))
+        k = n_s + n_w + k_q + k_e_dyn
+        k_e = n_s + n_w + k_e_dyn
+        E0 = len(res[0].roles.candidates)
+        for t, r in enumerate(res):
+            S = r.sel.blocks
+            assert len(S) <= k
+            assert not set(r.sel.query) & set(r.sel.agnostic)        # I4
+            assert set(r.sel.agnostic) <= r.eligible                   # I4
+            assert len(r.sel.query) == min(k_q, len(r.roles.candidates))
+            assert len(r.eligible) >= min(k_e_dyn, E0)                 # I5
+            if t == 0:
+                continue
+            p = res[t - 1]
+            fresh = set(r.roles.candidates) - set(p.roles.candidates)
+            assert r.eligible - fresh <= p.eligible                    # I2
+            assert r.eligible <= set(p.sel.blocks)                     # I3
+            gamma = o.locality(p.sel.blocks, S, r.new_block)
+            assert gamma >= k_e / k - 1e-12, (case, t, gamma)          # I1
+            assert len(r.misses) <= k_q                                # I7
+            have = set(p.sel.blocks) | ({r.new_block} - {None})
+            assert r.misses == [b for b in S if b not in have]
+
+
+# ------------------------------------------------------------------ attention
+
+def pin_attention_full_coverage_sdpa(o):
+    """When the selection covers every block, sparse attention is full
+    attention: torch's scaled_dot_product_attention in float64 with the
+    eviction score as an additive mask (and without it for beta = 0)."""
+    import torch
+    rng = _rng(11)
+    for L in (1, 63, 64, 65, 200, 511):
+        G, d = 4, 128
+        q = _bf16_vals(rng, (G, d), 2.0)
+        K = _bf16_vals(rng, (L, d))
+        V = _bf16_vals(rng, (L, d))
+        s = rng.standard_normal(L) * 0.3
+        blocks = list(range(-(-L // 64)))
+        for beta in (1.0, 0.0):
+            got = o.attend(q, K, V, s, blocks, L, beta)
+            tq, tk, tv = (torch.from_numpy(a)[None] for a in (q, K, V))
+            mask = torch.from_numpy(beta * s)[None, None, :].expand(1, G, L)
+            want = torch.nn.functional.scaled_dot_product_attention(
+                tq, tk, tv, attn_mask=mask)[0].numpy()
+            assert np.allclose(got, want, rtol=1e-12, atol=1e-13), (L, beta)
+
+
+def pin_attention_closed_form(o):
+    """Two tokens whose logits (bias included) differ by ln 3 mix their
+    values 1:3; tokens past L and unselected blocks are ignored."""
+    d = 128
+    q = np.zeros((1, d))
+    K = np.zeros((130, d))
+    V = np.zeros((130, d))
+    V[0, 0], V[64, 0], V[129, 0] = 4.0, 8.0, 1000.0
+    s = np.zeros(130)
+    s[64] = math.log(3.0)
+    o_ = o.attend(q, K, V, s, [0, 1, 2], 65, 1.0)
+    # block 0: 64 tokens of logit 0 (only token 0 has a nonzero value);
+    # block 1: token 64 with logit ln 3; block 2 and token 129 lie past L
+    w64 = 3.0 / (64.0 + 3.0)
+    w0 = 1.0 / (64.0 + 3.0)
+    assert math.isclose(o_[0, 0], w0 * 4.0 + w64 * 8.0, rel_tol=1e-13)
+
+
+# ------------------------------------------------------------------ budget
+
+def pin_budget_golden(o):
+    """The main-experiment budget printed in the aiwiki article."""
+    want = {k: v for k, v in read_golden("main_experiment_budget.txt")}
+    b = o.budget(int(want["k_tokens"]), int(want["k_q_tokens"]),
+                 int(want["n_sink_blocks"]), int(want["window_tokens"]))
+    assert b["k"] == int(want["k_blocks"])
+    assert b["k_q"] == int(want["k_q_blocks"])
+    assert b["k_e"] == int(want["k_e_blocks"])
+    assert b["k_e_dyn"] == int(want["k_e_dynamic_blocks"])
+    assert b["dynamic"] == int(want["dynamic_blocks"])
+    assert math.isclose(b["bound"], float(want["locality_bound"]))
+    assert b["transfer_unit"] == int(want["transfer_unit_bytes"])
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,161 @@
+"""The oracle against its pins, and planted mistakes against the pins.
+
+CPU only. A planted mistake lives in a private copy of the oracle module (never
+in the HIP path); each one must make at least one pin fail, which shows the
+pins would catch that kind of slip in the oracle itself.
+"""
+
+import importlib.util
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle.nosa_oracle as real
+import oracle_pins as P
+
+ORACLE_SRC = os.path.join(os.path.dirname(real.__file__), "nosa_oracle.py")
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(real)
+
+
+_copies = 0
+
+
+def _fresh_oracle():
+    global _copies
+    _copies += 1
+    name = f"nosa_oracle_copy_{_copies}"
+    spec = importlib.util.spec_from_file_location(name, ORACLE_SRC)
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules[name] = mod          # dataclasses look their module up here
+    spec.loader.exec_module(mod)
+    return mod
+
+
+# ------------------------------------------------------------ planted mistakes
+
+def _chunks_by_start(o):
+    def chunks_of_block(b, C):               # only chunks starting in b
+        lo = min(C, 4 * b)
+        return range(lo, min(C, 4 * b + 4))
+    o.chunks_of_block = chunks_of_block
+
+
+def _no_score_scale(o):
+    def query_chunk_scores(q, ckeys):
+        logits = q @ ckeys.T
+        e = np.exp(logits - logits.max(axis=1, keepdims=True))
+        return (e / e.sum(axis=1, keepdims=True)).sum(axis=0)
+    o.query_chunk_scores = query_chunk_scores
+
+
+def _softmax_over_heads(o):
+    def query_chunk_scores(q, ckeys):
+        logits = (q @ ckeys.T) / math.sqrt(q.shape[1])
+        e = np.exp(logits - logits.max(axis=0, keepdims=True))
+        return (e / e.sum(axis=0, keepdims=True)).sum(axis=0)
+    o.query_chunk_scores = query_chunk_scores
+
+
+def _transposed_w1(o):
+    def eviction_scores(V, W1, W2):
+        return o.softplus(V @ W1.T) @ W2
+    o.eviction_scores = eviction_scores
+
+
+def _swapped_pool(o):
+    o.POOL_KERNEL, o.POOL_STRIDE = 16, 32
+
+
+def _sum_not_mean(o):
+    def chunk_means(s, L=None):
+        L = s.shape[0] if L is None else L
+        return np.array([s[16 * i:16 * i + 32].sum()
+                         for i in range(o.n_chunks(L))])
+    o.chunk_means = chunk_means
+
+
+def _ties_high_index(o):
+    def top_by_score(ids, scores, k):
+        return sorted(ids, key=lambda b: (-scores[b], -b))[:max(0, k)]
+    o.top_by_score = top_by_score
+
+
+def _bias_sign(o):
+    orig = o.attend
+
+    def attend(q, K, V, s, blocks, L, beta):
+        return orig(q, K, V, s, blocks, L, -beta)
+    o.attend = attend
+
+
+def _window_without_partial(o):
+    orig = o.block_roles
+
+    def block_roles(L, n_sink, n_win):
+        r = orig(L, n_sink, n_win)
+        if L % 64 and r.window:
+            r.window = r.window[:-1]
+        return r
+    o.block_roles = block_roles
+
+
+def _double_rounding(o):
+    def bf16_round(x):
+        f = np.asarray(x, dtype=np.float64).astype(np.float32)
+        u = f.view(np.uint32).astype(np.uint64)
+        u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+        return u.astype(np.uint32).view(np.float32).astype(np.float64)
+    o.bf16_round = bf16_round
+
+
+def _float_sum_compress(o):
+    def compress_chunk(rows):
+        return o.bf16_round(rows.astype(np.float32).sum(axis=0,
+                                                        dtype=np.float32) / 32)
+    o.compress_chunk = compress_chunk
+
+
+def _evict_on_agnostic_only(o):
+    orig = o.select_blocks
+
+    def select_blocks(Qb, Eb, eligible, roles, k_q, k_e_dyn):
+        sel = orig(Qb, Eb, eligible, roles, k_q, k_e_dyn)
+        # a Q pick of an eligible block now costs it its eligibility
+        eligible.difference_update(set(sel.query))
+        return sel
+    o.select_blocks = select_blocks
+
+
+def _fill_shortfall(o):
+    orig = o.select_blocks
+
+    def select_blocks(Qb, Eb, eligible, roles, k_q, k_e_dyn):
+        everything = set(roles.candidates)
+        return orig(Qb, Eb, everything, roles, k_q, k_e_dyn)
+    o.select_blocks = select_blocks
+
+
+MUTATIONS = [_chunks_by_start, _no_score_scale, _softmax_over_heads,
+             _transposed_w1, _swapped_pool, _sum_not_mean, _ties_high_index,
+             _bias_sign, _window_without_partial, _double_rounding,
+             _float_sum_compress, _evict_on_agnostic_only, _fill_shortfall]
+
+
+@pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
+def test_planted_mistake_is_caught(mutate):
+    o = _fresh_oracle()
+    mutate(o)
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(o)
+        except Exception:
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught {mutate.__name__}"
