@@ -1,0 +1,236 @@
+/*
+ * nosa.h -- C ABI of the NOSA batched decode-step hot path on MI355X (gfx950).
+ *
+ * NOSA (Native and Offloadable Sparse Attention) attends, at each decode
+ * step, to an attention-sink block, a sliding window and k_q + k_e' dynamic
+ * 64-token blocks, and keeps the full KV cache in pinned host memory with a
+ * per-layer GPU cache of the previous step's blocks (aiwiki "NOSA", How NOSA
+ * works and NOSI: the inference system; SparDA article on aliyun,
+ * KV 预取的运行时实现). One decode step of one layer is four calls, in order:
+ *
+ *   nosa_compress_append  append the step's K, V; per-token eviction score;
+ *                         CompressK chunk and block-score bookkeeping
+ *   nosa_select           query-aware chunk scores, two-stage block selection
+ *                         under the never-reselect rule
+ *   nosa_fetch_delta      (offload only) set difference against the cached
+ *                         blocks, then copy only the missing blocks from host
+ *   nosa_sparse_decode    attention over the selected blocks with the
+ *                         eviction-score logit bias
+ *
+ * Conventions
+ *  - Every pointer is caller-owned. The library never allocates or frees
+ *    memory and keeps no device state of its own.
+ *  - bf16 values are passed as uint16_t bit patterns.
+ *  - Calls only enqueue work on `stream` and return; none synchronises the
+ *    host. One state is used from one stream at a time; distinct states are
+ *    independent.
+ *  - Argument checks are pure host code and run before any HIP call, so a
+ *    rejected call enqueues nothing. Kernel launch failures return
+ *    NOSA_ERR_HIP; nosa_last_error() then holds a message (thread-local).
+ *    Conditions only the device can see (a sequence that would outgrow
+ *    max_context) set bits in state->status and leave that sequence's data
+ *    untouched; they surface when the caller reads status.
+ *  - A pair is (sequence b, KV head g); pair index p = b * n_kv_heads + g.
+ *    Query head h belongs to KV head h / (n_q_heads / n_kv_heads).
+ */
+#ifndef NOSA_H
+#define NOSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ error codes */
+enum {
+  NOSA_OK = 0,
+  NOSA_ERR_INVALID = -1,     /* NULL pointer, inconsistent budget or sizes  */
+  NOSA_ERR_UNSUPPORTED = -2, /* a shape or parameter this build does not do */
+  NOSA_ERR_CAPACITY = -3,    /* max_len_host beyond max_context             */
+  NOSA_ERR_WORKSPACE = -4,   /* workspace missing or too small              */
+  NOSA_ERR_HIP = -5          /* a HIP launch or runtime call failed         */
+};
+
+/* status bits written by kernels into state->status[0] */
+#define NOSA_STATUS_CAPACITY 1u   /* an append found seq_len == max_context  */
+#define NOSA_STATUS_BAD_SEL  2u   /* fetch/decode saw a block id out of range */
+#define NOSA_STATUS_LEN_HINT 4u   /* select met a length above max_len_host   */
+
+/* config flags */
+#define NOSA_EVICT_BIAS 1u /* add the eviction score s_j to the logits      */
+#define NOSA_OFFLOAD    2u /* full KV lives in pinned host memory           */
+
+/* ------------------------------------------------------------ config
+ * Supported: head_dim 128; n_q_heads a multiple of n_kv_heads with group
+ * size 1..16; block_size 64, pool_kernel 32, pool_stride 16 (aiwiki "NOSA",
+ * Main-experiment configuration; NOSA-1B 核心组件揭秘, 核心组件一);
+ * window_tokens a multiple of 64 and >= 128 (so every candidate block's
+ * chunks are complete); k_blocks = k_q_blocks + k_e_blocks <= 64 with
+ * k_e_blocks >= n_sink_blocks + window_tokens / 64 (k_e counts the sink and
+ * window blocks, aiwiki "NOSA" Main-experiment configuration);
+ * evict_hidden 128; 64 <= max_context <= 262144; batch * n_kv_heads <= 65535.
+ */
+typedef struct nosa_config {
+  int32_t batch, n_q_heads, n_kv_heads, head_dim;
+  int32_t block_size, pool_kernel, pool_stride;
+  int32_t n_sink_blocks, window_tokens;
+  int32_t k_blocks, k_q_blocks, k_e_blocks;
+  int32_t max_context, evict_hidden;
+  uint32_t flags;
+} nosa_config;
+
+/* ------------------------------------------------------------ state
+ * One layer's decode state. Sizes (in elements) come from nosa_state_bytes;
+ * write C_max = (max_context - 32) / 16 + 1 chunks, NB_max =
+ * ceil(max_context / 64) blocks, P = batch * n_kv_heads pairs.
+ *
+ * KV block layout (device pool, device cache and host store alike): one
+ * block of one pair is 32 KiB = K then V, bf16:
+ *     K part  [64 tokens][128 dims]   (row = token)
+ *     V part  [128 dims][64 tokens]   (row = dim; V transposed)
+ * A block is the pages' 16 KiB-per-tensor transfer unit (aiwiki "NOSA",
+ * Main-experiment configuration), with K and V adjacent.
+ */
+typedef struct nosa_state {
+  int32_t *seq_len;       /* dev [B]: tokens per sequence; +1 per append    */
+  int32_t *arrive;        /* dev [B]: zero; append's per-sequence counter   */
+  uint32_t *status;       /* dev [1]: NOSA_STATUS_* bits (sticky)           */
+  uint16_t *ckey;         /* dev [P][C_max][128] bf16 compressed keys       */
+  float *tok_s;           /* dev [P][NB_max*64] eviction score per token    */
+  float *chunk_e;         /* dev [P][C_max] mean eviction score per chunk   */
+  float *blk_e;           /* dev [P][NB_max] query-agnostic block score     */
+  uint32_t *eligible;     /* dev [P][ceil(NB_max/32)] never-reselect bits   */
+  uint16_t *tail_keys;    /* dev [P][32][128] last 32 keys (ring by pos%32) */
+  uint16_t *kv_dev;       /* dev: resident pool [P][NB_max][32 KiB block] or
+                             offload cache [P][k_blocks+1][32 KiB block]    */
+  uint16_t *kv_host;      /* device-usable alias of the pinned host store
+                             [P][NB_max][32 KiB block]; NULL when resident  */
+  int32_t *slot_of_block; /* dev [P][NB_max] cache slot or -1 (offload)     */
+  int32_t *block_of_slot; /* dev [P][k_blocks+1] block id or -1 (offload)   */
+  const uint16_t *w1;     /* dev [Hkv][128 in][128 hidden] bf16 eviction W1 */
+  const uint16_t *w2;     /* dev [Hkv][128 hidden] bf16 eviction W2         */
+} nosa_state;
+
+enum {
+  NOSA_BUF_SEQ_LEN = 0, NOSA_BUF_ARRIVE, NOSA_BUF_STATUS, NOSA_BUF_CKEY,
+  NOSA_BUF_TOK_S, NOSA_BUF_CHUNK_E, NOSA_BUF_BLK_E, NOSA_BUF_ELIGIBLE,
+  NOSA_BUF_TAIL_KEYS, NOSA_BUF_KV_DEV, NOSA_BUF_KV_HOST,
+  NOSA_BUF_SLOT_OF_BLOCK, NOSA_BUF_BLOCK_OF_SLOT, NOSA_BUF_W1, NOSA_BUF_W2,
+  NOSA_NUM_BUFFERS
+};
+
+/* kind codes written by nosa_select */
+enum { NOSA_KIND_NONE = 0, NOSA_KIND_SINK = 1, NOSA_KIND_WINDOW = 2,
+       NOSA_KIND_QUERY = 3, NOSA_KIND_AGNOSTIC = 4 };
+
+/* workspace users */
+enum { NOSA_WS_SELECT = 1, NOSA_WS_FETCH = 2, NOSA_WS_DECODE = 3 };
+
+/* ------------------------------------------------------------ sizing */
+
+/* Checks a config against the supported set. NOSA_OK, NOSA_ERR_INVALID or
+ * NOSA_ERR_UNSUPPORTED. Host only. */
+int nosa_validate_config(const nosa_config *cfg);
+
+/* Byte size of every state buffer, indexed by NOSA_BUF_*. Buffers a mode
+ * does not use (kv_host and the slot maps when resident) get 0. Host only. */
+int nosa_state_bytes(const nosa_config *cfg, size_t sizes_out[NOSA_NUM_BUFFERS]);
+
+/* Workspace bytes that call `which` needs for sequences up to max_len
+ * tokens; 0 for an invalid config. A workspace must be 256-byte aligned.
+ * The decode workspace must be zero-filled before its first use (its
+ * per-pair arrival counters return to zero at the end of every call). */
+size_t nosa_workspace_bytes(const nosa_config *cfg, int which, int32_t max_len);
+
+/* ------------------------------------------------------------ calls */
+
+/* Builds the decode state from a prefilled context (untimed set-up).
+ * Precondition: seq_len[b] holds each sequence's prefilled length
+ * (<= max_len_host <= max_context) and the context's K, V sit in kv_dev
+ * (resident) or in the host store (offload) in the block layout above.
+ * Computes tok_s for every token (eviction head, aiwiki "NOSA" How NOSA
+ * works), every complete compressed key and chunk mean, blk_e of every
+ * complete block, fills tail_keys, sets every eligible bit (E(0) = all
+ * candidates), empties the offload cache, clears arrive and status. */
+int nosa_prefill_init(const nosa_config *cfg, const nosa_state *st,
+                      int32_t max_len_host, hipStream_t stream);
+
+/* Appends one token per pair at position seq_len[b] and increments
+ * seq_len[b]. k_new, v_new: dev bf16 [B][Hkv][128].
+ *  - writes K, V into kv_dev (resident) or into the host store, and into the
+ *    cache slot of its block when that block is cached (offload); a token
+ *    that opens a new block takes a free cache slot for it;
+ *  - tok_s[pos] = softplus(v W1) W2 in fp32 (aiwiki "NOSA", How NOSA works;
+ *    l189 article, 2.1, eq. 4);
+ *  - when a 32-token chunk completes (L >= 32 and (L - 32) % 16 == 0):
+ *    ckey = bf16 round-to-nearest-even of the exact mean of its 32 keys
+ *    (NOSA-1B 核心组件揭秘, 核心组件一), chunk_e = mean of its tok_s, and
+ *    when chunk 4b+3 completes, blk_e[b] = max of chunk_e over the chunks
+ *    overlapping block b (l189 article, 2.1, eqs. 5-6).
+ * max_len_host: an upper bound on seq_len after the call. */
+int nosa_compress_append(const nosa_config *cfg, const nosa_state *st,
+                         const uint16_t *k_new, const uint16_t *v_new,
+                         int32_t max_len_host, hipStream_t stream);
+
+/* Two-stage block selection for the current length L = seq_len[b].
+ * q: dev bf16 [B][Hq][128] (post-RoPE query of the step).
+ *  - query-aware score: per query head, softmax over all complete chunks of
+ *    q . ckey / sqrt(128); summed over the GQA group; max-pooled over the
+ *    chunks overlapping each block (NOSA-1B 核心组件揭秘, 核心组件三);
+ *  - candidates: complete blocks in [n_sink, nb - n_win), nb = ceil(L/64);
+ *  - stage 1: the k_q candidates of highest query-aware score; stage 2: the
+ *    k_e - n_sink - n_win eligible remaining candidates of highest blk_e
+ *    (aiwiki "NOSA", How NOSA works); ties go to the lower block id;
+ *  - eligibility: a candidate not selected loses its bit for good.
+ * Outputs: sel dev int32 [B][Hkv][k_blocks], the selected block ids in
+ * ascending order, -1 padded; n_sel dev int32 [B][Hkv]; kind (optional) dev
+ * uint8 [B][Hkv][k_blocks] NOSA_KIND_*; dbg_qscore (optional) dev fp32
+ * [B][Hkv][NB_max], the query-aware block score of each candidate (other
+ * entries untouched). ws: NOSA_WS_SELECT bytes. */
+int nosa_select(const nosa_config *cfg, const nosa_state *st,
+                const uint16_t *q, int32_t *sel, int32_t *n_sel,
+                uint8_t *kind, float *dbg_qscore, void *ws, size_t ws_bytes,
+                int32_t max_len_host, hipStream_t stream);
+
+/* Offload mode only: brings the selected blocks into the device cache.
+ * Set difference of sel against the cached blocks (NOSI's set-difference
+ * kernel, aiwiki "NOSA", NOSI: the inference system): slots whose block is
+ * not selected are freed, each missing block gets a free slot and is copied
+ * as one 32 KiB block from the host store (block-wise, not token-wise
+ * transfers, aiwiki "NOSA", How NOSA works). Outputs: phys dev int32
+ * [B][Hkv][k_blocks] = cache slot of each sel entry (-1 padded); n_miss dev
+ * int32 [B][Hkv] = blocks copied. ws: NOSA_WS_FETCH bytes. */
+int nosa_fetch_delta(const nosa_config *cfg, const nosa_state *st,
+                     const int32_t *sel, const int32_t *n_sel, int32_t *phys,
+                     int32_t *n_miss, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* Sparse attention for the step. For query head h of pair (b, g):
+ *   out[b][h] = sum_j softmax_j(q_h . k_j / sqrt(128) + beta * tok_s[j]) v_j
+ * over the existing tokens (j < seq_len[b]) of the blocks listed in sel;
+ * beta = 1 with NOSA_EVICT_BIAS, else 0 (aiwiki "NOSA", How NOSA works;
+ * l189 article, 2.1, eq. 8). K, V are read from kv_dev at block index
+ * phys[i] (resident: pass phys = sel). out: dev fp32 [B][Hq][128].
+ * ws: NOSA_WS_DECODE bytes, zero-filled before first use. */
+int nosa_sparse_decode(const nosa_config *cfg, const nosa_state *st,
+                       const uint16_t *q, const int32_t *sel,
+                       const int32_t *phys, const int32_t *n_sel, float *out,
+                       void *ws, size_t ws_bytes, int32_t max_len_host,
+                       hipStream_t stream);
+
+/* Device-usable address of pinned host memory (hipHostGetDevicePointer);
+ * allocates nothing. */
+int nosa_host_alias(void *pinned_host_ptr, void **dev_alias);
+
+const char *nosa_strerror(int code);
+const char *nosa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NOSA_H */

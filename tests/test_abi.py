@@ -1,0 +1,137 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/nosa.h declares, and rejects bad arguments in host code before any
+HIP call."""
+
+import ctypes
+
+import pytest
+
+import trainable_offloadable_block_amd as nosa
+from trainable_offloadable_block_amd import _lib as L
+from trainable_offloadable_block_amd.layer import LayerShape
+
+
+def _cfg(**kw):
+    base = dict(batch=2, n_q_heads=16, n_kv_heads=2, n_sink_blocks=1,
+                window_tokens=1024, k_blocks=64, k_q_blocks=16, k_e_blocks=48,
+                max_context=16640)
+    base.update(kw)
+    return LayerShape(**base).config()
+
+
+def test_exports_every_declared_function():
+    lib = nosa.lib()
+    names = L.header_functions()
+    assert len(names) >= 11
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_valid_configs_of_the_workloads():
+    from synth import WORKLOADS
+    for wl in WORKLOADS.values():
+        c = LayerShape(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_sink_blocks,
+                       wl.window_tokens, wl.k_blocks, wl.k_q_blocks,
+                       wl.k_e_blocks, wl.max_context, wl.offload).config()
+        assert nosa.lib().nosa_validate_config(ctypes.byref(c)) == 0, wl.name
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_q_heads=15), L.NOSA_ERR_INVALID),           # not a multiple
+    (dict(n_q_heads=64, n_kv_heads=2), L.NOSA_ERR_UNSUPPORTED),  # G = 32
+    (dict(k_blocks=63), L.NOSA_ERR_INVALID),             # k != k_q + k_e
+    (dict(k_e_blocks=10, k_blocks=26), L.NOSA_ERR_INVALID),  # < sink + window
+    (dict(window_tokens=1000), L.NOSA_ERR_INVALID),      # not block-aligned
+    (dict(window_tokens=64, k_e_blocks=2, k_blocks=18), L.NOSA_ERR_UNSUPPORTED),
+    (dict(k_blocks=80, k_q_blocks=32), L.NOSA_ERR_UNSUPPORTED),   # k > 64
+    (dict(max_context=1 << 20), L.NOSA_ERR_UNSUPPORTED),
+    (dict(max_context=32), L.NOSA_ERR_UNSUPPORTED),
+    (dict(batch=0), L.NOSA_ERR_INVALID),
+])
+def test_validate_rejects(kw, code):
+    c = _cfg(**kw)
+    assert nosa.lib().nosa_validate_config(ctypes.byref(c)) == code
+    assert nosa.lib().nosa_last_error()
+
+
+def test_validate_rejects_bad_fields():
+    lib = nosa.lib()
+    for field, value, code in (("head_dim", 64, L.NOSA_ERR_UNSUPPORTED),
+                               ("pool_stride", 32, L.NOSA_ERR_UNSUPPORTED),
+                               ("block_size", 128, L.NOSA_ERR_UNSUPPORTED),
+                               ("evict_hidden", 64, L.NOSA_ERR_UNSUPPORTED),
+                               ("flags", 8, L.NOSA_ERR_INVALID)):
+        c = _cfg()
+        setattr(c, field, value)
+        assert lib.nosa_validate_config(ctypes.byref(c)) == code, field
+    assert lib.nosa_validate_config(None) == L.NOSA_ERR_INVALID
+
+
+def test_state_bytes_layout():
+    lib = nosa.lib()
+    c = _cfg()
+    sizes = (ctypes.c_size_t * len(L.BUFFERS))()
+    assert lib.nosa_state_bytes(ctypes.byref(c), sizes) == 0
+    s = dict(zip(L.BUFFERS, sizes))
+    P, NB, C = 4, 16640 // 64, (16640 - 32) // 16 + 1
+    assert s["kv_dev"] == P * NB * 32768          # resident pool
+    assert s["kv_host"] == 0 and s["slot_of_block"] == 0
+    assert s["ckey"] == P * C * 256
+    assert s["tok_s"] == P * NB * 64 * 4
+    assert s["eligible"] == P * ((NB + 31) // 32) * 4
+    c.flags |= L.NOSA_OFFLOAD
+    assert lib.nosa_state_bytes(ctypes.byref(c), sizes) == 0
+    s = dict(zip(L.BUFFERS, sizes))
+    assert s["kv_dev"] == P * 65 * 32768          # k + 1 cache slots
+    assert s["kv_host"] == P * NB * 32768
+    assert s["block_of_slot"] == P * 65 * 4
+
+
+def test_workspace_sizes():
+    lib = nosa.lib()
+    c = _cfg()
+    for which in (L.NOSA_WS_SELECT, L.NOSA_WS_FETCH, L.NOSA_WS_DECODE):
+        n = lib.nosa_workspace_bytes(ctypes.byref(c), which, 16640)
+        assert n > 0 and n % 256 == 0
+    assert lib.nosa_workspace_bytes(ctypes.byref(c), 99, 16640) == 0
+    assert lib.nosa_workspace_bytes(ctypes.byref(c), L.NOSA_WS_SELECT, 10 ** 6) == 0
+    # select workspace grows with the length bound
+    small = lib.nosa_workspace_bytes(ctypes.byref(c), L.NOSA_WS_SELECT, 1024)
+    big = lib.nosa_workspace_bytes(ctypes.byref(c), L.NOSA_WS_SELECT, 16640)
+    assert small < big
+
+
+def test_calls_reject_before_any_hip_call():
+    """Bad arguments come back as error codes without touching a device."""
+    lib = nosa.lib()
+    c = _cfg()
+    st = L.NosaState()                      # all NULL
+    null = ctypes.c_void_p(0)
+    assert lib.nosa_prefill_init(ctypes.byref(c), ctypes.byref(st), 16, null) == L.NOSA_ERR_INVALID
+    assert lib.nosa_compress_append(ctypes.byref(c), None, null, null, 16, null) == L.NOSA_ERR_INVALID
+    # a state with every pointer set (never dereferenced by host code)
+    for name in L.BUFFERS:
+        setattr(st, name, 256)
+    assert lib.nosa_compress_append(ctypes.byref(c), ctypes.byref(st), null, null, 16,
+                                    null) == L.NOSA_ERR_INVALID
+    assert lib.nosa_compress_append(ctypes.byref(c), ctypes.byref(st), 256, 256,
+                                    c.max_context + 1, null) == L.NOSA_ERR_CAPACITY
+    # select: workspace too small / misaligned
+    assert lib.nosa_select(ctypes.byref(c), ctypes.byref(st), 256, 256, 256, null, null,
+                           256, 16, 16640, null) == L.NOSA_ERR_WORKSPACE
+    assert lib.nosa_select(ctypes.byref(c), ctypes.byref(st), 256, 256, 256, null, null,
+                           260, 1 << 40, 16640, null) == L.NOSA_ERR_WORKSPACE
+    assert lib.nosa_sparse_decode(ctypes.byref(c), ctypes.byref(st), 256, 256, 256, 256,
+                                  256, null, 0, 16640, null) == L.NOSA_ERR_WORKSPACE
+    # offload without a host store
+    c.flags |= L.NOSA_OFFLOAD
+    st.kv_host = None
+    assert lib.nosa_fetch_delta(ctypes.byref(c), ctypes.byref(st), 256, 256, 256, 256,
+                                256, 1 << 20, null) == L.NOSA_ERR_INVALID
+
+
+def test_strerror():
+    lib = nosa.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.nosa_strerror(code)
+    assert b"unknown" in lib.nosa_strerror(42)

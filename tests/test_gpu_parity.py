@@ -1,0 +1,127 @@
+"""HIP path against the CPU oracle, through the C ABI (needs an MI355X).
+
+Bars: selected blocks and kinds identical (up to the near-tie protocol of
+``nosa_harness``), compressed keys bit-identical, attention output within
+max-abs 1e-2 and relative L2 2e-3 of the float64 oracle.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from synth import WORKLOADS, small_workload
+from nosa_harness import Lockstep, summary
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(wl, **kw):
+    steps = kw.pop("run_steps", None)
+    cache_every = kw.pop("cache_every", 0)
+    _say(f"[parity] {wl.name} {kw}")
+    ls = Lockstep(wl, **kw)
+    ls.check_prefill()
+    reps = ls.run(steps, cache_every=cache_every)
+    if ls.shape.offload:
+        ls.check_cache()
+    s = summary(reps)
+    _say(f"[parity] {wl.name}: {s}")
+    return ls, s
+
+
+def test_native_library_loaded():
+    import trainable_offloadable_block_amd as nosa
+    nosa.lib()
+    maps = open("/proc/self/maps").read()
+    assert "libnosa.so" in maps
+    assert torch.cuda.is_available()
+
+
+def test_small_resident():
+    _run(small_workload(101))
+
+
+def test_small_offload():
+    _run(small_workload(102, offload=True), cache_every=2)
+
+
+def test_small_no_bias():
+    _run(small_workload(103, evict_bias=False))
+
+
+def test_ragged_lengths():
+    """Different lengths per sequence: ragged last blocks, a sequence with no
+    candidates yet, one that opens a block on the first step."""
+    wl = small_workload(104, batch=4, steps=70)
+    _run(wl, lengths=[1000, 700, 129, 64])
+
+
+def test_group_16_and_4():
+    _run(small_workload(105, n_q_heads=32, n_kv_heads=2))
+    _run(small_workload(106, n_q_heads=8, n_kv_heads=2, batch=3))
+
+
+def test_budget_corner_cases():
+    # no query-aware stage
+    _run(small_workload(107, k_blocks=6, k_q_blocks=0, k_e_blocks=6))
+    # no agnostic dynamic blocks (plain top-k)
+    _run(small_workload(108, k_blocks=7, k_q_blocks=4, k_e_blocks=3))
+    # no sink, wide window
+    _run(small_workload(109, n_sink_blocks=0, window_tokens=256, k_blocks=9,
+                        k_q_blocks=3, k_e_blocks=6))
+
+
+def test_short_context_everything_selected():
+    """Contexts shorter than the budget: every block is attended, which is
+    full attention (checked against the oracle, itself pinned to SDPA)."""
+    _run(small_workload(110, context=200, steps=80, k_blocks=10, k_q_blocks=3,
+                        k_e_blocks=7))
+
+
+def test_long_run_offload_locality():
+    """Many steps in offload mode: misses match the oracle's cache model and
+    never exceed k_q per pair after the first step."""
+    wl = small_workload(111, offload=True, steps=150, context=2048, k_blocks=12,
+                        k_q_blocks=3, k_e_blocks=9, n_hot=4)
+    ls, _ = _run(wl, cache_every=25)
+    for r in ls.reports[1:]:
+        for p, (got, want) in r.misses.items():
+            assert got <= wl.k_q_blocks
+
+
+def test_tiny_decode_workload():
+    _run(WORKLOADS[1])
+
+
+def test_nosa1b_layer_sampled():
+    """Full-size 1B-shaped layer (batch 32, 16K context, k = 64), the launch
+    configuration the benchmark times; the oracle checks 4 sampled pairs."""
+    wl = WORKLOADS[2]
+    _run(wl, check_pairs=[0, 17, 40, 63], steps=8)
+
+
+def test_capacity_sets_status():
+    wl = small_workload(112, context=120, steps=8)
+    ls = Lockstep(wl, steps=8)
+    g = ls.gpu
+    # the state was sized for context + steps tokens: fill it, then one more
+    for t in range(8):
+        kd, vd, qd = ls.inputs(t)
+        g.append(kd, vd)
+    torch.cuda.synchronize()
+    assert g.status_bits() == 0
+    assert g.seq_len.cpu().tolist() == [128] * wl.batch
+    kd, vd, _ = ls.inputs(0)
+    g.max_len = g.shape.max_context - 1        # host bound stays in range
+    g.append(kd, vd)
+    torch.cuda.synchronize()
+    assert g.status_bits() & 1
+    assert g.seq_len.cpu().tolist() == [128] * wl.batch

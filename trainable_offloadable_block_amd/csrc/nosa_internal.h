@@ -1,0 +1,54 @@
+// Host-side launchers and workspace layouts shared by the C ABI and the
+// kernel files. Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+
+#include "nosa_common.h"
+
+namespace nosa {
+
+// --- select workspace: per-pair chunk weights e = exp(l - m_split) for each
+// head of the group, and per-(split, head) (m_split, Z_split).
+constexpr int kChunksPerSplit = 128;   // 4 waves x one 32-chunk MFMA group
+
+struct SelectLayout {
+  int n_splits;      // chunk splits per pair
+  int c_pad;         // n_splits * kChunksPerSplit
+  size_t e_off, stats_off, bytes;
+};
+SelectLayout select_layout(const Dims &d, int max_len);
+
+// --- fetch workspace: per-pair copy list of (block, slot).
+struct FetchLayout {
+  size_t list_off, bytes;
+};
+FetchLayout fetch_layout(const Dims &d);
+
+// --- decode workspace: split-K partials.
+struct DecodeLayout {
+  int blocks_per_split, n_splits;
+  size_t o_off, ml_off, bytes;
+};
+DecodeLayout decode_layout(const Dims &d);
+
+hipError_t launch_prefill(const Dims &d, const nosa_state &st, int max_len,
+                          hipStream_t s);
+hipError_t launch_append(const Dims &d, const nosa_state &st,
+                         const uint16_t *k_new, const uint16_t *v_new,
+                         hipStream_t s);
+hipError_t launch_select(const Dims &d, const nosa_state &st,
+                         const uint16_t *q, int32_t *sel, int32_t *n_sel,
+                         uint8_t *kind, float *dbg_qscore, void *ws,
+                         const SelectLayout &lay, hipStream_t s);
+hipError_t launch_fetch(const Dims &d, const nosa_state &st,
+                        const int32_t *sel, const int32_t *n_sel,
+                        int32_t *phys, int32_t *n_miss, void *ws,
+                        const FetchLayout &lay, hipStream_t s);
+hipError_t launch_decode(const Dims &d, const nosa_state &st,
+                         const uint16_t *q, const int32_t *sel,
+                         const int32_t *phys, const int32_t *n_sel,
+                         float *out, void *ws, const DecodeLayout &lay,
+                         hipStream_t s);
+
+}  // namespace nosa

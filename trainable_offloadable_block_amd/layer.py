@@ -1,0 +1,244 @@
+"""One layer's NOSA decode state on one GPU, driven through the C ABI.
+
+Torch supplies device memory, pinned host memory and the stream; every step
+of the decode path runs in libnosa's HIP kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+BLOCK = 64
+HEAD_DIM = 128
+BLOCK_ELEMS = 2 * BLOCK * HEAD_DIM
+
+
+@dataclass(frozen=True)
+class LayerShape:
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    n_sink_blocks: int
+    window_tokens: int
+    k_blocks: int
+    k_q_blocks: int
+    k_e_blocks: int
+    max_context: int
+    offload: bool = False
+    evict_bias: bool = True
+
+    def config(self) -> L.NosaConfig:
+        c = L.NosaConfig()
+        c.batch, c.n_q_heads, c.n_kv_heads = self.batch, self.n_q_heads, self.n_kv_heads
+        c.head_dim, c.block_size, c.pool_kernel, c.pool_stride = HEAD_DIM, BLOCK, 32, 16
+        c.n_sink_blocks, c.window_tokens = self.n_sink_blocks, self.window_tokens
+        c.k_blocks, c.k_q_blocks, c.k_e_blocks = self.k_blocks, self.k_q_blocks, self.k_e_blocks
+        c.max_context, c.evict_hidden = self.max_context, 128
+        c.flags = (L.NOSA_EVICT_BIAS if self.evict_bias else 0) | (
+            L.NOSA_OFFLOAD if self.offload else 0)
+        return c
+
+    @property
+    def group(self):
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def pairs(self):
+        return self.batch * self.n_kv_heads
+
+    @property
+    def nb_max(self):
+        return -(-self.max_context // BLOCK)
+
+    @property
+    def c_max(self):
+        return (self.max_context - 32) // 16 + 1
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def to_block_layout(K: np.ndarray, V: np.ndarray, nb: int) -> np.ndarray:
+    """Token-major K, V ([L][128] uint16 bf16 bits) -> nb blocks of 32 KiB:
+    K rows [64][128] then V transposed [128][64], zero past L."""
+    Lt = K.shape[0]
+    out = np.zeros((nb, 2, BLOCK * HEAD_DIM), dtype=np.uint16)
+    full = min(nb, Lt // BLOCK)
+    if full:
+        out[:full, 0] = K[:full * BLOCK].reshape(full, BLOCK * HEAD_DIM)
+        out[:full, 1] = V[:full * BLOCK].reshape(full, BLOCK, HEAD_DIM).transpose(
+            0, 2, 1).reshape(full, BLOCK * HEAD_DIM)
+    rest = Lt - full * BLOCK
+    if rest and full < nb:
+        kb = np.zeros((BLOCK, HEAD_DIM), dtype=np.uint16)
+        vb = np.zeros((BLOCK, HEAD_DIM), dtype=np.uint16)
+        kb[:rest] = K[full * BLOCK:]
+        vb[:rest] = V[full * BLOCK:]
+        out[full, 0] = kb.reshape(-1)
+        out[full, 1] = vb.T.reshape(-1)
+    return out
+
+
+class NosaLayer:
+    """Decode state of one layer: buffers, workspaces and the four calls."""
+
+    def __init__(self, shape: LayerShape, device: str = "cuda"):
+        self.shape = shape
+        self.device = torch.device(device)
+        self.cfg = shape.config()
+        lib = L.lib()
+        L.check(lib.nosa_validate_config(ctypes.byref(self.cfg)), "validate_config")
+        sizes = (ctypes.c_size_t * len(L.BUFFERS))()
+        L.check(lib.nosa_state_bytes(ctypes.byref(self.cfg), sizes), "state_bytes")
+        self.sizes = dict(zip(L.BUFFERS, list(sizes)))
+        dev = self.device
+        P, nbm = shape.pairs, shape.nb_max
+
+        def buf(name, dtype, elem):
+            n = self.sizes[name] // elem
+            return torch.zeros(n, dtype=dtype, device=dev) if n else None
+
+        self.seq_len = buf("seq_len", torch.int32, 4)
+        self.arrive = buf("arrive", torch.int32, 4)
+        self.status = buf("status", torch.int32, 4)
+        self.ckey = buf("ckey", torch.int16, 2)
+        self.tok_s = buf("tok_s", torch.float32, 4)
+        self.chunk_e = buf("chunk_e", torch.float32, 4)
+        self.blk_e = buf("blk_e", torch.float32, 4)
+        self.eligible = buf("eligible", torch.int32, 4)
+        self.tail_keys = buf("tail_keys", torch.int16, 2)
+        self.kv_dev = buf("kv_dev", torch.int16, 2)
+        self.slot_of_block = buf("slot_of_block", torch.int32, 4)
+        self.block_of_slot = buf("block_of_slot", torch.int32, 4)
+        self.w1 = buf("w1", torch.int16, 2)
+        self.w2 = buf("w2", torch.int16, 2)
+        self.kv_host = None
+        self.kv_host_alias = ctypes.c_void_p(0)
+        if shape.offload:
+            n = self.sizes["kv_host"] // 2
+            self.kv_host = torch.zeros(n, dtype=torch.int16, pin_memory=True)
+            alias = ctypes.c_void_p()
+            L.check(lib.nosa_host_alias(ctypes.c_void_p(self.kv_host.data_ptr()),
+                                        ctypes.byref(alias)), "host_alias")
+            self.kv_host_alias = alias
+        st = L.NosaState()
+        for name in L.BUFFERS:
+            if name == "kv_host":
+                st.kv_host = self.kv_host_alias.value
+            else:
+                t = getattr(self, name)
+                setattr(st, name, t.data_ptr() if t is not None else None)
+        self.state = st
+        mc = shape.max_context
+        self.ws_select = self._ws(L.NOSA_WS_SELECT, mc)
+        self.ws_fetch = self._ws(L.NOSA_WS_FETCH, mc)
+        self.ws_decode = self._ws(L.NOSA_WS_DECODE, mc)
+        k = shape.k_blocks
+        self.sel = torch.full((P * k,), -1, dtype=torch.int32, device=dev)
+        self.n_sel = torch.zeros(P, dtype=torch.int32, device=dev)
+        self.kind = torch.zeros(P * k, dtype=torch.uint8, device=dev)
+        self.phys = torch.full((P * k,), -1, dtype=torch.int32, device=dev)
+        self.n_miss = torch.zeros(P, dtype=torch.int32, device=dev)
+        self.out = torch.zeros(shape.batch * shape.n_q_heads * HEAD_DIM,
+                               dtype=torch.float32, device=dev)
+        self.dbg_q = None
+        self.max_len = 0
+        del nbm
+
+    def _ws(self, which, max_len):
+        n = L.lib().nosa_workspace_bytes(ctypes.byref(self.cfg), which, max_len)
+        # 256-byte alignment: torch's caching allocator hands out 512-byte
+        # aligned blocks
+        t = torch.zeros(max(n, 256), dtype=torch.uint8, device=self.device)
+        assert t.data_ptr() % 256 == 0
+        return t
+
+    @property
+    def stream(self):
+        return ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+
+    # ------------------------------------------------------------ set-up
+    def set_weights(self, w1: np.ndarray, w2: np.ndarray):
+        """w1 uint16 [Hkv][128][128] (input-major), w2 uint16 [Hkv][128]."""
+        self.w1.copy_(torch.from_numpy(np.ascontiguousarray(w1).view(np.int16).reshape(-1)))
+        self.w2.copy_(torch.from_numpy(np.ascontiguousarray(w2).view(np.int16).reshape(-1)))
+
+    def load_pair_context(self, p: int, K: np.ndarray, V: np.ndarray):
+        """Writes pair p's prefilled K, V (token-major uint16 bf16 bits) into
+        the pool (resident) or the pinned host store (offload)."""
+        nbm = self.shape.nb_max
+        blocks = to_block_layout(K, V, -(-K.shape[0] // BLOCK)).view(np.int16)
+        nb = blocks.shape[0]
+        flat = blocks.reshape(-1)
+        base = p * nbm * BLOCK_ELEMS
+        if self.shape.offload:
+            self.kv_host.numpy()[base:base + flat.size] = flat
+        else:
+            self.kv_dev[base:base + flat.size].copy_(torch.from_numpy(flat))
+        del nb
+
+    def prefill(self, lengths):
+        """Sets seq_len and builds the decode state from the loaded context."""
+        lengths = np.asarray(lengths, dtype=np.int32)
+        self.seq_len.copy_(torch.from_numpy(lengths))
+        self.max_len = int(lengths.max())
+        L.check(L.lib().nosa_prefill_init(ctypes.byref(self.cfg), ctypes.byref(self.state),
+                                          self.max_len, self.stream), "prefill_init")
+
+    # ------------------------------------------------------------ the step
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor):
+        self.max_len = min(self.max_len + 1, self.shape.max_context)
+        L.check(L.lib().nosa_compress_append(
+            ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(k_new), _ptr(v_new),
+            self.max_len, self.stream), "compress_append")
+
+    def select(self, q: torch.Tensor, want_kind=True, want_qscore=False):
+        if want_qscore and self.dbg_q is None:
+            self.dbg_q = torch.full((self.shape.pairs * self.shape.nb_max,), float("nan"),
+                                    dtype=torch.float32, device=self.device)
+        L.check(L.lib().nosa_select(
+            ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(q), _ptr(self.sel),
+            _ptr(self.n_sel), _ptr(self.kind) if want_kind else ctypes.c_void_p(0),
+            _ptr(self.dbg_q) if want_qscore else ctypes.c_void_p(0),
+            _ptr(self.ws_select), self.ws_select.numel(), self.max_len, self.stream),
+            "select")
+
+    def fetch(self, sel=None, n_sel=None):
+        sel = self.sel if sel is None else sel
+        n_sel = self.n_sel if n_sel is None else n_sel
+        L.check(L.lib().nosa_fetch_delta(
+            ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(sel), _ptr(n_sel),
+            _ptr(self.phys), _ptr(self.n_miss), _ptr(self.ws_fetch), self.ws_fetch.numel(),
+            self.stream), "fetch_delta")
+
+    def decode(self, q: torch.Tensor, sel=None, phys=None, n_sel=None):
+        sel = self.sel if sel is None else sel
+        phys = self.phys if phys is None else phys
+        n_sel = self.n_sel if n_sel is None else n_sel
+        L.check(L.lib().nosa_sparse_decode(
+            ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(q), _ptr(sel),
+            _ptr(phys), _ptr(n_sel), _ptr(self.out), _ptr(self.ws_decode),
+            self.ws_decode.numel(), self.max_len, self.stream), "sparse_decode")
+
+    def step(self, k_new, v_new, q, want_kind=False, want_qscore=False):
+        """append -> select -> fetch -> decode, all enqueued on one stream."""
+        self.append(k_new, v_new)
+        self.select(q, want_kind=want_kind, want_qscore=want_qscore)
+        self.fetch()
+        self.decode(q)
+        return self.out
+
+    # ------------------------------------------------------------ views
+    def status_bits(self) -> int:
+        return int(self.status.cpu().item()) & 0xFFFFFFFF
+
+    def eligible_words(self) -> np.ndarray:
+        words = (self.shape.nb_max + 31) // 32
+        return self.eligible.cpu().numpy().view(np.uint32).reshape(self.shape.pairs, words)
