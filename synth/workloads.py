@@ -163,6 +163,8 @@ def hot_blocks(wl: Workload, layer: int, b: int, g: int) -> np.ndarray:
     n_win = wl.window_tokens // wl.block
     lo, hi = wl.n_sink_blocks, wl.context // wl.block - n_win
     n = 64 if wl.drift else wl.n_hot
+    if n == 0:
+        return np.zeros(0, dtype=np.int64)
     if hi - lo < n:
         raise ValueError("context too short for the planted blocks")
     return _rng(wl, "HOT", layer, b, g).choice(np.arange(lo, hi), size=n,

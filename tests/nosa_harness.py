@@ -130,8 +130,10 @@ class Lockstep:
             C = len(o.ckeys)
             want = O.bf16_bits(np.array(o.ckeys)) if C else np.zeros((0, 128), np.uint16)
             assert np.array_equal(ck[p, :C], want), f"pair {p}: compressed keys differ"
+            # float32 sum of 128 terms: error relative to the score's scale
             s_ref = o.s[:o.L]
-            err = np.abs(ts[p, :o.L] - s_ref) / np.maximum(np.abs(s_ref), 1e-3)
+            scale = math.sqrt(float(np.mean(s_ref ** 2)))
+            err = np.abs(ts[p, :o.L] - s_ref) / scale
             assert err.max() < 1e-5, f"pair {p}: eviction score rel err {err.max()}"
 
     def _near_tie(self, res, gq, ga):
@@ -230,7 +232,8 @@ class Lockstep:
                 if wl.k_q_blocks > 0:
                     qr = np.abs(dq[p, c] - res.Qb[c]) / np.abs(res.Qb[c])
                     rep.qscore_rel = max(rep.qscore_rel, float(qr.max()))
-                er = np.abs(be[p, c] - res.Eb[c]) / np.maximum(np.abs(res.Eb[c]), 1e-6)
+                scale = math.sqrt(float(np.mean(res.Eb[c] ** 2)))
+                er = np.abs(be[p, c] - res.Eb[c]) / scale
                 rep.escore_rel = max(rep.escore_rel, float(er.max()))
             assert rep.qscore_rel < 1e-4, f"step {t}: query score rel err {rep.qscore_rel}"
             assert rep.escore_rel < 1e-4, f"step {t}: agnostic score rel err {rep.escore_rel}"
@@ -274,13 +277,21 @@ class Lockstep:
         sel = g.sel.cpu().numpy().reshape(self.P, k)
         phys = g.phys.cpu().numpy().reshape(self.P, k)
         nsel = g.n_sel.cpu().numpy()
-        cache = g.kv_dev.view(self.P, k + 1, -1)
-        host = g.kv_host.view(self.P, self.shape.nb_max, -1)
+        seq = g.seq_len.cpu().numpy()
+        cache = g.kv_dev.view(self.P, k + 1, 2, 64, 128)
+        host = g.kv_host.view(self.P, self.shape.nb_max, 2, 64, 128)
         for p in self.check:
+            Lb = int(seq[p // self.wl.n_kv_heads])
             for i in range(nsel[p]):
+                blk = int(sel[p, i])
+                n = min(64, Lb - 64 * blk)        # tokens that exist
                 a = cache[p, phys[p, i]].cpu()
-                bblk = host[p, sel[p, i]]
-                assert torch.equal(a, bblk), f"pair {p} block {sel[p, i]}: cache bytes differ"
+                h = host[p, blk]
+                # K rows, then V transposed: [dim][token]
+                same = (torch.equal(a[0, :n], h[0, :n]) and
+                        torch.equal(a[1].reshape(128, 64)[:, :n],
+                                    h[1].reshape(128, 64)[:, :n]))
+                assert same, f"pair {p} block {blk}: cache bytes differ"
 
     def run(self, steps=None, check_scores=True, cache_every=0):
         n = self.steps if steps is None else steps

@@ -83,7 +83,7 @@ def test_short_context_everything_selected():
     """Contexts shorter than the budget: every block is attended, which is
     full attention (checked against the oracle, itself pinned to SDPA)."""
     _run(small_workload(110, context=200, steps=80, k_blocks=10, k_q_blocks=3,
-                        k_e_blocks=7))
+                        k_e_blocks=7, n_hot=0))
 
 
 def test_long_run_offload_locality():
@@ -109,7 +109,7 @@ def test_nosa1b_layer_sampled():
 
 
 def test_capacity_sets_status():
-    wl = small_workload(112, context=120, steps=8)
+    wl = small_workload(112, context=120, steps=8, n_hot=0)
     ls = Lockstep(wl, steps=8)
     g = ls.gpu
     # the state was sized for context + steps tokens: fill it, then one more
@@ -125,3 +125,22 @@ def test_capacity_sets_status():
     torch.cuda.synchronize()
     assert g.status_bits() & 1
     assert g.seq_len.cpu().tolist() == [128] * wl.batch
+
+
+def test_nan_bytes_past_length_are_ignored():
+    """Pool bytes past each sequence's length hold NaN patterns: attention
+    must not see them (masked logits, and V zeroed past L)."""
+    wl = small_workload(113, context=1000, steps=20)
+    ls = Lockstep(wl, lengths=[1000, 937])
+    g = ls.gpu
+    pool = g.kv_dev.view(ls.P, ls.shape.nb_max, 2, 64, 128)
+    nan = int(np.array([0x7FC0], dtype=np.uint16).view(np.int16)[0])
+    for p in range(ls.P):
+        Lb = int(ls.lengths[p // wl.n_kv_heads])
+        blk, r = divmod(Lb, 64)
+        pool[p, blk, 0, r:] = nan
+        pool[p, blk, 1].view(128, 64)[:, r:] = nan
+        pool[p, blk + 1:] = nan
+    torch.cuda.synchronize()
+    ls.check_prefill()
+    ls.run()

@@ -84,6 +84,18 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_splitk_kernel(
       for (int dt = 0; dt < 8; ++dt)
         va[dt] = ldg16(vb + (16 * dt + h) * kBlock + 32 * half + 8 * lg);
       const int key0 = tok0 + 32 * half + 8 * lg;   // this lane's 8 keys
+      if (tok0 + 32 * half + 32 > L) {
+        // partial block: zero V of keys past L so that stale or uninitialised
+        // cache bytes cannot reach the sum (their probabilities are 0)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          u16x8 v = __builtin_bit_cast(u16x8, va[dt]);
+#pragma unroll
+          for (int m = 0; m < 8; ++m)
+            if (key0 + m >= L) v[m] = 0;
+          va[dt] = __builtin_bit_cast(uint4, v);
+        }
+      }
       const float4 s0 = *reinterpret_cast<const float4 *>(tsp + key0);
       const float4 s1 = *reinterpret_cast<const float4 *>(tsp + key0 + 4);
       const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
