@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the NOSA hot path on one MI355X.
+
+Workload: the NOSA-1B-shaped layer (batch 32, 16 query / 2 KV heads,
+head_dim 128, 16384-token prefilled context, block 64, 1 sink block, 1024-token
+window, k = 64 blocks = 16 query-aware + 48 query-agnostic), KV resident in
+HBM, seeded synthetic inputs (see synth/workloads.py). A step is one decode
+token through a stack of --layers independent layers of that shape, each
+layer running the whole path: compress_append -> select -> fetch_delta ->
+sparse_decode. A stack (as in a real model) keeps one layer's KV from
+staying in the 256 MB last-level cache between its steps.
+
+Prints ONE JSON line. value = decode tokens/s per layer = batch * layers *
+steps / elapsed. roofline: the sparse-decode kernel's algorithmic bytes per
+launch over its HIP-event-timed average duration, against 8 TB/s.
+"""
+
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s per layer (batch x steps/s) + % HBM peak, 1B-shape 16K/32K"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=8,
+                    help="independent layers of the workload's shape per step")
+    ap.add_argument("--cpu-pairs", type=int, default=16)
+    ap.add_argument("--cpu-steps", type=int, default=48)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--breakdown-steps", type=int, default=4)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def build_layer(wl, li, shape, pool):
+    import numpy as np
+    from synth import context_kv, eviction_weights
+    from trainable_offloadable_block_amd import NosaLayer
+    layer = NosaLayer(shape)
+    w = [eviction_weights(wl, li, g) for g in range(wl.n_kv_heads)]
+    layer.set_weights(np.stack([x[0] for x in w]), np.stack([x[1] for x in w]))
+    P = wl.batch * wl.n_kv_heads
+    ctx = list(pool.map(lambda p: context_kv(wl, li, *divmod(p, wl.n_kv_heads)), range(P)))
+    for p, (K, V) in enumerate(ctx):
+        layer.load_pair_context(p, K, V)
+    layer.prefill([wl.context] * wl.batch)
+    return layer
+
+
+def step_inputs(wl, li, n, pool, device):
+    """Per-step q, k_new, v_new for one layer, resident on the device:
+    [n][B][Hq][128], [n][B][Hkv][128] x2 (bf16 bits as int16)."""
+    import numpy as np
+    import torch
+    from synth import new_tokens, queries
+    B, Hq, Hkv = wl.batch, wl.n_q_heads, wl.n_kv_heads
+    qs = list(pool.map(lambda bh: queries(wl, li, *divmod(bh, Hq))[:n], range(B * Hq)))
+    q = np.stack(qs).reshape(B, Hq, n, 128).transpose(2, 0, 1, 3)
+    toks = list(pool.map(lambda bg: new_tokens(wl, li, *divmod(bg, Hkv)), range(B * Hkv)))
+    k = np.stack([t[0][:n] for t in toks]).reshape(B, Hkv, n, 128).transpose(2, 0, 1, 3)
+    v = np.stack([t[1][:n] for t in toks]).reshape(B, Hkv, n, 128).transpose(2, 0, 1, 3)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)  # noqa: E731
+    return dev(q), dev(k), dev(v)
+
+
+def decode_bytes(wl, n_att_per_pair):
+    """Algorithmic bytes of one sparse-decode launch: K, V (bf16) and the
+    eviction score (fp32) of every attended token, q (bf16) and out (fp32),
+    the selection and slot lists (int32)."""
+    B, Hq, Hkv, k = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.k_blocks
+    return (n_att_per_pair * B * Hkv * (2 * 128 * 2 + 4) + B * Hq * 128 * (2 + 4)
+            + B * Hkv * k * 8)
+
+
+def attended_tokens(layer, wl):
+    """Mean attended tokens per pair of the layer's last decode call."""
+    import numpy as np
+    k = wl.k_blocks
+    sel = layer.sel.cpu().numpy().reshape(-1, k)
+    nsel = layer.n_sel.cpu().numpy()
+    seq = layer.seq_len.cpu().numpy()
+    tot = 0
+    for p in range(sel.shape[0]):
+        L = int(seq[p // wl.n_kv_heads])
+        blocks = sel[p, :nsel[p]].astype(np.int64)
+        tot += int(np.minimum(64, L - 64 * blocks).sum())
+    return tot / sel.shape[0]
+
+
+def cpu_baseline(wl, n_pairs, n_steps):
+    """The oracle as it stands, on a bounded sample: n_pairs pairs of layer 0,
+    n_steps decode steps each (append + select + attend)."""
+    import numpy as np
+    import oracle.nosa_oracle as O
+    from synth import bf16_bits_to_f64, context_kv, eviction_weights, new_tokens, queries
+    G, Hkv = wl.group, wl.n_kv_heads
+    P = wl.batch * Hkv
+    pairs = [int(x) for x in np.linspace(0, P - 1, n_pairs)]
+    n_w = wl.window_tokens // 64
+    k_e_dyn = wl.k_e_blocks - wl.n_sink_blocks - n_w
+    work = []
+    for p in pairs:
+        b, g = divmod(p, Hkv)
+        K, V = context_kv(wl, 0, b, g)
+        w1, w2 = eviction_weights(wl, 0, g)
+        cap = wl.context + n_steps
+        Kf, Vf = np.zeros((cap, 128)), np.zeros((cap, 128))
+        Kf[:wl.context], Vf[:wl.context] = bf16_bits_to_f64(K), bf16_bits_to_f64(V)
+        o = O.PairOracle(Kf, Vf, bf16_bits_to_f64(w1), bf16_bits_to_f64(w2), wl.context,
+                         wl.n_sink_blocks, n_w, wl.k_q_blocks, k_e_dyn, 1.0)
+        kn, vn = new_tokens(wl, 0, b, g)
+        q = np.stack([queries(wl, 0, b, g * G + h) for h in range(G)])
+        work.append((o, kn, vn, q))
+    t0 = time.perf_counter()
+    for t in range(n_steps):
+        for o, kn, vn, q in work:
+            o.step(bf16_bits_to_f64(kn[t]), bf16_bits_to_f64(vn[t]), bf16_bits_to_f64(q[:, t]))
+    el = time.perf_counter() - t0
+    per_pair_step = el / (len(pairs) * n_steps)
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        blas = 1
+    return {
+        "value": wl.batch / (per_pair_step * P),
+        "unit": "tokens/s/layer",
+        "cores": int(blas),
+        "host_cores": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "seconds": round(el, 2),
+        "sample": (f"{len(pairs)} of {P} (sequence, KV head) pairs of layer 0 x "
+                   f"{n_steps} decode steps (append+select+attend, float64 numpy); "
+                   f"per-layer step time = per-pair step time x {P} pairs"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the NOSA "
+              "decode path has no cross-GPU step; pairs would shard by sequence "
+              "or KV head with no exchange.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from synth import WORKLOADS
+    from trainable_offloadable_block_amd import LayerShape
+
+    wl = WORKLOADS[2]
+    R, W, K = args.layers, args.warmup, args.steps
+    n_tok = W + K + args.breakdown_steps
+    shape = LayerShape(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_sink_blocks,
+                       wl.window_tokens, wl.k_blocks, wl.k_q_blocks, wl.k_e_blocks,
+                       wl.context + n_tok)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_setup = time.perf_counter()
+    workers = min(16, len(os.sched_getaffinity(0)))
+    layers, inputs = [], []
+    with cf.ThreadPoolExecutor(workers) as pool:
+        for li in range(R):
+            layers.append(build_layer(wl, li, shape, pool))
+            inputs.append(step_inputs(wl, li, n_tok, pool, dev))
+            log(f"layer {li} ready ({time.perf_counter() - t_setup:.1f}s)")
+    torch.cuda.synchronize()
+
+    def run_step(t, events=None):
+        for li, layer in enumerate(layers):
+            q, kn, vn = inputs[li][0][t], inputs[li][1][t], inputs[li][2][t]
+            layer.append(kn, vn)
+            layer.select(q, want_kind=False)
+            layer.fetch()
+            if events is not None:
+                events[0].append(torch.cuda.Event(enable_timing=True))
+                events[1].append(torch.cuda.Event(enable_timing=True))
+                events[0][-1].record()
+            layer.decode(q)
+            if events is not None:
+                events[1][-1].record()
+
+    for t in range(W):
+        run_step(t)
+    torch.cuda.synchronize()
+    ev = ([], [])
+    t0 = time.perf_counter()
+    for t in range(W, W + K):
+        run_step(t, ev)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    dec_ms = [a.elapsed_time(b) for a, b in zip(*ev)]
+
+    # per-call breakdown on a few extra steps (untimed region); these steps
+    # also give the exact number of attended tokens per decode launch (the
+    # stage-2 pool can run short, so a selection may hold fewer than k blocks)
+    names = ("append", "select", "fetch", "decode")
+    bd = {n: [] for n in names}
+    n_att_samples = []
+    for t in range(W + K, n_tok):
+        for li, layer in enumerate(layers):
+            q, kn, vn = inputs[li][0][t], inputs[li][1][t], inputs[li][2][t]
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            evs[0].record()
+            layer.append(kn, vn)
+            evs[1].record()
+            layer.select(q, want_kind=False)
+            evs[2].record()
+            layer.fetch()
+            evs[3].record()
+            layer.decode(q)
+            evs[4].record()
+            torch.cuda.synchronize()
+            for i, n in enumerate(names):
+                bd[n].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)
+            n_att_samples.append(attended_tokens(layer, wl))
+    status = [ly.status_bits() for ly in layers]
+    assert not any(status), f"device status bits set: {status}"
+    n_att = float(np.mean(n_att_samples))
+    dbytes = decode_bytes(wl, n_att)
+    dec_avg_s = float(np.mean(dec_ms)) / 1e3
+    achieved = dbytes / dec_avg_s / 1e9
+    value = wl.batch * R * K / el
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(el * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "n_q_heads": wl.n_q_heads,
+            "n_kv_heads": wl.n_kv_heads, "head_dim": 128, "context": wl.context,
+            "block": 64, "n_sink_blocks": wl.n_sink_blocks,
+            "window_tokens": wl.window_tokens, "k_blocks": wl.k_blocks,
+            "k_q_blocks": wl.k_q_blocks, "k_e_blocks": wl.k_e_blocks,
+            "kv": "hbm", "layers_per_step": R, "evict_bias": True,
+        },
+        "roofline": {
+            "kernel": "nosa_sparse_decode", "bound": "hbm",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "bytes_per_launch": int(dbytes), "avg_launch_us": round(dec_avg_s * 1e6, 2),
+            "attended_tokens_per_pair": round(n_att, 2),
+        },
+        "breakdown_us": {n: round(float(np.median(v)), 2) for n, v in bd.items()},
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_pairs, args.cpu_steps)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -124,8 +124,10 @@ def f32_to_bf16_bits(x) -> np.ndarray:
     f = np.ascontiguousarray(x, dtype=np.float32)
     if not np.all(np.isfinite(f)):
         raise ValueError("generator produced a non-finite value")
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    # finite float32 bit patterns are <= 0xFF7FFFFF, so adding at most
+    # 0x8000 cannot wrap a uint32
+    u = f.view(np.uint32)
+    u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return u.astype(np.uint16)
 
 

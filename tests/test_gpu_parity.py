@@ -101,11 +101,16 @@ def test_tiny_decode_workload():
     _run(WORKLOADS[1])
 
 
-def test_nosa1b_layer_sampled():
+def test_nosa1b_layer_all_pairs():
     """Full-size 1B-shaped layer (batch 32, 16K context, k = 64), the launch
-    configuration the benchmark times; the oracle checks 4 sampled pairs."""
-    wl = WORKLOADS[2]
-    _run(wl, check_pairs=[0, 17, 40, 63], steps=8)
+    configuration the benchmark times; every pair against the oracle."""
+    _run(WORKLOADS[2], steps=6)
+
+
+def test_nosa1b_layer_sampled_long():
+    """Same layer, 4 sampled pairs over 70 steps: covers the window sliding
+    by a block at step 64 and the eligible pool running short."""
+    _run(WORKLOADS[2], check_pairs=[0, 12, 47, 63], steps=70)
 
 
 def test_capacity_sets_status():
