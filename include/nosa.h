@@ -93,7 +93,10 @@ typedef struct nosa_config {
  *     K part  [64 tokens][128 dims]   (row = token)
  *     V part  [128 dims][64 tokens]   (row = dim; V transposed)
  * A block is the pages' 16 KiB-per-tensor transfer unit (aiwiki "NOSA",
- * Main-experiment configuration), with K and V adjacent.
+ * Main-experiment configuration), with K and V adjacent. Inside a
+ * sequence's newest block the positions at and past seq_len hold zeros:
+ * nosa_prefill_init clears them and nosa_compress_append clears a block when
+ * a token opens it; callers must not write there between calls.
  */
 typedef struct nosa_state {
   int32_t *seq_len;       /* dev [B]: tokens per sequence; +1 per append    */
@@ -141,9 +144,8 @@ int nosa_validate_config(const nosa_config *cfg);
 int nosa_state_bytes(const nosa_config *cfg, size_t sizes_out[NOSA_NUM_BUFFERS]);
 
 /* Workspace bytes that call `which` needs for sequences up to max_len
- * tokens; 0 for an invalid config. A workspace must be 256-byte aligned.
- * The decode workspace must be zero-filled before its first use (its
- * per-pair arrival counters return to zero at the end of every call). */
+ * tokens; 0 for an invalid config. A workspace must be 256-byte aligned;
+ * its contents need no initialisation. */
 size_t nosa_workspace_bytes(const nosa_config *cfg, int which, int32_t max_len);
 
 /* ------------------------------------------------------------ calls */
@@ -215,7 +217,7 @@ int nosa_fetch_delta(const nosa_config *cfg, const nosa_state *st,
  * beta = 1 with NOSA_EVICT_BIAS, else 0 (aiwiki "NOSA", How NOSA works;
  * l189 article, 2.1, eq. 8). K, V are read from kv_dev at block index
  * phys[i] (resident: pass phys = sel). out: dev fp32 [B][Hq][128].
- * ws: NOSA_WS_DECODE bytes, zero-filled before first use. */
+ * ws: NOSA_WS_DECODE bytes. */
 int nosa_sparse_decode(const nosa_config *cfg, const nosa_state *st,
                        const uint16_t *q, const int32_t *sel,
                        const int32_t *phys, const int32_t *n_sel, float *out,

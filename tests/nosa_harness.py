@@ -61,7 +61,7 @@ class StepReport:
 
 class Lockstep:
     def __init__(self, wl, layer=0, check_pairs=None, lengths=None,
-                 offload=None, steps=None):
+                 offload=None, steps=None, before_prefill=None):
         self.wl = wl
         self.layer_idx = layer
         B, Hkv, G = wl.batch, wl.n_kv_heads, wl.group
@@ -95,6 +95,8 @@ class Lockstep:
                     Kf, Vf, bf16_bits_to_f64(w1[g]), bf16_bits_to_f64(w2[g]), Lb,
                     wl.n_sink_blocks, self.n_w, wl.k_q_blocks, self.k_e_dyn,
                     1.0 if wl.evict_bias else 0.0)
+        if before_prefill is not None:
+            before_prefill(self)
         self.gpu.prefill(self.lengths)
         # per-step inputs for every pair / head
         Hq = wl.n_q_heads
@@ -267,7 +269,7 @@ class Lockstep:
         # the wrongly fetched blocks are simply cached extra; fetching the
         # oracle's selection now evicts them
         g.fetch(sel_t, nsel_t)
-        g.decode(qd, sel_t, g.phys, nsel_t)
+        g.decode(qd, sel_t, g.phys if self.shape.offload else sel_t, nsel_t)
         torch.cuda.synchronize()
 
     def check_cache(self):

@@ -133,19 +133,38 @@ def test_capacity_sets_status():
 
 
 def test_nan_bytes_past_length_are_ignored():
-    """Pool bytes past each sequence's length hold NaN patterns: attention
-    must not see them (masked logits, and V zeroed past L)."""
-    wl = small_workload(113, context=1000, steps=20)
-    ls = Lockstep(wl, lengths=[1000, 937])
-    g = ls.gpu
-    pool = g.kv_dev.view(ls.P, ls.shape.nb_max, 2, 64, 128)
+    """The pool holds NaN patterns past each sequence's length when prefill
+    runs: prefill clears the tail of the partial block, append clears each
+    block it opens, so attention never meets them."""
+    wl = small_workload(113, context=1000, steps=80)
     nan = int(np.array([0x7FC0], dtype=np.uint16).view(np.int16)[0])
-    for p in range(ls.P):
-        Lb = int(ls.lengths[p // wl.n_kv_heads])
-        blk, r = divmod(Lb, 64)
-        pool[p, blk, 0, r:] = nan
-        pool[p, blk, 1].view(128, 64)[:, r:] = nan
-        pool[p, blk + 1:] = nan
-    torch.cuda.synchronize()
+
+    def plant(ls):
+        pool = ls.gpu.kv_dev.view(ls.P, ls.shape.nb_max, 2, 64, 128)
+        for p in range(ls.P):
+            Lb = int(ls.lengths[p // wl.n_kv_heads])
+            blk, r = divmod(Lb, 64)
+            pool[p, blk, 0, r:] = nan
+            pool[p, blk, 1].view(128, 64)[:, r:] = nan
+            pool[p, blk + 1:] = nan
+        torch.cuda.synchronize()
+
+    ls = Lockstep(wl, lengths=[1000, 937], before_prefill=plant)
     ls.check_prefill()
     ls.run()
+
+
+def test_resident_fetch_is_identity():
+    """With resident KV, nosa_fetch_delta only sets phys = sel, n_miss = 0."""
+    wl = small_workload(114)
+    ls = Lockstep(wl)
+    kd, vd, qd = ls.inputs(0)
+    g = ls.gpu
+    g.append(kd, vd)
+    g.select(qd)
+    g.phys.fill_(-7)
+    g.n_miss.fill_(5)
+    g.fetch(force=True)
+    torch.cuda.synchronize()
+    assert torch.equal(g.phys, g.sel)
+    assert int(g.n_miss.abs().sum()) == 0

@@ -14,7 +14,9 @@ import re
 import torch  # noqa: F401  (provides the HIP runtime; see module docstring)
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libnosa.so")
+# NOSA_LIBRARY may name another build of the same library (e.g. a tuning
+# variant); by default the in-tree build is used.
+LIB_PATH = os.environ.get("NOSA_LIBRARY") or os.path.join(PKG, "libnosa.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "nosa.h")
 
 NOSA_OK = 0

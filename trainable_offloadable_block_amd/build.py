@@ -53,10 +53,10 @@ def sources():
                   if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src,
-           "-o", obj]
+def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [_hipcc(), *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", INCLUDE,
+           "-I", CSRC, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
@@ -67,23 +67,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compiles every HIP source and links libnosa.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = True, out_path: str = LIB_PATH, defines=()) -> str:
+    """Compiles every HIP source and links libnosa.so (or out_path, with
+    extra preprocessor defines for a tuning variant); returns its path."""
+    build_dir = BUILD_DIR if out_path == LIB_PATH else out_path + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda f: _compile(f, build_dir, defines), srcs))
     tlib = _torch_lib_dir()
-    tmp = LIB_PATH + ".tmp"
+    tmp = out_path + ".tmp"
     cmd = ["g++", "-shared", "-o", tmp, *objs, f"-L{tlib}", "-lamdhip64",
            f"-Wl,-rpath,{tlib}", "-Wl,--no-undefined", "-lstdc++"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out_path)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {out_path}")
+    return out_path
 
 
 if __name__ == "__main__":

@@ -30,6 +30,15 @@ __device__ float evict_score_128(const float *v_sh, const uint16_t *__restrict__
   return red2[0] + red2[1];
 }
 
+// Zeroes one 32 KiB block with the workgroup's 128 threads; the barrier
+// orders the zeros before the caller's token writes into the same block.
+__device__ void clear_block(uint16_t *blk) {
+  uint4 *b4 = reinterpret_cast<uint4 *>(blk);
+  for (int i = threadIdx.x; i < kBlockElems * 2 / 16; i += blockDim.x) b4[i] = make_uint4(0, 0, 0, 0);
+  __threadfence_block();
+  __syncthreads();
+}
+
 // ------------------------------------------------------------- append
 // grid (Hkv, B), block 128: one pair per workgroup, thread t = dim t.
 __global__ __launch_bounds__(128) void append_kernel(
@@ -52,6 +61,7 @@ __global__ __launch_bounds__(128) void append_kernel(
     // 1. store K, V (K row-major, V transposed inside the block)
     if (!d.offload) {
       uint16_t *base = st.kv_dev + ((size_t)p * d.NB_max + blk) * kBlockElems;
+      if (r == 0) clear_block(base);
       base[r * kHeadDim + t] = kb;
       base[kBlock * kHeadDim + t * kBlock + r] = vb;
     } else {
@@ -82,6 +92,7 @@ __global__ __launch_bounds__(128) void append_kernel(
       }
       if (slot >= 0) {
         uint16_t *cb = st.kv_dev + ((size_t)p * (d.k + 1) + slot) * kBlockElems;
+        if (r == 0) clear_block(cb);
         cb[r * kHeadDim + t] = kb;
         cb[kBlock * kHeadDim + t * kBlock + r] = vb;
       }
@@ -131,11 +142,13 @@ __global__ __launch_bounds__(128) void append_kernel(
       }
     }
   }
-  // last workgroup of this sequence advances its length
+  // last workgroup of this sequence advances its length. Every workgroup
+  // has consumed seq_len[b] (all its addresses depend on it) before it
+  // arrives, so no fence is needed (a device-scope fence would write back
+  // the XCD's whole L2).
   __syncthreads();
   if (t == 0) {
     if (!ok) atomicOr(st.status, NOSA_STATUS_CAPACITY);
-    __threadfence();
     const int old = atomicAdd(&st.arrive[b], 1);
     if (old == d.Hkv - 1) {
       st.arrive[b] = 0;
@@ -221,6 +234,16 @@ __global__ __launch_bounds__(128) void prefill_finish_kernel(Dims d, nosa_state 
   if (d.offload) {
     if (idx < d.NB_max) st.slot_of_block[(size_t)p * d.NB_max + idx] = -1;
     if (idx <= d.k) st.block_of_slot[(size_t)p * (d.k + 1) + idx] = -1;
+  }
+  if (L % kBlock) {
+    // tail of the last, partial block: K rows and V^T columns past L read 0
+    uint16_t *base = (d.offload ? st.kv_host : st.kv_dev) +
+                     ((size_t)p * d.NB_max + L / kBlock) * kBlockElems;
+    const int r0 = L % kBlock, n = (kBlock - r0) * kHeadDim;
+    for (int i = idx; i < n; i += gridDim.x * blockDim.x) {
+      base[r0 * kHeadDim + i] = 0;                                   // K
+      base[kBlock * kHeadDim + (i / (kBlock - r0)) * kBlock + r0 + i % (kBlock - r0)] = 0;  // V^T
+    }
   }
   if (blockIdx.x == 0) {
     // ring slot j holds the key of the latest position congruent to j mod 32

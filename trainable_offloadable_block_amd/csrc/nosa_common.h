@@ -20,6 +20,8 @@ constexpr int kMaxContext = 1 << 18;   // 262144 tokens
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __host__ __device__ inline int chunks_for(int L) {
   return L < kPoolKernel ? 0 : (L - kPoolKernel) / kPoolStride + 1;

@@ -2,44 +2,207 @@
 // 解码阶段如何只用 64 个 KV 块; aiwiki "NOSA", How NOSA works: the eviction
 // score enters the logits as an additive bias; l189 article, 2.1, eq. 8).
 //
-// decode_splitk_kernel: grid (splits, pairs), 4 waves. Each wave walks whole
-//   64-token blocks of its split; per 32-token half it computes the group's
-//   logits S^T = K Q^T on MFMA (16 query rows padded to the 16x16x32 shape),
-//   an online softmax in the log2 domain, and O^T += V^T P^T on MFMA with P
-//   split into bf16 hi + lo parts (P alone in bf16 would cost ~1e-3 relative
-//   error). The 4 waves merge in LDS; one partial (m, l, o) per split.
-// decode_combine_kernel: merges the split partials and normalises.
+// decode_kernel: grid (splits, pairs), 4 waves per workgroup. Each wave
+//   streams its share of the pair's selected blocks half by half (32 tokens),
+//   with the next half's loads in flight while the current one is computed:
+//   logits S^T = K Q^T on MFMA (the GQA group padded to 16 rows of the
+//   16x16x32 shape), an online softmax in the log2 domain with the bias
+//   fused, and O^T += V^T P^T on MFMA with P split into bf16 hi + lo parts
+//   (P alone in bf16 would cost ~1e-3 relative error). The 4 waves merge in
+//   LDS into one partial (m, l, o) per split.
+// decode_combine_kernel: merges the splits of each (pair, head) and
+//   normalises. (A merge by the last-arriving workgroup would need a
+//   device-scope release per workgroup, which writes back the whole L2 of
+//   its XCD: far dearer than a second launch.)
 #include "nosa_internal.h"
 
 namespace nosa {
 namespace {
 
+#ifndef NOSA_DECODE_GLOBAL_LOADS
+#define NOSA_DECODE_GLOBAL_LOADS 0
+#endif
+#ifndef NOSA_DECODE_MIN_WAVES
+#define NOSA_DECODE_MIN_WAVES 1
+#endif
+
 constexpr int kDecThreads = 256;
+constexpr int kMaxSplits = 16;   // k <= 64 blocks, >= 4 blocks per split
 constexpr float kLog2e = 1.4426950408889634f;
 
+// A-row r of tile t <-> row 8*(r/4) + 4*t + (r%4) of a 32-row group, so that
+// lane group j ends up holding rows 8j .. 8j+7 of the group (see select).
 __device__ inline int tile_row(int r, int t) { return 8 * (r >> 2) + 4 * t + (r & 3); }
 
 __device__ inline uint4 ldg16(const uint16_t *p) {
   return *reinterpret_cast<const uint4 *>(p);
 }
 
-__global__ __launch_bounds__(kDecThreads, 2) void decode_splitk_kernel(
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over [base, base + bytes): loads past the end read 0.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Bytes past a sequence's length inside its newest block are zero (append
+// clears a block when a token opens it, prefill clears the tail of the last
+// partial block), so V there is finite and its probability 0 keeps it out.
+
+// One 32-token half of a selected block, as this lane's MFMA operands.
+struct Half {
+  uint4 k[2][4];   // K rows of the two QK tiles, 4 k-steps each
+  uint4 v[8];      // V^T rows of the 8 dim tiles: 8 keys of one dim
+  float s;         // eviction score of key (lane % 32) of the half
+  int key_base;    // token index of the half's first key (wave-uniform)
+  int ok;          // 0: past the wave's list or an invalid entry (uniform)
+};
+
+struct DecodeArgs {
+  const int32_t *sel, *phys;
+  __amdgpu_buffer_rsrc_t kv;   // this pair's blocks
+  __amdgpu_buffer_rsrc_t ts;   // this pair's eviction scores
+  const uint16_t *kv_ptr;      // the same, as plain pointers
+  const float *ts_ptr;
+  int koff[2], voff, soff;     // per-lane byte offsets inside a block / half
+  int p, slots, e_first, e_end;
+};
+
+// Issues the loads of half j (< the wave's half count) of the wave's list
+// (entries e_first, e_first + 4, ...; two halves each). The loads are
+// unconditional, so the compiler can keep one half in flight while another
+// is computed; an invalid entry reads slot 0 and is marked not ok.
+__device__ inline void load_half(Half &hb, int j, const DecodeArgs &a, const Dims &d,
+                                 uint32_t *status) {
+  const int e = a.e_first + (j >> 1) * 4, half = j & 1;
+  int blk = a.sel[(size_t)a.p * d.k + e];
+  int slot = a.phys[(size_t)a.p * d.k + e];
+  hb.ok = 1;
+  if (blk < 0 || blk >= d.NB_max || slot < 0 || slot >= a.slots) {
+    if (half == 0 && (threadIdx.x & 63) == 0) atomicOr(status, NOSA_STATUS_BAD_SEL);
+    hb.ok = 0;
+    blk = 0;
+    slot = 0;
+  }
+  const int kbase = slot * (kBlockElems * 2) + half * (32 * kHeadDim * 2);
+  const int vbase = slot * (kBlockElems * 2) + kBlock * kHeadDim * 2 + half * 64;
+  hb.key_base = blk * kBlock + 32 * half;
+#if NOSA_DECODE_GLOBAL_LOADS
+  const char *kvb = reinterpret_cast<const char *>(a.kv_ptr);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      hb.k[t][s] = *reinterpret_cast<const uint4 *>(kvb + kbase + a.koff[t] + 64 * s);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    hb.v[dt] = *reinterpret_cast<const uint4 *>(kvb + vbase + a.voff + 16 * kBlock * 2 * dt);
+  hb.s = a.ts_ptr[hb.key_base + (threadIdx.x & 31)];
+#else
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) hb.k[t][s] = bload16(a.kv, a.koff[t] + 64 * s, kbase);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) hb.v[dt] = bload16(a.kv, a.voff + 16 * kBlock * 2 * dt, vbase);
+  hb.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(a.ts, a.soff,
+                                                                        hb.key_base * 4, 0));
+#endif
+}
+
+// Online-softmax update with one half: logits on MFMA, then O^T += V^T P^T.
+__device__ inline void process_half(Half &hb, const bf16x8 (&qop)[4], float qscale,
+                                    float bscale, int L, int lg, float &m_run, float &l_run,
+                                    f32x4 (&o)[8]) {
+  if (!hb.ok) return;                          // wave-uniform
+  f32x4 acc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc[t] = mfma16x16x32(as_bf16x8(hb.k[t][s]), qop[s], acc[t]);
+  }
+  const int key0 = hb.key_base + 8 * lg;       // this lane's first key
+  float x[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const float sv = __shfl(hb.s, 8 * lg + m, 64);
+    const float lg2 = acc[m >> 2][m & 3] * qscale + sv * bscale;
+    x[m] = (key0 + m) < L ? lg2 : -INFINITY;
+    mx = fmaxf(mx, x[m]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float m_new = fmaxf(m_run, mx);
+  if (m_new == -INFINITY) return;              // wave-uniform: nothing valid
+  const float alpha = exp2f(m_run - m_new);    // 0 while m_run = -inf
+  m_run = m_new;
+  float psum = 0.0f;
+  uint32_t phi[4], plo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2 pm = {exp2f(x[2 * i] - m_new), exp2f(x[2 * i + 1] - m_new)};
+    psum += pm[0] + pm[1];
+    // P = hi + lo, both bf16 (round to nearest even)
+    const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(pm, bf16x2));
+    const f32x2 back = {__uint_as_float(hi << 16), __uint_as_float(hi & 0xFFFF0000u)};
+    phi[i] = hi;
+    plo[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pm - back, bf16x2));
+  }
+  l_run = l_run * alpha + psum;
+  const bf16x8 bhi = __builtin_bit_cast(bf16x8, uint4{phi[0], phi[1], phi[2], phi[3]});
+  const bf16x8 blo = __builtin_bit_cast(bf16x8, uint4{plo[0], plo[1], plo[2], plo[3]});
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    o[dt] *= alpha;
+    o[dt] = mfma16x16x32(as_bf16x8(hb.v[dt]), bhi, o[dt]);
+    o[dt] = mfma16x16x32(as_bf16x8(hb.v[dt]), blo, o[dt]);
+  }
+}
+
+__global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_kernel(
     Dims d, const int32_t *__restrict__ seq_len, const uint16_t *__restrict__ q,
     const int32_t *__restrict__ sel, const int32_t *__restrict__ phys,
-    const int32_t *__restrict__ n_sel, const uint16_t *__restrict__ kv,
-    int slots_per_pair, const float *__restrict__ tok_s,
-    float *__restrict__ ws_o, float2 *__restrict__ ws_ml, int bps, int n_splits,
-    uint32_t *status) {
+    const int32_t *__restrict__ n_sel, const uint16_t *__restrict__ kv, int slots_per_pair,
+    const float *__restrict__ tok_s, float *__restrict__ ws_o, float2 *__restrict__ ws_ml,
+    int bps, int n_splits, uint32_t *status) {
   const int split = blockIdx.x, p = blockIdx.y;
   const int b = p / d.Hkv, g = p % d.Hkv;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
   const int h = l & 15, lg = l >> 4;
   const int L = seq_len[b];
   const int ns = max(0, min(n_sel[p], d.k));
-  const int e0 = split * bps, e1 = min(ns, e0 + bps);
 
   __shared__ float sm_m[4][16], sm_l[4][16];
   __shared__ float sm_o[4][16][kHeadDim + 4];
+
+  DecodeArgs a;
+  a.sel = sel;
+  a.phys = phys;
+  a.kv = make_rsrc(kv + (size_t)p * slots_per_pair * kBlockElems,
+                   (uint32_t)slots_per_pair * kBlockElems * 2);
+  a.ts = make_rsrc(tok_s + (size_t)p * d.tok_stride, (uint32_t)d.tok_stride * 4);
+  a.kv_ptr = kv + (size_t)p * slots_per_pair * kBlockElems;
+  a.ts_ptr = tok_s + (size_t)p * d.tok_stride;
+  a.koff[0] = tile_row(h, 0) * kHeadDim * 2 + 16 * lg;
+  a.koff[1] = tile_row(h, 1) * kHeadDim * 2 + 16 * lg;
+  a.voff = h * kBlock * 2 + 16 * lg;
+  a.soff = 4 * (l & 31);
+  a.p = p;
+  a.slots = slots_per_pair;
+  a.e_first = split * bps + w;
+  a.e_end = min(ns, split * bps + bps);
+  const int n_mine = a.e_first < a.e_end ? (a.e_end - a.e_first + 3) / 4 : 0;
+  const int nh = 2 * n_mine;
+
+  Half A, B;
+  if (nh > 0) load_half(A, 0, a, d, status);
 
   bf16x8 qop[4];
   if (h < d.G) {
@@ -52,100 +215,28 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_splitk_kernel(
   }
   const float qscale = 0.08838834764831845f * kLog2e;   // log2(e) / sqrt(128)
   const float bscale = d.bias ? kLog2e : 0.0f;
-  const float *tsp = tok_s + (size_t)p * d.tok_stride;
 
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4 o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int e = e0 + w; e < e1; e += 4) {
-    const int blk = sel[(size_t)p * d.k + e];
-    const int slot = phys[(size_t)p * d.k + e];
-    if (blk < 0 || blk >= d.NB_max || slot < 0 || slot >= slots_per_pair) {
-      if (l == 0) atomicOr(status, NOSA_STATUS_BAD_SEL);
-      continue;
-    }
-    const uint16_t *kb = kv + ((size_t)p * slots_per_pair + slot) * kBlockElems;
-    const uint16_t *vb = kb + kBlock * kHeadDim;
-    const int tok0 = blk * kBlock;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      // issue this half's loads: K rows, V^T rows, eviction scores
-      uint4 ka[2][4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint16_t *kr = kb + (32 * half + tile_row(h, t)) * kHeadDim + 8 * lg;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) ka[t][s] = ldg16(kr + 32 * s);
-      }
-      uint4 va[8];
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        va[dt] = ldg16(vb + (16 * dt + h) * kBlock + 32 * half + 8 * lg);
-      const int key0 = tok0 + 32 * half + 8 * lg;   // this lane's 8 keys
-      if (tok0 + 32 * half + 32 > L) {
-        // partial block: zero V of keys past L so that stale or uninitialised
-        // cache bytes cannot reach the sum (their probabilities are 0)
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          u16x8 v = __builtin_bit_cast(u16x8, va[dt]);
-#pragma unroll
-          for (int m = 0; m < 8; ++m)
-            if (key0 + m >= L) v[m] = 0;
-          va[dt] = __builtin_bit_cast(uint4, v);
-        }
-      }
-      const float4 s0 = *reinterpret_cast<const float4 *>(tsp + key0);
-      const float4 s1 = *reinterpret_cast<const float4 *>(tsp + key0 + 4);
-      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-
-      f32x4 acc[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[t] = mfma16x16x32(as_bf16x8(ka[t][s]), qop[s], acc[t]);
-      }
-      float x[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float lg2 = acc[m >> 2][m & 3] * qscale + sv[m] * bscale;
-        x[m] = (key0 + m) < L ? lg2 : -INFINITY;
-        mx = fmaxf(mx, x[m]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      if (m_new == -INFINITY) continue;            // nothing valid yet
-      const float alpha = exp2f(m_run - m_new);    // 0 when m_run = -inf
-      m_run = m_new;
-      float psum = 0.0f;
-      uint16_t phi[8], plo[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float pm = exp2f(x[m] - m_new);
-        psum += pm;
-        const uint16_t hi = f32_to_bf16_rne(pm);
-        phi[m] = hi;
-        plo[m] = f32_to_bf16_rne(pm - bf16_to_f32(hi));
-      }
-      l_run = l_run * alpha + psum;
-      const bf16x8 bhi = __builtin_bit_cast(bf16x8, u16x8{phi[0], phi[1], phi[2], phi[3],
-                                                          phi[4], phi[5], phi[6], phi[7]});
-      const bf16x8 blo = __builtin_bit_cast(bf16x8, u16x8{plo[0], plo[1], plo[2], plo[3],
-                                                          plo[4], plo[5], plo[6], plo[7]});
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        o[dt] *= alpha;
-        o[dt] = mfma16x16x32(as_bf16x8(va[dt]), bhi, o[dt]);
-        o[dt] = mfma16x16x32(as_bf16x8(va[dt]), blo, o[dt]);
-      }
-    }
+  // nh is even (two halves per entry); the last pair is peeled so that no
+  // load inside the loop is conditional
+  for (int j = 0; j < nh - 2; j += 2) {
+    load_half(B, j + 1, a, d, status);
+    process_half(A, qop, qscale, bscale, L, lg, m_run, l_run, o);
+    load_half(A, j + 2, a, d, status);
+    process_half(B, qop, qscale, bscale, L, lg, m_run, l_run, o);
   }
+  if (nh > 0) {
+    load_half(B, nh - 1, a, d, status);
+    process_half(A, qop, qscale, bscale, L, lg, m_run, l_run, o);
+    process_half(B, qop, qscale, bscale, L, lg, m_run, l_run, o);
+  }
+
   // lane (h, lg): head h's running max, its keys' partial sum, and
-  // O^T[16*dt + 4*lg + i][h]
+  // O^T[16*dt + 4*lg + i][h]; merge the 4 waves in LDS
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   if (lg == 0) {
@@ -173,42 +264,53 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_splitk_kernel(
     ws_o[(part * d.G + hh) * kHeadDim + dim] = acc;
     if (dim == 0) ws_ml[part * d.G + hh] = make_float2(M, lsum);
   }
+
 }
 
-// grid (P), block 256: out[b][g*G + h][dim] = sum_s w_s o_s / sum_s w_s l_s
-__global__ __launch_bounds__(kDecThreads) void decode_combine_kernel(
-    Dims d, const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml,
-    int n_splits, float *__restrict__ out) {
-  const int p = blockIdx.x;
+// grid (G, P), block 128 (one thread per dim): merges the split partials of
+// one query head and normalises. The split loads of each output element are
+// independent, so they are in flight together.
+__global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(
+    Dims d, const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml, int n_splits,
+    float *__restrict__ out) {
+  const int hh = blockIdx.x, p = blockIdx.y, dim = threadIdx.x;
   const int b = p / d.Hkv, g = p % d.Hkv;
-  for (int idx = threadIdx.x; idx < d.G * kHeadDim; idx += kDecThreads) {
-    const int hh = idx / kHeadDim, dim = idx % kHeadDim;
-    float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, ws_ml[((size_t)p * n_splits + s) * d.G + hh].x);
-    float acc = 0.0f, lsum = 0.0f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < n_splits; ++s) {
-        const size_t part = (size_t)p * n_splits + s;
-        const float2 ml = ws_ml[part * d.G + hh];
-        const float f = exp2f(ml.x - M);
-        acc += f * ws_o[(part * d.G + hh) * kHeadDim + dim];
-        lsum += f * ml.y;
-      }
-    }
-    out[((size_t)b * d.Hq + g * d.G + hh) * kHeadDim + dim] = lsum > 0.0f ? acc / lsum : 0.0f;
+  float mv[kMaxSplits], lv[kMaxSplits], ov[kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    const size_t part = ((size_t)p * n_splits + sp) * d.G + hh;
+    const bool in = sp < n_splits;
+    const float2 ml = in ? ws_ml[part] : make_float2(-INFINITY, 0.0f);
+    mv[sp] = ml.x;
+    lv[sp] = ml.y;
+    ov[sp] = in ? ws_o[part * kHeadDim + dim] : 0.0f;
   }
+  float M = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) M = fmaxf(M, mv[sp]);
+  float acc = 0.0f, lsum = 0.0f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp) {
+      const float f = exp2f(mv[sp] - M);   // 0 for empty splits (m = -inf)
+      acc += f * ov[sp];
+      lsum += f * lv[sp];
+    }
+  }
+  out[((size_t)b * d.Hq + g * d.G + hh) * kHeadDim + dim] = lsum > 0.0f ? acc / lsum : 0.0f;
 }
 
 }  // namespace
 
 DecodeLayout decode_layout(const Dims &d) {
   DecodeLayout lay;
-  int bps = 4;
-  // enough workgroups to cover the chip about twice, whole waves per block
-  while (bps < 16 && (long)d.P * ((d.k + 2 * bps - 1) / (2 * bps)) >= 1024) bps *= 2;
+  // 16 blocks per workgroup (4 per wave, streamed with one half in flight)
+  // while the grid still covers every CU; fewer when the pair count is small
+  int bps = 16;
+  while (bps > 4 && (long)d.P * ((d.k + bps - 1) / bps) < 256) bps /= 2;
   if (const char *env = getenv("NOSA_DECODE_BPS")) {
     const int v = atoi(env);
-    if (v >= 1 && v <= 64) bps = v;
+    if (v >= 4 && v <= 64) bps = v;
   }
   lay.blocks_per_split = bps;
   lay.n_splits = (d.k + bps - 1) / bps;
@@ -220,16 +322,16 @@ DecodeLayout decode_layout(const Dims &d) {
 }
 
 hipError_t launch_decode(const Dims &d, const nosa_state &st, const uint16_t *q,
-                         const int32_t *sel, const int32_t *phys,
-                         const int32_t *n_sel, float *out, void *ws,
-                         const DecodeLayout &lay, hipStream_t s) {
-  float *ws_o = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.o_off);
-  float2 *ws_ml = reinterpret_cast<float2 *>(static_cast<char *>(ws) + lay.ml_off);
+                         const int32_t *sel, const int32_t *phys, const int32_t *n_sel,
+                         float *out, void *ws, const DecodeLayout &lay, hipStream_t s) {
+  char *base = static_cast<char *>(ws);
+  float *ws_o = reinterpret_cast<float *>(base + lay.o_off);
+  float2 *ws_ml = reinterpret_cast<float2 *>(base + lay.ml_off);
   const int slots = d.offload ? d.k + 1 : d.NB_max;
-  decode_splitk_kernel<<<dim3(lay.n_splits, d.P), kDecThreads, 0, s>>>(
+  decode_kernel<<<dim3(lay.n_splits, d.P), kDecThreads, 0, s>>>(
       d, st.seq_len, q, sel, phys, n_sel, st.kv_dev, slots, st.tok_s, ws_o, ws_ml,
       lay.blocks_per_split, lay.n_splits, st.status);
-  decode_combine_kernel<<<dim3(d.P), kDecThreads, 0, s>>>(d, ws_o, ws_ml, lay.n_splits, out);
+  decode_combine_kernel<<<dim3(d.G, d.P), kHeadDim, 0, s>>>(d, ws_o, ws_ml, lay.n_splits, out);
   return hipGetLastError();
 }
 

@@ -210,7 +210,12 @@ class NosaLayer:
             _ptr(self.ws_select), self.ws_select.numel(), self.max_len, self.stream),
             "select")
 
-    def fetch(self, sel=None, n_sel=None):
+    def fetch(self, sel=None, n_sel=None, force=False):
+        """Offload: brings the selection's missing blocks into the cache.
+        Resident KV needs no fetch (decode reads each block at its own
+        index), so the call is skipped unless force=True."""
+        if not self.shape.offload and not force:
+            return
         sel = self.sel if sel is None else sel
         n_sel = self.n_sel if n_sel is None else n_sel
         L.check(L.lib().nosa_fetch_delta(
@@ -220,7 +225,8 @@ class NosaLayer:
 
     def decode(self, q: torch.Tensor, sel=None, phys=None, n_sel=None):
         sel = self.sel if sel is None else sel
-        phys = self.phys if phys is None else phys
+        if phys is None:
+            phys = self.phys if self.shape.offload else sel
         n_sel = self.n_sel if n_sel is None else n_sel
         L.check(L.lib().nosa_sparse_decode(
             ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(q), _ptr(sel),
