@@ -11,17 +11,30 @@
 namespace nosa {
 namespace {
 
-// s = softplus(v W1) W2 for one value vector held in LDS as fp32. Called by
-// all 128 threads of a group; thread t owns hidden unit t. The summation
-// order is fixed (e ascending, then a fixed reduction tree), so every caller
-// gets the same bits for the same v.
-__device__ float evict_score_128(const float *v_sh, const uint16_t *__restrict__ W1g,
+// Copies one KV head's W1 (32 KiB bf16) into LDS: 16 independent 16-byte
+// loads per thread for a 128-thread group, then a barrier.
+__device__ void stage_w1(uint16_t *w1_sh, const uint16_t *__restrict__ W1g) {
+  const uint4 *src = reinterpret_cast<const uint4 *>(W1g);
+  uint4 *dst = reinterpret_cast<uint4 *>(w1_sh);
+  uint4 v[kHeadDim * kHeadDim * 2 / 16 / 128];
+#pragma unroll
+  for (int j = 0; j < kHeadDim * kHeadDim * 2 / 16 / 128; ++j) v[j] = src[threadIdx.x + 128 * j];
+#pragma unroll
+  for (int j = 0; j < kHeadDim * kHeadDim * 2 / 16 / 128; ++j) dst[threadIdx.x + 128 * j] = v[j];
+  __syncthreads();
+}
+
+// s = softplus(v W1) W2 for one value vector held in LDS as fp32, with W1
+// staged in LDS. Called by all 128 threads of a group; thread t owns hidden
+// unit t. The summation order is fixed (e ascending, then a fixed reduction
+// tree), so every caller gets the same bits for the same v.
+__device__ float evict_score_128(const float *v_sh, const uint16_t *w1_sh,
                                  const uint16_t *__restrict__ W2g, float *red2) {
   const int t = threadIdx.x & 127;
   float acc = 0.0f;
-#pragma unroll 8
+#pragma unroll 16
   for (int e = 0; e < kHeadDim; ++e)
-    acc = fmaf(v_sh[e], bf16_to_f32(W1g[e * kHeadDim + t]), acc);
+    acc = fmaf(v_sh[e], bf16_to_f32(w1_sh[e * kHeadDim + t]), acc);
   float x = softplus_f32(acc) * bf16_to_f32(W2g[t]);
   x = wave_sum(x);
   __syncthreads();                       // red2 may still be read by a caller
@@ -49,6 +62,7 @@ __global__ __launch_bounds__(128) void append_kernel(
   __shared__ float v_sh[kHeadDim];
   __shared__ float red2[2];
   __shared__ int slot_sh;
+  __shared__ __align__(16) uint16_t w1_sh[kHeadDim * kHeadDim];
 
   const int pos = st.seq_len[b];
   const bool ok = pos >= 0 && pos < d.max_context;
@@ -104,9 +118,8 @@ __global__ __launch_bounds__(128) void append_kernel(
 
     // 3. eviction score of the new token
     v_sh[t] = bf16_to_f32(vb);
-    __syncthreads();
-    const float s = evict_score_128(v_sh, st.w1 + (size_t)g * kHeadDim * kHeadDim,
-                                    st.w2 + (size_t)g * kHeadDim, red2);
+    stage_w1(w1_sh, st.w1 + (size_t)g * kHeadDim * kHeadDim);   // ends in a barrier
+    const float s = evict_score_128(v_sh, w1_sh, st.w2 + (size_t)g * kHeadDim, red2);
     float *tok_s = st.tok_s + (size_t)p * d.tok_stride;
     if (t == 0) tok_s[pos] = s;
 
@@ -169,19 +182,19 @@ __global__ __launch_bounds__(128) void prefill_scores_kernel(Dims d, nosa_state 
   __shared__ uint4 vt_sh[kBlock * kHeadDim * 2 / 16];   // V part, 16 KiB
   __shared__ float v_sh[kHeadDim];
   __shared__ float red2[2];
+  __shared__ __align__(16) uint16_t w1_sh[kHeadDim * kHeadDim];
   const uint16_t *src = (d.offload ? st.kv_host : st.kv_dev) +
                         ((size_t)p * d.NB_max + blk) * kBlockElems + kBlock * kHeadDim;
   const uint4 *src4 = reinterpret_cast<const uint4 *>(src);
   for (int i = t; i < kBlock * kHeadDim * 2 / 16; i += blockDim.x) vt_sh[i] = src4[i];
-  __syncthreads();
+  stage_w1(w1_sh, st.w1 + (size_t)g * kHeadDim * kHeadDim);   // ends in a barrier
   const uint16_t *vt = reinterpret_cast<const uint16_t *>(vt_sh);
   const int n = min(kBlock, L - blk * kBlock);
   float *tok_s = st.tok_s + (size_t)p * d.tok_stride;
   for (int r = 0; r < n; ++r) {
     v_sh[t] = bf16_to_f32(vt[t * kBlock + r]);
     __syncthreads();
-    const float s = evict_score_128(v_sh, st.w1 + (size_t)g * kHeadDim * kHeadDim,
-                                    st.w2 + (size_t)g * kHeadDim, red2);
+    const float s = evict_score_128(v_sh, w1_sh, st.w2 + (size_t)g * kHeadDim, red2);
     if (t == 0) tok_s[blk * kBlock + r] = s;
   }
 }

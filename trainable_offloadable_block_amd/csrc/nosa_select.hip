@@ -7,7 +7,8 @@
 // pool_topk_kernel (one workgroup per pair): combines the split statistics
 //   into the per-head softmax, sums the group's heads, max-pools the chunks
 //   overlapping each block, then stage 1 (top k_q by the query-aware score)
-//   and stage 2 (top k_e' eligible by the agnostic score), writes the
+//   and stage 2 (top k_e' eligible by the agnostic score), each a wave-level
+//   bitonic top-k over 64-candidate chunks merged across waves, writes the
 //   ascending selection and clears the eligibility of every candidate left
 //   out (never re-selected by the agnostic stage).
 #include "nosa_internal.h"
@@ -137,83 +138,136 @@ __device__ int block_excl_scan(int v, int *sh, int *total) {
   return base + incl - v;
 }
 
-// Marks (kind[i] = val) the k items of largest key among keys[0..n); key 0
-// means "not eligible"; among equal keys the lower index wins. Radix select
-// on 8-bit digits from the top, then one ordered pass for the ties.
-__device__ void topk_mark(const uint32_t *keys, int n, int k, uint8_t *kind,
-                          uint8_t val, int *hist, int *sh) {
-  const int t = threadIdx.x;
-  if (k <= 0 || n <= 0) return;
-  int cnt = 0;
-  for (int i = t; i < n; i += kTopkThreads) cnt += keys[i] != 0u;
-  int valid = 0;
-  block_excl_scan(cnt, sh, &valid);
-  if (valid <= k) {
-    for (int i = t; i < n; i += kTopkThreads)
-      if (keys[i] != 0u) kind[i] = val;
-    __syncthreads();
-    return;
+// ---- wave-level top-k on 64-bit composite keys --------------------------
+// A key is (order_key(score) << 32) | ~block: larger score first, then the
+// lower block id, all keys distinct; 0 marks "not a candidate".
+
+// Value of lane (lane ^ MASK): DPP for masks 1 and 2, ds_swizzle (xor within
+// 32 lanes) for 4, 8, 16, ds_bpermute for 32.
+template <int MASK>
+__device__ inline uint32_t xor_lane(uint32_t v) {
+  const int x = static_cast<int>(v);
+  if constexpr (MASK == 1) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (MASK == 2) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+  } else if constexpr (MASK < 32) {
+    return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(x, 0x1F | (MASK << 10)));
+  } else {
+    return static_cast<uint32_t>(__shfl_xor(x, MASK, 64));
   }
-  uint32_t prefix = 0, mask = 0;
-  int rem = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[t] = 0;
-    __syncthreads();
-    for (int i = t; i < n; i += kTopkThreads) {
-      const uint32_t key = keys[i];
-      if (key != 0u && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    if (t < 64) {
-      const int c0 = hist[255 - 4 * t], c1 = hist[254 - 4 * t];
-      const int c2 = hist[253 - 4 * t], c3 = hist[252 - 4 * t];
-      const int s = c0 + c1 + c2 + c3;
-      int incl = s;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int nb = __shfl_up(incl, o, 64);
-        if (t >= o) incl += nb;
-      }
-      const int excl = incl - s;
-      if (excl < rem && rem <= incl) {
-        const int r = rem - excl;
-        int digit, above = excl;
-        if (r <= c0) {
-          digit = 255 - 4 * t;
-        } else if (r <= c0 + c1) {
-          digit = 254 - 4 * t; above += c0;
-        } else if (r <= c0 + c1 + c2) {
-          digit = 253 - 4 * t; above += c0 + c1;
-        } else {
-          digit = 252 - 4 * t; above += c0 + c1 + c2;
-        }
-        sh[4] = digit;
-        sh[5] = rem - above;
-      }
-    }
-    __syncthreads();
-    prefix |= static_cast<uint32_t>(sh[4]) << shift;
-    mask |= 0xFFu << shift;
-    rem = sh[5];
-    __syncthreads();
-  }
-  // keys above the threshold are in; `rem` threshold-equal keys join them,
-  // lowest index first
-  const int per = (n + kTopkThreads - 1) / kTopkThreads;
-  const int lo = t * per, hi = min(n, lo + per);
-  int eq = 0;
-  for (int i = lo; i < hi; ++i) eq += keys[i] == prefix;
-  int before = block_excl_scan(eq, sh, nullptr);
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t key = keys[i];
-    if (key > prefix) {
-      kind[i] = val;
-    } else if (key == prefix) {
-      if (before < rem) kind[i] = val;
-      ++before;
-    }
+}
+
+template <int MASK>
+__device__ inline uint64_t xor_lane_u64(uint64_t v) {
+  const uint32_t lo = xor_lane<MASK>(static_cast<uint32_t>(v));
+  const uint32_t hi = xor_lane<MASK>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ inline uint64_t lane_u64(uint64_t v, int src) {
+  const int lo = __shfl(static_cast<int>(v & 0xFFFFFFFFu), src, 64);
+  const int hi = __shfl(static_cast<int>(v >> 32), src, 64);
+  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+// One compare-exchange step of a bitonic network with partner lane ^ J;
+// lanes whose (lane & J) == 0 keep the max when `keep_max_low`.
+template <int J>
+__device__ inline uint64_t cas_step(uint64_t v, bool keep_max_low) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t o = xor_lane_u64<J>(v);
+  const bool lower = (lane & J) == 0;
+  return (lower == keep_max_low) ? (v > o ? v : o) : (v < o ? v : o);
+}
+
+template <int K>
+__device__ inline uint64_t sort_stage(uint64_t v) {
+  const bool desc = ((threadIdx.x & 63) & K) == 0;   // direction of this K-block
+  if constexpr (K >= 64) v = cas_step<32>(v, desc);
+  if constexpr (K >= 32) v = cas_step<16>(v, desc);
+  if constexpr (K >= 16) v = cas_step<8>(v, desc);
+  if constexpr (K >= 8) v = cas_step<4>(v, desc);
+  if constexpr (K >= 4) v = cas_step<2>(v, desc);
+  v = cas_step<1>(v, desc);
+  return v;
+}
+
+// Bitonic sort of one key per lane; afterwards lane i holds the i-th largest.
+__device__ inline uint64_t wave_sort_desc(uint64_t v) {
+  v = sort_stage<2>(v);
+  v = sort_stage<4>(v);
+  v = sort_stage<8>(v);
+  v = sort_stage<16>(v);
+  v = sort_stage<32>(v);
+  return sort_stage<64>(v);
+}
+
+// Top 64 of two descending-sorted wave lists, sorted descending: the
+// element-wise max of a and reversed b is bitonic and holds the 64 largest.
+__device__ inline uint64_t wave_merge_desc(uint64_t a, uint64_t b) {
+  const uint64_t br = lane_u64(b, 63 - (threadIdx.x & 63));
+  uint64_t v = a > br ? a : br;
+  v = cas_step<32>(v, true);
+  v = cas_step<16>(v, true);
+  v = cas_step<8>(v, true);
+  v = cas_step<4>(v, true);
+  v = cas_step<2>(v, true);
+  return cas_step<1>(v, true);
+}
+
+__device__ inline uint64_t compose_key(float score, int blk) {
+  return (static_cast<uint64_t>(order_key(score)) << 32) |
+         static_cast<uint32_t>(0xFFFFFFFFu - static_cast<uint32_t>(blk));
+}
+
+__device__ inline int key_block(uint64_t key) {
+  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key & 0xFFFFFFFFu));
+}
+
+// Combines the four waves' sorted top-64 lists and marks the best k blocks
+// (kind[b] = val). Called by all threads of the workgroup.
+__device__ void finish_topk(uint64_t best, int k, uint8_t *kind, uint8_t val,
+                            uint64_t (*top_sh)[64]) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  top_sh[w][lane] = best;
+  __syncthreads();
+  if (w == 0) {
+    const uint64_t b1 = top_sh[1][lane], b2 = top_sh[2][lane], b3 = top_sh[3][lane];
+    best = wave_merge_desc(wave_merge_desc(best, b1), wave_merge_desc(b2, b3));
+    if (lane < k && best != 0) kind[key_block(best)] = val;
   }
   __syncthreads();
+}
+
+// Query-aware score of block bb from the 5 x G chunk weights ev (chunks
+// 4bb-1 .. 4bb+3), with the per-split softmax factors f_sh.
+__device__ inline float block_qscore(const float (&ev)[5][kMaxGroup], int bb, int C,
+                                     const float *f_sh, int G) {
+  float qb = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const int c = 4 * bb - 1 + j;
+    if (c < 0 || c >= C) continue;
+    const float *fs = f_sh + (c / kChunksPerSplit) * G;
+    float a = 0.0f;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+      if (h < G) a = fmaf(ev[j][h], fs[h], a);
+    qb = fmaxf(qb, a);
+  }
+  return qb;
+}
+
+__device__ inline void load_weights(float (&ev)[5][kMaxGroup], const float *ep, int bb, int C,
+                                    int c_pad, int G) {
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const int c = 4 * bb - 1 + j;
+    const bool cin = c >= 0 && c < C;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) ev[j][h] = (cin && h < G) ? ep[(size_t)h * c_pad + c] : 0.0f;
+  }
 }
 
 __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
@@ -222,13 +276,14 @@ __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
     int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
     uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
   extern __shared__ __align__(16) uint8_t smem[];
-  float *f_sh = reinterpret_cast<float *>(smem);                       // [n_splits][G]
-  uint32_t *keys = reinterpret_cast<uint32_t *>(f_sh + n_splits * d.G); // [NB_max]
-  uint8_t *kind = reinterpret_cast<uint8_t *>(keys + d.NB_max);         // [NB_max]
-  __shared__ int hist[256];
+  float *f_sh = reinterpret_cast<float *>(smem);                            // [n_splits][G]
+  uint32_t *el_sh = reinterpret_cast<uint32_t *>(f_sh + n_splits * d.G);    // [elig_words]
+  uint8_t *kind = reinterpret_cast<uint8_t *>(el_sh + d.elig_words);        // [NB_max]
+  __shared__ uint64_t top_sh[kTopkThreads / 64][64];
   __shared__ int sh[8];
 
   const int p = blockIdx.x, t = threadIdx.x;
+  const int w = t >> 6, lane = t & 63;
   const int b = p / d.Hkv;
   const int L = max(0, min(st.seq_len[b], d.max_context));
   int C = chunks_for(L);
@@ -240,65 +295,83 @@ __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
   const int win_lo = max(d.n_sink, nb - d.n_win);
   const int n_cand = max(0, win_lo - d.n_sink);
   const int used = (C + kChunksPerSplit - 1) / kChunksPerSplit;
+  const bool do_q = d.k_q > 0 && n_cand > 0, do_e = d.k_e_dyn > 0 && n_cand > 0;
 
-  // 1. per-split factors exp(m_split - M) / Z of each head's softmax
-  if (n_cand > 0 && d.k_q > 0) {
-    const int h = t >> 4, j = t & 15;
-    if (h < d.G) {
-      const float2 *stp = ws_stats + (size_t)p * n_splits * d.G;
-      double m = -INFINITY;
-      for (int s = j; s < used; s += 16) m = fmax(m, (double)stp[s * d.G + h].x);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) m = fmax(m, __shfl_xor(m, o, 64));
-      double z = 0.0;
-      for (int s = j; s < used; s += 16) {
-        const float2 v = stp[s * d.G + h];
-        if (v.y > 0.0f) z += (double)v.y * exp((double)v.x - m);
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
-      for (int s = j; s < used; s += 16) {
-        const float2 v = stp[s * d.G + h];
-        f_sh[s * d.G + h] = v.y > 0.0f ? (float)(exp((double)v.x - m) / z) : 0.0f;
-      }
-    }
-  }
+  // 0. issue this thread's global loads together: split statistics, the
+  // chunk weights and agnostic score of its first candidate, eligibility
+  const float *ep = ws_e + (size_t)p * d.G * c_pad;
+  const float *be = st.blk_e + (size_t)p * d.NB_max;
+  const int i0 = 64 * w + lane, bb0 = d.n_sink + i0;
+  const bool have0 = i0 < n_cand;
+  float ev[5][kMaxGroup];
+  if (do_q) load_weights(ev, ep, have0 ? bb0 : 0, have0 ? C : 0, c_pad, d.G);
+  const float e0 = (do_e && have0) ? be[bb0] : 0.0f;
+  const int sh_h = t >> 4, sh_j = t & 15;
+  float2 stv = make_float2(-INFINITY, 0.0f);
+  if (do_q && sh_h < d.G && sh_j < used) stv = ws_stats[((size_t)p * n_splits + sh_j) * d.G + sh_h];
+  for (int i = t; i < d.elig_words; i += kTopkThreads)
+    el_sh[i] = st.eligible[(size_t)p * d.elig_words + i];
   for (int bb = t; bb < nb; bb += kTopkThreads)
     kind[bb] = bb < d.n_sink ? NOSA_KIND_SINK : (bb >= win_lo ? NOSA_KIND_WINDOW : NOSA_KIND_NONE);
+
+  // 1. per-split factors exp(m_split - M) / Z of each head's softmax
+  if (do_q && sh_h < d.G) {
+    const float2 *stp = ws_stats + (size_t)p * n_splits * d.G;
+    double m = stv.x;
+    for (int s = sh_j + 16; s < used; s += 16) m = fmax(m, (double)stp[s * d.G + sh_h].x);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = fmax(m, __shfl_xor(m, o, 64));
+    double z = stv.y > 0.0f ? (double)stv.y * exp((double)stv.x - m) : 0.0;
+    for (int s = sh_j + 16; s < used; s += 16) {
+      const float2 v = stp[s * d.G + sh_h];
+      if (v.y > 0.0f) z += (double)v.y * exp((double)v.x - m);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
+    if (sh_j < used) f_sh[sh_j * d.G + sh_h] = stv.y > 0.0f ? (float)(exp((double)stv.x - m) / z) : 0.0f;
+    for (int s = sh_j + 16; s < used; s += 16) {
+      const float2 v = stp[s * d.G + sh_h];
+      f_sh[s * d.G + sh_h] = v.y > 0.0f ? (float)(exp((double)v.x - m) / z) : 0.0f;
+    }
+  }
   __syncthreads();
 
-  // 2. query-aware block score: max over overlapping chunks of the group sum
-  if (d.k_q > 0) {
-    const float *ep = ws_e + (size_t)p * d.G * c_pad;
-    for (int i = t; i < n_cand; i += kTopkThreads) {
-      const int bb = d.n_sink + i;
-      const int lo = max(0, 4 * bb - 1), hi = min(C, 4 * bb + 4);
-      float qb = -INFINITY;
-      for (int c = lo; c < hi; ++c) {
-        const float *fs = f_sh + (c / kChunksPerSplit) * d.G;
-        float a = 0.0f;
-        for (int h = 0; h < d.G; ++h) a = fmaf(ep[(size_t)h * c_pad + c], fs[h], a);
-        qb = fmaxf(qb, a);
+  // 2. stage 1: top k_q candidates by the query-aware score (max over the
+  // overlapping chunks of the group's softmax sum; heads summed in order, so
+  // a chunk shared by two blocks gives both the same value)
+  if (do_q) {
+    uint64_t best = 0;
+    for (int base = 64 * w; base < n_cand; base += kTopkThreads) {   // wave-uniform
+      const int i = base + lane, bb = d.n_sink + i;
+      if (base != 64 * w) load_weights(ev, ep, i < n_cand ? bb : 0, i < n_cand ? C : 0, c_pad, d.G);
+      uint64_t key = 0;
+      if (i < n_cand) {
+        const float qb = block_qscore(ev, bb, C, f_sh, d.G);
+        key = compose_key(qb, bb);
+        if (dbg) dbg[(size_t)p * d.NB_max + bb] = qb;
       }
-      keys[i] = order_key(qb);
-      if (dbg) dbg[(size_t)p * d.NB_max + bb] = qb;
+      best = wave_merge_desc(best, wave_sort_desc(key));
     }
-    __syncthreads();
-    topk_mark(keys, n_cand, d.k_q, kind + d.n_sink, NOSA_KIND_QUERY, hist, sh);
+    finish_topk(best, d.k_q, kind, NOSA_KIND_QUERY, top_sh);
   }
 
-  // 3. agnostic stage over eligible candidates not taken by stage 1
-  if (d.k_e_dyn > 0) {
-    const uint32_t *el = st.eligible + (size_t)p * d.elig_words;
-    const float *be = st.blk_e + (size_t)p * d.NB_max;
-    for (int i = t; i < n_cand; i += kTopkThreads) {
-      const int bb = d.n_sink + i;
-      const bool elig = (el[bb >> 5] >> (bb & 31)) & 1u;
-      keys[i] = (elig && kind[bb] != NOSA_KIND_QUERY) ? order_key(be[bb]) : 0u;
+  // 3. stage 2: top k_e' of the eligible candidates left by stage 1, by the
+  // query-agnostic score
+  if (do_e) {
+    uint64_t best = 0;
+    for (int base = 64 * w; base < n_cand; base += kTopkThreads) {   // wave-uniform
+      const int i = base + lane, bb = d.n_sink + i;
+      uint64_t key = 0;
+      if (i < n_cand) {
+        const float eb = base == 64 * w ? e0 : be[bb];
+        const bool elig = (el_sh[bb >> 5] >> (bb & 31)) & 1u;
+        if (elig && kind[bb] != NOSA_KIND_QUERY) key = compose_key(eb, bb);
+      }
+      best = wave_merge_desc(best, wave_sort_desc(key));
     }
-    __syncthreads();
-    topk_mark(keys, n_cand, d.k_e_dyn, kind + d.n_sink, NOSA_KIND_AGNOSTIC, hist, sh);
+    finish_topk(best, d.k_e_dyn, kind, NOSA_KIND_AGNOSTIC, top_sh);
   }
+  __syncthreads();
 
   // 4. ascending selection list
   {
@@ -334,7 +407,7 @@ __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
         const int bb = wd * 32 + j;
         if (bb >= d.n_sink && bb < win_lo && kind[bb] == NOSA_KIND_NONE) clear |= 1u << j;
       }
-      if (clear) el[wd] &= ~clear;
+      if (clear) el[wd] = el_sh[wd] & ~clear;
     }
   }
 }
@@ -360,7 +433,7 @@ hipError_t launch_select(const Dims &d, const nosa_state &st, const uint16_t *q,
   score_kernel<<<dim3(lay.n_splits, d.P), kScoreThreads, 0, s>>>(
       d, st.seq_len, st.ckey, q, ws_e, ws_stats, lay.c_pad, lay.n_splits);
   const size_t lds = (size_t)lay.n_splits * d.G * sizeof(float) +
-                     (size_t)d.NB_max * sizeof(uint32_t) + (size_t)d.NB_max;
+                     (size_t)d.elig_words * sizeof(uint32_t) + (size_t)d.NB_max;
   pool_topk_kernel<<<dim3(d.P), kTopkThreads, lds, s>>>(
       d, st, ws_e, ws_stats, lay.c_pad, lay.n_splits, sel, n_sel, kind, dbg);
   return hipGetLastError();
