@@ -35,14 +35,17 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64)
-    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--steps", type=int, default=240)
+    ap.add_argument("--warmup", type=int, default=12)
     ap.add_argument("--layers", type=int, default=8,
                     help="independent layers of the workload's shape per step")
-    ap.add_argument("--cpu-pairs", type=int, default=16)
-    ap.add_argument("--cpu-steps", type=int, default=48)
+    ap.add_argument("--cpu-pairs", type=int, default=64)
+    ap.add_argument("--cpu-steps", type=int, default=80)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--breakdown-steps", type=int, default=4)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="run one plain device copy of MIB MiB first (a known "
+                         "byte count for calibrating HBM traffic counters)")
     return ap.parse_args()
 
 
@@ -103,6 +106,26 @@ def attended_tokens(layer, wl):
         blocks = sel[p, :nsel[p]].astype(np.int64)
         tot += int(np.minimum(64, L - 64 * blocks).sum())
     return tot / sel.shape[0]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs
+    (profiles/decode_kernel_traffic.json), or None when the decode kernel's
+    sources have changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["source_sha256"]:
+            return None
+        return int(rec["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(wl, n_pairs, n_steps):
@@ -173,6 +196,14 @@ def main():
                        wl.context + n_tok)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     t_setup = time.perf_counter()
     workers = min(16, len(os.sched_getaffinity(0)))
     layers, inputs = [], []
@@ -262,7 +293,7 @@ def main():
         "roofline": {
             "kernel": "nosa_sparse_decode", "bound": "hbm",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
             "bytes_per_launch": int(dbytes), "avg_launch_us": round(dec_avg_s * 1e6, 2),
             "attended_tokens_per_pair": round(n_att, 2),
         },
