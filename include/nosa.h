@@ -144,8 +144,10 @@ int nosa_validate_config(const nosa_config *cfg);
 int nosa_state_bytes(const nosa_config *cfg, size_t sizes_out[NOSA_NUM_BUFFERS]);
 
 /* Workspace bytes that call `which` needs for sequences up to max_len
- * tokens; 0 for an invalid config. A workspace must be 256-byte aligned;
- * its contents need no initialisation. */
+ * tokens; 0 for an invalid config. A workspace must be 256-byte aligned.
+ * The decode workspace must be zero-filled before its first use (it holds
+ * per-pair arrival counters that every call leaves at zero); the others need
+ * no initialisation. */
 size_t nosa_workspace_bytes(const nosa_config *cfg, int which, int32_t max_len);
 
 /* ------------------------------------------------------------ calls */
@@ -217,7 +219,7 @@ int nosa_fetch_delta(const nosa_config *cfg, const nosa_state *st,
  * beta = 1 with NOSA_EVICT_BIAS, else 0 (aiwiki "NOSA", How NOSA works;
  * l189 article, 2.1, eq. 8). K, V are read from kv_dev at block index
  * phys[i] (resident: pass phys = sel). out: dev fp32 [B][Hq][128].
- * ws: NOSA_WS_DECODE bytes. */
+ * ws: NOSA_WS_DECODE bytes, zero-filled before its first use. */
 int nosa_sparse_decode(const nosa_config *cfg, const nosa_state *st,
                        const uint16_t *q, const int32_t *sel,
                        const int32_t *phys, const int32_t *n_sel, float *out,

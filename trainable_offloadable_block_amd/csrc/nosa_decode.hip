@@ -9,11 +9,8 @@
 //   16x16x32 shape), an online softmax in the log2 domain with the bias
 //   fused, and O^T += V^T P^T on MFMA with P split into bf16 hi + lo parts
 //   (P alone in bf16 would cost ~1e-3 relative error). The 4 waves merge in
-//   LDS into one partial (m, l, o) per split.
-// decode_combine_kernel: merges the splits of each (pair, head) and
-//   normalises. (A merge by the last-arriving workgroup would need a
-//   device-scope release per workgroup, which writes back the whole L2 of
-//   its XCD: far dearer than a second launch.)
+//   LDS into one partial (m, l, o) per split; the last workgroup of a pair to
+//   finish merges all splits and writes the normalised output.
 #include "nosa_internal.h"
 
 namespace nosa {
@@ -74,14 +71,16 @@ struct DecodeArgs {
 };
 
 // Issues the loads of half j (< the wave's half count) of the wave's list
-// (entries e_first, e_first + 4, ...; two halves each). The loads are
-// unconditional, so the compiler can keep one half in flight while another
-// is computed; an invalid entry reads slot 0 and is marked not ok.
+// (entries e_first, e_first + 4, ...; two halves each). Lane i holds the
+// block and slot ids of the wave's i-th entry (loaded once at the start), so
+// no memory round trip precedes the loads. The loads are unconditional, so
+// the compiler can keep one half in flight while another is computed; an
+// invalid entry reads slot 0 and is marked not ok.
 __device__ inline void load_half(Half &hb, int j, const DecodeArgs &a, const Dims &d,
-                                 uint32_t *status) {
-  const int e = a.e_first + (j >> 1) * 4, half = j & 1;
-  int blk = a.sel[(size_t)a.p * d.k + e];
-  int slot = a.phys[(size_t)a.p * d.k + e];
+                                 int lane_blk, int lane_slot, uint32_t *status) {
+  const int half = j & 1;
+  int blk = __builtin_amdgcn_readlane(lane_blk, j >> 1);
+  int slot = __builtin_amdgcn_readlane(lane_slot, j >> 1);
   hb.ok = 1;
   if (blk < 0 || blk >= d.NB_max || slot < 0 || slot >= a.slots) {
     if (half == 0 && (threadIdx.x & 63) == 0) atomicOr(status, NOSA_STATUS_BAD_SEL);
@@ -171,7 +170,8 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
     const int32_t *__restrict__ sel, const int32_t *__restrict__ phys,
     const int32_t *__restrict__ n_sel, const uint16_t *__restrict__ kv, int slots_per_pair,
     const float *__restrict__ tok_s, float *__restrict__ ws_o, float2 *__restrict__ ws_ml,
-    int bps, int n_splits, uint32_t *status) {
+    int32_t *__restrict__ ws_count, int bps, int n_splits, float *__restrict__ out,
+    uint32_t *status) {
   const int split = blockIdx.x, p = blockIdx.y;
   const int b = p / d.Hkv, g = p % d.Hkv;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
@@ -181,6 +181,7 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
 
   __shared__ float sm_m[4][16], sm_l[4][16];
   __shared__ float sm_o[4][16][kHeadDim + 4];
+  __shared__ int sm_last;
 
   DecodeArgs a;
   a.sel = sel;
@@ -199,10 +200,17 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   a.e_first = split * bps + w;
   a.e_end = min(ns, split * bps + bps);
   const int n_mine = a.e_first < a.e_end ? (a.e_end - a.e_first + 3) / 4 : 0;
+  // lane i: block and slot ids of this wave's i-th entry (n_mine <= 16)
+  int lane_blk = -1, lane_slot = -1;
+  if (l < n_mine) {
+    lane_blk = sel[(size_t)p * d.k + a.e_first + 4 * l];
+    lane_slot = phys[(size_t)p * d.k + a.e_first + 4 * l];
+  }
+
   const int nh = 2 * n_mine;
 
   Half A, B;
-  if (nh > 0) load_half(A, 0, a, d, status);
+  if (nh > 0) load_half(A, 0, a, d, lane_blk, lane_slot, status);
 
   bf16x8 qop[4];
   if (h < d.G) {
@@ -224,13 +232,13 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   // nh is even (two halves per entry); the last pair is peeled so that no
   // load inside the loop is conditional
   for (int j = 0; j < nh - 2; j += 2) {
-    load_half(B, j + 1, a, d, status);
+    load_half(B, j + 1, a, d, lane_blk, lane_slot, status);
     process_half(A, qop, qscale, bscale, L, lg, m_run, l_run, o);
-    load_half(A, j + 2, a, d, status);
+    load_half(A, j + 2, a, d, lane_blk, lane_slot, status);
     process_half(B, qop, qscale, bscale, L, lg, m_run, l_run, o);
   }
   if (nh > 0) {
-    load_half(B, nh - 1, a, d, status);
+    load_half(B, nh - 1, a, d, lane_blk, lane_slot, status);
     process_half(A, qop, qscale, bscale, L, lg, m_run, l_run, o);
     process_half(B, qop, qscale, bscale, L, lg, m_run, l_run, o);
   }
@@ -248,7 +256,12 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
 #pragma unroll
     for (int i = 0; i < 4; ++i) sm_o[w][h][16 * dt + 4 * lg + i] = o[dt][i];
   __syncthreads();
+  // publish this split's partial with device-coherent (agent-scope) stores,
+  // wait for them, then count arrivals; the last workgroup of the pair reads
+  // every partial back with device-coherent loads and merges. No
+  // device-scope fence: that would write back the XCD's whole L2.
   const size_t part = (size_t)p * n_splits + split;
+  float *mlf = reinterpret_cast<float *>(ws_ml);
   for (int idx = threadIdx.x; idx < d.G * kHeadDim; idx += kDecThreads) {
     const int hh = idx / kHeadDim, dim = idx % kHeadDim;
     const float M = fmaxf(fmaxf(sm_m[0][hh], sm_m[1][hh]), fmaxf(sm_m[2][hh], sm_m[3][hh]));
@@ -261,43 +274,62 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
         lsum += f * sm_l[ww][hh];
       }
     }
-    ws_o[(part * d.G + hh) * kHeadDim + dim] = acc;
-    if (dim == 0) ws_ml[part * d.G + hh] = make_float2(M, lsum);
-  }
-
-}
-
-// grid (G, P), block 128 (one thread per dim): merges the split partials of
-// one query head and normalises. The split loads of each output element are
-// independent, so they are in flight together.
-__global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(
-    Dims d, const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml, int n_splits,
-    float *__restrict__ out) {
-  const int hh = blockIdx.x, p = blockIdx.y, dim = threadIdx.x;
-  const int b = p / d.Hkv, g = p % d.Hkv;
-  float mv[kMaxSplits], lv[kMaxSplits], ov[kMaxSplits];
-#pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp) {
-    const size_t part = ((size_t)p * n_splits + sp) * d.G + hh;
-    const bool in = sp < n_splits;
-    const float2 ml = in ? ws_ml[part] : make_float2(-INFINITY, 0.0f);
-    mv[sp] = ml.x;
-    lv[sp] = ml.y;
-    ov[sp] = in ? ws_o[part * kHeadDim + dim] : 0.0f;
-  }
-  float M = -INFINITY;
-#pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp) M = fmaxf(M, mv[sp]);
-  float acc = 0.0f, lsum = 0.0f;
-  if (M != -INFINITY) {
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp) {
-      const float f = exp2f(mv[sp] - M);   // 0 for empty splits (m = -inf)
-      acc += f * ov[sp];
-      lsum += f * lv[sp];
+    __hip_atomic_store(&ws_o[(part * d.G + hh) * kHeadDim + dim], acc, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    if (dim == 0) {
+      __hip_atomic_store(&mlf[2 * (part * d.G + hh)], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&mlf[2 * (part * d.G + hh) + 1], lsum, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  out[((size_t)b * d.Hq + g * d.G + hh) * kHeadDim + dim] = lsum > 0.0f ? acc / lsum : 0.0f;
+  __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    sm_last = __hip_atomic_fetch_add(&ws_count[p], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              n_splits - 1;
+  __syncthreads();
+  if (!sm_last) return;
+  float *sm_w = &sm_o[0][0][0];                       // [kMaxSplits][16] m, then weights
+  float *sm_lv = sm_w + kMaxSplits * 16;              // [kMaxSplits][16] l
+  float *sm_lh = sm_lv + kMaxSplits * 16;             // [16] merged l
+  const float *mlp = mlf + (size_t)2 * p * n_splits * d.G;
+  const float *op = ws_o + (size_t)p * n_splits * d.G * kHeadDim;
+  if (threadIdx.x < n_splits * d.G) {
+    sm_w[threadIdx.x] = __hip_atomic_load(&mlp[2 * threadIdx.x], __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    sm_lv[threadIdx.x] = __hip_atomic_load(&mlp[2 * threadIdx.x + 1], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (threadIdx.x < d.G) {
+    const int hh = threadIdx.x;
+    float M = -INFINITY;
+    for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, sm_w[sp * d.G + hh]);
+    float lsum = 0.0f;
+    for (int sp = 0; sp < n_splits; ++sp) {
+      const float f = M == -INFINITY ? 0.0f : exp2f(sm_w[sp * d.G + hh] - M);
+      sm_w[sp * d.G + hh] = f;
+      lsum += f * sm_lv[sp * d.G + hh];
+    }
+    sm_lh[hh] = lsum;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < d.G * kHeadDim; idx += kDecThreads) {
+    const int hh = idx / kHeadDim, dim = idx % kHeadDim;
+    float ov[kMaxSplits];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp)
+      ov[sp] = sp < n_splits ? __hip_atomic_load(&op[((size_t)sp * d.G + hh) * kHeadDim + dim],
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                             : 0.0f;
+    float acc = 0.0f;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp)
+      if (sp < n_splits) acc += sm_w[sp * d.G + hh] * ov[sp];
+    const float lsum = sm_lh[hh];
+    out[((size_t)b * d.Hq + g * d.G + hh) * kHeadDim + dim] = lsum > 0.0f ? acc / lsum : 0.0f;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&ws_count[p], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -317,7 +349,8 @@ DecodeLayout decode_layout(const Dims &d) {
   lay.o_off = 0;
   const size_t parts = (size_t)d.P * lay.n_splits * d.G;
   lay.ml_off = (parts * kHeadDim * sizeof(float) + 255) & ~(size_t)255;
-  lay.bytes = lay.ml_off + ((parts * sizeof(float2) + 255) & ~(size_t)255);
+  lay.count_off = lay.ml_off + ((parts * sizeof(float2) + 255) & ~(size_t)255);
+  lay.bytes = lay.count_off + (((size_t)d.P * sizeof(int32_t) + 255) & ~(size_t)255);
   return lay;
 }
 
@@ -327,11 +360,11 @@ hipError_t launch_decode(const Dims &d, const nosa_state &st, const uint16_t *q,
   char *base = static_cast<char *>(ws);
   float *ws_o = reinterpret_cast<float *>(base + lay.o_off);
   float2 *ws_ml = reinterpret_cast<float2 *>(base + lay.ml_off);
+  int32_t *ws_count = reinterpret_cast<int32_t *>(base + lay.count_off);
   const int slots = d.offload ? d.k + 1 : d.NB_max;
   decode_kernel<<<dim3(lay.n_splits, d.P), kDecThreads, 0, s>>>(
-      d, st.seq_len, q, sel, phys, n_sel, st.kv_dev, slots, st.tok_s, ws_o, ws_ml,
-      lay.blocks_per_split, lay.n_splits, st.status);
-  decode_combine_kernel<<<dim3(d.G, d.P), kHeadDim, 0, s>>>(d, ws_o, ws_ml, lay.n_splits, out);
+      d, st.seq_len, q, sel, phys, n_sel, st.kv_dev, slots, st.tok_s, ws_o, ws_ml, ws_count,
+      lay.blocks_per_split, lay.n_splits, out, st.status);
   return hipGetLastError();
 }
 

@@ -25,10 +25,11 @@ struct FetchLayout {
 };
 FetchLayout fetch_layout(const Dims &d);
 
-// --- decode workspace: split-K partials.
+// --- decode workspace: split-K partials and one arrival counter per pair
+// (zero at rest: the last workgroup of a pair resets it).
 struct DecodeLayout {
   int blocks_per_split, n_splits;
-  size_t o_off, ml_off, bytes;
+  size_t o_off, ml_off, count_off, bytes;
 };
 DecodeLayout decode_layout(const Dims &d);
 
