@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-steps", type=int, default=80)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--breakdown-steps", type=int, default=4)
+    ap.add_argument("--no-offload", action="store_true",
+                    help="skip the host-link leg (offloaded 128K workload)")
+    ap.add_argument("--offload-steps", type=int, default=24)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of MIB MiB first (a known "
                          "byte count for calibrating HBM traffic counters)")
@@ -176,6 +179,84 @@ def cpu_baseline(wl, n_pairs, n_steps):
     }
 
 
+def host_link_leg(n_steps, pool, dev):
+    """Delta fetch over the host link on the offloaded low-locality 128K
+    workload (8 sequences, 32 query / 8 KV heads, k_q = k_e = 32): fetch
+    GB/s on the cold first step and in steady state, against the pinned
+    host-to-device hipMemcpy peak measured in the same process, and a
+    per-32-KiB hipMemcpy baseline for fragmented copies."""
+    import numpy as np
+    import torch
+    from synth import WORKLOADS
+    from trainable_offloadable_block_amd import LayerShape
+    wl = WORKLOADS[5]
+    shape = LayerShape(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_sink_blocks,
+                       wl.window_tokens, wl.k_blocks, wl.k_q_blocks, wl.k_e_blocks,
+                       wl.context + n_steps, offload=True)
+    layer = build_layer(wl, 0, shape, pool)
+    q, kn, vn = step_inputs(wl, 0, n_steps, pool, dev)
+    torch.cuda.synchronize()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # pinned host -> device copy peak (1 GiB, best of 5)
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+    best = 0.0
+    for _ in range(5):
+        a, b = ev(), ev()
+        a.record()
+        dst.copy_(src, non_blocking=True)
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, nb / (a.elapsed_time(b) * 1e-3) / 1e9)
+    # fragmented: 2048 copies of 32 KiB from scattered offsets
+    rng = np.random.default_rng(0)
+    offs = rng.choice(nb // 32768, size=2048, replace=False) * 32768
+    a, b = ev(), ev()
+    a.record()
+    for o in offs:
+        dst[o:o + 32768].copy_(src[o:o + 32768], non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    frag = 2048 * 32768 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    # delta fetch per step
+    recs = []
+    for t in range(n_steps):
+        layer.append(kn[t], vn[t])
+        layer.select(q[t], want_kind=False)
+        a, b = ev(), ev()
+        a.record()
+        layer.fetch()
+        b.record()
+        layer.decode(q[t])
+        torch.cuda.synchronize()
+        misses = int(layer.n_miss.sum().item())
+        recs.append((misses * 32768, a.elapsed_time(b) * 1e3))
+    status = layer.status_bits()
+    assert not status, f"device status bits set: {status}"
+    cold_b, cold_us = recs[0]
+    steady = recs[4:]
+    st_b = float(np.mean([r[0] for r in steady]))
+    st_us = float(np.median([r[1] for r in steady]))
+    gbps = lambda b_, us: b_ / (us * 1e-6) / 1e9  # noqa: E731
+    return {
+        "workload": wl.name, "pairs": wl.batch * wl.n_kv_heads,
+        "h2d_memcpy_peak_GBps": round(best, 2),
+        "fragmented_32KiB_memcpy_GBps": round(frag, 2),
+        "fetch_cold": {"bytes": cold_b, "us": round(cold_us, 1),
+                       "GBps": round(gbps(cold_b, cold_us), 2),
+                       "frac_of_peak": round(gbps(cold_b, cold_us) / best, 4)},
+        "fetch_steady": {"bytes_per_step": int(st_b), "us_median": round(st_us, 1),
+                         "GBps": round(gbps(st_b, st_us), 2),
+                         "frac_of_peak": round(gbps(st_b, st_us) / best, 4),
+                         "steps": len(steady)},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -299,6 +380,13 @@ def main():
         },
         "breakdown_us": {n: round(float(np.median(v)), 2) for n, v in bd.items()},
     }
+    if not args.no_offload:
+        log("host-link leg (offloaded 128K workload)")
+        layers.clear()
+        inputs.clear()
+        torch.cuda.empty_cache()
+        with cf.ThreadPoolExecutor(workers) as pool:
+            res["host_link"] = host_link_leg(args.offload_steps, pool, dev)
     if not args.no_cpu:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_pairs, args.cpu_steps)

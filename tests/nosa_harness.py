@@ -22,7 +22,9 @@ oracle's state.
 
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -78,10 +80,13 @@ class Lockstep:
         self.n_w = wl.window_tokens // 64
         self.k_e_dyn = wl.k_e_blocks - wl.n_sink_blocks - self.n_w
         self.oracles = {}
-        self.ctx = {}
+        with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as pool:
+            ctx = list(pool.map(lambda p: context_kv(wl, layer, *divmod(p, Hkv)),
+                                range(self.P)))
         for p in range(self.P):
             b, g = divmod(p, Hkv)
-            K, V = context_kv(wl, layer, b, g)
+            K, V = ctx[p]
+            ctx[p] = None
             Lb = int(self.lengths[b])
             K, V = K[:Lb], V[:Lb]
             self.gpu.load_pair_context(p, K, V)

@@ -168,3 +168,20 @@ def test_resident_fetch_is_identity():
     torch.cuda.synchronize()
     assert torch.equal(g.phys, g.sel)
     assert int(g.n_miss.abs().sum()) == 0
+
+
+def test_offload_128k_drift_sampled():
+    """Offloaded 128K low-locality workload (8 sequences, 32/8 heads,
+    k_q = k_e = 32) at full size: 4 sampled pairs against the oracle, fetched
+    blocks equal the oracle's misses, cache bytes equal the host store."""
+    _run(WORKLOADS[5], check_pairs=[0, 21, 42, 63], steps=20, cache_every=5)
+
+
+def test_offload_8b_64k_sampled():
+    """Offloaded 8B-shaped 64K layer (32 sequences, 32/8 heads) at full size."""
+    _run(WORKLOADS[4], check_pairs=[0, 100, 255], steps=8, cache_every=4)
+
+
+def test_offload_1b_32k_layer_sampled():
+    """One layer (layer 13) of the offloaded 28-layer 32K stack (64 sequences)."""
+    _run(WORKLOADS[3], layer=13, check_pairs=[0, 77, 127], steps=8, cache_every=4)
