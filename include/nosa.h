@@ -91,7 +91,10 @@ typedef struct nosa_config {
  * KV block layout (device pool, device cache and host store alike): one
  * block of one pair is 32 KiB = K then V, bf16:
  *     K part  [64 tokens][128 dims]   (row = token)
- *     V part  [128 dims][64 tokens]   (row = dim; V transposed)
+ *     V part  1 KiB tiles [2 halves][8 dim tiles][4 token groups][16 dims]
+ *             [8 tokens]: token t, dim c at element
+ *             ((((t/32)*8 + c/16)*4 + (t%32)/8)*16 + c%16)*8 + t%8
+ *             (a tile is 16 dims x 32 tokens, one MFMA operand per wave)
  * A block is the pages' 16 KiB-per-tensor transfer unit (aiwiki "NOSA",
  * Main-experiment configuration), with K and V adjacent. Inside a
  * sequence's newest block the positions at and past seq_len hold zeros:

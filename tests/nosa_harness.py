@@ -33,7 +33,7 @@ import torch
 import oracle.nosa_oracle as O
 from synth import (bf16_bits_to_f64, context_kv, eviction_weights, new_tokens,
                    queries)
-from trainable_offloadable_block_amd import LayerShape, NosaLayer
+from trainable_offloadable_block_amd import LayerShape, NosaLayer, v_from_tiles
 from trainable_offloadable_block_amd import _lib as L
 
 TIE_REL = 1e-5
@@ -294,10 +294,11 @@ class Lockstep:
                 n = min(64, Lb - 64 * blk)        # tokens that exist
                 a = cache[p, phys[p, i]].cpu()
                 h = host[p, blk]
-                # K rows, then V transposed: [dim][token]
+                # K rows, then V in tile order
+                av = v_from_tiles(a[1].reshape(-1).numpy())
+                hv = v_from_tiles(h[1].reshape(-1).numpy())
                 same = (torch.equal(a[0, :n], h[0, :n]) and
-                        torch.equal(a[1].reshape(128, 64)[:, :n],
-                                    h[1].reshape(128, 64)[:, :n]))
+                        np.array_equal(av[:n], hv[:n]))
                 assert same, f"pair {p} block {blk}: cache bytes differ"
 
     def run(self, steps=None, check_scores=True, cache_every=0):

@@ -135,3 +135,18 @@ def test_strerror():
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.nosa_strerror(code)
     assert b"unknown" in lib.nosa_strerror(42)
+
+
+def test_v_tile_order_matches_the_header_formula():
+    """The block's V part: token t, dim c at element
+    ((((t/32)*8 + c/16)*4 + (t%32)/8)*16 + c%16)*8 + t%8 (include/nosa.h)."""
+    import numpy as np
+    v = (np.arange(64)[:, None] * 1000 + np.arange(128)[None, :]).astype(np.int64)
+    flat = nosa.v_to_tiles(v)
+    for t in range(64):
+        for c in range(128):
+            i = ((((t // 32) * 8 + c // 16) * 4 + (t % 32) // 8) * 16 + c % 16) * 8 + t % 8
+            assert flat[i] == t * 1000 + c
+    assert np.array_equal(nosa.v_from_tiles(flat), v)
+    many = np.random.default_rng(3).integers(0, 1 << 16, (5, 64, 128))
+    assert np.array_equal(nosa.v_from_tiles(nosa.v_to_tiles(many)), many)

@@ -14,6 +14,7 @@ import torch
 
 from synth import WORKLOADS, small_workload
 from nosa_harness import Lockstep, summary
+from trainable_offloadable_block_amd import v_to_tiles
 
 pytestmark = pytest.mark.gpu
 
@@ -145,7 +146,9 @@ def test_nan_bytes_past_length_are_ignored():
             Lb = int(ls.lengths[p // wl.n_kv_heads])
             blk, r = divmod(Lb, 64)
             pool[p, blk, 0, r:] = nan
-            pool[p, blk, 1].view(128, 64)[:, r:] = nan
+            past = np.broadcast_to((np.arange(64) >= r)[:, None], (64, 128))
+            mask = torch.from_numpy(v_to_tiles(past).copy()).to(pool.device)
+            pool[p, blk, 1].view(-1)[mask] = nan
             pool[p, blk + 1:] = nan
         torch.cuda.synchronize()
 

@@ -72,16 +72,16 @@ __global__ __launch_bounds__(128) void append_kernel(
     const uint16_t vb = v_new[p * kHeadDim + t];
     const int blk = pos / kBlock, r = pos % kBlock;
 
-    // 1. store K, V (K row-major, V transposed inside the block)
+    // 1. store K, V (K row-major, V in the block's tile order)
     if (!d.offload) {
       uint16_t *base = st.kv_dev + ((size_t)p * d.NB_max + blk) * kBlockElems;
       if (r == 0) clear_block(base);
       base[r * kHeadDim + t] = kb;
-      base[kBlock * kHeadDim + t * kBlock + r] = vb;
+      base[kBlock * kHeadDim + v_index(r, t)] = vb;
     } else {
       uint16_t *hb = st.kv_host + ((size_t)p * d.NB_max + blk) * kBlockElems;
       hb[r * kHeadDim + t] = kb;
-      hb[kBlock * kHeadDim + t * kBlock + r] = vb;
+      hb[kBlock * kHeadDim + v_index(r, t)] = vb;
       int32_t *sob = st.slot_of_block + (size_t)p * d.NB_max;
       int32_t *bos = st.block_of_slot + (size_t)p * (d.k + 1);
       if (t == 0) slot_sh = sob[blk];
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(128) void append_kernel(
         uint16_t *cb = st.kv_dev + ((size_t)p * (d.k + 1) + slot) * kBlockElems;
         if (r == 0) clear_block(cb);
         cb[r * kHeadDim + t] = kb;
-        cb[kBlock * kHeadDim + t * kBlock + r] = vb;
+        cb[kBlock * kHeadDim + v_index(r, t)] = vb;
       }
     }
 
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(128) void prefill_scores_kernel(Dims d, nosa_state 
   const int n = min(kBlock, L - blk * kBlock);
   float *tok_s = st.tok_s + (size_t)p * d.tok_stride;
   for (int r = 0; r < n; ++r) {
-    v_sh[t] = bf16_to_f32(vt[t * kBlock + r]);
+    v_sh[t] = bf16_to_f32(vt[v_index(r, t)]);
     __syncthreads();
     const float s = evict_score_128(v_sh, w1_sh, st.w2 + (size_t)g * kHeadDim, red2);
     if (t == 0) tok_s[blk * kBlock + r] = s;
@@ -249,13 +249,14 @@ __global__ __launch_bounds__(128) void prefill_finish_kernel(Dims d, nosa_state 
     if (idx <= d.k) st.block_of_slot[(size_t)p * (d.k + 1) + idx] = -1;
   }
   if (L % kBlock) {
-    // tail of the last, partial block: K rows and V^T columns past L read 0
+    // tail of the last, partial block: K and V of the positions past L read 0
     uint16_t *base = (d.offload ? st.kv_host : st.kv_dev) +
                      ((size_t)p * d.NB_max + L / kBlock) * kBlockElems;
     const int r0 = L % kBlock, n = (kBlock - r0) * kHeadDim;
     for (int i = idx; i < n; i += gridDim.x * blockDim.x) {
-      base[r0 * kHeadDim + i] = 0;                                   // K
-      base[kBlock * kHeadDim + (i / (kBlock - r0)) * kBlock + r0 + i % (kBlock - r0)] = 0;  // V^T
+      const int tok = r0 + i / kHeadDim, dim = i % kHeadDim;
+      base[tok * kHeadDim + dim] = 0;                                // K
+      base[kBlock * kHeadDim + v_index(tok, dim)] = 0;               // V
     }
   }
   if (blockIdx.x == 0) {

@@ -30,6 +30,14 @@ __host__ __device__ inline int blocks_for(int L) {
   return (L + kBlock - 1) / kBlock;
 }
 
+// Element offset of (token, dim) inside a block's V part: 1 KiB tiles
+// [2 halves][8 dim tiles][4 token groups][16 dims][8 tokens], so that one
+// 16-byte load per lane of a wave fetches one whole tile, already in the
+// shape of a 16x16x32 MFMA operand (16 dims x 32 tokens of one half).
+__host__ __device__ inline int v_index(int tok, int dim) {
+  return ((((tok >> 5) * 8 + (dim >> 4)) * 4 + ((tok >> 3) & 3)) * 16 + (dim & 15)) * 8 + (tok & 7);
+}
+
 __device__ inline float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }

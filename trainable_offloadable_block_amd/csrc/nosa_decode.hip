@@ -54,7 +54,7 @@ __device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
 // One 32-token half of a selected block, as this lane's MFMA operands.
 struct Half {
   uint4 k[2][4];   // K rows of the two QK tiles, 4 k-steps each
-  uint4 v[8];      // V^T rows of the 8 dim tiles: 8 keys of one dim
+  uint4 v[8];      // the half's 8 V tiles: 8 keys of one dim per lane
   float s;         // eviction score of key (lane % 32) of the half
   int key_base;    // token index of the half's first key (wave-uniform)
   int ok;          // 0: past the wave's list or an invalid entry (uniform)
@@ -89,7 +89,7 @@ __device__ inline void load_half(Half &hb, int j, const DecodeArgs &a, const Dim
     slot = 0;
   }
   const int kbase = slot * (kBlockElems * 2) + half * (32 * kHeadDim * 2);
-  const int vbase = slot * (kBlockElems * 2) + kBlock * kHeadDim * 2 + half * 64;
+  const int vbase = slot * (kBlockElems * 2) + kBlock * kHeadDim * 2 + half * 8192;
   hb.key_base = blk * kBlock + 32 * half;
 #if NOSA_DECODE_GLOBAL_LOADS
   const char *kvb = reinterpret_cast<const char *>(a.kv_ptr);
@@ -100,7 +100,7 @@ __device__ inline void load_half(Half &hb, int j, const DecodeArgs &a, const Dim
       hb.k[t][s] = *reinterpret_cast<const uint4 *>(kvb + kbase + a.koff[t] + 64 * s);
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
-    hb.v[dt] = *reinterpret_cast<const uint4 *>(kvb + vbase + a.voff + 16 * kBlock * 2 * dt);
+    hb.v[dt] = *reinterpret_cast<const uint4 *>(kvb + vbase + a.voff + 1024 * dt);
   hb.s = a.ts_ptr[hb.key_base + (threadIdx.x & 31)];
 #else
 #pragma unroll
@@ -108,7 +108,7 @@ __device__ inline void load_half(Half &hb, int j, const DecodeArgs &a, const Dim
 #pragma unroll
     for (int s = 0; s < 4; ++s) hb.k[t][s] = bload16(a.kv, a.koff[t] + 64 * s, kbase);
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) hb.v[dt] = bload16(a.kv, a.voff + 16 * kBlock * 2 * dt, vbase);
+  for (int dt = 0; dt < 8; ++dt) hb.v[dt] = bload16(a.kv, a.voff + 1024 * dt, vbase);
   hb.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(a.ts, a.soff,
                                                                         hb.key_base * 4, 0));
 #endif
@@ -165,6 +165,78 @@ __device__ inline void process_half(Half &hb, const bf16x8 (&qop)[4], float qsca
   }
 }
 
+__device__ inline float load_agent(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Final merge of a pair's split partials, by the pair's last workgroup.
+// Thread t owns outputs t + 256 i (i < NI; NI * 256 >= G * 128). Every
+// partial is read with device-coherent loads, SB = 16 / NI splits per batch,
+// the first batch issued before the (m, l) round trip so the two overlap.
+template <int NI>
+__device__ void merge_splits(const Dims &d, int p, int b, int g, int n_splits,
+                             const float *mlf, const float *ws_o, float *sm, float *out) {
+  constexpr int SB = 16 / NI;
+  const int t = threadIdx.x;
+  const int n_out = d.G * kHeadDim;
+  const float *mlp = mlf + (size_t)2 * p * n_splits * d.G;
+  const float *op = ws_o + (size_t)p * n_splits * n_out;
+  float *sm_w = sm;                                   // [kMaxSplits][16]: m, then weights
+  float *sm_lv = sm_w + kMaxSplits * 16;              // [kMaxSplits][16]: l
+  float *sm_lh = sm_lv + kMaxSplits * 16;             // [16]: merged l
+  float v[SB][NI];
+  auto issue = [&](int sp0) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int idx = t + kDecThreads * i;
+        v[u][i] = (sp0 + u < n_splits && idx < n_out)
+                      ? load_agent(&op[(size_t)(sp0 + u) * n_out + idx]) : 0.0f;
+      }
+  };
+  issue(0);
+  if (t < n_splits * d.G) {
+    sm_w[t] = load_agent(&mlp[2 * t]);
+    sm_lv[t] = load_agent(&mlp[2 * t + 1]);
+  }
+  __syncthreads();
+  if (t < d.G) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, sm_w[sp * d.G + t]);
+    float lsum = 0.0f;
+    for (int sp = 0; sp < n_splits; ++sp) {
+      const float f = M == -INFINITY ? 0.0f : exp2f(sm_w[sp * d.G + t] - M);
+      sm_w[sp * d.G + t] = f;
+      lsum += f * sm_lv[sp * d.G + t];
+    }
+    sm_lh[t] = lsum;
+  }
+  __syncthreads();
+  float acc[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) acc[i] = 0.0f;
+  for (int sp0 = 0; sp0 < n_splits; sp0 += SB) {
+    if (sp0 > 0) issue(sp0);
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int idx = t + kDecThreads * i;
+        if (sp0 + u < n_splits && idx < n_out) acc[i] += sm_w[(sp0 + u) * d.G + idx / kHeadDim] * v[u][i];
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int idx = t + kDecThreads * i;
+    if (idx < n_out) {
+      const int hh = idx / kHeadDim, dim = idx % kHeadDim;
+      const float lsum = sm_lh[hh];
+      out[((size_t)b * d.Hq + g * d.G + hh) * kHeadDim + dim] = lsum > 0.0f ? acc[i] / lsum : 0.0f;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_kernel(
     Dims d, const int32_t *__restrict__ seq_len, const uint16_t *__restrict__ q,
     const int32_t *__restrict__ sel, const int32_t *__restrict__ phys,
@@ -193,7 +265,7 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   a.ts_ptr = tok_s + (size_t)p * d.tok_stride;
   a.koff[0] = tile_row(h, 0) * kHeadDim * 2 + 16 * lg;
   a.koff[1] = tile_row(h, 1) * kHeadDim * 2 + 16 * lg;
-  a.voff = h * kBlock * 2 + 16 * lg;
+  a.voff = 16 * l;   // V tile: lane l holds dim l % 16, tokens 8 (l / 16) .. + 7
   a.soff = 4 * (l & 31);
   a.p = p;
   a.slots = slots_per_pair;
@@ -289,46 +361,10 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
               n_splits - 1;
   __syncthreads();
   if (!sm_last) return;
-  float *sm_w = &sm_o[0][0][0];                       // [kMaxSplits][16] m, then weights
-  float *sm_lv = sm_w + kMaxSplits * 16;              // [kMaxSplits][16] l
-  float *sm_lh = sm_lv + kMaxSplits * 16;             // [16] merged l
-  const float *mlp = mlf + (size_t)2 * p * n_splits * d.G;
-  const float *op = ws_o + (size_t)p * n_splits * d.G * kHeadDim;
-  if (threadIdx.x < n_splits * d.G) {
-    sm_w[threadIdx.x] = __hip_atomic_load(&mlp[2 * threadIdx.x], __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-    sm_lv[threadIdx.x] = __hip_atomic_load(&mlp[2 * threadIdx.x + 1], __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (threadIdx.x < d.G) {
-    const int hh = threadIdx.x;
-    float M = -INFINITY;
-    for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, sm_w[sp * d.G + hh]);
-    float lsum = 0.0f;
-    for (int sp = 0; sp < n_splits; ++sp) {
-      const float f = M == -INFINITY ? 0.0f : exp2f(sm_w[sp * d.G + hh] - M);
-      sm_w[sp * d.G + hh] = f;
-      lsum += f * sm_lv[sp * d.G + hh];
-    }
-    sm_lh[hh] = lsum;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < d.G * kHeadDim; idx += kDecThreads) {
-    const int hh = idx / kHeadDim, dim = idx % kHeadDim;
-    float ov[kMaxSplits];
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp)
-      ov[sp] = sp < n_splits ? __hip_atomic_load(&op[((size_t)sp * d.G + hh) * kHeadDim + dim],
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                             : 0.0f;
-    float acc = 0.0f;
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp)
-      if (sp < n_splits) acc += sm_w[sp * d.G + hh] * ov[sp];
-    const float lsum = sm_lh[hh];
-    out[((size_t)b * d.Hq + g * d.G + hh) * kHeadDim + dim] = lsum > 0.0f ? acc / lsum : 0.0f;
-  }
+  if (d.G <= 8)
+    merge_splits<4>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
+  else
+    merge_splits<8>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
   if (threadIdx.x == 0) __hip_atomic_store(&ws_count[p], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -65,16 +65,35 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def v_to_tiles(v: np.ndarray) -> np.ndarray:
+    """V of whole blocks, [..., 64 tokens, 128 dims] -> the blocks' V parts
+    in tile order [..., 2 halves, 8 dim tiles, 4 token groups, 16 dims,
+    8 tokens], flattened per block."""
+    lead = v.shape[:-2]
+    t = v.reshape(*lead, 2, 4, 8, 8, 16)          # half, group, tok, tile, dim
+    n = len(lead)
+    t = t.transpose(*range(n), n, n + 3, n + 1, n + 4, n + 2)
+    return t.reshape(*lead, BLOCK * HEAD_DIM)
+
+
+def v_from_tiles(flat: np.ndarray) -> np.ndarray:
+    """Inverse of v_to_tiles: [..., 64*128] tile order -> [..., 64, 128]."""
+    lead = flat.shape[:-1]
+    t = flat.reshape(*lead, 2, 8, 4, 16, 8)       # half, tile, group, dim, tok
+    n = len(lead)
+    t = t.transpose(*range(n), n, n + 2, n + 4, n + 1, n + 3)
+    return t.reshape(*lead, BLOCK, HEAD_DIM)
+
+
 def to_block_layout(K: np.ndarray, V: np.ndarray, nb: int) -> np.ndarray:
     """Token-major K, V ([L][128] uint16 bf16 bits) -> nb blocks of 32 KiB:
-    K rows [64][128] then V transposed [128][64], zero past L."""
+    K rows [64][128], then V in tile order (v_to_tiles); zero past L."""
     Lt = K.shape[0]
     out = np.zeros((nb, 2, BLOCK * HEAD_DIM), dtype=np.uint16)
     full = min(nb, Lt // BLOCK)
     if full:
         out[:full, 0] = K[:full * BLOCK].reshape(full, BLOCK * HEAD_DIM)
-        out[:full, 1] = V[:full * BLOCK].reshape(full, BLOCK, HEAD_DIM).transpose(
-            0, 2, 1).reshape(full, BLOCK * HEAD_DIM)
+        out[:full, 1] = v_to_tiles(V[:full * BLOCK].reshape(full, BLOCK, HEAD_DIM))
     rest = Lt - full * BLOCK
     if rest and full < nb:
         kb = np.zeros((BLOCK, HEAD_DIM), dtype=np.uint16)
@@ -82,7 +101,7 @@ def to_block_layout(K: np.ndarray, V: np.ndarray, nb: int) -> np.ndarray:
         kb[:rest] = K[full * BLOCK:]
         vb[:rest] = V[full * BLOCK:]
         out[full, 0] = kb.reshape(-1)
-        out[full, 1] = vb.T.reshape(-1)
+        out[full, 1] = v_to_tiles(vb)
     return out
 
 
