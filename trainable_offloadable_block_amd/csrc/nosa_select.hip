@@ -7,10 +7,10 @@
 // pool_topk_kernel (one workgroup per pair): combines the split statistics
 //   into the per-head softmax, sums the group's heads, max-pools the chunks
 //   overlapping each block, then stage 1 (top k_q by the query-aware score)
-//   and stage 2 (top k_e' eligible by the agnostic score), each a wave-level
-//   bitonic top-k over 64-candidate chunks merged across waves, writes the
-//   ascending selection and clears the eligibility of every candidate left
-//   out (never re-selected by the agnostic stage).
+//   and stage 2 (top k_e' eligible by the agnostic score), each an exact
+//   workgroup top-k by histogram range refinement, writes the ascending
+//   selection and clears the eligibility of every candidate left out (never
+//   re-selected by the agnostic stage).
 #include "nosa_internal.h"
 
 namespace nosa {
@@ -28,6 +28,10 @@ constexpr int kTopkThreads = 256;
 // so that, over two tiles, lane group j holds 8 consecutive rows (chunks):
 // tile t, A-row r  <->  row 8*(r/4) + 4*t + (r%4) of the 32-row group.
 __device__ inline int tile_row(int r, int t) { return 8 * (r >> 2) + 4 * t + (r & 3); }
+
+// Heads per chunk in the chunk-weight layout: the group padded to 4, 8 or 16
+// so that one 16-byte load never straddles two chunks.
+__host__ __device__ inline int padded_group(int G) { return G <= 4 ? 4 : (G <= 8 ? 8 : 16); }
 
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     Dims d, const int32_t *__restrict__ seq_len, const uint16_t *__restrict__ ckey,
@@ -97,16 +101,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   z += __shfl_xor(z, 16, 64);
   z += __shfl_xor(z, 32, 64);
   if (lg == 0) red_z[w][h] = z;
-  if (h < d.G) {
-    float *dst = ws_e + ((size_t)p * d.G + h) * c_pad + cg + 8 * lg;
-    if (cg + 8 * lg + 8 <= C) {
-      reinterpret_cast<float4 *>(dst)[0] = make_float4(ev[0], ev[1], ev[2], ev[3]);
-      reinterpret_cast<float4 *>(dst)[1] = make_float4(ev[4], ev[5], ev[6], ev[7]);
-    } else {
+  const int Gp = padded_group(d.G);
+  if (h < Gp) {                                    // chunk-major [c][Gp], pad = 0
+    float *dst = ws_e + ((size_t)p * c_pad + cg + 8 * lg) * Gp + h;
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
-        if (cg + 8 * lg + m < C) dst[m] = ev[m];
-    }
+    for (int m = 0; m < 8; ++m)
+      if (cg + 8 * lg + m < C) dst[m * Gp] = h < d.G ? ev[m] : 0.0f;
   }
   __syncthreads();
   if (threadIdx.x < d.G) {
@@ -117,170 +117,265 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   }
 }
 
-// Exclusive prefix sum over the 256 threads of a workgroup.
-__device__ int block_excl_scan(int v, int *sh, int *total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += n;
-  }
-  if (lane == 63) sh[w] = incl;
-  __syncthreads();
-  int base = 0, tot = 0;
-  for (int j = 0; j < kTopkThreads / 64; ++j) {
-    if (j < w) base += sh[j];
-    tot += sh[j];
-  }
-  __syncthreads();
-  if (total) *total = tot;
-  return base + incl - v;
-}
-
-// ---- wave-level top-k on 64-bit composite keys --------------------------
+// ---- workgroup top-k on 64-bit composite keys ----------------------------
 // A key is (order_key(score) << 32) | ~block: larger score first, then the
-// lower block id, all keys distinct; 0 marks "not a candidate".
-
-// Value of lane (lane ^ MASK): DPP for masks 1 and 2, ds_swizzle (xor within
-// 32 lanes) for 4, 8, 16, ds_bpermute for 32.
-template <int MASK>
-__device__ inline uint32_t xor_lane(uint32_t v) {
-  const int x = static_cast<int>(v);
-  if constexpr (MASK == 1) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
-  } else if constexpr (MASK == 2) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
-  } else if constexpr (MASK < 32) {
-    return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(x, 0x1F | (MASK << 10)));
-  } else {
-    return static_cast<uint32_t>(__shfl_xor(x, MASK, 64));
-  }
-}
-
-template <int MASK>
-__device__ inline uint64_t xor_lane_u64(uint64_t v) {
-  const uint32_t lo = xor_lane<MASK>(static_cast<uint32_t>(v));
-  const uint32_t hi = xor_lane<MASK>(static_cast<uint32_t>(v >> 32));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-__device__ inline uint64_t lane_u64(uint64_t v, int src) {
-  const int lo = __shfl(static_cast<int>(v & 0xFFFFFFFFu), src, 64);
-  const int hi = __shfl(static_cast<int>(v >> 32), src, 64);
-  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
-}
-
-// One compare-exchange step of a bitonic network with partner lane ^ J;
-// lanes whose (lane & J) == 0 keep the max when `keep_max_low`.
-template <int J>
-__device__ inline uint64_t cas_step(uint64_t v, bool keep_max_low) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t o = xor_lane_u64<J>(v);
-  const bool lower = (lane & J) == 0;
-  return (lower == keep_max_low) ? (v > o ? v : o) : (v < o ? v : o);
-}
-
-template <int K>
-__device__ inline uint64_t sort_stage(uint64_t v) {
-  const bool desc = ((threadIdx.x & 63) & K) == 0;   // direction of this K-block
-  if constexpr (K >= 64) v = cas_step<32>(v, desc);
-  if constexpr (K >= 32) v = cas_step<16>(v, desc);
-  if constexpr (K >= 16) v = cas_step<8>(v, desc);
-  if constexpr (K >= 8) v = cas_step<4>(v, desc);
-  if constexpr (K >= 4) v = cas_step<2>(v, desc);
-  v = cas_step<1>(v, desc);
-  return v;
-}
-
-// Bitonic sort of one key per lane; afterwards lane i holds the i-th largest.
-__device__ inline uint64_t wave_sort_desc(uint64_t v) {
-  v = sort_stage<2>(v);
-  v = sort_stage<4>(v);
-  v = sort_stage<8>(v);
-  v = sort_stage<16>(v);
-  v = sort_stage<32>(v);
-  return sort_stage<64>(v);
-}
-
-// Top 64 of two descending-sorted wave lists, sorted descending: the
-// element-wise max of a and reversed b is bitonic and holds the 64 largest.
-__device__ inline uint64_t wave_merge_desc(uint64_t a, uint64_t b) {
-  const uint64_t br = lane_u64(b, 63 - (threadIdx.x & 63));
-  uint64_t v = a > br ? a : br;
-  v = cas_step<32>(v, true);
-  v = cas_step<16>(v, true);
-  v = cas_step<8>(v, true);
-  v = cas_step<4>(v, true);
-  v = cas_step<2>(v, true);
-  return cas_step<1>(v, true);
-}
+// lower block id; keys are distinct and 0 marks "not a candidate".
 
 __device__ inline uint64_t compose_key(float score, int blk) {
   return (static_cast<uint64_t>(order_key(score)) << 32) |
          static_cast<uint32_t>(0xFFFFFFFFu - static_cast<uint32_t>(blk));
 }
 
-__device__ inline int key_block(uint64_t key) {
-  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key & 0xFFFFFFFFu));
+// DPP lane exchange inside a row of 16 lanes: xor 1, xor 2 (quad
+// permutations), then the mirrors of 8 and 16 lanes; for min / max / sum
+// any pairing that joins the two halves serves.
+template <int CTRL>
+__device__ inline uint32_t dpp32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ inline uint64_t dpp64(uint64_t v) {
+  return (static_cast<uint64_t>(dpp32<CTRL>(static_cast<uint32_t>(v >> 32))) << 32) |
+         dpp32<CTRL>(static_cast<uint32_t>(v));
+}
+template <int CTRL>
+__device__ inline void row_step(uint64_t &mn, uint64_t &mx, uint32_t &c) {
+  const uint64_t a = dpp64<CTRL>(mn), b = dpp64<CTRL>(mx);
+  mn = a < mn ? a : mn;
+  mx = b > mx ? b : mx;
+  c += dpp32<CTRL>(c);
 }
 
-// Combines the four waves' sorted top-64 lists and marks the best k blocks
-// (kind[b] = val). Called by all threads of the workgroup.
-__device__ void finish_topk(uint64_t best, int k, uint8_t *kind, uint8_t val,
-                            uint64_t (*top_sh)[64]) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  top_sh[w][lane] = best;
-  __syncthreads();
-  if (w == 0) {
-    const uint64_t b1 = top_sh[1][lane], b2 = top_sh[2][lane], b3 = top_sh[3][lane];
-    best = wave_merge_desc(wave_merge_desc(best, b1), wave_merge_desc(b2, b3));
-    if (lane < k && best != 0) kind[key_block(best)] = val;
+__device__ inline uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(v), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), l);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Inclusive prefix sum over the 64 lanes: DPP row shifts inside each row of
+// 16 lanes, then the row totals (lanes 15, 31, 47) carried forward.
+__device__ inline uint32_t wave_incl_scan(uint32_t x) {
+  x += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x111, 0xF, 0xF, true));
+  x += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x112, 0xF, 0xF, true));
+  x += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x114, 0xF, 0xF, true));
+  x += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x118, 0xF, 0xF, true));
+  const uint32_t r0 = __builtin_amdgcn_readlane(static_cast<int>(x), 15);
+  const uint32_t r1 = __builtin_amdgcn_readlane(static_cast<int>(x), 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(static_cast<int>(x), 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
+}
+
+constexpr int kTopkBits = 8, kTopkBins = 1 << kTopkBits;   // bins per refinement round
+
+struct __align__(16) TopkLds {
+  uint32_t hist[2][kTopkBins];
+  uint64_t mn[2][kTopkThreads / 64], mx[2][kTopkThreads / 64];
+  uint32_t cnt[2][kTopkThreads / 64];
+};
+
+// Marks kind[bb0 + t + 256 r] = val for the k largest nonzero keys of the
+// workgroup (thread t holds the keys of candidates t + 256 r, r < R).
+// Exact selection by range refinement: each round histograms the active keys
+// into 256 bins over [min, max] (the top 8 bits of their spread), keeps every
+// key above the bin holding the k-th largest, drops those below it, and goes
+// on inside that bin; a bin whose keys are all wanted ends it. The spread
+// shrinks by 8 bits per round, so 64-bit keys need at most 8 rounds.
+// hist[0] must be zero on entry; both are zero again on return. Called by
+// all threads; the caller syncs before reading kind.
+template <int R>
+__device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0, uint8_t *kind, uint8_t val,
+                        TopkLds &sh) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  bool act[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) act[r] = key[r] != 0;
+  int need = k;
+  for (int round = 0; need > 0 && round < 9; ++round) {    // uniform; <= 8 refinements
+    const int par = round & 1;
+    uint64_t mn = ~0ull, mx = 0;
+    uint32_t c = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (act[r]) {
+        mn = key[r] < mn ? key[r] : mn;
+        mx = key[r] > mx ? key[r] : mx;
+        ++c;
+      }
+    row_step<0xB1>(mn, mx, c);            // quad_perm [1,0,3,2]
+    row_step<0x4E>(mn, mx, c);            // quad_perm [2,3,0,1]
+    row_step<0x141>(mn, mx, c);           // row_half_mirror
+    row_step<0x140>(mn, mx, c);           // row_mirror
+    {
+      uint64_t wm = readlane_u64(mn, 0), wx = readlane_u64(mx, 0);
+      uint32_t wc = __builtin_amdgcn_readlane(static_cast<int>(c), 0);
+#pragma unroll
+      for (int row = 1; row < 4; ++row) {
+        const uint64_t a = readlane_u64(mn, 16 * row), b = readlane_u64(mx, 16 * row);
+        wm = a < wm ? a : wm;
+        wx = b > wx ? b : wx;
+        wc += __builtin_amdgcn_readlane(static_cast<int>(c), 16 * row);
+      }
+      if (lane == 0) {
+        sh.mn[par][w] = wm;
+        sh.mx[par][w] = wx;
+        sh.cnt[par][w] = wc;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kTopkBins / kTopkThreads; ++i)         // next round's bins
+      sh.hist[par ^ 1][t + kTopkThreads * i] = 0;
+    mn = ~0ull;
+    mx = 0;
+    c = 0;
+#pragma unroll
+    for (int i = 0; i < kTopkThreads / 64; ++i) {
+      const uint64_t a = sh.mn[par][i], b = sh.mx[par][i];
+      mn = a < mn ? a : mn;
+      mx = b > mx ? b : mx;
+      c += sh.cnt[par][i];
+    }
+    if (c <= static_cast<uint32_t>(need)) {                  // uniform: take them all
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (act[r]) kind[bb0 + t + kTopkThreads * r] = val;
+      break;
+    }
+    const int span = mx > mn ? 64 - __builtin_clzll(mx - mn) : 0;   // c >= 2 distinct keys
+    const int shift = span > kTopkBits ? span - kTopkBits : 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (act[r]) atomicAdd(&sh.hist[par][(key[r] - mn) >> shift], 1u);
+    __syncthreads();
+    // bin holding the need-th largest: lane l sums the BPL bins below
+    // kTopkBins - BPL l, a prefix over lanes counts from the top
+    constexpr int BPL = kTopkBins / 64;
+    uint32_t hb[BPL], s4 = 0;
+    {
+      const uint4 *hv = reinterpret_cast<const uint4 *>(&sh.hist[par][kTopkBins - BPL * (lane + 1)]);
+#pragma unroll
+      for (int i = 0; i < BPL / 4; ++i) {
+        const uint4 v = hv[BPL / 4 - 1 - i];     // descending bin order
+        hb[4 * i] = v.w;
+        hb[4 * i + 1] = v.z;
+        hb[4 * i + 2] = v.y;
+        hb[4 * i + 3] = v.x;
+      }
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) s4 += hb[i];
+    }
+    const uint32_t incl = wave_incl_scan(s4);
+    const uint64_t hit = __ballot(incl >= static_cast<uint32_t>(need));
+    const int ls = __builtin_ctzll(hit);                     // exists: total c > need
+    int bstar = 0;
+    uint32_t above = incl - s4, inbin = 0;
+    {
+      bool found = false;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        if (!found && above + hb[i] >= static_cast<uint32_t>(need)) {
+          bstar = kTopkBins - 1 - BPL * lane - i;
+          inbin = hb[i];
+          found = true;
+        } else if (!found) {
+          above += hb[i];
+        }
+      }
+    }
+    bstar = __builtin_amdgcn_readlane(bstar, ls);
+    above = __builtin_amdgcn_readlane(static_cast<int>(above), ls);
+    inbin = __builtin_amdgcn_readlane(static_cast<int>(inbin), ls);
+    const int rest = need - static_cast<int>(above);
+    const bool all_in = inbin == static_cast<uint32_t>(rest);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (act[r]) {
+        const int bin = static_cast<int>((key[r] - mn) >> shift);
+        if (bin > bstar || (bin == bstar && all_in)) {
+          kind[bb0 + t + kTopkThreads * r] = val;
+          act[r] = false;
+        } else if (bin < bstar) {
+          act[r] = false;
+        }
+      }
+    if (all_in) break;                                       // uniform
+    need = rest;
   }
+  // leave both histograms zero for the next call
   __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kTopkBins / kTopkThreads; ++i) {
+    sh.hist[0][t + kTopkThreads * i] = 0;
+    sh.hist[1][t + kTopkThreads * i] = 0;
+  }
 }
 
-// Query-aware score of block bb from the 5 x G chunk weights ev (chunks
-// 4bb-1 .. 4bb+3), with the per-split softmax factors f_sh.
-__device__ inline float block_qscore(const float (&ev)[5][kMaxGroup], int bb, int C,
-                                     const float *f_sh, int G) {
+// Query-aware score of block bb: max over its overlapping chunks
+// 4bb-1 .. 4bb+3 of the chunk score a_c.
+__device__ inline float block_qscore(const float *a_sh, int bb, int C) {
   float qb = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 5; ++j) {
     const int c = 4 * bb - 1 + j;
-    if (c < 0 || c >= C) continue;
-    const float *fs = f_sh + (c / kChunksPerSplit) * G;
-    float a = 0.0f;
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h)
-      if (h < G) a = fmaf(ev[j][h], fs[h], a);
-    qb = fmaxf(qb, a);
+    if (c >= 0 && c < C) qb = fmaxf(qb, a_sh[c]);
   }
   return qb;
 }
 
-__device__ inline void load_weights(float (&ev)[5][kMaxGroup], const float *ep, int bb, int C,
-                                    int c_pad, int G) {
+// Both selection stages with R candidate slots per thread (candidate
+// t + 256 r, block n_sink + t + 256 r). Stage 1: the k_q candidates of
+// highest query-aware score; stage 2: the k_e' eligible candidates of highest
+// agnostic score among the rest.
+template <int R>
+__device__ __forceinline__ void select_stages(const Dims &d, int p, int n_cand, int C, bool do_q, bool do_e,
+                              const float *a_sh, const uint32_t *el_sh, const float *be,
+                              float e0, uint8_t *kind, float *dbg, TopkLds &tk) {
+  const int t = threadIdx.x;
+  if (do_q) {
+    uint64_t kq[R];
 #pragma unroll
-  for (int j = 0; j < 5; ++j) {
-    const int c = 4 * bb - 1 + j;
-    const bool cin = c >= 0 && c < C;
+    for (int r = 0; r < R; ++r) {
+      const int i = t + kTopkThreads * r, bb = d.n_sink + i;
+      kq[r] = 0;
+      if (i < n_cand) {
+        const float qb = block_qscore(a_sh, bb, C);
+        kq[r] = compose_key(qb, bb);
+        if (dbg) dbg[(size_t)p * d.NB_max + bb] = qb;
+      }
+    }
+    wg_topk(kq, d.k_q, d.n_sink, kind, NOSA_KIND_QUERY, tk);
+    __syncthreads();
+  }
+  if (do_e) {
+    uint64_t ke[R];
 #pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) ev[j][h] = (cin && h < G) ? ep[(size_t)h * c_pad + c] : 0.0f;
+    for (int r = 0; r < R; ++r) {
+      const int i = t + kTopkThreads * r, bb = d.n_sink + i;
+      ke[r] = 0;
+      if (i < n_cand && ((el_sh[bb >> 5] >> (bb & 31)) & 1u) && kind[bb] != NOSA_KIND_QUERY)
+        ke[r] = compose_key(r == 0 ? e0 : be[bb], bb);
+    }
+    wg_topk(ke, d.k_e_dyn, d.n_sink, kind, NOSA_KIND_AGNOSTIC, tk);
   }
 }
+
+constexpr int kMaxCandPerThread = (kMaxContext / kBlock) / kTopkThreads;   // 16
+constexpr int kLoadBatch = 8;     // chunk-weight float4 loads in flight per thread
 
 __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
     Dims d, nosa_state st, const float *__restrict__ ws_e,
     const float2 *__restrict__ ws_stats, int c_pad, int n_splits,
     int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
     uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
+  const int Gp = padded_group(d.G);
   extern __shared__ __align__(16) uint8_t smem[];
-  float *f_sh = reinterpret_cast<float *>(smem);                            // [n_splits][G]
-  uint32_t *el_sh = reinterpret_cast<uint32_t *>(f_sh + n_splits * d.G);    // [elig_words]
+  float *f_sh = reinterpret_cast<float *>(smem);                            // [n_splits][Gp]
+  float *a_sh = f_sh + n_splits * Gp;                                       // [c_pad]
+  uint32_t *el_sh = reinterpret_cast<uint32_t *>(a_sh + c_pad);             // [elig_words]
   uint8_t *kind = reinterpret_cast<uint8_t *>(el_sh + d.elig_words);        // [NB_max]
-  __shared__ uint64_t top_sh[kTopkThreads / 64][64];
-  __shared__ int sh[8];
+  __shared__ TopkLds tk;
+  __shared__ int cnt_sh[2][kTopkThreads / 64];
 
   const int p = blockIdx.x, t = threadIdx.x;
   const int w = t >> 6, lane = t & 63;
@@ -297,15 +392,20 @@ __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
   const int used = (C + kChunksPerSplit - 1) / kChunksPerSplit;
   const bool do_q = d.k_q > 0 && n_cand > 0, do_e = d.k_e_dyn > 0 && n_cand > 0;
 
-  // 0. issue this thread's global loads together: split statistics, the
-  // chunk weights and agnostic score of its first candidate, eligibility
-  const float *ep = ws_e + (size_t)p * d.G * c_pad;
+  // 0. issue the global loads together: split statistics, the first batch
+  // of chunk weights (coalesced float4s of the chunk-major [c][Gp] array),
+  // the candidates' agnostic scores, eligibility
+  const float4 *ep4 = reinterpret_cast<const float4 *>(ws_e + (size_t)p * c_pad * Gp);
+  const int n4 = do_q ? C * Gp / 4 : 0;
+  float4 eb[kLoadBatch];
+#pragma unroll
+  for (int u = 0; u < kLoadBatch; ++u) {
+    const int k4 = t + kTopkThreads * u;
+    eb[u] = k4 < n4 ? ep4[k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   const float *be = st.blk_e + (size_t)p * d.NB_max;
-  const int i0 = 64 * w + lane, bb0 = d.n_sink + i0;
-  const bool have0 = i0 < n_cand;
-  float ev[5][kMaxGroup];
-  if (do_q) load_weights(ev, ep, have0 ? bb0 : 0, have0 ? C : 0, c_pad, d.G);
-  const float e0 = (do_e && have0) ? be[bb0] : 0.0f;
+  const bool have0 = t < n_cand;
+  const float e0 = (do_e && have0) ? be[d.n_sink + t] : 0.0f;
   const int sh_h = t >> 4, sh_j = t & 15;
   float2 stv = make_float2(-INFINITY, 0.0f);
   if (do_q && sh_h < d.G && sh_j < used) stv = ws_stats[((size_t)p * n_splits + sh_j) * d.G + sh_h];
@@ -313,101 +413,133 @@ __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
     el_sh[i] = st.eligible[(size_t)p * d.elig_words + i];
   for (int bb = t; bb < nb; bb += kTopkThreads)
     kind[bb] = bb < d.n_sink ? NOSA_KIND_SINK : (bb >= win_lo ? NOSA_KIND_WINDOW : NOSA_KIND_NONE);
-
-  // 1. per-split factors exp(m_split - M) / Z of each head's softmax
-  if (do_q && sh_h < d.G) {
-    const float2 *stp = ws_stats + (size_t)p * n_splits * d.G;
-    double m = stv.x;
-    for (int s = sh_j + 16; s < used; s += 16) m = fmax(m, (double)stp[s * d.G + sh_h].x);
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m = fmax(m, __shfl_xor(m, o, 64));
-    double z = stv.y > 0.0f ? (double)stv.y * exp((double)stv.x - m) : 0.0;
-    for (int s = sh_j + 16; s < used; s += 16) {
-      const float2 v = stp[s * d.G + sh_h];
-      if (v.y > 0.0f) z += (double)v.y * exp((double)v.x - m);
-    }
+  for (int i = 0; i < kTopkBins / kTopkThreads; ++i) {
+    tk.hist[0][t + kTopkThreads * i] = 0;
+    tk.hist[1][t + kTopkThreads * i] = 0;
+  }
+
+  // 1. per-split factors exp(m_split - M) / Z of each head's softmax (0 for
+  // the padding heads)
+  if (do_q && sh_h < Gp) {
+    const float2 *stp = ws_stats + (size_t)p * n_splits * d.G;
+    const bool real = sh_h < d.G;
+    float m = stv.x;
+    if (real)
+      for (int s = sh_j + 16; s < used; s += 16) m = fmaxf(m, stp[s * d.G + sh_h].x);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float e0s = stv.y > 0.0f ? expf(stv.x - m) : 0.0f;
+    float z = stv.y * e0s;
+    if (real)
+      for (int s = sh_j + 16; s < used; s += 16) {
+        const float2 v = stp[s * d.G + sh_h];
+        if (v.y > 0.0f) z += v.y * expf(v.x - m);
+      }
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
-    if (sh_j < used) f_sh[sh_j * d.G + sh_h] = stv.y > 0.0f ? (float)(exp((double)stv.x - m) / z) : 0.0f;
+    const float rz = real ? 1.0f / z : 0.0f;
+    if (sh_j < used) f_sh[sh_j * Gp + sh_h] = e0s * rz;
     for (int s = sh_j + 16; s < used; s += 16) {
-      const float2 v = stp[s * d.G + sh_h];
-      f_sh[s * d.G + sh_h] = v.y > 0.0f ? (float)(exp((double)v.x - m) / z) : 0.0f;
+      const float2 v = real ? stp[s * d.G + sh_h] : make_float2(-INFINITY, 0.0f);
+      f_sh[s * Gp + sh_h] = v.y > 0.0f ? expf(v.x - m) * rz : 0.0f;
     }
   }
   __syncthreads();
 
-  // 2. stage 1: top k_q candidates by the query-aware score (max over the
-  // overlapping chunks of the group's softmax sum; heads summed in order, so
-  // a chunk shared by two blocks gives both the same value)
+  // 2. chunk scores a_c = sum over the group's heads of the head's softmax
+  // weight, once per chunk (a chunk shared by two blocks gives both the same
+  // value): each float4 covers 4 heads of one chunk, the Gp / 4 lanes of a
+  // chunk are adjacent and combine with lane exchanges
   if (do_q) {
-    uint64_t best = 0;
-    for (int base = 64 * w; base < n_cand; base += kTopkThreads) {   // wave-uniform
-      const int i = base + lane, bb = d.n_sink + i;
-      if (base != 64 * w) load_weights(ev, ep, i < n_cand ? bb : 0, i < n_cand ? C : 0, c_pad, d.G);
-      uint64_t key = 0;
-      if (i < n_cand) {
-        const float qb = block_qscore(ev, bb, C, f_sh, d.G);
-        key = compose_key(qb, bb);
-        if (dbg) dbg[(size_t)p * d.NB_max + bb] = qb;
+    const int lpc = Gp / 4;                          // lanes per chunk: 1, 2, 4
+    for (int k0 = 0; k0 < n4; k0 += kTopkThreads * kLoadBatch) {     // uniform
+      if (k0 > 0) {
+#pragma unroll
+        for (int u = 0; u < kLoadBatch; ++u) {
+          const int k4 = k0 + t + kTopkThreads * u;
+          eb[u] = k4 < n4 ? ep4[k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
-      best = wave_merge_desc(best, wave_sort_desc(key));
-    }
-    finish_topk(best, d.k_q, kind, NOSA_KIND_QUERY, top_sh);
-  }
-
-  // 3. stage 2: top k_e' of the eligible candidates left by stage 1, by the
-  // query-agnostic score
-  if (do_e) {
-    uint64_t best = 0;
-    for (int base = 64 * w; base < n_cand; base += kTopkThreads) {   // wave-uniform
-      const int i = base + lane, bb = d.n_sink + i;
-      uint64_t key = 0;
-      if (i < n_cand) {
-        const float eb = base == 64 * w ? e0 : be[bb];
-        const bool elig = (el_sh[bb >> 5] >> (bb & 31)) & 1u;
-        if (elig && kind[bb] != NOSA_KIND_QUERY) key = compose_key(eb, bb);
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u) {
+        const int k4 = k0 + t + kTopkThreads * u;
+        const int c = k4 / lpc, h0 = 4 * (k4 % lpc);
+        float a = 0.0f;
+        if (k4 < n4) {
+          const float *fs = f_sh + (c / kChunksPerSplit) * Gp + h0;
+          a = eb[u].x * fs[0];
+          a = fmaf(eb[u].y, fs[1], a);
+          a = fmaf(eb[u].z, fs[2], a);
+          a = fmaf(eb[u].w, fs[3], a);
+        }
+        if (lpc >= 2) a += __shfl_xor(a, 1, 64);
+        if (lpc >= 4) a += __shfl_xor(a, 2, 64);
+        if (k4 < n4 && h0 == 0) a_sh[c] = a;
       }
-      best = wave_merge_desc(best, wave_sort_desc(key));
     }
-    finish_topk(best, d.k_e_dyn, kind, NOSA_KIND_AGNOSTIC, top_sh);
   }
   __syncthreads();
 
-  // 4. ascending selection list
+  // 3. both stages, with as many candidate slots per thread as needed
   {
-    const int per = (nb + kTopkThreads - 1) / kTopkThreads;
-    const int lo = t * per, hi = min(nb, lo + per);
-    int cnt = 0;
-    for (int bb = lo; bb < hi; ++bb) cnt += kind[bb] != NOSA_KIND_NONE;
-    int total = 0;
-    int off = block_excl_scan(cnt, sh, &total);
+    const int m = (n_cand + kTopkThreads - 1) / kTopkThreads;   // <= kMaxCandPerThread
+    if (m <= 1)
+      select_stages<1>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
+    else if (m <= 2)
+      select_stages<2>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
+    else if (m <= 4)
+      select_stages<4>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
+    else if (m <= 8)
+      select_stages<8>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
+    else
+      select_stages<kMaxCandPerThread>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind,
+                                       dbg, tk);
+  }
+  __syncthreads();
+
+  // 4. ascending selection list: ballot + prefix count per 256 blocks
+  {
     int32_t *sp = sel + (size_t)p * d.k;
     uint8_t *kp = kind_out ? kind_out + (size_t)p * d.k : nullptr;
-    for (int bb = lo; bb < hi; ++bb) {
-      if (kind[bb] != NOSA_KIND_NONE && off < d.k) {
+    int running = 0;
+    for (int base = 0; base < nb; base += kTopkThreads) {            // uniform
+      const int bb = base + t;
+      const bool in = bb < nb && kind[bb] != NOSA_KIND_NONE;
+      const uint64_t mask = __ballot(in);
+      const int below = __popcll(mask & ((1ull << lane) - 1ull));
+      if (lane == 0) cnt_sh[(base / kTopkThreads) & 1][w] = __popcll(mask);
+      __syncthreads();
+      const int *cs = cnt_sh[(base / kTopkThreads) & 1];
+      int off = running, tot = 0;
+#pragma unroll
+      for (int ww = 0; ww < kTopkThreads / 64; ++ww) {
+        if (ww < w) off += cs[ww];
+        tot += cs[ww];
+      }
+      off += below;
+      if (in && off < d.k) {
         sp[off] = bb;
         if (kp) kp[off] = kind[bb];
-        ++off;
       }
+      running += tot;
     }
-    for (int j = total + t; j < d.k; j += kTopkThreads) {
+    for (int j = running + t; j < d.k; j += kTopkThreads) {
       sp[j] = -1;
       if (kp) kp[j] = NOSA_KIND_NONE;
     }
-    if (t == 0) n_sel[p] = min(total, d.k);
+    if (t == 0) n_sel[p] = min(running, d.k);
   }
 
   // 5. eligibility: a candidate outside the selection is out for good
   if (n_cand > 0) {
     uint32_t *el = st.eligible + (size_t)p * d.elig_words;
-    const int w0 = d.n_sink >> 5, w1 = (win_lo - 1) >> 5;
-    for (int wd = w0 + t; wd <= w1; wd += kTopkThreads) {
-      uint32_t clear = 0u;
-      for (int j = 0; j < 32; ++j) {
-        const int bb = wd * 32 + j;
-        if (bb >= d.n_sink && bb < win_lo && kind[bb] == NOSA_KIND_NONE) clear |= 1u << j;
-      }
-      if (clear) el[wd] = el_sh[wd] & ~clear;
+    for (int base = 64 * w; base < win_lo; base += kTopkThreads) {   // wave-uniform
+      const int bb = base + lane;
+      const bool out = bb >= d.n_sink && bb < win_lo && kind[bb] == NOSA_KIND_NONE;
+      const uint64_t mask = __ballot(out);
+      const uint32_t clear = static_cast<uint32_t>(mask >> (lane & 32));
+      if ((lane & 31) == 0 && clear) el[bb >> 5] = el_sh[bb >> 5] & ~clear;
     }
   }
 }
@@ -420,7 +552,7 @@ SelectLayout select_layout(const Dims &d, int max_len) {
   s.n_splits = C > 0 ? (C + kChunksPerSplit - 1) / kChunksPerSplit : 1;
   s.c_pad = s.n_splits * kChunksPerSplit;
   s.e_off = 0;
-  s.stats_off = ((size_t)d.P * d.G * s.c_pad * sizeof(float) + 255) & ~(size_t)255;
+  s.stats_off = ((size_t)d.P * s.c_pad * padded_group(d.G) * sizeof(float) + 255) & ~(size_t)255;
   s.bytes = s.stats_off + (((size_t)d.P * s.n_splits * d.G * sizeof(float2) + 255) & ~(size_t)255);
   return s;
 }
@@ -432,7 +564,7 @@ hipError_t launch_select(const Dims &d, const nosa_state &st, const uint16_t *q,
   float2 *ws_stats = reinterpret_cast<float2 *>(static_cast<char *>(ws) + lay.stats_off);
   score_kernel<<<dim3(lay.n_splits, d.P), kScoreThreads, 0, s>>>(
       d, st.seq_len, st.ckey, q, ws_e, ws_stats, lay.c_pad, lay.n_splits);
-  const size_t lds = (size_t)lay.n_splits * d.G * sizeof(float) +
+  const size_t lds = ((size_t)lay.n_splits * padded_group(d.G) + lay.c_pad) * sizeof(float) +
                      (size_t)d.elig_words * sizeof(uint32_t) + (size_t)d.NB_max;
   pool_topk_kernel<<<dim3(d.P), kTopkThreads, lds, s>>>(
       d, st, ws_e, ws_stats, lay.c_pad, lay.n_splits, sel, n_sel, kind, dbg);
