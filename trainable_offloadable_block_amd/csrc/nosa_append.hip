@@ -11,17 +11,24 @@
 namespace nosa {
 namespace {
 
-// Copies one KV head's W1 (32 KiB bf16) into LDS: 16 independent 16-byte
-// loads per thread for a 128-thread group, then a barrier.
-__device__ void stage_w1(uint16_t *w1_sh, const uint16_t *__restrict__ W1g) {
+// One KV head's W1 (32 KiB bf16) for a 128-thread group: 16 independent
+// 16-byte loads per thread into registers, then into LDS (and a barrier).
+constexpr int kW1Vecs = kHeadDim * kHeadDim * 2 / 16 / 128;
+__device__ inline void load_w1(uint4 (&v)[kW1Vecs], const uint16_t *__restrict__ W1g) {
   const uint4 *src = reinterpret_cast<const uint4 *>(W1g);
+#pragma unroll
+  for (int j = 0; j < kW1Vecs; ++j) v[j] = src[threadIdx.x + 128 * j];
+}
+__device__ inline void store_w1(uint16_t *w1_sh, const uint4 (&v)[kW1Vecs]) {
   uint4 *dst = reinterpret_cast<uint4 *>(w1_sh);
-  uint4 v[kHeadDim * kHeadDim * 2 / 16 / 128];
 #pragma unroll
-  for (int j = 0; j < kHeadDim * kHeadDim * 2 / 16 / 128; ++j) v[j] = src[threadIdx.x + 128 * j];
-#pragma unroll
-  for (int j = 0; j < kHeadDim * kHeadDim * 2 / 16 / 128; ++j) dst[threadIdx.x + 128 * j] = v[j];
+  for (int j = 0; j < kW1Vecs; ++j) dst[threadIdx.x + 128 * j] = v[j];
   __syncthreads();
+}
+__device__ void stage_w1(uint16_t *w1_sh, const uint16_t *__restrict__ W1g) {
+  uint4 v[kW1Vecs];
+  load_w1(v, W1g);
+  store_w1(w1_sh, v);
 }
 
 // s = softplus(v W1) W2 for one value vector held in LDS as fp32, with W1
@@ -60,16 +67,29 @@ __global__ __launch_bounds__(128) void append_kernel(
   const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int p = b * d.Hkv + g;
   __shared__ float v_sh[kHeadDim];
+  __shared__ uint16_t k_sh[kHeadDim];
   __shared__ float red2[2];
   __shared__ int slot_sh;
   __shared__ __align__(16) uint16_t w1_sh[kHeadDim * kHeadDim];
 
+  // loads that do not depend on the length first, so the kernel waits for
+  // one memory round trip: the new key and value, this head's W1
+  // (both go to LDS before the barrier, so neither load sinks into the
+  // branch below, where they are used)
+  const uint16_t kb_ld = k_new[p * kHeadDim + t];
+  const uint16_t vb = v_new[p * kHeadDim + t];
   const int pos = st.seq_len[b];
+  {
+    uint4 w1v[kW1Vecs];
+    load_w1(w1v, st.w1 + (size_t)g * kHeadDim * kHeadDim);
+    v_sh[t] = bf16_to_f32(vb);
+    k_sh[t] = kb_ld;
+    store_w1(w1_sh, w1v);                // ends in a barrier
+  }
+  const uint16_t kb = k_sh[t];
   const bool ok = pos >= 0 && pos < d.max_context;
   if (ok) {
     const int L = pos + 1;
-    const uint16_t kb = k_new[p * kHeadDim + t];
-    const uint16_t vb = v_new[p * kHeadDim + t];
     const int blk = pos / kBlock, r = pos % kBlock;
 
     // 1. store K, V (K row-major, V in the block's tile order)
@@ -117,8 +137,6 @@ __global__ __launch_bounds__(128) void append_kernel(
     ring[(pos % kPoolKernel) * kHeadDim + t] = kb;
 
     // 3. eviction score of the new token
-    v_sh[t] = bf16_to_f32(vb);
-    stage_w1(w1_sh, st.w1 + (size_t)g * kHeadDim * kHeadDim);   // ends in a barrier
     const float s = evict_score_128(v_sh, w1_sh, st.w2 + (size_t)g * kHeadDim, red2);
     float *tok_s = st.tok_s + (size_t)p * d.tok_stride;
     if (t == 0) tok_s[pos] = s;

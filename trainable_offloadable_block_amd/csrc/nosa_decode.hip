@@ -73,21 +73,20 @@ struct DecodeArgs {
 // Issues the loads of half j (< the wave's half count) of the wave's list
 // (entries e_first, e_first + 4, ...; two halves each). Lane i holds the
 // block and slot ids of the wave's i-th entry (loaded once at the start), so
-// no memory round trip precedes the loads. The loads are unconditional, so
-// the compiler can keep one half in flight while another is computed; an
-// invalid entry reads slot 0 and is marked not ok.
+// no memory round trip precedes the loads. The loads are unconditional and
+// their offsets wave-uniform (no branch defines them), so the compiler keeps
+// one half in flight while another is computed; an invalid entry reads slot
+// 0, is marked not ok and sets `bad`.
 __device__ inline void load_half(Half &hb, int j, const DecodeArgs &a, const Dims &d,
-                                 int lane_blk, int lane_slot, uint32_t *status) {
+                                 int lane_blk, int lane_slot, bool &bad) {
   const int half = j & 1;
   int blk = __builtin_amdgcn_readlane(lane_blk, j >> 1);
   int slot = __builtin_amdgcn_readlane(lane_slot, j >> 1);
-  hb.ok = 1;
-  if (blk < 0 || blk >= d.NB_max || slot < 0 || slot >= a.slots) {
-    if (half == 0 && (threadIdx.x & 63) == 0) atomicOr(status, NOSA_STATUS_BAD_SEL);
-    hb.ok = 0;
-    blk = 0;
-    slot = 0;
-  }
+  const bool ok = blk >= 0 && blk < d.NB_max && slot >= 0 && slot < a.slots;
+  hb.ok = ok ? 1 : 0;
+  bad = bad || !ok;
+  blk = __builtin_amdgcn_readfirstlane(ok ? blk : 0);
+  slot = __builtin_amdgcn_readfirstlane(ok ? slot : 0);
   const int kbase = slot * (kBlockElems * 2) + half * (32 * kHeadDim * 2);
   const int vbase = slot * (kBlockElems * 2) + kBlock * kHeadDim * 2 + half * 8192;
   hb.key_base = blk * kBlock + 32 * half;
@@ -248,6 +247,15 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   const int b = p / d.Hkv, g = p % d.Hkv;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
   const int h = l & 15, lg = l >> 4;
+  // lane i: block and slot ids of this wave's i-th list entry, loaded
+  // before the list length is known (every entry < k exists), so the first
+  // KV loads wait for one memory round trip, not two
+  const int e_lane = split * bps + w + 4 * l;
+  int lane_blk = -1, lane_slot = -1;
+  if (l < 16 && e_lane < d.k) {
+    lane_blk = sel[(size_t)p * d.k + e_lane];
+    lane_slot = phys[(size_t)p * d.k + e_lane];
+  }
   const int L = seq_len[b];
   const int ns = max(0, min(n_sel[p], d.k));
 
@@ -272,17 +280,13 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   a.e_first = split * bps + w;
   a.e_end = min(ns, split * bps + bps);
   const int n_mine = a.e_first < a.e_end ? (a.e_end - a.e_first + 3) / 4 : 0;
-  // lane i: block and slot ids of this wave's i-th entry (n_mine <= 16)
-  int lane_blk = -1, lane_slot = -1;
-  if (l < n_mine) {
-    lane_blk = sel[(size_t)p * d.k + a.e_first + 4 * l];
-    lane_slot = phys[(size_t)p * d.k + a.e_first + 4 * l];
-  }
+  // n_mine <= 16: only lanes below it hold entries of the list
 
   const int nh = 2 * n_mine;
 
   Half A, B;
-  if (nh > 0) load_half(A, 0, a, d, lane_blk, lane_slot, status);
+  bool bad = false;                                  // wave-uniform
+  if (nh > 0) load_half(A, 0, a, d, lane_blk, lane_slot, bad);
 
   bf16x8 qop[4];
   if (h < d.G) {
@@ -304,17 +308,18 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   // nh is even (two halves per entry); the last pair is peeled so that no
   // load inside the loop is conditional
   for (int j = 0; j < nh - 2; j += 2) {
-    load_half(B, j + 1, a, d, lane_blk, lane_slot, status);
+    load_half(B, j + 1, a, d, lane_blk, lane_slot, bad);
     process_half(A, qop, qscale, bscale, L, lg, m_run, l_run, o);
-    load_half(A, j + 2, a, d, lane_blk, lane_slot, status);
+    load_half(A, j + 2, a, d, lane_blk, lane_slot, bad);
     process_half(B, qop, qscale, bscale, L, lg, m_run, l_run, o);
   }
   if (nh > 0) {
-    load_half(B, nh - 1, a, d, lane_blk, lane_slot, status);
+    load_half(B, nh - 1, a, d, lane_blk, lane_slot, bad);
     process_half(A, qop, qscale, bscale, L, lg, m_run, l_run, o);
     process_half(B, qop, qscale, bscale, L, lg, m_run, l_run, o);
   }
 
+  if (bad && l == 0) atomicOr(status, NOSA_STATUS_BAD_SEL);
   // lane (h, lg): head h's running max, its keys' partial sum, and
   // O^T[16*dt + 4*lg + i][h]; merge the 4 waves in LDS
   l_run += __shfl_xor(l_run, 16, 64);

@@ -39,42 +39,46 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     float2 *__restrict__ ws_stats, int c_pad, int n_splits) {
   const int split = blockIdx.x, p = blockIdx.y;
   const int b = p / d.Hkv, g = p % d.Hkv;
-  const int C = min(chunks_for(seq_len[b]), d.C_max);
   const int c0 = split * kChunksPerSplit;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int h = l & 15, lg = l >> 4;
   __shared__ float red_m[4][16], red_z[4][16];
+  // the query rows and every stored compressed key of this split's chunks
+  // are loaded before the length is known (rows past it are masked below),
+  // so the kernel waits for one memory round trip
+  const int cg = c0 + 32 * w;
+  uint4 qv[4], kv[2][4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qv[s] = make_uint4(0, 0, 0, 0);
+  if (h < d.G) {
+    const uint16_t *qh = q + ((size_t)b * d.Hq + g * d.G + h) * kHeadDim + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qv[s] = *reinterpret_cast<const uint4 *>(qh + 32 * s);
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int chunk = cg + tile_row(l & 15, t);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kv[t][s] = make_uint4(0, 0, 0, 0);
+    if (chunk < d.C_max) {
+      const uint16_t *src = ckey + ((size_t)p * d.C_max + chunk) * kHeadDim + 8 * lg;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kv[t][s] = *reinterpret_cast<const uint4 *>(src + 32 * s);
+    }
+  }
+  const int C = min(chunks_for(seq_len[b]), d.C_max);
   float2 *stats = ws_stats + (size_t)(p * n_splits + split) * d.G;
   if (c0 >= C) {
     if (threadIdx.x < d.G) stats[threadIdx.x] = make_float2(-INFINITY, 0.0f);
     return;
   }
-  bf16x8 qop[4];
-  if (h < d.G) {
-    const uint16_t *qh = q + ((size_t)b * d.Hq + g * d.G + h) * kHeadDim + 8 * lg;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qop[s] = as_bf16x8(*reinterpret_cast<const uint4 *>(qh + 32 * s));
-  } else {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qop[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
-  }
-  const int cg = c0 + 32 * w;
+  // logits on MFMA; a row past the length only feeds its own (masked) output
   f32x4 acc[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int chunk = cg + tile_row(l & 15, t);
-    uint4 a[4];
-    if (chunk < C) {
-      const uint16_t *src = ckey + ((size_t)p * d.C_max + chunk) * kHeadDim + 8 * lg;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) a[s] = *reinterpret_cast<const uint4 *>(src + 32 * s);
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) a[s] = make_uint4(0, 0, 0, 0);
-    }
     acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc[t] = mfma16x16x32(as_bf16x8(a[s]), qop[s], acc[t]);
+    for (int s = 0; s < 4; ++s) acc[t] = mfma16x16x32(as_bf16x8(kv[t][s]), as_bf16x8(qv[s]), acc[t]);
   }
   // lane (h, lg) now holds head h against chunks cg + 8*lg + m, m = 0..7
   const float scale = 0.08838834764831845f;   // 1/sqrt(128)
@@ -380,6 +384,26 @@ __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
   const int p = blockIdx.x, t = threadIdx.x;
   const int w = t >> 6, lane = t & 63;
   const int b = p / d.Hkv;
+
+  // 0. issue the global loads together, bounded by the buffers' extents
+  // rather than the length (which is itself being loaded), so the kernel
+  // waits for one memory round trip: the first batch of chunk weights
+  // (coalesced float4s of the chunk-major [c][Gp] array), split statistics,
+  // the candidates' agnostic scores, eligibility
+  const float4 *ep4 = reinterpret_cast<const float4 *>(ws_e + (size_t)p * c_pad * Gp);
+  const int n4_ext = c_pad * Gp / 4;
+  float4 eb[kLoadBatch];
+#pragma unroll
+  for (int u = 0; u < kLoadBatch; ++u) {
+    const int k4 = t + kTopkThreads * u;
+    eb[u] = k4 < n4_ext ? ep4[k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const float *be = st.blk_e + (size_t)p * d.NB_max;
+  const float e0_raw = d.n_sink + t < d.NB_max ? be[d.n_sink + t] : 0.0f;
+  const int sh_h = t >> 4, sh_j = t & 15;
+  float2 stv_raw = make_float2(-INFINITY, 0.0f);
+  if (sh_h < d.G && sh_j < n_splits) stv_raw = ws_stats[((size_t)p * n_splits + sh_j) * d.G + sh_h];
+
   const int L = max(0, min(st.seq_len[b], d.max_context));
   int C = chunks_for(L);
   if (C > c_pad) {                      // caller's length bound was too small
@@ -391,24 +415,10 @@ __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
   const int n_cand = max(0, win_lo - d.n_sink);
   const int used = (C + kChunksPerSplit - 1) / kChunksPerSplit;
   const bool do_q = d.k_q > 0 && n_cand > 0, do_e = d.k_e_dyn > 0 && n_cand > 0;
-
-  // 0. issue the global loads together: split statistics, the first batch
-  // of chunk weights (coalesced float4s of the chunk-major [c][Gp] array),
-  // the candidates' agnostic scores, eligibility
-  const float4 *ep4 = reinterpret_cast<const float4 *>(ws_e + (size_t)p * c_pad * Gp);
   const int n4 = do_q ? C * Gp / 4 : 0;
-  float4 eb[kLoadBatch];
-#pragma unroll
-  for (int u = 0; u < kLoadBatch; ++u) {
-    const int k4 = t + kTopkThreads * u;
-    eb[u] = k4 < n4 ? ep4[k4] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  const float *be = st.blk_e + (size_t)p * d.NB_max;
   const bool have0 = t < n_cand;
-  const float e0 = (do_e && have0) ? be[d.n_sink + t] : 0.0f;
-  const int sh_h = t >> 4, sh_j = t & 15;
-  float2 stv = make_float2(-INFINITY, 0.0f);
-  if (do_q && sh_h < d.G && sh_j < used) stv = ws_stats[((size_t)p * n_splits + sh_j) * d.G + sh_h];
+  const float e0 = (do_e && have0) ? e0_raw : 0.0f;
+  const float2 stv = (do_q && sh_h < d.G && sh_j < used) ? stv_raw : make_float2(-INFINITY, 0.0f);
   for (int i = t; i < d.elig_words; i += kTopkThreads)
     el_sh[i] = st.eligible[(size_t)p * d.elig_words + i];
   for (int bb = t; bb < nb; bb += kTopkThreads)
