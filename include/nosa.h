@@ -148,9 +148,9 @@ int nosa_state_bytes(const nosa_config *cfg, size_t sizes_out[NOSA_NUM_BUFFERS])
 
 /* Workspace bytes that call `which` needs for sequences up to max_len
  * tokens; 0 for an invalid config. A workspace must be 256-byte aligned.
- * The decode workspace must be zero-filled before its first use (it holds
- * per-pair arrival counters that every call leaves at zero); the others need
- * no initialisation. */
+ * The select and decode workspaces must be zero-filled before their first
+ * use (each holds per-pair arrival counters that every call leaves at zero);
+ * the fetch workspace needs no initialisation. */
 size_t nosa_workspace_bytes(const nosa_config *cfg, int which, int32_t max_len);
 
 /* ------------------------------------------------------------ calls */
@@ -197,7 +197,9 @@ int nosa_compress_append(const nosa_config *cfg, const nosa_state *st,
  * ascending order, -1 padded; n_sel dev int32 [B][Hkv]; kind (optional) dev
  * uint8 [B][Hkv][k_blocks] NOSA_KIND_*; dbg_qscore (optional) dev fp32
  * [B][Hkv][NB_max], the query-aware block score of each candidate (other
- * entries untouched). ws: NOSA_WS_SELECT bytes. */
+ * entries untouched). ws: NOSA_WS_SELECT bytes, zero-filled before the
+ * first call and left at zero by every call; calls that share one ws must be
+ * ordered (one stream). */
 int nosa_select(const nosa_config *cfg, const nosa_state *st,
                 const uint16_t *q, int32_t *sel, int32_t *n_sel,
                 uint8_t *kind, float *dbg_qscore, void *ws, size_t ws_bytes,

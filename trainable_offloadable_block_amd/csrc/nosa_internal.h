@@ -15,7 +15,7 @@ constexpr int kChunksPerSplit = 128;   // 4 waves x one 32-chunk MFMA group
 struct SelectLayout {
   int n_splits;      // chunk splits per pair
   int c_pad;         // n_splits * kChunksPerSplit
-  size_t e_off, stats_off, bytes;
+  size_t e_off, stats_off, count_off, bytes;   // count: per-pair arrivals, zero at rest
 };
 SelectLayout select_layout(const Dims &d, int max_len);
 

@@ -1,16 +1,19 @@
 // Two-stage block selection (aiwiki "NOSA", How NOSA works; NOSA-1B
 // 核心组件揭秘, 核心组件三; l189 article, 2.1).
 //
-// score_kernel  (pairs x chunk splits): query-aware logits of the GQA group
-//   against the compressed keys on MFMA, l = q . c / sqrt(128); per split and
-//   head, m = max l, Z = sum exp(l - m); stores e = exp(l - m) per chunk.
-// pool_topk_kernel (one workgroup per pair): combines the split statistics
-//   into the per-head softmax, sums the group's heads, max-pools the chunks
-//   overlapping each block, then stage 1 (top k_q by the query-aware score)
-//   and stage 2 (top k_e' eligible by the agnostic score), each an exact
-//   workgroup top-k by histogram range refinement, writes the ascending
-//   selection and clears the eligibility of every candidate left out (never
-//   re-selected by the agnostic stage).
+// select_kernel (chunk splits x pairs), one launch:
+//  - every workgroup scores one split: query-aware logits of the GQA group
+//    against the compressed keys on MFMA, l = q . c / sqrt(128); per split
+//    and head, m = max l, Z = sum exp(l - m); it publishes e = exp(l - m) per
+//    chunk and (m, Z) with device-coherent stores and arrives on the pair's
+//    counter;
+//  - the pair's last workgroup combines the split statistics into the
+//    per-head softmax, sums the group's heads, max-pools the chunks
+//    overlapping each block, then stage 1 (top k_q by the query-aware score)
+//    and stage 2 (top k_e' eligible by the agnostic score), each an exact
+//    workgroup top-k by histogram range refinement, writes the ascending
+//    selection and clears the eligibility of every candidate left out (never
+//    re-selected by the agnostic stage).
 #include "nosa_internal.h"
 
 namespace nosa {
@@ -33,11 +36,34 @@ __device__ inline int tile_row(int r, int t) { return 8 * (r >> 2) + 4 * t + (r 
 // so that one 16-byte load never straddles two chunks.
 __host__ __device__ inline int padded_group(int G) { return G <= 4 ? 4 : (G <= 8 ? 8 : 16); }
 
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(
-    Dims d, const int32_t *__restrict__ seq_len, const uint16_t *__restrict__ ckey,
-    const uint16_t *__restrict__ q, float *__restrict__ ws_e,
-    float2 *__restrict__ ws_stats, int c_pad, int n_splits) {
-  const int split = blockIdx.x, p = blockIdx.y;
+// Device-coherent (agent-scope) stores and loads: how the score workgroups
+// of a pair hand their results to the pair's last workgroup without a
+// device-scope fence (which would write back the XCD's whole L2).
+__device__ inline void put(float *a, float v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float get(const float *a) {
+  return __hip_atomic_load(const_cast<float *>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+constexpr int kCoherent = 16;   // buffer-load cache policy: sc1, as the agent-scope loads
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ inline float4 load4_coherent(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCoherent));
+}
+__device__ inline float2 load2_coherent(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kCoherent));
+}
+
+// Split `split` of pair p: logits of the group against this split's
+// compressed keys, published with device-coherent stores.
+__device__ __forceinline__ void score_split(const Dims &d, const int32_t *__restrict__ seq_len,
+                                            const uint16_t *__restrict__ ckey,
+                                            const uint16_t *__restrict__ q, float *ws_e,
+                                            float *ws_stats, int c_pad, int n_splits, int split,
+                                            int p) {
   const int b = p / d.Hkv, g = p % d.Hkv;
   const int c0 = split * kChunksPerSplit;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -67,9 +93,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     }
   }
   const int C = min(chunks_for(seq_len[b]), d.C_max);
-  float2 *stats = ws_stats + (size_t)(p * n_splits + split) * d.G;
+  float *stats = ws_stats + (size_t)2 * (p * n_splits + split) * d.G;   // (M, Z) per head
   if (c0 >= C) {
-    if (threadIdx.x < d.G) stats[threadIdx.x] = make_float2(-INFINITY, 0.0f);
+    if (threadIdx.x < d.G) {
+      put(&stats[2 * threadIdx.x], -INFINITY);
+      put(&stats[2 * threadIdx.x + 1], 0.0f);
+    }
     return;
   }
   // logits on MFMA; a row past the length only feeds its own (masked) output
@@ -110,14 +139,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     float *dst = ws_e + ((size_t)p * c_pad + cg + 8 * lg) * Gp + h;
 #pragma unroll
     for (int m = 0; m < 8; ++m)
-      if (cg + 8 * lg + m < C) dst[m * Gp] = h < d.G ? ev[m] : 0.0f;
+      if (cg + 8 * lg + m < C) put(&dst[m * Gp], h < d.G ? ev[m] : 0.0f);
   }
   __syncthreads();
   if (threadIdx.x < d.G) {
     const int hh = threadIdx.x;
     const float Mh = fmaxf(fmaxf(red_m[0][hh], red_m[1][hh]), fmaxf(red_m[2][hh], red_m[3][hh]));
     const float Zh = (red_z[0][hh] + red_z[1][hh]) + (red_z[2][hh] + red_z[3][hh]);
-    stats[hh] = make_float2(Mh, Zh);
+    put(&stats[2 * hh], Mh);
+    put(&stats[2 * hh + 1], Zh);
   }
 }
 
@@ -367,11 +397,14 @@ __device__ __forceinline__ void select_stages(const Dims &d, int p, int n_cand, 
 constexpr int kMaxCandPerThread = (kMaxContext / kBlock) / kTopkThreads;   // 16
 constexpr int kLoadBatch = 8;     // chunk-weight float4 loads in flight per thread
 
-__global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
-    Dims d, nosa_state st, const float *__restrict__ ws_e,
-    const float2 *__restrict__ ws_stats, int c_pad, int n_splits,
-    int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
-    uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
+// Pooling and both stages for pair p, run by the pair's last score
+// workgroup once every split has published (so the chunk weights and split
+// statistics are read with device-coherent loads).
+__device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
+                                            const float *ws_e, const float *ws_stats,
+                                            int c_pad, int n_splits, int32_t *sel,
+                                            int32_t *n_sel, uint8_t *kind_out, float *dbg,
+                                            int p) {
   const int Gp = padded_group(d.G);
   extern __shared__ __align__(16) uint8_t smem[];
   float *f_sh = reinterpret_cast<float *>(smem);                            // [n_splits][Gp]
@@ -381,7 +414,7 @@ __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
   __shared__ TopkLds tk;
   __shared__ int cnt_sh[2][kTopkThreads / 64];
 
-  const int p = blockIdx.x, t = threadIdx.x;
+  const int t = threadIdx.x;
   const int w = t >> 6, lane = t & 63;
   const int b = p / d.Hkv;
 
@@ -390,19 +423,21 @@ __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
   // waits for one memory round trip: the first batch of chunk weights
   // (coalesced float4s of the chunk-major [c][Gp] array), split statistics,
   // the candidates' agnostic scores, eligibility
-  const float4 *ep4 = reinterpret_cast<const float4 *>(ws_e + (size_t)p * c_pad * Gp);
   const int n4_ext = c_pad * Gp / 4;
+  const __amdgpu_buffer_rsrc_t er = make_rsrc(ws_e + (size_t)p * c_pad * Gp, (uint32_t)n4_ext * 16);
   float4 eb[kLoadBatch];
 #pragma unroll
   for (int u = 0; u < kLoadBatch; ++u) {
     const int k4 = t + kTopkThreads * u;
-    eb[u] = k4 < n4_ext ? ep4[k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    eb[u] = k4 < n4_ext ? load4_coherent(er, 16 * k4) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const float *be = st.blk_e + (size_t)p * d.NB_max;
   const float e0_raw = d.n_sink + t < d.NB_max ? be[d.n_sink + t] : 0.0f;
   const int sh_h = t >> 4, sh_j = t & 15;
+  const __amdgpu_buffer_rsrc_t sr =
+      make_rsrc(ws_stats + (size_t)2 * p * n_splits * d.G, (uint32_t)n_splits * d.G * 8);
   float2 stv_raw = make_float2(-INFINITY, 0.0f);
-  if (sh_h < d.G && sh_j < n_splits) stv_raw = ws_stats[((size_t)p * n_splits + sh_j) * d.G + sh_h];
+  if (sh_h < d.G && sh_j < n_splits) stv_raw = load2_coherent(sr, 8 * (sh_j * d.G + sh_h));
 
   const int L = max(0, min(st.seq_len[b], d.max_context));
   int C = chunks_for(L);
@@ -432,18 +467,17 @@ __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
   // 1. per-split factors exp(m_split - M) / Z of each head's softmax (0 for
   // the padding heads)
   if (do_q && sh_h < Gp) {
-    const float2 *stp = ws_stats + (size_t)p * n_splits * d.G;
     const bool real = sh_h < d.G;
     float m = stv.x;
     if (real)
-      for (int s = sh_j + 16; s < used; s += 16) m = fmaxf(m, stp[s * d.G + sh_h].x);
+      for (int s = sh_j + 16; s < used; s += 16) m = fmaxf(m, load2_coherent(sr, 8 * (s * d.G + sh_h)).x);
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     const float e0s = stv.y > 0.0f ? expf(stv.x - m) : 0.0f;
     float z = stv.y * e0s;
     if (real)
       for (int s = sh_j + 16; s < used; s += 16) {
-        const float2 v = stp[s * d.G + sh_h];
+        const float2 v = load2_coherent(sr, 8 * (s * d.G + sh_h));
         if (v.y > 0.0f) z += v.y * expf(v.x - m);
       }
 #pragma unroll
@@ -451,7 +485,7 @@ __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
     const float rz = real ? 1.0f / z : 0.0f;
     if (sh_j < used) f_sh[sh_j * Gp + sh_h] = e0s * rz;
     for (int s = sh_j + 16; s < used; s += 16) {
-      const float2 v = real ? stp[s * d.G + sh_h] : make_float2(-INFINITY, 0.0f);
+      const float2 v = real ? load2_coherent(sr, 8 * (s * d.G + sh_h)) : make_float2(-INFINITY, 0.0f);
       f_sh[s * Gp + sh_h] = v.y > 0.0f ? expf(v.x - m) * rz : 0.0f;
     }
   }
@@ -468,7 +502,7 @@ __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
 #pragma unroll
         for (int u = 0; u < kLoadBatch; ++u) {
           const int k4 = k0 + t + kTopkThreads * u;
-          eb[u] = k4 < n4 ? ep4[k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+          eb[u] = k4 < n4 ? load4_coherent(er, 16 * k4) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
       }
 #pragma unroll
@@ -554,6 +588,27 @@ __global__ __launch_bounds__(kTopkThreads) void pool_topk_kernel(
   }
 }
 
+// grid (splits, pairs): every workgroup scores its split and arrives on the
+// pair's counter once its results have landed; the last one pools and
+// selects, then resets the counter (zero at rest).
+__global__ __launch_bounds__(kScoreThreads) void select_kernel(
+    Dims d, nosa_state st, const uint16_t *__restrict__ q, float *ws_e, float *ws_stats,
+    int32_t *ws_count, int c_pad, int n_splits, int32_t *__restrict__ sel,
+    int32_t *__restrict__ n_sel, uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
+  const int split = blockIdx.x, p = blockIdx.y;
+  __shared__ int sm_last;
+  score_split(d, st.seq_len, st.ckey, q, ws_e, ws_stats, c_pad, n_splits, split, p);
+  __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    sm_last = __hip_atomic_fetch_add(&ws_count[p], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              n_splits - 1;
+  __syncthreads();
+  if (!sm_last) return;
+  pool_select(d, st, ws_e, ws_stats, c_pad, n_splits, sel, n_sel, kind_out, dbg, p);
+  if (threadIdx.x == 0) __hip_atomic_store(&ws_count[p], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace
 
 SelectLayout select_layout(const Dims &d, int max_len) {
@@ -563,21 +618,22 @@ SelectLayout select_layout(const Dims &d, int max_len) {
   s.c_pad = s.n_splits * kChunksPerSplit;
   s.e_off = 0;
   s.stats_off = ((size_t)d.P * s.c_pad * padded_group(d.G) * sizeof(float) + 255) & ~(size_t)255;
-  s.bytes = s.stats_off + (((size_t)d.P * s.n_splits * d.G * sizeof(float2) + 255) & ~(size_t)255);
+  s.count_off = s.stats_off + (((size_t)d.P * s.n_splits * d.G * sizeof(float2) + 255) & ~(size_t)255);
+  s.bytes = s.count_off + (((size_t)d.P * sizeof(int32_t) + 255) & ~(size_t)255);
   return s;
 }
 
 hipError_t launch_select(const Dims &d, const nosa_state &st, const uint16_t *q,
                          int32_t *sel, int32_t *n_sel, uint8_t *kind, float *dbg,
                          void *ws, const SelectLayout &lay, hipStream_t s) {
-  float *ws_e = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.e_off);
-  float2 *ws_stats = reinterpret_cast<float2 *>(static_cast<char *>(ws) + lay.stats_off);
-  score_kernel<<<dim3(lay.n_splits, d.P), kScoreThreads, 0, s>>>(
-      d, st.seq_len, st.ckey, q, ws_e, ws_stats, lay.c_pad, lay.n_splits);
+  char *base = static_cast<char *>(ws);
+  float *ws_e = reinterpret_cast<float *>(base + lay.e_off);
+  float *ws_stats = reinterpret_cast<float *>(base + lay.stats_off);
+  int32_t *ws_count = reinterpret_cast<int32_t *>(base + lay.count_off);
   const size_t lds = ((size_t)lay.n_splits * padded_group(d.G) + lay.c_pad) * sizeof(float) +
                      (size_t)d.elig_words * sizeof(uint32_t) + (size_t)d.NB_max;
-  pool_topk_kernel<<<dim3(d.P), kTopkThreads, lds, s>>>(
-      d, st, ws_e, ws_stats, lay.c_pad, lay.n_splits, sel, n_sel, kind, dbg);
+  select_kernel<<<dim3(lay.n_splits, d.P), kScoreThreads, lds, s>>>(
+      d, st, q, ws_e, ws_stats, ws_count, lay.c_pad, lay.n_splits, sel, n_sel, kind, dbg);
   return hipGetLastError();
 }
 
