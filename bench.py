@@ -6,9 +6,10 @@ head_dim 128, 16384-token prefilled context, block 64, 1 sink block, 1024-token
 window, k = 64 blocks = 16 query-aware + 48 query-agnostic), KV resident in
 HBM, seeded synthetic inputs (see synth/workloads.py). A step is one decode
 token through a stack of --layers independent layers of that shape, each
-layer running the whole path: compress_append -> select -> fetch_delta ->
-sparse_decode. A stack (as in a real model) keeps one layer's KV from
-staying in the 256 MB last-level cache between its steps.
+layer running the whole path: compress_append + select (one launch,
+nosa_append_select) -> fetch_delta -> sparse_decode. A stack (as in a real
+model) keeps one layer's KV from staying in the 256 MB last-level cache
+between its steps.
 
 Prints ONE JSON line. value = decode tokens/s per layer = batch * layers *
 steps / elapsed. roofline: the sparse-decode kernel's algorithmic bytes per
@@ -226,8 +227,7 @@ def host_link_leg(n_steps, pool, dev):
     # delta fetch per step
     recs = []
     for t in range(n_steps):
-        layer.append(kn[t], vn[t])
-        layer.select(q[t], want_kind=False)
+        layer.append_select(kn[t], vn[t], q[t], want_kind=False)
         a, b = ev(), ev()
         a.record()
         layer.fetch()
@@ -298,8 +298,7 @@ def main():
     def run_step(t, events=None):
         for li, layer in enumerate(layers):
             q, kn, vn = inputs[li][0][t], inputs[li][1][t], inputs[li][2][t]
-            layer.append(kn, vn)
-            layer.select(q, want_kind=False)
+            layer.append_select(kn, vn, q, want_kind=False)
             layer.fetch()
             if events is not None:
                 events[0].append(torch.cuda.Event(enable_timing=True))
@@ -323,22 +322,20 @@ def main():
     # per-call breakdown on a few extra steps (untimed region); these steps
     # also give the exact number of attended tokens per decode launch (the
     # stage-2 pool can run short, so a selection may hold fewer than k blocks)
-    names = ("append", "select", "fetch", "decode")
+    names = ("append_select", "fetch", "decode")
     bd = {n: [] for n in names}
     n_att_samples = []
     for t in range(W + K, n_tok):
         for li, layer in enumerate(layers):
             q, kn, vn = inputs[li][0][t], inputs[li][1][t], inputs[li][2][t]
-            evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             evs[0].record()
-            layer.append(kn, vn)
+            layer.append_select(kn, vn, q, want_kind=False)
             evs[1].record()
-            layer.select(q, want_kind=False)
-            evs[2].record()
             layer.fetch()
-            evs[3].record()
+            evs[2].record()
             layer.decode(q)
-            evs[4].record()
+            evs[3].record()
             torch.cuda.synchronize()
             for i, n in enumerate(names):
                 bd[n].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)

@@ -205,6 +205,19 @@ int nosa_select(const nosa_config *cfg, const nosa_state *st,
                 uint8_t *kind, float *dbg_qscore, void *ws, size_t ws_bytes,
                 int32_t max_len_host, hipStream_t stream);
 
+/* nosa_compress_append followed by nosa_select, in one launch: the same
+ * results (state, sel, n_sel, kind, dbg_qscore) as the two calls in a row
+ * with the same arguments, the append's token at position seq_len[b] and
+ * the selection at the new length. ws and max_len_host as for nosa_select
+ * (max_len_host bounds the length after the append). For callers that run
+ * the two steps back to back (one launch and its dispatch fewer). */
+int nosa_append_select(const nosa_config *cfg, const nosa_state *st,
+                       const uint16_t *k_new, const uint16_t *v_new,
+                       const uint16_t *q, int32_t *sel, int32_t *n_sel,
+                       uint8_t *kind, float *dbg_qscore, void *ws,
+                       size_t ws_bytes, int32_t max_len_host,
+                       hipStream_t stream);
+
 /* Offload mode only: brings the selected blocks into the device cache.
  * Set difference of sel against the cached blocks (NOSI's set-difference
  * kernel, aiwiki "NOSA", NOSI: the inference system): slots whose block is

@@ -63,8 +63,9 @@ class StepReport:
 
 class Lockstep:
     def __init__(self, wl, layer=0, check_pairs=None, lengths=None,
-                 offload=None, steps=None, before_prefill=None):
+                 offload=None, steps=None, before_prefill=None, fused=False):
         self.wl = wl
+        self.fused = fused          # nosa_append_select instead of the two calls
         self.layer_idx = layer
         B, Hkv, G = wl.batch, wl.n_kv_heads, wl.group
         self.lengths = np.full(B, wl.context, dtype=np.int64) if lengths is None \
@@ -178,8 +179,11 @@ class Lockstep:
         wl, G, Hkv, k = self.wl, self.wl.group, self.wl.n_kv_heads, self.wl.k_blocks
         kd, vd, qd = self.inputs(t)
         g = self.gpu
-        g.append(kd, vd)
-        g.select(qd, want_kind=True, want_qscore=check_scores)
+        if self.fused:
+            g.append_select(kd, vd, qd, want_kind=True, want_qscore=check_scores)
+        else:
+            g.append(kd, vd)
+            g.select(qd, want_kind=True, want_qscore=check_scores)
         g.fetch()
         g.decode(qd)
         torch.cuda.synchronize()

@@ -46,12 +46,14 @@ def test_native_library_loaded():
     assert torch.cuda.is_available()
 
 
-def test_small_resident():
-    _run(small_workload(101))
+@pytest.mark.parametrize("fused", [False, True])
+def test_small_resident(fused):
+    _run(small_workload(101), fused=fused)
 
 
-def test_small_offload():
-    _run(small_workload(102, offload=True), cache_every=2)
+@pytest.mark.parametrize("fused", [False, True])
+def test_small_offload(fused):
+    _run(small_workload(102, offload=True), cache_every=2, fused=fused)
 
 
 def test_small_no_bias():
@@ -104,8 +106,9 @@ def test_tiny_decode_workload():
 
 def test_nosa1b_layer_all_pairs():
     """Full-size 1B-shaped layer (batch 32, 16K context, k = 64), the launch
-    configuration the benchmark times; every pair against the oracle."""
-    _run(WORKLOADS[2], steps=6)
+    configuration the benchmark times (append and select in one launch);
+    every pair against the oracle."""
+    _run(WORKLOADS[2], steps=6, fused=True)
 
 
 def test_nosa1b_layer_sampled_long():
@@ -177,7 +180,7 @@ def test_offload_128k_drift_sampled():
     """Offloaded 128K low-locality workload (8 sequences, 32/8 heads,
     k_q = k_e = 32) at full size: 4 sampled pairs against the oracle, fetched
     blocks equal the oracle's misses, cache bytes equal the host store."""
-    _run(WORKLOADS[5], check_pairs=[0, 21, 42, 63], steps=20, cache_every=5)
+    _run(WORKLOADS[5], check_pairs=[0, 21, 42, 63], steps=20, cache_every=5, fused=True)
 
 
 def test_offload_8b_64k_sampled():
@@ -188,3 +191,54 @@ def test_offload_8b_64k_sampled():
 def test_offload_1b_32k_layer_sampled():
     """One layer (layer 13) of the offloaded 28-layer 32K stack (64 sequences)."""
     _run(WORKLOADS[3], layer=13, check_pairs=[0, 77, 127], steps=8, cache_every=4)
+
+
+def _state_tensors(g):
+    names = ["seq_len", "arrive", "status", "ckey", "tok_s", "chunk_e", "blk_e",
+             "eligible", "tail_keys", "kv_dev", "kv_host", "slot_of_block", "block_of_slot"]
+    return {n: getattr(g, n) for n in names if getattr(g, n, None) is not None}
+
+
+@pytest.mark.parametrize("offload", [False, True])
+def test_append_select_equals_separate_calls(offload):
+    """nosa_append_select leaves the same state and returns the same selection,
+    bit for bit, as nosa_compress_append then nosa_select: 80 steps from a
+    1000-token context cross chunk completions every 16 tokens, block
+    completions, a block opening at 1024 and the window sliding by a block."""
+    wl = small_workload(121, context=1000, steps=80, offload=offload)
+    a = Lockstep(wl, check_pairs=[], lengths=[1000, 963])
+    b = Lockstep(wl, check_pairs=[], lengths=[1000, 963], fused=True)
+    for t in range(wl.steps):
+        kd, vd, qd = a.inputs(t)
+        a.gpu.append(kd, vd)
+        a.gpu.select(qd, want_kind=True, want_qscore=True)
+        b.gpu.append_select(kd, vd, qd, want_kind=True, want_qscore=True)
+        for ls in (a, b):
+            ls.gpu.fetch()
+        torch.cuda.synchronize()
+        for n in ("sel", "n_sel", "kind", "phys", "n_miss"):
+            assert torch.equal(getattr(a.gpu, n), getattr(b.gpu, n)), f"step {t}: {n}"
+        assert torch.equal(torch.nan_to_num(a.gpu.dbg_q, nan=-7.0),
+                           torch.nan_to_num(b.gpu.dbg_q, nan=-7.0)), f"step {t}: qscore"
+        sa, sb = _state_tensors(a.gpu), _state_tensors(b.gpu)
+        for n in sa:
+            assert torch.equal(sa[n], sb[n]), f"step {t}: state {n}"
+    assert a.gpu.status_bits() == 0 and b.gpu.status_bits() == 0
+
+
+def test_append_select_capacity_sets_status():
+    wl = small_workload(122, context=120, steps=8, n_hot=0)
+    ls = Lockstep(wl, steps=8, fused=True)
+    g = ls.gpu
+    for t in range(8):
+        kd, vd, qd = ls.inputs(t)
+        g.append_select(kd, vd, qd)
+    torch.cuda.synchronize()
+    assert g.status_bits() == 0
+    assert g.seq_len.cpu().tolist() == [128] * wl.batch
+    kd, vd, qd = ls.inputs(0)
+    g.max_len = g.shape.max_context - 1        # host bound stays in range
+    g.append_select(kd, vd, qd)
+    torch.cuda.synchronize()
+    assert g.status_bits() & 1
+    assert g.seq_len.cpu().tolist() == [128] * wl.batch

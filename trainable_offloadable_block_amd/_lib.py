@@ -86,6 +86,8 @@ def lib():
         "nosa_compress_append": (ctypes.c_int, [cfgp, stp, _P, _P, _I32, _P]),
         "nosa_select": (ctypes.c_int, [cfgp, stp, _P, _P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _I32, _P]),
+        "nosa_append_select": (ctypes.c_int, [cfgp, stp, _P, _P, _P, _P, _P, _P, _P, _P,
+                                              ctypes.c_size_t, _I32, _P]),
         "nosa_fetch_delta": (ctypes.c_int, [cfgp, stp, _P, _P, _P, _P, _P,
                                             ctypes.c_size_t, _P]),
         "nosa_sparse_decode": (ctypes.c_int, [cfgp, stp, _P, _P, _P, _P, _P,

@@ -180,6 +180,24 @@ int nosa_select(const nosa_config *cfg, const nosa_state *st, const uint16_t *q,
   return hip_result(nosa::launch_select(d, *st, q, sel, n_sel, kind, dbg_qscore, ws, lay, stream));
 }
 
+int nosa_append_select(const nosa_config *cfg, const nosa_state *st, const uint16_t *k_new,
+                       const uint16_t *v_new, const uint16_t *q, int32_t *sel, int32_t *n_sel,
+                       uint8_t *kind, float *dbg_qscore, void *ws, size_t ws_bytes,
+                       int32_t max_len_host, hipStream_t stream) {
+  nosa::Dims d;
+  int rc = make_dims(cfg, &d);
+  if (!rc) rc = check_state(d, st);
+  if (!rc) rc = check_len(d, max_len_host);
+  if (rc) return rc;
+  if (!k_new || !v_new) return fail(NOSA_ERR_INVALID, "k_new / v_new is NULL");
+  if (!q || !sel || !n_sel) return fail(NOSA_ERR_INVALID, "q / sel / n_sel is NULL");
+  const nosa::SelectLayout lay = nosa::select_layout(d, max_len_host);
+  rc = check_ws(ws, ws_bytes, lay.bytes);
+  if (rc) return rc;
+  return hip_result(nosa::launch_append_select(d, *st, k_new, v_new, q, sel, n_sel, kind,
+                                               dbg_qscore, ws, lay, stream));
+}
+
 int nosa_fetch_delta(const nosa_config *cfg, const nosa_state *st, const int32_t *sel,
                      const int32_t *n_sel, int32_t *phys, int32_t *n_miss, void *ws,
                      size_t ws_bytes, hipStream_t stream) {

@@ -6,58 +6,10 @@
 // stride 16, summed exactly in fp64 and rounded once to bf16 (NOSA-1B
 // 核心组件揭秘, 核心组件一). Block agnostic score: max over the chunks that
 // overlap a block of the per-chunk mean score (l189 article, 2.1, eqs. 5-6).
-#include "nosa_internal.h"
+#include "nosa_append_dev.h"
 
 namespace nosa {
 namespace {
-
-// One KV head's W1 (32 KiB bf16) for a 128-thread group: 16 independent
-// 16-byte loads per thread into registers, then into LDS (and a barrier).
-constexpr int kW1Vecs = kHeadDim * kHeadDim * 2 / 16 / 128;
-__device__ inline void load_w1(uint4 (&v)[kW1Vecs], const uint16_t *__restrict__ W1g) {
-  const uint4 *src = reinterpret_cast<const uint4 *>(W1g);
-#pragma unroll
-  for (int j = 0; j < kW1Vecs; ++j) v[j] = src[threadIdx.x + 128 * j];
-}
-__device__ inline void store_w1(uint16_t *w1_sh, const uint4 (&v)[kW1Vecs]) {
-  uint4 *dst = reinterpret_cast<uint4 *>(w1_sh);
-#pragma unroll
-  for (int j = 0; j < kW1Vecs; ++j) dst[threadIdx.x + 128 * j] = v[j];
-  __syncthreads();
-}
-__device__ void stage_w1(uint16_t *w1_sh, const uint16_t *__restrict__ W1g) {
-  uint4 v[kW1Vecs];
-  load_w1(v, W1g);
-  store_w1(w1_sh, v);
-}
-
-// s = softplus(v W1) W2 for one value vector held in LDS as fp32, with W1
-// staged in LDS. Called by all 128 threads of a group; thread t owns hidden
-// unit t. The summation order is fixed (e ascending, then a fixed reduction
-// tree), so every caller gets the same bits for the same v.
-__device__ float evict_score_128(const float *v_sh, const uint16_t *w1_sh,
-                                 const uint16_t *__restrict__ W2g, float *red2) {
-  const int t = threadIdx.x & 127;
-  float acc = 0.0f;
-#pragma unroll 16
-  for (int e = 0; e < kHeadDim; ++e)
-    acc = fmaf(v_sh[e], bf16_to_f32(w1_sh[e * kHeadDim + t]), acc);
-  float x = softplus_f32(acc) * bf16_to_f32(W2g[t]);
-  x = wave_sum(x);
-  __syncthreads();                       // red2 may still be read by a caller
-  if ((t & 63) == 0) red2[t >> 6] = x;
-  __syncthreads();
-  return red2[0] + red2[1];
-}
-
-// Zeroes one 32 KiB block with the workgroup's 128 threads; the barrier
-// orders the zeros before the caller's token writes into the same block.
-__device__ void clear_block(uint16_t *blk) {
-  uint4 *b4 = reinterpret_cast<uint4 *>(blk);
-  for (int i = threadIdx.x; i < kBlockElems * 2 / 16; i += blockDim.x) b4[i] = make_uint4(0, 0, 0, 0);
-  __threadfence_block();
-  __syncthreads();
-}
 
 // ------------------------------------------------------------- append
 // grid (Hkv, B), block 128: one pair per workgroup, thread t = dim t.
@@ -65,120 +17,16 @@ __global__ __launch_bounds__(128) void append_kernel(
     Dims d, nosa_state st, const uint16_t *__restrict__ k_new,
     const uint16_t *__restrict__ v_new) {
   const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const int p = b * d.Hkv + g;
-  __shared__ float v_sh[kHeadDim];
-  __shared__ uint16_t k_sh[kHeadDim];
-  __shared__ float red2[2];
-  __shared__ int slot_sh;
-  __shared__ __align__(16) uint16_t w1_sh[kHeadDim * kHeadDim];
-
-  // loads that do not depend on the length first, so the kernel waits for
-  // one memory round trip: the new key and value, this head's W1
-  // (both go to LDS before the barrier, so neither load sinks into the
-  // branch below, where they are used)
-  const uint16_t kb_ld = k_new[p * kHeadDim + t];
-  const uint16_t vb = v_new[p * kHeadDim + t];
+  __shared__ AppendLds sh;
   const int pos = st.seq_len[b];
-  {
-    uint4 w1v[kW1Vecs];
-    load_w1(w1v, st.w1 + (size_t)g * kHeadDim * kHeadDim);
-    v_sh[t] = bf16_to_f32(vb);
-    k_sh[t] = kb_ld;
-    store_w1(w1_sh, w1v);                // ends in a barrier
-  }
-  const uint16_t kb = k_sh[t];
-  const bool ok = pos >= 0 && pos < d.max_context;
-  if (ok) {
-    const int L = pos + 1;
-    const int blk = pos / kBlock, r = pos % kBlock;
-
-    // 1. store K, V (K row-major, V in the block's tile order)
-    if (!d.offload) {
-      uint16_t *base = st.kv_dev + ((size_t)p * d.NB_max + blk) * kBlockElems;
-      if (r == 0) clear_block(base);
-      base[r * kHeadDim + t] = kb;
-      base[kBlock * kHeadDim + v_index(r, t)] = vb;
-    } else {
-      uint16_t *hb = st.kv_host + ((size_t)p * d.NB_max + blk) * kBlockElems;
-      hb[r * kHeadDim + t] = kb;
-      hb[kBlock * kHeadDim + v_index(r, t)] = vb;
-      int32_t *sob = st.slot_of_block + (size_t)p * d.NB_max;
-      int32_t *bos = st.block_of_slot + (size_t)p * (d.k + 1);
-      if (t == 0) slot_sh = sob[blk];
-      __syncthreads();
-      int slot = slot_sh;
-      if (slot < 0 && r == 0) {          // this token opens a block: cache it
-        __syncthreads();
-        if (t == 0) slot_sh = 0x7fffffff;
-        __syncthreads();
-        for (int s = t; s <= d.k; s += blockDim.x)
-          if (bos[s] < 0) atomicMin(&slot_sh, s);
-        __syncthreads();
-        slot = slot_sh == 0x7fffffff ? -1 : slot_sh;
-        if (t == 0) {
-          if (slot >= 0) {
-            bos[slot] = blk;
-            sob[blk] = slot;
-          } else {
-            atomicOr(st.status, NOSA_STATUS_BAD_SEL);
-          }
-        }
-      }
-      if (slot >= 0) {
-        uint16_t *cb = st.kv_dev + ((size_t)p * (d.k + 1) + slot) * kBlockElems;
-        if (r == 0) clear_block(cb);
-        cb[r * kHeadDim + t] = kb;
-        cb[kBlock * kHeadDim + v_index(r, t)] = vb;
-      }
-    }
-
-    // 2. ring of the last 32 keys (feeds the chunk mean)
-    uint16_t *ring = st.tail_keys + (size_t)p * kPoolKernel * kHeadDim;
-    ring[(pos % kPoolKernel) * kHeadDim + t] = kb;
-
-    // 3. eviction score of the new token
-    const float s = evict_score_128(v_sh, w1_sh, st.w2 + (size_t)g * kHeadDim, red2);
-    float *tok_s = st.tok_s + (size_t)p * d.tok_stride;
-    if (t == 0) tok_s[pos] = s;
-
-    // 4. a chunk completes when L >= 32 and (L - 32) % 16 == 0
-    if (L >= kPoolKernel && (L - kPoolKernel) % kPoolStride == 0) {
-      const int i = (L - kPoolKernel) / kPoolStride;
-      double sum = 0.0;                  // exact for bf16 inputs of sane range
-      for (int j = 0; j < kPoolKernel; ++j) {
-        const int tok = pos - (kPoolKernel - 1) + j;
-        const uint16_t kv = tok == pos ? kb : ring[(tok % kPoolKernel) * kHeadDim + t];
-        sum += (double)bf16_to_f32(kv);
-      }
-      st.ckey[((size_t)p * d.C_max + i) * kHeadDim + t] =
-          f64_to_bf16_rne(sum * (1.0 / kPoolKernel));
-      if (t < 64) {                      // wave 0: mean eviction score
-        double se = 0.0;
-        if (t < kPoolKernel) {
-          const int tok = pos - (kPoolKernel - 1) + t;
-          se = tok == pos ? (double)s : (double)tok_s[tok];
-        }
-        se = wave_sum(se);
-        if (t == 0) {
-          const float em = (float)(se * (1.0 / kPoolKernel));
-          float *ce = st.chunk_e + (size_t)p * d.C_max;
-          ce[i] = em;
-          if (i % 4 == 3) {              // block (i-3)/4 now has all chunks
-            const int bb = (i - 3) / 4;
-            float m = em;
-            for (int c = (bb > 0 ? 4 * bb - 1 : 0); c < i; ++c) m = fmaxf(m, ce[c]);
-            st.blk_e[(size_t)p * d.NB_max + bb] = m;
-          }
-        }
-      }
-    }
-  }
+  append_pair<128>(d, st, k_new, v_new, b, g, pos, false, sh);
   // last workgroup of this sequence advances its length. Every workgroup
   // has consumed seq_len[b] (all its addresses depend on it) before it
   // arrives, so no fence is needed (a device-scope fence would write back
   // the XCD's whole L2).
   __syncthreads();
   if (t == 0) {
+    const bool ok = pos >= 0 && pos < d.max_context;
     if (!ok) atomicOr(st.status, NOSA_STATUS_CAPACITY);
     const int old = atomicAdd(&st.arrive[b], 1);
     if (old == d.Hkv - 1) {

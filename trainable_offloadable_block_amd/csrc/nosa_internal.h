@@ -18,6 +18,7 @@ struct SelectLayout {
   size_t e_off, stats_off, count_off, bytes;   // count: per-pair arrivals, zero at rest
 };
 SelectLayout select_layout(const Dims &d, int max_len);
+size_t select_dyn_lds(const Dims &d, const SelectLayout &lay);   // pooling's dynamic LDS
 
 // --- fetch workspace: per-pair copy list of (block, slot).
 struct FetchLayout {
@@ -42,6 +43,11 @@ hipError_t launch_select(const Dims &d, const nosa_state &st,
                          const uint16_t *q, int32_t *sel, int32_t *n_sel,
                          uint8_t *kind, float *dbg_qscore, void *ws,
                          const SelectLayout &lay, hipStream_t s);
+hipError_t launch_append_select(const Dims &d, const nosa_state &st,
+                                const uint16_t *k_new, const uint16_t *v_new,
+                                const uint16_t *q, int32_t *sel, int32_t *n_sel,
+                                uint8_t *kind, float *dbg_qscore, void *ws,
+                                const SelectLayout &lay, hipStream_t s);
 hipError_t launch_fetch(const Dims &d, const nosa_state &st,
                         const int32_t *sel, const int32_t *n_sel,
                         int32_t *phys, int32_t *n_miss, void *ws,

@@ -14,579 +14,10 @@
 //    workgroup top-k by histogram range refinement, writes the ascending
 //    selection and clears the eligibility of every candidate left out (never
 //    re-selected by the agnostic stage).
-#include "nosa_internal.h"
+#include "nosa_select_dev.h"
 
 namespace nosa {
 namespace {
-
-constexpr int kScoreThreads = 256;
-constexpr int kTopkThreads = 256;
-
-// MFMA 16x16x32 (bf16 -> fp32) operand mapping used here and in decode:
-//  A (16 rows x 32 k): lane l gives row (l % 16), 8 k-values of group l / 16
-//  B (32 k x 16 cols): lane l gives col (l % 16), 8 k-values of group l / 16
-//  D (16 x 16):        lane l holds rows 4*(l/16) + i, i = 0..3, col l % 16
-// Dot products only need A and B to assign the same k to the same
-// (lane group, slot), which holds by construction. Rows of A are permuted
-// so that, over two tiles, lane group j holds 8 consecutive rows (chunks):
-// tile t, A-row r  <->  row 8*(r/4) + 4*t + (r%4) of the 32-row group.
-__device__ inline int tile_row(int r, int t) { return 8 * (r >> 2) + 4 * t + (r & 3); }
-
-// Heads per chunk in the chunk-weight layout: the group padded to 4, 8 or 16
-// so that one 16-byte load never straddles two chunks.
-__host__ __device__ inline int padded_group(int G) { return G <= 4 ? 4 : (G <= 8 ? 8 : 16); }
-
-// Device-coherent (agent-scope) stores and loads: how the score workgroups
-// of a pair hand their results to the pair's last workgroup without a
-// device-scope fence (which would write back the XCD's whole L2).
-__device__ inline void put(float *a, float v) {
-  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline float get(const float *a) {
-  return __hip_atomic_load(const_cast<float *>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-constexpr int kCoherent = 16;   // buffer-load cache policy: sc1, as the agent-scope loads
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-__device__ inline float4 load4_coherent(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCoherent));
-}
-__device__ inline float2 load2_coherent(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kCoherent));
-}
-
-// Split `split` of pair p: logits of the group against this split's
-// compressed keys, published with device-coherent stores.
-__device__ __forceinline__ void score_split(const Dims &d, const int32_t *__restrict__ seq_len,
-                                            const uint16_t *__restrict__ ckey,
-                                            const uint16_t *__restrict__ q, float *ws_e,
-                                            float *ws_stats, int c_pad, int n_splits, int split,
-                                            int p) {
-  const int b = p / d.Hkv, g = p % d.Hkv;
-  const int c0 = split * kChunksPerSplit;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int h = l & 15, lg = l >> 4;
-  __shared__ float red_m[4][16], red_z[4][16];
-  // the query rows and every stored compressed key of this split's chunks
-  // are loaded before the length is known (rows past it are masked below),
-  // so the kernel waits for one memory round trip
-  const int cg = c0 + 32 * w;
-  uint4 qv[4], kv[2][4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) qv[s] = make_uint4(0, 0, 0, 0);
-  if (h < d.G) {
-    const uint16_t *qh = q + ((size_t)b * d.Hq + g * d.G + h) * kHeadDim + 8 * lg;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qv[s] = *reinterpret_cast<const uint4 *>(qh + 32 * s);
-  }
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int chunk = cg + tile_row(l & 15, t);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) kv[t][s] = make_uint4(0, 0, 0, 0);
-    if (chunk < d.C_max) {
-      const uint16_t *src = ckey + ((size_t)p * d.C_max + chunk) * kHeadDim + 8 * lg;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kv[t][s] = *reinterpret_cast<const uint4 *>(src + 32 * s);
-    }
-  }
-  const int C = min(chunks_for(seq_len[b]), d.C_max);
-  float *stats = ws_stats + (size_t)2 * (p * n_splits + split) * d.G;   // (M, Z) per head
-  if (c0 >= C) {
-    if (threadIdx.x < d.G) {
-      put(&stats[2 * threadIdx.x], -INFINITY);
-      put(&stats[2 * threadIdx.x + 1], 0.0f);
-    }
-    return;
-  }
-  // logits on MFMA; a row past the length only feeds its own (masked) output
-  f32x4 acc[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc[t] = mfma16x16x32(as_bf16x8(kv[t][s]), as_bf16x8(qv[s]), acc[t]);
-  }
-  // lane (h, lg) now holds head h against chunks cg + 8*lg + m, m = 0..7
-  const float scale = 0.08838834764831845f;   // 1/sqrt(128)
-  float x[8];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int c = cg + 8 * lg + m;
-    x[m] = c < C ? acc[m >> 2][m & 3] * scale : -INFINITY;
-    mx = fmaxf(mx, x[m]);
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  if (lg == 0) red_m[w][h] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
-  float ev[8];
-  float z = 0.0f;
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    ev[m] = x[m] == -INFINITY ? 0.0f : expf(x[m] - M);
-    z += ev[m];
-  }
-  z += __shfl_xor(z, 16, 64);
-  z += __shfl_xor(z, 32, 64);
-  if (lg == 0) red_z[w][h] = z;
-  const int Gp = padded_group(d.G);
-  if (h < Gp) {                                    // chunk-major [c][Gp], pad = 0
-    float *dst = ws_e + ((size_t)p * c_pad + cg + 8 * lg) * Gp + h;
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-      if (cg + 8 * lg + m < C) put(&dst[m * Gp], h < d.G ? ev[m] : 0.0f);
-  }
-  __syncthreads();
-  if (threadIdx.x < d.G) {
-    const int hh = threadIdx.x;
-    const float Mh = fmaxf(fmaxf(red_m[0][hh], red_m[1][hh]), fmaxf(red_m[2][hh], red_m[3][hh]));
-    const float Zh = (red_z[0][hh] + red_z[1][hh]) + (red_z[2][hh] + red_z[3][hh]);
-    put(&stats[2 * hh], Mh);
-    put(&stats[2 * hh + 1], Zh);
-  }
-}
-
-// ---- workgroup top-k on 64-bit composite keys ----------------------------
-// A key is (order_key(score) << 32) | ~block: larger score first, then the
-// lower block id; keys are distinct and 0 marks "not a candidate".
-
-__device__ inline uint64_t compose_key(float score, int blk) {
-  return (static_cast<uint64_t>(order_key(score)) << 32) |
-         static_cast<uint32_t>(0xFFFFFFFFu - static_cast<uint32_t>(blk));
-}
-
-// DPP lane exchange inside a row of 16 lanes: xor 1, xor 2 (quad
-// permutations), then the mirrors of 8 and 16 lanes; for min / max / sum
-// any pairing that joins the two halves serves.
-template <int CTRL>
-__device__ inline uint32_t dpp32(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, true));
-}
-template <int CTRL>
-__device__ inline uint64_t dpp64(uint64_t v) {
-  return (static_cast<uint64_t>(dpp32<CTRL>(static_cast<uint32_t>(v >> 32))) << 32) |
-         dpp32<CTRL>(static_cast<uint32_t>(v));
-}
-template <int CTRL>
-__device__ inline void row_step(uint64_t &mn, uint64_t &mx, uint32_t &c) {
-  const uint64_t a = dpp64<CTRL>(mn), b = dpp64<CTRL>(mx);
-  mn = a < mn ? a : mn;
-  mx = b > mx ? b : mx;
-  c += dpp32<CTRL>(c);
-}
-
-__device__ inline uint64_t readlane_u64(uint64_t v, int l) {
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(v), l);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), l);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-// Inclusive prefix sum over the 64 lanes: DPP row shifts inside each row of
-// 16 lanes, then the row totals (lanes 15, 31, 47) carried forward.
-__device__ inline uint32_t wave_incl_scan(uint32_t x) {
-  x += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x111, 0xF, 0xF, true));
-  x += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x112, 0xF, 0xF, true));
-  x += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x114, 0xF, 0xF, true));
-  x += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x118, 0xF, 0xF, true));
-  const uint32_t r0 = __builtin_amdgcn_readlane(static_cast<int>(x), 15);
-  const uint32_t r1 = __builtin_amdgcn_readlane(static_cast<int>(x), 31);
-  const uint32_t r2 = __builtin_amdgcn_readlane(static_cast<int>(x), 47);
-  const int row = (threadIdx.x & 63) >> 4;
-  return x + (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
-}
-
-constexpr int kTopkBits = 8, kTopkBins = 1 << kTopkBits;   // bins per refinement round
-
-struct __align__(16) TopkLds {
-  uint32_t hist[2][kTopkBins];
-  uint64_t mn[2][kTopkThreads / 64], mx[2][kTopkThreads / 64];
-  uint32_t cnt[2][kTopkThreads / 64];
-};
-
-// Marks kind[bb0 + t + 256 r] = val for the k largest nonzero keys of the
-// workgroup (thread t holds the keys of candidates t + 256 r, r < R).
-// Exact selection by range refinement: each round histograms the active keys
-// into 256 bins over [min, max] (the top 8 bits of their spread), keeps every
-// key above the bin holding the k-th largest, drops those below it, and goes
-// on inside that bin; a bin whose keys are all wanted ends it. The spread
-// shrinks by 8 bits per round, so 64-bit keys need at most 8 rounds.
-// hist[0] must be zero on entry; both are zero again on return. Called by
-// all threads; the caller syncs before reading kind.
-template <int R>
-__device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0, uint8_t *kind, uint8_t val,
-                        TopkLds &sh) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  bool act[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) act[r] = key[r] != 0;
-  int need = k;
-  for (int round = 0; need > 0 && round < 9; ++round) {    // uniform; <= 8 refinements
-    const int par = round & 1;
-    uint64_t mn = ~0ull, mx = 0;
-    uint32_t c = 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (act[r]) {
-        mn = key[r] < mn ? key[r] : mn;
-        mx = key[r] > mx ? key[r] : mx;
-        ++c;
-      }
-    row_step<0xB1>(mn, mx, c);            // quad_perm [1,0,3,2]
-    row_step<0x4E>(mn, mx, c);            // quad_perm [2,3,0,1]
-    row_step<0x141>(mn, mx, c);           // row_half_mirror
-    row_step<0x140>(mn, mx, c);           // row_mirror
-    {
-      uint64_t wm = readlane_u64(mn, 0), wx = readlane_u64(mx, 0);
-      uint32_t wc = __builtin_amdgcn_readlane(static_cast<int>(c), 0);
-#pragma unroll
-      for (int row = 1; row < 4; ++row) {
-        const uint64_t a = readlane_u64(mn, 16 * row), b = readlane_u64(mx, 16 * row);
-        wm = a < wm ? a : wm;
-        wx = b > wx ? b : wx;
-        wc += __builtin_amdgcn_readlane(static_cast<int>(c), 16 * row);
-      }
-      if (lane == 0) {
-        sh.mn[par][w] = wm;
-        sh.mx[par][w] = wx;
-        sh.cnt[par][w] = wc;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kTopkBins / kTopkThreads; ++i)         // next round's bins
-      sh.hist[par ^ 1][t + kTopkThreads * i] = 0;
-    mn = ~0ull;
-    mx = 0;
-    c = 0;
-#pragma unroll
-    for (int i = 0; i < kTopkThreads / 64; ++i) {
-      const uint64_t a = sh.mn[par][i], b = sh.mx[par][i];
-      mn = a < mn ? a : mn;
-      mx = b > mx ? b : mx;
-      c += sh.cnt[par][i];
-    }
-    if (c <= static_cast<uint32_t>(need)) {                  // uniform: take them all
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-        if (act[r]) kind[bb0 + t + kTopkThreads * r] = val;
-      break;
-    }
-    const int span = mx > mn ? 64 - __builtin_clzll(mx - mn) : 0;   // c >= 2 distinct keys
-    const int shift = span > kTopkBits ? span - kTopkBits : 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (act[r]) atomicAdd(&sh.hist[par][(key[r] - mn) >> shift], 1u);
-    __syncthreads();
-    // bin holding the need-th largest: lane l sums the BPL bins below
-    // kTopkBins - BPL l, a prefix over lanes counts from the top
-    constexpr int BPL = kTopkBins / 64;
-    uint32_t hb[BPL], s4 = 0;
-    {
-      const uint4 *hv = reinterpret_cast<const uint4 *>(&sh.hist[par][kTopkBins - BPL * (lane + 1)]);
-#pragma unroll
-      for (int i = 0; i < BPL / 4; ++i) {
-        const uint4 v = hv[BPL / 4 - 1 - i];     // descending bin order
-        hb[4 * i] = v.w;
-        hb[4 * i + 1] = v.z;
-        hb[4 * i + 2] = v.y;
-        hb[4 * i + 3] = v.x;
-      }
-#pragma unroll
-      for (int i = 0; i < BPL; ++i) s4 += hb[i];
-    }
-    const uint32_t incl = wave_incl_scan(s4);
-    const uint64_t hit = __ballot(incl >= static_cast<uint32_t>(need));
-    const int ls = __builtin_ctzll(hit);                     // exists: total c > need
-    int bstar = 0;
-    uint32_t above = incl - s4, inbin = 0;
-    {
-      bool found = false;
-#pragma unroll
-      for (int i = 0; i < BPL; ++i) {
-        if (!found && above + hb[i] >= static_cast<uint32_t>(need)) {
-          bstar = kTopkBins - 1 - BPL * lane - i;
-          inbin = hb[i];
-          found = true;
-        } else if (!found) {
-          above += hb[i];
-        }
-      }
-    }
-    bstar = __builtin_amdgcn_readlane(bstar, ls);
-    above = __builtin_amdgcn_readlane(static_cast<int>(above), ls);
-    inbin = __builtin_amdgcn_readlane(static_cast<int>(inbin), ls);
-    const int rest = need - static_cast<int>(above);
-    const bool all_in = inbin == static_cast<uint32_t>(rest);
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (act[r]) {
-        const int bin = static_cast<int>((key[r] - mn) >> shift);
-        if (bin > bstar || (bin == bstar && all_in)) {
-          kind[bb0 + t + kTopkThreads * r] = val;
-          act[r] = false;
-        } else if (bin < bstar) {
-          act[r] = false;
-        }
-      }
-    if (all_in) break;                                       // uniform
-    need = rest;
-  }
-  // leave both histograms zero for the next call
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kTopkBins / kTopkThreads; ++i) {
-    sh.hist[0][t + kTopkThreads * i] = 0;
-    sh.hist[1][t + kTopkThreads * i] = 0;
-  }
-}
-
-// Query-aware score of block bb: max over its overlapping chunks
-// 4bb-1 .. 4bb+3 of the chunk score a_c.
-__device__ inline float block_qscore(const float *a_sh, int bb, int C) {
-  float qb = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 5; ++j) {
-    const int c = 4 * bb - 1 + j;
-    if (c >= 0 && c < C) qb = fmaxf(qb, a_sh[c]);
-  }
-  return qb;
-}
-
-// Both selection stages with R candidate slots per thread (candidate
-// t + 256 r, block n_sink + t + 256 r). Stage 1: the k_q candidates of
-// highest query-aware score; stage 2: the k_e' eligible candidates of highest
-// agnostic score among the rest.
-template <int R>
-__device__ __forceinline__ void select_stages(const Dims &d, int p, int n_cand, int C, bool do_q, bool do_e,
-                              const float *a_sh, const uint32_t *el_sh, const float *be,
-                              float e0, uint8_t *kind, float *dbg, TopkLds &tk) {
-  const int t = threadIdx.x;
-  if (do_q) {
-    uint64_t kq[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int i = t + kTopkThreads * r, bb = d.n_sink + i;
-      kq[r] = 0;
-      if (i < n_cand) {
-        const float qb = block_qscore(a_sh, bb, C);
-        kq[r] = compose_key(qb, bb);
-        if (dbg) dbg[(size_t)p * d.NB_max + bb] = qb;
-      }
-    }
-    wg_topk(kq, d.k_q, d.n_sink, kind, NOSA_KIND_QUERY, tk);
-    __syncthreads();
-  }
-  if (do_e) {
-    uint64_t ke[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int i = t + kTopkThreads * r, bb = d.n_sink + i;
-      ke[r] = 0;
-      if (i < n_cand && ((el_sh[bb >> 5] >> (bb & 31)) & 1u) && kind[bb] != NOSA_KIND_QUERY)
-        ke[r] = compose_key(r == 0 ? e0 : be[bb], bb);
-    }
-    wg_topk(ke, d.k_e_dyn, d.n_sink, kind, NOSA_KIND_AGNOSTIC, tk);
-  }
-}
-
-constexpr int kMaxCandPerThread = (kMaxContext / kBlock) / kTopkThreads;   // 16
-constexpr int kLoadBatch = 8;     // chunk-weight float4 loads in flight per thread
-
-// Pooling and both stages for pair p, run by the pair's last score
-// workgroup once every split has published (so the chunk weights and split
-// statistics are read with device-coherent loads).
-__device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
-                                            const float *ws_e, const float *ws_stats,
-                                            int c_pad, int n_splits, int32_t *sel,
-                                            int32_t *n_sel, uint8_t *kind_out, float *dbg,
-                                            int p) {
-  const int Gp = padded_group(d.G);
-  extern __shared__ __align__(16) uint8_t smem[];
-  float *f_sh = reinterpret_cast<float *>(smem);                            // [n_splits][Gp]
-  float *a_sh = f_sh + n_splits * Gp;                                       // [c_pad]
-  uint32_t *el_sh = reinterpret_cast<uint32_t *>(a_sh + c_pad);             // [elig_words]
-  uint8_t *kind = reinterpret_cast<uint8_t *>(el_sh + d.elig_words);        // [NB_max]
-  __shared__ TopkLds tk;
-  __shared__ int cnt_sh[2][kTopkThreads / 64];
-
-  const int t = threadIdx.x;
-  const int w = t >> 6, lane = t & 63;
-  const int b = p / d.Hkv;
-
-  // 0. issue the global loads together, bounded by the buffers' extents
-  // rather than the length (which is itself being loaded), so the kernel
-  // waits for one memory round trip: the first batch of chunk weights
-  // (coalesced float4s of the chunk-major [c][Gp] array), split statistics,
-  // the candidates' agnostic scores, eligibility
-  const int n4_ext = c_pad * Gp / 4;
-  const __amdgpu_buffer_rsrc_t er = make_rsrc(ws_e + (size_t)p * c_pad * Gp, (uint32_t)n4_ext * 16);
-  float4 eb[kLoadBatch];
-#pragma unroll
-  for (int u = 0; u < kLoadBatch; ++u) {
-    const int k4 = t + kTopkThreads * u;
-    eb[u] = k4 < n4_ext ? load4_coherent(er, 16 * k4) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  const float *be = st.blk_e + (size_t)p * d.NB_max;
-  const float e0_raw = d.n_sink + t < d.NB_max ? be[d.n_sink + t] : 0.0f;
-  const int sh_h = t >> 4, sh_j = t & 15;
-  const __amdgpu_buffer_rsrc_t sr =
-      make_rsrc(ws_stats + (size_t)2 * p * n_splits * d.G, (uint32_t)n_splits * d.G * 8);
-  float2 stv_raw = make_float2(-INFINITY, 0.0f);
-  if (sh_h < d.G && sh_j < n_splits) stv_raw = load2_coherent(sr, 8 * (sh_j * d.G + sh_h));
-
-  const int L = max(0, min(st.seq_len[b], d.max_context));
-  int C = chunks_for(L);
-  if (C > c_pad) {                      // caller's length bound was too small
-    if (t == 0) atomicOr(st.status, NOSA_STATUS_LEN_HINT);
-    C = c_pad;
-  }
-  const int nb = blocks_for(L);
-  const int win_lo = max(d.n_sink, nb - d.n_win);
-  const int n_cand = max(0, win_lo - d.n_sink);
-  const int used = (C + kChunksPerSplit - 1) / kChunksPerSplit;
-  const bool do_q = d.k_q > 0 && n_cand > 0, do_e = d.k_e_dyn > 0 && n_cand > 0;
-  const int n4 = do_q ? C * Gp / 4 : 0;
-  const bool have0 = t < n_cand;
-  const float e0 = (do_e && have0) ? e0_raw : 0.0f;
-  const float2 stv = (do_q && sh_h < d.G && sh_j < used) ? stv_raw : make_float2(-INFINITY, 0.0f);
-  for (int i = t; i < d.elig_words; i += kTopkThreads)
-    el_sh[i] = st.eligible[(size_t)p * d.elig_words + i];
-  for (int bb = t; bb < nb; bb += kTopkThreads)
-    kind[bb] = bb < d.n_sink ? NOSA_KIND_SINK : (bb >= win_lo ? NOSA_KIND_WINDOW : NOSA_KIND_NONE);
-#pragma unroll
-  for (int i = 0; i < kTopkBins / kTopkThreads; ++i) {
-    tk.hist[0][t + kTopkThreads * i] = 0;
-    tk.hist[1][t + kTopkThreads * i] = 0;
-  }
-
-  // 1. per-split factors exp(m_split - M) / Z of each head's softmax (0 for
-  // the padding heads)
-  if (do_q && sh_h < Gp) {
-    const bool real = sh_h < d.G;
-    float m = stv.x;
-    if (real)
-      for (int s = sh_j + 16; s < used; s += 16) m = fmaxf(m, load2_coherent(sr, 8 * (s * d.G + sh_h)).x);
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    const float e0s = stv.y > 0.0f ? expf(stv.x - m) : 0.0f;
-    float z = stv.y * e0s;
-    if (real)
-      for (int s = sh_j + 16; s < used; s += 16) {
-        const float2 v = load2_coherent(sr, 8 * (s * d.G + sh_h));
-        if (v.y > 0.0f) z += v.y * expf(v.x - m);
-      }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
-    const float rz = real ? 1.0f / z : 0.0f;
-    if (sh_j < used) f_sh[sh_j * Gp + sh_h] = e0s * rz;
-    for (int s = sh_j + 16; s < used; s += 16) {
-      const float2 v = real ? load2_coherent(sr, 8 * (s * d.G + sh_h)) : make_float2(-INFINITY, 0.0f);
-      f_sh[s * Gp + sh_h] = v.y > 0.0f ? expf(v.x - m) * rz : 0.0f;
-    }
-  }
-  __syncthreads();
-
-  // 2. chunk scores a_c = sum over the group's heads of the head's softmax
-  // weight, once per chunk (a chunk shared by two blocks gives both the same
-  // value): each float4 covers 4 heads of one chunk, the Gp / 4 lanes of a
-  // chunk are adjacent and combine with lane exchanges
-  if (do_q) {
-    const int lpc = Gp / 4;                          // lanes per chunk: 1, 2, 4
-    for (int k0 = 0; k0 < n4; k0 += kTopkThreads * kLoadBatch) {     // uniform
-      if (k0 > 0) {
-#pragma unroll
-        for (int u = 0; u < kLoadBatch; ++u) {
-          const int k4 = k0 + t + kTopkThreads * u;
-          eb[u] = k4 < n4 ? load4_coherent(er, 16 * k4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kLoadBatch; ++u) {
-        const int k4 = k0 + t + kTopkThreads * u;
-        const int c = k4 / lpc, h0 = 4 * (k4 % lpc);
-        float a = 0.0f;
-        if (k4 < n4) {
-          const float *fs = f_sh + (c / kChunksPerSplit) * Gp + h0;
-          a = eb[u].x * fs[0];
-          a = fmaf(eb[u].y, fs[1], a);
-          a = fmaf(eb[u].z, fs[2], a);
-          a = fmaf(eb[u].w, fs[3], a);
-        }
-        if (lpc >= 2) a += __shfl_xor(a, 1, 64);
-        if (lpc >= 4) a += __shfl_xor(a, 2, 64);
-        if (k4 < n4 && h0 == 0) a_sh[c] = a;
-      }
-    }
-  }
-  __syncthreads();
-
-  // 3. both stages, with as many candidate slots per thread as needed
-  {
-    const int m = (n_cand + kTopkThreads - 1) / kTopkThreads;   // <= kMaxCandPerThread
-    if (m <= 1)
-      select_stages<1>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
-    else if (m <= 2)
-      select_stages<2>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
-    else if (m <= 4)
-      select_stages<4>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
-    else if (m <= 8)
-      select_stages<8>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
-    else
-      select_stages<kMaxCandPerThread>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind,
-                                       dbg, tk);
-  }
-  __syncthreads();
-
-  // 4. ascending selection list: ballot + prefix count per 256 blocks
-  {
-    int32_t *sp = sel + (size_t)p * d.k;
-    uint8_t *kp = kind_out ? kind_out + (size_t)p * d.k : nullptr;
-    int running = 0;
-    for (int base = 0; base < nb; base += kTopkThreads) {            // uniform
-      const int bb = base + t;
-      const bool in = bb < nb && kind[bb] != NOSA_KIND_NONE;
-      const uint64_t mask = __ballot(in);
-      const int below = __popcll(mask & ((1ull << lane) - 1ull));
-      if (lane == 0) cnt_sh[(base / kTopkThreads) & 1][w] = __popcll(mask);
-      __syncthreads();
-      const int *cs = cnt_sh[(base / kTopkThreads) & 1];
-      int off = running, tot = 0;
-#pragma unroll
-      for (int ww = 0; ww < kTopkThreads / 64; ++ww) {
-        if (ww < w) off += cs[ww];
-        tot += cs[ww];
-      }
-      off += below;
-      if (in && off < d.k) {
-        sp[off] = bb;
-        if (kp) kp[off] = kind[bb];
-      }
-      running += tot;
-    }
-    for (int j = running + t; j < d.k; j += kTopkThreads) {
-      sp[j] = -1;
-      if (kp) kp[j] = NOSA_KIND_NONE;
-    }
-    if (t == 0) n_sel[p] = min(running, d.k);
-  }
-
-  // 5. eligibility: a candidate outside the selection is out for good
-  if (n_cand > 0) {
-    uint32_t *el = st.eligible + (size_t)p * d.elig_words;
-    for (int base = 64 * w; base < win_lo; base += kTopkThreads) {   // wave-uniform
-      const int bb = base + lane;
-      const bool out = bb >= d.n_sink && bb < win_lo && kind[bb] == NOSA_KIND_NONE;
-      const uint64_t mask = __ballot(out);
-      const uint32_t clear = static_cast<uint32_t>(mask >> (lane & 32));
-      if ((lane & 31) == 0 && clear) el[bb >> 5] = el_sh[bb >> 5] & ~clear;
-    }
-  }
-}
 
 // grid (splits, pairs): every workgroup scores its split and arrives on the
 // pair's counter once its results have landed; the last one pools and
@@ -597,7 +28,10 @@ __global__ __launch_bounds__(kScoreThreads) void select_kernel(
     int32_t *__restrict__ n_sel, uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
   const int split = blockIdx.x, p = blockIdx.y;
   __shared__ int sm_last;
-  score_split(d, st.seq_len, st.ckey, q, ws_e, ws_stats, c_pad, n_splits, split, p);
+  ScoreIn in;
+  score_load(d, st.ckey, q, split, p, in);
+  const int L = st.seq_len[p / d.Hkv];
+  score_compute(d, L, in, -1, nullptr, ws_e, ws_stats, c_pad, n_splits, split, p);
   __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
   __syncthreads();
   if (threadIdx.x == 0)
@@ -605,7 +39,7 @@ __global__ __launch_bounds__(kScoreThreads) void select_kernel(
               n_splits - 1;
   __syncthreads();
   if (!sm_last) return;
-  pool_select(d, st, ws_e, ws_stats, c_pad, n_splits, sel, n_sel, kind_out, dbg, p);
+  pool_select(d, st, L, ws_e, ws_stats, c_pad, n_splits, sel, n_sel, kind_out, dbg, p);
   if (threadIdx.x == 0) __hip_atomic_store(&ws_count[p], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -623,6 +57,11 @@ SelectLayout select_layout(const Dims &d, int max_len) {
   return s;
 }
 
+size_t select_dyn_lds(const Dims &d, const SelectLayout &lay) {
+  return ((size_t)lay.n_splits * padded_group(d.G) + lay.c_pad) * sizeof(float) +
+         (size_t)d.elig_words * sizeof(uint32_t) + (size_t)d.NB_max;
+}
+
 hipError_t launch_select(const Dims &d, const nosa_state &st, const uint16_t *q,
                          int32_t *sel, int32_t *n_sel, uint8_t *kind, float *dbg,
                          void *ws, const SelectLayout &lay, hipStream_t s) {
@@ -630,9 +69,7 @@ hipError_t launch_select(const Dims &d, const nosa_state &st, const uint16_t *q,
   float *ws_e = reinterpret_cast<float *>(base + lay.e_off);
   float *ws_stats = reinterpret_cast<float *>(base + lay.stats_off);
   int32_t *ws_count = reinterpret_cast<int32_t *>(base + lay.count_off);
-  const size_t lds = ((size_t)lay.n_splits * padded_group(d.G) + lay.c_pad) * sizeof(float) +
-                     (size_t)d.elig_words * sizeof(uint32_t) + (size_t)d.NB_max;
-  select_kernel<<<dim3(lay.n_splits, d.P), kScoreThreads, lds, s>>>(
+  select_kernel<<<dim3(lay.n_splits, d.P), kScoreThreads, select_dyn_lds(d, lay), s>>>(
       d, st, q, ws_e, ws_stats, ws_count, lay.c_pad, lay.n_splits, sel, n_sel, kind, dbg);
   return hipGetLastError();
 }

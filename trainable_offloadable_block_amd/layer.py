@@ -229,6 +229,21 @@ class NosaLayer:
             _ptr(self.ws_select), self.ws_select.numel(), self.max_len, self.stream),
             "select")
 
+    def append_select(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                      want_kind=True, want_qscore=False):
+        """append then select, in one launch (same results as the two calls)."""
+        if want_qscore and self.dbg_q is None:
+            self.dbg_q = torch.full((self.shape.pairs * self.shape.nb_max,), float("nan"),
+                                    dtype=torch.float32, device=self.device)
+        self.max_len = min(self.max_len + 1, self.shape.max_context)
+        L.check(L.lib().nosa_append_select(
+            ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(k_new), _ptr(v_new),
+            _ptr(q), _ptr(self.sel), _ptr(self.n_sel),
+            _ptr(self.kind) if want_kind else ctypes.c_void_p(0),
+            _ptr(self.dbg_q) if want_qscore else ctypes.c_void_p(0),
+            _ptr(self.ws_select), self.ws_select.numel(), self.max_len, self.stream),
+            "append_select")
+
     def fetch(self, sel=None, n_sel=None, force=False):
         """Offload: brings the selection's missing blocks into the cache.
         Resident KV needs no fetch (decode reads each block at its own
@@ -253,9 +268,9 @@ class NosaLayer:
             self.ws_decode.numel(), self.max_len, self.stream), "sparse_decode")
 
     def step(self, k_new, v_new, q, want_kind=False, want_qscore=False):
-        """append -> select -> fetch -> decode, all enqueued on one stream."""
-        self.append(k_new, v_new)
-        self.select(q, want_kind=want_kind, want_qscore=want_qscore)
+        """append + select (one launch) -> fetch -> decode, all enqueued on
+        one stream."""
+        self.append_select(k_new, v_new, q, want_kind=want_kind, want_qscore=want_qscore)
         self.fetch()
         self.decode(q)
         return self.out
