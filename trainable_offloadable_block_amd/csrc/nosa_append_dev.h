@@ -65,7 +65,6 @@ __device__ __forceinline__ void clear_block(uint16_t *blk) {
 struct AppendLds {
   float v_sh[kHeadDim];
   uint16_t k_sh[kHeadDim];
-  uint16_t c_sh[kHeadDim];        // compressed key of the chunk this token completes
   float red2[2];
   int slot_sh;
   __align__(16) uint16_t w1_sh[kHeadDim * kHeadDim];
@@ -76,12 +75,12 @@ struct AppendLds {
 // (resident) or into the host store and the pair's cache slot (offload; a
 // token that opens a block takes a free slot), the tail ring, the token's
 // eviction score and, when the token completes a chunk, the chunk's
-// compressed key (also left in sh.c_sh), its mean score and, when that
-// completes a block, the block's agnostic score (stored device-coherently
-// when `coherent`, for readers in the same launch). Does nothing when pos is
+// compressed key, its mean score and, when that
+// completes a block, the block's agnostic score (the key and the block score
+// stored device-coherently when `coherent`, for readers in the same launch). Does nothing when pos is
 // outside [0, max_context). Returns the completed chunk's index, or -1.
 // Loads that do not depend on pos are issued first. Called by all NT
-// threads; the caller syncs before reading sh.c_sh.
+// threads.
 template <int NT>
 __device__ __forceinline__ int append_pair(const Dims &d, const nosa_state &st, const uint16_t *__restrict__ k_new,
                            const uint16_t *__restrict__ v_new, int b, int g, int pos,
@@ -181,8 +180,14 @@ __device__ __forceinline__ int append_pair(const Dims &d, const nosa_state &st, 
       sum += (double)bf16_to_f32(kv);
     }
     const uint16_t c = f64_to_bf16_rne(sum * (1.0 / kPoolKernel));
-    st.ckey[((size_t)p * d.C_max + i) * kHeadDim + t] = c;
-    sh.c_sh[t] = c;
+    uint16_t *row = st.ckey + ((size_t)p * d.C_max + i) * kHeadDim;
+    if (coherent) {
+      const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+          row, (short)0, kHeadDim * 2, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b16(c, rr, 2 * t, 0, 16);   // sc1: device-coherent
+    } else {
+      row[t] = c;
+    }
   }
   if (t < 64) {                          // wave 0: mean eviction score
     double se = 0.0;

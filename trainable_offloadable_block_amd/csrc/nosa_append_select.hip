@@ -2,15 +2,14 @@
 // of aiwiki "NOSA", How NOSA works, in order), for callers that run them
 // back to back: the separate append launch and its dispatch disappear.
 //
-// grid (chunk splits, pairs), 256 threads, as the select kernel:
-//  - every workgroup issues its split's score loads, then reads the
-//    sequence length; the workgroup whose split holds the pair's newest
-//    chunk first appends the token (K, V, ring, eviction score, and the
-//    compressed key, chunk score and block score the token completes); it
-//    scores the completed chunk from the fresh row it keeps in LDS;
-//  - every workgroup scores its split at the new length and arrives on the
-//    pair's counter; the last one pools and selects (reading the block
-//    scores with device-coherent loads: the append may have updated one);
+// grid (chunk splits + 1, pairs), 256 threads:
+//  - workgroup `n_splits` of a pair appends the token (K, V, ring, eviction
+//    score, and the compressed key, chunk score and block score the token
+//    completes, the last two stored device-coherently);
+//  - the others score their splits as the select kernel does (every chunk
+//    but the newest, which the append may be writing), in parallel;
+//  - all arrive on the pair's counter; the last one scores the newest chunk,
+//    pools and selects (block scores read device-coherently);
 //  - the last pair of a sequence to finish advances the sequence's length:
 //    by then every workgroup of the sequence has read it.
 #include "nosa_append_dev.h"
@@ -28,28 +27,24 @@ __global__ __launch_bounds__(kScoreThreads) void append_select_kernel(
   const int b = p / d.Hkv, g = p % d.Hkv;
   __shared__ AppendLds ash;
   __shared__ int sm_last;
-  ScoreIn in;
-  score_load(d, st.ckey, q, split, p, in);
   const int pos = st.seq_len[b];
   const bool ok = pos >= 0 && pos < d.max_context;
   const int L = ok ? pos + 1 : pos;
-  // the split holding chunk C - 1 at the new length (clamped to the grid)
-  const int C = min(chunks_for(L), d.C_max);
-  const int owner = min(max(C - 1, 0) / kChunksPerSplit, n_splits - 1);
-  int new_chunk = -1;
-  if (split == owner) {                                    // uniform
-    new_chunk = append_pair<kScoreThreads>(d, st, k_new, v_new, b, g, pos, true, ash);
-    __syncthreads();                                       // ash.c_sh is complete
+  if (split == n_splits) {                                 // uniform
+    append_pair<kScoreThreads>(d, st, k_new, v_new, b, g, pos, true, ash);
+  } else {
+    ScoreIn in;
+    score_load(d, st.ckey, q, split, p, in);
+    score_compute(d, split_chunks(d, L, c_pad), in, ws_e, ws_stats, c_pad, n_splits, split, p);
   }
-  score_compute(d, L, in, new_chunk, ash.c_sh, ws_e, ws_stats, c_pad, n_splits, split, p);
   __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
   __syncthreads();
   if (threadIdx.x == 0)
     sm_last = __hip_atomic_fetch_add(&ws_count[p], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              n_splits - 1;
+              n_splits;                  // n_splits score workgroups + the append
   __syncthreads();
   if (!sm_last) return;
-  pool_select(d, st, L, ws_e, ws_stats, c_pad, n_splits, sel, n_sel, kind_out, dbg, p);
+  pool_select(d, st, q, L, ws_e, ws_stats, c_pad, n_splits, sel, n_sel, kind_out, dbg, p);
   if (threadIdx.x == 0) {
     __hip_atomic_store(&ws_count[p], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // every workgroup of this pair has read the length; the last pair of
@@ -74,7 +69,7 @@ hipError_t launch_append_select(const Dims &d, const nosa_state &st, const uint1
   float *ws_e = reinterpret_cast<float *>(base + lay.e_off);
   float *ws_stats = reinterpret_cast<float *>(base + lay.stats_off);
   int32_t *ws_count = reinterpret_cast<int32_t *>(base + lay.count_off);
-  append_select_kernel<<<dim3(lay.n_splits, d.P), kScoreThreads, select_dyn_lds(d, lay), s>>>(
+  append_select_kernel<<<dim3(lay.n_splits + 1, d.P), kScoreThreads, select_dyn_lds(d, lay), s>>>(
       d, st, k_new, v_new, q, ws_e, ws_stats, ws_count, lay.c_pad, lay.n_splits, sel, n_sel, kind,
       dbg);
   return hipGetLastError();

@@ -6,9 +6,10 @@
 //    against the compressed keys on MFMA, l = q . c / sqrt(128); per split
 //    and head, m = max l, Z = sum exp(l - m); it publishes e = exp(l - m) per
 //    chunk and (m, Z) with device-coherent stores and arrives on the pair's
-//    counter;
-//  - the pair's last workgroup combines the split statistics into the
-//    per-head softmax, sums the group's heads, max-pools the chunks
+//    counter; the newest chunk is left to
+//  - the pair's last workgroup, which scores it, combines the split
+//    statistics into the per-head softmax, sums the group's heads, max-pools
+//    the chunks
 //    overlapping each block, then stage 1 (top k_q by the query-aware score)
 //    and stage 2 (top k_e' eligible by the agnostic score), each an exact
 //    workgroup top-k by histogram range refinement, writes the ascending
@@ -31,7 +32,7 @@ __global__ __launch_bounds__(kScoreThreads) void select_kernel(
   ScoreIn in;
   score_load(d, st.ckey, q, split, p, in);
   const int L = st.seq_len[p / d.Hkv];
-  score_compute(d, L, in, -1, nullptr, ws_e, ws_stats, c_pad, n_splits, split, p);
+  score_compute(d, split_chunks(d, L, c_pad), in, ws_e, ws_stats, c_pad, n_splits, split, p);
   __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
   __syncthreads();
   if (threadIdx.x == 0)
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(kScoreThreads) void select_kernel(
               n_splits - 1;
   __syncthreads();
   if (!sm_last) return;
-  pool_select(d, st, L, ws_e, ws_stats, c_pad, n_splits, sel, n_sel, kind_out, dbg, p);
+  pool_select(d, st, q, L, ws_e, ws_stats, c_pad, n_splits, sel, n_sel, kind_out, dbg, p);
   if (threadIdx.x == 0) __hip_atomic_store(&ws_count[p], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -84,12 +84,16 @@ __device__ __forceinline__ void score_load(const Dims &d, const uint16_t *__rest
   }
 }
 
-// Split `split` of pair p at sequence length L: logits of the group against
-// the split's compressed keys (chunk new_chunk, if in this split, taken from
-// new_row in LDS instead of the loaded copy), published with device-coherent
-// stores.
-__device__ __forceinline__ void score_compute(const Dims &d, int L, ScoreIn &in, int new_chunk,
-                                              const uint16_t *new_row, float *ws_e,
+// Chunks scored by the split workgroups at length L: every complete chunk
+// (at most c_pad) except the newest, which the pair's last workgroup scores
+// (the append of the same launch may be writing it).
+__device__ inline int split_chunks(const Dims &d, int L, int c_pad) {
+  return max(min(min(chunks_for(L), d.C_max), c_pad) - 1, 0);
+}
+
+// Split `split` of pair p: logits of the group against the split's
+// compressed keys among chunks [0, C), published with device-coherent stores.
+__device__ __forceinline__ void score_compute(const Dims &d, int C, ScoreIn &in, float *ws_e,
                                               float *ws_stats, int c_pad, int n_splits,
                                               int split, int p) {
   const int c0 = split * kChunksPerSplit;
@@ -97,7 +101,6 @@ __device__ __forceinline__ void score_compute(const Dims &d, int L, ScoreIn &in,
   const int h = l & 15, lg = l >> 4;
   const int cg = c0 + 32 * w;
   __shared__ float red_m[4][16], red_z[4][16];
-  const int C = min(chunks_for(L), d.C_max);
   float *stats = ws_stats + (size_t)2 * (p * n_splits + split) * d.G;   // (M, Z) per head
   if (c0 >= C) {
     if (threadIdx.x < d.G) {
@@ -105,15 +108,6 @@ __device__ __forceinline__ void score_compute(const Dims &d, int L, ScoreIn &in,
       put(&stats[2 * threadIdx.x + 1], 0.0f);
     }
     return;
-  }
-  if (new_chunk >= c0 && new_chunk < c0 + kChunksPerSplit) {     // uniform
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-      if (cg + tile_row(l & 15, t) == new_chunk) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          in.kv[t][s] = *reinterpret_cast<const uint4 *>(new_row + 8 * lg + 32 * s);
-      }
   }
   const uint4 (&qv)[4] = in.qv;
   const uint4 (&kv)[2][4] = in.kv;
@@ -417,18 +411,21 @@ constexpr int kLoadBatch = 8;     // chunk-weight float4 loads in flight per thr
 // workgroup once every split has published (so the chunk weights and split
 // statistics are read with device-coherent loads).
 // L is the pair's sequence length (after this step's append).
-__device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st, int L_in,
+__device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
+                                            const uint16_t *__restrict__ q, int L_in,
                                             const float *ws_e, const float *ws_stats,
                                             int c_pad, int n_splits, int32_t *sel,
                                             int32_t *n_sel, uint8_t *kind_out, float *dbg,
                                             int p) {
   const int Gp = padded_group(d.G);
+  const int b = p / d.Hkv;
   extern __shared__ __align__(16) uint8_t smem[];
   float *f_sh = reinterpret_cast<float *>(smem);                            // [n_splits][Gp]
   float *a_sh = f_sh + n_splits * Gp;                                       // [c_pad]
   uint32_t *el_sh = reinterpret_cast<uint32_t *>(a_sh + c_pad);             // [elig_words]
   uint8_t *kind = reinterpret_cast<uint8_t *>(el_sh + d.elig_words);        // [NB_max]
   __shared__ TopkLds tk;
+  __shared__ float lnew_sh[kMaxGroup], wlast_sh[kMaxGroup];
   __shared__ int cnt_sh[2][kTopkThreads / 64];
 
   const int t = threadIdx.x;
@@ -464,12 +461,44 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
   const int nb = blocks_for(L);
   const int win_lo = max(d.n_sink, nb - d.n_win);
   const int n_cand = max(0, win_lo - d.n_sink);
-  const int used = (C + kChunksPerSplit - 1) / kChunksPerSplit;
+  const int Cs = max(C - 1, 0);          // chunks scored by the splits; C - 1 here
+  const int used = (Cs + kChunksPerSplit - 1) / kChunksPerSplit;
   const bool do_q = d.k_q > 0 && n_cand > 0, do_e = d.k_e_dyn > 0 && n_cand > 0;
-  const int n4 = do_q ? C * Gp / 4 : 0;
+  const int n4 = do_q ? Cs * Gp / 4 : 0;
   const bool have0 = t < n_cand;
   const float e0 = (do_e && have0) ? e0_raw : 0.0f;
   const float2 stv = (do_q && sh_h < d.G && sh_j < used) ? stv_raw : make_float2(-INFINITY, 0.0f);
+  // the newest chunk (C - 1): the group's logits against it on wave 0, with
+  // the split kernels' MFMA (its row in A-row 0, read device-coherently:
+  // the append of the same launch may have just written it)
+  const bool last_q = do_q && C >= 1;                          // uniform
+  if (last_q && w == 0) {
+    const int h = lane & 15, lg = lane >> 4;
+    const __amdgpu_buffer_rsrc_t kr =
+        make_rsrc(st.ckey + ((size_t)p * d.C_max + (C - 1)) * kHeadDim, kHeadDim * 2);
+    uint4 av[4], qv[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      av[s4] = make_uint4(0, 0, 0, 0);
+      qv[s4] = make_uint4(0, 0, 0, 0);
+    }
+    if (h == 0) {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        av[s4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               kr, 2 * (8 * lg + 32 * s4), 0, kCoherent));
+    }
+    if (h < d.G) {
+      const uint16_t *qh = q + ((size_t)b * d.Hq + (p % d.Hkv) * d.G + h) * kHeadDim + 8 * lg;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) qv[s4] = *reinterpret_cast<const uint4 *>(qh + 32 * s4);
+    }
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) acc = mfma16x16x32(as_bf16x8(av[s4]), as_bf16x8(qv[s4]), acc);
+    // D row 0 sits in lanes 0..15 (element 0): head = lane
+    if (lane < kMaxGroup) lnew_sh[lane] = acc[0] * 0.08838834764831845f;   // 1/sqrt(128)
+  }
   for (int i = t; i < d.elig_words; i += kTopkThreads)
     el_sh[i] = st.eligible[(size_t)p * d.elig_words + i];
   for (int bb = t; bb < nb; bb += kTopkThreads)
@@ -480,8 +509,9 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
     tk.hist[1][t + kTopkThreads * i] = 0;
   }
 
-  // 1. per-split factors exp(m_split - M) / Z of each head's softmax (0 for
-  // the padding heads)
+  if (last_q) __syncthreads();                                 // lnew_sh is set
+  // 1. per-split factors exp(m_split - M) / Z of each head's softmax over
+  // all complete chunks, the newest included (0 for the padding heads)
   if (do_q && sh_h < Gp) {
     const bool real = sh_h < d.G;
     float m = stv.x;
@@ -489,6 +519,8 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
       for (int s = sh_j + 16; s < used; s += 16) m = fmaxf(m, load2_coherent(sr, 8 * (s * d.G + sh_h)).x);
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float ln = (real && last_q) ? lnew_sh[sh_h] : -INFINITY;
+    m = fmaxf(m, ln);
     const float e0s = stv.y > 0.0f ? expf(stv.x - m) : 0.0f;
     float z = stv.y * e0s;
     if (real)
@@ -498,7 +530,10 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
       }
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
+    const float el = ln == -INFINITY ? 0.0f : expf(ln - m);
+    z += el;
     const float rz = real ? 1.0f / z : 0.0f;
+    if (sh_j == 0) wlast_sh[sh_h] = el * rz;
     if (sh_j < used) f_sh[sh_j * Gp + sh_h] = e0s * rz;
     for (int s = sh_j + 16; s < used; s += 16) {
       const float2 v = real ? load2_coherent(sr, 8 * (s * d.G + sh_h)) : make_float2(-INFINITY, 0.0f);
@@ -537,6 +572,11 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
         if (lpc >= 4) a += __shfl_xor(a, 2, 64);
         if (k4 < n4 && h0 == 0) a_sh[c] = a;
       }
+    }
+    if (last_q && t == 0) {                  // the newest chunk, heads in order
+      float a = 0.0f;
+      for (int h = 0; h < d.G; ++h) a += wlast_sh[h];
+      a_sh[C - 1] = a;
     }
   }
   __syncthreads();
