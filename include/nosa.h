@@ -69,7 +69,7 @@ enum {
  * size 1..16; block_size 64, pool_kernel 32, pool_stride 16 (aiwiki "NOSA",
  * Main-experiment configuration; NOSA-1B 核心组件揭秘, 核心组件一);
  * window_tokens a multiple of 64 and >= 128 (so every candidate block's
- * chunks are complete); k_blocks = k_q_blocks + k_e_blocks <= 64 with
+ * chunks are complete); k_blocks = k_q_blocks + k_e_blocks <= 128 with
  * k_e_blocks >= n_sink_blocks + window_tokens / 64 (k_e counts the sink and
  * window blocks, aiwiki "NOSA" Main-experiment configuration);
  * evict_hidden 128; 64 <= max_context <= 262144; batch * n_kv_heads <= 65535.

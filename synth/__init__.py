@@ -7,6 +7,7 @@ benchmark) take their inputs from here, so both see identical bf16 bits.
 """
 
 from .workloads import (  # noqa: F401
+    NEXT_WORKLOADS,
     WORKLOADS,
     Workload,
     bf16_bits_to_f32,

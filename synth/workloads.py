@@ -103,6 +103,17 @@ WORKLOADS = {
                 rho=0.8, n_hot=64, offload=True, drift=True),
 }
 
+# Beyond the five benchmark configurations: the pages' own 8B head layout
+# (32 query / 2 KV heads, GQA 16; aiwiki "NOSA", Models and training table)
+# with the 96-block budget SparDA uses for NOSA-8B (24 query-aware blocks, a
+# 1024-token window; aiwiki "NOSA", Adoption in SparDA), at its native 32K.
+NEXT_WORKLOADS = {
+    "gqa16-k96": Workload("nosa8b-gqa16-k96-32k-b16", 6, batch=16, n_q_heads=32,
+                          n_kv_heads=2, context=32768, steps=64, n_sink_blocks=1,
+                          window_tokens=1024, k_blocks=96, k_q_blocks=24,
+                          k_e_blocks=72, rho=0.9, n_hot=_hot_count(32768)),
+}
+
 
 def small_workload(cfg_id: int = 100, **kw) -> Workload:
     """A small workload for tests; keyword arguments override the defaults."""

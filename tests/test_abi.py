@@ -43,7 +43,7 @@ def test_valid_configs_of_the_workloads():
     (dict(k_e_blocks=10, k_blocks=26), L.NOSA_ERR_INVALID),  # < sink + window
     (dict(window_tokens=1000), L.NOSA_ERR_INVALID),      # not block-aligned
     (dict(window_tokens=64, k_e_blocks=2, k_blocks=18), L.NOSA_ERR_UNSUPPORTED),
-    (dict(k_blocks=80, k_q_blocks=32), L.NOSA_ERR_UNSUPPORTED),   # k > 64
+    (dict(k_blocks=144, k_q_blocks=96), L.NOSA_ERR_UNSUPPORTED),  # k > 128
     (dict(max_context=1 << 20), L.NOSA_ERR_UNSUPPORTED),
     (dict(max_context=32), L.NOSA_ERR_UNSUPPORTED),
     (dict(batch=0), L.NOSA_ERR_INVALID),
@@ -52,6 +52,16 @@ def test_validate_rejects(kw, code):
     c = _cfg(**kw)
     assert nosa.lib().nosa_validate_config(ctypes.byref(c)) == code
     assert nosa.lib().nosa_last_error()
+
+
+def test_validate_accepts_k_up_to_128():
+    """The 8B shape with GQA 16 and a 96-block budget (24 query-aware,
+    window 1024), and the largest budget, 128 blocks."""
+    lib = nosa.lib()
+    for kw in (dict(n_q_heads=32, n_kv_heads=2, k_blocks=96, k_q_blocks=24, k_e_blocks=72),
+               dict(k_blocks=128, k_q_blocks=64, k_e_blocks=64)):
+        c = _cfg(**kw)
+        assert lib.nosa_validate_config(ctypes.byref(c)) == L.NOSA_OK, kw
 
 
 def test_validate_rejects_bad_fields():

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from synth import WORKLOADS, small_workload
+from synth import NEXT_WORKLOADS, WORKLOADS, small_workload
 from nosa_harness import Lockstep, summary
 from trainable_offloadable_block_amd import v_to_tiles
 
@@ -242,3 +242,21 @@ def test_append_select_capacity_sets_status():
     torch.cuda.synchronize()
     assert g.status_bits() & 1
     assert g.seq_len.cpu().tolist() == [128] * wl.batch
+
+
+@pytest.mark.parametrize("offload", [False, True])
+def test_gqa16_k96_sampled(offload):
+    """The pages' 8B head layout (32/2 heads, GQA 16) with SparDA's 96-block
+    budget (24 query-aware, window 1024) at 32K, 16 sequences: 3 sampled
+    pairs against the oracle; offloaded, the cache must equal the host store."""
+    wl = NEXT_WORKLOADS["gqa16-k96"].replace(offload=offload)
+    _run(wl, check_pairs=[0, 13, 31], steps=8, cache_every=4, fused=True)
+
+
+@pytest.mark.parametrize("offload", [False, True])
+def test_k128_budget(offload):
+    """The largest budget, k = 128 blocks (32 query-aware, 96 agnostic with a
+    1024-token window), over 70 steps of a 12K context."""
+    wl = small_workload(131, context=12288, steps=70, n_q_heads=16, window_tokens=1024,
+                        k_blocks=128, k_q_blocks=32, k_e_blocks=96, offload=offload)
+    _run(wl, cache_every=10, fused=True)

@@ -39,7 +39,7 @@ int check_config(const nosa_config *c) {
     return fail(NOSA_ERR_INVALID, "k_blocks must equal k_q_blocks + k_e_blocks");
   if (c->k_e_blocks < c->n_sink_blocks + c->window_tokens / nosa::kBlock)
     return fail(NOSA_ERR_INVALID, "k_e_blocks must cover the sink and window blocks");
-  if (c->k_blocks > nosa::kMaxK) return fail(NOSA_ERR_UNSUPPORTED, "k_blocks must be <= 64");
+  if (c->k_blocks > nosa::kMaxK) return fail(NOSA_ERR_UNSUPPORTED, "k_blocks must be <= 128");
   if (c->max_context < nosa::kBlock || c->max_context > nosa::kMaxContext)
     return fail(NOSA_ERR_UNSUPPORTED, "max_context must be in [64, 262144]");
   if ((long)c->batch * c->n_kv_heads > 65535)

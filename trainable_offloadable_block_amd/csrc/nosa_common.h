@@ -14,7 +14,7 @@ constexpr int kPoolKernel = 32;
 constexpr int kPoolStride = 16;
 constexpr int kBlockElems = 2 * kBlock * kHeadDim;   // K part + V part, bf16
 constexpr int kMaxGroup = 16;
-constexpr int kMaxK = 64;
+constexpr int kMaxK = 128;
 constexpr int kMaxContext = 1 << 18;   // 262144 tokens
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

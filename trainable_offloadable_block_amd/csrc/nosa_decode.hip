@@ -24,7 +24,7 @@ namespace {
 #endif
 
 constexpr int kDecThreads = 256;
-constexpr int kMaxSplits = 16;   // k <= 64 blocks, >= 4 blocks per split
+constexpr int kMaxSplits = 32;   // k <= 128 blocks, >= 4 blocks per split
 constexpr float kLog2e = 1.4426950408889634f;
 
 // A-row r of tile t <-> row 8*(r/4) + 4*t + (r%4) of a 32-row group, so that
@@ -195,9 +195,9 @@ __device__ void merge_splits(const Dims &d, int p, int b, int g, int n_splits,
       }
   };
   issue(0);
-  if (t < n_splits * d.G) {
-    sm_w[t] = load_agent(&mlp[2 * t]);
-    sm_lv[t] = load_agent(&mlp[2 * t + 1]);
+  for (int i = t; i < n_splits * d.G; i += kDecThreads) {
+    sm_w[i] = load_agent(&mlp[2 * i]);
+    sm_lv[i] = load_agent(&mlp[2 * i + 1]);
   }
   __syncthreads();
   if (t < d.G) {
@@ -385,6 +385,7 @@ DecodeLayout decode_layout(const Dims &d) {
     const int v = atoi(env);
     if (v >= 4 && v <= 64) bps = v;
   }
+  while (bps < 64 && (d.k + bps - 1) / bps > kMaxSplits) bps *= 2;   // merge bound
   lay.blocks_per_split = bps;
   lay.n_splits = (d.k + bps - 1) / bps;
   lay.o_off = 0;

@@ -7,7 +7,8 @@
 // setdiff_kernel: one wavefront per pair. Slots whose block left the
 //   selection are freed; each selected block that is not cached takes a free
 //   slot (lowest first, in ascending block order) and becomes a copy-list
-//   entry. O(k) work, one lane per selection entry / cache slot.
+//   entry. O(k) work, a lane per selection entry (two for k > 64) and per
+//   cache slot.
 // gather_kernel: copies each listed 32 KiB block from the host store to its
 //   cache slot, reading host memory through its device alias.
 #include "nosa_internal.h"
@@ -30,12 +31,19 @@ __global__ __launch_bounds__(64) void setdiff_kernel(
   for (int i = l; i < d.elig_words; i += 64) sel_bits[i] = 0u;
   __syncthreads();
   const int ns = max(0, min(n_sel[p], d.k));
-  int blk = l < ns ? sel[(size_t)p * d.k + l] : -1;
-  if (blk >= d.NB_max) {
-    atomicOr(st.status, NOSA_STATUS_BAD_SEL);
-    blk = -1;
+  // lane l holds selection entries l and l + 64 (k <= 128)
+  constexpr int kPer = kMaxK / 64;
+  int blk[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int e = l + 64 * r;
+    blk[r] = e < ns ? sel[(size_t)p * d.k + e] : -1;
+    if (blk[r] >= d.NB_max) {
+      atomicOr(st.status, NOSA_STATUS_BAD_SEL);
+      blk[r] = -1;
+    }
+    if (blk[r] >= 0) atomicOr(&sel_bits[blk[r] >> 5], 1u << (blk[r] & 31));
   }
-  if (blk >= 0) atomicOr(&sel_bits[blk >> 5], 1u << (blk & 31));
   __syncthreads();
 
   // slots: keep those holding a selected block, free the rest
@@ -60,25 +68,31 @@ __global__ __launch_bounds__(64) void setdiff_kernel(
   }
   __syncthreads();
 
-  // misses take free slots in order
-  int slot = blk >= 0 ? sob[blk] : -1;
-  const bool miss = blk >= 0 && slot < 0;
-  const unsigned long long mm = __ballot(miss);
-  const int rank = __popcll(mm & ((1ull << l) - 1ull));
-  if (miss) {
-    slot = rank < n_free ? free_list[rank] : -1;
-    if (slot >= 0) {
-      bos_new[slot] = blk;
-      sob[blk] = slot;
-      list[(size_t)p * d.k + rank] = make_int2(blk, slot);
-    } else {
-      atomicOr(st.status, NOSA_STATUS_BAD_SEL);
+  // misses take free slots in order (entry order = ascending block order)
+  int n_missed = 0;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int e = l + 64 * r;
+    int slot = blk[r] >= 0 ? sob[blk[r]] : -1;
+    const bool miss = blk[r] >= 0 && slot < 0;
+    const unsigned long long mm = __ballot(miss);
+    const int rank = n_missed + __popcll(mm & ((1ull << l) - 1ull));
+    if (miss) {
+      slot = rank < n_free ? free_list[rank] : -1;
+      if (slot >= 0) {
+        bos_new[slot] = blk[r];
+        sob[blk[r]] = slot;
+        list[(size_t)p * d.k + rank] = make_int2(blk[r], slot);
+      } else {
+        atomicOr(st.status, NOSA_STATUS_BAD_SEL);
+      }
     }
+    n_missed += __popcll(mm);
+    if (e < d.k) phys[(size_t)p * d.k + e] = e < ns ? slot : -1;
   }
   __syncthreads();
   for (int s = l; s < slots; s += 64) bos[s] = bos_new[s];
-  if (l < d.k) phys[(size_t)p * d.k + l] = l < ns ? slot : -1;
-  if (l == 0) n_miss[p] = min(__popcll(mm), n_free);
+  if (l == 0) n_miss[p] = min(n_missed, n_free);
 }
 
 // grid (k, P), block 256: entry r of pair p, if it exists.
