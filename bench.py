@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the host-link leg (offloaded 128K workload)")
     ap.add_argument("--offload-steps", type=int, default=24)
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the GQA-16, 96-block leg (beyond the five configs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of MIB MiB first (a known "
                          "byte count for calibrating HBM traffic counters)")
@@ -257,42 +259,25 @@ def host_link_leg(n_steps, pool, dev):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the NOSA "
-              "decode path has no cross-GPU step; pairs would shard by sequence "
-              "or KV head with no exchange.", file=sys.stderr)
-        sys.exit(2)
+def time_stack(wl, R, W, K, n_bd, dev, workers):
+    """Times K decode steps (after W warm-up steps) of a stack of R
+    independent layers of workload wl, with HIP events around every decode
+    launch; n_bd further steps give a per-call breakdown and the exact
+    number of attended tokens."""
     import numpy as np
     import torch
-    from synth import WORKLOADS
     from trainable_offloadable_block_amd import LayerShape
-
-    wl = WORKLOADS[2]
-    R, W, K = args.layers, args.warmup, args.steps
-    n_tok = W + K + args.breakdown_steps
+    n_tok = W + K + n_bd
     shape = LayerShape(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_sink_blocks,
                        wl.window_tokens, wl.k_blocks, wl.k_q_blocks, wl.k_e_blocks,
                        wl.context + n_tok)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.copy_probe:
-        n = args.copy_probe << 20
-        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     t_setup = time.perf_counter()
-    workers = min(16, len(os.sched_getaffinity(0)))
     layers, inputs = [], []
     with cf.ThreadPoolExecutor(workers) as pool:
         for li in range(R):
             layers.append(build_layer(wl, li, shape, pool))
             inputs.append(step_inputs(wl, li, n_tok, pool, dev))
-            log(f"layer {li} ready ({time.perf_counter() - t_setup:.1f}s)")
+            log(f"{wl.name}: layer {li} ready ({time.perf_counter() - t_setup:.1f}s)")
     torch.cuda.synchronize()
 
     def run_step(t, events=None):
@@ -342,11 +327,61 @@ def main():
             n_att_samples.append(attended_tokens(layer, wl))
     status = [ly.status_bits() for ly in layers]
     assert not any(status), f"device status bits set: {status}"
-    n_att = float(np.mean(n_att_samples))
+    out = {"value": wl.batch * R * K / el, "elapsed": el,
+           "n_att": float(np.mean(n_att_samples)),
+           "dec_avg_s": float(np.mean(dec_ms)) / 1e3,
+           "breakdown": {n: round(float(np.median(v)), 2) for n, v in bd.items()}}
+    layers.clear()
+    inputs.clear()
+    torch.cuda.empty_cache()
+    return out
+
+
+def next_leg(dev, workers, R=4, W=8, K=48):
+    """The GQA-16, 96-block workload (beyond the five benchmark configs):
+    step throughput and the decode kernel against the HBM roofline."""
+    from synth import NEXT_WORKLOADS
+    wl = NEXT_WORKLOADS["gqa16-k96"]
+    m = time_stack(wl, R, W, K, 2, dev, workers)
+    dbytes = decode_bytes(wl, m["n_att"])
+    ach = dbytes / m["dec_avg_s"] / 1e9
+    return {"workload": wl.name, "layers_per_step": R, "steps": K,
+            "value": round(m["value"], 1), "unit": "tokens/s/layer",
+            "ms_per_step": round(m["elapsed"] * 1e3 / K, 4),
+            "decode": {"achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": int(dbytes),
+                       "avg_launch_us": round(m["dec_avg_s"] * 1e6, 2),
+                       "attended_tokens_per_pair": round(m["n_att"], 2)},
+            "breakdown_us": m["breakdown"]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the NOSA "
+              "decode path has no cross-GPU step; pairs would shard by sequence "
+              "or KV head with no exchange.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from synth import WORKLOADS
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    workers = min(16, len(os.sched_getaffinity(0)))
+    wl = WORKLOADS[2]
+    R, W, K = args.layers, args.warmup, args.steps
+    m = time_stack(wl, R, W, K, args.breakdown_steps, dev, workers)
+    value, el, n_att, dec_avg_s, bd = m["value"], m["elapsed"], m["n_att"], m["dec_avg_s"], m["breakdown"]
     dbytes = decode_bytes(wl, n_att)
-    dec_avg_s = float(np.mean(dec_ms)) / 1e3
     achieved = dbytes / dec_avg_s / 1e9
-    value = wl.batch * R * K / el
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -375,13 +410,13 @@ def main():
             "bytes_per_launch": int(dbytes), "avg_launch_us": round(dec_avg_s * 1e6, 2),
             "attended_tokens_per_pair": round(n_att, 2),
         },
-        "breakdown_us": {n: round(float(np.median(v)), 2) for n, v in bd.items()},
+        "breakdown_us": bd,
     }
+    if not args.no_next:
+        log("GQA-16 96-block leg")
+        res["gqa16_k96"] = next_leg(dev, workers)
     if not args.no_offload:
         log("host-link leg (offloaded 128K workload)")
-        layers.clear()
-        inputs.clear()
-        torch.cuda.empty_cache()
         with cf.ThreadPoolExecutor(workers) as pool:
             res["host_link"] = host_link_leg(args.offload_steps, pool, dev)
     if not args.no_cpu:

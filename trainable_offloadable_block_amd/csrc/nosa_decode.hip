@@ -20,7 +20,7 @@ namespace {
 #define NOSA_DECODE_GLOBAL_LOADS 0
 #endif
 #ifndef NOSA_DECODE_MIN_WAVES
-#define NOSA_DECODE_MIN_WAVES 1
+#define NOSA_DECODE_MIN_WAVES 2     // <= 256 registers: two workgroups per CU fit
 #endif
 
 constexpr int kDecThreads = 256;
@@ -377,10 +377,11 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
 
 DecodeLayout decode_layout(const Dims &d) {
   DecodeLayout lay;
-  // 16 blocks per workgroup (4 per wave, streamed with one half in flight)
-  // while the grid still covers every CU; fewer when the pair count is small
-  int bps = 16;
-  while (bps > 4 && (long)d.P * ((d.k + bps - 1) / bps) < 256) bps /= 2;
+  // one round of workgroups that covers the chip: about 256 / pairs splits
+  // per pair (at most kMaxSplits), each a run of bps >= 4 list entries
+  // (256 workgroups of 16 blocks each at 64 pairs and k = 64)
+  const int want = max(1, min(kMaxSplits, (256 + d.P - 1) / d.P));
+  int bps = max(4, (d.k + want - 1) / want);
   if (const char *env = getenv("NOSA_DECODE_BPS")) {
     const int v = atoi(env);
     if (v >= 4 && v <= 64) bps = v;
