@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the host-link leg (offloaded 128K workload)")
     ap.add_argument("--offload-steps", type=int, default=24)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the hipGraph replay leg of the same layer stack")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the GQA-16, 96-block leg (beyond the five configs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -81,6 +83,7 @@ def step_inputs(wl, li, n, pool, device):
     import torch
     from synth import new_tokens, queries
     B, Hq, Hkv = wl.batch, wl.n_q_heads, wl.n_kv_heads
+    wl = wl.replace(steps=max(wl.steps, n))     # the same streams, drawn further
     qs = list(pool.map(lambda bh: queries(wl, li, *divmod(bh, Hq))[:n], range(B * Hq)))
     q = np.stack(qs).reshape(B, Hq, n, 128).transpose(2, 0, 1, 3)
     toks = list(pool.map(lambda bg: new_tokens(wl, li, *divmod(bg, Hkv)), range(B * Hkv)))
@@ -259,15 +262,19 @@ def host_link_leg(n_steps, pool, dev):
     }
 
 
-def time_stack(wl, R, W, K, n_bd, dev, workers):
+def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0):
     """Times K decode steps (after W warm-up steps) of a stack of R
     independent layers of workload wl, with HIP events around every decode
     launch; n_bd further steps give a per-call breakdown and the exact
-    number of attended tokens."""
+    number of attended tokens. With graph_steps, the same stack then runs
+    that many steps (after 4 untimed ones) as replays of one captured HIP
+    graph of a whole step, each step's inputs copied into the graph's static
+    buffer first."""
     import numpy as np
     import torch
     from trainable_offloadable_block_amd import LayerShape
-    n_tok = W + K + n_bd
+    n_graph = graph_steps + 4 if graph_steps else 0
+    n_tok = W + K + n_bd + n_graph
     shape = LayerShape(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_sink_blocks,
                        wl.window_tokens, wl.k_blocks, wl.k_q_blocks, wl.k_e_blocks,
                        wl.context + n_tok)
@@ -310,7 +317,7 @@ def time_stack(wl, R, W, K, n_bd, dev, workers):
     names = ("append_select", "fetch", "decode")
     bd = {n: [] for n in names}
     n_att_samples = []
-    for t in range(W + K, n_tok):
+    for t in range(W + K, W + K + n_bd):
         for li, layer in enumerate(layers):
             q, kn, vn = inputs[li][0][t], inputs[li][1][t], inputs[li][2][t]
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -325,16 +332,73 @@ def time_stack(wl, R, W, K, n_bd, dev, workers):
             for i, n in enumerate(names):
                 bd[n].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)
             n_att_samples.append(attended_tokens(layer, wl))
+    graph = None
+    if graph_steps:
+        graph = graph_replays(layers, inputs, W + K + n_bd, graph_steps, shape)
     status = [ly.status_bits() for ly in layers]
     assert not any(status), f"device status bits set: {status}"
     out = {"value": wl.batch * R * K / el, "elapsed": el,
            "n_att": float(np.mean(n_att_samples)),
            "dec_avg_s": float(np.mean(dec_ms)) / 1e3,
            "breakdown": {n: round(float(np.median(v)), 2) for n, v in bd.items()}}
+    if graph is not None:
+        out["graph"] = {"steps": graph_steps, "ms_per_step": round(graph * 1e3 / graph_steps, 4),
+                        "value": round(wl.batch * R * graph_steps / graph, 1)}
     layers.clear()
     inputs.clear()
     torch.cuda.empty_cache()
     return out
+
+
+def graph_replays(layers, inputs, t0, n, shape):
+    """Captures one step of every layer (append_select, fetch, decode) as a
+    HIP graph over a static input buffer, then replays it for steps t0 + 4 ..
+    t0 + 4 + n - 1 (4 untimed first); returns the timed seconds. The length
+    hint is the layers' capacity, so the baked grid sizes hold for every
+    replay."""
+    import torch
+    R = len(layers)
+    parts = [[inputs[li][j] for j in range(3)] for li in range(R)]
+    sizes = [x[0].numel() for row in parts for x in row]
+    static = torch.empty(sum(sizes), dtype=torch.int16, device=parts[0][0].device)
+    views, off = [], 0
+    for row in parts:
+        v = []
+        for x in row:
+            v.append(static[off:off + x[0].numel()].view(x[0].shape))
+            off += x[0].numel()
+        views.append(v)
+    packed = torch.stack([torch.cat([x[t].reshape(-1) for row in parts for x in row])
+                          for t in range(t0, t0 + n + 4)])
+    saved = [ly.max_len for ly in layers]
+    for ly in layers:
+        ly.max_len = shape.max_context - 1       # becomes the bound inside
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for li, ly in enumerate(layers):
+                q, kn, vn = views[li]
+                ly.append_select(kn, vn, q, want_kind=False)
+                ly.fetch()
+                ly.decode(q)
+    torch.cuda.current_stream().wait_stream(side)
+    for ly, m in zip(layers, saved):
+        ly.max_len = m
+    for t in range(4):
+        static.copy_(packed[t])
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for t in range(4, n + 4):
+        static.copy_(packed[t])
+        g.replay()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t1
+    for ly in layers:                            # the lengths moved on by n + 4
+        ly.max_len = min(ly.max_len + n + 4, shape.max_context)
+    return el
 
 
 def next_leg(dev, workers, R=4, W=8, K=48):
@@ -378,7 +442,8 @@ def main():
     workers = min(16, len(os.sched_getaffinity(0)))
     wl = WORKLOADS[2]
     R, W, K = args.layers, args.warmup, args.steps
-    m = time_stack(wl, R, W, K, args.breakdown_steps, dev, workers)
+    m = time_stack(wl, R, W, K, args.breakdown_steps, dev, workers,
+                   graph_steps=0 if args.no_graph else K)
     value, el, n_att, dec_avg_s, bd = m["value"], m["elapsed"], m["n_att"], m["dec_avg_s"], m["breakdown"]
     dbytes = decode_bytes(wl, n_att)
     achieved = dbytes / dec_avg_s / 1e9
@@ -412,6 +477,8 @@ def main():
         },
         "breakdown_us": bd,
     }
+    if "graph" in m:
+        res["graph_replay"] = m["graph"]
     if not args.no_next:
         log("GQA-16 96-block leg")
         res["gqa16_k96"] = next_leg(dev, workers)

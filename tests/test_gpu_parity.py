@@ -260,3 +260,48 @@ def test_k128_budget(offload):
     wl = small_workload(131, context=12288, steps=70, n_q_heads=16, window_tokens=1024,
                         k_blocks=128, k_q_blocks=32, k_e_blocks=96, offload=offload)
     _run(wl, cache_every=10, fused=True)
+
+
+@pytest.mark.parametrize("offload", [False, True])
+def test_graph_replay_matches_eager(offload):
+    """A whole step (append_select, fetch, decode) captured as a HIP graph
+    over static input buffers and replayed 24 times, with eager work and
+    synchronisations between the replays: every replay's selection, output
+    and state equal, bit for bit, those of an identical layer run eagerly."""
+    wl = small_workload(141, context=1000, steps=24, offload=offload)
+    a = Lockstep(wl, check_pairs=[], lengths=[1000, 990])
+    b = Lockstep(wl, check_pairs=[], lengths=[1000, 990])
+    bound = b.shape.max_context
+    for ls in (a, b):
+        ls.gpu.max_len = bound - 1          # the same grid sizes on both paths
+    kd, vd, qd = b.inputs(0)
+    ks, vs, qs = kd.clone(), vd.clone(), qd.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            b.gpu.append_select(ks, vs, qs)
+            b.gpu.fetch()
+            b.gpu.decode(qs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for t in range(wl.steps):
+        kd, vd, qd = a.inputs(t)
+        a.gpu.max_len = bound - 1
+        a.gpu.append_select(kd, vd, qd)
+        a.gpu.fetch()
+        a.gpu.decode(qd)
+        ks.copy_(kd)
+        vs.copy_(vd)
+        qs.copy_(qd)
+        g.replay()
+        scratch.add_(1.0)                   # eager work between replays
+        torch.cuda.synchronize()
+        for n in ("sel", "n_sel", "kind", "phys", "n_miss", "out"):
+            assert torch.equal(getattr(a.gpu, n), getattr(b.gpu, n)), f"replay {t}: {n}"
+        sa, sb = _state_tensors(a.gpu), _state_tensors(b.gpu)
+        for n in sa:
+            assert torch.equal(sa[n], sb[n]), f"replay {t}: state {n}"
+    assert a.gpu.status_bits() == 0 and b.gpu.status_bits() == 0
