@@ -277,7 +277,7 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0):
     n_tok = W + K + n_bd + n_graph
     shape = LayerShape(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_sink_blocks,
                        wl.window_tokens, wl.k_blocks, wl.k_q_blocks, wl.k_e_blocks,
-                       wl.context + n_tok)
+                       wl.context + n_tok, offload=wl.offload)
     t_setup = time.perf_counter()
     layers, inputs = [], []
     with cf.ThreadPoolExecutor(workers) as pool:
@@ -317,6 +317,7 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0):
     names = ("append_select", "fetch", "decode")
     bd = {n: [] for n in names}
     n_att_samples = []
+    fetched = []                                  # (bytes, us) per fetch call
     for t in range(W + K, W + K + n_bd):
         for li, layer in enumerate(layers):
             q, kn, vn = inputs[li][0][t], inputs[li][1][t], inputs[li][2][t]
@@ -332,6 +333,9 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0):
             for i, n in enumerate(names):
                 bd[n].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)
             n_att_samples.append(attended_tokens(layer, wl))
+            if wl.offload:
+                fetched.append((int(layer.n_miss.sum().item()) * 32768,
+                                evs[1].elapsed_time(evs[2]) * 1e3))
     graph = None
     if graph_steps:
         graph = graph_replays(layers, inputs, W + K + n_bd, graph_steps, shape)
@@ -341,6 +345,11 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0):
            "n_att": float(np.mean(n_att_samples)),
            "dec_avg_s": float(np.mean(dec_ms)) / 1e3,
            "breakdown": {n: round(float(np.median(v)), 2) for n, v in bd.items()}}
+    if fetched:
+        b_ = float(np.mean([f[0] for f in fetched]))
+        us = float(np.mean([f[1] for f in fetched]))
+        out["fetch"] = {"bytes_per_call": int(b_), "us_mean": round(us, 1),
+                        "GBps": round(b_ / (us * 1e-6) / 1e9, 2)}
     if graph is not None:
         out["graph"] = {"steps": graph_steps, "ms_per_step": round(graph * 1e3 / graph_steps, 4),
                         "value": round(wl.batch * R * graph_steps / graph, 1)}
@@ -399,6 +408,26 @@ def graph_replays(layers, inputs, t0, n, shape):
     for ly in layers:                            # the lengths moved on by n + 4
         ly.max_len = min(ly.max_len + n + 4, shape.max_context)
     return el
+
+
+def offload_32k_leg(dev, workers, R=4, W=4, K=24, n_bd=8):
+    """The offloaded 32K 1B-shaped stack (64 sequences, 16/2 heads, k = 64,
+    full KV in pinned host memory; R of its 28 layers): decode tokens/s per
+    layer with the delta fetch on the step path, and the decode kernel
+    (reading the device block cache) against the HBM roofline."""
+    from synth import WORKLOADS
+    wl = WORKLOADS[3]
+    m = time_stack(wl, R, W, K, n_bd, dev, workers)
+    dbytes = decode_bytes(wl, m["n_att"])
+    ach = dbytes / m["dec_avg_s"] / 1e9
+    return {"workload": wl.name, "layers_per_step": R, "steps": K,
+            "value": round(m["value"], 1), "unit": "tokens/s/layer",
+            "ms_per_step": round(m["elapsed"] * 1e3 / K, 4),
+            "decode": {"achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": int(dbytes),
+                       "avg_launch_us": round(m["dec_avg_s"] * 1e6, 2),
+                       "attended_tokens_per_pair": round(m["n_att"], 2)},
+            "breakdown_us": m["breakdown"], "delta_fetch": m.get("fetch")}
 
 
 def next_leg(dev, workers, R=4, W=8, K=48):
@@ -483,6 +512,8 @@ def main():
         log("GQA-16 96-block leg")
         res["gqa16_k96"] = next_leg(dev, workers)
     if not args.no_offload:
+        log("offloaded 32K stack leg")
+        res["offload_32k"] = offload_32k_leg(dev, workers)
         log("host-link leg (offloaded 128K workload)")
         with cf.ThreadPoolExecutor(workers) as pool:
             res["host_link"] = host_link_leg(args.offload_steps, pool, dev)
