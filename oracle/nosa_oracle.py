@@ -9,6 +9,7 @@ Sources (the pages are web text; each function names the passage it follows):
   [B1B]   "NOSA-1B 核心组件揭秘" (blog post on the NOSA-1B repository)
   [SPARDA] aliyun article on SparDA ("提前预测下一层 KV 访问范围")
   [L189]  "NOSA原生可卸载稀疏注意力机制解析" (l189.com)
+  [AIW-S] aiwiki "NOSA", section Adoption in SparDA
 
 Everything is float64 except where a rounding is part of the definition
 (compressed keys are bf16, see ``compress_keys``). Inputs are the bf16 bit
@@ -34,6 +35,15 @@ constant below):
       (beta = 1); beta = 0 gives plain attention.
   R13 one (W1, W2) per KV head, no biases.
   R14 compressed keys are stored in bf16, rounded once from the exact mean.
+  R15 SparDA's forecast score: one forecast head per KV group, the logit
+      f . c / sqrt(d) against each compressed key, with neither the softmax
+      nor a sum over heads, max-pooled to blocks like the query-aware score.
+  R16 the layer-ahead selection is taken before the step's token is appended,
+      for the length after that append, from the compressed keys that exist
+      then; the blocks a forecast picks replace stage 1 (query-aware), and
+      stage 2 and the never-reselect rule are NOSA's own.
+  R17 a selected block that holds no token yet (the one the coming token
+      opens) is not fetched: the append creates it on the device.
 All functions are pinned by tests (closed forms, brute force, invariants);
 the readings themselves are definitional, not fixed by the pages.
 """
@@ -222,6 +232,16 @@ def query_chunk_scores(q: np.ndarray, ckeys: np.ndarray) -> np.ndarray:
     return p.sum(axis=0)
 
 
+def forecast_chunk_scores(f: np.ndarray, ckeys: np.ndarray) -> np.ndarray:
+    """SparDA's forecast score of each chunk (R15): the KV group's single
+    forecast head against the compressed keys, as a plain scaled logit --
+    SparDA keeps one forecast head per KV head and drops the softmax used to
+    combine a group's query heads ([SPARDA] 解耦选块与注意力计算, 轻量化设计与训练).
+    f is [d], ckeys is [C][d]."""
+    d = f.shape[0]
+    return (ckeys @ f) / math.sqrt(d)
+
+
 # ----------------------------------------------------------------- selection
 
 def n_blocks(L: int) -> int:
@@ -375,11 +395,29 @@ class PairOracle:
                 self.s[i * POOL_STRIDE:i * POOL_STRIDE + POOL_KERNEL].mean())
         return j
 
-    def select(self, q_group: np.ndarray) -> StepResult:
-        roles = block_roles(self.L, self.n_sink, self.n_win)
+    def _ckeys(self) -> np.ndarray:
         C = len(self.ckeys)
-        ck = np.array(self.ckeys) if C else np.zeros((0, self.K.shape[1]))
-        a = query_chunk_scores(q_group, ck) if C else np.zeros(0)
+        return np.array(self.ckeys) if C else np.zeros((0, self.K.shape[1]))
+
+    def select(self, q_group: np.ndarray) -> StepResult:
+        """NOSA's selection at the current length (after the append)."""
+        ck = self._ckeys()
+        a = query_chunk_scores(q_group, ck) if len(ck) else np.zeros(0)
+        return self._select_at(self.L, a, self.L - 1)
+
+    def select_ahead(self, f: np.ndarray) -> StepResult:
+        """SparDA's layer-ahead selection (R15, R16; [SPARDA]
+        解耦选块与注意力计算, KV 预取的运行时实现): taken before the step's
+        token is appended, for the length L + 1 it will have, with the
+        forecast head f [d] in place of the group's queries."""
+        ck = self._ckeys()
+        a = forecast_chunk_scores(f, ck) if len(ck) else np.zeros(0)
+        return self._select_at(self.L + 1, a, self.L)
+
+    def _select_at(self, L: int, a: np.ndarray, newest: int) -> StepResult:
+        """Both stages and the eligibility update at length L, from the
+        chunk scores a; `newest` is the position of the step's token."""
+        roles = block_roles(L, self.n_sink, self.n_win)
         Qb = block_max_pool(a, roles.nb)
         Eb = block_max_pool(np.array(self.e_chunks), roles.nb)
         # eligibility, [W] How NOSA works: a block not selected at step t is
@@ -392,9 +430,7 @@ class PairOracle:
         sel = select_blocks(Qb, Eb, eligible, roles, self.k_q, self.k_e_dyn)
         self.carry = eligible & set(sel.blocks)
         self.prev_cand = roles.candidates
-        new_block = self.L - 1 if (self.L - 1) % BLOCK == 0 else None
-        if new_block is not None:
-            new_block //= BLOCK
+        new_block = newest // BLOCK if newest % BLOCK == 0 else None
         if self.prev_sel is None:
             misses = [b for b in sel.blocks if b != new_block]
         else:
@@ -402,8 +438,7 @@ class PairOracle:
             misses = [b for b in sel.blocks
                       if b not in have and b != new_block]
         self.prev_sel = list(sel.blocks)
-        return StepResult(self.L, roles, sel, Qb, Eb, eligible, misses,
-                          new_block)
+        return StepResult(L, roles, sel, Qb, Eb, eligible, misses, new_block)
 
     def attend(self, q_group: np.ndarray, blocks) -> np.ndarray:
         return attend(q_group, self.K, self.V, self.s, blocks, self.L,
@@ -413,6 +448,15 @@ class PairOracle:
         """append -> select -> fetch model -> attend, as one decode step."""
         self.append(k_new, v_new)
         r = self.select(q_group)
+        r.out = self.attend(q_group, r.sel.blocks)
+        return r
+
+    def step_ahead(self, f, k_new, v_new, q_group) -> StepResult:
+        """SparDA's order: layer-ahead selection (and fetch) -> append ->
+        attend over the selected blocks with the layer's own queries."""
+        r = self.select_ahead(f)
+        self.append(k_new, v_new)
+        assert self.L == r.L
         r.out = self.attend(q_group, r.sel.blocks)
         return r
 

@@ -249,7 +249,7 @@ def pin_select_reduces_to_plain_topk(o):
 
 
 def _run_pair(o, rng, L0, steps, n_s, n_w, k_q, k_e_dyn, G=2, d=8,
-              hot=False):
+              hot=False, ahead=False):
     cap = L0 + steps
     K = _bf16_vals(rng, (cap, d))
     V = _bf16_vals(rng, (cap, d))
@@ -265,7 +265,11 @@ def _run_pair(o, rng, L0, steps, n_s, n_w, k_q, k_e_dyn, G=2, d=8,
     out = []
     for t in range(steps):
         qg = _bf16_vals(rng, (G, d), 2.0)
-        out.append(p.step(K[L0 + t], V[L0 + t], qg))
+        if ahead:
+            f = _bf16_vals(rng, (d,), 2.0)
+            out.append(p.step_ahead(f, K[L0 + t], V[L0 + t], qg))
+        else:
+            out.append(p.step(K[L0 + t], V[L0 + t], qg))
     return out
 
 
@@ -283,7 +287,7 @@ def pin_agnostic_only_is_streaming_topk(o):
         assert cur.sel.agnostic == want, t
 
 
-def pin_invariants(o, seed=10, cases=12):
+def pin_invariants(o, seed=10, cases=12, ahead=False):
     """Theorem 2's bound gamma(t) >= k_e / k, the eligible set only shrinking
     or extending forward in time ([W] How NOSA works), and the bookkeeping
     facts that follow from the construction."""
@@ -295,7 +299,7 @@ def pin_invariants(o, seed=10, cases=12):
         k_e_dyn = int(rng.integers(0, 6))
         L0 = 64 * int(rng.integers(1, 25)) + int(rng.integers(0, 64))
         res = _run_pair(o, rng, L0, 150, n_s, n_w, k_q, k_e_dyn,
-                        hot=bool(case % 2))
+                        hot=bool(case % 2), ahead=ahead)
         k = n_s + n_w + k_q + k_e_dyn
         k_e = n_s + n_w + k_e_dyn
         E0 = len(res[0].roles.candidates)
@@ -317,6 +321,67 @@ def pin_invariants(o, seed=10, cases=12):
             assert len(r.misses) <= k_q                                # I7
             have = set(p.sel.blocks) | ({r.new_block} - {None})
             assert r.misses == [b for b in S if b not in have]
+
+
+def pin_invariants_ahead(o):
+    """The same bound and bookkeeping when every step selects one layer ahead
+    with a forecast head (SparDA's order: select and fetch, then append):
+    the never-reselect rule and Theorem 2 do not depend on what ranks the
+    query-aware stage."""
+    pin_invariants(o, seed=12, cases=8, ahead=True)
+
+
+# ------------------------------------------------------------------ forecast
+
+def pin_forecast_closed_form(o):
+    """A forecast head against hand-built compressed keys: the plain logit
+    f . c / sqrt(d) per chunk, no normalisation (a softmax would make the
+    values sum to 1)."""
+    d = 128
+    f = np.zeros(d)
+    f[0], f[1] = 2.0 * math.sqrt(d), -math.sqrt(d)
+    c = np.zeros((3, d))
+    c[0, 0] = 1.5                      # 2 * 1.5
+    c[1, 1] = 4.0                      # -1 * 4
+    c[2, 0], c[2, 1] = 0.25, 0.5       # 0.5 - 0.5
+    got = o.forecast_chunk_scores(f, c)
+    assert np.allclose(got, [3.0, -4.0, 0.0], rtol=0, atol=1e-12), got
+
+
+def pin_ahead_equals_single_head_select(o):
+    """Selecting one step ahead with forecast head f picks what NOSA's own
+    selection picks after the append with f as a one-head group: a softmax
+    over one head is increasing in the logit, max-pooling commutes with an
+    increasing map, and the chunk the appended token may complete lies in
+    the window. Started just below block boundaries, so the length used
+    (after the coming token, not before) decides the window and candidates
+    at some steps."""
+    import copy
+    rng = _rng(13)
+    d = 8
+    for case in range(6):
+        n_s, n_w = int(rng.integers(0, 3)), int(rng.integers(2, 5))
+        k_q, k_e_dyn = int(rng.integers(1, 5)), int(rng.integers(0, 5))
+        L0 = 64 * int(rng.integers(4, 20)) + 62 - case
+        cap = L0 + 80
+        K = _bf16_vals(rng, (cap, d))
+        V = _bf16_vals(rng, (cap, d))
+        W1 = _bf16_vals(rng, (d, d), 0.5)
+        W2 = _bf16_vals(rng, (d,), 0.5)
+        a = o.PairOracle(K.copy(), V.copy(), W1, W2, L0, n_s, n_w, k_q,
+                         k_e_dyn, 1.0)
+        b = copy.deepcopy(a)
+        for t in range(70):
+            f = _bf16_vals(rng, (d,), 2.0)
+            ra = a.select_ahead(f)
+            a.append(K[L0 + t], V[L0 + t])
+            b.append(K[L0 + t], V[L0 + t])
+            rb = b.select(f[None, :])
+            assert ra.L == rb.L == L0 + t + 1
+            assert ra.sel.blocks == rb.sel.blocks, (case, t)
+            assert ra.sel.kinds == rb.sel.kinds, (case, t)
+            assert ra.eligible == rb.eligible, (case, t)
+            assert ra.misses == rb.misses, (case, t)
 
 
 # ------------------------------------------------------------------ attention

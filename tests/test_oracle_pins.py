@@ -142,10 +142,31 @@ def _fill_shortfall(o):
     o.select_blocks = select_blocks
 
 
+def _forecast_softmax(o):
+    def forecast_chunk_scores(f, ckeys):
+        x = (ckeys @ f) / math.sqrt(f.shape[0])
+        e = np.exp(x - x.max())
+        return e / e.sum()
+    o.forecast_chunk_scores = forecast_chunk_scores
+
+
+def _forecast_unscaled(o):
+    o.forecast_chunk_scores = lambda f, ckeys: ckeys @ f
+
+
+def _ahead_at_current_length(o):
+    def select_ahead(self, f):
+        ck = self._ckeys()
+        a = o.forecast_chunk_scores(f, ck) if len(ck) else np.zeros(0)
+        return self._select_at(self.L, a, self.L)
+    o.PairOracle.select_ahead = select_ahead
+
+
 MUTATIONS = [_chunks_by_start, _no_score_scale, _softmax_over_heads,
              _transposed_w1, _swapped_pool, _sum_not_mean, _ties_high_index,
              _bias_sign, _window_without_partial, _double_rounding,
-             _float_sum_compress, _evict_on_agnostic_only, _fill_shortfall]
+             _float_sum_compress, _evict_on_agnostic_only, _fill_shortfall,
+             _forecast_softmax, _forecast_unscaled, _ahead_at_current_length]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
