@@ -47,6 +47,12 @@ def parse():
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the host-link leg (offloaded 128K workload)")
     ap.add_argument("--offload-steps", type=int, default=24)
+    ap.add_argument("--no-ahead", action="store_true",
+                    help="skip the layer-ahead (SparDA order) leg")
+    ap.add_argument("--only-ahead", action="store_true",
+                    help="run only the layer-ahead leg and print its JSON")
+    ap.add_argument("--fetch-wg", type=int, default=32,
+                    help="workgroup budget of the layer-ahead fetch")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the hipGraph replay leg of the same layer stack")
     ap.add_argument("--no-next", action="store_true",
@@ -430,6 +436,104 @@ def offload_32k_leg(dev, workers, R=4, W=4, K=24, n_bd=8):
             "breakdown_us": m["breakdown"], "delta_fetch": m.get("fetch")}
 
 
+def forecast_inputs(wl, li, n, pool, device):
+    """Per-step forecast heads that select layer li: [n][B][Hkv][128]."""
+    import numpy as np
+    import torch
+    from synth import forecasts
+    B, Hkv = wl.batch, wl.n_kv_heads
+    wl = wl.replace(steps=max(wl.steps, n))
+    fs = list(pool.map(lambda bg: forecasts(wl, li, *divmod(bg, Hkv))[:n], range(B * Hkv)))
+    f = np.stack(fs).reshape(B, Hkv, n, 128).transpose(2, 0, 1, 3)
+    return torch.from_numpy(np.ascontiguousarray(f).view(np.int16)).to(device)
+
+
+def layer_ahead_leg(dev, workers, R=4, W=4, K=24, n_bd=4, n_wg=32):
+    """SparDA's layer-ahead order on the 1B-shaped 32K stack (64 sequences,
+    16/2 heads, k = 64; R of its 28 layers, layer 0's KV on the GPU and the
+    rest in pinned host memory, as SparDA keeps layer 0 resident): each
+    layer's blocks are selected by a forecast head before its append, and
+    fetched with n_wg looping workgroups. The same layers run K steps
+    layer by layer on one stream, then K steps with layer l+1's selection and
+    fetch on a second stream beside layer l's append and decode."""
+    import numpy as np
+    import torch
+    from synth import WORKLOADS
+    from trainable_offloadable_block_amd import LayerAheadStack, LayerShape
+    wl = WORKLOADS[3]
+    n_tok = 2 * W + 2 * K + n_bd
+    t_setup = time.perf_counter()
+    layers, ins = [], []
+    with cf.ThreadPoolExecutor(workers) as pool:
+        for li in range(R):
+            shape = LayerShape(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_sink_blocks,
+                               wl.window_tokens, wl.k_blocks, wl.k_q_blocks, wl.k_e_blocks,
+                               wl.context + n_tok, offload=li > 0)
+            layers.append(build_layer(wl, li, shape, pool))
+            q, k, v = step_inputs(wl, li, n_tok, pool, dev)
+            ins.append((forecast_inputs(wl, li, n_tok, pool, dev), k, v, q))
+            log(f"layer-ahead: layer {li} ready ({time.perf_counter() - t_setup:.1f}s)")
+    torch.cuda.synchronize()
+    serial = LayerAheadStack(layers, fetch_workgroups=n_wg, overlap=False)
+    overlap = LayerAheadStack(layers, fetch_workgroups=n_wg, overlap=True)
+
+    def run(pipe, t0, n):
+        for t in range(t0, t0 + n):
+            pipe.step([tuple(x[t] for x in ins[li]) for li in range(R)])
+
+    res = {"workload": wl.name + "-layer-ahead", "layers_per_step": R, "steps": K,
+           "fetch_workgroups": n_wg, "unit": "tokens/s/layer",
+           "layer0": "resident (SparDA keeps layer 0 on the GPU)"}
+    t = 0
+    for name, pipe in (("serial", serial), ("overlap", overlap)):
+        run(pipe, t, W)
+        torch.cuda.synchronize()
+        t += W
+        t0 = time.perf_counter()
+        run(pipe, t, K)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        t += K
+        res[name] = {"value": round(wl.batch * R * K / el, 1),
+                     "ms_per_step": round(el * 1e3 / K, 4)}
+    res["speedup"] = round(res["overlap"]["value"] / res["serial"]["value"], 3)
+    # per-call breakdown of the offloaded layers, serial order (untimed)
+    names = ("select_forecast", "fetch_wg", "append", "decode")
+    bd = {n: [] for n in names}
+    fetched = []
+    for _ in range(n_bd):
+        for li in range(1, R):
+            f, k, v, q = (x[t] for x in ins[li])
+            ly = layers[li]
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            evs[0].record()
+            ly.select_forecast(f, want_kind=False)
+            evs[1].record()
+            ly.fetch_wg(n_wg)
+            evs[2].record()
+            ly.append(k, v)
+            evs[3].record()
+            ly.decode(q)
+            evs[4].record()
+            torch.cuda.synchronize()
+            for i, n in enumerate(names):
+                bd[n].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)
+            fetched.append((int(ly.n_miss.sum().item()) * 32768,
+                            evs[1].elapsed_time(evs[2]) * 1e3))
+        t += 1
+    res["breakdown_us"] = {n: round(float(np.median(v)), 2) for n, v in bd.items()}
+    b_ = float(np.mean([x[0] for x in fetched]))
+    us = float(np.mean([x[1] for x in fetched]))
+    res["fetch"] = {"bytes_per_call": int(b_), "us_mean": round(us, 1),
+                    "GBps": round(b_ / (us * 1e-6) / 1e9, 2)}
+    status = [ly.status_bits() for ly in layers]
+    assert not any(status), f"device status bits set: {status}"
+    layers.clear()
+    ins.clear()
+    torch.cuda.empty_cache()
+    return res
+
+
 def next_leg(dev, workers, R=4, W=8, K=48):
     """The GQA-16, 96-block workload (beyond the five benchmark configs):
     step throughput and the decode kernel against the HBM roofline."""
@@ -469,6 +573,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     workers = min(16, len(os.sched_getaffinity(0)))
+    if args.only_ahead:
+        print(json.dumps(layer_ahead_leg(dev, workers, n_wg=args.fetch_wg)), flush=True)
+        return
     wl = WORKLOADS[2]
     R, W, K = args.layers, args.warmup, args.steps
     m = time_stack(wl, R, W, K, args.breakdown_steps, dev, workers,
@@ -514,6 +621,9 @@ def main():
     if not args.no_offload:
         log("offloaded 32K stack leg")
         res["offload_32k"] = offload_32k_leg(dev, workers)
+        if not args.no_ahead:
+            log("layer-ahead leg (SparDA order, offloaded 32K stack)")
+            res["layer_ahead"] = layer_ahead_leg(dev, workers, n_wg=args.fetch_wg)
         log("host-link leg (offloaded 128K workload)")
         with cf.ThreadPoolExecutor(workers) as pool:
             res["host_link"] = host_link_leg(args.offload_steps, pool, dev)

@@ -17,6 +17,13 @@
  *   nosa_sparse_decode    attention over the selected blocks with the
  *                         eviction-score logit bias
  *
+ * SparDA's layer-ahead order (aliyun article on SparDA, 解耦选块与注意力计算
+ * and KV 预取的运行时实现; aiwiki "NOSA", Adoption in SparDA) replaces the
+ * first two calls: while layer l runs, nosa_select_forecast picks layer
+ * l+1's blocks from a forecast head and nosa_fetch_delta_wg brings them in
+ * on a second stream with a bounded number of workgroups; layer l+1 then
+ * runs nosa_compress_append and nosa_sparse_decode.
+ *
  * Conventions
  *  - Every pointer is caller-owned. The library never allocates or frees
  *    memory and keeps no device state of its own.
@@ -59,6 +66,9 @@ enum {
 #define NOSA_STATUS_CAPACITY 1u   /* an append found seq_len == max_context  */
 #define NOSA_STATUS_BAD_SEL  2u   /* fetch/decode saw a block id out of range */
 #define NOSA_STATUS_LEN_HINT 4u   /* select met a length above max_len_host   */
+
+/* largest workgroup budget nosa_fetch_delta_wg accepts */
+#define NOSA_MAX_FETCH_WORKGROUPS 4096
 
 /* config flags */
 #define NOSA_EVICT_BIAS 1u /* add the eviction score s_j to the logits      */
@@ -218,18 +228,55 @@ int nosa_append_select(const nosa_config *cfg, const nosa_state *st,
                        size_t ws_bytes, int32_t max_len_host,
                        hipStream_t stream);
 
+/* SparDA's layer-ahead selection (aliyun article, 解耦选块与注意力计算 and
+ * 轻量化设计与训练): the same two stages, eligibility rule and outputs as
+ * nosa_select, taken BEFORE the step's token is appended, for the length
+ * L = seq_len[b] + 1 that the next nosa_compress_append gives the sequence,
+ * with stage 1 ranked by a forecast head instead of the group's queries:
+ *  - f: dev bf16 [B][Hkv][128], one forecast head per KV group (produced by
+ *    the previous layer);
+ *  - forecast score of a block: max over the compressed keys overlapping it
+ *    of f . ckey / sqrt(128), with no softmax and no sum over heads;
+ *  - every candidate block's chunks exist before the append (window_tokens
+ *    >= 128), so the coming token changes nothing but the window.
+ * dbg_fscore (optional) dev fp32 [B][Hkv][NB_max]: the forecast score of
+ * each candidate. ws: NOSA_WS_SELECT bytes, as for nosa_select;
+ * max_len_host bounds seq_len + 1. The caller then runs nosa_fetch_delta
+ * (or nosa_fetch_delta_wg), nosa_compress_append and nosa_sparse_decode on
+ * this selection, with no other select call in between. */
+int nosa_select_forecast(const nosa_config *cfg, const nosa_state *st,
+                         const uint16_t *f, int32_t *sel, int32_t *n_sel,
+                         uint8_t *kind, float *dbg_fscore, void *ws,
+                         size_t ws_bytes, int32_t max_len_host,
+                         hipStream_t stream);
+
 /* Offload mode only: brings the selected blocks into the device cache.
  * Set difference of sel against the cached blocks (NOSI's set-difference
  * kernel, aiwiki "NOSA", NOSI: the inference system): slots whose block is
  * not selected are freed, each missing block gets a free slot and is copied
  * as one 32 KiB block from the host store (block-wise, not token-wise
- * transfers, aiwiki "NOSA", How NOSA works). Outputs: phys dev int32
+ * transfers, aiwiki "NOSA", How NOSA works). A missing block that holds no
+ * token yet (first position >= seq_len[b]: the block the next append opens,
+ * which a layer-ahead selection includes) gets its slot but is not copied;
+ * the append clears and fills it. Outputs: phys dev int32
  * [B][Hkv][k_blocks] = cache slot of each sel entry (-1 padded); n_miss dev
  * int32 [B][Hkv] = blocks copied. ws: NOSA_WS_FETCH bytes. */
 int nosa_fetch_delta(const nosa_config *cfg, const nosa_state *st,
                      const int32_t *sel, const int32_t *n_sel, int32_t *phys,
                      int32_t *n_miss, void *ws, size_t ws_bytes,
                      hipStream_t stream);
+
+/* nosa_fetch_delta with the copies made by n_workgroups workgroups that
+ * loop over the missing blocks (1 <= n_workgroups <=
+ * NOSA_MAX_FETCH_WORKGROUPS), SparDA's persistent copy kernel with a
+ * workgroup budget (aliyun article, KV 预取的运行时实现): for a fetch that
+ * runs beside compute on another stream and should hold only that many
+ * workgroup slots. Same outputs, state changes and ws as nosa_fetch_delta;
+ * in resident mode identical to it. */
+int nosa_fetch_delta_wg(const nosa_config *cfg, const nosa_state *st,
+                        const int32_t *sel, const int32_t *n_sel,
+                        int32_t *phys, int32_t *n_miss, int32_t n_workgroups,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Sparse attention for the step. For query head h of pair (b, g):
  *   out[b][h] = sum_j softmax_j(q_h . k_j / sqrt(128) + beta * tok_s[j]) v_j

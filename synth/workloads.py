@@ -18,6 +18,9 @@ be regenerated alone):
 * queries follow an AR(1) walk toward mu*u with mu = sqrt(128):
   q_0 = mu*u + xi_0, q_t = rho*q_{t-1} + (1-rho)*mu*u(t) + sqrt(1-rho^2)*xi_t,
   kept in float64 and rounded to bf16 per step
+* forecast heads (SparDA's layer-ahead selection; the trained Forecast
+  projection does not exist here): one per (layer, sequence, KV head), the
+  same AR(1) walk as a query head of that layer, from a stream of its own
 * every decode step appends one token with k, v elements ~ N(0, 1)
 * eviction-head weights W1 [128][128] (input-dim major) and W2 [128], one
   pair per (layer, KV head), elements ~ N(0, 0.02^2) (0.02 is the standard
@@ -38,7 +41,7 @@ HEAD_DIM = 128
 BLOCK = 64
 
 _TAG = {"K": 0, "V": 1, "HOT": 2, "U": 3, "Q": 4, "KNEW": 5, "VNEW": 6,
-        "W1": 7, "W2": 8}
+        "W1": 7, "W2": 8, "F": 9}
 
 
 @dataclass(frozen=True)
@@ -206,9 +209,20 @@ def context_kv(wl: Workload, layer: int, b: int, g: int):
 def queries(wl: Workload, layer: int, b: int, h: int) -> np.ndarray:
     """Per-step queries for one (layer, sequence, q head): uint16 [steps][128]."""
     g = h // wl.group
-    u = _directions(wl, layer, g)
-    mu = math.sqrt(wl.head_dim)
     xi = _rng(wl, "Q", layer, b, h).standard_normal((wl.steps, wl.head_dim))
+    return _ar1_walk(wl, _directions(wl, layer, g), xi)
+
+
+def forecasts(wl: Workload, layer: int, b: int, g: int) -> np.ndarray:
+    """Per-step forecast head that selects layer `layer`'s blocks for one
+    (sequence, KV head): uint16 [steps][128], drawn like a query head of that
+    layer (toward its direction) from its own stream."""
+    xi = _rng(wl, "F", layer, b, g).standard_normal((wl.steps, wl.head_dim))
+    return _ar1_walk(wl, _directions(wl, layer, g), xi)
+
+
+def _ar1_walk(wl: Workload, u: np.ndarray, xi: np.ndarray) -> np.ndarray:
+    mu = math.sqrt(wl.head_dim)
     rho = wl.rho
     out = np.empty((wl.steps, wl.head_dim), dtype=np.float64)
     q = None

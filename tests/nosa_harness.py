@@ -9,6 +9,13 @@ full size). After each step the harness compares, per checked pair:
   checked heads;
 * compressed keys bit for bit, eviction and block scores to float32 error.
 
+Layer-ahead mode (``ahead=True``, SparDA's order): each step selects with
+the synthetic forecast head before the append (nosa_select_forecast against
+PairOracle.step_ahead), then fetches (optionally with a workgroup budget),
+appends and decodes. Forecast scores are plain logits that can sit near 0, so
+their ties and score errors are measured against max(|tau|, rms of the
+candidates' scores) instead of |tau| alone.
+
 Near-tie protocol: when the GPU and the oracle pick different blocks, the
 step still passes if every block in the symmetric difference of the
 query-aware picks scores within 1e-5 (relative) of the oracle's k_q-th best
@@ -31,8 +38,8 @@ import numpy as np
 import torch
 
 import oracle.nosa_oracle as O
-from synth import (bf16_bits_to_f64, context_kv, eviction_weights, new_tokens,
-                   queries)
+from synth import (bf16_bits_to_f64, context_kv, eviction_weights, forecasts,
+                   new_tokens, queries)
 from trainable_offloadable_block_amd import LayerShape, NosaLayer, v_from_tiles
 from trainable_offloadable_block_amd import _lib as L
 
@@ -63,9 +70,12 @@ class StepReport:
 
 class Lockstep:
     def __init__(self, wl, layer=0, check_pairs=None, lengths=None,
-                 offload=None, steps=None, before_prefill=None, fused=False):
+                 offload=None, steps=None, before_prefill=None, fused=False,
+                 ahead=False, fetch_workgroups=0):
         self.wl = wl
         self.fused = fused          # nosa_append_select instead of the two calls
+        self.ahead = ahead          # layer-ahead selection with a forecast head
+        self.fetch_workgroups = fetch_workgroups
         self.layer_idx = layer
         B, Hkv, G = wl.batch, wl.n_kv_heads, wl.group
         self.lengths = np.full(B, wl.context, dtype=np.int64) if lengths is None \
@@ -115,6 +125,10 @@ class Lockstep:
             vn.append(np.stack([x[:self.steps] for x in vv]))
         self.knew = np.stack(kn)   # [B][Hkv][steps][128]
         self.vnew = np.stack(vn)
+        self.f = None
+        if ahead:
+            self.f = np.stack([np.stack([forecasts(wl, layer, b, g)[:self.steps]
+                                         for g in range(Hkv)]) for b in range(B)])
         self.reports = []
 
     # ---------------------------------------------------------------- inputs
@@ -152,8 +166,11 @@ class Lockstep:
         if gq != oq:
             ranked = sorted(cand, key=lambda b: (-res.Qb[b], b))
             tau = res.Qb[ranked[min(len(ranked), self.wl.k_q_blocks) - 1]]
+            ref = abs(tau)
+            if self.ahead:
+                ref = max(ref, math.sqrt(float(np.mean(res.Qb[cand] ** 2))))
             for b in gq ^ oq:
-                if abs(res.Qb[b] - tau) > TIE_REL * abs(tau):
+                if abs(res.Qb[b] - tau) > TIE_REL * ref:
                     return False
         pool = [b for b in cand if b in res.eligible and b not in gq]
         agn = set(O.top_by_score(pool, res.Eb, self.k_e_dyn))
@@ -179,12 +196,21 @@ class Lockstep:
         wl, G, Hkv, k = self.wl, self.wl.group, self.wl.n_kv_heads, self.wl.k_blocks
         kd, vd, qd = self.inputs(t)
         g = self.gpu
-        if self.fused:
+        if self.ahead:
+            g.select_forecast(self._dev(self.f[:, :, t]), want_kind=True,
+                              want_fscore=check_scores)
+            if self.fetch_workgroups:
+                g.fetch_wg(self.fetch_workgroups)
+            else:
+                g.fetch()
+            g.append(kd, vd)
+        elif self.fused:
             g.append_select(kd, vd, qd, want_kind=True, want_qscore=check_scores)
+            g.fetch()
         else:
             g.append(kd, vd)
             g.select(qd, want_kind=True, want_qscore=check_scores)
-        g.fetch()
+            g.fetch()
         g.decode(qd)
         torch.cuda.synchronize()
         sel = g.sel.cpu().numpy().reshape(self.P, k)
@@ -198,8 +224,13 @@ class Lockstep:
         for p, o in self.oracles.items():
             b, gg = divmod(p, Hkv)
             qg = bf16_bits_to_f64(self.q[b, gg * G:(gg + 1) * G, t])
-            res = o.step(bf16_bits_to_f64(self.knew[b, gg, t]),
-                         bf16_bits_to_f64(self.vnew[b, gg, t]), qg)
+            if self.ahead:
+                res = o.step_ahead(bf16_bits_to_f64(self.f[b, gg, t]),
+                                   bf16_bits_to_f64(self.knew[b, gg, t]),
+                                   bf16_bits_to_f64(self.vnew[b, gg, t]), qg)
+            else:
+                res = o.step(bf16_bits_to_f64(self.knew[b, gg, t]),
+                             bf16_bits_to_f64(self.vnew[b, gg, t]), qg)
             results[p] = res
             gb = [int(x) for x in sel[p, :nsel[p]]]
             gk = {int(x): int(c) for x, c in zip(sel[p, :nsel[p]], kind[p, :nsel[p]])}
@@ -241,7 +272,10 @@ class Lockstep:
                 if not c:
                     continue
                 if wl.k_q_blocks > 0:
-                    qr = np.abs(dq[p, c] - res.Qb[c]) / np.abs(res.Qb[c])
+                    den = np.abs(res.Qb[c])
+                    if self.ahead:
+                        den = np.maximum(den, math.sqrt(float(np.mean(res.Qb[c] ** 2))))
+                    qr = np.abs(dq[p, c] - res.Qb[c]) / den
                     rep.qscore_rel = max(rep.qscore_rel, float(qr.max()))
                 scale = math.sqrt(float(np.mean(res.Eb[c] ** 2)))
                 er = np.abs(be[p, c] - res.Eb[c]) / scale

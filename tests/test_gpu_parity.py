@@ -305,3 +305,88 @@ def test_graph_replay_matches_eager(offload):
         for n in sa:
             assert torch.equal(sa[n], sb[n]), f"replay {t}: state {n}"
     assert a.gpu.status_bits() == 0 and b.gpu.status_bits() == 0
+
+
+# ------------------------------------------------- SparDA layer-ahead order
+
+@pytest.mark.parametrize("offload", [False, True])
+def test_forecast_small(offload):
+    """Selection one layer ahead with a forecast head (before the append, for
+    the length after it) against the oracle over 80 steps from 1000 and 963
+    tokens: chunk and block completions, a block opened at 1024 (selected
+    before it holds a token: given a slot, not fetched) and the window
+    sliding by a block."""
+    wl = small_workload(151, context=1000, steps=80, offload=offload)
+    _run(wl, lengths=[1000, 963], ahead=True, cache_every=7)
+
+
+def test_forecast_fetch_wg_long_offload():
+    """Layer-ahead selection with the fetch made by 3 looping workgroups
+    (many entries each) over 150 steps: copies equal the oracle's misses."""
+    wl = small_workload(152, offload=True, steps=150, context=2048, k_blocks=12,
+                        k_q_blocks=3, k_e_blocks=9, n_hot=4, batch=3)
+    _run(wl, ahead=True, fetch_workgroups=3, cache_every=25)
+
+
+def test_forecast_1b_32k_sampled():
+    """One offloaded layer of the 1B-shaped 32K stack (64 sequences) in the
+    layer-ahead order with a 32-workgroup fetch: 3 sampled pairs."""
+    _run(WORKLOADS[3], layer=7, check_pairs=[0, 64, 127], steps=8, cache_every=4,
+         ahead=True, fetch_workgroups=32)
+
+
+@pytest.mark.parametrize("n_wg", [1, 7, 64])
+def test_fetch_wg_equals_fetch(n_wg):
+    """nosa_fetch_delta_wg with any workgroup budget leaves the same slot
+    maps, phys, copy counts and cache bytes as nosa_fetch_delta."""
+    wl = small_workload(153, context=1500, steps=40, offload=True, k_blocks=12,
+                        k_q_blocks=4, k_e_blocks=8, batch=3)
+    a = Lockstep(wl, check_pairs=[])
+    b = Lockstep(wl, check_pairs=[])
+    for t in range(wl.steps):
+        kd, vd, qd = a.inputs(t)
+        for ls in (a, b):
+            ls.gpu.append_select(kd, vd, qd)
+        a.gpu.fetch()
+        b.gpu.fetch_wg(n_wg)
+        torch.cuda.synchronize()
+        for n in ("phys", "n_miss"):
+            assert torch.equal(getattr(a.gpu, n), getattr(b.gpu, n)), f"step {t}: {n}"
+        sa, sb = _state_tensors(a.gpu), _state_tensors(b.gpu)
+        for n in sa:
+            assert torch.equal(sa[n], sb[n]), f"step {t}: state {n}"
+
+
+def _stack(wl, n_layers):
+    # layer 0 keeps its KV on the GPU (as SparDA does); the rest offload
+    return [Lockstep(wl, layer=li, check_pairs=[], ahead=True, offload=li > 0)
+            for li in range(n_layers)]
+
+
+def test_layer_ahead_stack_overlap_equals_serial():
+    """The two-stream cross-layer pipeline (layer l+1's selection and fetch on
+    a second stream while layer l appends and decodes) gives, bit for bit,
+    the outputs, selections and state of the same stack run layer by layer
+    on one stream, over 70 steps of 3 layers."""
+    from trainable_offloadable_block_amd import LayerAheadStack
+    wl = small_workload(154, context=1000, steps=70)
+    sa, sb = _stack(wl, 3), _stack(wl, 3)
+    pa = LayerAheadStack([ls.gpu for ls in sa], fetch_workgroups=8, overlap=True)
+    pb = LayerAheadStack([ls.gpu for ls in sb], fetch_workgroups=8, overlap=False)
+    for t in range(wl.steps):
+        for pipe, st in ((pa, sa), (pb, sb)):
+            ins = []
+            for ls in st:
+                kd, vd, qd = ls.inputs(t)
+                ins.append((ls._dev(ls.f[:, :, t]), kd, vd, qd))
+            pipe.step(ins)
+        torch.cuda.synchronize()
+        for la, lb in zip(sa, sb):
+            for n in ("sel", "n_sel", "phys", "n_miss", "out"):
+                assert torch.equal(getattr(la.gpu, n), getattr(lb.gpu, n)), f"step {t}: {n}"
+            ta, tb = _state_tensors(la.gpu), _state_tensors(lb.gpu)
+            for n in ta:
+                assert torch.equal(ta[n], tb[n]), f"step {t}: state {n}"
+    for st in (sa, sb):
+        for ls in st:
+            assert ls.gpu.status_bits() == 0

@@ -11,4 +11,6 @@ from ._lib import (  # noqa: F401
     KIND_AGNOSTIC, KIND_NONE, KIND_QUERY, KIND_SINK, KIND_WINDOW,
     NosaConfig, NosaError, NosaState, header_functions, lib,
 )
-from .layer import LayerShape, NosaLayer, to_block_layout, v_from_tiles, v_to_tiles  # noqa: F401
+from .layer import (  # noqa: F401
+    LayerAheadStack, LayerShape, NosaLayer, to_block_layout, v_from_tiles, v_to_tiles,
+)

@@ -30,6 +30,8 @@ NOSA_STATUS_CAPACITY = 1
 NOSA_STATUS_BAD_SEL = 2
 NOSA_STATUS_LEN_HINT = 4
 
+NOSA_MAX_FETCH_WORKGROUPS = 4096
+
 NOSA_EVICT_BIAS = 1
 NOSA_OFFLOAD = 2
 
@@ -90,6 +92,10 @@ def lib():
                                               ctypes.c_size_t, _I32, _P]),
         "nosa_fetch_delta": (ctypes.c_int, [cfgp, stp, _P, _P, _P, _P, _P,
                                             ctypes.c_size_t, _P]),
+        "nosa_select_forecast": (ctypes.c_int, [cfgp, stp, _P, _P, _P, _P, _P, _P,
+                                                ctypes.c_size_t, _I32, _P]),
+        "nosa_fetch_delta_wg": (ctypes.c_int, [cfgp, stp, _P, _P, _P, _P, _I32, _P,
+                                               ctypes.c_size_t, _P]),
         "nosa_sparse_decode": (ctypes.c_int, [cfgp, stp, _P, _P, _P, _P, _P,
                                               _P, ctypes.c_size_t, _I32, _P]),
         "nosa_host_alias": (ctypes.c_int, [_P, ctypes.POINTER(_P)]),

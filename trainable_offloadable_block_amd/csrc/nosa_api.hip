@@ -198,9 +198,25 @@ int nosa_append_select(const nosa_config *cfg, const nosa_state *st, const uint1
                                                dbg_qscore, ws, lay, stream));
 }
 
-int nosa_fetch_delta(const nosa_config *cfg, const nosa_state *st, const int32_t *sel,
-                     const int32_t *n_sel, int32_t *phys, int32_t *n_miss, void *ws,
-                     size_t ws_bytes, hipStream_t stream) {
+int nosa_select_forecast(const nosa_config *cfg, const nosa_state *st, const uint16_t *f,
+                         int32_t *sel, int32_t *n_sel, uint8_t *kind, float *dbg_fscore,
+                         void *ws, size_t ws_bytes, int32_t max_len_host, hipStream_t stream) {
+  nosa::Dims d;
+  int rc = make_dims(cfg, &d);
+  if (!rc) rc = check_state(d, st);
+  if (!rc) rc = check_len(d, max_len_host);
+  if (rc) return rc;
+  if (!f || !sel || !n_sel) return fail(NOSA_ERR_INVALID, "f / sel / n_sel is NULL");
+  const nosa::SelectLayout lay = nosa::select_layout(d, max_len_host);
+  rc = check_ws(ws, ws_bytes, lay.bytes);
+  if (rc) return rc;
+  return hip_result(
+      nosa::launch_select_forecast(d, *st, f, sel, n_sel, kind, dbg_fscore, ws, lay, stream));
+}
+
+static int fetch_common(const nosa_config *cfg, const nosa_state *st, const int32_t *sel,
+                        const int32_t *n_sel, int32_t *phys, int32_t *n_miss, int n_wg,
+                        void *ws, size_t ws_bytes, hipStream_t stream) {
   nosa::Dims d;
   int rc = make_dims(cfg, &d);
   if (!rc) rc = check_state(d, st);
@@ -212,7 +228,21 @@ int nosa_fetch_delta(const nosa_config *cfg, const nosa_state *st, const int32_t
     rc = check_ws(ws, ws_bytes, lay.bytes);
     if (rc) return rc;
   }
-  return hip_result(nosa::launch_fetch(d, *st, sel, n_sel, phys, n_miss, ws, lay, stream));
+  return hip_result(nosa::launch_fetch(d, *st, sel, n_sel, phys, n_miss, ws, lay, stream, n_wg));
+}
+
+int nosa_fetch_delta(const nosa_config *cfg, const nosa_state *st, const int32_t *sel,
+                     const int32_t *n_sel, int32_t *phys, int32_t *n_miss, void *ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  return fetch_common(cfg, st, sel, n_sel, phys, n_miss, 0, ws, ws_bytes, stream);
+}
+
+int nosa_fetch_delta_wg(const nosa_config *cfg, const nosa_state *st, const int32_t *sel,
+                        const int32_t *n_sel, int32_t *phys, int32_t *n_miss,
+                        int32_t n_workgroups, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (n_workgroups < 1 || n_workgroups > NOSA_MAX_FETCH_WORKGROUPS)
+    return fail(NOSA_ERR_INVALID, "n_workgroups outside [1, NOSA_MAX_FETCH_WORKGROUPS]");
+  return fetch_common(cfg, st, sel, n_sel, phys, n_miss, n_workgroups, ws, ws_bytes, stream);
 }
 
 int nosa_sparse_decode(const nosa_config *cfg, const nosa_state *st, const uint16_t *q,

@@ -7,10 +7,19 @@
 // setdiff_kernel: one wavefront per pair. Slots whose block left the
 //   selection are freed; each selected block that is not cached takes a free
 //   slot (lowest first, in ascending block order) and becomes a copy-list
-//   entry. O(k) work, a lane per selection entry (two for k > 64) and per
-//   cache slot.
+//   entry, unless it holds no token yet (a selection made one layer ahead,
+//   before the append, includes the block the coming token opens: the
+//   append creates it in its slot). O(k) work, a lane per selection entry
+//   (two for k > 64) and per cache slot.
 // gather_kernel: copies each listed 32 KiB block from the host store to its
-//   cache slot, reading host memory through its device alias.
+//   cache slot, reading host memory through its device alias; one
+//   workgroup per list entry.
+// gather_wg_kernel: the same copies by a fixed number of workgroups that
+//   loop over the entries (SparDA's persistent copy kernel with a workgroup
+//   budget, aliyun article, KV 预取的运行时实现), so a fetch running beside
+//   compute on another stream holds only that many workgroup slots.
+#include <stdlib.h>
+
 #include "nosa_internal.h"
 
 namespace nosa {
@@ -31,6 +40,7 @@ __global__ __launch_bounds__(64) void setdiff_kernel(
   for (int i = l; i < d.elig_words; i += 64) sel_bits[i] = 0u;
   __syncthreads();
   const int ns = max(0, min(n_sel[p], d.k));
+  const int L = st.seq_len[p / d.Hkv];          // blocks at or past it hold no token
   // lane l holds selection entries l and l + 64 (k <= 128)
   constexpr int kPer = kMaxK / 64;
   int blk[kPer];
@@ -68,8 +78,9 @@ __global__ __launch_bounds__(64) void setdiff_kernel(
   }
   __syncthreads();
 
-  // misses take free slots in order (entry order = ascending block order)
-  int n_missed = 0;
+  // misses take free slots in order (entry order = ascending block order);
+  // those that hold tokens are listed for copying
+  int n_missed = 0, n_copy = 0;
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     const int e = l + 64 * r;
@@ -77,22 +88,26 @@ __global__ __launch_bounds__(64) void setdiff_kernel(
     const bool miss = blk[r] >= 0 && slot < 0;
     const unsigned long long mm = __ballot(miss);
     const int rank = n_missed + __popcll(mm & ((1ull << l) - 1ull));
+    const bool copy = miss && rank < n_free && blk[r] * kBlock < L;
+    const unsigned long long cm = __ballot(copy);
+    const int crank = n_copy + __popcll(cm & ((1ull << l) - 1ull));
     if (miss) {
       slot = rank < n_free ? free_list[rank] : -1;
       if (slot >= 0) {
         bos_new[slot] = blk[r];
         sob[blk[r]] = slot;
-        list[(size_t)p * d.k + rank] = make_int2(blk[r], slot);
+        if (copy) list[(size_t)p * d.k + crank] = make_int2(blk[r], slot);
       } else {
         atomicOr(st.status, NOSA_STATUS_BAD_SEL);
       }
     }
     n_missed += __popcll(mm);
+    n_copy += __popcll(cm);
     if (e < d.k) phys[(size_t)p * d.k + e] = e < ns ? slot : -1;
   }
   __syncthreads();
   for (int s = l; s < slots; s += 64) bos[s] = bos_new[s];
-  if (l == 0) n_miss[p] = min(n_missed, n_free);
+  if (l == 0) n_miss[p] = n_copy;
 }
 
 // grid (k, P), block 256: entry r of pair p, if it exists.
@@ -111,6 +126,42 @@ __global__ __launch_bounds__(256) void gather_kernel(
   for (int j = 0; j < kVec / 256; ++j) v[j] = src[threadIdx.x + 256 * j];
 #pragma unroll
   for (int j = 0; j < kVec / 256; ++j) dst[threadIdx.x + 256 * j] = v[j];
+}
+
+// grid (n_wg), block 256: workgroup i copies list entries i, i + n_wg, ...
+// in entry-major order (entry r of every pair before entry r + 1), up to
+// the largest copy count over the pairs; each block moves in pieces of
+// VPT * 4 KiB, so a workgroup has at most that much host data in flight.
+template <int VPT>
+__global__ __launch_bounds__(256) void gather_wg_kernel(
+    Dims d, const uint16_t *__restrict__ host, uint16_t *__restrict__ cache,
+    const int32_t *__restrict__ n_miss, const int2 *__restrict__ list) {
+  __shared__ int red[4];
+  int m = 0;
+  for (int i = threadIdx.x; i < d.P; i += 256) m = max(m, n_miss[i]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) m = max(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const int mx = min(max(max(red[0], red[1]), max(red[2], red[3])), d.k);
+  const int total = mx * d.P;
+  constexpr int kVec = kBlockElems * 2 / 16;   // 2048 uint4 per block
+  for (int task = blockIdx.x; task < total; task += gridDim.x) {   // uniform
+    const int r = task / d.P, p = task - r * d.P;
+    if (r >= n_miss[p]) continue;
+    const int2 e = list[(size_t)p * d.k + r];
+    const uint4 *src = reinterpret_cast<const uint4 *>(
+        host + ((size_t)p * d.NB_max + e.x) * kBlockElems);
+    uint4 *dst = reinterpret_cast<uint4 *>(cache + ((size_t)p * (d.k + 1) + e.y) * kBlockElems);
+#pragma unroll
+    for (int j0 = 0; j0 < kVec / 256; j0 += VPT) {
+      uint4 v[VPT];
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) v[j] = src[threadIdx.x + 256 * (j0 + j)];
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) dst[threadIdx.x + 256 * (j0 + j)] = v[j];
+    }
+  }
 }
 
 // Resident KV: every selected block already sits in the device pool at its
@@ -134,7 +185,7 @@ FetchLayout fetch_layout(const Dims &d) {
 
 hipError_t launch_fetch(const Dims &d, const nosa_state &st, const int32_t *sel,
                         const int32_t *n_sel, int32_t *phys, int32_t *n_miss,
-                        void *ws, const FetchLayout &lay, hipStream_t s) {
+                        void *ws, const FetchLayout &lay, hipStream_t s, int n_wg) {
   if (!d.offload) {
     resident_phys_kernel<<<dim3(d.P), 64, 0, s>>>(d, sel, phys, n_miss);
     return hipGetLastError();
@@ -142,7 +193,19 @@ hipError_t launch_fetch(const Dims &d, const nosa_state &st, const int32_t *sel,
   int2 *list = reinterpret_cast<int2 *>(static_cast<char *>(ws) + lay.list_off);
   setdiff_kernel<<<dim3(d.P), 64, (size_t)d.elig_words * sizeof(uint32_t), s>>>(
       d, st, sel, n_sel, phys, n_miss, list);
-  gather_kernel<<<dim3(d.k, d.P), 256, 0, s>>>(d, st.kv_host, st.kv_dev, n_miss, list);
+  if (n_wg > 0) {
+    int vpt = 8;
+    if (const char *env = getenv("NOSA_GATHER_VPT")) vpt = atoi(env);
+    if (vpt == 1)
+      gather_wg_kernel<1><<<dim3(n_wg), 256, 0, s>>>(d, st.kv_host, st.kv_dev, n_miss, list);
+    else if (vpt == 2)
+      gather_wg_kernel<2><<<dim3(n_wg), 256, 0, s>>>(d, st.kv_host, st.kv_dev, n_miss, list);
+    else if (vpt == 4)
+      gather_wg_kernel<4><<<dim3(n_wg), 256, 0, s>>>(d, st.kv_host, st.kv_dev, n_miss, list);
+    else
+      gather_wg_kernel<8><<<dim3(n_wg), 256, 0, s>>>(d, st.kv_host, st.kv_dev, n_miss, list);
+  } else
+    gather_kernel<<<dim3(d.k, d.P), 256, 0, s>>>(d, st.kv_host, st.kv_dev, n_miss, list);
   return hipGetLastError();
 }
 

@@ -48,10 +48,16 @@ hipError_t launch_append_select(const Dims &d, const nosa_state &st,
                                 const uint16_t *q, int32_t *sel, int32_t *n_sel,
                                 uint8_t *kind, float *dbg_qscore, void *ws,
                                 const SelectLayout &lay, hipStream_t s);
+hipError_t launch_select_forecast(const Dims &d, const nosa_state &st,
+                                  const uint16_t *f, int32_t *sel,
+                                  int32_t *n_sel, uint8_t *kind,
+                                  float *dbg_fscore, void *ws,
+                                  const SelectLayout &lay, hipStream_t s);
+// n_wg > 0: copy with that many looping workgroups; 0: one per list entry
 hipError_t launch_fetch(const Dims &d, const nosa_state &st,
                         const int32_t *sel, const int32_t *n_sel,
                         int32_t *phys, int32_t *n_miss, void *ws,
-                        const FetchLayout &lay, hipStream_t s);
+                        const FetchLayout &lay, hipStream_t s, int n_wg = 0);
 hipError_t launch_decode(const Dims &d, const nosa_state &st,
                          const uint16_t *q, const int32_t *sel,
                          const int32_t *phys, const int32_t *n_sel,

@@ -407,6 +407,83 @@ __device__ __forceinline__ void select_stages(const Dims &d, int p, int n_cand, 
 constexpr int kMaxCandPerThread = (kMaxContext / kBlock) / kTopkThreads;   // 16
 constexpr int kLoadBatch = 8;     // chunk-weight float4 loads in flight per thread
 
+// Both stages, the ascending selection list and the eligibility update of
+// pair p at a length with nb blocks, once the chunk scores a_sh[0, C), the
+// eligibility words el_sh and the kinds of the sink and window blocks sit in
+// LDS (kind[] of every other block NOSA_KIND_NONE); e0 is candidate t's
+// agnostic score, loaded early. Called by all threads.
+__device__ __forceinline__ void finish_select(const Dims &d, const nosa_state &st, int p, int nb,
+                                              int win_lo, int n_cand, int C, bool do_q,
+                                              bool do_e, const float *a_sh,
+                                              const uint32_t *el_sh, const float *be, float e0,
+                                              uint8_t *kind, int32_t *sel, int32_t *n_sel,
+                                              uint8_t *kind_out, float *dbg, TopkLds &tk) {
+  __shared__ int cnt_sh[2][kTopkThreads / 64];
+  const int t = threadIdx.x;
+  const int w = t >> 6, lane = t & 63;
+  // 3. both stages, with as many candidate slots per thread as needed
+  {
+    const int m = (n_cand + kTopkThreads - 1) / kTopkThreads;   // <= kMaxCandPerThread
+    if (m <= 1)
+      select_stages<1>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
+    else if (m <= 2)
+      select_stages<2>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
+    else if (m <= 4)
+      select_stages<4>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
+    else if (m <= 8)
+      select_stages<8>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
+    else
+      select_stages<kMaxCandPerThread>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind,
+                                       dbg, tk);
+  }
+  __syncthreads();
+
+  // 4. ascending selection list: ballot + prefix count per 256 blocks
+  {
+    int32_t *sp = sel + (size_t)p * d.k;
+    uint8_t *kp = kind_out ? kind_out + (size_t)p * d.k : nullptr;
+    int running = 0;
+    for (int base = 0; base < nb; base += kTopkThreads) {            // uniform
+      const int bb = base + t;
+      const bool in = bb < nb && kind[bb] != NOSA_KIND_NONE;
+      const uint64_t mask = __ballot(in);
+      const int below = __popcll(mask & ((1ull << lane) - 1ull));
+      if (lane == 0) cnt_sh[(base / kTopkThreads) & 1][w] = __popcll(mask);
+      __syncthreads();
+      const int *cs = cnt_sh[(base / kTopkThreads) & 1];
+      int off = running, tot = 0;
+#pragma unroll
+      for (int ww = 0; ww < kTopkThreads / 64; ++ww) {
+        if (ww < w) off += cs[ww];
+        tot += cs[ww];
+      }
+      off += below;
+      if (in && off < d.k) {
+        sp[off] = bb;
+        if (kp) kp[off] = kind[bb];
+      }
+      running += tot;
+    }
+    for (int j = running + t; j < d.k; j += kTopkThreads) {
+      sp[j] = -1;
+      if (kp) kp[j] = NOSA_KIND_NONE;
+    }
+    if (t == 0) n_sel[p] = min(running, d.k);
+  }
+
+  // 5. eligibility: a candidate outside the selection is out for good
+  if (n_cand > 0) {
+    uint32_t *el = st.eligible + (size_t)p * d.elig_words;
+    for (int base = 64 * w; base < win_lo; base += kTopkThreads) {   // wave-uniform
+      const int bb = base + lane;
+      const bool out = bb >= d.n_sink && bb < win_lo && kind[bb] == NOSA_KIND_NONE;
+      const uint64_t mask = __ballot(out);
+      const uint32_t clear = static_cast<uint32_t>(mask >> (lane & 32));
+      if ((lane & 31) == 0 && clear) el[bb >> 5] = el_sh[bb >> 5] & ~clear;
+    }
+  }
+}
+
 // Pooling and both stages for pair p, run by the pair's last score
 // workgroup once every split has published (so the chunk weights and split
 // statistics are read with device-coherent loads).
@@ -426,7 +503,6 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
   uint8_t *kind = reinterpret_cast<uint8_t *>(el_sh + d.elig_words);        // [NB_max]
   __shared__ TopkLds tk;
   __shared__ float lnew_sh[kMaxGroup], wlast_sh[kMaxGroup];
-  __shared__ int cnt_sh[2][kTopkThreads / 64];
 
   const int t = threadIdx.x;
   const int w = t >> 6, lane = t & 63;
@@ -581,67 +657,8 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
   }
   __syncthreads();
 
-  // 3. both stages, with as many candidate slots per thread as needed
-  {
-    const int m = (n_cand + kTopkThreads - 1) / kTopkThreads;   // <= kMaxCandPerThread
-    if (m <= 1)
-      select_stages<1>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
-    else if (m <= 2)
-      select_stages<2>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
-    else if (m <= 4)
-      select_stages<4>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
-    else if (m <= 8)
-      select_stages<8>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, dbg, tk);
-    else
-      select_stages<kMaxCandPerThread>(d, p, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind,
-                                       dbg, tk);
-  }
-  __syncthreads();
-
-  // 4. ascending selection list: ballot + prefix count per 256 blocks
-  {
-    int32_t *sp = sel + (size_t)p * d.k;
-    uint8_t *kp = kind_out ? kind_out + (size_t)p * d.k : nullptr;
-    int running = 0;
-    for (int base = 0; base < nb; base += kTopkThreads) {            // uniform
-      const int bb = base + t;
-      const bool in = bb < nb && kind[bb] != NOSA_KIND_NONE;
-      const uint64_t mask = __ballot(in);
-      const int below = __popcll(mask & ((1ull << lane) - 1ull));
-      if (lane == 0) cnt_sh[(base / kTopkThreads) & 1][w] = __popcll(mask);
-      __syncthreads();
-      const int *cs = cnt_sh[(base / kTopkThreads) & 1];
-      int off = running, tot = 0;
-#pragma unroll
-      for (int ww = 0; ww < kTopkThreads / 64; ++ww) {
-        if (ww < w) off += cs[ww];
-        tot += cs[ww];
-      }
-      off += below;
-      if (in && off < d.k) {
-        sp[off] = bb;
-        if (kp) kp[off] = kind[bb];
-      }
-      running += tot;
-    }
-    for (int j = running + t; j < d.k; j += kTopkThreads) {
-      sp[j] = -1;
-      if (kp) kp[j] = NOSA_KIND_NONE;
-    }
-    if (t == 0) n_sel[p] = min(running, d.k);
-  }
-
-  // 5. eligibility: a candidate outside the selection is out for good
-  if (n_cand > 0) {
-    uint32_t *el = st.eligible + (size_t)p * d.elig_words;
-    for (int base = 64 * w; base < win_lo; base += kTopkThreads) {   // wave-uniform
-      const int bb = base + lane;
-      const bool out = bb >= d.n_sink && bb < win_lo && kind[bb] == NOSA_KIND_NONE;
-      const uint64_t mask = __ballot(out);
-      const uint32_t clear = static_cast<uint32_t>(mask >> (lane & 32));
-      if ((lane & 31) == 0 && clear) el[bb >> 5] = el_sh[bb >> 5] & ~clear;
-    }
-  }
+  finish_select(d, st, p, nb, win_lo, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, sel,
+                n_sel, kind_out, dbg, tk);
 }
 
 }  // namespace

@@ -257,6 +257,30 @@ class NosaLayer:
             _ptr(self.phys), _ptr(self.n_miss), _ptr(self.ws_fetch), self.ws_fetch.numel(),
             self.stream), "fetch_delta")
 
+    def select_forecast(self, f: torch.Tensor, want_kind=True, want_fscore=False):
+        """SparDA's layer-ahead selection, taken before this step's append
+        for the length it will give: stage 1 ranked by the forecast head f
+        (dev bf16 [B][Hkv][128]); stage 2 and eligibility as select()."""
+        if want_fscore and self.dbg_q is None:
+            self.dbg_q = torch.full((self.shape.pairs * self.shape.nb_max,), float("nan"),
+                                    dtype=torch.float32, device=self.device)
+        L.check(L.lib().nosa_select_forecast(
+            ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(f), _ptr(self.sel),
+            _ptr(self.n_sel), _ptr(self.kind) if want_kind else ctypes.c_void_p(0),
+            _ptr(self.dbg_q) if want_fscore else ctypes.c_void_p(0),
+            _ptr(self.ws_select), self.ws_select.numel(),
+            min(self.max_len + 1, self.shape.max_context), self.stream), "select_forecast")
+
+    def fetch_wg(self, n_workgroups: int, force=False):
+        """fetch() with the copies made by n_workgroups looping workgroups
+        (for a fetch that runs beside compute on another stream)."""
+        if not self.shape.offload and not force:
+            return
+        L.check(L.lib().nosa_fetch_delta_wg(
+            ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(self.sel), _ptr(self.n_sel),
+            _ptr(self.phys), _ptr(self.n_miss), int(n_workgroups), _ptr(self.ws_fetch),
+            self.ws_fetch.numel(), self.stream), "fetch_delta_wg")
+
     def decode(self, q: torch.Tensor, sel=None, phys=None, n_sel=None):
         sel = self.sel if sel is None else sel
         if phys is None:
@@ -275,6 +299,18 @@ class NosaLayer:
         self.decode(q)
         return self.out
 
+    def step_ahead(self, f, k_new, v_new, q, fetch_workgroups=0, want_kind=False):
+        """One layer in SparDA's order, on one stream: layer-ahead selection
+        -> fetch -> append -> decode."""
+        self.select_forecast(f, want_kind=want_kind)
+        if fetch_workgroups:
+            self.fetch_wg(fetch_workgroups)
+        else:
+            self.fetch()
+        self.append(k_new, v_new)
+        self.decode(q)
+        return self.out
+
     # ------------------------------------------------------------ views
     def status_bits(self) -> int:
         return int(self.status.cpu().item()) & 0xFFFFFFFF
@@ -282,3 +318,65 @@ class NosaLayer:
     def eligible_words(self) -> np.ndarray:
         words = (self.shape.nb_max + 31) // 32
         return self.eligible.cpu().numpy().view(np.uint32).reshape(self.shape.pairs, words)
+
+
+class LayerAheadStack:
+    """SparDA's cross-layer pipeline over a stack of layers (aliyun article,
+    KV 预取的运行时实现): when layer l starts, its forecast head selects layer
+    l+1's blocks and the fetch of those blocks starts on a second stream,
+    while layer l appends and attends on the main stream; layer l+1 waits for
+    its fetch before its append. The first layer selects with its own
+    forecast head and fetches (when offloaded) on the main stream. Both
+    streams keep the default priority.
+
+    Ordering: the side stream starts layer l+1's work after an event the main
+    stream records once layer l-1's decode is enqueued, so it follows layer
+    l+1's previous decode (which reads the slots it refills) and append
+    (which moved its length); the main stream's append of layer l+1 follows
+    the fetch that reassigns its cache slots.
+    """
+
+    def __init__(self, layers, fetch_workgroups: int = 32, overlap: bool = True):
+        self.layers = list(layers)
+        self.fetch_workgroups = int(fetch_workgroups)
+        self.overlap = overlap
+        dev = self.layers[0].device
+        self.side = torch.cuda.Stream(device=dev)
+        n = len(self.layers)
+        self.ev_start = [torch.cuda.Event() for _ in range(n)]
+        self.ev_fetch = [torch.cuda.Event() for _ in range(n)]
+
+    def _select_fetch(self, layer, f):
+        layer.select_forecast(f, want_kind=False)
+        if self.fetch_workgroups:
+            layer.fetch_wg(self.fetch_workgroups)
+        else:
+            layer.fetch()
+
+    def step(self, inputs):
+        """inputs[l] = (f, k_new, v_new, q) of layer l for this step, where f
+        is the forecast head that selects layer l (made by layer l-1, or
+        layer 0's own). Enqueues the whole step; returns the layers' outputs
+        (written when the main stream reaches them)."""
+        main = torch.cuda.current_stream(self.layers[0].device)
+        n = len(self.layers)
+        if not self.overlap:
+            for layer, (f, k, v, q) in zip(self.layers, inputs):
+                self._select_fetch(layer, f)
+                layer.append(k, v)
+                layer.decode(q)
+            return [layer.out for layer in self.layers]
+        self._select_fetch(self.layers[0], inputs[0][0])
+        for li in range(n):
+            if li + 1 < n:
+                self.ev_start[li].record(main)
+                with torch.cuda.stream(self.side):
+                    self.side.wait_event(self.ev_start[li])
+                    self._select_fetch(self.layers[li + 1], inputs[li + 1][0])
+                    self.ev_fetch[li + 1].record(self.side)
+            if li > 0:
+                main.wait_event(self.ev_fetch[li])
+            _, k, v, q = inputs[li]
+            self.layers[li].append(k, v)
+            self.layers[li].decode(q)
+        return [layer.out for layer in self.layers]
