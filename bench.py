@@ -526,12 +526,53 @@ def layer_ahead_leg(dev, workers, R=4, W=4, K=24, n_bd=4, n_wg=32):
     us = float(np.mean([x[1] for x in fetched]))
     res["fetch"] = {"bytes_per_call": int(b_), "us_mean": round(us, 1),
                     "GBps": round(b_ / (us * 1e-6) / 1e9, 2)}
+    res["decode_beside_us"] = decode_beside(layers[1], ins[1][3][t - 1], layers[2], n_wg)
     status = [ly.status_bits() for ly in layers]
     assert not any(status), f"device status bits set: {status}"
     layers.clear()
     ins.clear()
     torch.cuda.empty_cache()
     return res
+
+
+def decode_beside(dec_layer, q, fetch_layer, n_wg, n=6):
+    """Median decode-launch time (us) of dec_layer alone, beside a large
+    delta fetch of fetch_layer on a second stream (its cache emptied first,
+    so every selected block is copied by n_wg workgroups reading host
+    memory), and beside a 256 MiB pinned-host-to-device copy on the DMA
+    engines. fetch_layer is not stepped afterwards: emptying its cache drops
+    the tokens its newest block holds only there.""" 
+    import numpy as np
+    import torch
+    side = torch.cuda.Stream()
+    pin = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(256 << 20, dtype=torch.uint8, device=dec_layer.device)
+
+    def decodes():
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a, b in evs:
+            a.record()
+            dec_layer.decode(q)
+            b.record()
+        return evs
+
+    out = {}
+    for mode in ("alone", "fetch_wg", "dma_copy"):
+        torch.cuda.synchronize()
+        if mode == "fetch_wg":
+            fetch_layer.slot_of_block.fill_(-1)
+            fetch_layer.block_of_slot.fill_(-1)
+            torch.cuda.synchronize()
+            with torch.cuda.stream(side):
+                fetch_layer.fetch_wg(n_wg)
+        elif mode == "dma_copy":
+            with torch.cuda.stream(side):
+                dst.copy_(pin, non_blocking=True)
+        evs = decodes()
+        torch.cuda.synchronize()
+        out[mode] = round(float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs])), 1)
+    return out
 
 
 def next_leg(dev, workers, R=4, W=8, K=48):

@@ -178,9 +178,14 @@ int nosa_prefill_init(const nosa_config *cfg, const nosa_state *st,
 
 /* Appends one token per pair at position seq_len[b] and increments
  * seq_len[b]. k_new, v_new: dev bf16 [B][Hkv][128].
- *  - writes K, V into kv_dev (resident) or into the host store, and into the
- *    cache slot of its block when that block is cached (offload); a token
- *    that opens a new block takes a free cache slot for it;
+ *  - writes K, V into kv_dev (resident), or (offload) into the cache slot
+ *    of its block, a token that opens a new block taking a free slot for it;
+ *    the host store receives a block from its cache slot, whole, when the
+ *    block's last token arrives (it stays cached until then: every
+ *    selection holds the window), and a token whose block is not cached
+ *    (before the first fetch) goes to the host store directly. A selection
+ *    passed to nosa_fetch_delta must therefore include each sequence's
+ *    newest block, as every nosa_select / nosa_select_forecast result does;
  *  - tok_s[pos] = softplus(v W1) W2 in fp32 (aiwiki "NOSA", How NOSA works;
  *    l189 article, 2.1, eq. 4);
  *  - when a 32-token chunk completes (L >= 32 and (L - 32) % 16 == 0):

@@ -35,14 +35,14 @@ constant below):
       (beta = 1); beta = 0 gives plain attention.
   R13 one (W1, W2) per KV head, no biases.
   R14 compressed keys are stored in bf16, rounded once from the exact mean.
-  R15 SparDA's forecast score: one forecast head per KV group, the logit
+  R19 SparDA's forecast score: one forecast head per KV group, the logit
       f . c / sqrt(d) against each compressed key, with neither the softmax
       nor a sum over heads, max-pooled to blocks like the query-aware score.
-  R16 the layer-ahead selection is taken before the step's token is appended,
+  R20 the layer-ahead selection is taken before the step's token is appended,
       for the length after that append, from the compressed keys that exist
       then; the blocks a forecast picks replace stage 1 (query-aware), and
       stage 2 and the never-reselect rule are NOSA's own.
-  R17 a selected block that holds no token yet (the one the coming token
+  R21 a selected block that holds no token yet (the one the coming token
       opens) is not fetched: the append creates it on the device.
 All functions are pinned by tests (closed forms, brute force, invariants);
 the readings themselves are definitional, not fixed by the pages.
@@ -233,7 +233,7 @@ def query_chunk_scores(q: np.ndarray, ckeys: np.ndarray) -> np.ndarray:
 
 
 def forecast_chunk_scores(f: np.ndarray, ckeys: np.ndarray) -> np.ndarray:
-    """SparDA's forecast score of each chunk (R15): the KV group's single
+    """SparDA's forecast score of each chunk (R19): the KV group's single
     forecast head against the compressed keys, as a plain scaled logit --
     SparDA keeps one forecast head per KV head and drops the softmax used to
     combine a group's query heads ([SPARDA] 解耦选块与注意力计算, 轻量化设计与训练).
@@ -406,7 +406,7 @@ class PairOracle:
         return self._select_at(self.L, a, self.L - 1)
 
     def select_ahead(self, f: np.ndarray) -> StepResult:
-        """SparDA's layer-ahead selection (R15, R16; [SPARDA]
+        """SparDA's layer-ahead selection (R19, R20; [SPARDA]
         解耦选块与注意力计算, KV 预取的运行时实现): taken before the step's
         token is appended, for the length L + 1 it will have, with the
         forecast head f [d] in place of the group's queries."""

@@ -316,8 +316,10 @@ class Lockstep:
         torch.cuda.synchronize()
 
     def check_cache(self):
-        """Offload mode: each selected block's cache slot holds exactly the
-        host store's bytes for that block."""
+        """Offload mode: each selected block's cache slot holds the oracle's
+        K and V for the block's existing tokens, and a complete block's host
+        copy equals its cache slot (the host store receives a block when its
+        last token arrives; until then the cache holds the newest tokens)."""
         g, k = self.gpu, self.wl.k_blocks
         sel = g.sel.cpu().numpy().reshape(self.P, k)
         phys = g.phys.cpu().numpy().reshape(self.P, k)
@@ -327,17 +329,22 @@ class Lockstep:
         host = g.kv_host.view(self.P, self.shape.nb_max, 2, 64, 128)
         for p in self.check:
             Lb = int(seq[p // self.wl.n_kv_heads])
+            o = self.oracles.get(p)
             for i in range(nsel[p]):
                 blk = int(sel[p, i])
                 n = min(64, Lb - 64 * blk)        # tokens that exist
                 a = cache[p, phys[p, i]].cpu()
-                h = host[p, blk]
-                # K rows, then V in tile order
-                av = v_from_tiles(a[1].reshape(-1).numpy())
-                hv = v_from_tiles(h[1].reshape(-1).numpy())
-                same = (torch.equal(a[0, :n], h[0, :n]) and
-                        np.array_equal(av[:n], hv[:n]))
-                assert same, f"pair {p} block {blk}: cache bytes differ"
+                ak = a[0, :n].numpy().view(np.uint16)
+                av = v_from_tiles(a[1].reshape(-1).numpy())[:n].view(np.uint16)
+                if o is not None:
+                    rows = slice(64 * blk, 64 * blk + n)
+                    assert np.array_equal(ak, O.bf16_bits(o.K[rows])), \
+                        f"pair {p} block {blk}: cached K differs from the oracle"
+                    assert np.array_equal(av, O.bf16_bits(o.V[rows])), \
+                        f"pair {p} block {blk}: cached V differs from the oracle"
+                if n == 64:
+                    h = host[p, blk]
+                    assert torch.equal(a, h), f"pair {p} block {blk}: host copy differs"
 
     def run(self, steps=None, check_scores=True, cache_every=0):
         n = self.steps if steps is None else steps

@@ -123,11 +123,12 @@ __device__ __forceinline__ int append_pair(const Dims &d, const nosa_state &st, 
       base[kBlock * kHeadDim + v_index(r, t)] = vb;
     }
   } else {
+    // offload: the token goes to its block's cache slot; the host store gets
+    // the whole block, in coalesced 16-byte writes, when its last token
+    // arrives (a block stays cached until then: the window holds it). A token
+    // whose block is not cached (before the first fetch) goes to the host
+    // store directly.
     uint16_t *hb = st.kv_host + ((size_t)p * d.NB_max + blk) * kBlockElems;
-    if (dim) {
-      hb[r * kHeadDim + t] = kb;
-      hb[kBlock * kHeadDim + v_index(r, t)] = vb;
-    }
     int32_t *sob = st.slot_of_block + (size_t)p * d.NB_max;
     int32_t *bos = st.block_of_slot + (size_t)p * (d.k + 1);
     if (t == 0) sh.slot_sh = sob[blk];
@@ -157,6 +158,15 @@ __device__ __forceinline__ int append_pair(const Dims &d, const nosa_state &st, 
         cb[r * kHeadDim + t] = kb;
         cb[kBlock * kHeadDim + v_index(r, t)] = vb;
       }
+      if (r == kBlock - 1) {               // complete: write it back
+        __syncthreads();
+        const uint4 *c4 = reinterpret_cast<const uint4 *>(cb);
+        uint4 *h4 = reinterpret_cast<uint4 *>(hb);
+        for (int i = t; i < kBlockElems * 2 / 16; i += NT) h4[i] = c4[i];
+      }
+    } else if (dim) {
+      hb[r * kHeadDim + t] = kb;
+      hb[kBlock * kHeadDim + v_index(r, t)] = vb;
     }
   }
 
