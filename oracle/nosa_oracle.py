@@ -44,6 +44,11 @@ constant below):
       stage 2 and the never-reselect rule are NOSA's own.
   R21 a selected block that holds no token yet (the one the coming token
       opens) is not fetched: the append creates it on the device.
+  R22 sparse prefill (NOSA_S, sparse in both phases): a prompt query at
+      position i is scored exactly as a decode step at length i + 1 would
+      score it -- over the chunks complete at that length, candidates between
+      the sink and that length's window -- so many queries' scores are one
+      causal product against the compressed keys.
 All functions are pinned by tests (closed forms, brute force, invariants);
 the readings themselves are definitional, not fixed by the pages.
 """
@@ -240,6 +245,32 @@ def forecast_chunk_scores(f: np.ndarray, ckeys: np.ndarray) -> np.ndarray:
     f is [d], ckeys is [C][d]."""
     d = f.shape[0]
     return (ckeys @ f) / math.sqrt(d)
+
+
+def prefill_block_scores(Q: np.ndarray, pos0: int, ckeys: np.ndarray,
+                         n_sink: int, n_win: int) -> np.ndarray:
+    """Query-aware block scores of many prompt queries at once (R22; the
+    query-aware score of [B1B] 核心组件三 and R3, applied per query with
+    causal chunk sets; NOSA_S is sparse in both phases, [W] Results).
+
+    Q is [T][G][d]: query i sits at position pos0 + i. ckeys holds at least
+    every chunk complete at length pos0 + T. Returns [T][nb] with nb the block
+    count at length pos0 + T: row i holds Q_b for the candidate blocks of
+    length pos0 + i + 1 and -inf elsewhere.
+    """
+    T = Q.shape[0]
+    nb_all = n_blocks(pos0 + T)
+    out = np.full((T, nb_all), -np.inf)
+    for i in range(T):
+        L = pos0 + i + 1
+        C = n_chunks(L)
+        roles = block_roles(L, n_sink, n_win)
+        if C == 0 or not roles.candidates:
+            continue
+        a = query_chunk_scores(Q[i], ckeys[:C])
+        Qb = block_max_pool(a, roles.nb)
+        out[i, roles.candidates] = Qb[roles.candidates]
+    return out
 
 
 # ----------------------------------------------------------------- selection

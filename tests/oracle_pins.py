@@ -384,6 +384,49 @@ def pin_ahead_equals_single_head_select(o):
             assert ra.misses == rb.misses, (case, t)
 
 
+# ------------------------------------------------------------------ prefill
+
+def pin_prefill_scores_match_decode(o):
+    """A prompt query at position L - 1 gets the block scores NOSA's decode
+    selection computes at length L for the same query (the decode path is
+    pinned above), over 150 steps crossing chunk, block and window
+    boundaries."""
+    rng = _rng(14)
+    d, G = 8, 2
+    L0, steps = 64 * 6 + 5, 150
+    K = _bf16_vals(rng, (L0 + steps, d))
+    V = _bf16_vals(rng, (L0 + steps, d))
+    W1 = _bf16_vals(rng, (d, d), 0.5)
+    W2 = _bf16_vals(rng, (d,), 0.5)
+    p = o.PairOracle(K.copy(), V.copy(), W1, W2, L0, 1, 2, 3, 2, 1.0)
+    for t in range(steps):
+        qg = _bf16_vals(rng, (G, d), 2.0)
+        p.append(K[L0 + t], V[L0 + t])
+        r = p.select(qg)
+        got = o.prefill_block_scores(qg[None], p.L - 1, np.array(p.ckeys), 1, 2)
+        c = r.roles.candidates
+        assert np.array_equal(got[0, c], r.Qb[c]), t
+        others = [b for b in range(got.shape[1]) if b not in set(c)]
+        assert np.all(got[0, others] == -np.inf), t
+
+
+def pin_prefill_scores_causal(o):
+    """Row i depends only on tokens up to position pos0 + i: rewriting every
+    later key leaves it unchanged, while the last row sees them."""
+    rng = _rng(15)
+    d, G, T, pos0 = 8, 4, 70, 64 * 5 + 3
+    K = _bf16_vals(rng, (pos0 + T, d))
+    Q = _bf16_vals(rng, (T, G, d), 2.0)
+    base = o.prefill_block_scores(Q, pos0, o.compress_keys(K, pos0 + T), 1, 2)
+    for i in (0, 17, 40, T - 2):
+        K2 = K.copy()
+        K2[pos0 + i + 1:] = _bf16_vals(rng, (T - i - 1, d), 3.0)
+        got = o.prefill_block_scores(Q, pos0, o.compress_keys(K2, pos0 + T), 1, 2)
+        assert np.array_equal(got[:i + 1], base[:i + 1]), i
+        if T - 1 - i >= 48:                   # a complete chunk of the last row changed
+            assert not np.array_equal(got[T - 1], base[T - 1]), i
+
+
 # ------------------------------------------------------------------ attention
 
 def pin_attention_full_coverage_sdpa(o):

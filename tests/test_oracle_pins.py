@@ -162,11 +162,36 @@ def _ahead_at_current_length(o):
     o.PairOracle.select_ahead = select_ahead
 
 
+def _prefill_off_by_one(o):
+    orig = o.prefill_block_scores
+
+    def prefill_block_scores(Q, pos0, ckeys, n_sink, n_win):
+        return orig(Q, pos0 - 1, ckeys, n_sink, n_win)[:, :o.n_blocks(pos0 + Q.shape[0])] \
+            if pos0 > 0 else orig(Q, pos0, ckeys, n_sink, n_win)
+    o.prefill_block_scores = prefill_block_scores
+
+
+def _prefill_not_causal(o):
+    def prefill_block_scores(Q, pos0, ckeys, n_sink, n_win):
+        T = Q.shape[0]
+        out = np.full((T, o.n_blocks(pos0 + T)), -np.inf)
+        C = o.n_chunks(pos0 + T)                  # every chunk, for every row
+        for i in range(T):
+            roles = o.block_roles(pos0 + i + 1, n_sink, n_win)
+            if C and roles.candidates:
+                a = o.query_chunk_scores(Q[i], ckeys[:C])
+                Qb = o.block_max_pool(a, roles.nb)
+                out[i, roles.candidates] = Qb[roles.candidates]
+        return out
+    o.prefill_block_scores = prefill_block_scores
+
+
 MUTATIONS = [_chunks_by_start, _no_score_scale, _softmax_over_heads,
              _transposed_w1, _swapped_pool, _sum_not_mean, _ties_high_index,
              _bias_sign, _window_without_partial, _double_rounding,
              _float_sum_compress, _evict_on_agnostic_only, _fill_shortfall,
-             _forecast_softmax, _forecast_unscaled, _ahead_at_current_length]
+             _forecast_softmax, _forecast_unscaled, _ahead_at_current_length,
+             _prefill_off_by_one, _prefill_not_causal]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
