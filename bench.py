@@ -78,8 +78,18 @@ def build_layer(wl, li, shape, pool):
     ctx = list(pool.map(lambda p: context_kv(wl, li, *divmod(p, wl.n_kv_heads)), range(P)))
     for p, (K, V) in enumerate(ctx):
         layer.load_pair_context(p, K, V)
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
     layer.prefill([wl.context] * wl.batch)
+    e1.record()
+    torch.cuda.synchronize()
+    PREFILL_MS.append((wl.name, e0.elapsed_time(e1)))
     return layer
+
+
+PREFILL_MS = []          # (workload, ms) of every nosa_prefill_init call
 
 
 def step_inputs(wl, li, n, pool, device):
@@ -600,6 +610,7 @@ def main():
               "decode path has no cross-GPU step; pairs would shard by sequence "
               "or KV head with no exchange.", file=sys.stderr)
         sys.exit(2)
+    import numpy as np
     import torch
     from synth import WORKLOADS
 
@@ -656,6 +667,14 @@ def main():
     }
     if "graph" in m:
         res["graph_replay"] = m["graph"]
+    pf = [ms for name, ms in PREFILL_MS if name == wl.name]
+    if pf:
+        # the state build reads every context token's K and V once (512 B)
+        ms = float(np.median(pf))
+        byt = wl.batch * wl.n_kv_heads * wl.context * 512
+        res["state_build"] = {"call": "nosa_prefill_init", "ms_per_layer": round(ms, 3),
+                              "context_tokens_per_s": round(wl.batch * wl.context / (ms * 1e-3), 1),
+                              "kv_GBps": round(byt / (ms * 1e-3) / 1e9, 1)}
     if not args.no_next:
         log("GQA-16 96-block leg")
         res["gqa16_k96"] = next_leg(dev, workers)

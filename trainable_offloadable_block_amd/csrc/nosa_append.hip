@@ -1,5 +1,6 @@
 // Append + CompressK + eviction score (one decode step), and the bulk
-// version used once to build the state from a prefilled context.
+// version used once to build the state from a prefilled context (the
+// eviction head of every prefilled token as a dense MFMA product).
 //
 // Eviction head: s_j = softplus(v_j W1) W2, fp32 (aiwiki "NOSA", How NOSA
 // works; l189 article, 2.1, eq. 4). CompressK: the mean of 32 keys with
@@ -37,31 +38,87 @@ __global__ __launch_bounds__(128) void append_kernel(
 }
 
 // ------------------------------------------------------------- prefill
-// Eviction scores of every prefilled token. grid (blocks, P), block 128:
-// the V half of one 64-token block is staged in LDS, then one token at a
-// time goes through the same eviction head as append.
-__global__ __launch_bounds__(128) void prefill_scores_kernel(Dims d, nosa_state st) {
-  const int blk = blockIdx.x, p = blockIdx.y, t = threadIdx.x;
+// Eviction scores of every prefilled token as one dense product on MFMA:
+// S = V W1 (tokens x hidden, bf16 in, fp32 accumulate), then
+// s = softplus(S) W2 per token. grid (ceil(blocks / kPfBlocks), P), 4 waves:
+// W1 is staged once per workgroup, transposed to [hidden][input] so a lane's
+// 8 consecutive inputs are one 16-byte LDS read; each 64-token block's V part
+// (tile order) is staged as [token][dim]; wave w takes tokens 16w .. 16w+15
+// of the block against all 128 hidden units (8 column tiles x 4 k-steps).
+constexpr int kPfBlocks = 8;                 // 64-token blocks per workgroup
+constexpr int kPfPad = kHeadDim + 8;         // LDS row pitch (elements)
+
+__global__ __launch_bounds__(256) void prefill_scores_kernel(Dims d, nosa_state st) {
+  const int p = blockIdx.y, t = threadIdx.x;
   const int b = p / d.Hkv, g = p % d.Hkv;
   const int L = min(st.seq_len[b], d.max_context);
-  if (blk * kBlock >= L) return;
-  __shared__ uint4 vt_sh[kBlock * kHeadDim * 2 / 16];   // V part, 16 KiB
-  __shared__ float v_sh[kHeadDim];
-  __shared__ float red2[2];
-  __shared__ __align__(16) uint16_t w1_sh[kHeadDim * kHeadDim];
-  const uint16_t *src = (d.offload ? st.kv_host : st.kv_dev) +
-                        ((size_t)p * d.NB_max + blk) * kBlockElems + kBlock * kHeadDim;
-  const uint4 *src4 = reinterpret_cast<const uint4 *>(src);
-  for (int i = t; i < kBlock * kHeadDim * 2 / 16; i += blockDim.x) vt_sh[i] = src4[i];
-  stage_w1(w1_sh, st.w1 + (size_t)g * kHeadDim * kHeadDim);   // ends in a barrier
-  const uint16_t *vt = reinterpret_cast<const uint16_t *>(vt_sh);
-  const int n = min(kBlock, L - blk * kBlock);
+  const int blk0 = blockIdx.x * kPfBlocks;
+  if (blk0 * kBlock >= L) return;
+  __shared__ __align__(16) uint16_t w1t[kHeadDim * kPfPad];   // [hidden][input]
+  __shared__ __align__(16) uint16_t vs[kBlock * kPfPad];      // [token][dim]
+  __shared__ float w2s[kHeadDim];
+  const int w = t >> 6, l = t & 63, lr = l & 15, lg = l >> 4;
+
+  {   // W1 [input][hidden] -> w1t[hidden][input]
+    const uint4 *src = reinterpret_cast<const uint4 *>(st.w1 + (size_t)g * kHeadDim * kHeadDim);
+#pragma unroll
+    for (int j = 0; j < kHeadDim * kHeadDim / 8 / 256; ++j) {
+      const int i = t + 256 * j;             // 16-byte piece: input e, hidden 8h8 .. 8h8+7
+      const int e = i >> 4, h8 = i & 15;
+      const uint4 v = src[i];
+      const uint16_t *x = reinterpret_cast<const uint16_t *>(&v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) w1t[(8 * h8 + q) * kPfPad + e] = x[q];
+    }
+    if (t < kHeadDim) w2s[t] = bf16_to_f32(st.w2[(size_t)g * kHeadDim + t]);
+  }
+  const uint16_t *kvb = d.offload ? st.kv_host : st.kv_dev;
   float *tok_s = st.tok_s + (size_t)p * d.tok_stride;
-  for (int r = 0; r < n; ++r) {
-    v_sh[t] = bf16_to_f32(vt[v_index(r, t)]);
+  const int blk_end = min(blk0 + kPfBlocks, blocks_for(L));
+  for (int blk = blk0; blk < blk_end; ++blk) {
+    __syncthreads();                         // W1 staged / previous block's vs consumed
+    {   // V part, tile order -> vs[token][dim]
+      const uint4 *src = reinterpret_cast<const uint4 *>(
+          kvb + ((size_t)p * d.NB_max + blk) * kBlockElems + kBlock * kHeadDim);
+#pragma unroll
+      for (int j = 0; j < kBlock * kHeadDim / 8 / 256; ++j) {
+        const int gi = t + 256 * j;           // 8 tokens of one dim
+        const int half = gi >> 9, ct = (gi >> 6) & 7, tg = (gi >> 4) & 3, c16 = gi & 15;
+        const int tok0 = 32 * half + 8 * tg, dim = 16 * ct + c16;
+        const uint4 v = src[gi];
+        const uint16_t *x = reinterpret_cast<const uint16_t *>(&v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) vs[(tok0 + q) * kPfPad + dim] = x[q];
+      }
+    }
     __syncthreads();
-    const float s = evict_score_128(v_sh, w1_sh, st.w2 + (size_t)g * kHeadDim, red2);
-    if (t == 0) tok_s[blk * kBlock + r] = s;
+    bf16x8 a[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      a[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(&vs[(16 * w + lr) * kPfPad + 32 * ks + 8 * lg]));
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 bop = as_bf16x8(
+            *reinterpret_cast<const uint4 *>(&w1t[(16 * ct + lr) * kPfPad + 32 * ks + 8 * lg]));
+        acc = mfma16x16x32(a[ks], bop, acc);
+      }
+      // lane (lr, lg): tokens 16w + 4lg + i against hidden unit 16ct + lr
+      const float w2v = w2s[16 * ct + lr];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[i] = fmaf(softplus_f32(acc[i]), w2v, part[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = part[i];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
+      const int tok = blk * kBlock + 16 * w + 4 * lg + i;
+      if (lr == 0 && tok < L) tok_s[tok] = x;
+    }
   }
 }
 
@@ -149,7 +206,7 @@ hipError_t launch_prefill(const Dims &d, const nosa_state &st, int max_len,
                           hipStream_t s) {
   const int nbl = blocks_for(max_len);
   if (nbl > 0) {
-    prefill_scores_kernel<<<dim3(nbl, d.P), 128, 0, s>>>(d, st);
+    prefill_scores_kernel<<<dim3((nbl + kPfBlocks - 1) / kPfBlocks, d.P), 256, 0, s>>>(d, st);
     prefill_chunks_kernel<<<dim3(nbl, d.P), 128, 0, s>>>(d, st);
   }
   const int span = d.NB_max > d.elig_words ? d.NB_max : d.elig_words;
