@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the host-link leg (offloaded 128K workload)")
     ap.add_argument("--offload-steps", type=int, default=24)
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the many-query block-score (sparse prefill) leg")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="run only the many-query block-score leg and print its JSON")
     ap.add_argument("--no-ahead", action="store_true",
                     help="skip the layer-ahead (SparDA order) leg")
     ap.add_argument("--only-ahead", action="store_true",
@@ -585,6 +589,51 @@ def decode_beside(dec_layer, q, fetch_layer, n_wg, n=6):
     return out
 
 
+def prefill_scores_leg(dev, workers, T=4096, K=10):
+    """Block scores of T prompt queries per sequence at once (the selection
+    side of NOSA_S's sparse prefill) on the 16K 1B-shaped layer: the last T
+    positions of the 16K prompt, all 64 pairs; MFMA rate of the logits."""
+    import numpy as np
+    import torch
+    from synth import WORKLOADS, queries
+    from trainable_offloadable_block_amd import LayerShape
+    wl = WORKLOADS[2]
+    pos0 = wl.context - T
+    shape = LayerShape(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_sink_blocks,
+                       wl.window_tokens, wl.k_blocks, wl.k_q_blocks, wl.k_e_blocks,
+                       wl.context + 1)
+    with cf.ThreadPoolExecutor(workers) as pool:
+        layer = build_layer(wl, 0, shape, pool)
+        wq = wl.replace(steps=T)
+        B, Hq = wl.batch, wl.n_q_heads
+        qs = list(pool.map(lambda bh: queries(wq, 0, *divmod(bh, Hq)), range(B * Hq)))
+    q = np.stack(qs).reshape(B, Hq, T, 128).transpose(0, 2, 1, 3)
+    qd = torch.from_numpy(np.ascontiguousarray(q).view(np.int16)).to(dev)
+    del qs, q
+    layer.prefill_block_scores(qd, T, pos0)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for a, b in evs:
+        a.record()
+        layer.prefill_block_scores(qd, T, pos0)
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+    assert layer.status_bits() == 0
+    chunks = sum((pos0 + i + 1 - 32) // 16 + 1 for i in range(T))          # per (query, head)
+    flops = 2.0 * 128 * chunks * wl.n_q_heads * wl.batch                    # one logit pass
+    nb = -(-(pos0 + T) // 64)
+    out_bytes = wl.batch * wl.n_kv_heads * T * nb * 4
+    del layer, qd
+    torch.cuda.empty_cache()
+    return {"workload": wl.name + "-prompt-scores", "queries_per_sequence": T, "pos0": pos0,
+            "us": round(us, 1), "queries_per_s": round(wl.batch * T / (us * 1e-6), 1),
+            "logit_TFLOPs": round(flops / (us * 1e-6) / 1e12, 1), "peak_TFLOPs": 2500.0,
+            "frac": round(flops / (us * 1e-6) / 1e12 / 2500.0, 4),
+            "out_bytes": out_bytes}
+
+
 def next_leg(dev, workers, R=4, W=8, K=48):
     """The GQA-16, 96-block workload (beyond the five benchmark configs):
     step throughput and the decode kernel against the HBM roofline."""
@@ -627,6 +676,9 @@ def main():
     workers = min(16, len(os.sched_getaffinity(0)))
     if args.only_ahead:
         print(json.dumps(layer_ahead_leg(dev, workers, n_wg=args.fetch_wg)), flush=True)
+        return
+    if args.only_prefill:
+        print(json.dumps(prefill_scores_leg(dev, workers)), flush=True)
         return
     wl = WORKLOADS[2]
     R, W, K = args.layers, args.warmup, args.steps
@@ -675,6 +727,9 @@ def main():
         res["state_build"] = {"call": "nosa_prefill_init", "ms_per_layer": round(ms, 3),
                               "context_tokens_per_s": round(wl.batch * wl.context / (ms * 1e-3), 1),
                               "kv_GBps": round(byt / (ms * 1e-3) / 1e9, 1)}
+    if not args.no_prefill:
+        log("prefill block-score leg")
+        res["prefill_scores"] = prefill_scores_leg(dev, workers)
     if not args.no_next:
         log("GQA-16 96-block leg")
         res["gqa16_k96"] = next_leg(dev, workers)

@@ -66,6 +66,7 @@ enum {
 #define NOSA_STATUS_CAPACITY 1u   /* an append found seq_len == max_context  */
 #define NOSA_STATUS_BAD_SEL  2u   /* fetch/decode saw a block id out of range */
 #define NOSA_STATUS_LEN_HINT 4u   /* select met a length above max_len_host   */
+#define NOSA_STATUS_SHORT_CONTEXT 8u /* prefill scores asked past seq_len   */
 
 /* largest workgroup budget nosa_fetch_delta_wg accepts */
 #define NOSA_MAX_FETCH_WORKGROUPS 4096
@@ -295,6 +296,24 @@ int nosa_sparse_decode(const nosa_config *cfg, const nosa_state *st,
                        const int32_t *phys, const int32_t *n_sel, float *out,
                        void *ws, size_t ws_bytes, int32_t max_len_host,
                        hipStream_t stream);
+
+/* Block scores of many prompt queries at once: the selection side of NOSA_S's
+ * sparse prefill (aiwiki "NOSA", Results: NOSA_S is sparse in both phases),
+ * each query scored exactly as a decode step at its own length would score it
+ * (the query-aware score of nosa_select; NOSA-1B 核心组件揭秘, 核心组件三).
+ * q: dev bf16 [B][n_queries][Hq][128]; query i of every sequence sits at
+ * position pos0 + i, and the state (nosa_prefill_init) must already hold the
+ * prompt up to pos0 + n_queries (seq_len[b] >= pos0 + n_queries; a sequence
+ * that falls short sets NOSA_STATUS_SHORT_CONTEXT and gets no output).
+ * out: dev fp32 [B][Hkv][n_queries][nb], nb = ceil((pos0 + n_queries) / 64):
+ * row i holds, for each candidate block of length L = pos0 + i + 1 (between
+ * the sink and L's window), the max over the block's chunks of the sum over
+ * the group's heads of the per-head softmax over the chunks complete at L of
+ * q . ckey / sqrt(128); -inf for every other block. One dense MFMA product
+ * per (query, head) row against the compressed keys. */
+int nosa_prefill_block_scores(const nosa_config *cfg, const nosa_state *st,
+                              const uint16_t *q, int32_t n_queries,
+                              int32_t pos0, float *out, hipStream_t stream);
 
 /* Device-usable address of pinned host memory (hipHostGetDevicePointer);
  * allocates nothing. */

@@ -133,6 +133,21 @@ def test_calls_reject_before_any_hip_call():
                            260, 1 << 40, 16640, null) == L.NOSA_ERR_WORKSPACE
     assert lib.nosa_sparse_decode(ctypes.byref(c), ctypes.byref(st), 256, 256, 256, 256,
                                   256, null, 0, 16640, null) == L.NOSA_ERR_WORKSPACE
+    # forecast selection: workspace too small; budgeted fetch: bad budget
+    assert lib.nosa_select_forecast(ctypes.byref(c), ctypes.byref(st), 256, 256, 256, null,
+                                    null, 256, 16, 16640, null) == L.NOSA_ERR_WORKSPACE
+    for n_wg in (0, -3, L.NOSA_MAX_FETCH_WORKGROUPS + 1):
+        assert lib.nosa_fetch_delta_wg(ctypes.byref(c), ctypes.byref(st), 256, 256, 256, 256,
+                                       n_wg, 256, 1 << 20, null) == L.NOSA_ERR_INVALID
+    # prefill scores: no queries, negative position, past max_context, NULL out
+    assert lib.nosa_prefill_block_scores(ctypes.byref(c), ctypes.byref(st), 256, 0, 0, 256,
+                                         null) == L.NOSA_ERR_INVALID
+    assert lib.nosa_prefill_block_scores(ctypes.byref(c), ctypes.byref(st), 256, 4, -1, 256,
+                                         null) == L.NOSA_ERR_INVALID
+    assert lib.nosa_prefill_block_scores(ctypes.byref(c), ctypes.byref(st), 256, 64,
+                                         c.max_context - 10, 256, null) == L.NOSA_ERR_CAPACITY
+    assert lib.nosa_prefill_block_scores(ctypes.byref(c), ctypes.byref(st), 256, 4, 0, None,
+                                         null) == L.NOSA_ERR_INVALID
     # offload without a host store
     c.flags |= L.NOSA_OFFLOAD
     st.kv_host = None

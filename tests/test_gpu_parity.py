@@ -390,3 +390,70 @@ def test_layer_ahead_stack_overlap_equals_serial():
     for st in (sa, sb):
         for ls in st:
             assert ls.gpu.status_bits() == 0
+
+
+# ------------------------------------------- sparse prefill: bulk block scores
+
+def _prefill_scores_case(wl, T, pos0, check_pairs=None, rows=None):
+    import oracle.nosa_oracle as O
+    from synth import bf16_bits_to_f64, context_kv, queries
+    _say(f"[prefill-scores] {wl.name} T={T} pos0={pos0}")
+    ls = Lockstep(wl, check_pairs=[], steps=1)
+    B, Hq, Hkv, G = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.group
+    wq = wl.replace(steps=T)
+    qs = np.stack([np.stack([queries(wq, 0, b, h) for h in range(Hq)], axis=1)
+                   for b in range(B)])                                  # [B][T][Hq][128]
+    qd = torch.from_numpy(np.ascontiguousarray(qs).view(np.int16)).to(ls.gpu.device)
+    out = ls.gpu.prefill_block_scores(qd, T, pos0)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert ls.gpu.status_bits() == 0
+    n_s, n_w = wl.n_sink_blocks, wl.window_tokens // 64
+    worst = 0.0
+    for p in (range(B * Hkv) if check_pairs is None else check_pairs):
+        b, g = divmod(p, Hkv)
+        K, _ = context_kv(wl, 0, b, g)
+        ck = O.compress_keys(bf16_bits_to_f64(K), wl.context)
+        Q = bf16_bits_to_f64(qs[b][:, g * G:(g + 1) * G])                # [T][G][128]
+        for i in (range(T) if rows is None else rows):
+            want = O.prefill_block_scores(Q[i:i + 1], pos0 + i, ck, n_s, n_w)[0]
+            got = out[b, g, i, :want.shape[0]]
+            fin = np.isfinite(want)
+            assert np.array_equal(np.isfinite(got), fin), (p, i)
+            assert np.all(out[b, g, i, want.shape[0]:] == -np.inf), (p, i)
+            if fin.any():
+                rel = np.abs(got[fin] - want[fin]) / np.abs(want[fin])
+                worst = max(worst, float(rel.max()))
+    _say(f"[prefill-scores] worst relative error {worst:.2e}")
+    assert worst < 1e-4
+
+
+@pytest.mark.parametrize("n_q_heads", [2, 8, 16, 32])
+def test_prefill_block_scores_small(n_q_heads):
+    """Block scores of 600 prompt queries per sequence at positions 900-1499
+    (chunk and block completions, the window moving) for GQA groups of 1, 4,
+    8 and 16, every pair and query against the oracle."""
+    wl = small_workload(161, context=1500, n_q_heads=n_q_heads, n_kv_heads=2)
+    _prefill_scores_case(wl, 600, 900)
+
+
+def test_prefill_block_scores_from_start():
+    """Queries from position 0: rows with no complete chunk or no candidate
+    are all -inf."""
+    _prefill_scores_case(small_workload(162, context=700), 700, 0)
+
+
+def test_prefill_block_scores_16k_sampled():
+    """The 1B-shaped 16K layer (64 pairs): the last 1024 prompt positions,
+    3 pairs x 12 rows against the oracle."""
+    rows = [0, 1, 2, 255, 256, 511, 600, 777, 900, 1000, 1022, 1023]
+    _prefill_scores_case(WORKLOADS[2], 1024, 16384 - 1024, check_pairs=[0, 33, 63], rows=rows)
+
+
+def test_prefill_block_scores_short_context_sets_status():
+    wl = small_workload(163, context=500)
+    ls = Lockstep(wl, check_pairs=[], steps=1)
+    q = torch.zeros(wl.batch * 8 * wl.n_q_heads * 128, dtype=torch.int16, device="cuda")
+    ls.gpu.prefill_block_scores(q, 8, 493)          # reaches position 501 > 500
+    torch.cuda.synchronize()
+    assert ls.gpu.status_bits() & 8

@@ -29,6 +29,7 @@ NOSA_ERR_HIP = -5
 NOSA_STATUS_CAPACITY = 1
 NOSA_STATUS_BAD_SEL = 2
 NOSA_STATUS_LEN_HINT = 4
+NOSA_STATUS_SHORT_CONTEXT = 8
 
 NOSA_MAX_FETCH_WORKGROUPS = 4096
 
@@ -98,6 +99,7 @@ def lib():
                                                ctypes.c_size_t, _P]),
         "nosa_sparse_decode": (ctypes.c_int, [cfgp, stp, _P, _P, _P, _P, _P,
                                               _P, ctypes.c_size_t, _I32, _P]),
+        "nosa_prefill_block_scores": (ctypes.c_int, [cfgp, stp, _P, _I32, _I32, _P, _P]),
         "nosa_host_alias": (ctypes.c_int, [_P, ctypes.POINTER(_P)]),
         "nosa_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "nosa_last_error": (ctypes.c_char_p, []),

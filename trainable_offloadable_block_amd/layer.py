@@ -311,6 +311,19 @@ class NosaLayer:
         self.decode(q)
         return self.out
 
+    def prefill_block_scores(self, q: torch.Tensor, n_queries: int, pos0: int) -> torch.Tensor:
+        """Block scores of n_queries prompt queries per sequence (q: dev bf16
+        [B][n_queries][Hq][128], query i at position pos0 + i): fp32
+        [B][Hkv][n_queries][ceil((pos0 + n_queries) / 64)], -inf off the
+        candidates."""
+        nb = -(-(pos0 + n_queries) // BLOCK)
+        out = torch.empty(self.shape.pairs * n_queries * nb, dtype=torch.float32,
+                          device=self.device)
+        L.check(L.lib().nosa_prefill_block_scores(
+            ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(q), int(n_queries),
+            int(pos0), _ptr(out), self.stream), "prefill_block_scores")
+        return out.view(self.shape.batch, self.shape.n_kv_heads, n_queries, nb)
+
     # ------------------------------------------------------------ views
     def status_bits(self) -> int:
         return int(self.status.cpu().item()) & 0xFFFFFFFF
