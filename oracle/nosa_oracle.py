@@ -49,6 +49,11 @@ constant below):
       score it -- over the chunks complete at that length, candidates between
       the sink and that length's window -- so many queries' scores are one
       causal product against the compressed keys.
+  R23 sparse prefill selects per prompt query with both of NOSA's stages and
+      every candidate eligible (the never-reselect state starts at decode,
+      R9), and attends like a decode step at the query's own length: sink,
+      window and selected blocks, tokens up to the query's position, with the
+      eviction-score bias.
 All functions are pinned by tests (closed forms, brute force, invariants);
 the readings themselves are definitional, not fixed by the pages.
 """
@@ -271,6 +276,27 @@ def prefill_block_scores(Q: np.ndarray, pos0: int, ckeys: np.ndarray,
         Qb = block_max_pool(a, roles.nb)
         out[i, roles.candidates] = Qb[roles.candidates]
     return out
+
+
+def prefill_sparse_attend(Q: np.ndarray, pos0: int, K: np.ndarray,
+                          V: np.ndarray, s: np.ndarray, ckeys: np.ndarray,
+                          e_chunks: np.ndarray, n_sink: int, n_win: int,
+                          k_q: int, k_e_dyn: int, beta: float):
+    """NOSA_S-style sparse prefill of T prompt queries of one pair (R22, R23;
+    [W] Results: sparse in both phases). Q is [T][G][d]; query i sits at
+    position pos0 + i; K, V, s hold the prompt's tokens, ckeys and e_chunks
+    its complete chunks. Returns (outputs [T][G][d], selections)."""
+    scores = prefill_block_scores(Q, pos0, ckeys, n_sink, n_win)
+    outs, sels = [], []
+    for i in range(Q.shape[0]):
+        L = pos0 + i + 1
+        roles = block_roles(L, n_sink, n_win)
+        Eb = block_max_pool(np.asarray(e_chunks[:n_chunks(L)]), roles.nb)
+        sel = select_blocks(scores[i, :roles.nb], Eb, set(roles.candidates),
+                            roles, k_q, k_e_dyn)
+        outs.append(attend(Q[i], K, V, s, sel.blocks, L, beta))
+        sels.append(sel)
+    return np.stack(outs), sels
 
 
 # ----------------------------------------------------------------- selection

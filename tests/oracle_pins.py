@@ -427,6 +427,54 @@ def pin_prefill_scores_causal(o):
             assert not np.array_equal(got[T - 1], base[T - 1]), i
 
 
+def pin_prefill_full_budget_is_causal_attention(o):
+    """With a budget that covers every block, sparse prefill is full causal
+    attention: torch's scaled_dot_product_attention in float64 with the
+    eviction-score bias, over the tokens up to each query's position."""
+    import torch
+    rng = _rng(16)
+    d, G, T, pos0 = 128, 2, 90, 200
+    L = pos0 + T
+    K = _bf16_vals(rng, (L, d))
+    V = _bf16_vals(rng, (L, d))
+    s = rng.standard_normal(L) * 0.3
+    Q = _bf16_vals(rng, (T, G, d), 2.0)
+    ck = o.compress_keys(K, L)
+    ec = o.chunk_means(s, L)
+    nb = -(-L // 64)
+    out, sels = o.prefill_sparse_attend(Q, pos0, K, V, s, ck, ec, 1, 2, nb, nb, 1.0)
+    for i in (0, 37, T - 1):
+        Li = pos0 + i + 1
+        assert sels[i].blocks == list(range(-(-Li // 64))), i
+        tq = torch.from_numpy(Q[i])[None]                       # [1][G][d]
+        tk = torch.from_numpy(K[:Li])[None]
+        tv = torch.from_numpy(V[:Li])[None]
+        mask = torch.from_numpy(s[:Li])[None, None, :].expand(1, G, Li)
+        want = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, attn_mask=mask)[0].numpy()
+        assert np.allclose(out[i], want, rtol=1e-12, atol=1e-13), i
+
+
+def pin_prefill_last_query_is_first_decode_step(o):
+    """The prompt's last query, selected and attended at the prompt's length,
+    is the first decode step after that prompt (every candidate still
+    eligible there, R9)."""
+    rng = _rng(17)
+    d, G, pos0, T = 8, 2, 64 * 9 + 20, 30
+    L = pos0 + T
+    K = _bf16_vals(rng, (L + 1, d))
+    V = _bf16_vals(rng, (L + 1, d))
+    W1 = _bf16_vals(rng, (d, d), 0.5)
+    W2 = _bf16_vals(rng, (d,), 0.5)
+    Q = _bf16_vals(rng, (T, G, d), 2.0)
+    p = o.PairOracle(K.copy(), V.copy(), W1, W2, L - 1, 1, 2, 2, 3, 1.0)
+    r = p.step(K[L - 1], V[L - 1], Q[-1])                    # length L
+    out, sels = o.prefill_sparse_attend(
+        Q, pos0, p.K, p.V, p.s, np.array(p.ckeys), np.array(p.e_chunks), 1, 2, 2, 3, 1.0)
+    assert sels[-1].blocks == r.sel.blocks and sels[-1].kinds == r.sel.kinds
+    assert np.allclose(out[-1], r.out, rtol=1e-13, atol=1e-14)
+
+
 # ------------------------------------------------------------------ attention
 
 def pin_attention_full_coverage_sdpa(o):

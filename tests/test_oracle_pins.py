@@ -186,12 +186,32 @@ def _prefill_not_causal(o):
     o.prefill_block_scores = prefill_block_scores
 
 
+def _prefill_attend_not_causal(o):
+    orig = o.attend
+
+    def prefill_sparse_attend(Q, pos0, K, V, s, ckeys, e_chunks, n_sink, n_win, k_q,
+                              k_e_dyn, beta):
+        T = Q.shape[0]
+        scores = o.prefill_block_scores(Q, pos0, ckeys, n_sink, n_win)
+        outs, sels = [], []
+        for i in range(T):
+            L = pos0 + i + 1
+            roles = o.block_roles(L, n_sink, n_win)
+            Eb = o.block_max_pool(np.asarray(e_chunks[:o.n_chunks(L)]), roles.nb)
+            sel = o.select_blocks(scores[i, :roles.nb], Eb, set(roles.candidates), roles,
+                                  k_q, k_e_dyn)
+            outs.append(orig(Q[i], K, V, s, sel.blocks, pos0 + T, beta))   # sees the future
+            sels.append(sel)
+        return np.stack(outs), sels
+    o.prefill_sparse_attend = prefill_sparse_attend
+
+
 MUTATIONS = [_chunks_by_start, _no_score_scale, _softmax_over_heads,
              _transposed_w1, _swapped_pool, _sum_not_mean, _ties_high_index,
              _bias_sign, _window_without_partial, _double_rounding,
              _float_sum_compress, _evict_on_agnostic_only, _fill_shortfall,
              _forecast_softmax, _forecast_unscaled, _ahead_at_current_length,
-             _prefill_off_by_one, _prefill_not_causal]
+             _prefill_off_by_one, _prefill_not_causal, _prefill_attend_not_causal]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
