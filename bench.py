@@ -625,13 +625,59 @@ def prefill_scores_leg(dev, workers, T=4096, K=10):
     flops = 2.0 * 128 * chunks * wl.n_q_heads * wl.batch                    # one logit pass
     nb = -(-(pos0 + T) // 64)
     out_bytes = wl.batch * wl.n_kv_heads * T * nb * 4
-    del layer, qd
+    res = {"workload": wl.name + "-prompt-scores", "queries_per_sequence": T, "pos0": pos0,
+           "us": round(us, 1), "queries_per_s": round(wl.batch * T / (us * 1e-6), 1),
+           "logit_TFLOPs": round(flops / (us * 1e-6) / 1e12, 1), "peak_TFLOPs": 2500.0,
+           "frac": round(flops / (us * 1e-6) / 1e12 / 2500.0, 4),
+           "out_bytes": out_bytes}
+    # the whole sparse prefill of the same queries: scores, per-query
+    # selection, attention (each query attends as a decode step would)
+    import ctypes
+    from trainable_offloadable_block_amd import _lib as L
+    P, k = layer.shape.pairs, layer.shape.k_blocks
+    scores = layer.prefill_block_scores(qd, T, pos0)
+    sel = torch.empty(P * T * k, dtype=torch.int32, device=dev)
+    nsel = torch.empty(P * T, dtype=torch.int32, device=dev)
+    out = torch.empty(wl.batch * T * wl.n_q_heads * 128, dtype=torch.float32, device=dev)
+    lib = L.lib()
+
+    def sel_call():
+        L.check(lib.nosa_prefill_select(ctypes.byref(layer.cfg), ctypes.byref(layer.state),
+                                        ctypes.c_void_p(scores.data_ptr()), T, pos0,
+                                        ctypes.c_void_p(sel.data_ptr()),
+                                        ctypes.c_void_p(nsel.data_ptr()), layer.stream), "sel")
+
+    def att_call():
+        L.check(lib.nosa_prefill_attend(ctypes.byref(layer.cfg), ctypes.byref(layer.state),
+                                        ctypes.c_void_p(qd.data_ptr()), T, pos0,
+                                        ctypes.c_void_p(sel.data_ptr()),
+                                        ctypes.c_void_p(nsel.data_ptr()),
+                                        ctypes.c_void_p(out.data_ptr()), layer.stream), "att")
+
+    times = {}
+    for name, fn in (("select", sel_call), ("attend", att_call)):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(3)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        times[name] = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    n_att = float(nsel.float().mean().item()) * 64            # tokens per (query, pair), about
+    assert layer.status_bits() == 0
+    total = us + times["select"] + times["attend"]
+    res["sparse_prefill"] = {
+        "select_us": round(times["select"], 1), "attend_us": round(times["attend"], 1),
+        "total_us": round(total, 1), "prompt_tokens_per_s": round(wl.batch * T / (total * 1e-6), 1),
+        "attended_tokens_per_query_pair": round(n_att, 1),
+        "attend_kv_GBps_if_unshared": round(wl.batch * wl.n_kv_heads * T * n_att * 516 /
+                                            (times["attend"] * 1e-6) / 1e9, 1)}
+    del layer, qd, scores, sel, nsel, out
     torch.cuda.empty_cache()
-    return {"workload": wl.name + "-prompt-scores", "queries_per_sequence": T, "pos0": pos0,
-            "us": round(us, 1), "queries_per_s": round(wl.batch * T / (us * 1e-6), 1),
-            "logit_TFLOPs": round(flops / (us * 1e-6) / 1e12, 1), "peak_TFLOPs": 2500.0,
-            "frac": round(flops / (us * 1e-6) / 1e12 / 2500.0, 4),
-            "out_bytes": out_bytes}
+    return res
 
 
 def next_leg(dev, workers, R=4, W=8, K=48):

@@ -315,6 +315,33 @@ int nosa_prefill_block_scores(const nosa_config *cfg, const nosa_state *st,
                               const uint16_t *q, int32_t n_queries,
                               int32_t pos0, float *out, hipStream_t stream);
 
+/* Sparse prefill selection, NOSA_S style (aiwiki "NOSA", Results; aiwiki
+ * "NOSA", How NOSA works): for each of n_queries prompt queries (query i at
+ * position pos0 + i, length L = pos0 + i + 1), NOSA's two stages with every
+ * candidate eligible (the never-reselect state begins with decoding): the
+ * k_q candidates of highest block score, then the k_e - n_sink - n_win
+ * others of highest blk_e; ties to the lower block id. scores: the output of
+ * nosa_prefill_block_scores for the same n_queries and pos0. Outputs: sel
+ * dev int32 [B][Hkv][n_queries][k_blocks], each row the ascending list of
+ * sink, window and selected blocks, -1 padded; n_sel dev int32
+ * [B][Hkv][n_queries]. */
+int nosa_prefill_select(const nosa_config *cfg, const nosa_state *st,
+                        const float *scores, int32_t n_queries, int32_t pos0,
+                        int32_t *sel, int32_t *n_sel, hipStream_t stream);
+
+/* Sparse prefill attention (resident KV only): each prompt query attends as
+ * a decode step at its own length would (nosa_sparse_decode's formula), over
+ * the tokens at or before its position in the blocks of its row of sel.
+ * q: dev bf16 [B][n_queries][Hq][128]; sel, n_sel from nosa_prefill_select
+ * with the same n_queries and pos0; out: dev fp32 [B][n_queries][Hq][128].
+ * An entry that names a block past the query's position or beyond NB_max is
+ * skipped and sets NOSA_STATUS_BAD_SEL. Offload configs get
+ * NOSA_ERR_UNSUPPORTED. */
+int nosa_prefill_attend(const nosa_config *cfg, const nosa_state *st,
+                        const uint16_t *q, int32_t n_queries, int32_t pos0,
+                        const int32_t *sel, const int32_t *n_sel, float *out,
+                        hipStream_t stream);
+
 /* Device-usable address of pinned host memory (hipHostGetDevicePointer);
  * allocates nothing. */
 int nosa_host_alias(void *pinned_host_ptr, void **dev_alias);

@@ -148,6 +148,17 @@ def test_calls_reject_before_any_hip_call():
                                          c.max_context - 10, 256, null) == L.NOSA_ERR_CAPACITY
     assert lib.nosa_prefill_block_scores(ctypes.byref(c), ctypes.byref(st), 256, 4, 0, None,
                                          null) == L.NOSA_ERR_INVALID
+    # sparse prefill: bad sizes, NULLs; attention rejects offloaded KV
+    assert lib.nosa_prefill_select(ctypes.byref(c), ctypes.byref(st), 256, 0, 0, 256, 256,
+                                   null) == L.NOSA_ERR_INVALID
+    assert lib.nosa_prefill_select(ctypes.byref(c), ctypes.byref(st), None, 4, 0, 256, 256,
+                                   null) == L.NOSA_ERR_INVALID
+    assert lib.nosa_prefill_attend(ctypes.byref(c), ctypes.byref(st), 256, 4, c.max_context,
+                                   256, 256, 256, null) == L.NOSA_ERR_CAPACITY
+    c_off = _cfg()
+    c_off.flags |= L.NOSA_OFFLOAD
+    assert lib.nosa_prefill_attend(ctypes.byref(c_off), ctypes.byref(st), 256, 4, 0, 256, 256,
+                                   256, null) == L.NOSA_ERR_UNSUPPORTED
     # offload without a host store
     c.flags |= L.NOSA_OFFLOAD
     st.kv_host = None

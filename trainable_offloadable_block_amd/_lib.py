@@ -100,6 +100,8 @@ def lib():
         "nosa_sparse_decode": (ctypes.c_int, [cfgp, stp, _P, _P, _P, _P, _P,
                                               _P, ctypes.c_size_t, _I32, _P]),
         "nosa_prefill_block_scores": (ctypes.c_int, [cfgp, stp, _P, _I32, _I32, _P, _P]),
+        "nosa_prefill_select": (ctypes.c_int, [cfgp, stp, _P, _I32, _I32, _P, _P, _P]),
+        "nosa_prefill_attend": (ctypes.c_int, [cfgp, stp, _P, _I32, _I32, _P, _P, _P, _P]),
         "nosa_host_alias": (ctypes.c_int, [_P, ctypes.POINTER(_P)]),
         "nosa_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "nosa_last_error": (ctypes.c_char_p, []),

@@ -275,6 +275,36 @@ int nosa_prefill_block_scores(const nosa_config *cfg, const nosa_state *st, cons
   return hip_result(nosa::launch_prefill_block_scores(d, *st, q, n_queries, pos0, out, stream));
 }
 
+int nosa_prefill_select(const nosa_config *cfg, const nosa_state *st, const float *scores,
+                        int32_t n_queries, int32_t pos0, int32_t *sel, int32_t *n_sel,
+                        hipStream_t stream) {
+  nosa::Dims d;
+  int rc = make_dims(cfg, &d);
+  if (!rc) rc = check_state(d, st);
+  if (rc) return rc;
+  if (!scores || !sel || !n_sel) return fail(NOSA_ERR_INVALID, "scores / sel / n_sel is NULL");
+  if (n_queries < 1 || pos0 < 0) return fail(NOSA_ERR_INVALID, "n_queries < 1 or pos0 < 0");
+  if ((long)pos0 + n_queries > d.max_context)
+    return fail(NOSA_ERR_CAPACITY, "pos0 + n_queries beyond max_context");
+  return hip_result(nosa::launch_prefill_select(d, *st, scores, n_queries, pos0, sel, n_sel, stream));
+}
+
+int nosa_prefill_attend(const nosa_config *cfg, const nosa_state *st, const uint16_t *q,
+                        int32_t n_queries, int32_t pos0, const int32_t *sel,
+                        const int32_t *n_sel, float *out, hipStream_t stream) {
+  nosa::Dims d;
+  int rc = make_dims(cfg, &d);
+  if (!rc) rc = check_state(d, st);
+  if (rc) return rc;
+  if (d.offload) return fail(NOSA_ERR_UNSUPPORTED, "sparse prefill reads resident KV only");
+  if (!q || !sel || !n_sel || !out) return fail(NOSA_ERR_INVALID, "q / sel / n_sel / out is NULL");
+  if (n_queries < 1 || pos0 < 0) return fail(NOSA_ERR_INVALID, "n_queries < 1 or pos0 < 0");
+  if ((long)pos0 + n_queries > d.max_context)
+    return fail(NOSA_ERR_CAPACITY, "pos0 + n_queries beyond max_context");
+  return hip_result(
+      nosa::launch_prefill_attend(d, *st, q, n_queries, pos0, sel, n_sel, out, stream));
+}
+
 int nosa_host_alias(void *pinned_host_ptr, void **dev_alias) {
   if (!pinned_host_ptr || !dev_alias) return fail(NOSA_ERR_INVALID, "NULL argument");
   return hip_result(hipHostGetDevicePointer(dev_alias, pinned_host_ptr, 0));

@@ -56,6 +56,13 @@ hipError_t launch_select_forecast(const Dims &d, const nosa_state &st,
 hipError_t launch_prefill_block_scores(const Dims &d, const nosa_state &st,
                                        const uint16_t *q, int T, int pos0,
                                        float *out, hipStream_t s);
+hipError_t launch_prefill_select(const Dims &d, const nosa_state &st,
+                                 const float *scores, int T, int pos0,
+                                 int32_t *sel, int32_t *n_sel, hipStream_t s);
+hipError_t launch_prefill_attend(const Dims &d, const nosa_state &st,
+                                 const uint16_t *q, int T, int pos0,
+                                 const int32_t *sel, const int32_t *n_sel,
+                                 float *out, hipStream_t s);
 // n_wg > 0: copy with that many looping workgroups; 0: one per list entry
 hipError_t launch_fetch(const Dims &d, const nosa_state &st,
                         const int32_t *sel, const int32_t *n_sel,

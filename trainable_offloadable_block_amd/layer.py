@@ -324,6 +324,28 @@ class NosaLayer:
             int(pos0), _ptr(out), self.stream), "prefill_block_scores")
         return out.view(self.shape.batch, self.shape.n_kv_heads, n_queries, nb)
 
+    def prefill_sparse(self, q: torch.Tensor, n_queries: int, pos0: int):
+        """NOSA_S-style sparse prefill of n_queries prompt queries per sequence
+        (q: dev bf16 [B][n_queries][Hq][128], query i at position pos0 + i):
+        block scores, per-query selection, attention. Returns (out fp32
+        [B][n_queries][Hq][128], sel [B][Hkv][n_queries][k], n_sel)."""
+        scores = self.prefill_block_scores(q, n_queries, pos0)
+        P, k = self.shape.pairs, self.shape.k_blocks
+        sel = torch.empty(P * n_queries * k, dtype=torch.int32, device=self.device)
+        n_sel = torch.empty(P * n_queries, dtype=torch.int32, device=self.device)
+        out = torch.empty(self.shape.batch * n_queries * self.shape.n_q_heads * HEAD_DIM,
+                          dtype=torch.float32, device=self.device)
+        lib = L.lib()
+        L.check(lib.nosa_prefill_select(
+            ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(scores), int(n_queries),
+            int(pos0), _ptr(sel), _ptr(n_sel), self.stream), "prefill_select")
+        L.check(lib.nosa_prefill_attend(
+            ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(q), int(n_queries),
+            int(pos0), _ptr(sel), _ptr(n_sel), _ptr(out), self.stream), "prefill_attend")
+        B, Hkv = self.shape.batch, self.shape.n_kv_heads
+        return (out.view(B, n_queries, self.shape.n_q_heads, HEAD_DIM),
+                sel.view(B, Hkv, n_queries, k), n_sel.view(B, Hkv, n_queries))
+
     # ------------------------------------------------------------ views
     def status_bits(self) -> int:
         return int(self.status.cpu().item()) & 0xFFFFFFFF
