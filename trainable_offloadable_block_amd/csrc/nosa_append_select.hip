@@ -2,12 +2,13 @@
 // of aiwiki "NOSA", How NOSA works, in order), for callers that run them
 // back to back: the separate append launch and its dispatch disappear.
 //
-// grid (chunk splits + 1, pairs), 256 threads:
-//  - workgroup `n_splits` of a pair appends the token (K, V, ring, eviction
+// grid (scoring workgroups + 1, pairs), 256 threads:
+//  - the last workgroup of a pair appends the token (K, V, ring, eviction
 //    score, and the compressed key, chunk score and block score the token
 //    completes, the last two stored device-coherently);
-//  - the others score their splits as the select kernel does (every chunk
-//    but the newest, which the append may be writing), in parallel;
+//  - the others score their splits (one or several each) as the select
+//    kernel does (every chunk but the newest, which the append may be
+//    writing), in parallel;
 //  - all arrive on the pair's counter; the last one scores the newest chunk,
 //    pools and selects (block scores read device-coherently);
 //  - the last pair of a sequence to finish advances the sequence's length:
@@ -21,27 +22,25 @@ namespace {
 __global__ __launch_bounds__(kScoreThreads) void append_select_kernel(
     Dims d, nosa_state st, const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
     const uint16_t *__restrict__ q, float *ws_e, float *ws_stats, int32_t *ws_count, int c_pad,
-    int n_splits, int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
+    int n_splits, int subs, int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
     uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
-  const int split = blockIdx.x, p = blockIdx.y;
+  const int wg = blockIdx.x, p = blockIdx.y, n_wg = gridDim.x - 1;
   const int b = p / d.Hkv, g = p % d.Hkv;
   __shared__ AppendLds ash;
   __shared__ int sm_last;
   const int pos = st.seq_len[b];
   const bool ok = pos >= 0 && pos < d.max_context;
   const int L = ok ? pos + 1 : pos;
-  if (split == n_splits) {                                 // uniform
+  if (wg == n_wg) {                                       // uniform
     append_pair<kScoreThreads>(d, st, k_new, v_new, b, g, pos, true, ash);
   } else {
-    ScoreIn in;
-    score_load(d, st.ckey, q, split, p, in);
-    score_compute(d, split_chunks(d, L, c_pad), in, ws_e, ws_stats, c_pad, n_splits, split, p);
+    score_splits(d, st.ckey, q, L, ws_e, ws_stats, c_pad, n_splits, subs, wg, p);
   }
   __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
   __syncthreads();
   if (threadIdx.x == 0)
     sm_last = __hip_atomic_fetch_add(&ws_count[p], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              n_splits;                  // n_splits score workgroups + the append
+              n_wg;                      // n_wg score workgroups + the append
   __syncthreads();
   if (!sm_last) return;
   pool_select(d, st, q, L, ws_e, ws_stats, c_pad, n_splits, sel, n_sel, kind_out, dbg, p);
@@ -69,9 +68,9 @@ hipError_t launch_append_select(const Dims &d, const nosa_state &st, const uint1
   float *ws_e = reinterpret_cast<float *>(base + lay.e_off);
   float *ws_stats = reinterpret_cast<float *>(base + lay.stats_off);
   int32_t *ws_count = reinterpret_cast<int32_t *>(base + lay.count_off);
-  append_select_kernel<<<dim3(lay.n_splits + 1, d.P), kScoreThreads, select_dyn_lds(d, lay), s>>>(
-      d, st, k_new, v_new, q, ws_e, ws_stats, ws_count, lay.c_pad, lay.n_splits, sel, n_sel, kind,
-      dbg);
+  append_select_kernel<<<dim3(lay.n_wg + 1, d.P), kScoreThreads, select_dyn_lds(d, lay), s>>>(
+      d, st, k_new, v_new, q, ws_e, ws_stats, ws_count, lay.c_pad, lay.n_splits, lay.subs, sel,
+      n_sel, kind, dbg);
   return hipGetLastError();
 }
 

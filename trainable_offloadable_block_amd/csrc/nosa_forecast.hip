@@ -4,10 +4,10 @@
 // is matched against layer l+1's compressed keys to pick layer l+1's
 // query-aware blocks, so layer l+1's delta fetch can start a layer early.
 //
-// forecast_select_kernel (chunk splits x pairs), one launch, run before the
+// forecast_select_kernel (scoring workgroups x pairs), one launch, run before the
 // step's token is appended to the layer, for the length seq_len + 1 that
 // token gives it:
-//  - every workgroup scores one split of the chunks that exist: the plain
+//  - every workgroup scores its splits of the chunks that exist: the plain
 //    logit f . c / sqrt(128) of the pair's forecast head on MFMA (one B
 //    column of the 16x16x32 shape), with neither a softmax nor a sum over
 //    heads, published with device-coherent stores;
@@ -121,22 +121,27 @@ __device__ __forceinline__ void pool_forecast(const Dims &d, const nosa_state &s
 
 __global__ __launch_bounds__(kScoreThreads) void forecast_select_kernel(
     Dims d, nosa_state st, const uint16_t *__restrict__ f, float *ws_l, int32_t *ws_count,
-    int c_pad, int n_splits, int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
+    int c_pad, int n_splits, int subs, int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
     uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
-  const int split = blockIdx.x, p = blockIdx.y;
+  const int p = blockIdx.y;
   __shared__ int sm_last;
   Dims df = d;                       // f is [B][Hkv][128]: a group of one head
   df.G = 1;
   df.Hq = d.Hkv;
-  ScoreIn in;
-  score_load(df, st.ckey, f, split, p, in);
   const int L = max(0, min(st.seq_len[p / d.Hkv], d.max_context));
-  forecast_score(min(min(chunks_for(L), d.C_max), c_pad), in, ws_l, c_pad, split, p);
+  const int C = min(min(chunks_for(L), d.C_max), c_pad);
+  for (int j = 0; j < subs; ++j) {                 // uniform: this workgroup's splits
+    const int split = blockIdx.x * subs + j;
+    if (split >= n_splits) break;
+    ScoreIn in;
+    score_load(df, st.ckey, f, split, p, in);
+    forecast_score(C, in, ws_l, c_pad, split, p);
+  }
   __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
   __syncthreads();
   if (threadIdx.x == 0)
     sm_last = __hip_atomic_fetch_add(&ws_count[p], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              n_splits - 1;
+              (int)gridDim.x - 1;
   __syncthreads();
   if (!sm_last) return;
   pool_forecast(d, st, L, ws_l, c_pad, sel, n_sel, kind_out, dbg, p);
@@ -153,8 +158,8 @@ hipError_t launch_select_forecast(const Dims &d, const nosa_state &st, const uin
   int32_t *ws_count = reinterpret_cast<int32_t *>(base + lay.count_off);
   const size_t lds = (size_t)lay.c_pad * sizeof(float) + (size_t)d.elig_words * sizeof(uint32_t) +
                      (size_t)d.NB_max;
-  forecast_select_kernel<<<dim3(lay.n_splits, d.P), kScoreThreads, lds, s>>>(
-      d, st, f, ws_l, ws_count, lay.c_pad, lay.n_splits, sel, n_sel, kind, dbg);
+  forecast_select_kernel<<<dim3(lay.n_wg, d.P), kScoreThreads, lds, s>>>(
+      d, st, f, ws_l, ws_count, lay.c_pad, lay.n_splits, lay.subs, sel, n_sel, kind, dbg);
   return hipGetLastError();
 }
 

@@ -14,6 +14,8 @@ constexpr int kChunksPerSplit = 128;   // 4 waves x one 32-chunk MFMA group
 
 struct SelectLayout {
   int n_splits;      // chunk splits per pair
+  int subs;          // splits scored by one workgroup, one after another
+  int n_wg;          // scoring workgroups per pair: ceil(n_splits / subs)
   int c_pad;         // n_splits * kChunksPerSplit
   size_t e_off, stats_off, count_off, bytes;   // count: per-pair arrivals, zero at rest
 };

@@ -15,29 +15,29 @@
 //    workgroup top-k by histogram range refinement, writes the ascending
 //    selection and clears the eligibility of every candidate left out (never
 //    re-selected by the agnostic stage).
+#include <stdlib.h>
+
 #include "nosa_select_dev.h"
 
 namespace nosa {
 namespace {
 
-// grid (splits, pairs): every workgroup scores its split and arrives on the
-// pair's counter once its results have landed; the last one pools and
-// selects, then resets the counter (zero at rest).
+// grid (scoring workgroups, pairs): every workgroup scores its `subs`
+// splits and arrives on the pair's counter once its results have landed; the
+// last one pools and selects, then resets the counter (zero at rest).
 __global__ __launch_bounds__(kScoreThreads) void select_kernel(
     Dims d, nosa_state st, const uint16_t *__restrict__ q, float *ws_e, float *ws_stats,
-    int32_t *ws_count, int c_pad, int n_splits, int32_t *__restrict__ sel,
+    int32_t *ws_count, int c_pad, int n_splits, int subs, int32_t *__restrict__ sel,
     int32_t *__restrict__ n_sel, uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
-  const int split = blockIdx.x, p = blockIdx.y;
+  const int p = blockIdx.y;
   __shared__ int sm_last;
-  ScoreIn in;
-  score_load(d, st.ckey, q, split, p, in);
   const int L = st.seq_len[p / d.Hkv];
-  score_compute(d, split_chunks(d, L, c_pad), in, ws_e, ws_stats, c_pad, n_splits, split, p);
+  score_splits(d, st.ckey, q, L, ws_e, ws_stats, c_pad, n_splits, subs, blockIdx.x, p);
   __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
   __syncthreads();
   if (threadIdx.x == 0)
     sm_last = __hip_atomic_fetch_add(&ws_count[p], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              n_splits - 1;
+              (int)gridDim.x - 1;
   __syncthreads();
   if (!sm_last) return;
   pool_select(d, st, q, L, ws_e, ws_stats, c_pad, n_splits, sel, n_sel, kind_out, dbg, p);
@@ -51,6 +51,17 @@ SelectLayout select_layout(const Dims &d, int max_len) {
   const int C = chunks_for(max_len);
   s.n_splits = C > 0 ? (C + kChunksPerSplit - 1) / kChunksPerSplit : 1;
   s.c_pad = s.n_splits * kChunksPerSplit;
+  // one round of workgroups where possible: several splits per workgroup
+  // once pairs x (splits + 1) passes the chip's resident count (4 per CU)
+  s.subs = 1;
+  while (s.subs < s.n_splits &&
+         (long)d.P * ((s.n_splits + s.subs - 1) / s.subs + 1) > kSelectWgBudget)
+    ++s.subs;
+  if (const char *env = getenv("NOSA_SELECT_SUBS")) {
+    const int v = atoi(env);
+    if (v >= 1 && v <= s.n_splits) s.subs = v;
+  }
+  s.n_wg = (s.n_splits + s.subs - 1) / s.subs;
   s.e_off = 0;
   s.stats_off = ((size_t)d.P * s.c_pad * padded_group(d.G) * sizeof(float) + 255) & ~(size_t)255;
   s.count_off = s.stats_off + (((size_t)d.P * s.n_splits * d.G * sizeof(float2) + 255) & ~(size_t)255);
@@ -70,8 +81,9 @@ hipError_t launch_select(const Dims &d, const nosa_state &st, const uint16_t *q,
   float *ws_e = reinterpret_cast<float *>(base + lay.e_off);
   float *ws_stats = reinterpret_cast<float *>(base + lay.stats_off);
   int32_t *ws_count = reinterpret_cast<int32_t *>(base + lay.count_off);
-  select_kernel<<<dim3(lay.n_splits, d.P), kScoreThreads, select_dyn_lds(d, lay), s>>>(
-      d, st, q, ws_e, ws_stats, ws_count, lay.c_pad, lay.n_splits, sel, n_sel, kind, dbg);
+  select_kernel<<<dim3(lay.n_wg, d.P), kScoreThreads, select_dyn_lds(d, lay), s>>>(
+      d, st, q, ws_e, ws_stats, ws_count, lay.c_pad, lay.n_splits, lay.subs, sel, n_sel, kind,
+      dbg);
   return hipGetLastError();
 }
 

@@ -161,6 +161,25 @@ __device__ __forceinline__ void score_compute(const Dims &d, int C, ScoreIn &in,
   }
 }
 
+constexpr int kSelectWgBudget = 1024;   // resident workgroups of one round (4 per CU)
+
+// Splits ws * subs .. ws * subs + subs - 1 of pair p (those below n_splits),
+// one after another: the newest chunk left out (split_chunks).
+__device__ __forceinline__ void score_splits(const Dims &d, const uint16_t *__restrict__ ckey,
+                                             const uint16_t *__restrict__ q, int L, float *ws_e,
+                                             float *ws_stats, int c_pad, int n_splits, int subs,
+                                             int ws, int p) {
+  const int C = split_chunks(d, L, c_pad);
+  for (int j = 0; j < subs; ++j) {                 // uniform
+    const int split = ws * subs + j;
+    if (split >= n_splits) break;
+    if (j > 0) __syncthreads();                    // the last split's reductions are read
+    ScoreIn in;
+    score_load(d, ckey, q, split, p, in);
+    score_compute(d, C, in, ws_e, ws_stats, c_pad, n_splits, split, p);
+  }
+}
+
 // ---- workgroup top-k on 64-bit composite keys ----------------------------
 // A key is (order_key(score) << 32) | ~block: larger score first, then the
 // lower block id; keys are distinct and 0 marks "not a candidate".
