@@ -7,9 +7,11 @@
 //   stage 1 takes the k_q candidates of highest block score (from
 //   nosa_prefill_block_scores), stage 2 the k_e' others of highest agnostic
 //   score; the ascending list of sink, window and selected blocks.
-// prefill_attend_kernel: grid (query groups, pairs), 4 waves; a wave takes
-//   16 / Gp consecutive queries (16 MFMA columns of (query, head)), forms the
-//   union of their selections in LDS and streams those blocks half by half:
+// prefill_attend_kernel: grid (query groups, pairs), 8 waves; a wave takes
+//   16 / Gp consecutive queries (16 MFMA columns of (query, head)); the
+//   workgroup forms the union of its queries' selections in LDS and stages
+//   each union block there once for its 8 waves (the next block loaded into
+//   registers meanwhile), and each wave runs over it half by half:
 //   logits S^T = K Q^T on MFMA, a column is masked where its query did not
 //   select the block or the key lies past the query's position, an online
 //   softmax per column in the log2 domain with the eviction-score bias, and
@@ -20,7 +22,6 @@ namespace nosa {
 namespace {
 
 __host__ __device__ inline int pa_rows(int G) { return G <= 4 ? 4 : (G <= 8 ? 8 : 16); }
-constexpr int kPaWaves = 4;
 
 // ---------------------------------------------------------------- select
 template <int R>
@@ -106,73 +107,59 @@ __global__ __launch_bounds__(kTopkThreads) void prefill_select_kernel(
 }
 
 // ---------------------------------------------------------------- attend
-constexpr int kPaMaxQ = 4;                 // queries per wave (Gp = 4)
-constexpr int kPaMaxWords = kMaxContext / kBlock / 32;   // bitmap words
-constexpr int kPaMaxUnion = kPaMaxQ * kMaxK;
+constexpr int kPaWaves = 8;
+constexpr int kPaKPitch = kHeadDim * 2 + 16;     // LDS bytes per K row: no bank conflicts
+constexpr int kPaKBytes = kBlock * kPaKPitch;    // K part of a staged block
+constexpr int kPaVBytes = kBlock * kHeadDim * 2; // V part (tile order, as stored)
+
+__host__ __device__ inline int pa_queries_per_wave(int G) { return 16 / pa_rows(G); }
 
 // A-row r of tile t <-> key 8*(r/4) + 4*t + (r%4) of a 32-key half, so that
 // lane group j holds keys 8j .. 8j+7 of the half (the decode kernel's order).
 __device__ inline int pa_tile_row(int r, int t) { return 8 * (r >> 2) + 4 * t + (r & 3); }
 
-__global__ __launch_bounds__(kPaWaves * 64) void prefill_attend_kernel(
+// grid (query groups, pairs), 8 waves (two workgroups share a CU, so two
+// blocks are in flight per CU); dynamic LDS: the workgroup's
+// selection bitmaps [queries][words] and their union [words].
+__global__ __launch_bounds__(kPaWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void prefill_attend_kernel(
     Dims d, nosa_state st, const uint16_t *__restrict__ q, int T, int pos0,
     const int32_t *__restrict__ sel, const int32_t *__restrict__ n_sel,
     float *__restrict__ out) {
-  __shared__ uint32_t bits[kPaWaves][kPaMaxQ][kPaMaxWords];
-  __shared__ int ulist[kPaWaves][kPaMaxUnion];
-  __shared__ uint8_t umask[kPaWaves][kPaMaxUnion];
+  constexpr int NT = kPaWaves * 64;
+  constexpr int kVecs = kBlockElems * 2 / 16 / NT;           // uint4 per thread per block
+  __shared__ __align__(16) uint8_t kv_sh[kPaKBytes + kPaVBytes];
+  __shared__ float s_sh[kBlock];
+  extern __shared__ uint32_t dyn[];
   const int p = blockIdx.y, b = p / d.Hkv, g = p % d.Hkv;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, h = l & 15, lg = l >> 4;
-  const int Gp = pa_rows(d.G), QT = 16 / Gp;
-  const int q0 = (blockIdx.x * kPaWaves + w) * QT;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, h = l & 15, lg = l >> 4;
+  const int Gp = pa_rows(d.G), QT = pa_queries_per_wave(d.G), QW = kPaWaves * QT;
   const int words = d.elig_words;
+  uint32_t *bits = dyn;                                      // [QW][words]
+  uint32_t *orb = dyn + QW * words;                          // [words]
+  const int qw0 = blockIdx.x * QW;                           // first query of the workgroup
 
-  // 1. the wave's queries' selections as bitmaps, then their union
-  for (int qq = 0; qq < QT; ++qq)
-    for (int i = l; i < words; i += 64) bits[w][qq][i] = 0u;
+  // 1. selection bitmaps of the workgroup's queries, and their union
+  for (int i = t; i < (QW + 1) * words; i += NT) dyn[i] = 0u;
   __syncthreads();
   bool bad = false;
-  for (int qq = 0; qq < QT; ++qq) {
-    const int qi = q0 + qq;
+  for (int ql = w; ql < QW; ql += kPaWaves) {
+    const int qi = qw0 + ql;
     if (qi >= T) break;
     const int ns = max(0, min(n_sel[(size_t)p * T + qi], d.k));
     for (int e = l; e < ns; e += 64) {
       const int blk = sel[((size_t)p * T + qi) * d.k + e];
-      if (blk >= 0 && blk < d.NB_max && blk * kBlock <= pos0 + qi)
-        atomicOr(&bits[w][qq][blk >> 5], 1u << (blk & 31));
-      else
+      if (blk >= 0 && blk < d.NB_max && blk * kBlock <= pos0 + qi) {
+        atomicOr(&bits[ql * words + (blk >> 5)], 1u << (blk & 31));
+        atomicOr(&orb[blk >> 5], 1u << (blk & 31));
+      } else {
         bad = true;
-    }
-  }
-  __syncthreads();
-  int n_union = 0;
-  for (int base = 0; base < words; base += 64) {             // wave-uniform
-    const int wi = base + l;
-    uint32_t u = 0u;
-    if (wi < words)
-      for (int qq = 0; qq < QT; ++qq) u |= bits[w][qq][wi];
-    const uint32_t cnt = __popc(u);
-    const uint32_t incl = wave_incl_scan(cnt);
-    int off = n_union + static_cast<int>(incl - cnt);
-    while (u) {
-      const int bit = __builtin_ctz(u);
-      u &= u - 1u;
-      const int blk = 32 * wi + bit;
-      uint8_t m = 0;
-      for (int qq = 0; qq < QT; ++qq) m |= ((bits[w][qq][wi] >> bit) & 1u) << qq;
-      if (off < kPaMaxUnion) {
-        ulist[w][off] = blk;
-        umask[w][off] = m;
       }
-      ++off;
     }
-    n_union += static_cast<int>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
   }
-  n_union = min(n_union, kPaMaxUnion);
   __syncthreads();
 
-  // 2. this lane's column: query qq = h / Gp, head hh = h % Gp
-  const int qq = h / Gp, hh = h % Gp, qi = q0 + qq;
+  // 2. this lane's column: query ql = w * QT + h / Gp, head hh = h % Gp
+  const int ql = w * QT + h / Gp, hh = h % Gp, qi = qw0 + ql;
   const bool col_ok = hh < d.G && qi < T;
   const int qpos = pos0 + qi;                                // keys <= qpos
   bf16x8 qop[4];
@@ -186,75 +173,123 @@ __global__ __launch_bounds__(kPaWaves * 64) void prefill_attend_kernel(
   }
   const float qscale = 0.08838834764831845f * 1.4426950408889634f;
   const float bscale = d.bias ? 1.4426950408889634f : 0.0f;
-  const char *kvp = reinterpret_cast<const char *>(st.kv_dev + (size_t)p * d.NB_max * kBlockElems);
+  const uint4 *kvg = reinterpret_cast<const uint4 *>(st.kv_dev + (size_t)p * d.NB_max * kBlockElems);
   const float *tsp = st.tok_s + (size_t)p * d.tok_stride;
-  const int koff0 = pa_tile_row(h, 0) * kHeadDim * 2 + 16 * lg;
-  const int koff1 = pa_tile_row(h, 1) * kHeadDim * 2 + 16 * lg;
+  const int koff0 = pa_tile_row(h, 0) * kPaKPitch + 16 * lg;
+  const int koff1 = pa_tile_row(h, 1) * kPaKPitch + 16 * lg;
+
+  // union cursor (uniform): the next set bit of orb at or after block `from`
+  auto next_block = [&](int from) {
+    for (int wi = from >> 5; wi < words; ++wi) {
+      uint32_t u = orb[wi];
+      if (wi == (from >> 5)) u &= ~0u << (from & 31);
+      if (u) return 32 * wi + __builtin_ctz(u);
+    }
+    return -1;
+  };
+  // staging: thread t moves 16-byte pieces t + NT j of a block; pieces below
+  // kBlock * 16 are K (row v / 16, dims 8 (v % 16)), the rest V
+  static_assert(kVecs == 4 && NT * 2 == kBlock * kHeadDim / 8,
+                "a thread stages two K pieces and two V pieces");
+  uint4 pre0, pre1, pre2, pre3;                              // pieces t + NT j
+  float spre = 0.0f;
 
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4 o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int j = 0; j < 2 * n_union; ++j) {                    // wave-uniform
-    const int blk = ulist[w][j >> 1], half = j & 1;
-    const bool sel_col = col_ok && ((umask[w][j >> 1] >> qq) & 1);
-    const char *kb = kvp + (size_t)blk * (kBlockElems * 2) + half * (32 * kHeadDim * 2);
-    const char *vb = kvp + (size_t)blk * (kBlockElems * 2) + kBlock * kHeadDim * 2 + half * 8192;
-    uint4 kk[2][4], vv[8];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      kk[0][s] = *reinterpret_cast<const uint4 *>(kb + koff0 + 64 * s);
-      kk[1][s] = *reinterpret_cast<const uint4 *>(kb + koff1 + 64 * s);
+  int blk = next_block(0);
+  if (blk >= 0) {
+    const uint4 *src = kvg + (size_t)blk * (kBlockElems * 2 / 16) + t;
+    pre0 = src[0];
+    pre1 = src[NT];
+    pre2 = src[2 * NT];
+    pre3 = src[3 * NT];
+    if (t < kBlock) spre = tsp[blk * kBlock + t];
+  }
+  while (blk >= 0) {                                          // uniform
+    __syncthreads();                                          // the last block is consumed
+    {
+      // pieces t and t + NT are K (row v / 16, dims 8 (v % 16)), t + 2 NT
+      // and t + 3 NT the V part
+      *reinterpret_cast<uint4 *>(kv_sh + (t >> 4) * kPaKPitch + 16 * (t & 15)) = pre0;
+      *reinterpret_cast<uint4 *>(kv_sh + ((t + NT) >> 4) * kPaKPitch + 16 * (t & 15)) = pre1;
+      *reinterpret_cast<uint4 *>(kv_sh + kPaKBytes + 16 * t) = pre2;
+      *reinterpret_cast<uint4 *>(kv_sh + kPaKBytes + 16 * (t + NT)) = pre3;
+      if (t < kBlock) s_sh[t] = spre;
+    }
+    __syncthreads();
+    const int nxt = next_block(blk + 1);
+    if (nxt >= 0) {
+      const uint4 *src = kvg + (size_t)nxt * (kBlockElems * 2 / 16) + t;
+      pre0 = src[0];
+      pre1 = src[NT];
+      pre2 = src[2 * NT];
+      pre3 = src[3 * NT];
+      if (t < kBlock) spre = tsp[nxt * kBlock + t];
+    }
+    const bool sel_col = col_ok && ((bits[ql * words + (blk >> 5)] >> (blk & 31)) & 1u);
+    if (__ballot(sel_col) == 0) {                             // none of this wave's queries
+      blk = nxt;
+      continue;
     }
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) vv[dt] = *reinterpret_cast<const uint4 *>(vb + 16 * l + 1024 * dt);
-    const int key_base = blk * kBlock + 32 * half;
-    const float sv_lane = tsp[key_base + (l & 31)];
-    f32x4 acc[2];
+    for (int half = 0; half < 2; ++half) {
+      uint4 kk[2][4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < 4; ++s) {
+        kk[0][s] = *reinterpret_cast<const uint4 *>(kv_sh + half * 32 * kPaKPitch + koff0 + 64 * s);
+        kk[1][s] = *reinterpret_cast<const uint4 *>(kv_sh + half * 32 * kPaKPitch + koff1 + 64 * s);
+      }
+      f32x4 acc[2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc[t] = mfma16x16x32(as_bf16x8(kk[t][s]), qop[s], acc[t]);
+      for (int tt = 0; tt < 2; ++tt) {
+        acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc[tt] = mfma16x16x32(as_bf16x8(kk[tt][s]), qop[s], acc[tt]);
+      }
+      const int key0 = blk * kBlock + 32 * half + 8 * lg;   // this lane's first key
+      float x[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float sv = s_sh[32 * half + 8 * lg + m];
+        const float lg2 = acc[m >> 2][m & 3] * qscale + sv * bscale;
+        x[m] = (sel_col && key0 + m <= qpos) ? lg2 : -INFINITY;
+        mx = fmaxf(mx, x[m]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const bool live = m_new != -INFINITY;                  // this column has a key so far
+      const float alpha = live ? exp2f(m_run - m_new) : 1.0f;
+      float psum = 0.0f;
+      uint32_t phi[4], plo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 pm = live ? f32x2{exp2f(x[2 * i] - m_new), exp2f(x[2 * i + 1] - m_new)}
+                              : f32x2{0.f, 0.f};
+        psum += pm[0] + pm[1];
+        const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(pm, bf16x2));
+        const f32x2 back = {__uint_as_float(hi << 16), __uint_as_float(hi & 0xFFFF0000u)};
+        phi[i] = hi;
+        plo[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pm - back, bf16x2));
+      }
+      if (live) m_run = m_new;
+      l_run = l_run * alpha + psum;
+      const bf16x8 bhi = __builtin_bit_cast(bf16x8, uint4{phi[0], phi[1], phi[2], phi[3]});
+      const bf16x8 blo = __builtin_bit_cast(bf16x8, uint4{plo[0], plo[1], plo[2], plo[3]});
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16x8 vt = as_bf16x8(*reinterpret_cast<const uint4 *>(
+            kv_sh + kPaKBytes + half * 8192 + 16 * l + 1024 * dt));
+        o[dt] *= alpha;
+        o[dt] = mfma16x16x32(vt, bhi, o[dt]);
+        o[dt] = mfma16x16x32(vt, blo, o[dt]);
+      }
     }
-    const int key0 = key_base + 8 * lg;                      // this lane's first key
-    float x[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const float sv = __shfl(sv_lane, 8 * lg + m, 64);
-      const float lg2 = acc[m >> 2][m & 3] * qscale + sv * bscale;
-      x[m] = (sel_col && key0 + m <= qpos) ? lg2 : -INFINITY;
-      mx = fmaxf(mx, x[m]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const bool live = m_new != -INFINITY;                    // this column has a key so far
-    const float alpha = live ? exp2f(m_run - m_new) : 1.0f;
-    float psum = 0.0f;
-    uint32_t phi[4], plo[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x2 pm = live ? f32x2{exp2f(x[2 * i] - m_new), exp2f(x[2 * i + 1] - m_new)}
-                            : f32x2{0.f, 0.f};
-      psum += pm[0] + pm[1];
-      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(pm, bf16x2));
-      const f32x2 back = {__uint_as_float(hi << 16), __uint_as_float(hi & 0xFFFF0000u)};
-      phi[i] = hi;
-      plo[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pm - back, bf16x2));
-    }
-    if (live) m_run = m_new;
-    l_run = l_run * alpha + psum;
-    const bf16x8 bhi = __builtin_bit_cast(bf16x8, uint4{phi[0], phi[1], phi[2], phi[3]});
-    const bf16x8 blo = __builtin_bit_cast(bf16x8, uint4{plo[0], plo[1], plo[2], plo[3]});
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      o[dt] *= alpha;
-      o[dt] = mfma16x16x32(as_bf16x8(vv[dt]), bhi, o[dt]);
-      o[dt] = mfma16x16x32(as_bf16x8(vv[dt]), blo, o[dt]);
-    }
+    blk = nxt;
   }
   if (__ballot(bad) && l == 0) atomicOr(st.status, NOSA_STATUS_BAD_SEL);
 
@@ -283,8 +318,9 @@ hipError_t launch_prefill_select(const Dims &d, const nosa_state &st, const floa
 hipError_t launch_prefill_attend(const Dims &d, const nosa_state &st, const uint16_t *q, int T,
                                  int pos0, const int32_t *sel, const int32_t *n_sel, float *out,
                                  hipStream_t s) {
-  const int QG = kPaWaves * (16 / pa_rows(d.G));
-  prefill_attend_kernel<<<dim3((T + QG - 1) / QG, d.P), kPaWaves * 64, 0, s>>>(
+  const int QW = kPaWaves * pa_queries_per_wave(d.G);
+  const size_t lds = (size_t)(QW + 1) * d.elig_words * sizeof(uint32_t);
+  prefill_attend_kernel<<<dim3((T + QW - 1) / QW, d.P), kPaWaves * 64, lds, s>>>(
       d, st, q, T, pos0, sel, n_sel, out);
   return hipGetLastError();
 }
