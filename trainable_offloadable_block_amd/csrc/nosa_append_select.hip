@@ -19,6 +19,7 @@
 namespace nosa {
 namespace {
 
+template <bool MULTI>
 __global__ __launch_bounds__(kScoreThreads) void append_select_kernel(
     Dims d, nosa_state st, const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
     const uint16_t *__restrict__ q, float *ws_e, float *ws_stats, int32_t *ws_count, int c_pad,
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(kScoreThreads) void append_select_kernel(
   if (wg == n_wg) {                                       // uniform
     append_pair<kScoreThreads>(d, st, k_new, v_new, b, g, pos, true, ash);
   } else {
-    score_splits(d, st.ckey, q, L, ws_e, ws_stats, c_pad, n_splits, subs, wg, p);
+    score_splits<MULTI>(d, st.ckey, q, L, ws_e, ws_stats, c_pad, n_splits, subs, wg, p);
   }
   __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
   __syncthreads();
@@ -68,7 +69,8 @@ hipError_t launch_append_select(const Dims &d, const nosa_state &st, const uint1
   float *ws_e = reinterpret_cast<float *>(base + lay.e_off);
   float *ws_stats = reinterpret_cast<float *>(base + lay.stats_off);
   int32_t *ws_count = reinterpret_cast<int32_t *>(base + lay.count_off);
-  append_select_kernel<<<dim3(lay.n_wg + 1, d.P), kScoreThreads, select_dyn_lds(d, lay), s>>>(
+  auto kernel = lay.subs > 1 ? append_select_kernel<true> : append_select_kernel<false>;
+  kernel<<<dim3(lay.n_wg + 1, d.P), kScoreThreads, select_dyn_lds(d, lay), s>>>(
       d, st, k_new, v_new, q, ws_e, ws_stats, ws_count, lay.c_pad, lay.n_splits, lay.subs, sel,
       n_sel, kind, dbg);
   return hipGetLastError();

@@ -25,6 +25,7 @@ namespace {
 // grid (scoring workgroups, pairs): every workgroup scores its `subs`
 // splits and arrives on the pair's counter once its results have landed; the
 // last one pools and selects, then resets the counter (zero at rest).
+template <bool MULTI>
 __global__ __launch_bounds__(kScoreThreads) void select_kernel(
     Dims d, nosa_state st, const uint16_t *__restrict__ q, float *ws_e, float *ws_stats,
     int32_t *ws_count, int c_pad, int n_splits, int subs, int32_t *__restrict__ sel,
@@ -32,7 +33,7 @@ __global__ __launch_bounds__(kScoreThreads) void select_kernel(
   const int p = blockIdx.y;
   __shared__ int sm_last;
   const int L = st.seq_len[p / d.Hkv];
-  score_splits(d, st.ckey, q, L, ws_e, ws_stats, c_pad, n_splits, subs, blockIdx.x, p);
+  score_splits<MULTI>(d, st.ckey, q, L, ws_e, ws_stats, c_pad, n_splits, subs, blockIdx.x, p);
   __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
   __syncthreads();
   if (threadIdx.x == 0)
@@ -81,7 +82,8 @@ hipError_t launch_select(const Dims &d, const nosa_state &st, const uint16_t *q,
   float *ws_e = reinterpret_cast<float *>(base + lay.e_off);
   float *ws_stats = reinterpret_cast<float *>(base + lay.stats_off);
   int32_t *ws_count = reinterpret_cast<int32_t *>(base + lay.count_off);
-  select_kernel<<<dim3(lay.n_wg, d.P), kScoreThreads, select_dyn_lds(d, lay), s>>>(
+  auto kernel = lay.subs > 1 ? select_kernel<true> : select_kernel<false>;
+  kernel<<<dim3(lay.n_wg, d.P), kScoreThreads, select_dyn_lds(d, lay), s>>>(
       d, st, q, ws_e, ws_stats, ws_count, lay.c_pad, lay.n_splits, lay.subs, sel, n_sel, kind,
       dbg);
   return hipGetLastError();

@@ -164,17 +164,24 @@ __device__ __forceinline__ void score_compute(const Dims &d, int C, ScoreIn &in,
 constexpr int kSelectWgBudget = 1024;   // resident workgroups of one round (4 per CU)
 
 // Splits ws * subs .. ws * subs + subs - 1 of pair p (those below n_splits),
-// one after another: the newest chunk left out (split_chunks).
+// one after another: the newest chunk left out (split_chunks). The first
+// split's loads go out before the length is used. MULTI = false compiles
+// the one-split case alone (subs = 1), without the loop's code.
+template <bool MULTI>
 __device__ __forceinline__ void score_splits(const Dims &d, const uint16_t *__restrict__ ckey,
                                              const uint16_t *__restrict__ q, int L, float *ws_e,
                                              float *ws_stats, int c_pad, int n_splits, int subs,
                                              int ws, int p) {
+  const int split0 = MULTI ? ws * subs : ws;       // < n_splits: ceil(n_splits / subs) groups
+  ScoreIn in;
+  score_load(d, ckey, q, split0, p, in);
   const int C = split_chunks(d, L, c_pad);
-  for (int j = 0; j < subs; ++j) {                 // uniform
-    const int split = ws * subs + j;
+  score_compute(d, C, in, ws_e, ws_stats, c_pad, n_splits, split0, p);
+  if (!MULTI) return;
+  for (int j = 1; j < subs; ++j) {                 // uniform
+    const int split = split0 + j;
     if (split >= n_splits) break;
-    if (j > 0) __syncthreads();                    // the last split's reductions are read
-    ScoreIn in;
+    __syncthreads();                               // the last split's reductions are read
     score_load(d, ckey, q, split, p, in);
     score_compute(d, C, in, ws_e, ws_stats, c_pad, n_splits, split, p);
   }
