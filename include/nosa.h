@@ -39,6 +39,13 @@
  *    untouched; they surface when the caller reads status.
  *  - A pair is (sequence b, KV head g); pair index p = b * n_kv_heads + g.
  *    Query head h belongs to KV head h / (n_q_heads / n_kv_heads).
+ *  - Launch-shape overrides for tuning sweeps, read from the environment at
+ *    each call (results do not depend on them): NOSA_DECODE_BPS (selection
+ *    entries per decode workgroup, 4..64; it sets the decode workspace size,
+ *    so it must not change between nosa_workspace_bytes and the calls),
+ *    NOSA_SELECT_SUBS (128-chunk splits per scoring workgroup),
+ *    NOSA_GATHER_VPT (1, 2, 4 or 8: 4 KiB pieces of a block a
+ *    nosa_fetch_delta_wg workgroup moves at a time).
  */
 #ifndef NOSA_H
 #define NOSA_H
