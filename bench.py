@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--offload-steps", type=int, default=24)
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the many-query block-score (sparse prefill) leg")
+    ap.add_argument("--only-next", action="store_true",
+                    help="run only the GQA-16 96-block leg and print its JSON")
     ap.add_argument("--only-prefill", action="store_true",
                     help="run only the many-query block-score leg and print its JSON")
     ap.add_argument("--no-ahead", action="store_true",
@@ -725,6 +727,9 @@ def main():
         return
     if args.only_prefill:
         print(json.dumps(prefill_scores_leg(dev, workers)), flush=True)
+        return
+    if args.only_next:
+        print(json.dumps(next_leg(dev, workers)), flush=True)
         return
     wl = WORKLOADS[2]
     R, W, K = args.layers, args.warmup, args.steps
