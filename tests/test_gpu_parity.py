@@ -530,3 +530,29 @@ def test_sparse_prefill_16k_sampled():
     rows against the oracle."""
     _sparse_prefill_case(WORKLOADS[2], 512, 16384 - 512, check_pairs=[0, 31, 63],
                          rows=[0, 1, 100, 255, 256, 400, 510, 511])
+
+
+def test_select_splits_per_workgroup_do_not_change_results():
+    """A scoring workgroup that takes several 128-chunk splits one after
+    another (the launch shape for large contexts) gives the same selection,
+    kinds and scores, bit for bit, as one split per workgroup."""
+    # 6000 tokens: 374 chunks in 3 splits; two per workgroup leaves one alone
+    wl = small_workload(181, context=6000, steps=20, k_blocks=12, k_q_blocks=4, k_e_blocks=8)
+    a = Lockstep(wl, check_pairs=[], fused=True)
+    b = Lockstep(wl, check_pairs=[], fused=True)
+    for t in range(wl.steps):
+        kd, vd, qd = a.inputs(t)
+        for ls, subs in ((a, "1"), (b, "2")):
+            os.environ["NOSA_SELECT_SUBS"] = subs
+            try:
+                ls.gpu.append_select(kd, vd, qd, want_kind=True, want_qscore=True)
+            finally:
+                os.environ.pop("NOSA_SELECT_SUBS", None)
+        torch.cuda.synchronize()
+        for n in ("sel", "n_sel", "kind"):
+            assert torch.equal(getattr(a.gpu, n), getattr(b.gpu, n)), f"step {t}: {n}"
+        assert torch.equal(torch.nan_to_num(a.gpu.dbg_q, nan=-7.0),
+                           torch.nan_to_num(b.gpu.dbg_q, nan=-7.0)), f"step {t}: qscore"
+        sa, sb = _state_tensors(a.gpu), _state_tensors(b.gpu)
+        for n in sa:
+            assert torch.equal(sa[n], sb[n]), f"step {t}: state {n}"
