@@ -25,7 +25,9 @@ __global__ __launch_bounds__(kScoreThreads) void append_select_kernel(
     const uint16_t *__restrict__ q, float *ws_e, float *ws_stats, int32_t *ws_count, int c_pad,
     int n_splits, int subs, int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
     uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
-  const int wg = blockIdx.x, p = blockIdx.y, n_wg = gridDim.x - 1;
+  int wg, p;
+  grid_unit(wg, p);
+  const int n_wg = gridDim.x - 1;
   const int b = p / d.Hkv, g = p % d.Hkv;
   __shared__ AppendLds ash;
   __shared__ int sm_last;

@@ -131,4 +131,18 @@ struct Dims {
   int offload, bias;
 };
 
+// This workgroup's (x, y) in a 2-D grid whose rows (one pair's workgroups,
+// x fastest) should share an XCD: the hardware deals workgroups to the 8
+// XCDs round-robin by linear id L, so unit (L % 8) * (total / 8) + L / 8
+// keeps each run of total / 8 consecutive units on XCD L % 8 (when total is
+// a multiple of 8; otherwise the ids are kept). Only placement depends on
+// it: the kernels' cross-workgroup traffic is device-coherent either way.
+__device__ inline void grid_unit(int &x, int &y) {
+  const int nx = gridDim.x, total = nx * gridDim.y;
+  int L = blockIdx.x + nx * blockIdx.y;
+  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+  x = L % nx;
+  y = L / nx;
+}
+
 }  // namespace nosa

@@ -243,7 +243,8 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
     const float *__restrict__ tok_s, float *__restrict__ ws_o, float2 *__restrict__ ws_ml,
     int32_t *__restrict__ ws_count, int bps, int n_splits, float *__restrict__ out,
     uint32_t *status) {
-  const int split = blockIdx.x, p = blockIdx.y;
+  int split, p;
+  grid_unit(split, p);
   const int b = p / d.Hkv, g = p % d.Hkv;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
   const int h = l & 15, lg = l >> 4;
@@ -258,6 +259,10 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   }
   const int L = seq_len[b];
   const int ns = max(0, min(n_sel[p], d.k));
+  // wait for the ids here, on every path: a path that skipped the wait
+  // would leave the compiler waiting for every load in flight at each
+  // iteration of the streaming loop, the prefetched half included
+  asm volatile("" ::"v"(lane_blk), "v"(lane_slot));
 
   __shared__ float sm_m[4][16], sm_l[4][16];
   __shared__ float sm_o[4][16][kHeadDim + 4];

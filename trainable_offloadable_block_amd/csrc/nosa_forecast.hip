@@ -123,7 +123,8 @@ __global__ __launch_bounds__(kScoreThreads) void forecast_select_kernel(
     Dims d, nosa_state st, const uint16_t *__restrict__ f, float *ws_l, int32_t *ws_count,
     int c_pad, int n_splits, int subs, int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
     uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
-  const int p = blockIdx.y;
+  int wg, p;
+  grid_unit(wg, p);
   __shared__ int sm_last;
   Dims df = d;                       // f is [B][Hkv][128]: a group of one head
   df.G = 1;
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(kScoreThreads) void forecast_select_kernel(
   const int L = max(0, min(st.seq_len[p / d.Hkv], d.max_context));
   const int C = min(min(chunks_for(L), d.C_max), c_pad);
   for (int j = 0; j < subs; ++j) {                 // uniform: this workgroup's splits
-    const int split = blockIdx.x * subs + j;
+    const int split = wg * subs + j;
     if (split >= n_splits) break;
     ScoreIn in;
     score_load(df, st.ckey, f, split, p, in);

@@ -30,10 +30,11 @@ __global__ __launch_bounds__(kScoreThreads) void select_kernel(
     Dims d, nosa_state st, const uint16_t *__restrict__ q, float *ws_e, float *ws_stats,
     int32_t *ws_count, int c_pad, int n_splits, int subs, int32_t *__restrict__ sel,
     int32_t *__restrict__ n_sel, uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
-  const int p = blockIdx.y;
+  int wg, p;
+  grid_unit(wg, p);
   __shared__ int sm_last;
   const int L = st.seq_len[p / d.Hkv];
-  score_splits<MULTI>(d, st.ckey, q, L, ws_e, ws_stats, c_pad, n_splits, subs, blockIdx.x, p);
+  score_splits<MULTI>(d, st.ckey, q, L, ws_e, ws_stats, c_pad, n_splits, subs, wg, p);
   __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
   __syncthreads();
   if (threadIdx.x == 0)
