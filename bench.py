@@ -51,6 +51,8 @@ def parse():
                     help="skip the many-query block-score (sparse prefill) leg")
     ap.add_argument("--only-next", action="store_true",
                     help="run only the GQA-16 96-block leg and print its JSON")
+    ap.add_argument("--only-8b", action="store_true",
+                    help="run only the offloaded 8B-shaped 64K leg and print its JSON")
     ap.add_argument("--only-prefill", action="store_true",
                     help="run only the many-query block-score leg and print its JSON")
     ap.add_argument("--no-ahead", action="store_true",
@@ -452,6 +454,27 @@ def offload_32k_leg(dev, workers, R=4, W=4, K=24, n_bd=8):
             "breakdown_us": m["breakdown"], "delta_fetch": m.get("fetch")}
 
 
+def offload_8b_64k_leg(dev, workers, W=4, K=32, n_bd=8):
+    """The offloaded 8B-shaped 64K layer (32 sequences, 32/8 heads, k = 64,
+    full KV in pinned host memory), one layer timed repeatedly: decode
+    tokens/s with the delta fetch on the step path, and the decode kernel
+    (256 pairs, one workgroup each, reading the device block cache) against
+    the HBM roofline."""
+    from synth import WORKLOADS
+    wl = WORKLOADS[4]
+    m = time_stack(wl, 1, W, K, n_bd, dev, workers)
+    dbytes = decode_bytes(wl, m["n_att"])
+    ach = dbytes / m["dec_avg_s"] / 1e9
+    return {"workload": wl.name, "layers_per_step": 1, "steps": K,
+            "value": round(m["value"], 1), "unit": "tokens/s/layer",
+            "ms_per_step": round(m["elapsed"] * 1e3 / K, 4),
+            "decode": {"achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": int(dbytes),
+                       "avg_launch_us": round(m["dec_avg_s"] * 1e6, 2),
+                       "attended_tokens_per_pair": round(m["n_att"], 2)},
+            "breakdown_us": m["breakdown"], "delta_fetch": m.get("fetch")}
+
+
 def forecast_inputs(wl, li, n, pool, device):
     """Per-step forecast heads that select layer li: [n][B][Hkv][128]."""
     import numpy as np
@@ -728,6 +751,9 @@ def main():
     if args.only_prefill:
         print(json.dumps(prefill_scores_leg(dev, workers)), flush=True)
         return
+    if args.only_8b:
+        print(json.dumps(offload_8b_64k_leg(dev, workers)), flush=True)
+        return
     if args.only_next:
         print(json.dumps(next_leg(dev, workers)), flush=True)
         return
@@ -787,6 +813,8 @@ def main():
     if not args.no_offload:
         log("offloaded 32K stack leg")
         res["offload_32k"] = offload_32k_leg(dev, workers)
+        log("offloaded 8B-shaped 64K leg")
+        res["offload_8b_64k"] = offload_8b_64k_leg(dev, workers)
         if not args.no_ahead:
             log("layer-ahead leg (SparDA order, offloaded 32K stack)")
             res["layer_ahead"] = layer_ahead_leg(dev, workers, n_wg=args.fetch_wg)

@@ -29,7 +29,10 @@ __global__ __launch_bounds__(kScoreThreads) void append_select_kernel(
   grid_unit(wg, p);
   const int n_wg = gridDim.x - 1;
   const int b = p / d.Hkv, g = p % d.Hkv;
-  __shared__ AppendLds ash;
+  // the append's LDS and the pooling's share the dynamic region: the append
+  // workgroup pools (if it arrives last) only after its append is done
+  extern __shared__ __align__(16) uint8_t dyn_sh[];
+  AppendLds &ash = *reinterpret_cast<AppendLds *>(dyn_sh);
   __shared__ int sm_last;
   const int pos = st.seq_len[b];
   const bool ok = pos >= 0 && pos < d.max_context;
@@ -72,7 +75,8 @@ hipError_t launch_append_select(const Dims &d, const nosa_state &st, const uint1
   float *ws_stats = reinterpret_cast<float *>(base + lay.stats_off);
   int32_t *ws_count = reinterpret_cast<int32_t *>(base + lay.count_off);
   auto kernel = lay.subs > 1 ? append_select_kernel<true> : append_select_kernel<false>;
-  kernel<<<dim3(lay.n_wg + 1, d.P), kScoreThreads, select_dyn_lds(d, lay), s>>>(
+  const size_t lds = std::max(select_dyn_lds(d, lay), sizeof(AppendLds));
+  kernel<<<dim3(lay.n_wg + 1, d.P), kScoreThreads, lds, s>>>(
       d, st, k_new, v_new, q, ws_e, ws_stats, ws_count, lay.c_pad, lay.n_splits, lay.subs, sel,
       n_sel, kind, dbg);
   return hipGetLastError();
