@@ -54,23 +54,12 @@ struct ScoreIn {
   uint4 qv[4], kv[2][4];
 };
 
-// Issues the loads of split `split` of pair p. They do not depend on the
-// sequence length (rows past it are masked later), so they go out before it
-// is known and the kernel waits for one memory round trip.
-__device__ __forceinline__ void score_load(const Dims &d, const uint16_t *__restrict__ ckey,
-                                           const uint16_t *__restrict__ q, int split, int p,
-                                           ScoreIn &in) {
-  const int b = p / d.Hkv, g = p % d.Hkv;
+// Issues the loads of split `split`'s compressed keys of pair p.
+__device__ __forceinline__ void score_load_keys(const Dims &d, const uint16_t *__restrict__ ckey,
+                                                int split, int p, ScoreIn &in) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int h = l & 15, lg = l >> 4;
+  const int lg = l >> 4;
   const int cg = split * kChunksPerSplit + 32 * w;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) in.qv[s] = make_uint4(0, 0, 0, 0);
-  if (h < d.G) {
-    const uint16_t *qh = q + ((size_t)b * d.Hq + g * d.G + h) * kHeadDim + 8 * lg;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) in.qv[s] = *reinterpret_cast<const uint4 *>(qh + 32 * s);
-  }
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int chunk = cg + tile_row(l & 15, t);
@@ -82,6 +71,25 @@ __device__ __forceinline__ void score_load(const Dims &d, const uint16_t *__rest
       for (int s = 0; s < 4; ++s) in.kv[t][s] = *reinterpret_cast<const uint4 *>(src + 32 * s);
     }
   }
+}
+
+// Issues the loads of split `split` of pair p. They do not depend on the
+// sequence length (rows past it are masked later), so they go out before it
+// is known and the kernel waits for one memory round trip.
+__device__ __forceinline__ void score_load(const Dims &d, const uint16_t *__restrict__ ckey,
+                                           const uint16_t *__restrict__ q, int split, int p,
+                                           ScoreIn &in) {
+  const int b = p / d.Hkv, g = p % d.Hkv;
+  const int l = threadIdx.x & 63;
+  const int h = l & 15, lg = l >> 4;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) in.qv[s] = make_uint4(0, 0, 0, 0);
+  if (h < d.G) {
+    const uint16_t *qh = q + ((size_t)b * d.Hq + g * d.G + h) * kHeadDim + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) in.qv[s] = *reinterpret_cast<const uint4 *>(qh + 32 * s);
+  }
+  score_load_keys(d, ckey, split, p, in);
 }
 
 // Chunks scored by the split workgroups at length L: every complete chunk
@@ -119,8 +127,9 @@ __device__ __forceinline__ void score_compute(const Dims &d, int C, ScoreIn &in,
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc[t] = mfma16x16x32(as_bf16x8(kv[t][s]), as_bf16x8(qv[s]), acc[t]);
   }
-  // lane (h, lg) now holds head h against chunks cg + 8*lg + m, m = 0..7
-  const float scale = 0.08838834764831845f;   // 1/sqrt(128)
+  // lane (h, lg) now holds head h against chunks cg + 8*lg + m, m = 0..7;
+  // logits in the log2 domain, so each weight is one hardware exp2
+  const float scale = 0.08838834764831845f * 1.4426950408889634f;   // log2(e) / sqrt(128)
   float x[8];
   float mx = -INFINITY;
 #pragma unroll
@@ -133,12 +142,14 @@ __device__ __forceinline__ void score_compute(const Dims &d, int C, ScoreIn &in,
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
   if (lg == 0) red_m[w][h] = mx;
   __syncthreads();
+  // the split's first chunk is below C, so M is finite and exp2 of a
+  // masked logit (-inf) is 0
   const float M = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
   float ev[8];
   float z = 0.0f;
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-    ev[m] = x[m] == -INFINITY ? 0.0f : expf(x[m] - M);
+    ev[m] = __builtin_amdgcn_exp2f(x[m] - M);
     z += ev[m];
   }
   z += __shfl_xor(z, 16, 64);
@@ -156,7 +167,7 @@ __device__ __forceinline__ void score_compute(const Dims &d, int C, ScoreIn &in,
     const int hh = threadIdx.x;
     const float Mh = fmaxf(fmaxf(red_m[0][hh], red_m[1][hh]), fmaxf(red_m[2][hh], red_m[3][hh]));
     const float Zh = (red_z[0][hh] + red_z[1][hh]) + (red_z[2][hh] + red_z[3][hh]);
-    put(&stats[2 * hh], Mh);
+    put(&stats[2 * hh], Mh * 0.6931471805599453f);   // back to the natural domain
     put(&stats[2 * hh + 1], Zh);
   }
 }
@@ -182,7 +193,7 @@ __device__ __forceinline__ void score_splits(const Dims &d, const uint16_t *__re
     const int split = split0 + j;
     if (split >= n_splits) break;
     __syncthreads();                               // the last split's reductions are read
-    score_load(d, ckey, q, split, p, in);
+    score_load_keys(d, ckey, split, p, in);        // the query rows stay
     score_compute(d, C, in, ws_e, ws_stats, c_pad, n_splits, split, p);
   }
 }
@@ -432,6 +443,7 @@ __device__ __forceinline__ void select_stages(const Dims &d, int p, int n_cand, 
 
 constexpr int kMaxCandPerThread = (kMaxContext / kBlock) / kTopkThreads;   // 16
 constexpr int kLoadBatch = 8;     // chunk-weight float4 loads in flight per thread
+constexpr int kStatBatches = 4;   // split statistics loaded early: 16 splits each
 
 // Both stages, the ascending selection list and the eligibility update of
 // pair p at a length with nb blocks, once the chunk scores a_sh[0, C), the
@@ -551,8 +563,14 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
   const int sh_h = t >> 4, sh_j = t & 15;
   const __amdgpu_buffer_rsrc_t sr =
       make_rsrc(ws_stats + (size_t)2 * p * n_splits * d.G, (uint32_t)n_splits * d.G * 8);
-  float2 stv_raw = make_float2(-INFINITY, 0.0f);
-  if (sh_h < d.G && sh_j < n_splits) stv_raw = load2_coherent(sr, 8 * (sh_j * d.G + sh_h));
+  // thread (sh_h, sh_j): head sh_h's statistics of splits sh_j + 16 i
+  float2 stv_raw[kStatBatches];
+#pragma unroll
+  for (int i = 0; i < kStatBatches; ++i) {
+    const int s = sh_j + 16 * i;
+    stv_raw[i] = (sh_h < d.G && s < n_splits) ? load2_coherent(sr, 8 * (s * d.G + sh_h))
+                                              : make_float2(-INFINITY, 0.0f);
+  }
 
   const int L = max(0, min(L_in, d.max_context));
   int C = chunks_for(L);
@@ -569,7 +587,6 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
   const int n4 = do_q ? Cs * Gp / 4 : 0;
   const bool have0 = t < n_cand;
   const float e0 = (do_e && have0) ? e0_raw : 0.0f;
-  const float2 stv = (do_q && sh_h < d.G && sh_j < used) ? stv_raw : make_float2(-INFINITY, 0.0f);
   // the newest chunk (C - 1): the group's logits against it on wave 0, with
   // the split kernels' MFMA (its row in A-row 0, read device-coherently:
   // the append of the same launch may have just written it)
@@ -616,17 +633,29 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
   // all complete chunks, the newest included (0 for the padding heads)
   if (do_q && sh_h < Gp) {
     const bool real = sh_h < d.G;
-    float m = stv.x;
+    constexpr int kPre = 16 * kStatBatches;          // splits held in registers
+    float2 sv[kStatBatches];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kStatBatches; ++i) {
+      sv[i] = (real && sh_j + 16 * i < used) ? stv_raw[i] : make_float2(-INFINITY, 0.0f);
+      m = fmaxf(m, sv[i].x);
+    }
     if (real)
-      for (int s = sh_j + 16; s < used; s += 16) m = fmaxf(m, load2_coherent(sr, 8 * (s * d.G + sh_h)).x);
+      for (int s = sh_j + kPre; s < used; s += 16) m = fmaxf(m, load2_coherent(sr, 8 * (s * d.G + sh_h)).x);
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     const float ln = (real && last_q) ? lnew_sh[sh_h] : -INFINITY;
     m = fmaxf(m, ln);
-    const float e0s = stv.y > 0.0f ? expf(stv.x - m) : 0.0f;
-    float z = stv.y * e0s;
+    float es[kStatBatches];
+    float z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kStatBatches; ++i) {
+      es[i] = sv[i].y > 0.0f ? expf(sv[i].x - m) : 0.0f;
+      z += sv[i].y * es[i];
+    }
     if (real)
-      for (int s = sh_j + 16; s < used; s += 16) {
+      for (int s = sh_j + kPre; s < used; s += 16) {
         const float2 v = load2_coherent(sr, 8 * (s * d.G + sh_h));
         if (v.y > 0.0f) z += v.y * expf(v.x - m);
       }
@@ -636,8 +665,10 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
     z += el;
     const float rz = real ? 1.0f / z : 0.0f;
     if (sh_j == 0) wlast_sh[sh_h] = el * rz;
-    if (sh_j < used) f_sh[sh_j * Gp + sh_h] = e0s * rz;
-    for (int s = sh_j + 16; s < used; s += 16) {
+#pragma unroll
+    for (int i = 0; i < kStatBatches; ++i)
+      if (sh_j + 16 * i < used) f_sh[(sh_j + 16 * i) * Gp + sh_h] = es[i] * rz;
+    for (int s = sh_j + kPre; s < used; s += 16) {
       const float2 v = real ? load2_coherent(sr, 8 * (s * d.G + sh_h)) : make_float2(-INFINITY, 0.0f);
       f_sh[s * Gp + sh_h] = v.y > 0.0f ? expf(v.x - m) * rz : 0.0f;
     }
