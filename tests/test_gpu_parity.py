@@ -556,3 +556,15 @@ def test_select_splits_per_workgroup_do_not_change_results():
         sa, sb = _state_tensors(a.gpu), _state_tensors(b.gpu)
         for n in sa:
             assert torch.equal(sa[n], sb[n]), f"step {t}: state {n}"
+
+
+def test_decode_one_split_per_pair():
+    """A pair whose whole selection is one workgroup's run (one split: the
+    output is normalised and written without the split merge) stays within
+    the oracle's tolerance, resident and offloaded."""
+    os.environ["NOSA_DECODE_BPS"] = "64"
+    try:
+        _run(small_workload(191, steps=12), fused=True)
+        _run(small_workload(192, steps=12, offload=True), fused=False)
+    finally:
+        os.environ.pop("NOSA_DECODE_BPS", None)

@@ -338,6 +338,23 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
 #pragma unroll
     for (int i = 0; i < 4; ++i) sm_o[w][h][16 * dt + 4 * lg + i] = o[dt][i];
   __syncthreads();
+  if (n_splits == 1) {                         // uniform: the pair's only split
+    for (int idx = threadIdx.x; idx < d.G * kHeadDim; idx += kDecThreads) {
+      const int hh = idx / kHeadDim, dim = idx % kHeadDim;
+      const float M = fmaxf(fmaxf(sm_m[0][hh], sm_m[1][hh]), fmaxf(sm_m[2][hh], sm_m[3][hh]));
+      float acc = 0.0f, lsum = 0.0f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const float f = exp2f(sm_m[ww][hh] - M);
+          acc += f * sm_o[ww][hh][dim];
+          lsum += f * sm_l[ww][hh];
+        }
+      }
+      out[((size_t)b * d.Hq + g * d.G + hh) * kHeadDim + dim] = lsum > 0.0f ? acc / lsum : 0.0f;
+    }
+    return;
+  }
   // publish this split's partial with device-coherent (agent-scope) stores,
   // wait for them, then count arrivals; the last workgroup of the pair reads
   // every partial back with device-coherent loads and merges. No
