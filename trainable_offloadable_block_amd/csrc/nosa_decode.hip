@@ -16,9 +16,6 @@
 namespace nosa {
 namespace {
 
-#ifndef NOSA_DECODE_GLOBAL_LOADS
-#define NOSA_DECODE_GLOBAL_LOADS 0
-#endif
 #ifndef NOSA_DECODE_MIN_WAVES
 #define NOSA_DECODE_MIN_WAVES 2     // <= 256 registers: two workgroups per CU fit
 #endif
@@ -64,8 +61,6 @@ struct DecodeArgs {
   const int32_t *sel, *phys;
   __amdgpu_buffer_rsrc_t kv;   // this pair's blocks
   __amdgpu_buffer_rsrc_t ts;   // this pair's eviction scores
-  const uint16_t *kv_ptr;      // the same, as plain pointers
-  const float *ts_ptr;
   int koff[2], voff, soff;     // per-lane byte offsets inside a block / half
   int p, slots, e_first, e_end;
 };
@@ -90,18 +85,6 @@ __device__ inline void load_half(Half &hb, int j, const DecodeArgs &a, const Dim
   const int kbase = slot * (kBlockElems * 2) + half * (32 * kHeadDim * 2);
   const int vbase = slot * (kBlockElems * 2) + kBlock * kHeadDim * 2 + half * 8192;
   hb.key_base = blk * kBlock + 32 * half;
-#if NOSA_DECODE_GLOBAL_LOADS
-  const char *kvb = reinterpret_cast<const char *>(a.kv_ptr);
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      hb.k[t][s] = *reinterpret_cast<const uint4 *>(kvb + kbase + a.koff[t] + 64 * s);
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-    hb.v[dt] = *reinterpret_cast<const uint4 *>(kvb + vbase + a.voff + 1024 * dt);
-  hb.s = a.ts_ptr[hb.key_base + (threadIdx.x & 31)];
-#else
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -110,7 +93,6 @@ __device__ inline void load_half(Half &hb, int j, const DecodeArgs &a, const Dim
   for (int dt = 0; dt < 8; ++dt) hb.v[dt] = bload16(a.kv, a.voff + 1024 * dt, vbase);
   hb.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(a.ts, a.soff,
                                                                         hb.key_base * 4, 0));
-#endif
 }
 
 // Online-softmax update with one half: logits on MFMA, then O^T += V^T P^T.
@@ -274,8 +256,6 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   a.kv = make_rsrc(kv + (size_t)p * slots_per_pair * kBlockElems,
                    (uint32_t)slots_per_pair * kBlockElems * 2);
   a.ts = make_rsrc(tok_s + (size_t)p * d.tok_stride, (uint32_t)d.tok_stride * 4);
-  a.kv_ptr = kv + (size_t)p * slots_per_pair * kBlockElems;
-  a.ts_ptr = tok_s + (size_t)p * d.tok_stride;
   a.koff[0] = tile_row(h, 0) * kHeadDim * 2 + 16 * lg;
   a.koff[1] = tile_row(h, 1) * kHeadDim * 2 + 16 * lg;
   a.voff = 16 * l;   // V tile: lane l holds dim l % 16, tokens 8 (l / 16) .. + 7
