@@ -288,8 +288,10 @@ def host_link_leg(n_steps, pool, dev):
 
 def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0):
     """Times K decode steps (after W warm-up steps) of a stack of R
-    independent layers of workload wl, with HIP events around every decode
-    launch; n_bd further steps give a per-call breakdown and the exact
+    independent layers of workload wl; every timed decode launch stamps its
+    own start and end into a pair of HIP events on its stream
+    (nosa_sparse_decode_timed); n_bd further steps give a per-call breakdown
+    (events recorded around each call) and the exact
     number of attended tokens. With graph_steps, the same stack then runs
     that many steps (after 4 untimed ones) as replays of one captured HIP
     graph of a whole step, each step's inputs copied into the graph's static
@@ -316,18 +318,20 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0):
             q, kn, vn = inputs[li][0][t], inputs[li][1][t], inputs[li][2][t]
             layer.append_select(kn, vn, q, want_kind=False)
             layer.fetch()
-            if events is not None:
-                events[0].append(torch.cuda.Event(enable_timing=True))
-                events[1].append(torch.cuda.Event(enable_timing=True))
-                events[0][-1].record()
-            layer.decode(q)
-            if events is not None:
-                events[1][-1].record()
+            if events is None:
+                layer.decode(q)
+            else:                  # the kernel stamps its own start and end
+                i = (t - W) * len(layers) + li
+                layer.decode(q, events=(events[0][i], events[1][i]))
 
     for t in range(W):
         run_step(t)
+    # the timed launches' events, created (first record) before the timed region
+    ev = tuple([torch.cuda.Event(enable_timing=True) for _ in range(K * R)] for _ in range(2))
+    for lst in ev:
+        for e in lst:
+            e.record()
     torch.cuda.synchronize()
-    ev = ([], [])
     t0 = time.perf_counter()
     for t in range(W, W + K):
         run_step(t, ev)
@@ -790,6 +794,8 @@ def main():
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
             "bytes_per_launch": int(dbytes), "avg_launch_us": round(dec_avg_s * 1e6, 2),
+            "timing": "HIP events stamped by each timed decode launch (hipExtLaunchKernel)",
+            "call_us_events_around": bd["decode"],
             "attended_tokens_per_pair": round(n_att, 2),
         },
         "breakdown_us": bd,

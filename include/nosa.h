@@ -304,6 +304,20 @@ int nosa_sparse_decode(const nosa_config *cfg, const nosa_state *st,
                        void *ws, size_t ws_bytes, int32_t max_len_host,
                        hipStream_t stream);
 
+/* nosa_sparse_decode whose kernel launch also stamps its own start and end
+ * into start_event and stop_event (hipExtLaunchKernel): the interval the
+ * command processor records for the dispatch, as a kernel trace reports it,
+ * without the dispatch gap that a hipEventRecord pair around the call adds.
+ * Both events are caller-created (hipEventCreate, timing enabled) and
+ * caller-owned; NULL for either returns NOSA_ERR_INVALID. Same outputs,
+ * state changes and ws as nosa_sparse_decode. */
+int nosa_sparse_decode_timed(const nosa_config *cfg, const nosa_state *st,
+                             const uint16_t *q, const int32_t *sel,
+                             const int32_t *phys, const int32_t *n_sel,
+                             float *out, void *ws, size_t ws_bytes,
+                             int32_t max_len_host, hipStream_t stream,
+                             hipEvent_t start_event, hipEvent_t stop_event);
+
 /* Block scores of many prompt queries at once: the selection side of NOSA_S's
  * sparse prefill (aiwiki "NOSA", Results: NOSA_S is sparse in both phases),
  * each query scored exactly as a decode step at its own length would score it

@@ -133,6 +133,14 @@ def test_calls_reject_before_any_hip_call():
                            260, 1 << 40, 16640, null) == L.NOSA_ERR_WORKSPACE
     assert lib.nosa_sparse_decode(ctypes.byref(c), ctypes.byref(st), 256, 256, 256, 256,
                                   256, null, 0, 16640, null) == L.NOSA_ERR_WORKSPACE
+    # timed decode: both events required; then the same checks as the plain call
+    for evs in ((null, null), (256, null), (null, 256)):
+        assert lib.nosa_sparse_decode_timed(ctypes.byref(c), ctypes.byref(st), 256, 256, 256,
+                                            256, 256, 256, 1 << 20, 16640, null,
+                                            *evs) == L.NOSA_ERR_INVALID
+    assert lib.nosa_sparse_decode_timed(ctypes.byref(c), ctypes.byref(st), 256, 256, 256, 256,
+                                        256, null, 0, 16640, null, 256,
+                                        256) == L.NOSA_ERR_WORKSPACE
     # forecast selection: workspace too small; budgeted fetch: bad budget
     assert lib.nosa_select_forecast(ctypes.byref(c), ctypes.byref(st), 256, 256, 256, null,
                                     null, 256, 16, 16640, null) == L.NOSA_ERR_WORKSPACE

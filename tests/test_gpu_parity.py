@@ -568,3 +568,29 @@ def test_decode_one_split_per_pair():
         _run(small_workload(192, steps=12, offload=True), fused=False)
     finally:
         os.environ.pop("NOSA_DECODE_BPS", None)
+
+
+def test_timed_decode_equals_decode():
+    """nosa_sparse_decode_timed writes the same output as nosa_sparse_decode,
+    bit for bit, and the interval its kernel stamps is positive and inside
+    the interval of events recorded around the call."""
+    wl = small_workload(193, steps=4)
+    ls = Lockstep(wl, check_pairs=[])
+    g = ls.gpu
+    kd, vd, qd = ls.inputs(0)
+    g.append_select(kd, vd, qd, want_kind=True)
+    g.fetch()
+    g.decode(qd)
+    torch.cuda.synchronize()
+    ref = g.out.clone()
+    g.out.fill_(-1.0)
+    e0, e1, a0, a1 = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in (e0, e1):
+        e.record()
+    a0.record()
+    g.decode(qd, events=(e0, e1))
+    a1.record()
+    torch.cuda.synchronize()
+    assert torch.equal(g.out, ref)
+    k_ms, c_ms = e0.elapsed_time(e1), a0.elapsed_time(a1)
+    assert 0.0 < k_ms <= c_ms + 1e-3, (k_ms, c_ms)

@@ -99,6 +99,8 @@ def lib():
                                                ctypes.c_size_t, _P]),
         "nosa_sparse_decode": (ctypes.c_int, [cfgp, stp, _P, _P, _P, _P, _P,
                                               _P, ctypes.c_size_t, _I32, _P]),
+        "nosa_sparse_decode_timed": (ctypes.c_int, [cfgp, stp, _P, _P, _P, _P, _P,
+                                                    _P, ctypes.c_size_t, _I32, _P, _P, _P]),
         "nosa_prefill_block_scores": (ctypes.c_int, [cfgp, stp, _P, _I32, _I32, _P, _P]),
         "nosa_prefill_select": (ctypes.c_int, [cfgp, stp, _P, _I32, _I32, _P, _P, _P]),
         "nosa_prefill_attend": (ctypes.c_int, [cfgp, stp, _P, _I32, _I32, _P, _P, _P, _P]),

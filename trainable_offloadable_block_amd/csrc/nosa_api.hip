@@ -245,10 +245,10 @@ int nosa_fetch_delta_wg(const nosa_config *cfg, const nosa_state *st, const int3
   return fetch_common(cfg, st, sel, n_sel, phys, n_miss, n_workgroups, ws, ws_bytes, stream);
 }
 
-int nosa_sparse_decode(const nosa_config *cfg, const nosa_state *st, const uint16_t *q,
-                       const int32_t *sel, const int32_t *phys, const int32_t *n_sel,
-                       float *out, void *ws, size_t ws_bytes, int32_t max_len_host,
-                       hipStream_t stream) {
+static int decode_common(const nosa_config *cfg, const nosa_state *st, const uint16_t *q,
+                         const int32_t *sel, const int32_t *phys, const int32_t *n_sel,
+                         float *out, void *ws, size_t ws_bytes, int32_t max_len_host,
+                         hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   nosa::Dims d;
   int rc = make_dims(cfg, &d);
   if (!rc) rc = check_state(d, st);
@@ -259,7 +259,25 @@ int nosa_sparse_decode(const nosa_config *cfg, const nosa_state *st, const uint1
   const nosa::DecodeLayout lay = nosa::decode_layout(d);
   rc = check_ws(ws, ws_bytes, lay.bytes);
   if (rc) return rc;
-  return hip_result(nosa::launch_decode(d, *st, q, sel, phys, n_sel, out, ws, lay, stream));
+  return hip_result(nosa::launch_decode(d, *st, q, sel, phys, n_sel, out, ws, lay, stream,
+                                        ev_start, ev_stop));
+}
+
+int nosa_sparse_decode(const nosa_config *cfg, const nosa_state *st, const uint16_t *q,
+                       const int32_t *sel, const int32_t *phys, const int32_t *n_sel,
+                       float *out, void *ws, size_t ws_bytes, int32_t max_len_host,
+                       hipStream_t stream) {
+  return decode_common(cfg, st, q, sel, phys, n_sel, out, ws, ws_bytes, max_len_host, stream,
+                       nullptr, nullptr);
+}
+
+int nosa_sparse_decode_timed(const nosa_config *cfg, const nosa_state *st, const uint16_t *q,
+                             const int32_t *sel, const int32_t *phys, const int32_t *n_sel,
+                             float *out, void *ws, size_t ws_bytes, int32_t max_len_host,
+                             hipStream_t stream, hipEvent_t start_event, hipEvent_t stop_event) {
+  if (!start_event || !stop_event) return fail(NOSA_ERR_INVALID, "start / stop event is NULL");
+  return decode_common(cfg, st, q, sel, phys, n_sel, out, ws, ws_bytes, max_len_host, stream,
+                       start_event, stop_event);
 }
 
 int nosa_prefill_block_scores(const nosa_config *cfg, const nosa_state *st, const uint16_t *q,

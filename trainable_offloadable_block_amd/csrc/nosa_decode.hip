@@ -11,6 +11,8 @@
 //   (P alone in bf16 would cost ~1e-3 relative error). The 4 waves merge in
 //   LDS into one partial (m, l, o) per split; the last workgroup of a pair to
 //   finish merges all splits and writes the normalised output.
+#include <hip/hip_ext.h>
+
 #include "nosa_internal.h"
 
 namespace nosa {
@@ -405,15 +407,23 @@ DecodeLayout decode_layout(const Dims &d) {
 
 hipError_t launch_decode(const Dims &d, const nosa_state &st, const uint16_t *q,
                          const int32_t *sel, const int32_t *phys, const int32_t *n_sel,
-                         float *out, void *ws, const DecodeLayout &lay, hipStream_t s) {
+                         float *out, void *ws, const DecodeLayout &lay, hipStream_t s,
+                         hipEvent_t ev_start, hipEvent_t ev_stop) {
   char *base = static_cast<char *>(ws);
   float *ws_o = reinterpret_cast<float *>(base + lay.o_off);
   float2 *ws_ml = reinterpret_cast<float2 *>(base + lay.ml_off);
   int32_t *ws_count = reinterpret_cast<int32_t *>(base + lay.count_off);
   const int slots = d.offload ? d.k + 1 : d.NB_max;
-  decode_kernel<<<dim3(lay.n_splits, d.P), kDecThreads, 0, s>>>(
-      d, st.seq_len, q, sel, phys, n_sel, st.kv_dev, slots, st.tok_s, ws_o, ws_ml, ws_count,
-      lay.blocks_per_split, lay.n_splits, out, st.status);
+  if (ev_start || ev_stop) {
+    hipExtLaunchKernelGGL(decode_kernel, dim3(lay.n_splits, d.P), dim3(kDecThreads), 0, s,
+                          ev_start, ev_stop, 0, d, st.seq_len, q, sel, phys, n_sel, st.kv_dev,
+                          slots, st.tok_s, ws_o, ws_ml, ws_count, lay.blocks_per_split,
+                          lay.n_splits, out, st.status);
+  } else {
+    decode_kernel<<<dim3(lay.n_splits, d.P), kDecThreads, 0, s>>>(
+        d, st.seq_len, q, sel, phys, n_sel, st.kv_dev, slots, st.tok_s, ws_o, ws_ml, ws_count,
+        lay.blocks_per_split, lay.n_splits, out, st.status);
+  }
   return hipGetLastError();
 }
 

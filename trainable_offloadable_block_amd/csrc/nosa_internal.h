@@ -70,10 +70,13 @@ hipError_t launch_fetch(const Dims &d, const nosa_state &st,
                         const int32_t *sel, const int32_t *n_sel,
                         int32_t *phys, int32_t *n_miss, void *ws,
                         const FetchLayout &lay, hipStream_t s, int n_wg = 0);
+// With ev_start / ev_stop, the launch records the kernel's own start and end
+// into them (hipExtLaunchKernel).
 hipError_t launch_decode(const Dims &d, const nosa_state &st,
                          const uint16_t *q, const int32_t *sel,
                          const int32_t *phys, const int32_t *n_sel,
                          float *out, void *ws, const DecodeLayout &lay,
-                         hipStream_t s);
+                         hipStream_t s, hipEvent_t ev_start = nullptr,
+                         hipEvent_t ev_stop = nullptr);
 
 }  // namespace nosa

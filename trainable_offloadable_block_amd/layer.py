@@ -281,15 +281,26 @@ class NosaLayer:
             _ptr(self.phys), _ptr(self.n_miss), int(n_workgroups), _ptr(self.ws_fetch),
             self.ws_fetch.numel(), self.stream), "fetch_delta_wg")
 
-    def decode(self, q: torch.Tensor, sel=None, phys=None, n_sel=None):
+    def decode(self, q: torch.Tensor, sel=None, phys=None, n_sel=None, events=None):
+        """Sparse attention of the step into self.out. With events = (start,
+        stop), two torch.cuda.Event(enable_timing=True) objects, the kernel
+        stamps its own start and end into them (nosa_sparse_decode_timed)."""
         sel = self.sel if sel is None else sel
         if phys is None:
             phys = self.phys if self.shape.offload else sel
         n_sel = self.n_sel if n_sel is None else n_sel
-        L.check(L.lib().nosa_sparse_decode(
-            ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(q), _ptr(sel),
-            _ptr(phys), _ptr(n_sel), _ptr(self.out), _ptr(self.ws_decode),
-            self.ws_decode.numel(), self.max_len, self.stream), "sparse_decode")
+        args = (ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(q), _ptr(sel),
+                _ptr(phys), _ptr(n_sel), _ptr(self.out), _ptr(self.ws_decode),
+                self.ws_decode.numel(), self.max_len, self.stream)
+        if events is None:
+            L.check(L.lib().nosa_sparse_decode(*args), "sparse_decode")
+            return
+        handles = []
+        for ev in events:
+            if not ev.cuda_event:          # torch creates the HIP event on first record
+                ev.record()
+            handles.append(ctypes.c_void_p(ev.cuda_event))
+        L.check(L.lib().nosa_sparse_decode_timed(*args, *handles), "sparse_decode_timed")
 
     def step(self, k_new, v_new, q, want_kind=False, want_qscore=False):
         """append + select (one launch) -> fetch -> decode, all enqueued on
