@@ -117,6 +117,24 @@ def step_inputs(wl, li, n, pool, device):
     return dev(q), dev(k), dev(v)
 
 
+def locality_step(prev, cur, seq_len, wl):
+    """Per pair: gamma(t), the share of this step's selection S(t) that was in
+    S(t-1) or is the block this step's token opened (the oracle's locality()
+    definition; bounded below by k_e / k). prev and cur are (sel [P][k],
+    n_sel [P]) host arrays; seq_len is the length after the step's append."""
+    (ps, pn), (cs, cn) = prev, cur
+    g = []
+    for p in range(cs.shape[0]):
+        if cn[p] <= 0:
+            continue
+        pos = int(seq_len[p // wl.n_kv_heads]) - 1
+        have = set(ps[p, :pn[p]].tolist())
+        if pos % 64 == 0:
+            have.add(pos // 64)
+        g.append(sum(1 for b in cs[p, :cn[p]].tolist() if b in have) / int(cn[p]))
+    return g
+
+
 def decode_bytes(wl, n_att_per_pair):
     """Algorithmic bytes of one sparse-decode launch: K, V (bf16) and the
     eviction score (fp32) of every attended token, q (bf16) and out (fp32),
@@ -255,6 +273,8 @@ def host_link_leg(n_steps, pool, dev):
     del src, dst
     # delta fetch per step
     recs = []
+    k = wl.k_blocks
+    prev, gammas, hits = None, [], []
     for t in range(n_steps):
         layer.append_select(kn[t], vn[t], q[t], want_kind=False)
         a, b = ev(), ev()
@@ -263,8 +283,13 @@ def host_link_leg(n_steps, pool, dev):
         b.record()
         layer.decode(q[t])
         torch.cuda.synchronize()
-        misses = int(layer.n_miss.sum().item())
-        recs.append((misses * 32768, a.elapsed_time(b) * 1e3))
+        miss = layer.n_miss.cpu().numpy()
+        cur = (layer.sel.cpu().numpy().reshape(-1, k), layer.n_sel.cpu().numpy())
+        if t >= 4:
+            gammas += locality_step(prev, cur, layer.seq_len.cpu().numpy(), wl)
+            hits += [1.0 - m / n for m, n in zip(miss.tolist(), cur[1].tolist()) if n > 0]
+        prev = cur
+        recs.append((int(miss.sum()) * 32768, a.elapsed_time(b) * 1e3))
     status = layer.status_bits()
     assert not status, f"device status bits set: {status}"
     cold_b, cold_us = recs[0]
@@ -282,7 +307,12 @@ def host_link_leg(n_steps, pool, dev):
         "fetch_steady": {"bytes_per_step": int(st_b), "us_median": round(st_us, 1),
                          "GBps": round(gbps(st_b, st_us), 2),
                          "frac_of_peak": round(gbps(st_b, st_us) / best, 4),
-                         "steps": len(steady)},
+                         "steps": len(steady),
+                         "bound_bytes_per_step": wl.batch * wl.n_kv_heads * wl.k_q_blocks * 32768,
+                         "cache_hit_rate": round(float(np.mean(hits)), 4)},
+        "locality": {"gamma_min": round(float(np.min(gammas)), 4),
+                     "gamma_mean": round(float(np.mean(gammas)), 4),
+                     "bound": round((k - wl.k_q_blocks) / k, 4), "samples": len(gammas)},
     }
 
 
@@ -346,6 +376,12 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0):
     bd = {n: [] for n in names}
     n_att_samples = []
     fetched = []                                  # (bytes, us) per fetch call
+    gammas, hits = [], []
+    k = wl.k_blocks
+
+    def selection(layer):
+        return (layer.sel.cpu().numpy().reshape(-1, k), layer.n_sel.cpu().numpy())
+    prev = [selection(ly) for ly in layers]
     for t in range(W + K, W + K + n_bd):
         for li, layer in enumerate(layers):
             q, kn, vn = inputs[li][0][t], inputs[li][1][t], inputs[li][2][t]
@@ -361,9 +397,13 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0):
             for i, n in enumerate(names):
                 bd[n].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)
             n_att_samples.append(attended_tokens(layer, wl))
+            cur = selection(layer)
+            gammas += locality_step(prev[li], cur, layer.seq_len.cpu().numpy(), wl)
+            prev[li] = cur
             if wl.offload:
-                fetched.append((int(layer.n_miss.sum().item()) * 32768,
-                                evs[1].elapsed_time(evs[2]) * 1e3))
+                miss = layer.n_miss.cpu().numpy()
+                hits += [1.0 - m / n for m, n in zip(miss.tolist(), cur[1].tolist()) if n > 0]
+                fetched.append((int(miss.sum()) * 32768, evs[1].elapsed_time(evs[2]) * 1e3))
     graph = None
     if graph_steps:
         graph = graph_replays(layers, inputs, W + K + n_bd, graph_steps, shape)
@@ -373,11 +413,18 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0):
            "n_att": float(np.mean(n_att_samples)),
            "dec_avg_s": float(np.mean(dec_ms)) / 1e3,
            "breakdown": {n: round(float(np.median(v)), 2) for n, v in bd.items()}}
+    out["locality"] = {"gamma_min": round(float(np.min(gammas)), 4),
+                       "gamma_mean": round(float(np.mean(gammas)), 4),
+                       "bound": round((k - wl.k_q_blocks) / k, 4),
+                       "samples": len(gammas), "steps": n_bd}
     if fetched:
         b_ = float(np.mean([f[0] for f in fetched]))
         us = float(np.mean([f[1] for f in fetched]))
+        P = wl.batch * wl.n_kv_heads
         out["fetch"] = {"bytes_per_call": int(b_), "us_mean": round(us, 1),
-                        "GBps": round(b_ / (us * 1e-6) / 1e9, 2)}
+                        "GBps": round(b_ / (us * 1e-6) / 1e9, 2),
+                        "bound_bytes_per_call": P * wl.k_q_blocks * 32768,
+                        "cache_hit_rate": round(float(np.mean(hits)), 4)}
     if graph is not None:
         out["graph"] = {"steps": graph_steps, "ms_per_step": round(graph * 1e3 / graph_steps, 4),
                         "value": round(wl.batch * R * graph_steps / graph, 1)}
@@ -455,7 +502,8 @@ def offload_32k_leg(dev, workers, R=4, W=4, K=24, n_bd=8):
                        "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": int(dbytes),
                        "avg_launch_us": round(m["dec_avg_s"] * 1e6, 2),
                        "attended_tokens_per_pair": round(m["n_att"], 2)},
-            "breakdown_us": m["breakdown"], "delta_fetch": m.get("fetch")}
+            "breakdown_us": m["breakdown"], "delta_fetch": m.get("fetch"),
+            "locality": m["locality"]}
 
 
 def offload_8b_64k_leg(dev, workers, W=4, K=32, n_bd=8):
@@ -476,7 +524,8 @@ def offload_8b_64k_leg(dev, workers, W=4, K=32, n_bd=8):
                        "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": int(dbytes),
                        "avg_launch_us": round(m["dec_avg_s"] * 1e6, 2),
                        "attended_tokens_per_pair": round(m["n_att"], 2)},
-            "breakdown_us": m["breakdown"], "delta_fetch": m.get("fetch")}
+            "breakdown_us": m["breakdown"], "delta_fetch": m.get("fetch"),
+            "locality": m["locality"]}
 
 
 def forecast_inputs(wl, li, n, pool, device):
@@ -724,7 +773,7 @@ def next_leg(dev, workers, R=4, W=8, K=48):
                        "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": int(dbytes),
                        "avg_launch_us": round(m["dec_avg_s"] * 1e6, 2),
                        "attended_tokens_per_pair": round(m["n_att"], 2)},
-            "breakdown_us": m["breakdown"]}
+            "breakdown_us": m["breakdown"], "locality": m["locality"]}
 
 
 def main():
@@ -799,6 +848,7 @@ def main():
             "attended_tokens_per_pair": round(n_att, 2),
         },
         "breakdown_us": bd,
+        "locality": m["locality"],
     }
     if "graph" in m:
         res["graph_replay"] = m["graph"]

@@ -1,0 +1,50 @@
+"""Host-side helpers of bench.py (no GPU): the per-step locality it reports
+equals the oracle's gamma(t) on random selections, and the algorithmic byte
+count of a decode launch follows its definition."""
+
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from oracle import nosa_oracle as o  # noqa: E402
+from synth import WORKLOADS, small_workload  # noqa: E402
+
+
+def test_locality_step_equals_oracle_gamma():
+    wl = small_workload(301, batch=3, n_kv_heads=2, k_blocks=8)
+    rng = np.random.default_rng(5)
+    P, k = wl.batch * wl.n_kv_heads, wl.k_blocks
+    for trial in range(50):
+        lens = rng.integers(200, 2000, size=wl.batch)
+        if trial % 5 == 0:
+            lens[0] = 64 * rng.integers(4, 30) + 1          # the token opens a block
+        nb = (lens + 63) // 64
+        ps = np.full((P, k), -1, np.int32)
+        cs = np.full((P, k), -1, np.int32)
+        pn = rng.integers(1, k + 1, size=P).astype(np.int32)
+        cn = rng.integers(1, k + 1, size=P).astype(np.int32)
+        for p in range(P):
+            top = int(nb[p // wl.n_kv_heads])
+            pn[p], cn[p] = min(pn[p], top), min(cn[p], top)
+            ps[p, :pn[p]] = np.sort(rng.choice(top, size=pn[p], replace=False))
+            cs[p, :cn[p]] = np.sort(rng.choice(top, size=cn[p], replace=False))
+        got = bench.locality_step((ps, pn), (cs, cn), lens, wl)
+        want = []
+        for p in range(P):
+            pos = int(lens[p // wl.n_kv_heads]) - 1
+            new_block = pos // 64 if pos % 64 == 0 else None
+            want.append(o.locality(ps[p, :pn[p]].tolist(), cs[p, :cn[p]].tolist(), new_block))
+        assert np.allclose(got, want, rtol=0, atol=0)
+
+
+def test_decode_bytes_definition():
+    wl = WORKLOADS[2]
+    n_att = 4032.44
+    want = (n_att * wl.batch * wl.n_kv_heads * (2 * 128 * 2 + 4)
+            + wl.batch * wl.n_q_heads * 128 * (2 + 4) + wl.batch * wl.n_kv_heads * wl.k_blocks * 8)
+    assert bench.decode_bytes(wl, n_att) == want
