@@ -14,6 +14,7 @@
 #include <hip/hip_ext.h>
 
 #include "nosa_internal.h"
+#include "nosa_lanes.h"
 
 namespace nosa {
 namespace {
@@ -119,8 +120,7 @@ __device__ inline void process_half(Half &hb, const bf16x8 (&qop)[4], float qsca
     x[m] = (key0 + m) < L ? lg2 : -INFINITY;
     mx = fmaxf(mx, x[m]);
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = xor32_max(xor16_max(mx));
   const float m_new = fmaxf(m_run, mx);
   if (m_new == -INFINITY) return;              // wave-uniform: nothing valid
   const float alpha = exp2f(m_run - m_new);    // 0 while m_run = -inf
@@ -309,8 +309,7 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   if (bad && l == 0) atomicOr(status, NOSA_STATUS_BAD_SEL);
   // lane (h, lg): head h's running max, its keys' partial sum, and
   // O^T[16*dt + 4*lg + i][h]; merge the 4 waves in LDS
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = xor32_sum(xor16_sum(l_run));
   if (lg == 0) {
     sm_m[w][h] = m_run;
     sm_l[w][h] = l_run;

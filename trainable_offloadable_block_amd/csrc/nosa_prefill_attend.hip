@@ -259,8 +259,7 @@ __global__ __launch_bounds__(kPaWaves * 64) __attribute__((amdgpu_waves_per_eu(4
         x[m] = (sel_col && key0 + m <= qpos) ? lg2 : -INFINITY;
         mx = fmaxf(mx, x[m]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = xor32_max(xor16_max(mx));
       const float m_new = fmaxf(m_run, mx);
       const bool live = m_new != -INFINITY;                  // this column has a key so far
       const float alpha = live ? exp2f(m_run - m_new) : 1.0f;
@@ -294,8 +293,7 @@ __global__ __launch_bounds__(kPaWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   if (__ballot(bad) && l == 0) atomicOr(st.status, NOSA_STATUS_BAD_SEL);
 
   // 3. normalise and write: lane (h, lg) holds O^T[16 dt + 4 lg + i][h]
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = xor32_sum(xor16_sum(l_run));
   if (col_ok) {
     const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
     float *op = out + (((size_t)b * T + qi) * d.Hq + g * d.G + hh) * kHeadDim;

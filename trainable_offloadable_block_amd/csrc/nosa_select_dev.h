@@ -5,6 +5,7 @@
 #pragma once
 
 #include "nosa_internal.h"
+#include "nosa_lanes.h"
 
 namespace nosa {
 namespace {
@@ -138,8 +139,7 @@ __device__ __forceinline__ void score_compute(const Dims &d, int C, ScoreIn &in,
     x[m] = c < C ? acc[m >> 2][m & 3] * scale : -INFINITY;
     mx = fmaxf(mx, x[m]);
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = xor32_max(xor16_max(mx));
   if (lg == 0) red_m[w][h] = mx;
   __syncthreads();
   // the split's first chunk is below C, so M is finite and exp2 of a
@@ -152,8 +152,7 @@ __device__ __forceinline__ void score_compute(const Dims &d, int C, ScoreIn &in,
     ev[m] = __builtin_amdgcn_exp2f(x[m] - M);
     z += ev[m];
   }
-  z += __shfl_xor(z, 16, 64);
-  z += __shfl_xor(z, 32, 64);
+  z = xor32_sum(xor16_sum(z));
   if (lg == 0) red_z[w][h] = z;
   const int Gp = padded_group(d.G);
   if (h < Gp) {                                    // chunk-major [c][Gp], pad = 0
@@ -643,8 +642,7 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
     }
     if (real)
       for (int s = sh_j + kPre; s < used; s += 16) m = fmaxf(m, load2_coherent(sr, 8 * (s * d.G + sh_h)).x);
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    m = row16_max(m);
     const float ln = (real && last_q) ? lnew_sh[sh_h] : -INFINITY;
     m = fmaxf(m, ln);
     float es[kStatBatches];
@@ -659,8 +657,7 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
         const float2 v = load2_coherent(sr, 8 * (s * d.G + sh_h));
         if (v.y > 0.0f) z += v.y * expf(v.x - m);
       }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
+    z = row16_sum(z);
     const float el = ln == -INFINITY ? 0.0f : expf(ln - m);
     z += el;
     const float rz = real ? 1.0f / z : 0.0f;
