@@ -55,7 +55,7 @@ __device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
 struct Half {
   uint4 k[2][4];   // K rows of the two QK tiles, 4 k-steps each
   uint4 v[8];      // the half's 8 V tiles: 8 keys of one dim per lane
-  float s;         // eviction score of key (lane % 32) of the half
+  float4 s[2];     // eviction scores of this lane's 8 keys: 8 (lane / 16) .. + 7
   int key_base;    // token index of the half's first key (wave-uniform)
   int ok;          // 0: past the wave's list or an invalid entry (uniform)
 };
@@ -64,7 +64,7 @@ struct DecodeArgs {
   const int32_t *sel, *phys;
   __amdgpu_buffer_rsrc_t kv;   // this pair's blocks
   __amdgpu_buffer_rsrc_t ts;   // this pair's eviction scores
-  int koff[2], voff, soff;     // per-lane byte offsets inside a block / half
+  int koff[2], voff, soff;     // per-lane byte offsets inside a block / half / scores
   int p, slots, e_first, e_end;
 };
 
@@ -94,8 +94,10 @@ __device__ inline void load_half(Half &hb, int j, const DecodeArgs &a, const Dim
     for (int s = 0; s < 4; ++s) hb.k[t][s] = bload16(a.kv, a.koff[t] + 64 * s, kbase);
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) hb.v[dt] = bload16(a.kv, a.voff + 1024 * dt, vbase);
-  hb.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(a.ts, a.soff,
-                                                                        hb.key_base * 4, 0));
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    hb.s[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             a.ts, a.soff + 16 * i, hb.key_base * 4, 0));
 }
 
 // Online-softmax update with one half: logits on MFMA, then O^T += V^T P^T.
@@ -115,7 +117,7 @@ __device__ inline void process_half(Half &hb, const bf16x8 (&qop)[4], float qsca
   float mx = -INFINITY;
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-    const float sv = __shfl(hb.s, 8 * lg + m, 64);
+    const float sv = hb.s[m >> 2][m & 3];
     const float lg2 = acc[m >> 2][m & 3] * qscale + sv * bscale;
     x[m] = (key0 + m) < L ? lg2 : -INFINITY;
     mx = fmaxf(mx, x[m]);
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   a.koff[0] = tile_row(h, 0) * kHeadDim * 2 + 16 * lg;
   a.koff[1] = tile_row(h, 1) * kHeadDim * 2 + 16 * lg;
   a.voff = 16 * l;   // V tile: lane l holds dim l % 16, tokens 8 (l / 16) .. + 7
-  a.soff = 4 * (l & 31);
+  a.soff = 32 * (l >> 4);   // lane group lg reads the scores of keys 8 lg .. 8 lg + 7
   a.p = p;
   a.slots = slots_per_pair;
   a.e_first = split * bps + w;
