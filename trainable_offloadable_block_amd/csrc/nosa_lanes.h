@@ -37,6 +37,16 @@ __device__ inline float dpp_f32(float v) {
   return pl_bits(static_cast<unsigned>(
       __builtin_amdgcn_mov_dpp(static_cast<int>(pl_u(v)), CTRL, 0xF, 0xF, true)));
 }
+// v of lane l + K (K > 0) or l - |K| (K < 0) in the same row of 16 lanes;
+// a lane whose source falls outside its row keeps its own v (as __shfl_down
+// / __shfl_up with width 16)
+template <int K>
+__device__ inline float row_shift(float v) {
+  constexpr int ctrl = K > 0 ? 0x100 + K : 0x110 - K;   // row_shl:K / row_shr:-K
+  return pl_bits(static_cast<unsigned>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(pl_u(v)), static_cast<int>(pl_u(v)), ctrl, 0xF, 0xF, false)));
+}
+
 // max / sum over each row of 16 lanes, left in every lane of the row
 __device__ inline float row16_max(float v) {
   v = fmaxf(v, dpp_f32<0xB1>(v));     // quad_perm [1,0,3,2]

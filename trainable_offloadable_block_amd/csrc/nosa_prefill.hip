@@ -17,6 +17,7 @@
 // their sum over the group's rows and a max over each block's chunks (the
 // chunk before a tile is carried over).
 #include "nosa_internal.h"
+#include "nosa_lanes.h"
 
 namespace nosa {
 namespace {
@@ -165,11 +166,9 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float mm = m[rt][i];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mm = fmaxf(mm, __shfl_xor(mm, o, 64));
+      mm = row16_max(mm);
       float zz = z[rt][i] * __builtin_amdgcn_exp2f(m[rt][i] - mm);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) zz += __shfl_xor(zz, o, 64);
+      zz = row16_sum(zz);
       m[rt][i] = mm;
       // now 1 / Z; 0 for padding heads and absent queries, whose rows the
       // unmasked tiles below still compute
@@ -204,14 +203,14 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(4
           if (in) s = fmaf(e, z[rt][i], s);
         }
         // the query's other lane groups (Gp = 8: two per query; 16: four)
-        if (Gp >= 8) s += __shfl_xor(s, 16, 64);
-        if (Gp >= 16) s += __shfl_xor(s, 32, 64);
+        if (Gp >= 8) s = xor16_sum(s);
+        if (Gp >= 16) s = xor32_sum(s);
         // lane group lg holds a_c (chunk c) of query row_q(rt)
-        const float prev = __shfl_up(s, 1, 16);          // chunk c - 1 (lane 0: its own)
+        const float prev = row_shift<-1>(s);             // chunk c - 1 (lane 0: its own)
         const float up = lr == 0 ? carry[rt] : prev;
-        float y = fmaxf(s, __shfl_down(s, 1, 16));
-        y = fmaxf(y, __shfl_down(s, 2, 16));
-        y = fmaxf(y, __shfl_down(s, 3, 16));
+        float y = fmaxf(s, row_shift<1>(s));
+        y = fmaxf(y, row_shift<2>(s));
+        y = fmaxf(y, row_shift<3>(s));
         y = fmaxf(y, up);                                // lane 4j: block 4 ct + j
         carry[rt] = __shfl(s, 15, 16);
         const int qi = row_q(rt);
