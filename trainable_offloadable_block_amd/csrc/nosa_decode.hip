@@ -10,7 +10,9 @@
 //   fused, and O^T += V^T P^T on MFMA with P split into bf16 hi + lo parts
 //   (P alone in bf16 would cost ~1e-3 relative error). The 4 waves merge in
 //   LDS into one partial (m, l, o) per split; the last workgroup of a pair to
-//   finish merges all splits and writes the normalised output.
+//   finish merges all splits and writes the normalised output (a pair with a
+//   single split writes it straight from the LDS merge). A pair's workgroups
+//   are placed on one XCD (grid_unit).
 #include <hip/hip_ext.h>
 
 #include "nosa_internal.h"
