@@ -135,6 +135,17 @@ def locality_step(prev, cur, seq_len, wl):
     return g
 
 
+def select_bytes(wl, L):
+    """Algorithmic bytes of one selection at sequence length L (every
+    sequence): each complete chunk's compressed key (bf16), an fp32 score and
+    an eviction score per block, the eligibility bits, the group's queries
+    (bf16) and the selection list (int32)."""
+    B, Hq, Hkv, k = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.k_blocks
+    C = (L - 32) // 16 + 1 if L >= 32 else 0
+    nb = (L + 63) // 64
+    return B * Hkv * (C * 128 * 2 + 2 * nb * 4 + nb / 4) + B * Hq * 128 * 2 + B * Hkv * k * 4
+
+
 def decode_bytes(wl, n_att_per_pair):
     """Algorithmic bytes of one sparse-decode launch: K, V (bf16) and the
     eviction score (fp32) of every attended token, q (bf16) and out (fp32),
@@ -869,6 +880,17 @@ def main():
         "breakdown_us": bd,
         "locality": m["locality"],
     }
+    # the selection against the same roofline: its algorithmic bytes over the
+    # fused append + select call's time (events around the call, so an upper
+    # bound on the selection's own time; the pool after the scoring splits is
+    # latency-bound)
+    L_mid = wl.context + W + K
+    sb = select_bytes(wl, L_mid)
+    res["select_roofline"] = {
+        "kernel": "nosa_append_select", "bound": "hbm", "bytes_per_launch": int(sb),
+        "call_us_events_around": bd["append_select"],
+        "achieved": round(sb / (bd["append_select"] * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+        "unit": "GB/s", "frac": round(sb / (bd["append_select"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     if "graph" in m:
         res["graph_replay"] = m["graph"]
     pf = [ms for name, ms in PREFILL_MS if name == wl.name]
