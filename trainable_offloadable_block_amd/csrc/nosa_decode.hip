@@ -224,6 +224,81 @@ __device__ void merge_splits(const Dims &d, int p, int b, int g, int n_splits,
   }
 }
 
+// merge_splits for a group of 8 or 16 heads (NV = G / 8): thread t owns
+// the NV float4s of outputs 4 (t + 256 j) .. + 3 (one head each), read with
+// unconditional 16-byte device-coherent buffer loads (a split past n_splits
+// reads zeros), SB = 4 / NV splits per batch.
+constexpr int kAgentCoherent = 16;   // buffer cache policy: sc1 (device scope)
+
+template <int NV>
+__device__ void merge_splits_v(const Dims &d, int p, int b, int g, int n_splits,
+                               const float *mlf, const float *ws_o, float *sm, float *out) {
+  constexpr int SB = 4 / NV;
+  const int t = threadIdx.x;
+  const int n_out = d.G * kHeadDim;                   // 1024 NV
+  const float *mlp = mlf + (size_t)2 * p * n_splits * d.G;
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc(ws_o + (size_t)p * n_splits * n_out, (uint32_t)(n_splits * n_out * 4));
+  float *sm_w = sm;                                   // [kMaxSplits][16]: m, then weights
+  float *sm_lv = sm_w + kMaxSplits * 16;              // [kMaxSplits][16]: l
+  float *sm_lh = sm_lv + kMaxSplits * 16;             // [16]: merged l
+  float4 v[SB][NV];
+  auto issue = [&](int sp0) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+        v[u][j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 ro, ((sp0 + u) * n_out + 4 * (t + kDecThreads * j)) * 4,
+                                                 0, kAgentCoherent));
+  };
+  issue(0);
+  for (int i = t; i < n_splits * d.G; i += kDecThreads) {
+    sm_w[i] = load_agent(&mlp[2 * i]);
+    sm_lv[i] = load_agent(&mlp[2 * i + 1]);
+  }
+  __syncthreads();
+  if (t < d.G) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, sm_w[sp * d.G + t]);
+    float lsum = 0.0f;
+    for (int sp = 0; sp < n_splits; ++sp) {
+      const float f = M == -INFINITY ? 0.0f : exp2f(sm_w[sp * d.G + t] - M);
+      sm_w[sp * d.G + t] = f;
+      lsum += f * sm_lv[sp * d.G + t];
+    }
+    sm_lh[t] = lsum;
+  }
+  __syncthreads();
+  float4 acc[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp0 = 0; sp0 < n_splits; sp0 += SB) {
+    if (sp0 > 0) issue(sp0);
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+      if (sp0 + u < n_splits) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const float wgt = sm_w[(sp0 + u) * d.G + 4 * (t + kDecThreads * j) / kHeadDim];
+          acc[j].x += wgt * v[u][j].x;
+          acc[j].y += wgt * v[u][j].y;
+          acc[j].z += wgt * v[u][j].z;
+          acc[j].w += wgt * v[u][j].w;
+        }
+      }
+  }
+  float *ob = out + ((size_t)b * d.Hq + g * d.G) * kHeadDim;   // the group's heads, contiguous
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int idx = 4 * (t + kDecThreads * j);
+    const float lsum = sm_lh[idx / kHeadDim];
+    *reinterpret_cast<float4 *>(ob + idx) =
+        lsum > 0.0f ? make_float4(acc[j].x / lsum, acc[j].y / lsum, acc[j].z / lsum, acc[j].w / lsum)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
 __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_kernel(
     Dims d, const int32_t *__restrict__ seq_len, const uint16_t *__restrict__ q,
     const int32_t *__restrict__ sel, const int32_t *__restrict__ phys,
@@ -373,7 +448,11 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
               n_splits - 1;
   __syncthreads();
   if (!sm_last) return;
-  if (d.G <= 8)
+  if (d.G == 8)
+    merge_splits_v<1>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
+  else if (d.G == 16)
+    merge_splits_v<2>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
+  else if (d.G <= 8)
     merge_splits<4>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
   else
     merge_splits<8>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
