@@ -38,6 +38,7 @@ __device__ inline uint4 ldg16(const uint16_t *p) {
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Raw buffer descriptor over [base, base + bytes): loads past the end read 0.
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   asm volatile("" ::"v"(lane_blk), "v"(lane_slot));
 
   __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ float sm_o[4][16][kHeadDim + 4];
+  __shared__ __align__(16) float sm_o[4][16][kHeadDim + 4];
   __shared__ int sm_last;
 
   DecodeArgs a;
@@ -421,6 +422,35 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   // device-scope fence: that would write back the XCD's whole L2.
   const size_t part = (size_t)p * n_splits + split;
   float *mlf = reinterpret_cast<float *>(ws_ml);
+  if (d.G == 8 || d.G == 16) {                 // uniform: 16-byte stores, one head each
+    const int n_out = d.G * kHeadDim;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(ws_o + part * n_out, (uint32_t)n_out * 4);
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(mlf + 2 * part * d.G, (uint32_t)d.G * 8);
+    for (int j = 0; j < d.G / 8; ++j) {
+      const int idx = 4 * (threadIdx.x + kDecThreads * j);
+      const int hh = idx / kHeadDim, dim = idx % kHeadDim;
+      const float M = fmaxf(fmaxf(sm_m[0][hh], sm_m[1][hh]), fmaxf(sm_m[2][hh], sm_m[3][hh]));
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      float lsum = 0.0f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const float f = exp2f(sm_m[ww][hh] - M);
+          const float4 ov = *reinterpret_cast<const float4 *>(&sm_o[ww][hh][dim]);
+          acc.x += f * ov.x;
+          acc.y += f * ov.y;
+          acc.z += f * ov.z;
+          acc.w += f * ov.w;
+          lsum += f * sm_l[ww][hh];
+        }
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ro, idx * 4, 0,
+                                             kAgentCoherent);
+      if (dim == 0)
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(u32x2, make_float2(M, lsum)), rm, hh * 8, 0, kAgentCoherent);
+    }
+  } else {
   for (int idx = threadIdx.x; idx < d.G * kHeadDim; idx += kDecThreads) {
     const int hh = idx / kHeadDim, dim = idx % kHeadDim;
     const float M = fmaxf(fmaxf(sm_m[0][hh], sm_m[1][hh]), fmaxf(sm_m[2][hh], sm_m[3][hh]));
@@ -440,6 +470,7 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
       __hip_atomic_store(&mlf[2 * (part * d.G + hh) + 1], lsum, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
   }
   __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
   __syncthreads();
