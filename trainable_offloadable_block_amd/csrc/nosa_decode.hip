@@ -225,10 +225,11 @@ __device__ void merge_splits(const Dims &d, int p, int b, int g, int n_splits,
   }
 }
 
-// merge_splits for a group of 8 or 16 heads (NV = G / 8): thread t owns
-// the NV float4s of outputs 4 (t + 256 j) .. + 3 (one head each), read with
-// unconditional 16-byte device-coherent buffer loads (a split past n_splits
-// reads zeros), SB = 4 / NV splits per batch.
+// merge_splits for a group of 4, 8 or 16 heads (NV = max(1, G / 8)): thread
+// t owns the float4s of outputs 4 (t + 256 j) .. + 3 below G * 128 (one head
+// each; at G = 4 the last two waves own none), read with unconditional
+// 16-byte device-coherent buffer loads (a split past n_splits reads zeros),
+// SB = 4 / NV splits per batch.
 constexpr int kAgentCoherent = 16;   // buffer cache policy: sc1 (device scope)
 
 template <int NV>
@@ -236,7 +237,7 @@ __device__ void merge_splits_v(const Dims &d, int p, int b, int g, int n_splits,
                                const float *mlf, const float *ws_o, float *sm, float *out) {
   constexpr int SB = 4 / NV;
   const int t = threadIdx.x;
-  const int n_out = d.G * kHeadDim;                   // 1024 NV
+  const int n_out = d.G * kHeadDim;                   // 512, 1024 or 2048
   const float *mlp = mlf + (size_t)2 * p * n_splits * d.G;
   const __amdgpu_buffer_rsrc_t ro =
       make_rsrc(ws_o + (size_t)p * n_splits * n_out, (uint32_t)(n_splits * n_out * 4));
@@ -281,6 +282,7 @@ __device__ void merge_splits_v(const Dims &d, int p, int b, int g, int n_splits,
       if (sp0 + u < n_splits) {
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
+          if (4 * (t + kDecThreads * j) >= n_out) break;   // wave-uniform (G = 4)
           const float wgt = sm_w[(sp0 + u) * d.G + 4 * (t + kDecThreads * j) / kHeadDim];
           acc[j].x += wgt * v[u][j].x;
           acc[j].y += wgt * v[u][j].y;
@@ -293,6 +295,7 @@ __device__ void merge_splits_v(const Dims &d, int p, int b, int g, int n_splits,
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int idx = 4 * (t + kDecThreads * j);
+    if (idx >= n_out) break;                          // wave-uniform (G = 4)
     const float lsum = sm_lh[idx / kHeadDim];
     *reinterpret_cast<float4 *>(ob + idx) =
         lsum > 0.0f ? make_float4(acc[j].x / lsum, acc[j].y / lsum, acc[j].z / lsum, acc[j].w / lsum)
@@ -399,6 +402,33 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
 #pragma unroll
     for (int i = 0; i < 4; ++i) sm_o[w][h][16 * dt + 4 * lg + i] = o[dt][i];
   __syncthreads();
+  if (n_splits == 1 && (d.G == 4 || d.G == 8 || d.G == 16)) {   // uniform
+    // the pair's only split: normalise and write, a float4 (one head) each
+    float *ob = out + ((size_t)b * d.Hq + g * d.G) * kHeadDim;
+    for (int j = 0; 4 * (threadIdx.x + kDecThreads * j) < d.G * kHeadDim; ++j) {
+      const int idx = 4 * (threadIdx.x + kDecThreads * j);
+      const int hh = idx / kHeadDim, dim = idx % kHeadDim;
+      const float M = fmaxf(fmaxf(sm_m[0][hh], sm_m[1][hh]), fmaxf(sm_m[2][hh], sm_m[3][hh]));
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      float lsum = 0.0f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const float f = exp2f(sm_m[ww][hh] - M);
+          const float4 ov = *reinterpret_cast<const float4 *>(&sm_o[ww][hh][dim]);
+          acc.x += f * ov.x;
+          acc.y += f * ov.y;
+          acc.z += f * ov.z;
+          acc.w += f * ov.w;
+          lsum += f * sm_l[ww][hh];
+        }
+      }
+      *reinterpret_cast<float4 *>(ob + idx) =
+          lsum > 0.0f ? make_float4(acc.x / lsum, acc.y / lsum, acc.z / lsum, acc.w / lsum)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
   if (n_splits == 1) {                         // uniform: the pair's only split
     for (int idx = threadIdx.x; idx < d.G * kHeadDim; idx += kDecThreads) {
       const int hh = idx / kHeadDim, dim = idx % kHeadDim;
@@ -422,11 +452,11 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   // device-scope fence: that would write back the XCD's whole L2.
   const size_t part = (size_t)p * n_splits + split;
   float *mlf = reinterpret_cast<float *>(ws_ml);
-  if (d.G == 8 || d.G == 16) {                 // uniform: 16-byte stores, one head each
+  if (d.G == 4 || d.G == 8 || d.G == 16) {     // uniform: 16-byte stores, one head each
     const int n_out = d.G * kHeadDim;
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(ws_o + part * n_out, (uint32_t)n_out * 4);
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(mlf + 2 * part * d.G, (uint32_t)d.G * 8);
-    for (int j = 0; j < d.G / 8; ++j) {
+    for (int j = 0; 4 * (threadIdx.x + kDecThreads * j) < n_out; ++j) {   // wave-uniform
       const int idx = 4 * (threadIdx.x + kDecThreads * j);
       const int hh = idx / kHeadDim, dim = idx % kHeadDim;
       const float M = fmaxf(fmaxf(sm_m[0][hh], sm_m[1][hh]), fmaxf(sm_m[2][hh], sm_m[3][hh]));
@@ -479,7 +509,7 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
               n_splits - 1;
   __syncthreads();
   if (!sm_last) return;
-  if (d.G == 8)
+  if (d.G == 4 || d.G == 8)
     merge_splits_v<1>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
   else if (d.G == 16)
     merge_splits_v<2>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
