@@ -19,6 +19,8 @@
 //    re-selected by the agnostic stage).
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "nosa_select_dev.h"
 
 namespace nosa {
@@ -74,8 +76,11 @@ SelectLayout select_layout(const Dims &d, int max_len) {
 }
 
 size_t select_dyn_lds(const Dims &d, const SelectLayout &lay) {
-  return ((size_t)lay.n_splits * padded_group(d.G) + lay.c_pad) * sizeof(float) +
-         (size_t)d.elig_words * sizeof(uint32_t) + (size_t)d.NB_max;
+  // the pool's arrays, or the scoring waves' transpose space if larger (a
+  // workgroup pools only after its scoring is done)
+  return std::max(((size_t)lay.n_splits * padded_group(d.G) + lay.c_pad) * sizeof(float) +
+                      (size_t)d.elig_words * sizeof(uint32_t) + (size_t)d.NB_max,
+                  kScoreTrBytes);
 }
 
 hipError_t launch_select(const Dims &d, const nosa_state &st, const uint16_t *q,

@@ -38,6 +38,11 @@ __device__ inline float get(const float *a) {
   return __hip_atomic_load(const_cast<float *>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 constexpr int kCoherent = 16;   // buffer-load cache policy: sc1, as the agent-scope loads
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+// LDS (dynamic region) per scoring wave for the transposed chunk weights:
+// 32 chunks x 16 heads
+constexpr int kScoreTrFloats = 32 * 16;
+constexpr size_t kScoreTrBytes = 4 * kScoreTrFloats * sizeof(float);   // 4 waves
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                            0x00020000);
@@ -155,11 +160,26 @@ __device__ __forceinline__ void score_compute(const Dims &d, int C, ScoreIn &in,
   z = xor32_sum(xor16_sum(z));
   if (lg == 0) red_z[w][h] = z;
   const int Gp = padded_group(d.G);
-  if (h < Gp) {                                    // chunk-major [c][Gp], pad = 0
-    float *dst = ws_e + ((size_t)p * c_pad + cg + 8 * lg) * Gp + h;
+  {
+    // the wave's 32 chunks x Gp heads (chunk-major [c][Gp], pad = 0) are one
+    // contiguous run of ws_e: transposed through this wave's part of the
+    // dynamic LDS, then written as 16-byte device-coherent stores
+    extern __shared__ __align__(16) uint8_t score_tr[];
+    float *tr = reinterpret_cast<float *>(score_tr) + w * kScoreTrFloats;
+    if (h < Gp) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-      if (cg + 8 * lg + m < C) put(&dst[m * Gp], h < d.G ? ev[m] : 0.0f);
+      for (int m = 0; m < 8; ++m) tr[(8 * lg + m) * Gp + h] = h < d.G ? ev[m] : 0.0f;
+    }
+    asm volatile("" ::: "memory");                // the wave's writes, then its reads (in order)
+    const __amdgpu_buffer_rsrc_t er =
+        make_rsrc(ws_e + (size_t)p * c_pad * Gp, (uint32_t)(c_pad * Gp * 4));
+    const int n4 = 8 * Gp;                        // float4s of the wave's run
+    for (int i = l; i < n4; i += 64) {            // uniform trip count per wave
+      if (cg + (4 * i) / Gp < C)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4v, *reinterpret_cast<const float4 *>(tr + 4 * i)), er,
+            (cg * Gp + 4 * i) * 4, 0, kCoherent);
+    }
   }
   __syncthreads();
   if (threadIdx.x < d.G) {
