@@ -39,12 +39,26 @@ __device__ __forceinline__ void forecast_score(int C, const ScoreIn &in, float *
     for (int s = 0; s < 4; ++s)
       acc[t] = mfma16x16x32(as_bf16x8(in.kv[t][s]), as_bf16x8(in.qv[s]), acc[t]);
   }
-  // lane (0, lg) holds the forecast head against chunks cg + 8*lg + m
+  // lane (0, lg) holds the forecast head against chunks cg + 8*lg + m: two
+  // runs of 4 contiguous logits, each one 16-byte device-coherent store when
+  // all 4 chunks exist (a run crossing C is written element by element)
   if (h == 0) {
-    float *dst = ws_l + (size_t)p * c_pad + cg + 8 * lg;
+    const __amdgpu_buffer_rsrc_t lr = make_rsrc(ws_l + (size_t)p * c_pad, (uint32_t)c_pad * 4);
+    const float sc = 0.08838834764831845f;   // 1 / sqrt(128)
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-      if (cg + 8 * lg + m < C) put(&dst[m], acc[m >> 2][m & 3] * 0.08838834764831845f);
+    for (int t = 0; t < 2; ++t) {
+      const int c = cg + 8 * lg + 4 * t;
+      if (c + 4 <= C) {
+        const float4 v = make_float4(acc[t][0] * sc, acc[t][1] * sc, acc[t][2] * sc, acc[t][3] * sc);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, v), lr, 4 * c, 0,
+                                               kCoherent);
+      } else {
+        float *dst = ws_l + (size_t)p * c_pad + c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (c + i < C) put(&dst[i], acc[t][i] * sc);
+      }
+    }
   }
 }
 
