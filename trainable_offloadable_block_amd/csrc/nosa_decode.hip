@@ -241,9 +241,6 @@ __device__ void merge_splits_v(const Dims &d, int p, int b, int g, int n_splits,
   const float *mlp = mlf + (size_t)2 * p * n_splits * d.G;
   const __amdgpu_buffer_rsrc_t ro =
       make_rsrc(ws_o + (size_t)p * n_splits * n_out, (uint32_t)(n_splits * n_out * 4));
-  float *sm_w = sm;                                   // [kMaxSplits][16]: m, then weights
-  float *sm_lv = sm_w + kMaxSplits * 16;              // [kMaxSplits][16]: l
-  float *sm_lh = sm_lv + kMaxSplits * 16;             // [16]: merged l
   float4 v[SB][NV];
   auto issue = [&](int sp0) {
 #pragma unroll
@@ -255,23 +252,26 @@ __device__ void merge_splits_v(const Dims &d, int p, int b, int g, int n_splits,
                                                  0, kAgentCoherent));
   };
   issue(0);
-  for (int i = t; i < n_splits * d.G; i += kDecThreads) {
-    sm_w[i] = load_agent(&mlp[2 * i]);
-    sm_lv[i] = load_agent(&mlp[2 * i + 1]);
-  }
-  __syncthreads();
-  if (t < d.G) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, sm_w[sp * d.G + t]);
-    float lsum = 0.0f;
-    for (int sp = 0; sp < n_splits; ++sp) {
-      const float f = M == -INFINITY ? 0.0f : exp2f(sm_w[sp * d.G + t] - M);
-      sm_w[sp * d.G + t] = f;
-      lsum += f * sm_lv[sp * d.G + t];
+  // split statistics without LDS or barriers: for its j-th float4 a lane's
+  // head is 2 w + 8 j (lanes 0..31) or 2 w + 8 j + 1 (lanes 32..63); lane
+  // (32 half + sp) loads that head's (m, l) of split sp, the two halves
+  // reduce separately, and each lane reads its half's weights back by lane
+  const int lane = t & 63, half = lane >> 5, spl = lane & 31;
+  const int w = t >> 6;
+  float fw[NV], lsum[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int hh = 2 * w + 8 * j + half;
+    float m = -INFINITY, lv = 0.0f;
+    if (spl < n_splits && hh < d.G) {
+      m = load_agent(&mlp[2 * (spl * d.G + hh)]);
+      lv = load_agent(&mlp[2 * (spl * d.G + hh) + 1]);
     }
-    sm_lh[t] = lsum;
+    const float M = xor16_max(row16_max(m));         // over the lane's half
+    const float f = (m == -INFINITY) ? 0.0f : exp2f(m - M);
+    fw[j] = f;
+    lsum[j] = xor16_sum(row16_sum(f * lv));
   }
-  __syncthreads();
   float4 acc[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -279,11 +279,14 @@ __device__ void merge_splits_v(const Dims &d, int p, int b, int g, int n_splits,
     if (sp0 > 0) issue(sp0);
 #pragma unroll
     for (int u = 0; u < SB; ++u)
-      if (sp0 + u < n_splits) {
+      if (sp0 + u < n_splits) {                       // uniform
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-          if (4 * (t + kDecThreads * j) >= n_out) break;   // wave-uniform (G = 4)
-          const float wgt = sm_w[(sp0 + u) * d.G + 4 * (t + kDecThreads * j) / kHeadDim];
+          const float wa = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fw[j]), sp0 + u));
+          const float wb = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fw[j]), 32 + sp0 + u));
+          const float wgt = half ? wb : wa;
           acc[j].x += wgt * v[u][j].x;
           acc[j].y += wgt * v[u][j].y;
           acc[j].z += wgt * v[u][j].z;
@@ -296,10 +299,10 @@ __device__ void merge_splits_v(const Dims &d, int p, int b, int g, int n_splits,
   for (int j = 0; j < NV; ++j) {
     const int idx = 4 * (t + kDecThreads * j);
     if (idx >= n_out) break;                          // wave-uniform (G = 4)
-    const float lsum = sm_lh[idx / kHeadDim];
+    const float ls = lsum[j];
     *reinterpret_cast<float4 *>(ob + idx) =
-        lsum > 0.0f ? make_float4(acc[j].x / lsum, acc[j].y / lsum, acc[j].z / lsum, acc[j].w / lsum)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
+        ls > 0.0f ? make_float4(acc[j].x / ls, acc[j].y / ls, acc[j].z / ls, acc[j].w / ls)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 
