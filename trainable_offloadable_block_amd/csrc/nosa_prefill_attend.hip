@@ -6,7 +6,10 @@
 // prefill_select_kernel: grid (queries, pairs), one workgroup per query:
 //   stage 1 takes the k_q candidates of highest block score (from
 //   nosa_prefill_block_scores), stage 2 the k_e' others of highest agnostic
-//   score; the ascending list of sink, window and selected blocks.
+//   score; the ascending list of sink, window and selected blocks. A prompt
+//   of at most 512 candidate blocks per query runs one wave per workgroup
+//   (up to 8 keys a lane): the work per query is a short chain of dependent
+//   reductions, so more resident workgroups per CU beat wider ones.
 // prefill_attend_kernel: grid (query groups, pairs), 8 waves; a wave takes
 //   16 / Gp consecutive queries (16 MFMA columns of (query, head)); the
 //   workgroup forms the union of its queries' selections in LDS and stages
@@ -24,7 +27,7 @@ namespace {
 __host__ __device__ inline int pa_rows(int G) { return G <= 4 ? 4 : (G <= 8 ? 8 : 16); }
 
 // ---------------------------------------------------------------- select
-template <int R>
+template <int R, int NT>
 __device__ __forceinline__ void pf_stages(const Dims &d, const float *__restrict__ sc,
                                           const float *__restrict__ be, int n_cand,
                                           uint8_t *kind, TopkLds &tk) {
@@ -33,68 +36,69 @@ __device__ __forceinline__ void pf_stages(const Dims &d, const float *__restrict
     uint64_t kq[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int i = t + kTopkThreads * r, bb = d.n_sink + i;
+      const int i = t + NT * r, bb = d.n_sink + i;
       kq[r] = i < n_cand ? compose_key(sc[bb], bb) : 0;
     }
-    wg_topk(kq, d.k_q, d.n_sink, kind, NOSA_KIND_QUERY, tk);
+    wg_topk<R, NT>(kq, d.k_q, d.n_sink, kind, NOSA_KIND_QUERY, tk);
     __syncthreads();
   }
   if (d.k_e_dyn > 0) {
     uint64_t ke[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int i = t + kTopkThreads * r, bb = d.n_sink + i;
+      const int i = t + NT * r, bb = d.n_sink + i;
       ke[r] = (i < n_cand && kind[bb] != NOSA_KIND_QUERY) ? compose_key(be[bb], bb) : 0;
     }
-    wg_topk(ke, d.k_e_dyn, d.n_sink, kind, NOSA_KIND_AGNOSTIC, tk);
+    wg_topk<R, NT>(ke, d.k_e_dyn, d.n_sink, kind, NOSA_KIND_AGNOSTIC, tk);
   }
 }
 
-__global__ __launch_bounds__(kTopkThreads) void prefill_select_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT) void prefill_select_kernel(
     Dims d, nosa_state st, const float *__restrict__ scores, int T, int pos0, int nb_out,
     int32_t *__restrict__ sel, int32_t *__restrict__ n_sel) {
   extern __shared__ __align__(16) uint8_t kind[];          // [NB_max]
   __shared__ TopkLds tk;
-  __shared__ int cnt_sh[2][kTopkThreads / 64];
+  __shared__ int cnt_sh[2][NT / 64];
   const int qi = blockIdx.x, p = blockIdx.y, t = threadIdx.x;
   const int w = t >> 6, lane = t & 63;
   const int L = pos0 + qi + 1;
   const int nb = blocks_for(L);
   const int win_lo = max(d.n_sink, nb - d.n_win);
   const int n_cand = max(0, win_lo - d.n_sink);
-  for (int bb = t; bb < nb; bb += kTopkThreads)
+  for (int bb = t; bb < nb; bb += NT)
     kind[bb] = bb < d.n_sink ? NOSA_KIND_SINK : (bb >= win_lo ? NOSA_KIND_WINDOW : NOSA_KIND_NONE);
 #pragma unroll
-  for (int i = 0; i < kTopkBins / kTopkThreads; ++i) {
-    tk.hist[0][t + kTopkThreads * i] = 0;
-    tk.hist[1][t + kTopkThreads * i] = 0;
+  for (int i = 0; i < kTopkBins / NT; ++i) {
+    tk.hist[0][t + NT * i] = 0;
+    tk.hist[1][t + NT * i] = 0;
   }
   __syncthreads();
   if (n_cand > 0) {                                         // uniform
     const float *sc = scores + ((size_t)p * T + qi) * nb_out;
     const float *be = st.blk_e + (size_t)p * d.NB_max;
-    const int m = (n_cand + kTopkThreads - 1) / kTopkThreads;
-    if (m <= 1) pf_stages<1>(d, sc, be, n_cand, kind, tk);
-    else if (m <= 2) pf_stages<2>(d, sc, be, n_cand, kind, tk);
-    else if (m <= 4) pf_stages<4>(d, sc, be, n_cand, kind, tk);
-    else if (m <= 8) pf_stages<8>(d, sc, be, n_cand, kind, tk);
-    else pf_stages<kMaxCandPerThread>(d, sc, be, n_cand, kind, tk);
+    const int m = (n_cand + NT - 1) / NT;
+    if (m <= 1) pf_stages<1, NT>(d, sc, be, n_cand, kind, tk);
+    else if (m <= 2) pf_stages<2, NT>(d, sc, be, n_cand, kind, tk);
+    else if (m <= 4) pf_stages<4, NT>(d, sc, be, n_cand, kind, tk);
+    else if (m <= 8 || NT == 64) pf_stages<8, NT>(d, sc, be, n_cand, kind, tk);   // NT 64: n_cand <= 512
+    else pf_stages<kMaxCandPerThread, NT>(d, sc, be, n_cand, kind, tk);
   }
   __syncthreads();
-  // ascending list: ballot + prefix count per 256 blocks
+  // ascending list: ballot + prefix count per NT blocks
   int32_t *sp = sel + ((size_t)p * T + qi) * d.k;
   int running = 0;
-  for (int base = 0; base < nb; base += kTopkThreads) {      // uniform
+  for (int base = 0; base < nb; base += NT) {      // uniform
     const int bb = base + t;
     const bool in = bb < nb && kind[bb] != NOSA_KIND_NONE;
     const uint64_t mask = __ballot(in);
     const int below = __popcll(mask & ((1ull << lane) - 1ull));
-    if (lane == 0) cnt_sh[(base / kTopkThreads) & 1][w] = __popcll(mask);
+    if (lane == 0) cnt_sh[(base / NT) & 1][w] = __popcll(mask);
     __syncthreads();
-    const int *cs = cnt_sh[(base / kTopkThreads) & 1];
+    const int *cs = cnt_sh[(base / NT) & 1];
     int off = running, tot = 0;
 #pragma unroll
-    for (int ww = 0; ww < kTopkThreads / 64; ++ww) {
+    for (int ww = 0; ww < NT / 64; ++ww) {
       if (ww < w) off += cs[ww];
       tot += cs[ww];
     }
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(kTopkThreads) void prefill_select_kernel(
     if (in && off < d.k) sp[off] = bb;
     running += tot;
   }
-  for (int j = running + t; j < d.k; j += kTopkThreads) sp[j] = -1;
+  for (int j = running + t; j < d.k; j += NT) sp[j] = -1;
   if (t == 0) n_sel[(size_t)p * T + qi] = min(running, d.k);
 }
 
@@ -308,8 +312,13 @@ __global__ __launch_bounds__(kPaWaves * 64) __attribute__((amdgpu_waves_per_eu(4
 
 hipError_t launch_prefill_select(const Dims &d, const nosa_state &st, const float *scores, int T,
                                  int pos0, int32_t *sel, int32_t *n_sel, hipStream_t s) {
-  prefill_select_kernel<<<dim3(T, d.P), kTopkThreads, (size_t)d.NB_max, s>>>(
-      d, st, scores, T, pos0, blocks_for(pos0 + T), sel, n_sel);
+  const int nb_out = blocks_for(pos0 + T);
+  if (nb_out - d.n_sink <= 8 * 64)          // at most 8 candidates per lane of one wave
+    prefill_select_kernel<64><<<dim3(T, d.P), 64, (size_t)d.NB_max, s>>>(
+        d, st, scores, T, pos0, nb_out, sel, n_sel);
+  else
+    prefill_select_kernel<kTopkThreads><<<dim3(T, d.P), kTopkThreads, (size_t)d.NB_max, s>>>(
+        d, st, scores, T, pos0, nb_out, sel, n_sel);
   return hipGetLastError();
 }
 

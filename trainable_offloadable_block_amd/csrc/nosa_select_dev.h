@@ -274,8 +274,8 @@ struct __align__(16) TopkLds {
   uint32_t cnt[2][kTopkThreads / 64];
 };
 
-// Marks kind[bb0 + t + 256 r] = val for the k largest nonzero keys of the
-// workgroup (thread t holds the keys of candidates t + 256 r, r < R).
+// Marks kind[bb0 + t + NT r] = val for the k largest nonzero keys of the
+// NT-thread workgroup (thread t holds the keys of candidates t + NT r, r < R).
 // Exact selection by range refinement: each round histograms the active keys
 // into 256 bins over [min, max] (the top 8 bits of their spread), keeps every
 // key above the bin holding the k-th largest, drops those below it, and goes
@@ -283,7 +283,7 @@ struct __align__(16) TopkLds {
 // shrinks by 8 bits per round, so 64-bit keys need at most 8 rounds.
 // hist[0] must be zero on entry; both are zero again on return. Called by
 // all threads; the caller syncs before reading kind.
-template <int R>
+template <int R, int NT = kTopkThreads>
 __device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0, uint8_t *kind, uint8_t val,
                         TopkLds &sh) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -324,13 +324,13 @@ __device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kTopkBins / kTopkThreads; ++i)         // next round's bins
-      sh.hist[par ^ 1][t + kTopkThreads * i] = 0;
+    for (int i = 0; i < kTopkBins / NT; ++i)         // next round's bins
+      sh.hist[par ^ 1][t + NT * i] = 0;
     mn = ~0ull;
     mx = 0;
     c = 0;
 #pragma unroll
-    for (int i = 0; i < kTopkThreads / 64; ++i) {
+    for (int i = 0; i < NT / 64; ++i) {
       const uint64_t a = sh.mn[par][i], b = sh.mx[par][i];
       mn = a < mn ? a : mn;
       mx = b > mx ? b : mx;
@@ -339,7 +339,7 @@ __device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0
     if (c <= static_cast<uint32_t>(need)) {                  // uniform: take them all
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        if (act[r]) kind[bb0 + t + kTopkThreads * r] = val;
+        if (act[r]) kind[bb0 + t + NT * r] = val;
       break;
     }
     const int span = mx > mn ? 64 - __builtin_clzll(mx - mn) : 0;   // c >= 2 distinct keys
@@ -393,7 +393,7 @@ __device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0
       if (act[r]) {
         const int bin = static_cast<int>((key[r] - mn) >> shift);
         if (bin > bstar || (bin == bstar && all_in)) {
-          kind[bb0 + t + kTopkThreads * r] = val;
+          kind[bb0 + t + NT * r] = val;
           act[r] = false;
         } else if (bin < bstar) {
           act[r] = false;
@@ -405,9 +405,9 @@ __device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0
   // leave both histograms zero for the next call
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kTopkBins / kTopkThreads; ++i) {
-    sh.hist[0][t + kTopkThreads * i] = 0;
-    sh.hist[1][t + kTopkThreads * i] = 0;
+  for (int i = 0; i < kTopkBins / NT; ++i) {
+    sh.hist[0][t + NT * i] = 0;
+    sh.hist[1][t + NT * i] = 0;
   }
 }
 
