@@ -113,6 +113,15 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   // that never see a chunk keep z = 0. (Separate max and sum sweeps save
   // vector work but measured slower: the extra sweep's MFMA, LDS reads and
   // barriers cost more.)
+  // One exponential per logit: exp2(-|x - m|) is the factor of whichever of
+  // the running sum and the new term is not at the new maximum (the other's
+  // factor is 1), the same values the two-exponential form gives.
+  auto online_step = [](float &m, float &z, float x) {
+    const float dl = x - m;
+    const float e = __builtin_amdgcn_exp2f(-fabsf(dl));
+    z = dl > 0.0f ? fmaf(z, e, 1.0f) : z + e;
+    m = fmaxf(m, x);
+  };
   constexpr float kFloor = -1.0e30f;
   float m[kPsRowTiles][4], z[kPsRowTiles][4];
 #pragma unroll
@@ -138,11 +147,7 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(4
         for (int rt = 0; rt < kPsRowTiles; ++rt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float x = acc[rt][i] * kScale2;
-            const float mn = fmaxf(m[rt][i], x);
-            z[rt][i] = fmaf(z[rt][i], __builtin_amdgcn_exp2f(m[rt][i] - mn),
-                            __builtin_amdgcn_exp2f(x - mn));
-            m[rt][i] = mn;
+            online_step(m[rt][i], z[rt][i], acc[rt][i] * kScale2);
           }
       } else {
 #pragma unroll
@@ -150,11 +155,7 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(4
           if (c >= row_C(rt)) continue;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float x = acc[rt][i] * kScale2;
-            const float mn = fmaxf(m[rt][i], x);
-            z[rt][i] = fmaf(z[rt][i], __builtin_amdgcn_exp2f(m[rt][i] - mn),
-                            __builtin_amdgcn_exp2f(x - mn));
-            m[rt][i] = mn;
+            online_step(m[rt][i], z[rt][i], acc[rt][i] * kScale2);
           }
         }
       }
