@@ -532,11 +532,13 @@ def test_sparse_prefill_16k_sampled():
                          rows=[0, 1, 100, 255, 256, 400, 510, 511])
 
 
-@pytest.mark.parametrize("context", [24000, 36000])
+@pytest.mark.parametrize("context", [24000, 32832, 32896, 36000])
 def test_sparse_prefill_long_prompt_sampled(context):
     """Prompt tails past 16K: about 360 candidate blocks per query (one wave
-    per query, up to 8 keys a lane) and about 550 (the 256-thread selection);
-    64 queries, 2 pairs x 6 rows against the oracle."""
+    per query, up to 8 keys a lane), the last prompt length on one wave
+    (513 blocks, 510 candidates) and the first past it (the 256-thread
+    selection), and about 560 candidates; 64 queries, 2 pairs x 6 rows
+    against the oracle."""
     wl = small_workload(173, context=context, k_blocks=40, k_q_blocks=16, k_e_blocks=24)
     _sparse_prefill_case(wl, 64, context - 64, check_pairs=[0, 3], rows=[0, 1, 31, 32, 62, 63])
 
