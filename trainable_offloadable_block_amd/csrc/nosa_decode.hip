@@ -128,13 +128,13 @@ __device__ inline void process_half(Half &hb, const bf16x8 (&qop)[4], float qsca
   mx = xor32_max(xor16_max(mx));
   const float m_new = fmaxf(m_run, mx);
   if (m_new == -INFINITY) return;              // wave-uniform: nothing valid
-  const float alpha = exp2f(m_run - m_new);    // 0 while m_run = -inf
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);    // 0 while m_run = -inf
   m_run = m_new;
   float psum = 0.0f;
   uint32_t phi[4], plo[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const f32x2 pm = {exp2f(x[2 * i] - m_new), exp2f(x[2 * i + 1] - m_new)};
+    const f32x2 pm = {__builtin_amdgcn_exp2f(x[2 * i] - m_new), __builtin_amdgcn_exp2f(x[2 * i + 1] - m_new)};
     psum += pm[0] + pm[1];
     // P = hi + lo, both bf16 (round to nearest even)
     const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(pm, bf16x2));

@@ -266,12 +266,13 @@ __global__ __launch_bounds__(kPaWaves * 64) __attribute__((amdgpu_waves_per_eu(4
       mx = xor32_max(xor16_max(mx));
       const float m_new = fmaxf(m_run, mx);
       const bool live = m_new != -INFINITY;                  // this column has a key so far
-      const float alpha = live ? exp2f(m_run - m_new) : 1.0f;
+      const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
       float psum = 0.0f;
       uint32_t phi[4], plo[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x2 pm = live ? f32x2{exp2f(x[2 * i] - m_new), exp2f(x[2 * i + 1] - m_new)}
+        const f32x2 pm = live ? f32x2{__builtin_amdgcn_exp2f(x[2 * i] - m_new),
+                                       __builtin_amdgcn_exp2f(x[2 * i + 1] - m_new)}
                               : f32x2{0.f, 0.f};
         psum += pm[0] + pm[1];
         const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(pm, bf16x2));
