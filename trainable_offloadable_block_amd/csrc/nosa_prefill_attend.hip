@@ -284,11 +284,16 @@ __global__ __launch_bounds__(kPaWaves * 64) __attribute__((amdgpu_waves_per_eu(4
       l_run = l_run * alpha + psum;
       const bf16x8 bhi = __builtin_bit_cast(bf16x8, uint4{phi[0], phi[1], phi[2], phi[3]});
       const bf16x8 blo = __builtin_bit_cast(bf16x8, uint4{plo[0], plo[1], plo[2], plo[3]});
+      // once the columns' maxima settle (usually within the first blocks)
+      // alpha is 1 in every lane and the rescale of O is skipped
+      if (__ballot(alpha != 1.0f) != 0) {                    // uniform
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+      }
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const bf16x8 vt = as_bf16x8(*reinterpret_cast<const uint4 *>(
             kv_sh + kPaKBytes + half * 8192 + 16 * l + 1024 * dt));
-        o[dt] *= alpha;
         o[dt] = mfma16x16x32(vt, bhi, o[dt]);
         o[dt] = mfma16x16x32(vt, blo, o[dt]);
       }
