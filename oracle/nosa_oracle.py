@@ -528,6 +528,24 @@ def locality(prev: list, cur: list, new_block) -> float:
     return sum(1 for b in cur if b in have) / len(cur)
 
 
+def selected_tokens(blocks, L: int) -> set:
+    """Positions of the existing tokens (< L) of the given blocks."""
+    return {j for b in blocks for j in range(b * BLOCK, min((b + 1) * BLOCK, L))}
+
+
+def token_locality(prev: list, L_prev: int, cur: list, L_cur: int) -> float:
+    """Token-level gamma(t), as [W] How NOSA works measures locality: the share
+    of the tokens selected at step t that were also selected at step t-1.
+    The token appended at this step (position L_cur - 1) could not have been
+    selected before, so it is left out of the count."""
+    now = selected_tokens(cur, L_cur)
+    now.discard(L_cur - 1)
+    if not now:
+        return 1.0
+    before = selected_tokens(prev, L_prev)
+    return len(now & before) / len(now)
+
+
 # ----------------------------------------------------------------- budget
 
 def budget(k_tokens: int, k_q_tokens: int, n_sink: int, window_tokens: int,

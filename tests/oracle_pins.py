@@ -323,6 +323,71 @@ def pin_invariants(o, seed=10, cases=12, ahead=False):
             assert r.misses == [b for b in S if b not in have]
 
 
+def pin_incremental_state_equals_bulk(o):
+    """Appending tokens one at a time leaves the state that building it in
+    bulk from the whole prefix gives: compressed keys equal compress_keys (the
+    pinned mean pooling of [B1B] 核心组件一), chunk means of the eviction score
+    equal chunk_means ([L189] 2.1, eqs. 5-6) and the per-token scores equal
+    eviction_scores over all values at once. Runs start from no token, from
+    just below chunk and block completions, and cross block and window
+    boundaries."""
+    rng = _rng(18)
+    d = 8
+    for L0, steps in ((0, 150), (31, 90), (64 * 3 + 15, 120), (64 * 5 + 63, 140)):
+        cap = L0 + steps
+        K = _bf16_vals(rng, (cap, d), 2.0)
+        V = _bf16_vals(rng, (cap, d))
+        W1 = _bf16_vals(rng, (d, d), 0.5)
+        W2 = _bf16_vals(rng, (d,), 0.5)
+        K0, V0 = np.zeros((cap, d)), np.zeros((cap, d))
+        K0[:L0], V0[:L0] = K[:L0], V[:L0]
+        p = o.PairOracle(K0, V0, W1, W2, L0, 1, 2, 2, 2, 1.0)
+        for t in range(steps):
+            p.append(K[L0 + t], V[L0 + t])
+            L = p.L
+            assert L == L0 + t + 1
+            if t % 7 and t != steps - 1:
+                continue
+            ck = np.array(p.ckeys).reshape(-1, d)
+            assert np.array_equal(ck, o.compress_keys(K, L)), (L0, t)
+            s_bulk = o.eviction_scores(V[:L], W1, W2)
+            assert np.allclose(p.s[:L], s_bulk, rtol=1e-12, atol=1e-300), (L0, t)
+            e_bulk = o.chunk_means(p.s, L)
+            assert len(p.e_chunks) == len(e_bulk) == o.n_chunks(L), (L0, t)
+            assert np.allclose(p.e_chunks, e_bulk, rtol=1e-14, atol=0), (L0, t)
+
+
+def pin_locality_closed_form(o):
+    """Hand-counted block-level gamma(t) = |S(t) kept| / |S(t)| ([W] How NOSA
+    works, Theorem 2), with the block this step's token opened counted as
+    present."""
+    # S(t-1) = {0,1,2,5,7}, S(t) = {0,1,2,6,7,8}: kept 0,1,2,7 (+8 if new)
+    assert o.locality([0, 1, 2, 5, 7], [0, 1, 2, 6, 7, 8], 8) == 5 / 6
+    assert o.locality([0, 1, 2, 5, 7], [0, 1, 2, 6, 7, 8], None) == 4 / 6
+    # the newest selected block is neither kept nor new: not counted
+    assert o.locality([0, 1, 2], [0, 1, 3], None) == 2 / 3
+    # an opened block that is not selected adds nothing
+    assert o.locality([0, 1], [0, 1, 4], 5) == 2 / 3
+    assert o.locality([4, 9], [4, 9], None) == 1.0
+
+
+def pin_token_locality_closed_form(o):
+    """Hand-counted token-level gamma(t): the share of the selected tokens
+    that were selected one step earlier, leaving out the token appended at
+    this step ([W] How NOSA works: locality as a fraction of selected
+    tokens)."""
+    # S(t-1) = {0, 2} at L = 150: tokens 0..63 and 128..149 (86).
+    # S(t) = {0, 1, 2} at L = 151: tokens 0..150 less the new 150 (150).
+    assert o.token_locality([0, 2], 150, [0, 1, 2], 151) == 86 / 150
+    # the new token opens block 2: everything else was selected
+    assert o.token_locality([0, 1], 128, [0, 2], 129) == 1.0
+    # block 3 dropped, block 1 added: kept 0..63 and 256..299 (108) of
+    # 0..127 and 256..299 (172)
+    assert o.token_locality([0, 3, 4], 300, [0, 1, 4], 301) == 108 / 172
+    # block-level and token-level agree when every block is full and kept
+    assert o.token_locality([1, 2], 640, [1, 2], 641) == 1.0
+
+
 def pin_invariants_ahead(o):
     """The same bound and bookkeeping when every step selects one layer ahead
     with a forecast head (SparDA's order: select and fetch, then append):

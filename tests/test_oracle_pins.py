@@ -206,12 +206,64 @@ def _prefill_attend_not_causal(o):
     o.prefill_sparse_attend = prefill_sparse_attend
 
 
+def _append_half_chunk_mean(o):
+    def append(self, k_new, v_new):
+        j = self.L
+        self.K[j] = k_new
+        self.V[j] = v_new
+        self.s[j] = o.eviction_scores(v_new[None, :], self.W1, self.W2)[0]
+        self.L += 1
+        while len(self.ckeys) < o.n_chunks(self.L):
+            i = len(self.ckeys)
+            self.ckeys.append(o.compress_chunk(self.K[16 * i:16 * i + 32]))
+            self.e_chunks.append(self.s[16 * i:16 * i + 16].mean())   # half the chunk
+        return j
+    o.PairOracle.append = append
+
+
+def _locality_newest_always_present(o):
+    def locality(prev, cur, new_block):
+        have = set(prev) | {max(cur)}
+        if new_block is not None:
+            have.add(new_block)
+        return sum(1 for b in cur if b in have) / len(cur)
+    o.locality = locality
+
+
+def _locality_previous_denominator(o):
+    def locality(prev, cur, new_block):
+        have = set(prev)
+        if new_block is not None:
+            have.add(new_block)
+        return sum(1 for b in cur if b in have) / len(prev)
+    o.locality = locality
+
+
+def _token_locality_counts_new_token(o):
+    def token_locality(prev, L_prev, cur, L_cur):
+        now = o.selected_tokens(cur, L_cur)
+        before = o.selected_tokens(prev, L_prev)
+        return len(now & before) / len(now)
+    o.token_locality = token_locality
+
+
+def _token_locality_whole_blocks(o):
+    def token_locality(prev, L_prev, cur, L_cur):
+        now = {j for b in cur for j in range(64 * b, 64 * b + 64) if j != L_cur - 1}
+        before = {j for b in prev for j in range(64 * b, 64 * b + 64)}
+        return len(now & before) / len(now)
+    o.token_locality = token_locality
+
+
 MUTATIONS = [_chunks_by_start, _no_score_scale, _softmax_over_heads,
              _transposed_w1, _swapped_pool, _sum_not_mean, _ties_high_index,
              _bias_sign, _window_without_partial, _double_rounding,
              _float_sum_compress, _evict_on_agnostic_only, _fill_shortfall,
              _forecast_softmax, _forecast_unscaled, _ahead_at_current_length,
-             _prefill_off_by_one, _prefill_not_causal, _prefill_attend_not_causal]
+             _prefill_off_by_one, _prefill_not_causal, _prefill_attend_not_causal,
+             _append_half_chunk_mean, _locality_newest_always_present,
+             _locality_previous_denominator, _token_locality_counts_new_token,
+             _token_locality_whole_blocks]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
