@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--cpu-pairs", type=int, default=64)
     ap.add_argument("--cpu-steps", type=int, default=80)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--breakdown-steps", type=int, default=4)
+    ap.add_argument("--breakdown-steps", type=int, default=8)
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the host-link leg (offloaded 128K workload)")
     ap.add_argument("--offload-steps", type=int, default=24)
@@ -68,6 +68,10 @@ def parse():
                     help="skip the hipGraph replay leg of the same layer stack")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the GQA-16, 96-block leg (beyond the five configs)")
+    ap.add_argument("--no-tiny", action="store_true",
+                    help="skip the tiny 4K single-layer leg")
+    ap.add_argument("--only-link", action="store_true",
+                    help="run only the host-link ceiling probe and print its JSON")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of MIB MiB first (a known "
                          "byte count for calibrating HBM traffic counters)")
@@ -138,6 +142,35 @@ def locality_step(prev, cur, seq_len, wl):
     return g
 
 
+def token_locality_step(prev, cur, seq_len, wl):
+    """Per pair: token-level gamma(t), the share of the tokens of S(t) that
+    were also selected at step t-1, leaving out the token this step appended
+    (the oracle's token_locality() definition). Arguments as for
+    locality_step."""
+    (ps, pn), (cs, cn) = prev, cur
+    g = []
+    for p in range(cs.shape[0]):
+        if cn[p] <= 0:
+            continue
+        L = int(seq_len[p // wl.n_kv_heads])
+        have = set(ps[p, :pn[p]].tolist())
+        now = kept = 0
+        for b in cs[p, :cn[p]].tolist():
+            n = max(0, min(64, L - 64 * b))
+            if b == (L - 1) // 64:
+                n -= 1                               # the step's own token
+            now += n
+            if b in have:
+                kept += max(0, min(64, L - 1 - 64 * b))
+        g.append(kept / now if now else 1.0)
+    return g
+
+
+def pct(v, q):
+    import numpy as np
+    return round(float(np.percentile(np.asarray(v, dtype=float), q)), 2)
+
+
 def select_bytes(wl, L):
     """Algorithmic bytes of one selection at sequence length L (every
     sequence): each complete chunk's compressed key (bf16), an fp32 score and
@@ -193,15 +226,36 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(wl, n_pairs, n_steps):
-    """The oracle as it stands, on a bounded sample: n_pairs pairs of layer 0,
-    n_steps decode steps each (append + select + attend)."""
+_CPU_BARRIER = None
+_CPU_BLAS = None
+
+
+def _oracle_worker_init(barrier):
+    """Pool worker set-up: the start barrier, and single-threaded BLAS so that
+    the worker processes, not BLAS threads, share the cores."""
+    global _CPU_BARRIER, _CPU_BLAS
+    _CPU_BARRIER = barrier
+    # before numpy loads its BLAS in this process (a spawned interpreter)
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    import numpy  # noqa: F401
+    try:
+        from threadpoolctl import threadpool_limits
+        _CPU_BLAS = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        _CPU_BLAS = None
+
+
+def _oracle_pairs(job):
+    """One worker's share of the CPU baseline: builds the oracle of its
+    pairs (untimed), waits for every worker, then steps them n_steps times.
+    Returns (start, end) on the system-wide monotonic clock."""
+    wl_id, pairs, n_steps = job
     import numpy as np
     import oracle.nosa_oracle as O
-    from synth import bf16_bits_to_f64, context_kv, eviction_weights, new_tokens, queries
+    from synth import WORKLOADS, bf16_bits_to_f64, context_kv, eviction_weights, new_tokens, queries
+    wl = WORKLOADS[wl_id]
     G, Hkv = wl.group, wl.n_kv_heads
-    P = wl.batch * Hkv
-    pairs = [int(x) for x in np.linspace(0, P - 1, n_pairs)]
     n_w = wl.window_tokens // 64
     k_e_dyn = wl.k_e_blocks - wl.n_sink_blocks - n_w
     work = []
@@ -216,37 +270,127 @@ def cpu_baseline(wl, n_pairs, n_steps):
                          wl.n_sink_blocks, n_w, wl.k_q_blocks, k_e_dyn, 1.0)
         kn, vn = new_tokens(wl, 0, b, g)
         q = np.stack([queries(wl, 0, b, g * G + h) for h in range(G)])
-        work.append((o, kn, vn, q))
-    t0 = time.perf_counter()
+        work.append((o, bf16_bits_to_f64(kn[:n_steps]), bf16_bits_to_f64(vn[:n_steps]),
+                     bf16_bits_to_f64(q[:, :n_steps])))
+    _CPU_BARRIER.wait(timeout=900)
+    t0 = time.monotonic()
     for t in range(n_steps):
         for o, kn, vn, q in work:
-            o.step(bf16_bits_to_f64(kn[t]), bf16_bits_to_f64(vn[t]), bf16_bits_to_f64(q[:, t]))
-    el = time.perf_counter() - t0
-    per_pair_step = el / (len(pairs) * n_steps)
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        blas = 1
+            o.step(kn[t], vn[t], q[:, t])
+    return t0, time.monotonic()
+
+
+def cpu_baseline(wl_id, n_pairs, n_steps):
+    """The oracle as it stands, on a bounded sample (n_pairs pairs of layer
+    0, n_steps decode steps each: append + select + attend), spread over one
+    single-threaded process per host core (at most 16, the GPU's share of a
+    box), every process starting together."""
+    import multiprocessing as mp
+    import numpy as np
+    from synth import WORKLOADS
+    wl = WORKLOADS[wl_id]
+    P = wl.batch * wl.n_kv_heads
+    pairs = sorted({int(x) for x in np.linspace(0, P - 1, n_pairs)})
+    n_proc = max(1, min(16, len(os.sched_getaffinity(0)), len(pairs)))
+    shares = [pairs[i::n_proc] for i in range(n_proc)]
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(n_proc)
+    with ctx.Pool(n_proc, initializer=_oracle_worker_init, initargs=(barrier,)) as pool:
+        spans = pool.map(_oracle_pairs, [(wl_id, sh, n_steps) for sh in shares], chunksize=1)
+    el = max(b for _, b in spans) - min(a for a, _ in spans)
+    step_s = el / n_steps * (P / len(pairs))          # all P pairs of one layer
     return {
-        "value": wl.batch / (per_pair_step * P),
+        "value": wl.batch / step_s,
         "unit": "tokens/s/layer",
-        "cores": int(blas),
+        "cores": n_proc,
         "host_cores": len(os.sched_getaffinity(0)),
+        "threads_per_process": 1,
         "kind": "oracle",
         "seconds": round(el, 2),
-        "sample": (f"{len(pairs)} of {P} (sequence, KV head) pairs of layer 0 x "
-                   f"{n_steps} decode steps (append+select+attend, float64 numpy); "
-                   f"per-layer step time = per-pair step time x {P} pairs"),
+        "sample": (f"{len(pairs)} of {P} (sequence, KV head) pairs of layer 0 of {wl.name} x "
+                   f"{n_steps} decode steps (append+select+attend, float64 numpy), split over "
+                   f"{n_proc} single-threaded processes; per-layer step time = wall time of "
+                   f"the parallel stepping / steps x {P} / {len(pairs)} pairs"),
     }
 
 
-def host_link_leg(n_steps, pool, dev):
+def host_link_peak(dev, nbytes=1 << 30, reps=5):
+    """The host-to-device link ceiling, measured in this process on a
+    contiguous pinned buffer of nbytes: the best of reps DMA copies
+    (hipMemcpyAsync through torch) and the best compute-unit read of the
+    same buffer through its device alias with nosa_link_copy (the delta
+    fetch's load path) over several workgroup counts. The peak is the larger
+    of the two."""
+    import ctypes
+    import torch
+    from trainable_offloadable_block_amd import _lib as L
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    src.fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    memcpy = 0.0
+    for _ in range(reps):
+        a, b = ev(), ev()
+        a.record()
+        dst.copy_(src, non_blocking=True)
+        b.record()
+        torch.cuda.synchronize()
+        memcpy = max(memcpy, nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+    alias = ctypes.c_void_p()
+    L.check(L.lib().nosa_host_alias(ctypes.c_void_p(src.data_ptr()), ctypes.byref(alias)),
+            "host_alias")
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    cu = {}
+    for n_wg in (32, 128, 512, 2048):
+        best = 0.0
+        for _ in range(reps):
+            a, b = ev(), ev()
+            a.record()
+            L.check(L.lib().nosa_link_copy(alias, ctypes.c_void_p(dst.data_ptr()), nbytes,
+                                           n_wg, stream), "link_copy")
+            b.record()
+            torch.cuda.synchronize()
+            best = max(best, nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+        cu[n_wg] = round(best, 2)
+    assert bool((dst[:4096] == 1).all()) and bool((dst[-4096:] == 1).all())
+    del src, dst
+    torch.cuda.empty_cache()
+    peak = max(memcpy, max(cu.values()))
+    return {"bytes": nbytes, "h2d_memcpy_GBps": round(memcpy, 2),
+            "cu_read_GBps_by_workgroups": {str(k): v for k, v in cu.items()},
+            "peak_GBps": round(peak, 2),
+            "peak_from": "memcpy" if memcpy >= max(cu.values()) else "cu_read"}
+
+
+def fetch_stats(fetched, wl, link_peak):
+    """Delta-fetch record of a leg: bytes and time summed over the calls
+    (GB/s = total bytes / total time), per-call median and p90, and the time
+    the same bytes need at the host-link peak."""
+    import numpy as np
+    b_tot = float(sum(f[0] for f in fetched))
+    us_tot = float(sum(f[1] for f in fetched))
+    gbps = b_tot / (us_tot * 1e-6) / 1e9 if us_tot else 0.0
+    out = {"calls": len(fetched), "bytes_per_call": int(b_tot / max(1, len(fetched))),
+           "us_mean": round(us_tot / max(1, len(fetched)), 1),
+           "us_median": pct([f[1] for f in fetched], 50),
+           "us_p90": pct([f[1] for f in fetched], 90),
+           "GBps": round(gbps, 2),
+           "bound_bytes_per_call": wl.batch * wl.n_kv_heads * wl.k_q_blocks * 32768}
+    if link_peak:
+        out["link_peak_GBps"] = link_peak
+        out["us_at_link_peak"] = round(b_tot / max(1, len(fetched)) / (link_peak * 1e9) * 1e6, 1)
+        out["frac_of_link_peak"] = round(gbps / link_peak, 4)
+    return out
+
+
+def host_link_leg(n_steps, pool, dev, link):
     """Delta fetch over the host link on the offloaded low-locality 128K
     workload (8 sequences, 32 query / 8 KV heads, k_q = k_e = 32): fetch
-    GB/s on the cold first step and in steady state, against the pinned
-    host-to-device hipMemcpy peak measured in the same process, and a
-    per-32-KiB hipMemcpy baseline for fragmented copies."""
+    GB/s on the cold first step and in steady state, against the host-link
+    peak measured in the same process (host_link_peak), and a per-32-KiB
+    hipMemcpy baseline for fragmented copies."""
     import numpy as np
     import torch
     from synth import WORKLOADS
@@ -262,19 +406,10 @@ def host_link_leg(n_steps, pool, dev):
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    # pinned host -> device copy peak (1 GiB, best of 5)
+    # fragmented: 2048 copies of 32 KiB from scattered offsets of 1 GiB
     nb = 1 << 30
     src = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
     dst = torch.empty(nb, dtype=torch.uint8, device=dev)
-    best = 0.0
-    for _ in range(5):
-        a, b = ev(), ev()
-        a.record()
-        dst.copy_(src, non_blocking=True)
-        b.record()
-        torch.cuda.synchronize()
-        best = max(best, nb / (a.elapsed_time(b) * 1e-3) / 1e9)
-    # fragmented: 2048 copies of 32 KiB from scattered offsets
     rng = np.random.default_rng(0)
     offs = rng.choice(nb // 32768, size=2048, replace=False) * 32768
     a, b = ev(), ev()
@@ -285,10 +420,11 @@ def host_link_leg(n_steps, pool, dev):
     torch.cuda.synchronize()
     frag = 2048 * 32768 / (a.elapsed_time(b) * 1e-3) / 1e9
     del src, dst
+    torch.cuda.empty_cache()
     # delta fetch per step
     recs = []
     k = wl.k_blocks
-    prev, gammas, hits = None, [], []
+    prev, gammas, tgammas, hits = None, [], [], []
     for t in range(n_steps):
         layer.append_select(kn[t], vn[t], q[t], want_kind=False)
         a, b = ev(), ev()
@@ -300,37 +436,35 @@ def host_link_leg(n_steps, pool, dev):
         miss = layer.n_miss.cpu().numpy()
         cur = (layer.sel.cpu().numpy().reshape(-1, k), layer.n_sel.cpu().numpy())
         if t >= 4:
-            gammas += locality_step(prev, cur, layer.seq_len.cpu().numpy(), wl)
+            seq = layer.seq_len.cpu().numpy()
+            gammas += locality_step(prev, cur, seq, wl)
+            tgammas += token_locality_step(prev, cur, seq, wl)
             hits += [1.0 - m / n for m, n in zip(miss.tolist(), cur[1].tolist()) if n > 0]
         prev = cur
         recs.append((int(miss.sum()) * 32768, a.elapsed_time(b) * 1e3))
     status = layer.status_bits()
     assert not status, f"device status bits set: {status}"
     cold_b, cold_us = recs[0]
-    steady = recs[4:]
-    st_b = float(np.mean([r[0] for r in steady]))
-    st_us = float(np.median([r[1] for r in steady]))
-    gbps = lambda b_, us: b_ / (us * 1e-6) / 1e9  # noqa: E731
+    peak = link["peak_GBps"]
+    cold_gbps = cold_b / (cold_us * 1e-6) / 1e9
+    steady = fetch_stats(recs[4:], wl, peak)
+    steady["cache_hit_rate"] = round(float(np.mean(hits)), 4)
     return {
         "workload": wl.name, "pairs": wl.batch * wl.n_kv_heads,
-        "h2d_memcpy_peak_GBps": round(best, 2),
+        "link": link,
         "fragmented_32KiB_memcpy_GBps": round(frag, 2),
-        "fetch_cold": {"bytes": cold_b, "us": round(cold_us, 1),
-                       "GBps": round(gbps(cold_b, cold_us), 2),
-                       "frac_of_peak": round(gbps(cold_b, cold_us) / best, 4)},
-        "fetch_steady": {"bytes_per_step": int(st_b), "us_median": round(st_us, 1),
-                         "GBps": round(gbps(st_b, st_us), 2),
-                         "frac_of_peak": round(gbps(st_b, st_us) / best, 4),
-                         "steps": len(steady),
-                         "bound_bytes_per_step": wl.batch * wl.n_kv_heads * wl.k_q_blocks * 32768,
-                         "cache_hit_rate": round(float(np.mean(hits)), 4)},
+        "fetch_cold": {"bytes": cold_b, "us": round(cold_us, 1), "GBps": round(cold_gbps, 2),
+                       "frac_of_link_peak": round(cold_gbps / peak, 4)},
+        "fetch_steady": steady,
         "locality": {"gamma_min": round(float(np.min(gammas)), 4),
                      "gamma_mean": round(float(np.mean(gammas)), 4),
+                     "token_gamma_min": round(float(np.min(tgammas)), 4),
+                     "token_gamma_mean": round(float(np.mean(tgammas)), 4),
                      "bound": round((k - wl.k_q_blocks) / k, 4), "samples": len(gammas)},
     }
 
 
-def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0):
+def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0, link_peak=None):
     """Times K decode steps (after W warm-up steps) of a stack of R
     independent layers of workload wl; every timed decode launch stamps its
     own start and end into a pair of HIP events on its stream
@@ -397,9 +531,10 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0):
     # stage-2 pool can run short, so a selection may hold fewer than k blocks)
     names = ("append_select", "fetch", "decode")
     bd = {n: [] for n in names}
+    layer_step = []                               # us per layer-step (the three calls)
     n_att_samples = []
     fetched = []                                  # (bytes, us) per fetch call
-    gammas, hits = [], []
+    gammas, tgammas, hits = [], [], []
     k = wl.k_blocks
 
     def selection(layer):
@@ -419,9 +554,12 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0):
             torch.cuda.synchronize()
             for i, n in enumerate(names):
                 bd[n].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)
+            layer_step.append(evs[0].elapsed_time(evs[3]) * 1e3)
             n_att_samples.append(attended_tokens(layer, wl))
             cur = selection(layer)
-            gammas += locality_step(prev[li], cur, layer.seq_len.cpu().numpy(), wl)
+            seq = layer.seq_len.cpu().numpy()
+            gammas += locality_step(prev[li], cur, seq, wl)
+            tgammas += token_locality_step(prev[li], cur, seq, wl)
             prev[li] = cur
             if wl.offload:
                 miss = layer.n_miss.cpu().numpy()
@@ -432,22 +570,25 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0):
         graph = graph_replays(layers, inputs, W + K + n_bd, graph_steps, shape)
     status = [ly.status_bits() for ly in layers]
     assert not any(status), f"device status bits set: {status}"
+    dec_us = [x * 1e3 for x in dec_ms]
     out = {"value": wl.batch * R * K / el, "elapsed": el,
            "n_att": float(np.mean(n_att_samples)),
            "dec_avg_s": float(np.mean(dec_ms)) / 1e3,
-           "breakdown": {n: round(float(np.median(v)), 2) for n, v in bd.items()}}
+           "dec_launch_us": {"median": pct(dec_us, 50), "p90": pct(dec_us, 90),
+                             "launches": len(dec_us)},
+           "breakdown": {n: round(float(np.median(v)), 2) for n, v in bd.items()},
+           "breakdown_p90": {n: pct(v, 90) for n, v in bd.items()},
+           "layer_step_us": {"median": pct(layer_step, 50), "p90": pct(layer_step, 90),
+                             "samples": len(layer_step)}}
     out["locality"] = {"gamma_min": round(float(np.min(gammas)), 4),
                        "gamma_mean": round(float(np.mean(gammas)), 4),
+                       "token_gamma_min": round(float(np.min(tgammas)), 4),
+                       "token_gamma_mean": round(float(np.mean(tgammas)), 4),
                        "bound": round((k - wl.k_q_blocks) / k, 4),
                        "samples": len(gammas), "steps": n_bd}
     if fetched:
-        b_ = float(np.mean([f[0] for f in fetched]))
-        us = float(np.mean([f[1] for f in fetched]))
-        P = wl.batch * wl.n_kv_heads
-        out["fetch"] = {"bytes_per_call": int(b_), "us_mean": round(us, 1),
-                        "GBps": round(b_ / (us * 1e-6) / 1e9, 2),
-                        "bound_bytes_per_call": P * wl.k_q_blocks * 32768,
-                        "cache_hit_rate": round(float(np.mean(hits)), 4)}
+        out["fetch"] = fetch_stats(fetched, wl, link_peak)
+        out["fetch"]["cache_hit_rate"] = round(float(np.mean(hits)), 4)
     if graph is not None:
         out["graph"] = {"steps": graph_steps, "ms_per_step": round(graph * 1e3 / graph_steps, 4),
                         "value": round(wl.batch * R * graph_steps / graph, 1)}
@@ -508,14 +649,14 @@ def graph_replays(layers, inputs, t0, n, shape):
     return el
 
 
-def offload_32k_leg(dev, workers, R=4, W=4, K=24, n_bd=8):
+def offload_32k_leg(dev, workers, R=4, W=4, K=24, n_bd=8, link_peak=None):
     """The offloaded 32K 1B-shaped stack (64 sequences, 16/2 heads, k = 64,
     full KV in pinned host memory; R of its 28 layers): decode tokens/s per
     layer with the delta fetch on the step path, and the decode kernel
     (reading the device block cache) against the HBM roofline."""
     from synth import WORKLOADS
     wl = WORKLOADS[3]
-    m = time_stack(wl, R, W, K, n_bd, dev, workers)
+    m = time_stack(wl, R, W, K, n_bd, dev, workers, link_peak=link_peak)
     dbytes = decode_bytes(wl, m["n_att"])
     ach = dbytes / m["dec_avg_s"] / 1e9
     return {"workload": wl.name, "layers_per_step": R, "steps": K,
@@ -525,11 +666,12 @@ def offload_32k_leg(dev, workers, R=4, W=4, K=24, n_bd=8):
                        "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": int(dbytes),
                        "avg_launch_us": round(m["dec_avg_s"] * 1e6, 2),
                        "attended_tokens_per_pair": round(m["n_att"], 2)},
-            "breakdown_us": m["breakdown"], "delta_fetch": m.get("fetch"),
+            "breakdown_us": m["breakdown"], "breakdown_p90_us": m["breakdown_p90"],
+            "layer_step_us": m["layer_step_us"], "delta_fetch": m.get("fetch"),
             "locality": m["locality"]}
 
 
-def offload_8b_64k_leg(dev, workers, W=4, K=32, n_bd=8):
+def offload_8b_64k_leg(dev, workers, W=4, K=32, n_bd=8, link_peak=None):
     """The offloaded 8B-shaped 64K layer (32 sequences, 32/8 heads, k = 64,
     full KV in pinned host memory), one layer timed repeatedly: decode
     tokens/s with the delta fetch on the step path, and the decode kernel
@@ -537,7 +679,7 @@ def offload_8b_64k_leg(dev, workers, W=4, K=32, n_bd=8):
     the HBM roofline."""
     from synth import WORKLOADS
     wl = WORKLOADS[4]
-    m = time_stack(wl, 1, W, K, n_bd, dev, workers)
+    m = time_stack(wl, 1, W, K, n_bd, dev, workers, link_peak=link_peak)
     dbytes = decode_bytes(wl, m["n_att"])
     ach = dbytes / m["dec_avg_s"] / 1e9
     return {"workload": wl.name, "layers_per_step": 1, "steps": K,
@@ -547,7 +689,8 @@ def offload_8b_64k_leg(dev, workers, W=4, K=32, n_bd=8):
                        "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": int(dbytes),
                        "avg_launch_us": round(m["dec_avg_s"] * 1e6, 2),
                        "attended_tokens_per_pair": round(m["n_att"], 2)},
-            "breakdown_us": m["breakdown"], "delta_fetch": m.get("fetch"),
+            "breakdown_us": m["breakdown"], "breakdown_p90_us": m["breakdown_p90"],
+            "layer_step_us": m["layer_step_us"], "delta_fetch": m.get("fetch"),
             "locality": m["locality"]}
 
 
@@ -799,6 +942,26 @@ def next_leg(dev, workers, R=4, W=8, K=48):
             "breakdown_us": m["breakdown"], "locality": m["locality"]}
 
 
+def tiny_leg(dev, workers, W=4, K=32):
+    """The tiny single-layer 4K workload (batch 1, 16/2 heads, k = 16 blocks:
+    4 query-aware + 12 agnostic, window 256): its 32 decode steps, a
+    latency-bound launch chain, as stream launches and as replays of one
+    captured HIP graph of a whole step."""
+    from synth import WORKLOADS
+    wl = WORKLOADS[1]
+    m = time_stack(wl, 1, W, K, K, dev, workers, graph_steps=K)
+    dbytes = decode_bytes(wl, m["n_att"])
+    return {"workload": wl.name, "layers_per_step": 1, "steps": K,
+            "value": round(m["value"], 1), "unit": "tokens/s/layer",
+            "ms_per_step": round(m["elapsed"] * 1e3 / K, 4),
+            "decode": {"bytes_per_launch": int(dbytes), "launch_us": m["dec_launch_us"],
+                       "achieved": round(dbytes / m["dec_avg_s"] / 1e9, 1), "unit": "GB/s",
+                       "bound": "latency (about 1 MB per launch)"},
+            "breakdown_us": m["breakdown"], "breakdown_p90_us": m["breakdown_p90"],
+            "layer_step_us": m["layer_step_us"], "graph_replay": m.get("graph"),
+            "locality": m["locality"]}
+
+
 def warm_leg(dev, workers, W=8, K=120):
     """The headline 16K layer alone, stepped repeatedly: its ~150 MB working
     set partly stays in the 256 MB last-level cache between steps, so these
@@ -840,6 +1003,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     workers = min(16, len(os.sched_getaffinity(0)))
+    if args.only_link:
+        print(json.dumps(host_link_peak(dev)), flush=True)
+        return
     if args.only_ahead:
         print(json.dumps(layer_ahead_leg(dev, workers, n_wg=args.fetch_wg)), flush=True)
         return
@@ -886,10 +1052,13 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
             "bytes_per_launch": int(dbytes), "avg_launch_us": round(dec_avg_s * 1e6, 2),
             "timing": "HIP events stamped by each timed decode launch (hipExtLaunchKernel)",
+            "launch_us": m["dec_launch_us"],
             "call_us_events_around": bd["decode"],
             "attended_tokens_per_pair": round(n_att, 2),
         },
         "breakdown_us": bd,
+        "breakdown_p90_us": m["breakdown_p90"],
+        "layer_step_us": m["layer_step_us"],
         "locality": m["locality"],
     }
     # the selection against the same roofline: its algorithmic bytes over the
@@ -915,6 +1084,9 @@ def main():
                               "kv_GBps": round(byt / (ms * 1e-3) / 1e9, 1)}
     log("warm single-layer leg")
     res["warm_1layer"] = warm_leg(dev, workers)
+    if not args.no_tiny:
+        log("tiny 4K leg")
+        res["tiny_4k"] = tiny_leg(dev, workers)
     if not args.no_prefill:
         log("prefill block-score leg")
         res["prefill_scores"] = prefill_scores_leg(dev, workers)
@@ -922,19 +1094,21 @@ def main():
         log("GQA-16 96-block leg")
         res["gqa16_k96"] = next_leg(dev, workers)
     if not args.no_offload:
+        log("host-link ceiling")
+        link = host_link_peak(dev)
         log("offloaded 32K stack leg")
-        res["offload_32k"] = offload_32k_leg(dev, workers)
+        res["offload_32k"] = offload_32k_leg(dev, workers, link_peak=link["peak_GBps"])
         log("offloaded 8B-shaped 64K leg")
-        res["offload_8b_64k"] = offload_8b_64k_leg(dev, workers)
+        res["offload_8b_64k"] = offload_8b_64k_leg(dev, workers, link_peak=link["peak_GBps"])
         if not args.no_ahead:
             log("layer-ahead leg (SparDA order, offloaded 32K stack)")
             res["layer_ahead"] = layer_ahead_leg(dev, workers, n_wg=args.fetch_wg)
         log("host-link leg (offloaded 128K workload)")
         with cf.ThreadPoolExecutor(workers) as pool:
-            res["host_link"] = host_link_leg(args.offload_steps, pool, dev)
+            res["host_link"] = host_link_leg(args.offload_steps, pool, dev, link)
     if not args.no_cpu:
         log("timing the CPU oracle")
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_pairs, args.cpu_steps)
+        res["cpu_baseline"] = cpu_baseline(2, args.cpu_pairs, args.cpu_steps)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -39,13 +39,9 @@
  *    untouched; they surface when the caller reads status.
  *  - A pair is (sequence b, KV head g); pair index p = b * n_kv_heads + g.
  *    Query head h belongs to KV head h / (n_q_heads / n_kv_heads).
- *  - Launch-shape overrides for tuning sweeps, read from the environment at
- *    each call (results do not depend on them): NOSA_DECODE_BPS (selection
- *    entries per decode workgroup, 4..64; it sets the decode workspace size,
- *    so it must not change between nosa_workspace_bytes and the calls),
- *    NOSA_SELECT_SUBS (128-chunk splits per scoring workgroup),
- *    NOSA_GATHER_VPT (1, 2, 4 or 8: 4 KiB pieces of a block a
- *    nosa_fetch_delta_wg workgroup moves at a time).
+ *  - Launch shapes are chosen from the config and the length bound; tests
+ *    and tuning sweeps can override three of them with nosa_set_tuning
+ *    (results do not depend on them).
  */
 #ifndef NOSA_H
 #define NOSA_H
@@ -366,6 +362,36 @@ int nosa_prefill_attend(const nosa_config *cfg, const nosa_state *st,
 /* Device-usable address of pinned host memory (hipHostGetDevicePointer);
  * allocates nothing. */
 int nosa_host_alias(void *pinned_host_ptr, void **dev_alias);
+
+/* Copies `bytes` (a multiple of 16) from src to dst with n_workgroups
+ * workgroups of 256 threads reading 16 bytes per thread and load, the load
+ * path of nosa_fetch_delta's copies. src may be a device-usable alias of
+ * pinned host memory (nosa_host_alias): the host-link ceiling that a delta
+ * fetch is measured against (aiwiki "NOSA", NOSI: the inference system: the
+ * GPU kernel that reads host memory directly, against the link's peak).
+ * 1 <= n_workgroups <= NOSA_MAX_FETCH_WORKGROUPS. */
+int nosa_link_copy(const void *src, void *dst, size_t bytes, int32_t n_workgroups,
+                   hipStream_t stream);
+
+/* ------------------------------------------------------------ tuning
+ * Process-wide launch-shape overrides, for tests and tuning sweeps (host
+ * state only; results do not depend on them). value 0 restores the
+ * library's choice; the call returns the previous value, or
+ * NOSA_ERR_INVALID for an unknown knob or a value outside its range.
+ *  NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT  selection entries per decode
+ *      workgroup, 4..64. It sets the decode split count and so the decode
+ *      workspace size: a call whose workspace was sized before a change
+ *      may return NOSA_ERR_WORKSPACE.
+ *  NOSA_TUNE_SELECT_SUBS  128-chunk splits scored by one selection
+ *      workgroup, 1..2048 (capped at the split count).
+ *  NOSA_TUNE_GATHER_VPT  4 KiB pieces of a block that a nosa_fetch_delta_wg
+ *      workgroup moves at a time: 1, 2, 4 or 8.
+ * The per-pair arrival counters of the select and decode workspaces sit at
+ * the start of each workspace whatever the launch shape, so a change
+ * between calls never leaves them on non-zero bytes. */
+enum { NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT = 0, NOSA_TUNE_SELECT_SUBS = 1,
+       NOSA_TUNE_GATHER_VPT = 2, NOSA_NUM_TUNE };
+int nosa_set_tuning(int knob, int32_t value);
 
 const char *nosa_strerror(int code);
 const char *nosa_last_error(void);

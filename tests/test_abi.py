@@ -194,3 +194,34 @@ def test_v_tile_order_matches_the_header_formula():
     assert np.array_equal(nosa.v_from_tiles(flat), v)
     many = np.random.default_rng(3).integers(0, 1 << 16, (5, 64, 128))
     assert np.array_equal(nosa.v_from_tiles(nosa.v_to_tiles(many)), many)
+
+
+def test_tuning_knobs():
+    """nosa_set_tuning: range checks, the previous value returned, 0 restores
+    the library's choice; the decode workspace follows the split size."""
+    lib = nosa.lib()
+    c = _cfg()
+    for knob, bad in ((L.NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT, 3),
+                      (L.NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT, 65),
+                      (L.NOSA_TUNE_SELECT_SUBS, -1),
+                      (L.NOSA_TUNE_GATHER_VPT, 3), (7, 1), (-1, 0)):
+        assert lib.nosa_set_tuning(knob, bad) == L.NOSA_ERR_INVALID, (knob, bad)
+    default = lib.nosa_workspace_bytes(ctypes.byref(c), L.NOSA_WS_DECODE, 16640)
+    with L.tuning(L.NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT, 64):
+        one_split = lib.nosa_workspace_bytes(ctypes.byref(c), L.NOSA_WS_DECODE, 16640)
+        assert lib.nosa_set_tuning(L.NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT, 64) == 64
+    assert lib.nosa_set_tuning(L.NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT, 0) == 0
+    assert one_split < default
+    assert lib.nosa_workspace_bytes(ctypes.byref(c), L.NOSA_WS_DECODE, 16640) == default
+
+
+def test_link_copy_rejects_before_any_hip_call():
+    lib = nosa.lib()
+    null = ctypes.c_void_p(0)
+    assert lib.nosa_link_copy(None, 256, 4096, 8, null) == L.NOSA_ERR_INVALID
+    assert lib.nosa_link_copy(256, None, 4096, 8, null) == L.NOSA_ERR_INVALID
+    assert lib.nosa_link_copy(256, 256, 4100, 8, null) == L.NOSA_ERR_INVALID
+    assert lib.nosa_link_copy(264, 256, 4096, 8, null) == L.NOSA_ERR_INVALID
+    for n_wg in (0, L.NOSA_MAX_FETCH_WORKGROUPS + 1):
+        assert lib.nosa_link_copy(256, 256, 4096, n_wg, null) == L.NOSA_ERR_INVALID
+    assert lib.nosa_link_copy(256, 256, 0, 8, null) == L.NOSA_OK

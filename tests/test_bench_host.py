@@ -42,6 +42,39 @@ def test_locality_step_equals_oracle_gamma():
         assert np.allclose(got, want, rtol=0, atol=0)
 
 
+def test_token_locality_step_equals_oracle():
+    wl = small_workload(302, batch=3, n_kv_heads=2, k_blocks=8)
+    rng = np.random.default_rng(6)
+    P, k = wl.batch * wl.n_kv_heads, wl.k_blocks
+    for trial in range(60):
+        lens = rng.integers(130, 2000, size=wl.batch)
+        if trial % 4 == 0:
+            lens[1] = 64 * rng.integers(3, 30) + 1          # the token opens a block
+        nb = (lens + 63) // 64
+        ps = np.full((P, k), -1, np.int32)
+        cs = np.full((P, k), -1, np.int32)
+        pn = np.zeros(P, np.int32)
+        cn = np.zeros(P, np.int32)
+        for p in range(P):
+            L = int(lens[p // wl.n_kv_heads])
+            top = int(nb[p // wl.n_kv_heads])
+            prev_top = (L - 1 + 63) // 64                   # blocks at the previous length
+            n1 = int(min(rng.integers(1, k + 1), prev_top))
+            n2 = int(min(rng.integers(1, k), top - 1))
+            ps[p, :n1] = np.sort(rng.choice(prev_top, size=n1, replace=False))
+            rest = np.sort(rng.choice(top - 1, size=n2, replace=False))
+            cur = np.unique(np.append(rest, top - 1))        # S(t) holds the newest block
+            cs[p, :len(cur)] = cur
+            pn[p], cn[p] = n1, len(cur)
+        got = bench.token_locality_step((ps, pn), (cs, cn), lens, wl)
+        want = []
+        for p in range(P):
+            L = int(lens[p // wl.n_kv_heads])
+            want.append(o.token_locality(ps[p, :pn[p]].tolist(), L - 1,
+                                         cs[p, :cn[p]].tolist(), L))
+        assert np.allclose(got, want, rtol=1e-15, atol=0)
+
+
 def test_decode_bytes_definition():
     wl = WORKLOADS[2]
     n_att = 4032.44

@@ -37,6 +37,7 @@ NOSA_EVICT_BIAS = 1
 NOSA_OFFLOAD = 2
 
 NOSA_WS_SELECT, NOSA_WS_FETCH, NOSA_WS_DECODE = 1, 2, 3
+NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT, NOSA_TUNE_SELECT_SUBS, NOSA_TUNE_GATHER_VPT = 0, 1, 2
 KIND_NONE, KIND_SINK, KIND_WINDOW, KIND_QUERY, KIND_AGNOSTIC = range(5)
 
 BUFFERS = ["seq_len", "arrive", "status", "ckey", "tok_s", "chunk_e", "blk_e",
@@ -105,6 +106,8 @@ def lib():
         "nosa_prefill_select": (ctypes.c_int, [cfgp, stp, _P, _I32, _I32, _P, _P, _P]),
         "nosa_prefill_attend": (ctypes.c_int, [cfgp, stp, _P, _I32, _I32, _P, _P, _P, _P]),
         "nosa_host_alias": (ctypes.c_int, [_P, ctypes.POINTER(_P)]),
+        "nosa_link_copy": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _I32, _P]),
+        "nosa_set_tuning": (ctypes.c_int, [ctypes.c_int, _I32]),
         "nosa_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "nosa_last_error": (ctypes.c_char_p, []),
     }
@@ -127,3 +130,22 @@ def header_functions() -> list[str]:
 def check(code: int, where: str):
     if code != NOSA_OK:
         raise NosaError(code, where)
+
+
+class tuning:
+    """Context manager that sets one nosa_set_tuning knob and restores its
+    previous value on exit."""
+
+    def __init__(self, knob: int, value: int):
+        self.knob, self.value, self.prev = knob, int(value), None
+
+    def __enter__(self):
+        prev = lib().nosa_set_tuning(self.knob, self.value)
+        if prev < 0:
+            raise NosaError(prev, "set_tuning")
+        self.prev = prev
+        return self
+
+    def __exit__(self, *exc):
+        lib().nosa_set_tuning(self.knob, self.prev)
+        return False

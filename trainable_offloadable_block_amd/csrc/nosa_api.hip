@@ -1,12 +1,13 @@
 // C ABI entry points: argument checks (host only, before any HIP call),
 // sizing, and launches. See include/nosa.h for the contract of each call.
-#include <stdlib.h>
-
+#include <atomic>
 #include <string>
 
 #include "nosa_internal.h"
 
 namespace {
+
+std::atomic<int> g_tuning[NOSA_NUM_TUNE];
 
 thread_local std::string g_last_error;
 
@@ -104,7 +105,35 @@ int hip_result(hipError_t e) {
 
 }  // namespace
 
+int nosa::tuning(int knob) {
+  return knob >= 0 && knob < NOSA_NUM_TUNE ? g_tuning[knob].load(std::memory_order_relaxed) : 0;
+}
+
 extern "C" {
+
+int nosa_set_tuning(int knob, int32_t value) {
+  bool ok = false;
+  switch (knob) {
+    case NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT: ok = value == 0 || (value >= 4 && value <= 64); break;
+    case NOSA_TUNE_SELECT_SUBS: ok = value >= 0 && value <= 2048; break;
+    case NOSA_TUNE_GATHER_VPT: ok = value == 0 || value == 1 || value == 2 || value == 4 || value == 8; break;
+    default: break;
+  }
+  if (!ok) return fail(NOSA_ERR_INVALID, "unknown tuning knob or value out of range");
+  return g_tuning[knob].exchange(value, std::memory_order_relaxed);
+}
+
+int nosa_link_copy(const void *src, void *dst, size_t bytes, int32_t n_workgroups,
+                   hipStream_t stream) {
+  if (!src || !dst) return fail(NOSA_ERR_INVALID, "src / dst is NULL");
+  if (bytes % 16) return fail(NOSA_ERR_INVALID, "bytes must be a multiple of 16");
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u)
+    return fail(NOSA_ERR_INVALID, "src and dst must be 16-byte aligned");
+  if (n_workgroups < 1 || n_workgroups > NOSA_MAX_FETCH_WORKGROUPS)
+    return fail(NOSA_ERR_INVALID, "n_workgroups outside [1, NOSA_MAX_FETCH_WORKGROUPS]");
+  if (bytes == 0) return NOSA_OK;
+  return hip_result(nosa::launch_link_copy(src, dst, bytes, n_workgroups, stream));
+}
 
 int nosa_validate_config(const nosa_config *cfg) { return check_config(cfg); }
 

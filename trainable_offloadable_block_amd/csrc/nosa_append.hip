@@ -134,15 +134,11 @@ __global__ __launch_bounds__(128) void prefill_chunks_kernel(Dims d, nosa_state 
   for (int c = 0; c < 4; ++c) {
     const int i = 4 * blk + c;
     if (i >= C) return;
-    double sum = 0.0;
-    for (int j = 0; j < kPoolKernel; ++j) {
+    st.ckey[((size_t)p * d.C_max + i) * kHeadDim + t] = mean32_bf16([&](int j) -> uint16_t {
       const int tok = i * kPoolStride + j;
-      const uint16_t *row = kvb + ((size_t)p * d.NB_max + tok / kBlock) * kBlockElems +
-                            (tok % kBlock) * kHeadDim;
-      sum += (double)bf16_to_f32(row[t]);
-    }
-    st.ckey[((size_t)p * d.C_max + i) * kHeadDim + t] =
-        f64_to_bf16_rne(sum * (1.0 / kPoolKernel));
+      return kvb[((size_t)p * d.NB_max + tok / kBlock) * kBlockElems +
+                 (tok % kBlock) * kHeadDim + t];
+    });
     if (t < 64) {
       double se = t < kPoolKernel ? (double)tok_s[i * kPoolStride + t] : 0.0;
       se = wave_sum(se);

@@ -183,13 +183,10 @@ __device__ __forceinline__ int append_pair(const Dims &d, const nosa_state &st, 
   if (L < kPoolKernel || (L - kPoolKernel) % kPoolStride != 0) return -1;
   const int i = (L - kPoolKernel) / kPoolStride;
   if (dim) {
-    double sum = 0.0;                    // exact for bf16 inputs of sane range
-    for (int j = 0; j < kPoolKernel; ++j) {
+    const uint16_t c = mean32_bf16([&](int j) -> uint16_t {
       const int tok = pos - (kPoolKernel - 1) + j;
-      const uint16_t kv = tok == pos ? kb : ring[(tok % kPoolKernel) * kHeadDim + t];
-      sum += (double)bf16_to_f32(kv);
-    }
-    const uint16_t c = f64_to_bf16_rne(sum * (1.0 / kPoolKernel));
+      return tok == pos ? kb : ring[(tok % kPoolKernel) * kHeadDim + t];
+    });
     uint16_t *row = st.ckey + ((size_t)p * d.C_max + i) * kHeadDim;
     if (coherent) {
       const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(

@@ -38,16 +38,16 @@ __host__ __device__ inline int v_index(int tok, int dim) {
   return ((((tok >> 5) * 8 + (dim >> 4)) * 4 + ((tok >> 3) & 3)) * 16 + (dim & 15)) * 8 + (tok & 7);
 }
 
-__device__ inline float bf16_to_f32(uint16_t b) {
-  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+__host__ __device__ inline float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
 }
 
 // bf16 round-to-nearest-even of a float64 value, computed from its bits in
 // one step (no intermediate float32 rounding). Handles zeros, subnormal
 // results (bf16 shares float32's exponent range: step 2^-133 below 2^-126)
 // and overflow to infinity; NaN stays NaN.
-__device__ inline uint16_t f64_to_bf16_rne(double x) {
-  uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+__host__ __device__ inline uint16_t f64_to_bf16_rne(double x) {
+  uint64_t u = __builtin_bit_cast(uint64_t, x);
   uint16_t sign = static_cast<uint16_t>((u >> 48) & 0x8000u);
   int e = static_cast<int>((u >> 52) & 0x7ff);
   uint64_t frac = u & 0xFFFFFFFFFFFFFull;
@@ -82,6 +82,111 @@ __device__ inline uint16_t f64_to_bf16_rne(double x) {
     bits = (static_cast<uint32_t>(be) << 7) | static_cast<uint32_t>(kept & 0x7f);
   }
   return sign | static_cast<uint16_t>(bits);
+}
+
+// bf16 round-to-nearest-even of the mean of 32 bf16 values (bit patterns
+// get(0) .. get(31)), from their exact sum, for any spread of magnitudes
+// (NOSA-1B 核心组件揭秘, 核心组件一: the compressed key is the mean of a
+// 32-token window). A bf16 value is an 8-bit integer times 2^(E' - 134) with
+// E' = max(E, 1) for exponent field E. The float64 sum of 32 of them is
+// exact when their E' span at most 40 binades (the sum needs span + 8 + 5
+// bits <= 53); a wider span, which no key of a normal range reaches, is
+// summed exactly as integers in 320 bits. Infinities and NaNs keep the
+// float64 sum's result.
+__host__ __device__ inline void add_shifted_u320(uint64_t (&acc)[5], uint64_t m, int sh) {
+  const int w = sh >> 6, o = sh & 63;
+  const uint64_t lo = m << o, hi = o ? (m >> (64 - o)) : 0;
+  uint64_t carry = 0;
+  for (int i = 0; i < 5; ++i) {
+    const uint64_t x = i == w ? lo : (i == w + 1 ? hi : 0);
+    const uint64_t s = acc[i] + x;
+    const uint64_t s2 = s + carry;
+    carry = (s < x) | (s2 < carry);
+    acc[i] = s2;
+  }
+}
+
+// Bits [lo, lo + n) of a 320-bit value, n <= 64, lo >= 0.
+__host__ __device__ inline uint64_t bits_u320(const uint64_t (&a)[5], int lo, int n) {
+  const int w = lo >> 6, o = lo & 63;
+  uint64_t v = a[w] >> o;
+  if (o && w + 1 < 5) v |= a[w + 1] << (64 - o);
+  return n >= 64 ? v : (v & ((1ull << n) - 1));
+}
+
+template <typename Get>
+__host__ __device__ uint16_t mean32_bf16_wide(Get get) {
+  uint64_t pos[5] = {0, 0, 0, 0, 0}, neg[5] = {0, 0, 0, 0, 0};
+  for (int j = 0; j < kPoolKernel; ++j) {
+    const uint16_t v = get(j);
+    const int E = (v >> 7) & 0xff;
+    const uint64_t m = (E ? 128u : 0u) + (v & 0x7fu);
+    if (m == 0) continue;
+    // |v| = m * 2^(E' - 134) = m * 2^(sh - 133), sh = E' - 1 in [0, 253]
+    if (v & 0x8000u) add_shifted_u320(neg, m, (E > 1 ? E : 1) - 1);
+    else add_shifted_u320(pos, m, (E > 1 ? E : 1) - 1);
+  }
+  // D = |pos - neg|: sum = +-D * 2^-133, mean = +-D * 2^-138
+  bool negative = false;
+  for (int i = 4; i >= 0; --i) {
+    if (pos[i] != neg[i]) { negative = neg[i] > pos[i]; break; }
+  }
+  uint64_t D[5];
+  const uint64_t(&x)[5] = negative ? neg : pos;
+  const uint64_t(&y)[5] = negative ? pos : neg;
+  uint64_t borrow = 0;
+  for (int i = 0; i < 5; ++i) {
+    const uint64_t t = x[i] - y[i];
+    const uint64_t b1 = x[i] < y[i];
+    D[i] = t - borrow;
+    borrow = b1 | (t < borrow);
+  }
+  int h = -1;                                   // top set bit of D
+  for (int i = 4; i >= 0 && h < 0; --i)
+    if (D[i]) h = 64 * i + 63 - __builtin_clzll(D[i]);
+  if (h < 0) return 0;                          // the exact mean is zero
+  const uint16_t sign = negative ? 0x8000u : 0u;
+  // mean in [2^(h-138), 2^(h-137)): bf16 exponent field h - 11
+  int be = h - 11;
+  const int drop = be >= 1 ? h - 7 : 5;         // normal: 8 kept bits; else quantum 2^-133
+  if (be < 1) be = 0;
+  uint64_t kept = bits_u320(D, drop, 64);
+  const bool half = bits_u320(D, drop - 1, 1) != 0;
+  bool sticky = false;
+  for (int i = 0; i < 5 && 64 * i < drop - 1; ++i) {
+    const int n = drop - 1 - 64 * i;            // bits of word i below the half bit
+    sticky |= (n >= 64 ? D[i] : (D[i] & ((1ull << n) - 1))) != 0;
+  }
+  if (half && (sticky || (kept & 1))) kept += 1;
+  uint32_t bits;
+  if (be == 0) {
+    bits = static_cast<uint32_t>(kept);         // a carry reaches the smallest normal
+  } else {
+    if (kept >> 8) { kept >>= 1; be += 1; }
+    if (be >= 255) return sign | 0x7F80u;
+    bits = (static_cast<uint32_t>(be) << 7) | static_cast<uint32_t>(kept & 0x7f);
+  }
+  return sign | static_cast<uint16_t>(bits);
+}
+
+template <typename Get>
+__host__ __device__ inline uint16_t mean32_bf16(Get get) {
+  double sum = 0.0;
+  int emax = 0, emin = 255;
+  bool special = false;
+  for (int j = 0; j < kPoolKernel; ++j) {
+    const uint16_t v = get(j);
+    sum += (double)bf16_to_f32(v);
+    const int E = (v >> 7) & 0xff;
+    special |= E == 0xff;
+    if (v & 0x7fffu) {
+      const int e = E > 1 ? E : 1;
+      emax = e > emax ? e : emax;
+      emin = e < emin ? e : emin;
+    }
+  }
+  if (special || emax - emin <= 40) return f64_to_bf16_rne(sum * (1.0 / kPoolKernel));
+  return mean32_bf16_wide(get);
 }
 
 // float -> bf16 round-to-nearest-even (finite inputs).

@@ -536,18 +536,15 @@ DecodeLayout decode_layout(const Dims &d) {
   // merge (at GQA 16 a pair's partials are 8 KiB each; 32 pairs x 96 blocks
   // measured 32.3 us at 16 per run against 33.3 us at 12)
   if (bps < 16 && (long)d.P * ((d.k + 15) / 16) >= 192) bps = 16;
-  if (const char *env = getenv("NOSA_DECODE_BPS")) {
-    const int v = atoi(env);
-    if (v >= 4 && v <= 64) bps = v;
-  }
+  if (const int v = tuning(NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT)) bps = v;
   while (bps < 64 && (d.k + bps - 1) / bps > kMaxSplits) bps *= 2;   // merge bound
   lay.blocks_per_split = bps;
   lay.n_splits = (d.k + bps - 1) / bps;
-  lay.o_off = 0;
   const size_t parts = (size_t)d.P * lay.n_splits * d.G;
-  lay.ml_off = (parts * kHeadDim * sizeof(float) + 255) & ~(size_t)255;
-  lay.count_off = lay.ml_off + ((parts * sizeof(float2) + 255) & ~(size_t)255);
-  lay.bytes = lay.count_off + (((size_t)d.P * sizeof(int32_t) + 255) & ~(size_t)255);
+  lay.count_off = 0;
+  lay.o_off = (((size_t)d.P * sizeof(int32_t) + 255) & ~(size_t)255);
+  lay.ml_off = lay.o_off + ((parts * kHeadDim * sizeof(float) + 255) & ~(size_t)255);
+  lay.bytes = lay.ml_off + ((parts * sizeof(float2) + 255) & ~(size_t)255);
   return lay;
 }
 

@@ -18,8 +18,6 @@
 //   loop over the entries (SparDA's persistent copy kernel with a workgroup
 //   budget, aliyun article, KV 预取的运行时实现), so a fetch running beside
 //   compute on another stream holds only that many workgroup slots.
-#include <stdlib.h>
-
 #include "nosa_internal.h"
 
 namespace nosa {
@@ -164,6 +162,28 @@ __global__ __launch_bounds__(256) void gather_wg_kernel(
   }
 }
 
+// grid (n_wg), block 256: a plain copy through the gather's load path
+// (16 bytes per thread and load, a workgroup moving 32 KiB per round like
+// one block), for measuring the host link.
+__global__ __launch_bounds__(256) void link_copy_kernel(const uint4 *__restrict__ src,
+                                                        uint4 *__restrict__ dst, size_t n16) {
+  constexpr int kPer = 8;
+  const size_t step = (size_t)gridDim.x * 256 * kPer;
+  for (size_t base = (size_t)blockIdx.x * 256 * kPer; base < n16; base += step) {
+    uint4 v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const size_t i = base + threadIdx.x + 256 * j;
+      if (i < n16) v[j] = src[i];
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const size_t i = base + threadIdx.x + 256 * j;
+      if (i < n16) dst[i] = v[j];
+    }
+  }
+}
+
 // Resident KV: every selected block already sits in the device pool at its
 // own index, so phys = sel and nothing moves. grid (P), block 64.
 __global__ __launch_bounds__(64) void resident_phys_kernel(
@@ -183,6 +203,13 @@ FetchLayout fetch_layout(const Dims &d) {
   return f;
 }
 
+hipError_t launch_link_copy(const void *src, void *dst, size_t bytes, int n_wg,
+                            hipStream_t s) {
+  link_copy_kernel<<<dim3(n_wg), 256, 0, s>>>(static_cast<const uint4 *>(src),
+                                              static_cast<uint4 *>(dst), bytes / 16);
+  return hipGetLastError();
+}
+
 hipError_t launch_fetch(const Dims &d, const nosa_state &st, const int32_t *sel,
                         const int32_t *n_sel, int32_t *phys, int32_t *n_miss,
                         void *ws, const FetchLayout &lay, hipStream_t s, int n_wg) {
@@ -194,8 +221,7 @@ hipError_t launch_fetch(const Dims &d, const nosa_state &st, const int32_t *sel,
   setdiff_kernel<<<dim3(d.P), 64, (size_t)d.elig_words * sizeof(uint32_t), s>>>(
       d, st, sel, n_sel, phys, n_miss, list);
   if (n_wg > 0) {
-    int vpt = 8;
-    if (const char *env = getenv("NOSA_GATHER_VPT")) vpt = atoi(env);
+    const int vpt = tuning(NOSA_TUNE_GATHER_VPT) ? tuning(NOSA_TUNE_GATHER_VPT) : 8;
     if (vpt == 1)
       gather_wg_kernel<1><<<dim3(n_wg), 256, 0, s>>>(d, st.kv_host, st.kv_dev, n_miss, list);
     else if (vpt == 2)

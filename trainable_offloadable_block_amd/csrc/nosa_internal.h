@@ -8,6 +8,9 @@
 
 namespace nosa {
 
+// Current value of a nosa_set_tuning knob (0: the library's choice).
+int tuning(int knob);
+
 // --- select workspace: per-pair chunk weights e = exp(l - m_split) for each
 // head of the group, and per-(split, head) (m_split, Z_split).
 constexpr int kChunksPerSplit = 128;   // 4 waves x one 32-chunk MFMA group
@@ -17,7 +20,8 @@ struct SelectLayout {
   int subs;          // splits scored by one workgroup, one after another
   int n_wg;          // scoring workgroups per pair: ceil(n_splits / subs)
   int c_pad;         // n_splits * kChunksPerSplit
-  size_t e_off, stats_off, count_off, bytes;   // count: per-pair arrivals, zero at rest
+  // count: per-pair arrivals, zero at rest, always at offset 0
+  size_t count_off, e_off, stats_off, bytes;
 };
 SelectLayout select_layout(const Dims &d, int max_len);
 size_t select_dyn_lds(const Dims &d, const SelectLayout &lay);   // pooling's dynamic LDS
@@ -32,7 +36,7 @@ FetchLayout fetch_layout(const Dims &d);
 // (zero at rest: the last workgroup of a pair resets it).
 struct DecodeLayout {
   int blocks_per_split, n_splits;
-  size_t o_off, ml_off, count_off, bytes;
+  size_t count_off, o_off, ml_off, bytes;   // count at offset 0
 };
 DecodeLayout decode_layout(const Dims &d);
 
@@ -65,6 +69,8 @@ hipError_t launch_prefill_attend(const Dims &d, const nosa_state &st,
                                  const uint16_t *q, int T, int pos0,
                                  const int32_t *sel, const int32_t *n_sel,
                                  float *out, hipStream_t s);
+hipError_t launch_link_copy(const void *src, void *dst, size_t bytes, int n_wg,
+                            hipStream_t s);
 // n_wg > 0: copy with that many looping workgroups; 0: one per list entry
 hipError_t launch_fetch(const Dims &d, const nosa_state &st,
                         const int32_t *sel, const int32_t *n_sel,

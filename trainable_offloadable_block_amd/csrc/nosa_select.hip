@@ -17,8 +17,6 @@
 //    workgroup top-k by histogram range refinement, writes the ascending
 //    selection and clears the eligibility of every candidate left out (never
 //    re-selected by the agnostic stage).
-#include <stdlib.h>
-
 #include <algorithm>
 
 #include "nosa_select_dev.h"
@@ -63,15 +61,13 @@ SelectLayout select_layout(const Dims &d, int max_len) {
   while (s.subs < s.n_splits &&
          (long)d.P * ((s.n_splits + s.subs - 1) / s.subs + 1) > kSelectWgBudget)
     ++s.subs;
-  if (const char *env = getenv("NOSA_SELECT_SUBS")) {
-    const int v = atoi(env);
-    if (v >= 1 && v <= s.n_splits) s.subs = v;
-  }
+  if (const int v = tuning(NOSA_TUNE_SELECT_SUBS)) s.subs = min(v, s.n_splits);
   s.n_wg = (s.n_splits + s.subs - 1) / s.subs;
-  s.e_off = 0;
-  s.stats_off = ((size_t)d.P * s.c_pad * padded_group(d.G) * sizeof(float) + 255) & ~(size_t)255;
-  s.count_off = s.stats_off + (((size_t)d.P * s.n_splits * d.G * sizeof(float2) + 255) & ~(size_t)255);
-  s.bytes = s.count_off + (((size_t)d.P * sizeof(int32_t) + 255) & ~(size_t)255);
+  s.count_off = 0;
+  s.e_off = (((size_t)d.P * sizeof(int32_t) + 255) & ~(size_t)255);
+  s.stats_off = s.e_off +
+                (((size_t)d.P * s.c_pad * padded_group(d.G) * sizeof(float) + 255) & ~(size_t)255);
+  s.bytes = s.stats_off + (((size_t)d.P * s.n_splits * d.G * sizeof(float2) + 255) & ~(size_t)255);
   return s;
 }
 

@@ -350,12 +350,20 @@ class NosaLayer:
         L.check(lib.nosa_prefill_select(
             ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(scores), int(n_queries),
             int(pos0), _ptr(sel), _ptr(n_sel), self.stream), "prefill_select")
-        L.check(lib.nosa_prefill_attend(
-            ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(q), int(n_queries),
-            int(pos0), _ptr(sel), _ptr(n_sel), _ptr(out), self.stream), "prefill_attend")
+        self.prefill_attend(q, n_queries, pos0, sel, n_sel, out)
         B, Hkv = self.shape.batch, self.shape.n_kv_heads
         return (out.view(B, n_queries, self.shape.n_q_heads, HEAD_DIM),
                 sel.view(B, Hkv, n_queries, k), n_sel.view(B, Hkv, n_queries))
+
+    def prefill_attend(self, q: torch.Tensor, n_queries: int, pos0: int, sel: torch.Tensor,
+                       n_sel: torch.Tensor, out: torch.Tensor):
+        """Attention of n_queries prompt queries per sequence over the given
+        selections (sel dev int32 [B][Hkv][n_queries][k], n_sel [B][Hkv][n_queries])
+        into out (dev fp32 [B][n_queries][Hq][128])."""
+        L.check(L.lib().nosa_prefill_attend(
+            ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(q), int(n_queries),
+            int(pos0), _ptr(sel), _ptr(n_sel), _ptr(out), self.stream), "prefill_attend")
+        return out
 
     # ------------------------------------------------------------ views
     def status_bits(self) -> int:
