@@ -314,6 +314,32 @@ int nosa_sparse_decode_timed(const nosa_config *cfg, const nosa_state *st,
                              int32_t max_len_host, hipStream_t stream,
                              hipEvent_t start_event, hipEvent_t stop_event);
 
+/* Size of the scratch that nosa_sparse_decode_static uses (8 MiB). */
+#define NOSA_DECODE_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/* nosa_sparse_decode for callers that cannot allocate memory -- code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc:
+ * the same kernels, results and state changes (bit for bit), with the
+ * decode workspace taken from a scratch array built into the library
+ * instead of a caller's ws. No call allocates or frees anything.
+ *  - Each GPU holds its own NOSA_DECODE_STATIC_SCRATCH_BYTES copy of the
+ *    scratch until the process ends; its address is looked up on the first
+ *    call on that device (with that device current).
+ *  - A config whose decode workspace (nosa_workspace_bytes(cfg,
+ *    NOSA_WS_DECODE, ...)) exceeds NOSA_DECODE_STATIC_SCRATCH_BYTES returns
+ *    NOSA_ERR_WORKSPACE and enqueues nothing.
+ *  - Every call on a GPU shares that GPU's scratch, which keeps the last
+ *    call's contents; calls that overlap on one GPU (different streams, or
+ *    a graph replay beside an eager call) race and must be ordered by the
+ *    caller. A call whose per-pair arrival counters reach past the previous
+ *    call's first clears them with a small fill kernel on `stream` (no
+ *    memset node), so a call's counters always start at zero. */
+int nosa_sparse_decode_static(const nosa_config *cfg, const nosa_state *st,
+                              const uint16_t *q, const int32_t *sel,
+                              const int32_t *phys, const int32_t *n_sel,
+                              float *out, int32_t max_len_host,
+                              hipStream_t stream);
+
 /* Block scores of many prompt queries at once: the selection side of NOSA_S's
  * sparse prefill (aiwiki "NOSA", Results: NOSA_S is sparse in both phases),
  * each query scored exactly as a decode step at its own length would score it

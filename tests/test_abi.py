@@ -225,3 +225,25 @@ def test_link_copy_rejects_before_any_hip_call():
     for n_wg in (0, L.NOSA_MAX_FETCH_WORKGROUPS + 1):
         assert lib.nosa_link_copy(256, 256, 4096, n_wg, null) == L.NOSA_ERR_INVALID
     assert lib.nosa_link_copy(256, 256, 0, 8, null) == L.NOSA_OK
+
+
+def test_static_decode_rejects_before_any_hip_call():
+    """nosa_sparse_decode_static: NULL arguments, and a config whose decode
+    workspace exceeds the static scratch, come back as errors before any HIP
+    call."""
+    lib = nosa.lib()
+    null = ctypes.c_void_p(0)
+    c = _cfg()
+    st = L.NosaState()
+    for name in L.BUFFERS:
+        setattr(st, name, 256)
+    assert lib.nosa_sparse_decode_static(ctypes.byref(c), ctypes.byref(st), None, 256, 256, 256,
+                                         256, 16640, null) == L.NOSA_ERR_INVALID
+    assert lib.nosa_sparse_decode_static(ctypes.byref(c), None, 256, 256, 256, 256, 256, 16640,
+                                         null) == L.NOSA_ERR_INVALID
+    big = _cfg(batch=8192, n_q_heads=32, n_kv_heads=2, max_context=4096, k_blocks=64)
+    need = lib.nosa_workspace_bytes(ctypes.byref(big), L.NOSA_WS_DECODE, 4096)
+    assert need > L.NOSA_DECODE_STATIC_SCRATCH_BYTES
+    assert lib.nosa_sparse_decode_static(ctypes.byref(big), ctypes.byref(st), 256, 256, 256, 256,
+                                         256, 4096, null) == L.NOSA_ERR_WORKSPACE
+    assert b"STATIC_SCRATCH" in lib.nosa_last_error()

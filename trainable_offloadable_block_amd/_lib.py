@@ -32,6 +32,7 @@ NOSA_STATUS_LEN_HINT = 4
 NOSA_STATUS_SHORT_CONTEXT = 8
 
 NOSA_MAX_FETCH_WORKGROUPS = 4096
+NOSA_DECODE_STATIC_SCRATCH_BYTES = 8 << 20
 
 NOSA_EVICT_BIAS = 1
 NOSA_OFFLOAD = 2
@@ -102,6 +103,7 @@ def lib():
                                               _P, ctypes.c_size_t, _I32, _P]),
         "nosa_sparse_decode_timed": (ctypes.c_int, [cfgp, stp, _P, _P, _P, _P, _P,
                                                     _P, ctypes.c_size_t, _I32, _P, _P, _P]),
+        "nosa_sparse_decode_static": (ctypes.c_int, [cfgp, stp, _P, _P, _P, _P, _P, _I32, _P]),
         "nosa_prefill_block_scores": (ctypes.c_int, [cfgp, stp, _P, _I32, _I32, _P, _P]),
         "nosa_prefill_select": (ctypes.c_int, [cfgp, stp, _P, _I32, _I32, _P, _P, _P]),
         "nosa_prefill_attend": (ctypes.c_int, [cfgp, stp, _P, _I32, _I32, _P, _P, _P, _P]),

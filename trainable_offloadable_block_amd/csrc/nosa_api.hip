@@ -309,6 +309,24 @@ int nosa_sparse_decode_timed(const nosa_config *cfg, const nosa_state *st, const
                        start_event, stop_event);
 }
 
+int nosa_sparse_decode_static(const nosa_config *cfg, const nosa_state *st, const uint16_t *q,
+                              const int32_t *sel, const int32_t *phys, const int32_t *n_sel,
+                              float *out, int32_t max_len_host, hipStream_t stream) {
+  nosa::Dims d;
+  int rc = make_dims(cfg, &d);
+  if (!rc) rc = check_state(d, st);
+  if (!rc) rc = check_len(d, max_len_host);
+  if (rc) return rc;
+  if (!q || !sel || !phys || !n_sel || !out)
+    return fail(NOSA_ERR_INVALID, "q / sel / phys / n_sel / out is NULL");
+  const nosa::DecodeLayout lay = nosa::decode_layout(d);
+  if (lay.bytes > nosa::kDecodeStaticScratchBytes)
+    return fail(NOSA_ERR_WORKSPACE,
+                "decode workspace of this config exceeds NOSA_DECODE_STATIC_SCRATCH_BYTES; "
+                "use nosa_sparse_decode with a caller workspace");
+  return hip_result(nosa::launch_decode_static(d, *st, q, sel, phys, n_sel, out, lay, stream));
+}
+
 int nosa_prefill_block_scores(const nosa_config *cfg, const nosa_state *st, const uint16_t *q,
                               int32_t n_queries, int32_t pos0, float *out, hipStream_t stream) {
   nosa::Dims d;

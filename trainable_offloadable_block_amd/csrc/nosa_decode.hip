@@ -15,8 +15,18 @@
 //   are placed on one XCD (grid_unit).
 #include <hip/hip_ext.h>
 
+#include <mutex>
+
 #include "nosa_internal.h"
 #include "nosa_lanes.h"
+
+// Scratch of nosa_sparse_decode_static, for callers that cannot allocate: the
+// decode workspace (per-pair arrival counters at offset 0, then the split
+// partials) of every call on a GPU lives here. Each GPU the library runs on
+// holds its own copy until the process ends. Host code never uses this name
+// as an address: it takes the copy's device address from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[nosa::kDecodeStaticScratchBytes];
 
 namespace nosa {
 namespace {
@@ -525,6 +535,20 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
 
 }  // namespace
 
+// Zeroes n32 words (the arrival counters of a static-scratch call).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t *__restrict__ w, int n32) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n32) w[i] = 0u;
+}
+
+// Per device: the scratch copy's address, and how many leading bytes of it
+// are known to be zero (the counter region of the last call: a call leaves
+// its counters at zero and its partials after them).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+size_t g_scratch_zero[kMaxDevices];
+
 DecodeLayout decode_layout(const Dims &d) {
   DecodeLayout lay;
   // one round of workgroups that covers the chip: about 256 / pairs splits
@@ -568,6 +592,40 @@ hipError_t launch_decode(const Dims &d, const nosa_state &st, const uint16_t *q,
         lay.blocks_per_split, lay.n_splits, out, st.status);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_decode_static(const Dims &d, const nosa_state &st, const uint16_t *q,
+                                const int32_t *sel, const int32_t *phys, const int32_t *n_sel,
+                                float *out, const DecodeLayout &lay, hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *ptr = nullptr;
+  size_t zero_before = 0;
+  const size_t counters = lay.o_off;          // counter region, a multiple of 256 bytes
+  {
+    std::lock_guard<std::mutex> guard(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {                // first call on this device (it is current)
+      e = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+      if (e != hipSuccess) {
+        g_scratch_ptr[dev] = nullptr;
+        return e;
+      }
+      g_scratch_zero[dev] = 0;
+    }
+    ptr = g_scratch_ptr[dev];
+    zero_before = g_scratch_zero[dev];
+    g_scratch_zero[dev] = counters;
+  }
+  if (counters > zero_before) {               // counters over bytes a larger call's partials used
+    const int n32 = static_cast<int>((counters - zero_before) / 4);
+    zero_words_kernel<<<dim3((n32 + 255) / 256), 256, 0, s>>>(
+        reinterpret_cast<uint32_t *>(static_cast<char *>(ptr) + zero_before), n32);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_decode(d, st, q, sel, phys, n_sel, out, ptr, lay, s);
 }
 
 }  // namespace nosa

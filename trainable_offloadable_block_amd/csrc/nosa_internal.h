@@ -76,6 +76,14 @@ hipError_t launch_fetch(const Dims &d, const nosa_state &st,
                         const int32_t *sel, const int32_t *n_sel,
                         int32_t *phys, int32_t *n_miss, void *ws,
                         const FetchLayout &lay, hipStream_t s, int n_wg = 0);
+// Size of the static scratch that nosa_sparse_decode_static uses in place of
+// a caller's workspace.
+constexpr size_t kDecodeStaticScratchBytes = size_t(8) << 20;
+static_assert(kDecodeStaticScratchBytes == NOSA_DECODE_STATIC_SCRATCH_BYTES,
+              "static scratch size differs from the header's");
+hipError_t launch_decode_static(const Dims &d, const nosa_state &st, const uint16_t *q,
+                                const int32_t *sel, const int32_t *phys, const int32_t *n_sel,
+                                float *out, const DecodeLayout &lay, hipStream_t s);
 // With ev_start / ev_stop, the launch records the kernel's own start and end
 // into them (hipExtLaunchKernel).
 hipError_t launch_decode(const Dims &d, const nosa_state &st,

@@ -302,6 +302,18 @@ class NosaLayer:
             handles.append(ctypes.c_void_p(ev.cuda_event))
         L.check(L.lib().nosa_sparse_decode_timed(*args, *handles), "sparse_decode_timed")
 
+    def decode_static(self, q: torch.Tensor, sel=None, phys=None, n_sel=None):
+        """decode() through nosa_sparse_decode_static: the library's own
+        scratch in place of this layer's decode workspace (nothing
+        allocated by the call)."""
+        sel = self.sel if sel is None else sel
+        if phys is None:
+            phys = self.phys if self.shape.offload else sel
+        n_sel = self.n_sel if n_sel is None else n_sel
+        L.check(L.lib().nosa_sparse_decode_static(
+            ctypes.byref(self.cfg), ctypes.byref(self.state), _ptr(q), _ptr(sel), _ptr(phys),
+            _ptr(n_sel), _ptr(self.out), self.max_len, self.stream), "sparse_decode_static")
+
     def step(self, k_new, v_new, q, want_kind=False, want_qscore=False):
         """append + select (one launch) -> fetch -> decode, all enqueued on
         one stream."""
