@@ -70,6 +70,11 @@ def parse():
                     help="skip the GQA-16, 96-block leg (beyond the five configs)")
     ap.add_argument("--no-tiny", action="store_true",
                     help="skip the tiny 4K single-layer leg")
+    ap.add_argument("--clock-warm", type=float, default=CLOCK_WARM_S, metavar="S",
+                    help="seconds of untimed decode launches before each timed region")
+    ap.add_argument("--phase-clocks", action="store_true",
+                    help="phase breakdown of the append + select and decode launches from the "
+                         "timing build's in-kernel clocks (NOSA_LIBRARY=.../libnosa_clocks.so)")
     ap.add_argument("--only-link", action="store_true",
                     help="run only the host-link ceiling probe and print its JSON")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -981,8 +986,138 @@ def warm_leg(dev, workers, W=8, K=120):
             "breakdown_us": m["breakdown"]}
 
 
+def phase_clocks(dev, workers, R=8, W=12, samples=24):
+    """Phase breakdown of the fused append + select and the decode launches
+    on the 16K stack, from the timing build's in-kernel clocks (load it with
+    NOSA_LIBRARY=trainable_offloadable_block_amd/libnosa_clocks.so). Every
+    other sampled step stops after the last layer's append + select (its
+    clocks copied out, the earlier launches having run back to back); the
+    others run whole and copy out the last layer's decode clocks. Times in
+    us from the launch's first workgroup start (100 MHz counter)."""
+    import ctypes
+    import numpy as np
+    import torch
+    from synth import WORKLOADS
+    from trainable_offloadable_block_amd import LayerShape
+    from trainable_offloadable_block_amd import _lib as L
+    lib = L.lib()
+    if not hasattr(lib, "nosa_phase_clocks_decode"):
+        raise SystemExit("--phase-clocks needs the timing build: python -m "
+                         "trainable_offloadable_block_amd.build --phase-clocks, then "
+                         "NOSA_LIBRARY=trainable_offloadable_block_amd/libnosa_clocks.so")
+    readers = {}
+    for name in ("append_select", "decode"):
+        fn = getattr(lib, f"nosa_phase_clocks_{name}")
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        readers[name] = fn
+    NP, ROWS, SLOTS = 512, 40, 16
+    wl = WORKLOADS[2]
+    P = wl.batch * wl.n_kv_heads
+    n_tok = W + samples
+    shape = LayerShape(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_sink_blocks,
+                       wl.window_tokens, wl.k_blocks, wl.k_q_blocks, wl.k_e_blocks,
+                       wl.context + n_tok)
+    layers, inputs = [], []
+    with cf.ThreadPoolExecutor(workers) as pool:
+        for li in range(R):
+            layers.append(build_layer(wl, li, shape, pool))
+            inputs.append(step_inputs(wl, li, n_tok, pool, dev))
+    torch.cuda.synchronize()
+
+    def read(name):
+        buf = np.zeros(NP * ROWS * SLOTS, dtype=np.uint64)
+        L.check(readers[name](ctypes.c_void_p(buf.ctypes.data), buf.nbytes, 1), name)
+        return buf.reshape(NP, ROWS, SLOTS)[:P].astype(np.float64)
+
+    for t in range(W):
+        for li, ly in enumerate(layers):
+            q, kn, vn = (x[t] for x in inputs[li])
+            ly.append_select(kn, vn, q, want_kind=False)
+            ly.decode(q)
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < CLOCK_WARM_S:
+        for _ in range(16):
+            for li, ly in enumerate(layers):
+                ly.decode(inputs[li][0][W - 1])
+        torch.cuda.synchronize()
+    sel_runs, dec_runs = [], []
+    for sidx in range(samples):
+        t = W + sidx
+        for name in readers:
+            readers[name](None, 0, 1)
+        for li, ly in enumerate(layers):
+            q, kn, vn = (x[t] for x in inputs[li])
+            ly.append_select(kn, vn, q, want_kind=False)
+            if li == R - 1 and sidx % 2 == 0:
+                torch.cuda.synchronize()
+                sel_runs.append(read("append_select"))
+            ly.decode(q)
+        torch.cuda.synchronize()
+        if sidx % 2 == 1:
+            dec_runs.append(read("decode"))
+
+    def us(a, t0):
+        return (a - t0) / 100.0
+
+    def stat(v):
+        v = np.asarray(v, dtype=float)
+        return {"mean": round(float(v.mean()), 2), "max": round(float(v.max()), 2)}
+
+    sel = {k: [] for k in ("start", "score_done", "score_done_max", "score_landed",
+                           "append_done", "append_done_max", "append_landed", "last_arrival",
+                           "last_arrival_max", "pool_loads", "pool_factors", "pool_chunk_scores",
+                           "pool_stage1", "pool_stage2", "pool_list", "pool_eligibility",
+                           "pool_eligibility_max", "end")}
+    for a in sel_runs:
+        rows = np.nonzero((a[:, :, 0] > 0).any(axis=0))[0]
+        n_wg = int(rows[rows < ROWS - 1].max())          # the append workgroup's row
+        t0 = a[:, :n_wg + 1, 0].min()
+        sel["start"].append(stat(us(a[:, :n_wg + 1, 0], t0))["max"])
+        sel["score_done"].append(float(us(a[:, :n_wg, 1], t0).mean()))
+        sel["score_done_max"].append(float(us(a[:, :n_wg, 1], t0).max()))
+        sel["score_landed"].append(float(us(a[:, :n_wg, 2], t0).mean()))
+        sel["append_done"].append(float(us(a[:, n_wg, 1], t0).mean()))
+        sel["append_done_max"].append(float(us(a[:, n_wg, 1], t0).max()))
+        sel["append_landed"].append(float(us(a[:, n_wg, 2], t0).mean()))
+        arr = us(a[:, :n_wg, 3].max(axis=1), t0)            # the pool's start, per pair
+        sel["last_arrival"].append(float(arr.mean()))
+        sel["last_arrival_max"].append(float(arr.max()))
+        for k, slot in (("pool_loads", 4), ("pool_factors", 5), ("pool_chunk_scores", 6),
+                        ("pool_stage1", 7), ("pool_stage2", 8), ("pool_list", 9),
+                        ("pool_eligibility", 10)):
+            sel[k].append(float(us(a[:, ROWS - 1, slot], t0).mean()))
+        sel["pool_eligibility_max"].append(float(us(a[:, ROWS - 1, 10], t0).max()))
+        sel["end"].append(float(max(us(a[:, ROWS - 1, 11], t0).max(),
+                                    us(a[:, n_wg, 2], t0).max())))
+    dec = {k: [] for k in ("start", "wave_loop_end_mean", "wave_loop_end_max", "lds_merge",
+                           "published", "last_arrival", "merge_end", "slowest_pair_vs_median")}
+    for a in dec_runs:
+        rows = np.nonzero((a[:, :, 0] > 0).any(axis=0))[0]
+        ns = int(rows.max()) + 1
+        t0 = a[:, :ns, 0].min()
+        dec["start"].append(float(us(a[:, :ns, 0], t0).max()))
+        loops = us(a[:, :ns, 6:10], t0)
+        dec["wave_loop_end_mean"].append(float(loops.mean()))
+        dec["wave_loop_end_max"].append(float(loops.max()))
+        dec["lds_merge"].append(float(us(a[:, :ns, 2], t0).mean()))
+        dec["published"].append(float(us(a[:, :ns, 3], t0).mean()))
+        arr = us(a[:, :ns, 4].max(axis=1), t0)
+        dec["last_arrival"].append(float(arr.mean()))
+        dec["merge_end"].append(float(us(a[:, :ns, 5].max(axis=1), t0).max()))
+        dec["slowest_pair_vs_median"].append(float(arr.max() - np.median(arr)))
+    out = {"workload": wl.name, "layers": R, "sampled_launches": {"append_select": len(sel_runs),
+                                                                 "decode": len(dec_runs)},
+           "unit": "us from the launch's first workgroup start; mean over sampled launches",
+           "append_select": {k: round(float(np.mean(v)), 2) for k, v in sel.items()},
+           "decode": {k: round(float(np.mean(v)), 2) for k, v in dec.items()}}
+    return out
+
+
 def main():
     args = parse()
+    global CLOCK_WARM_S
+    CLOCK_WARM_S = args.clock_warm
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the NOSA "
               "decode path has no cross-GPU step; pairs would shard by sequence "
@@ -1003,6 +1138,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     workers = min(16, len(os.sched_getaffinity(0)))
+    if args.phase_clocks:
+        print(json.dumps(phase_clocks(dev, workers)), flush=True)
+        return
     if args.only_link:
         print(json.dumps(host_link_peak(dev)), flush=True)
         return

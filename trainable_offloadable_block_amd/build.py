@@ -5,7 +5,8 @@ against the HIP runtime that PyTorch ships, found by name
 (``libamdhip64.so``), so a process that has imported torch uses exactly one
 HIP runtime for torch's memory and for these kernels.
 
-Usage: python -m trainable_offloadable_block_amd.build  (or build()).
+Usage: python -m trainable_offloadable_block_amd.build  (or build());
+``--phase-clocks`` builds the timing variant libnosa_clocks.so instead.
 """
 
 from __future__ import annotations
@@ -88,5 +89,18 @@ def build(verbose: bool = True, out_path: str = LIB_PATH, defines=()) -> str:
     return out_path
 
 
+CLOCKS_LIB_PATH = os.path.join(PKG, "libnosa_clocks.so")
+
+
+def build_phase_clocks(verbose: bool = True) -> str:
+    """The timing build: the same library with phase clocks in the append +
+    select and decode kernels (NOSA_PHASE_CLOCKS), as libnosa_clocks.so. Load
+    it with NOSA_LIBRARY=<path> (bench.py --phase-clocks)."""
+    return build(verbose, CLOCKS_LIB_PATH, defines=("NOSA_PHASE_CLOCKS",))
+
+
 if __name__ == "__main__":
-    build()
+    if "--phase-clocks" in sys.argv[1:]:
+        build_phase_clocks()
+    else:
+        build()

@@ -5,14 +5,17 @@
 // grid (scoring workgroups + 1, pairs), 256 threads:
 //  - the last workgroup of a pair appends the token (K, V, ring, eviction
 //    score, and the compressed key, chunk score and block score the token
-//    completes, the last two stored device-coherently);
+//    completes);
 //  - the others score their splits (one or several each) as the select
-//    kernel does (every chunk but the newest, which the append may be
-//    writing), in parallel;
-//  - all arrive on the pair's counter; the last one scores the newest chunk,
-//    pools and selects (block scores read device-coherently);
-//  - the last pair of a sequence to finish advances the sequence's length:
-//    by then every workgroup of the sequence has read it.
+//    kernel does, in parallel, and arrive on the pair's counter; the last of
+//    them pools and selects. The selection does not wait for the append:
+//    the only thing it needs from it is the key of a chunk the token
+//    completes, which the split holding that chunk builds itself from the
+//    key ring and the new key (the same bits the append stores); the block
+//    score the append may finalise belongs to a window block, which is
+//    never a candidate;
+//  - every pool and every append of a sequence arrive on the sequence's
+//    counter once they have read its length; the last of them advances it.
 #include "nosa_append_dev.h"
 #include "nosa_select_dev.h"
 
@@ -20,17 +23,18 @@ namespace nosa {
 namespace {
 
 template <bool MULTI>
-__global__ __launch_bounds__(kScoreThreads) void append_select_kernel(
+__global__ __launch_bounds__(kScoreThreads, 4) void append_select_kernel(
     Dims d, nosa_state st, const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
     const uint16_t *__restrict__ q, float *ws_e, float *ws_stats, int32_t *ws_count, int c_pad,
     int n_splits, int subs, int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
     uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
   int wg, p;
   grid_unit(wg, p);
+  NOSA_PHASE(p, wg, 0);
   const int n_wg = gridDim.x - 1;
   const int b = p / d.Hkv, g = p % d.Hkv;
-  // the append's LDS and the pooling's share the dynamic region: the append
-  // workgroup pools (if it arrives last) only after its append is done
+  // the append's LDS and the pooling's share the dynamic region (the append
+  // workgroup never pools)
   extern __shared__ __align__(16) uint8_t dyn_sh[];
   AppendLds &ash = *reinterpret_cast<AppendLds *>(dyn_sh);
   __shared__ int sm_last;
@@ -39,29 +43,38 @@ __global__ __launch_bounds__(kScoreThreads) void append_select_kernel(
   const int L = ok ? pos + 1 : pos;
   if (wg == n_wg) {                                       // uniform
     append_pair<kScoreThreads>(d, st, k_new, v_new, b, g, pos, true, ash);
+    NOSA_PHASE(p, wg, 1);
   } else {
-    score_splits<MULTI>(d, st.ckey, q, L, ws_e, ws_stats, c_pad, n_splits, subs, wg, p);
+    score_splits<MULTI>(d, st, q, L, ws_e, ws_stats, c_pad, n_splits, subs, wg, p,
+                        ok ? k_new : nullptr);
+    NOSA_PHASE(p, wg, 1);
+    __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
+    __syncthreads();
+    NOSA_PHASE(p, wg, 2);
+    if (threadIdx.x == 0)
+      sm_last = __hip_atomic_fetch_add(&ws_count[p], 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT) == n_wg - 1;
+    __syncthreads();
+    NOSA_PHASE(p, wg, 3);
+    if (!sm_last) return;
+    pool_select(d, st, L, ws_e, ws_stats, c_pad, n_splits, sel, n_sel, kind_out, dbg, p);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&ws_count[p], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
-  __syncthreads();
-  if (threadIdx.x == 0)
-    sm_last = __hip_atomic_fetch_add(&ws_count[p], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              n_wg;                      // n_wg score workgroups + the append
-  __syncthreads();
-  if (!sm_last) return;
-  pool_select(d, st, q, L, ws_e, ws_stats, c_pad, n_splits, sel, n_sel, kind_out, dbg, p);
   if (threadIdx.x == 0) {
-    __hip_atomic_store(&ws_count[p], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // every workgroup of this pair has read the length; the last pair of
-    // the sequence advances it (and leaves the sequence's counter at zero)
+    // every workgroup of this pair that reads the length has read it (the
+    // pool's scoring peers arrived before it); the last of the sequence's
+    // pools and appends advances it (and leaves the counter at zero)
     const int old = __hip_atomic_fetch_add(&st.arrive[b], 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
-    if (old == d.Hkv - 1) {
+    if (old == 2 * d.Hkv - 1) {
       __hip_atomic_store(&st.arrive[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (ok) __hip_atomic_store(&st.seq_len[b], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else atomicOr(st.status, NOSA_STATUS_CAPACITY);
     }
   }
+  if (wg == n_wg) NOSA_PHASE(p, wg, 2);
+  else NOSA_PHASE(p, kPhasePoolRow, 11);
 }
 
 }  // namespace
@@ -83,3 +96,7 @@ hipError_t launch_append_select(const Dims &d, const nosa_state &st, const uint1
 }
 
 }  // namespace nosa
+
+#ifdef NOSA_PHASE_CLOCKS
+NOSA_PHASE_READER(nosa_phase_clocks_append_select)
+#endif

@@ -19,6 +19,7 @@
 
 #include "nosa_internal.h"
 #include "nosa_lanes.h"
+#include "nosa_phase.h"
 
 // Scratch of nosa_sparse_decode_static, for callers that cannot allocate: the
 // decode workspace (per-pair arrival counters at offset 0, then the split
@@ -325,6 +326,7 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
     uint32_t *status) {
   int split, p;
   grid_unit(split, p);
+  NOSA_PHASE(p, split, 0);
   const int b = p / d.Hkv, g = p % d.Hkv;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
   const int h = l & 15, lg = l >> 4;
@@ -402,6 +404,7 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
     process_half(B, qop, qscale, bscale, L, lg, m_run, l_run, o);
   }
 
+  NOSA_PHASE_WAVE(p, split, 6 + w);
   if (bad && l == 0) atomicOr(status, NOSA_STATUS_BAD_SEL);
   // lane (h, lg): head h's running max, its keys' partial sum, and
   // O^T[16*dt + 4*lg + i][h]; merge the 4 waves in LDS
@@ -415,6 +418,7 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
 #pragma unroll
     for (int i = 0; i < 4; ++i) sm_o[w][h][16 * dt + 4 * lg + i] = o[dt][i];
   __syncthreads();
+  NOSA_PHASE(p, split, 2);
   if (n_splits == 1 && (d.G == 4 || d.G == 8 || d.G == 16)) {   // uniform
     // the pair's only split: normalise and write, a float4 (one head) each
     float *ob = out + ((size_t)b * d.Hq + g * d.G) * kHeadDim;
@@ -517,10 +521,12 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   }
   __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
   __syncthreads();
+  NOSA_PHASE(p, split, 3);
   if (threadIdx.x == 0)
     sm_last = __hip_atomic_fetch_add(&ws_count[p], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
               n_splits - 1;
   __syncthreads();
+  NOSA_PHASE(p, split, 4);
   if (!sm_last) return;
   if (d.G == 4 || d.G == 8)
     merge_splits_v<1>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
@@ -531,6 +537,7 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   else
     merge_splits<8>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
   if (threadIdx.x == 0) __hip_atomic_store(&ws_count[p], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  NOSA_PHASE(p, split, 5);
 }
 
 }  // namespace
@@ -629,3 +636,7 @@ hipError_t launch_decode_static(const Dims &d, const nosa_state &st, const uint1
 }
 
 }  // namespace nosa
+
+#ifdef NOSA_PHASE_CLOCKS
+NOSA_PHASE_READER(nosa_phase_clocks_decode)
+#endif

@@ -28,7 +28,7 @@ namespace {
 // splits and arrives on the pair's counter once its results have landed; the
 // last one pools and selects, then resets the counter (zero at rest).
 template <bool MULTI>
-__global__ __launch_bounds__(kScoreThreads) void select_kernel(
+__global__ __launch_bounds__(kScoreThreads, 4) void select_kernel(
     Dims d, nosa_state st, const uint16_t *__restrict__ q, float *ws_e, float *ws_stats,
     int32_t *ws_count, int c_pad, int n_splits, int subs, int32_t *__restrict__ sel,
     int32_t *__restrict__ n_sel, uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kScoreThreads) void select_kernel(
   grid_unit(wg, p);
   __shared__ int sm_last;
   const int L = st.seq_len[p / d.Hkv];
-  score_splits<MULTI>(d, st.ckey, q, L, ws_e, ws_stats, c_pad, n_splits, subs, wg, p);
+  score_splits<MULTI>(d, st, q, L, ws_e, ws_stats, c_pad, n_splits, subs, wg, p);
   __builtin_amdgcn_s_waitcnt(0);          // this thread's stores have landed
   __syncthreads();
   if (threadIdx.x == 0)
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kScoreThreads) void select_kernel(
               (int)gridDim.x - 1;
   __syncthreads();
   if (!sm_last) return;
-  pool_select(d, st, q, L, ws_e, ws_stats, c_pad, n_splits, sel, n_sel, kind_out, dbg, p);
+  pool_select(d, st, L, ws_e, ws_stats, c_pad, n_splits, sel, n_sel, kind_out, dbg, p);
   if (threadIdx.x == 0) __hip_atomic_store(&ws_count[p], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -6,6 +6,7 @@
 
 #include "nosa_internal.h"
 #include "nosa_lanes.h"
+#include "nosa_phase.h"
 
 namespace nosa {
 namespace {
@@ -99,17 +100,35 @@ __device__ __forceinline__ void score_load(const Dims &d, const uint16_t *__rest
 }
 
 // Chunks scored by the split workgroups at length L: every complete chunk
-// (at most c_pad) except the newest, which the pair's last workgroup scores
-// (the append of the same launch may be writing it).
+// (at most c_pad).
 __device__ inline int split_chunks(const Dims &d, int L, int c_pad) {
-  return max(min(min(chunks_for(L), d.C_max), c_pad) - 1, 0);
+  return max(min(min(chunks_for(L), d.C_max), c_pad), 0);
+}
+
+// The newest chunk's key when the token appended in the same launch completes
+// it (the append may still be writing it to memory): built from the key
+// ring (the chunk's 31 earlier keys) and the new key, the bits the append
+// stores. ring: the pair's [32][128] ring; k_new: the pair's new key; pos:
+// the new token's position. Threads t < 128 return dim t.
+__device__ inline uint16_t fresh_key_dim(const uint16_t *__restrict__ ring,
+                                         const uint16_t *__restrict__ k_new, int pos, int t) {
+  const uint16_t kb = k_new[t];
+  return mean32_bf16([&](int j) -> uint16_t {
+    const int tok = pos - (kPoolKernel - 1) + j;
+    return tok == pos ? kb : ring[(tok % kPoolKernel) * kHeadDim + t];
+  });
 }
 
 // Split `split` of pair p: logits of the group against the split's
 // compressed keys among chunks [0, C), published with device-coherent stores.
+// fresh_ring: when not NULL, chunk C - 1 was just completed by an append in
+// the same launch (position pos, new key fresh_k): the split holding it takes
+// that chunk's key from fresh_key_dim instead of memory.
 __device__ __forceinline__ void score_compute(const Dims &d, int C, ScoreIn &in, float *ws_e,
                                               float *ws_stats, int c_pad, int n_splits,
-                                              int split, int p) {
+                                              int split, int p,
+                                              const uint16_t *__restrict__ fresh_ring,
+                                              const uint16_t *__restrict__ fresh_k, int pos) {
   const int c0 = split * kChunksPerSplit;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int h = l & 15, lg = l >> 4;
@@ -122,6 +141,18 @@ __device__ __forceinline__ void score_compute(const Dims &d, int C, ScoreIn &in,
       put(&stats[2 * threadIdx.x + 1], 0.0f);
     }
     return;
+  }
+  if (fresh_ring && C - 1 < c0 + kChunksPerSplit) {               // uniform: this split holds it
+    __shared__ __align__(16) uint16_t fresh_sh[kHeadDim];
+    if (threadIdx.x < kHeadDim) fresh_sh[threadIdx.x] = fresh_key_dim(fresh_ring, fresh_k, pos, threadIdx.x);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      if (cg + tile_row(l & 15, t) == C - 1) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          in.kv[t][s] = *reinterpret_cast<const uint4 *>(&fresh_sh[8 * lg + 32 * s]);
+      }
   }
   const uint4 (&qv)[4] = in.qv;
   const uint4 (&kv)[2][4] = in.kv;
@@ -197,23 +228,31 @@ constexpr int kSelectWgBudget = 1024;   // resident workgroups of one round (4 p
 // one after another: the newest chunk left out (split_chunks). The first
 // split's loads go out before the length is used. MULTI = false compiles
 // the one-split case alone (subs = 1), without the loop's code.
+// k_new: when not NULL, the step's new keys (dev [P][128]) of an append in
+// the same launch; a chunk that token completes is then built from the key
+// ring (score_compute).
 template <bool MULTI>
-__device__ __forceinline__ void score_splits(const Dims &d, const uint16_t *__restrict__ ckey,
+__device__ __forceinline__ void score_splits(const Dims &d, const nosa_state &st,
                                              const uint16_t *__restrict__ q, int L, float *ws_e,
                                              float *ws_stats, int c_pad, int n_splits, int subs,
-                                             int ws, int p) {
+                                             int ws, int p,
+                                             const uint16_t *__restrict__ k_new = nullptr) {
   const int split0 = MULTI ? ws * subs : ws;       // < n_splits: ceil(n_splits / subs) groups
   ScoreIn in;
-  score_load(d, ckey, q, split0, p, in);
+  score_load(d, st.ckey, q, split0, p, in);
   const int C = split_chunks(d, L, c_pad);
-  score_compute(d, C, in, ws_e, ws_stats, c_pad, n_splits, split0, p);
+  const bool fresh = k_new != nullptr && L >= kPoolKernel && (L - kPoolKernel) % kPoolStride == 0 &&
+                     C == chunks_for(L);
+  const uint16_t *fring = fresh ? st.tail_keys + (size_t)p * kPoolKernel * kHeadDim : nullptr;
+  const uint16_t *fk = fresh ? k_new + (size_t)p * kHeadDim : nullptr;
+  score_compute(d, C, in, ws_e, ws_stats, c_pad, n_splits, split0, p, fring, fk, L - 1);
   if (!MULTI) return;
   for (int j = 1; j < subs; ++j) {                 // uniform
     const int split = split0 + j;
     if (split >= n_splits) break;
     __syncthreads();                               // the last split's reductions are read
-    score_load_keys(d, ckey, split, p, in);        // the query rows stay
-    score_compute(d, C, in, ws_e, ws_stats, c_pad, n_splits, split, p);
+    score_load_keys(d, st.ckey, split, p, in);     // the query rows stay
+    score_compute(d, C, in, ws_e, ws_stats, c_pad, n_splits, split, p, fring, fk, L - 1);
   }
 }
 
@@ -447,6 +486,7 @@ __device__ __forceinline__ void select_stages(const Dims &d, int p, int n_cand, 
     wg_topk(kq, d.k_q, d.n_sink, kind, NOSA_KIND_QUERY, tk);
     __syncthreads();
   }
+  NOSA_PHASE(p, kPhasePoolRow, 7);
   if (do_e) {
     uint64_t ke[R];
 #pragma unroll
@@ -461,7 +501,7 @@ __device__ __forceinline__ void select_stages(const Dims &d, int p, int n_cand, 
 }
 
 constexpr int kMaxCandPerThread = (kMaxContext / kBlock) / kTopkThreads;   // 16
-constexpr int kLoadBatch = 8;     // chunk-weight float4 loads in flight per thread
+constexpr int kLoadBatch = 10;    // chunk-weight float4 loads in flight per thread
 constexpr int kStatBatches = 4;   // split statistics loaded early: 16 splits each
 
 // Both stages, the ascending selection list and the eligibility update of
@@ -494,9 +534,43 @@ __device__ __forceinline__ void finish_select(const Dims &d, const nosa_state &s
                                        dbg, tk);
   }
   __syncthreads();
+  NOSA_PHASE(p, kPhasePoolRow, 8);
 
-  // 4. ascending selection list: ballot + prefix count per 256 blocks
-  {
+  // 4. ascending selection list: ballot + prefix count per 256 blocks (up
+  // to 512 blocks, two adjacent blocks per thread and one prefix)
+  if (nb <= 2 * kTopkThreads) {                                       // uniform
+    int32_t *sp = sel + (size_t)p * d.k;
+    uint8_t *kp = kind_out ? kind_out + (size_t)p * d.k : nullptr;
+    const int b0 = 2 * t;
+    const uint8_t k0 = b0 < nb ? kind[b0] : (uint8_t)NOSA_KIND_NONE;
+    const uint8_t k1 = b0 + 1 < nb ? kind[b0 + 1] : (uint8_t)NOSA_KIND_NONE;
+    const int mine = (k0 != NOSA_KIND_NONE ? 1 : 0) + (k1 != NOSA_KIND_NONE ? 1 : 0);
+    const uint32_t incl = wave_incl_scan(static_cast<uint32_t>(mine));
+    if (lane == 63) cnt_sh[0][w] = static_cast<int>(incl);
+    __syncthreads();
+    int off = static_cast<int>(incl) - mine, tot = 0;
+#pragma unroll
+    for (int ww = 0; ww < kTopkThreads / 64; ++ww) {
+      if (ww < w) off += cnt_sh[0][ww];
+      tot += cnt_sh[0][ww];
+    }
+    if (k0 != NOSA_KIND_NONE) {
+      if (off < d.k) {
+        sp[off] = b0;
+        if (kp) kp[off] = k0;
+      }
+      ++off;
+    }
+    if (k1 != NOSA_KIND_NONE && off < d.k) {
+      sp[off] = b0 + 1;
+      if (kp) kp[off] = k1;
+    }
+    for (int j = tot + t; j < d.k; j += kTopkThreads) {
+      sp[j] = -1;
+      if (kp) kp[j] = NOSA_KIND_NONE;
+    }
+    if (t == 0) n_sel[p] = min(tot, d.k);
+  } else {
     int32_t *sp = sel + (size_t)p * d.k;
     uint8_t *kp = kind_out ? kind_out + (size_t)p * d.k : nullptr;
     int running = 0;
@@ -527,6 +601,7 @@ __device__ __forceinline__ void finish_select(const Dims &d, const nosa_state &s
     }
     if (t == 0) n_sel[p] = min(running, d.k);
   }
+  NOSA_PHASE(p, kPhasePoolRow, 9);
 
   // 5. eligibility: a candidate outside the selection is out for good
   if (n_cand > 0) {
@@ -539,30 +614,67 @@ __device__ __forceinline__ void finish_select(const Dims &d, const nosa_state &s
       if ((lane & 31) == 0 && clear) el[bb >> 5] = el_sh[bb >> 5] & ~clear;
     }
   }
+  NOSA_PHASE(p, kPhasePoolRow, 10);
+}
+
+// Chunk scores of one batch of chunk-weight float4s (eb[u] = float4 k0 + t +
+// 256 u of the chunk-major [c][GP] array): each lane takes the dot product
+// of its 4 heads with their split factors, the GP / 4 adjacent lanes of a
+// chunk add theirs with DPP quad exchanges, and the chunk's first lane
+// stores a_c. Branch-free up to the stores, so the LDS reads of all of a
+// thread's float4s go out together.
+template <int GP>
+__device__ __forceinline__ void chunk_scores(const float4 (&eb)[kLoadBatch], int k0, int n4,
+                                             int n_splits, const float *f_sh, float *a_sh) {
+  constexpr int LPC = GP / 4;                    // lanes per chunk: 1, 2, 4
+  constexpr int kHalf = kLoadBatch / 2;          // float4s whose factors are read together
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u0 = 0; u0 < kLoadBatch; u0 += kHalf) {
+    float a[kHalf];
+#pragma unroll
+    for (int v = 0; v < kHalf; ++v) {
+      const int u = u0 + v;
+      const int k4 = k0 + t + kTopkThreads * u;
+      const int c = k4 / LPC, h0 = 4 * (k4 % LPC);
+      const int split = min(c / kChunksPerSplit, n_splits - 1);
+      const float4 f = *reinterpret_cast<const float4 *>(f_sh + split * GP + h0);
+      float x = eb[u].x * f.x;
+      x = fmaf(eb[u].y, f.y, x);
+      x = fmaf(eb[u].z, f.z, x);
+      a[v] = fmaf(eb[u].w, f.w, x);
+    }
+#pragma unroll
+    for (int v = 0; v < kHalf; ++v) {
+      if (LPC >= 2) a[v] += dpp_f32<0xB1>(a[v]);   // lane ^ 1
+      if (LPC >= 4) a[v] += dpp_f32<0x4E>(a[v]);   // lane ^ 2
+    }
+#pragma unroll
+    for (int v = 0; v < kHalf; ++v) {
+      const int k4 = k0 + t + kTopkThreads * (u0 + v);
+      if (k4 < n4 && k4 % LPC == 0) a_sh[k4 / LPC] = a[v];
+    }
+  }
 }
 
 // Pooling and both stages for pair p, run by the pair's last score
 // workgroup once every split has published (so the chunk weights and split
-// statistics are read with device-coherent loads).
-// L is the pair's sequence length (after this step's append).
-__device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
-                                            const uint16_t *__restrict__ q, int L_in,
+// statistics are read with device-coherent loads); the splits cover every
+// complete chunk. L is the pair's sequence length (after this step's append).
+__device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st, int L_in,
                                             const float *ws_e, const float *ws_stats,
                                             int c_pad, int n_splits, int32_t *sel,
                                             int32_t *n_sel, uint8_t *kind_out, float *dbg,
                                             int p) {
   const int Gp = padded_group(d.G);
-  const int b = p / d.Hkv;
   extern __shared__ __align__(16) uint8_t smem[];
   float *f_sh = reinterpret_cast<float *>(smem);                            // [n_splits][Gp]
   float *a_sh = f_sh + n_splits * Gp;                                       // [c_pad]
   uint32_t *el_sh = reinterpret_cast<uint32_t *>(a_sh + c_pad);             // [elig_words]
   uint8_t *kind = reinterpret_cast<uint8_t *>(el_sh + d.elig_words);        // [NB_max]
   __shared__ TopkLds tk;
-  __shared__ float lnew_sh[kMaxGroup], wlast_sh[kMaxGroup];
 
   const int t = threadIdx.x;
-  const int w = t >> 6, lane = t & 63;
 
   // 0. issue the global loads together, bounded by the buffers' extents
   // rather than the length (which is itself being loaded), so the kernel
@@ -600,43 +712,11 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
   const int nb = blocks_for(L);
   const int win_lo = max(d.n_sink, nb - d.n_win);
   const int n_cand = max(0, win_lo - d.n_sink);
-  const int Cs = max(C - 1, 0);          // chunks scored by the splits; C - 1 here
-  const int used = (Cs + kChunksPerSplit - 1) / kChunksPerSplit;
+  const int used = (C + kChunksPerSplit - 1) / kChunksPerSplit;
   const bool do_q = d.k_q > 0 && n_cand > 0, do_e = d.k_e_dyn > 0 && n_cand > 0;
-  const int n4 = do_q ? Cs * Gp / 4 : 0;
+  const int n4 = do_q ? C * Gp / 4 : 0;
   const bool have0 = t < n_cand;
   const float e0 = (do_e && have0) ? e0_raw : 0.0f;
-  // the newest chunk (C - 1): the group's logits against it on wave 0, with
-  // the split kernels' MFMA (its row in A-row 0, read device-coherently:
-  // the append of the same launch may have just written it)
-  const bool last_q = do_q && C >= 1;                          // uniform
-  if (last_q && w == 0) {
-    const int h = lane & 15, lg = lane >> 4;
-    const __amdgpu_buffer_rsrc_t kr =
-        make_rsrc(st.ckey + ((size_t)p * d.C_max + (C - 1)) * kHeadDim, kHeadDim * 2);
-    uint4 av[4], qv[4];
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      av[s4] = make_uint4(0, 0, 0, 0);
-      qv[s4] = make_uint4(0, 0, 0, 0);
-    }
-    if (h == 0) {
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        av[s4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               kr, 2 * (8 * lg + 32 * s4), 0, kCoherent));
-    }
-    if (h < d.G) {
-      const uint16_t *qh = q + ((size_t)b * d.Hq + (p % d.Hkv) * d.G + h) * kHeadDim + 8 * lg;
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) qv[s4] = *reinterpret_cast<const uint4 *>(qh + 32 * s4);
-    }
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) acc = mfma16x16x32(as_bf16x8(av[s4]), as_bf16x8(qv[s4]), acc);
-    // D row 0 sits in lanes 0..15 (element 0): head = lane
-    if (lane < kMaxGroup) lnew_sh[lane] = acc[0] * 0.08838834764831845f;   // 1/sqrt(128)
-  }
   for (int i = t; i < d.elig_words; i += kTopkThreads)
     el_sh[i] = st.eligible[(size_t)p * d.elig_words + i];
   for (int bb = t; bb < nb; bb += kTopkThreads)
@@ -647,9 +727,9 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
     tk.hist[1][t + kTopkThreads * i] = 0;
   }
 
-  if (last_q) __syncthreads();                                 // lnew_sh is set
+  NOSA_PHASE(p, kPhasePoolRow, 4);
   // 1. per-split factors exp(m_split - M) / Z of each head's softmax over
-  // all complete chunks, the newest included (0 for the padding heads)
+  // all complete chunks (0 for the padding heads)
   if (do_q && sh_h < Gp) {
     const bool real = sh_h < d.G;
     constexpr int kPre = 16 * kStatBatches;          // splits held in registers
@@ -663,8 +743,6 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
     if (real)
       for (int s = sh_j + kPre; s < used; s += 16) m = fmaxf(m, load2_coherent(sr, 8 * (s * d.G + sh_h)).x);
     m = row16_max(m);
-    const float ln = (real && last_q) ? lnew_sh[sh_h] : -INFINITY;
-    m = fmaxf(m, ln);
     float es[kStatBatches];
     float z = 0.0f;
 #pragma unroll
@@ -678,10 +756,7 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
         if (v.y > 0.0f) z += v.y * expf(v.x - m);
       }
     z = row16_sum(z);
-    const float el = ln == -INFINITY ? 0.0f : expf(ln - m);
-    z += el;
     const float rz = real ? 1.0f / z : 0.0f;
-    if (sh_j == 0) wlast_sh[sh_h] = el * rz;
 #pragma unroll
     for (int i = 0; i < kStatBatches; ++i)
       if (sh_j + 16 * i < used) f_sh[(sh_j + 16 * i) * Gp + sh_h] = es[i] * rz;
@@ -691,13 +766,13 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
     }
   }
   __syncthreads();
+  NOSA_PHASE(p, kPhasePoolRow, 5);
 
   // 2. chunk scores a_c = sum over the group's heads of the head's softmax
   // weight, once per chunk (a chunk shared by two blocks gives both the same
   // value): each float4 covers 4 heads of one chunk, the Gp / 4 lanes of a
-  // chunk are adjacent and combine with lane exchanges
+  // chunk are adjacent and combine with DPP lane exchanges
   if (do_q) {
-    const int lpc = Gp / 4;                          // lanes per chunk: 1, 2, 4
     for (int k0 = 0; k0 < n4; k0 += kTopkThreads * kLoadBatch) {     // uniform
       if (k0 > 0) {
 #pragma unroll
@@ -706,30 +781,16 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
           eb[u] = k4 < n4 ? load4_coherent(er, 16 * k4) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
       }
-#pragma unroll
-      for (int u = 0; u < kLoadBatch; ++u) {
-        const int k4 = k0 + t + kTopkThreads * u;
-        const int c = k4 / lpc, h0 = 4 * (k4 % lpc);
-        float a = 0.0f;
-        if (k4 < n4) {
-          const float *fs = f_sh + (c / kChunksPerSplit) * Gp + h0;
-          a = eb[u].x * fs[0];
-          a = fmaf(eb[u].y, fs[1], a);
-          a = fmaf(eb[u].z, fs[2], a);
-          a = fmaf(eb[u].w, fs[3], a);
-        }
-        if (lpc >= 2) a += __shfl_xor(a, 1, 64);
-        if (lpc >= 4) a += __shfl_xor(a, 2, 64);
-        if (k4 < n4 && h0 == 0) a_sh[c] = a;
-      }
-    }
-    if (last_q && t == 0) {                  // the newest chunk, heads in order
-      float a = 0.0f;
-      for (int h = 0; h < d.G; ++h) a += wlast_sh[h];
-      a_sh[C - 1] = a;
+      if (Gp == 4)
+        chunk_scores<4>(eb, k0, n4, n_splits, f_sh, a_sh);
+      else if (Gp == 8)
+        chunk_scores<8>(eb, k0, n4, n_splits, f_sh, a_sh);
+      else
+        chunk_scores<16>(eb, k0, n4, n_splits, f_sh, a_sh);
     }
   }
   __syncthreads();
+  NOSA_PHASE(p, kPhasePoolRow, 6);
 
   finish_select(d, st, p, nb, win_lo, n_cand, C, do_q, do_e, a_sh, el_sh, be, e0, kind, sel,
                 n_sel, kind_out, dbg, tk);
