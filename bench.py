@@ -64,6 +64,9 @@ def parse():
                     help="run only the layer-ahead leg and print its JSON")
     ap.add_argument("--fetch-wg", type=int, default=32,
                     help="workgroup budget of the layer-ahead fetch")
+    ap.add_argument("--fetch-wg-sweep", type=str, default="", metavar="N,N,...",
+                    help="run only the layer-ahead leg, once per workgroup budget, and "
+                         "print one JSON list")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the hipGraph replay leg of the same layer stack")
     ap.add_argument("--no-next", action="store_true",
@@ -711,20 +714,23 @@ def forecast_inputs(wl, li, n, pool, device):
     return torch.from_numpy(np.ascontiguousarray(f).view(np.int16)).to(device)
 
 
-def layer_ahead_leg(dev, workers, R=4, W=4, K=24, n_bd=4, n_wg=32):
+def layer_ahead_leg(dev, workers, R=4, W=4, K=24, n_bd=4, n_wg=32, sweep=None):
     """SparDA's layer-ahead order on the 1B-shaped 32K stack (64 sequences,
     16/2 heads, k = 64; R of its 28 layers, layer 0's KV on the GPU and the
     rest in pinned host memory, as SparDA keeps layer 0 resident): each
     layer's blocks are selected by a forecast head before its append, and
     fetched with n_wg looping workgroups. The same layers run K steps
     layer by layer on one stream, then K steps with layer l+1's selection and
-    fetch on a second stream beside layer l's append and decode."""
+    fetch on a second stream beside layer l's append and decode. With sweep
+    (a list of workgroup budgets), the same built stack is timed once per
+    budget and the result holds one record per budget."""
     import numpy as np
     import torch
     from synth import WORKLOADS
     from trainable_offloadable_block_amd import LayerAheadStack, LayerShape
     wl = WORKLOADS[3]
-    n_tok = 2 * W + 2 * K + n_bd
+    budgets = list(sweep) if sweep else [n_wg]
+    n_tok = len(budgets) * (2 * W + 2 * K + n_bd)
     t_setup = time.perf_counter()
     layers, ins = [], []
     with cf.ThreadPoolExecutor(workers) as pool:
@@ -737,65 +743,68 @@ def layer_ahead_leg(dev, workers, R=4, W=4, K=24, n_bd=4, n_wg=32):
             ins.append((forecast_inputs(wl, li, n_tok, pool, dev), k, v, q))
             log(f"layer-ahead: layer {li} ready ({time.perf_counter() - t_setup:.1f}s)")
     torch.cuda.synchronize()
-    serial = LayerAheadStack(layers, fetch_workgroups=n_wg, overlap=False)
-    overlap = LayerAheadStack(layers, fetch_workgroups=n_wg, overlap=True)
 
     def run(pipe, t0, n):
         for t in range(t0, t0 + n):
             pipe.step([tuple(x[t] for x in ins[li]) for li in range(R)])
 
-    res = {"workload": wl.name + "-layer-ahead", "layers_per_step": R, "steps": K,
-           "fetch_workgroups": n_wg, "unit": "tokens/s/layer",
-           "layer0": "resident (SparDA keeps layer 0 on the GPU)"}
+    records = []
     t = 0
-    for name, pipe in (("serial", serial), ("overlap", overlap)):
-        run(pipe, t, W)
-        torch.cuda.synchronize()
-        t += W
-        t0 = time.perf_counter()
-        run(pipe, t, K)
-        torch.cuda.synchronize()
-        el = time.perf_counter() - t0
-        t += K
-        res[name] = {"value": round(wl.batch * R * K / el, 1),
-                     "ms_per_step": round(el * 1e3 / K, 4)}
-    res["speedup"] = round(res["overlap"]["value"] / res["serial"]["value"], 3)
-    # per-call breakdown of the offloaded layers, serial order (untimed)
-    names = ("select_forecast", "fetch_wg", "append", "decode")
-    bd = {n: [] for n in names}
-    fetched = []
-    for _ in range(n_bd):
-        for li in range(1, R):
-            f, k, v, q = (x[t] for x in ins[li])
-            ly = layers[li]
-            evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-            evs[0].record()
-            ly.select_forecast(f, want_kind=False)
-            evs[1].record()
-            ly.fetch_wg(n_wg)
-            evs[2].record()
-            ly.append(k, v)
-            evs[3].record()
-            ly.decode(q)
-            evs[4].record()
+    for nw in budgets:
+        serial = LayerAheadStack(layers, fetch_workgroups=nw, overlap=False)
+        overlap = LayerAheadStack(layers, fetch_workgroups=nw, overlap=True)
+        res = {"workload": wl.name + "-layer-ahead", "layers_per_step": R, "steps": K,
+               "fetch_workgroups": nw, "unit": "tokens/s/layer",
+               "layer0": "resident (SparDA keeps layer 0 on the GPU)"}
+        for name, pipe in (("serial", serial), ("overlap", overlap)):
+            run(pipe, t, W)
             torch.cuda.synchronize()
-            for i, n in enumerate(names):
-                bd[n].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)
-            fetched.append((int(ly.n_miss.sum().item()) * 32768,
-                            evs[1].elapsed_time(evs[2]) * 1e3))
-        t += 1
-    res["breakdown_us"] = {n: round(float(np.median(v)), 2) for n, v in bd.items()}
-    b_ = float(np.mean([x[0] for x in fetched]))
-    us = float(np.mean([x[1] for x in fetched]))
-    res["fetch"] = {"bytes_per_call": int(b_), "us_mean": round(us, 1),
-                    "GBps": round(b_ / (us * 1e-6) / 1e9, 2)}
-    res["decode_beside_us"] = decode_beside(layers[1], ins[1][3][t - 1], layers[2], n_wg)
+            t += W
+            t0 = time.perf_counter()
+            run(pipe, t, K)
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            t += K
+            res[name] = {"value": round(wl.batch * R * K / el, 1),
+                         "ms_per_step": round(el * 1e3 / K, 4)}
+        res["speedup"] = round(res["overlap"]["value"] / res["serial"]["value"], 3)
+        # per-call breakdown of the offloaded layers, serial order (untimed)
+        names = ("select_forecast", "fetch_wg", "append", "decode")
+        bd = {n: [] for n in names}
+        fetched = []
+        for _ in range(n_bd):
+            for li in range(1, R):
+                f, k, v, q = (x[t] for x in ins[li])
+                ly = layers[li]
+                evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+                evs[0].record()
+                ly.select_forecast(f, want_kind=False)
+                evs[1].record()
+                ly.fetch_wg(nw)
+                evs[2].record()
+                ly.append(k, v)
+                evs[3].record()
+                ly.decode(q)
+                evs[4].record()
+                torch.cuda.synchronize()
+                for i, n in enumerate(names):
+                    bd[n].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)
+                fetched.append((int(ly.n_miss.sum().item()) * 32768,
+                                evs[1].elapsed_time(evs[2]) * 1e3))
+            t += 1
+        res["breakdown_us"] = {n: round(float(np.median(v)), 2) for n, v in bd.items()}
+        b_ = float(np.mean([x[0] for x in fetched]))
+        us = float(np.mean([x[1] for x in fetched]))
+        res["fetch"] = {"bytes_per_call": int(b_), "us_mean": round(us, 1),
+                        "GBps": round(b_ / (us * 1e-6) / 1e9, 2)}
+        res["decode_beside_us"] = decode_beside(layers[1], ins[1][3][t - 1], layers[2], nw)
+        records.append(res)
     status = [ly.status_bits() for ly in layers]
     assert not any(status), f"device status bits set: {status}"
     layers.clear()
     ins.clear()
     torch.cuda.empty_cache()
-    return res
+    return records if sweep else records[0]
 
 
 def decode_beside(dec_layer, q, fetch_layer, n_wg, n=6):
@@ -803,8 +812,9 @@ def decode_beside(dec_layer, q, fetch_layer, n_wg, n=6):
     delta fetch of fetch_layer on a second stream (its cache emptied first,
     so every selected block is copied by n_wg workgroups reading host
     memory), and beside a 256 MiB pinned-host-to-device copy on the DMA
-    engines. fetch_layer is not stepped afterwards: emptying its cache drops
-    the tokens its newest block holds only there.""" 
+    engines. Emptying fetch_layer's cache drops the tokens its newest block
+    holds only there, so that layer's later outputs are not meaningful (its
+    timings still are; a budget sweep goes on stepping it)."""  
     import numpy as np
     import torch
     side = torch.cuda.Stream()
@@ -1143,6 +1153,10 @@ def main():
         return
     if args.only_link:
         print(json.dumps(host_link_peak(dev)), flush=True)
+        return
+    if args.fetch_wg_sweep:
+        budgets = [int(x) for x in args.fetch_wg_sweep.split(",") if x]
+        print(json.dumps(layer_ahead_leg(dev, workers, sweep=budgets)), flush=True)
         return
     if args.only_ahead:
         print(json.dumps(layer_ahead_leg(dev, workers, n_wg=args.fetch_wg)), flush=True)
