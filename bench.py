@@ -1102,6 +1102,7 @@ def phase_clocks(dev, workers, R=8, W=12, samples=24):
                                     us(a[:, n_wg, 2], t0).max())))
     dec = {k: [] for k in ("start", "wave_loop_end_mean", "wave_loop_end_max", "lds_merge",
                            "published", "last_arrival", "merge_end", "slowest_pair_vs_median")}
+    xcd_loop = []             # per launch: mean over each XCD's workgroups of their slowest wave
     for a in dec_runs:
         rows = np.nonzero((a[:, :, 0] > 0).any(axis=0))[0]
         ns = int(rows.max()) + 1
@@ -1116,11 +1117,21 @@ def phase_clocks(dev, workers, R=8, W=12, samples=24):
         dec["last_arrival"].append(float(arr.mean()))
         dec["merge_end"].append(float(us(a[:, :ns, 5].max(axis=1), t0).max()))
         dec["slowest_pair_vs_median"].append(float(arr.max() - np.median(arr)))
+        # the step kernels deal a pair's workgroups to one XCD: unit p * ns + split
+        # of the total sits on XCD (p * ns + split) // (total / 8)
+        wg_end = loops.max(axis=2)                       # [P][ns]
+        unit = np.arange(P)[:, None] * ns + np.arange(ns)[None, :]
+        xcd = unit // max(1, (P * ns) // 8) if (P * ns) % 8 == 0 else unit % 8
+        xcd_loop.append([float(wg_end[xcd == x].mean()) for x in range(8)])
     out = {"workload": wl.name, "layers": R, "sampled_launches": {"append_select": len(sel_runs),
                                                                  "decode": len(dec_runs)},
            "unit": "us from the launch's first workgroup start; mean over sampled launches",
            "append_select": {k: round(float(np.mean(v)), 2) for k, v in sel.items()},
            "decode": {k: round(float(np.mean(v)), 2) for k, v in dec.items()}}
+    if xcd_loop:
+        out["decode"]["xcd_wg_loop_end_mean"] = [round(float(x), 2) for x in np.mean(xcd_loop, axis=0)]
+        out["decode"]["xcd_wg_loop_end_mean_by_launch_spread"] = round(
+            float(np.mean([max(r) - min(r) for r in xcd_loop])), 2)
     return out
 
 

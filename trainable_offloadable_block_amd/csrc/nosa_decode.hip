@@ -36,7 +36,11 @@ namespace {
 #define NOSA_DECODE_MIN_WAVES 2     // <= 256 registers: two workgroups per CU fit
 #endif
 
-constexpr int kDecThreads = 256;
+#ifndef NOSA_DECODE_WAVES
+#define NOSA_DECODE_WAVES 4         // waves per workgroup (one workgroup per CU at 16K)
+#endif
+constexpr int kDecWaves = NOSA_DECODE_WAVES;
+constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kMaxSplits = 32;   // k <= 128 blocks, >= 4 blocks per split
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -272,7 +276,7 @@ __device__ void merge_splits_v(const Dims &d, int p, int b, int g, int n_splits,
   float fw[NV], lsum[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int hh = 2 * w + 8 * j + half;
+    const int hh = 2 * w + (kDecThreads / 32) * j + half;
     float m = -INFINITY, lv = 0.0f;
     if (spl < n_splits && hh < d.G) {
       m = load_agent(&mlp[2 * (spl * d.G + hh)]);
@@ -333,7 +337,7 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   // lane i: block and slot ids of this wave's i-th list entry, loaded
   // before the list length is known (every entry < k exists), so the first
   // KV loads wait for one memory round trip, not two
-  const int e_lane = split * bps + w + 4 * l;
+  const int e_lane = split * bps + w + kDecWaves * l;
   int lane_blk = -1, lane_slot = -1;
   if (l < 16 && e_lane < d.k) {
     lane_blk = sel[(size_t)p * d.k + e_lane];
@@ -346,8 +350,14 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   // iteration of the streaming loop, the prefetched half included
   asm volatile("" ::"v"(lane_blk), "v"(lane_slot));
 
-  __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ __align__(16) float sm_o[4][16][kHeadDim + 4];
+  __shared__ float sm_m[kDecWaves][16], sm_l[kDecWaves][16];
+  __shared__ __align__(16) float sm_o[kDecWaves][16][kHeadDim + 4];
+  auto waves_max = [&](int hh) {
+    float M = sm_m[0][hh];
+#pragma unroll
+    for (int ww = 1; ww < kDecWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+    return M;
+  };
   __shared__ int sm_last;
 
   DecodeArgs a;
@@ -364,7 +374,7 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   a.slots = slots_per_pair;
   a.e_first = split * bps + w;
   a.e_end = min(ns, split * bps + bps);
-  const int n_mine = a.e_first < a.e_end ? (a.e_end - a.e_first + 3) / 4 : 0;
+  const int n_mine = a.e_first < a.e_end ? (a.e_end - a.e_first + kDecWaves - 1) / kDecWaves : 0;
   // n_mine <= 16: only lanes below it hold entries of the list
 
   const int nh = 2 * n_mine;
@@ -425,12 +435,12 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
     for (int j = 0; 4 * (threadIdx.x + kDecThreads * j) < d.G * kHeadDim; ++j) {
       const int idx = 4 * (threadIdx.x + kDecThreads * j);
       const int hh = idx / kHeadDim, dim = idx % kHeadDim;
-      const float M = fmaxf(fmaxf(sm_m[0][hh], sm_m[1][hh]), fmaxf(sm_m[2][hh], sm_m[3][hh]));
+      const float M = waves_max(hh);
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       float lsum = 0.0f;
       if (M != -INFINITY) {
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
+        for (int ww = 0; ww < kDecWaves; ++ww) {
           const float f = exp2f(sm_m[ww][hh] - M);
           const float4 ov = *reinterpret_cast<const float4 *>(&sm_o[ww][hh][dim]);
           acc.x += f * ov.x;
@@ -449,11 +459,11 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   if (n_splits == 1) {                         // uniform: the pair's only split
     for (int idx = threadIdx.x; idx < d.G * kHeadDim; idx += kDecThreads) {
       const int hh = idx / kHeadDim, dim = idx % kHeadDim;
-      const float M = fmaxf(fmaxf(sm_m[0][hh], sm_m[1][hh]), fmaxf(sm_m[2][hh], sm_m[3][hh]));
+      const float M = waves_max(hh);
       float acc = 0.0f, lsum = 0.0f;
       if (M != -INFINITY) {
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
+        for (int ww = 0; ww < kDecWaves; ++ww) {
           const float f = exp2f(sm_m[ww][hh] - M);
           acc += f * sm_o[ww][hh][dim];
           lsum += f * sm_l[ww][hh];
@@ -476,12 +486,12 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
     for (int j = 0; 4 * (threadIdx.x + kDecThreads * j) < n_out; ++j) {   // wave-uniform
       const int idx = 4 * (threadIdx.x + kDecThreads * j);
       const int hh = idx / kHeadDim, dim = idx % kHeadDim;
-      const float M = fmaxf(fmaxf(sm_m[0][hh], sm_m[1][hh]), fmaxf(sm_m[2][hh], sm_m[3][hh]));
+      const float M = waves_max(hh);
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       float lsum = 0.0f;
       if (M != -INFINITY) {
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
+        for (int ww = 0; ww < kDecWaves; ++ww) {
           const float f = exp2f(sm_m[ww][hh] - M);
           const float4 ov = *reinterpret_cast<const float4 *>(&sm_o[ww][hh][dim]);
           acc.x += f * ov.x;
@@ -500,11 +510,11 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   } else {
   for (int idx = threadIdx.x; idx < d.G * kHeadDim; idx += kDecThreads) {
     const int hh = idx / kHeadDim, dim = idx % kHeadDim;
-    const float M = fmaxf(fmaxf(sm_m[0][hh], sm_m[1][hh]), fmaxf(sm_m[2][hh], sm_m[3][hh]));
+    const float M = waves_max(hh);
     float acc = 0.0f, lsum = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
+      for (int ww = 0; ww < kDecWaves; ++ww) {
         const float f = exp2f(sm_m[ww][hh] - M);
         acc += f * sm_o[ww][hh][dim];
         lsum += f * sm_l[ww][hh];
@@ -531,7 +541,8 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   if (d.G == 4 || d.G == 8)
     merge_splits_v<1>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
   else if (d.G == 16)
-    merge_splits_v<2>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
+    merge_splits_v<(16 * 32 + kDecThreads - 1) / kDecThreads>(d, p, b, g, n_splits, mlf, ws_o,
+                                                             &sm_o[0][0][0], out);
   else if (d.G <= 8)
     merge_splits<4>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
   else
