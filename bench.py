@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--phase-clocks", action="store_true",
                     help="phase breakdown of the append + select and decode launches from the "
                          "timing build's in-kernel clocks (NOSA_LIBRARY=.../libnosa_clocks.so)")
+    ap.add_argument("--only-host-link", action="store_true",
+                    help="run only the host-link ceiling and the 128K host-link leg, print its JSON")
     ap.add_argument("--only-link", action="store_true",
                     help="run only the host-link ceiling probe and print its JSON")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -1161,6 +1163,11 @@ def main():
     workers = min(16, len(os.sched_getaffinity(0)))
     if args.phase_clocks:
         print(json.dumps(phase_clocks(dev, workers)), flush=True)
+        return
+    if args.only_host_link:
+        link = host_link_peak(dev)
+        with cf.ThreadPoolExecutor(workers) as pool:
+            print(json.dumps(host_link_leg(args.offload_steps, pool, dev, link)), flush=True)
         return
     if args.only_link:
         print(json.dumps(host_link_peak(dev)), flush=True)
