@@ -1080,7 +1080,8 @@ def phase_clocks(dev, workers, R=8, W=12, samples=24):
                            "append_done", "append_done_max", "append_landed", "last_arrival",
                            "last_arrival_max", "pool_loads", "pool_factors", "pool_chunk_scores",
                            "pool_stage1", "pool_stage2", "pool_list", "pool_eligibility",
-                           "pool_eligibility_max", "end")}
+                           "pool_eligibility_max", "end", "stage1_rounds", "stage2_rounds",
+                           "stage2_ranked")}
     for a in sel_runs:
         rows = np.nonzero((a[:, :, 0] > 0).any(axis=0))[0]
         n_wg = int(rows[rows < ROWS - 1].max())          # the append workgroup's row
@@ -1102,6 +1103,10 @@ def phase_clocks(dev, workers, R=8, W=12, samples=24):
         sel["pool_eligibility_max"].append(float(us(a[:, ROWS - 1, 10], t0).max()))
         sel["end"].append(float(max(us(a[:, ROWS - 1, 11], t0).max(),
                                     us(a[:, n_wg, 2], t0).max())))
+        # counts, not clocks: refinement rounds of each top-k stage and the
+        # candidates stage 2 ranks (eligible and not taken by stage 1)
+        for k, slot in (("stage1_rounds", 12), ("stage2_rounds", 13), ("stage2_ranked", 14)):
+            sel[k].append(float(a[:, ROWS - 1, slot].mean()))
     dec = {k: [] for k in ("start", "wave_loop_end_mean", "wave_loop_end_max", "lds_merge",
                            "published", "last_arrival", "merge_end", "slowest_pair_vs_median")}
     xcd_loop = []             # per launch: mean over each XCD's workgroups of their slowest wave

@@ -20,6 +20,13 @@ static __device__ unsigned long long
           __builtin_amdgcn_s_memrealtime();                                                \
   } while (0)
 #define NOSA_PHASE(p, row, slot) NOSA_PHASE_AT(threadIdx.x == 0, p, row, slot)
+// Stores a value (a count) rather than the clock.
+#define NOSA_PHASE_VAL(p, row, slot, val)                                                  \
+  do {                                                                                     \
+    if (threadIdx.x == 0 && (p) < nosa::kPhasePairs && (row) < nosa::kPhaseRows)           \
+      g_phase_clock[((p) * nosa::kPhaseRows + (row)) * nosa::kPhaseSlots + (slot)] =       \
+          (unsigned long long)(val);                                                       \
+  } while (0)
 #define NOSA_PHASE_WAVE(p, row, slot) NOSA_PHASE_AT((threadIdx.x & 63) == 0, p, row, slot)
 // Copies the array out (dst, when not NULL), then zeroes it (when clear).
 #define NOSA_PHASE_READER(name)                                                            \
@@ -39,5 +46,8 @@ static __device__ unsigned long long
   } while (0)
 #define NOSA_PHASE_WAVE(p, row, slot) \
   do {                                \
+  } while (0)
+#define NOSA_PHASE_VAL(p, row, slot, val) \
+  do {                                    \
   } while (0)
 #endif

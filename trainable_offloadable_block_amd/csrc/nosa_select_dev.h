@@ -324,13 +324,15 @@ struct __align__(16) TopkLds {
 // all threads; the caller syncs before reading kind.
 template <int R, int NT = kTopkThreads>
 __device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0, uint8_t *kind, uint8_t val,
-                        TopkLds &sh) {
+                        TopkLds &sh, int clk_p = 0, int clk_slot = -1) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   bool act[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) act[r] = key[r] != 0;
   int need = k;
+  int rounds = 0;
   for (int round = 0; need > 0 && round < 9; ++round) {    // uniform; <= 8 refinements
+    ++rounds;
     const int par = round & 1;
     uint64_t mn = ~0ull, mx = 0;
     uint32_t c = 0;
@@ -441,6 +443,7 @@ __device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0
     if (all_in) break;                                       // uniform
     need = rest;
   }
+  if (clk_slot >= 0) NOSA_PHASE_VAL(clk_p, kPhasePoolRow, clk_slot, rounds);
   // leave both histograms zero for the next call
   __syncthreads();
 #pragma unroll
@@ -465,12 +468,16 @@ __device__ inline float block_qscore(const float *a_sh, int bb, int C) {
 // Both selection stages with R candidate slots per thread (candidate
 // t + 256 r, block n_sink + t + 256 r). Stage 1: the k_q candidates of
 // highest query-aware score; stage 2: the k_e' eligible candidates of highest
-// agnostic score among the rest.
+// agnostic score among the rest. Once decoding is under way the eligible
+// candidates left after stage 1 rarely outnumber k_e' (the eligible set only
+// keeps blocks selected at the previous step), and then stage 2 takes them
+// all without ranking.
 template <int R>
 __device__ __forceinline__ void select_stages(const Dims &d, int p, int n_cand, int C, bool do_q, bool do_e,
                               const float *a_sh, const uint32_t *el_sh, const float *be,
                               float e0, uint8_t *kind, float *dbg, TopkLds &tk) {
-  const int t = threadIdx.x;
+  __shared__ int n_rank_sh[kTopkThreads / 64];
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   if (do_q) {
     uint64_t kq[R];
 #pragma unroll
@@ -483,20 +490,35 @@ __device__ __forceinline__ void select_stages(const Dims &d, int p, int n_cand, 
         if (dbg) dbg[(size_t)p * d.NB_max + bb] = qb;
       }
     }
-    wg_topk(kq, d.k_q, d.n_sink, kind, NOSA_KIND_QUERY, tk);
-    __syncthreads();
+    // returns after a barrier that follows its marks of kind[]
+    wg_topk(kq, d.k_q, d.n_sink, kind, NOSA_KIND_QUERY, tk, p, 12);
   }
   NOSA_PHASE(p, kPhasePoolRow, 7);
   if (do_e) {
     uint64_t ke[R];
+    int c = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int i = t + kTopkThreads * r, bb = d.n_sink + i;
       ke[r] = 0;
       if (i < n_cand && ((el_sh[bb >> 5] >> (bb & 31)) & 1u) && kind[bb] != NOSA_KIND_QUERY)
         ke[r] = compose_key(r == 0 ? e0 : get(&be[bb]), bb);
+      c += __popcll(__ballot(ke[r] != 0));
     }
-    wg_topk(ke, d.k_e_dyn, d.n_sink, kind, NOSA_KIND_AGNOSTIC, tk);
+    if (lane == 0) n_rank_sh[w] = c;
+    __syncthreads();
+    int n_rank = 0;
+#pragma unroll
+    for (int ww = 0; ww < kTopkThreads / 64; ++ww) n_rank += n_rank_sh[ww];
+    NOSA_PHASE_VAL(p, kPhasePoolRow, 14, n_rank);
+    if (n_rank <= d.k_e_dyn) {                                  // uniform: take them all
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (ke[r] != 0) kind[d.n_sink + t + kTopkThreads * r] = NOSA_KIND_AGNOSTIC;
+      NOSA_PHASE_VAL(p, kPhasePoolRow, 13, 0);
+    } else {
+      wg_topk(ke, d.k_e_dyn, d.n_sink, kind, NOSA_KIND_AGNOSTIC, tk, p, 13);
+    }
   }
 }
 
