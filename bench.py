@@ -1080,7 +1080,8 @@ def phase_clocks(dev, workers, R=8, W=12, samples=24):
                            "append_done", "append_done_max", "append_landed", "last_arrival",
                            "last_arrival_max", "pool_loads", "pool_factors", "pool_chunk_scores",
                            "pool_stage1", "pool_stage2", "pool_list", "pool_eligibility",
-                           "pool_eligibility_max", "end", "stage1_rounds", "stage2_rounds",
+                           "pool_eligibility_max", "end", "stage1_keys", "stage1_r0_minmax",
+                           "stage1_r0_hist", "stage1_r0_end", "stage1_rounds", "stage2_rounds",
                            "stage2_ranked")}
     for a in sel_runs:
         rows = np.nonzero((a[:, :, 0] > 0).any(axis=0))[0]
@@ -1097,6 +1098,8 @@ def phase_clocks(dev, workers, R=8, W=12, samples=24):
         sel["last_arrival"].append(float(arr.mean()))
         sel["last_arrival_max"].append(float(arr.max()))
         for k, slot in (("pool_loads", 4), ("pool_factors", 5), ("pool_chunk_scores", 6),
+                        ("stage1_keys", 0), ("stage1_r0_minmax", 1), ("stage1_r0_hist", 2),
+                        ("stage1_r0_end", 3),
                         ("pool_stage1", 7), ("pool_stage2", 8), ("pool_list", 9),
                         ("pool_eligibility", 10)):
             sel[k].append(float(us(a[:, ROWS - 1, slot], t0).mean()))

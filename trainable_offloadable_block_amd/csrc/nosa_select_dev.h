@@ -364,6 +364,7 @@ __device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0
       }
     }
     __syncthreads();
+    if (clk_slot == 12 && round == 0) NOSA_PHASE(clk_p, kPhasePoolRow, 1);
 #pragma unroll
     for (int i = 0; i < kTopkBins / NT; ++i)         // next round's bins
       sh.hist[par ^ 1][t + NT * i] = 0;
@@ -389,6 +390,7 @@ __device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0
     for (int r = 0; r < R; ++r)
       if (act[r]) atomicAdd(&sh.hist[par][(key[r] - mn) >> shift], 1u);
     __syncthreads();
+    if (clk_slot == 12 && round == 0) NOSA_PHASE(clk_p, kPhasePoolRow, 2);
     // bin holding the need-th largest: lane l sums the BPL bins below
     // kTopkBins - BPL l, a prefix over lanes counts from the top
     constexpr int BPL = kTopkBins / 64;
@@ -440,6 +442,7 @@ __device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0
           act[r] = false;
         }
       }
+    if (clk_slot == 12 && round == 0) NOSA_PHASE(clk_p, kPhasePoolRow, 3);
     if (all_in) break;                                       // uniform
     need = rest;
   }
@@ -491,6 +494,7 @@ __device__ __forceinline__ void select_stages(const Dims &d, int p, int n_cand, 
       }
     }
     // returns after a barrier that follows its marks of kind[]
+    NOSA_PHASE(p, kPhasePoolRow, 0);
     wg_topk(kq, d.k_q, d.n_sink, kind, NOSA_KIND_QUERY, tk, p, 12);
   }
   NOSA_PHASE(p, kPhasePoolRow, 7);
