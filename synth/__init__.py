@@ -15,6 +15,7 @@ from .workloads import (  # noqa: F401
     context_kv,
     eviction_weights,
     f32_to_bf16_bits,
+    f64_to_bf16_bits,
     forecasts,
     hot_blocks,
     new_tokens,

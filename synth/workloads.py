@@ -12,6 +12,8 @@ be regenerated alone):
 
 * stream = PCG64(SeedSequence(seed, spawn_key=(cfg_id, tag, layer, b, h)))
 * context K, V elements ~ N(0, 1), drawn as float32 and rounded to bf16 (RNE)
+  (values computed in float64 -- hot keys, queries -- are rounded to bf16
+  once, directly from float64)
 * each (layer, KV head) has a unit direction u (16 of them in the drift
   workload); hot 64-token blocks, drawn without replacement from the blocks
   that start out between the sink and the window, get keys u + 0.3 * N(0, I)
@@ -145,6 +147,24 @@ def f32_to_bf16_bits(x) -> np.ndarray:
     return u.astype(np.uint16)
 
 
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Round float64 values to bf16 once (round to nearest, ties to even),
+    with no float32 step in between. Input rounding for generated tensors
+    only (their magnitudes are far inside bf16's normal range); returns
+    uint16 bit patterns."""
+    f = np.ascontiguousarray(x, dtype=np.float64)
+    a = np.abs(f)
+    if not np.all(np.isfinite(f)) or np.any((a != 0) & ((a < 2.0 ** -126) | (a >= 2.0 ** 127))):
+        raise ValueError("generator produced a value outside bf16's normal range")
+    # keep 7 of float64's 52 fraction bits, rounding the other 45 to nearest
+    # even; the result has a float32 exponent and 7 fraction bits, so the
+    # float32 conversion is exact and its high half is the bf16 pattern
+    u = f.view(np.uint64)
+    u = (u + np.uint64((1 << 44) - 1) + ((u >> np.uint64(45)) & np.uint64(1))) >> np.uint64(45)
+    r = (u << np.uint64(45)).view(np.float64).astype(np.float32)
+    return (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
 def bf16_bits_to_f32(bits) -> np.ndarray:
     b = np.ascontiguousarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << 16).view(np.float32)
@@ -197,13 +217,12 @@ def context_kv(wl: Workload, layer: int, b: int, g: int):
     k = _rng(wl, "K", layer, b, g).standard_normal((L, d), dtype=np.float32)
     v = _rng(wl, "V", layer, b, g).standard_normal((L, d), dtype=np.float32)
     u = _directions(wl, layer, g)
-    hot = hot_blocks(wl, layer, b, g)
-    for j, blk in enumerate(hot):
+    kb = f32_to_bf16_bits(k)
+    for j, blk in enumerate(hot_blocks(wl, layer, b, g)):
         m = j // 4 if wl.drift else 0
         rows = slice(blk * wl.block, (blk + 1) * wl.block)
-        k[rows] = (u[m][None, :] + 0.3 * k[rows].astype(np.float64)).astype(
-            np.float32)
-    return f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+        kb[rows] = f64_to_bf16_bits(u[m][None, :] + 0.3 * k[rows].astype(np.float64))
+    return kb, f32_to_bf16_bits(v)
 
 
 def queries(wl: Workload, layer: int, b: int, h: int) -> np.ndarray:
@@ -234,7 +253,7 @@ def _ar1_walk(wl: Workload, u: np.ndarray, xi: np.ndarray) -> np.ndarray:
             q = rho * q + (1.0 - rho) * mu * target + math.sqrt(
                 1.0 - rho * rho) * xi[t]
         out[t] = q
-    return f32_to_bf16_bits(out.astype(np.float32))
+    return f64_to_bf16_bits(out)
 
 
 def new_tokens(wl: Workload, layer: int, b: int, g: int):

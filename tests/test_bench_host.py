@@ -6,6 +6,7 @@ import os
 import sys
 
 import numpy as np
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
@@ -81,3 +82,19 @@ def test_decode_bytes_definition():
     want = (n_att * wl.batch * wl.n_kv_heads * (2 * 128 * 2 + 4)
             + wl.batch * wl.n_q_heads * 128 * (2 + 4) + wl.batch * wl.n_kv_heads * wl.k_blocks * 8)
     assert bench.decode_bytes(wl, n_att) == want
+
+
+def test_generator_rounds_float64_to_bf16_once():
+    """Generated values computed in float64 (queries, hot keys) are rounded to
+    bf16 once: a value just above a bf16 tie that a float32 step would pull
+    onto the tie still rounds up; exact ties go to even."""
+    from synth import f64_to_bf16_bits
+    x = np.array([1 + 2.0 ** -8,                   # tie -> even (1.0)
+                  1 + 3 * 2.0 ** -8,               # tie -> even (1 + 2^-6)
+                  1 + 2.0 ** -8 + 2.0 ** -30,      # above the tie; float32 would land on it
+                  -(1 + 2.0 ** -8 + 2.0 ** -30),
+                  0.0, 3.0, 2.0 ** -126])
+    want = [0x3F80, 0x3F82, 0x3F81, 0xBF81, 0x0000, 0x4040, 0x0080]
+    assert f64_to_bf16_bits(x).tolist() == want
+    with pytest.raises(ValueError):
+        f64_to_bf16_bits(np.array([2.0 ** -130]))
