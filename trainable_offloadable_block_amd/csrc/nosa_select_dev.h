@@ -458,12 +458,17 @@ __device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0
 
 // Query-aware score of block bb: max over its overlapping chunks
 // 4bb-1 .. 4bb+3 of the chunk score a_c.
+// (C >= 1; the five reads are unconditional, at clamped indices, so they
+// go out together)
 __device__ inline float block_qscore(const float *a_sh, int bb, int C) {
+  float v[5];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) v[j] = a_sh[min(max(4 * bb - 1 + j, 0), C - 1)];
   float qb = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 5; ++j) {
     const int c = 4 * bb - 1 + j;
-    if (c >= 0 && c < C) qb = fmaxf(qb, a_sh[c]);
+    qb = (c >= 0 && c < C) ? fmaxf(qb, v[j]) : qb;
   }
   return qb;
 }
