@@ -476,9 +476,14 @@ def host_link_leg(n_steps, pool, dev, link):
 
 def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0, link_peak=None):
     """Times K decode steps (after W warm-up steps) of a stack of R
-    independent layers of workload wl; every timed decode launch stamps its
-    own start and end into a pair of HIP events on its stream
-    (nosa_sparse_decode_timed); n_bd further steps give a per-call breakdown
+    independent layers of workload wl, as plain stream launches. K more
+    steps give the decode's launch time: each runs every layer's append +
+    select (and fetch) first, then the R decode launches back to back
+    between two HIP events on their stream, so a decode follows a kernel
+    with no idle gap, as in the timed steps, and the events' own cost is
+    shared by R launches (a pair of events stamped by every launch, kept out
+    of the first K steps, cost the step about 9 % and each launch about
+    2 us); n_bd further steps give a per-call breakdown
     (events recorded around each call) and the exact
     number of attended tokens. With graph_steps, the same stack then runs
     that many steps (after 4 untimed ones) as replays of one captured HIP
@@ -488,7 +493,7 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0, link_peak=None):
     import torch
     from trainable_offloadable_block_amd import LayerShape
     n_graph = graph_steps + 4 if graph_steps else 0
-    n_tok = W + K + n_bd + n_graph
+    n_tok = W + 2 * K + n_bd + n_graph
     shape = LayerShape(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_sink_blocks,
                        wl.window_tokens, wl.k_blocks, wl.k_q_blocks, wl.k_e_blocks,
                        wl.context + n_tok, offload=wl.offload)
@@ -502,15 +507,29 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0, link_peak=None):
     torch.cuda.synchronize()
 
     def run_step(t, events=None):
-        for li, layer in enumerate(layers):
+        if events is None:
+            for li, layer in enumerate(layers):
+                q, kn, vn = inputs[li][0][t], inputs[li][1][t], inputs[li][2][t]
+                layer.append_select(kn, vn, q, want_kind=False)
+                layer.fetch()
+                layer.decode(q)
+            return
+        i = t - W - K
+        if len(layers) == 1:       # one layer: the launch stamps its own events
+            layer = layers[0]
+            q, kn, vn = inputs[0][0][t], inputs[0][1][t], inputs[0][2][t]
+            layer.append_select(kn, vn, q, want_kind=False)
+            layer.fetch()
+            layer.decode(q, events=(events[0][i], events[1][i]))
+            return
+        for li, layer in enumerate(layers):        # every layer's selection, then
             q, kn, vn = inputs[li][0][t], inputs[li][1][t], inputs[li][2][t]
             layer.append_select(kn, vn, q, want_kind=False)
             layer.fetch()
-            if events is None:
-                layer.decode(q)
-            else:                  # the kernel stamps its own start and end
-                i = (t - W) * len(layers) + li
-                layer.decode(q, events=(events[0][i], events[1][i]))
+        events[0][i].record()                       # the R decodes between two events
+        for li, layer in enumerate(layers):
+            layer.decode(inputs[li][0][t])
+        events[1][i].record()
 
     for t in range(W):
         run_step(t)
@@ -523,18 +542,25 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0, link_peak=None):
             for li, layer in enumerate(layers):
                 layer.decode(inputs[li][0][W - 1] if W > 0 else inputs[li][0][0])
         torch.cuda.synchronize()
-    # the timed launches' events, created (first record) before the timed region
-    ev = tuple([torch.cuda.Event(enable_timing=True) for _ in range(K * R)] for _ in range(2))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(W, W + K):
+        run_step(t)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    # the decode's launch time: K more steps with each step's R decodes back
+    # to back between two events (created, by a first record, beforehand)
+    ev = tuple([torch.cuda.Event(enable_timing=True) for _ in range(K)] for _ in range(2))
     for lst in ev:
         for e in lst:
             e.record()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for t in range(W, W + K):
+    t1 = time.perf_counter()
+    for t in range(W + K, W + 2 * K):
         run_step(t, ev)
     torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    dec_ms = [a.elapsed_time(b) for a, b in zip(*ev)]
+    el_stamped = time.perf_counter() - t1
+    dec_ms = [a.elapsed_time(b) / R for a, b in zip(*ev)]      # per launch, step by step
 
     # per-call breakdown on a few extra steps (untimed region); these steps
     # also give the exact number of attended tokens per decode launch (the
@@ -550,7 +576,7 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0, link_peak=None):
     def selection(layer):
         return (layer.sel.cpu().numpy().reshape(-1, k), layer.n_sel.cpu().numpy())
     prev = [selection(ly) for ly in layers]
-    for t in range(W + K, W + K + n_bd):
+    for t in range(W + 2 * K, W + 2 * K + n_bd):
         for li, layer in enumerate(layers):
             q, kn, vn = inputs[li][0][t], inputs[li][1][t], inputs[li][2][t]
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -577,15 +603,18 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0, link_peak=None):
                 fetched.append((int(miss.sum()) * 32768, evs[1].elapsed_time(evs[2]) * 1e3))
     graph = None
     if graph_steps:
-        graph = graph_replays(layers, inputs, W + K + n_bd, graph_steps, shape)
+        graph = graph_replays(layers, inputs, W + 2 * K + n_bd, graph_steps, shape)
     status = [ly.status_bits() for ly in layers]
     assert not any(status), f"device status bits set: {status}"
     dec_us = [x * 1e3 for x in dec_ms]
     out = {"value": wl.batch * R * K / el, "elapsed": el,
+           "decode_timing_steps": {"steps": K, "ms_per_step": round(el_stamped / K * 1e3, 4)},
            "n_att": float(np.mean(n_att_samples)),
            "dec_avg_s": float(np.mean(dec_ms)) / 1e3,
            "dec_launch_us": {"median": pct(dec_us, 50), "p90": pct(dec_us, 90),
-                             "launches": len(dec_us)},
+                             "launches": len(dec_us) * R,
+                             "samples": ("per launch" if R == 1 else
+                                         f"{len(dec_us)} step means of {R} launches")},
            "breakdown": {n: round(float(np.median(v)), 2) for n, v in bd.items()},
            "breakdown_p90": {n: pct(v, 90) for n, v in bd.items()},
            "layer_step_us": {"median": pct(layer_step, 50), "p90": pct(layer_step, 90),
@@ -1229,11 +1258,14 @@ def main():
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
             "bytes_per_launch": int(dbytes), "avg_launch_us": round(dec_avg_s * 1e6, 2),
-            "timing": "HIP events stamped by each timed decode launch (hipExtLaunchKernel)",
+            "timing": "HIP events around each step's 8 decode launches, run back to back "
+                      "after the step's selections, over the K steps that follow the value's "
+                      "timed region (the same stack; that region runs without events)",
             "launch_us": m["dec_launch_us"],
             "call_us_events_around": bd["decode"],
             "attended_tokens_per_pair": round(n_att, 2),
         },
+        "decode_timing_steps": m["decode_timing_steps"],
         "breakdown_us": bd,
         "breakdown_p90_us": m["breakdown_p90"],
         "layer_step_us": m["layer_step_us"],
