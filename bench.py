@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/s per layer (batch x steps/s) + % HBM peak, 1B-shape 16K/32K"
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA, MI355X
 
 
 CLOCK_WARM_S = 0.5      # untimed decode launches before each timed region
@@ -879,6 +880,18 @@ def decode_beside(dec_layer, q, fetch_layer, n_wg, n=6):
     return out
 
 
+def attend_roofline(head_tokens, us):
+    """The prompt attention against the bf16 MFMA peak: 4 x 128 flop per
+    (query head, attended token) -- the Q K^T logit and the P V product --
+    over the launch time (the kernel splits P into bf16 hi + lo for P V,
+    which doubles that product's MFMA work; the algorithmic count is the
+    plain one)."""
+    tf = 4 * 128 * head_tokens / (us * 1e-6) / 1e12
+    return {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "flop_per_launch": int(4 * 128 * head_tokens)}
+
+
 def prefill_scores_leg(dev, workers, T=4096, K=10):
     """Block scores of T prompt queries per sequence at once (the selection
     side of NOSA_S's sparse prefill) on the 16K 1B-shaped layer: the last T
@@ -964,7 +977,10 @@ def prefill_scores_leg(dev, workers, T=4096, K=10):
         "total_us": round(total, 1), "prompt_tokens_per_s": round(wl.batch * T / (total * 1e-6), 1),
         "attended_tokens_per_query_pair": round(n_att, 1),
         "attend_kv_GBps_if_unshared": round(wl.batch * wl.n_kv_heads * T * n_att * 516 /
-                                            (times["attend"] * 1e-6) / 1e9, 1)}
+                                            (times["attend"] * 1e-6) / 1e9, 1),
+        # the attention's own roofline: its contractions on MFMA, 2 x 128
+        # flop per (query head, attended token) for Q K^T and as many for P V
+        "attend_roofline": attend_roofline(wl.batch * wl.n_q_heads * T * n_att, times["attend"])}
     del layer, qd, scores, sel, nsel, out
     torch.cuda.empty_cache()
     return res

@@ -62,7 +62,14 @@ class LayerShape:
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    # a plain int: the bound functions declare their pointer arguments as
+    # c_void_p, which ctypes fills from an int (or None for NULL) directly
+    return t.data_ptr() if t is not None else None
+
+
+# the current stream's handle as an int, through torch's direct accessor
+# where it has one (about 10x cheaper per call than current_stream())
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def v_to_tiles(v: np.ndarray) -> np.ndarray:
@@ -111,6 +118,8 @@ class NosaLayer:
     def __init__(self, shape: LayerShape, device: str = "cuda"):
         self.shape = shape
         self.device = torch.device(device)
+        self._dev_index = (self.device.index if self.device.index is not None
+                           else torch.cuda.current_device())
         self.cfg = shape.config()
         lib = L.lib()
         L.check(lib.nosa_validate_config(ctypes.byref(self.cfg)), "validate_config")
@@ -181,7 +190,9 @@ class NosaLayer:
 
     @property
     def stream(self):
-        return ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+        if _raw_stream is not None:
+            return _raw_stream(self._dev_index)
+        return torch.cuda.current_stream(self.device).cuda_stream
 
     # ------------------------------------------------------------ set-up
     def set_weights(self, w1: np.ndarray, w2: np.ndarray):
