@@ -753,7 +753,9 @@ def layer_ahead_leg(dev, workers, R=4, W=4, K=24, n_bd=4, n_wg=32, sweep=None):
     layer's blocks are selected by a forecast head before its append, and
     fetched with n_wg looping workgroups. The same layers run K steps
     layer by layer on one stream, then K steps with layer l+1's selection and
-    fetch on a second stream beside layer l's append and decode. With sweep
+    fetch on a second stream beside layer l's append and decode, then K steps
+    with layer l's fetch on the second stream beside layer l+1's selection
+    (overlap_beside_select). With sweep
     (a list of workgroup budgets), the same built stack is timed once per
     budget and the result holds one record per budget."""
     import numpy as np
@@ -762,7 +764,7 @@ def layer_ahead_leg(dev, workers, R=4, W=4, K=24, n_bd=4, n_wg=32, sweep=None):
     from trainable_offloadable_block_amd import LayerAheadStack, LayerShape
     wl = WORKLOADS[3]
     budgets = list(sweep) if sweep else [n_wg]
-    n_tok = len(budgets) * (2 * W + 2 * K + n_bd)
+    n_tok = len(budgets) * (3 * W + 3 * K + n_bd)
     t_setup = time.perf_counter()
     layers, ins = [], []
     with cf.ThreadPoolExecutor(workers) as pool:
@@ -785,10 +787,12 @@ def layer_ahead_leg(dev, workers, R=4, W=4, K=24, n_bd=4, n_wg=32, sweep=None):
     for nw in budgets:
         serial = LayerAheadStack(layers, fetch_workgroups=nw, overlap=False)
         overlap = LayerAheadStack(layers, fetch_workgroups=nw, overlap=True)
+        beside_select = LayerAheadStack(layers, fetch_workgroups=nw, overlap="select")
         res = {"workload": wl.name + "-layer-ahead", "layers_per_step": R, "steps": K,
                "fetch_workgroups": nw, "unit": "tokens/s/layer",
                "layer0": "resident (SparDA keeps layer 0 on the GPU)"}
-        for name, pipe in (("serial", serial), ("overlap", overlap)):
+        for name, pipe in (("serial", serial), ("overlap", overlap),
+                           ("overlap_beside_select", beside_select)):
             run(pipe, t, W)
             torch.cuda.synchronize()
             t += W
@@ -800,6 +804,8 @@ def layer_ahead_leg(dev, workers, R=4, W=4, K=24, n_bd=4, n_wg=32, sweep=None):
             res[name] = {"value": round(wl.batch * R * K / el, 1),
                          "ms_per_step": round(el * 1e3 / K, 4)}
         res["speedup"] = round(res["overlap"]["value"] / res["serial"]["value"], 3)
+        res["speedup_beside_select"] = round(
+            res["overlap_beside_select"]["value"] / res["serial"]["value"], 3)
         # per-call breakdown of the offloaded layers, serial order (untimed)
         names = ("select_forecast", "fetch_wg", "append", "decode")
         bd = {n: [] for n in names}

@@ -438,15 +438,17 @@ def _stack(wl, n_layers):
             for li in range(n_layers)]
 
 
-def test_layer_ahead_stack_overlap_equals_serial():
-    """The two-stream cross-layer pipeline (layer l+1's selection and fetch on
-    a second stream while layer l appends and decodes) gives, bit for bit,
-    the outputs, selections and state of the same stack run layer by layer
-    on one stream, over 70 steps of 3 layers."""
+@pytest.mark.parametrize("order", [True, "select"], ids=["beside-decode", "beside-select"])
+def test_layer_ahead_stack_overlap_equals_serial(order):
+    """The two-stream cross-layer pipeline, in either order (layer l+1's
+    selection and fetch on a second stream while layer l appends and
+    decodes; or layer l's fetch on the second stream beside layer l+1's
+    selection), gives, bit for bit, the outputs, selections and state of the
+    same stack run layer by layer on one stream, over 70 steps of 3 layers."""
     from trainable_offloadable_block_amd import LayerAheadStack
     wl = small_workload(154, context=1000, steps=70)
     sa, sb = _stack(wl, 3), _stack(wl, 3)
-    pa = LayerAheadStack([ls.gpu for ls in sa], fetch_workgroups=8, overlap=True)
+    pa = LayerAheadStack([ls.gpu for ls in sa], fetch_workgroups=8, overlap=order)
     pb = LayerAheadStack([ls.gpu for ls in sb], fetch_workgroups=8, overlap=False)
     for t in range(wl.steps):
         for pipe, st in ((pa, sa), (pb, sb)):

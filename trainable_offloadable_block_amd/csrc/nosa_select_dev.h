@@ -330,7 +330,7 @@ __device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0
 #pragma unroll
   for (int r = 0; r < R; ++r) act[r] = key[r] != 0;
   int need = k;
-  int rounds = 0;
+  [[maybe_unused]] int rounds = 0;
   for (int round = 0; need > 0 && round < 9; ++round) {    // uniform; <= 8 refinements
     ++rounds;
     const int par = round & 1;

@@ -411,17 +411,25 @@ class LayerAheadStack:
     l+1's previous decode (which reads the slots it refills) and append
     (which moved its length); the main stream's append of layer l+1 follows
     the fetch that reassigns its cache slots.
+
+    overlap="select" is the other order the two streams allow: the main
+    stream runs layer l+1's selection while the side stream fetches layer
+    l's blocks (selected one layer earlier), and layer l's append and decode
+    wait for that fetch, so the host-memory reads of the gather meet only the
+    latency-bound selection, never a decode (a compute-unit gather halves HBM
+    streaming chip-wide while it runs).
     """
 
-    def __init__(self, layers, fetch_workgroups: int = 32, overlap: bool = True):
+    def __init__(self, layers, fetch_workgroups: int = 32, overlap=True):
         self.layers = list(layers)
         self.fetch_workgroups = int(fetch_workgroups)
-        self.overlap = overlap
+        self.overlap = overlap              # False, True (beside the decode) or "select"
         dev = self.layers[0].device
         self.side = torch.cuda.Stream(device=dev)
         n = len(self.layers)
         self.ev_start = [torch.cuda.Event() for _ in range(n)]
         self.ev_fetch = [torch.cuda.Event() for _ in range(n)]
+        self.ev_sel = [torch.cuda.Event() for _ in range(n)]
 
     def _select_fetch(self, layer, f):
         layer.select_forecast(f, want_kind=False)
@@ -440,6 +448,26 @@ class LayerAheadStack:
         if not self.overlap:
             for layer, (f, k, v, q) in zip(self.layers, inputs):
                 self._select_fetch(layer, f)
+                layer.append(k, v)
+                layer.decode(q)
+            return [layer.out for layer in self.layers]
+        if self.overlap == "select":
+            self.layers[0].select_forecast(inputs[0][0], want_kind=False)
+            self.ev_sel[0].record(main)
+            for li in range(n):
+                layer = self.layers[li]
+                with torch.cuda.stream(self.side):      # layer li's fetch ...
+                    self.side.wait_event(self.ev_sel[li])
+                    if self.fetch_workgroups:
+                        layer.fetch_wg(self.fetch_workgroups)
+                    else:
+                        layer.fetch()
+                    self.ev_fetch[li].record(self.side)
+                if li + 1 < n:                          # ... beside layer li+1's selection
+                    self.layers[li + 1].select_forecast(inputs[li + 1][0], want_kind=False)
+                    self.ev_sel[li + 1].record(main)
+                main.wait_event(self.ev_fetch[li])
+                _, k, v, q = inputs[li]
                 layer.append(k, v)
                 layer.decode(q)
             return [layer.out for layer in self.layers]
