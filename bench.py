@@ -63,8 +63,11 @@ def parse():
                     help="skip the layer-ahead (SparDA order) leg")
     ap.add_argument("--only-ahead", action="store_true",
                     help="run only the layer-ahead leg and print its JSON")
-    ap.add_argument("--fetch-wg", type=int, default=32,
-                    help="workgroup budget of the layer-ahead fetch")
+    ap.add_argument("--fetch-wg", type=int, default=8,
+                    help="workgroup budget of the layer-ahead fetch (8: the budget "
+                         "of the fastest two-stream order in the sweep)")
+    ap.add_argument("--ahead-steps", type=int, default=64,
+                    help="timed steps per order in the layer-ahead leg and its sweep")
     ap.add_argument("--fetch-wg-sweep", type=str, default="", metavar="N,N,...",
                     help="run only the layer-ahead leg, once per workgroup budget, and "
                          "print one JSON list")
@@ -746,7 +749,7 @@ def forecast_inputs(wl, li, n, pool, device):
     return torch.from_numpy(np.ascontiguousarray(f).view(np.int16)).to(device)
 
 
-def layer_ahead_leg(dev, workers, R=4, W=4, K=24, n_bd=4, n_wg=32, sweep=None):
+def layer_ahead_leg(dev, workers, R=4, W=4, K=64, n_bd=4, n_wg=8, sweep=None):
     """SparDA's layer-ahead order on the 1B-shaped 32K stack (64 sequences,
     16/2 heads, k = 64; R of its 28 layers, layer 0's KV on the GPU and the
     rest in pinned host memory, as SparDA keeps layer 0 resident): each
@@ -1233,10 +1236,12 @@ def main():
         return
     if args.fetch_wg_sweep:
         budgets = [int(x) for x in args.fetch_wg_sweep.split(",") if x]
-        print(json.dumps(layer_ahead_leg(dev, workers, sweep=budgets)), flush=True)
+        print(json.dumps(layer_ahead_leg(dev, workers, K=args.ahead_steps, sweep=budgets)),
+              flush=True)
         return
     if args.only_ahead:
-        print(json.dumps(layer_ahead_leg(dev, workers, n_wg=args.fetch_wg)), flush=True)
+        print(json.dumps(layer_ahead_leg(dev, workers, K=args.ahead_steps, n_wg=args.fetch_wg)),
+              flush=True)
         return
     if args.only_prefill:
         print(json.dumps(prefill_scores_leg(dev, workers)), flush=True)
@@ -1334,7 +1339,8 @@ def main():
         res["offload_8b_64k"] = offload_8b_64k_leg(dev, workers, link_peak=link["peak_GBps"])
         if not args.no_ahead:
             log("layer-ahead leg (SparDA order, offloaded 32K stack)")
-            res["layer_ahead"] = layer_ahead_leg(dev, workers, n_wg=args.fetch_wg)
+            res["layer_ahead"] = layer_ahead_leg(dev, workers, K=args.ahead_steps,
+                                                 n_wg=args.fetch_wg)
         log("host-link leg (offloaded 128K workload)")
         with cf.ThreadPoolExecutor(workers) as pool:
             res["host_link"] = host_link_leg(args.offload_steps, pool, dev, link)

@@ -413,11 +413,17 @@ class LayerAheadStack:
     the fetch that reassigns its cache slots.
 
     overlap="select" is the other order the two streams allow: the main
-    stream runs layer l+1's selection while the side stream fetches layer
-    l's blocks (selected one layer earlier), and layer l's append and decode
-    wait for that fetch, so the host-memory reads of the gather meet only the
-    latency-bound selection, never a decode (a compute-unit gather halves HBM
-    streaming chip-wide while it runs).
+    stream runs each layer's selection one layer ahead (layer l+1's right
+    after layer l's fetch is issued) and layer l's append and decode once
+    layer l's fetch is done; the side stream runs the fetches back to back,
+    each as soon as its selection is done. A fetch then meets the next
+    layer's selection and part of the previous layer's decode rather than a
+    whole decode; with a small gather budget (8 workgroups, which slow a
+    decode beside them about 4x where 32 slow it about 8x) this order ran
+    1.16x the one-stream step on the 32K stack. Holding each fetch until
+    the previous decode was done (so that a gather met only a selection)
+    measured slower than one stream (0.94-0.97x): the selection is too short
+    to hide a fetch behind.
     """
 
     def __init__(self, layers, fetch_workgroups: int = 32, overlap=True):
