@@ -416,14 +416,14 @@ class LayerAheadStack:
     stream runs each layer's selection one layer ahead (layer l+1's right
     after layer l's fetch is issued) and layer l's append and decode once
     layer l's fetch is done; the side stream runs the fetches back to back,
-    each as soon as its selection is done. A fetch then meets the next
-    layer's selection and part of the previous layer's decode rather than a
-    whole decode; with a small gather budget (8 workgroups, which slow a
-    decode beside them about 4x where 32 slow it about 8x) this order ran
-    1.16x the one-stream step on the 32K stack. Holding each fetch until
-    the previous decode was done (so that a gather met only a selection)
-    measured slower than one stream (0.94-0.97x): the selection is too short
-    to hide a fetch behind.
+    each as soon as its selection is done. The chain of fetches is then the
+    step's critical path, and the appends and decodes (slowed beside a
+    gather, which reads host memory from compute units) fit under it; with
+    a small gather budget (8 workgroups, which slow a decode beside them
+    about 4x where 32 slow it about 8x) this order ran 1.13-1.16x the
+    one-stream step on the 32K stack, where the first order ran 0.95-1.00x.
+    Holding each fetch until the previous decode was done (so that a gather
+    met only a selection) measured slower than one stream (0.94-0.97x).
     """
 
     def __init__(self, layers, fetch_workgroups: int = 32, overlap=True):
