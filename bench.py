@@ -63,6 +63,9 @@ def parse():
                     help="skip the layer-ahead (SparDA order) leg")
     ap.add_argument("--only-ahead", action="store_true",
                     help="run only the layer-ahead leg and print its JSON")
+    ap.add_argument("--select-pool", type=int, default=0, choices=(0, 1, 2),
+                    help="nosa_set_tuning NOSA_TUNE_SELECT_POOL for the whole run "
+                         "(0: the library's choice)")
     ap.add_argument("--fetch-wg", type=int, default=8,
                     help="workgroup budget of the layer-ahead fetch (8: the budget "
                          "of the fastest two-stream order in the sweep)")
@@ -1156,7 +1159,9 @@ def phase_clocks(dev, workers, R=8, W=12, samples=24):
                         ("stage1_r0_end", 3),
                         ("pool_stage1", 7), ("pool_stage2", 8), ("pool_list", 9),
                         ("pool_eligibility", 10)):
-            sel[k].append(float(us(a[:, ROWS - 1, slot], t0).mean()))
+            col = a[:P, ROWS - 1, slot]
+            if (col > 0).all():        # slots 1-3: stamped by the range refinement only
+                sel[k].append(float(us(col, t0).mean()))
         sel["pool_eligibility_max"].append(float(us(a[:, ROWS - 1, 10], t0).max()))
         sel["end"].append(float(max(us(a[:, ROWS - 1, 11], t0).max(),
                                     us(a[:, n_wg, 2], t0).max())))
@@ -1190,7 +1195,7 @@ def phase_clocks(dev, workers, R=8, W=12, samples=24):
     out = {"workload": wl.name, "layers": R, "sampled_launches": {"append_select": len(sel_runs),
                                                                  "decode": len(dec_runs)},
            "unit": "us from the launch's first workgroup start; mean over sampled launches",
-           "append_select": {k: round(float(np.mean(v)), 2) for k, v in sel.items()},
+           "append_select": {k: round(float(np.mean(v)), 2) for k, v in sel.items() if v},
            "decode": {k: round(float(np.mean(v)), 2) for k, v in dec.items()}}
     if xcd_loop:
         out["decode"]["xcd_wg_loop_end_mean"] = [round(float(x), 2) for x in np.mean(xcd_loop, axis=0)]
@@ -1223,6 +1228,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     workers = min(16, len(os.sched_getaffinity(0)))
+    if args.select_pool:
+        from trainable_offloadable_block_amd import _lib as L
+        L.check(L.lib().nosa_set_tuning(L.NOSA_TUNE_SELECT_POOL, args.select_pool), "set_tuning")
     if args.phase_clocks:
         print(json.dumps(phase_clocks(dev, workers)), flush=True)
         return

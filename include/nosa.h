@@ -412,11 +412,18 @@ int nosa_link_copy(const void *src, void *dst, size_t bytes, int32_t n_workgroup
  *      workgroup, 1..2048 (capped at the split count).
  *  NOSA_TUNE_GATHER_VPT  4 KiB pieces of a block that a nosa_fetch_delta_wg
  *      workgroup moves at a time: 1, 2, 4 or 8.
+ *  NOSA_TUNE_SELECT_POOL  how a selection's last workgroup finishes: 0 the
+ *      library's choice (2 where it applies), 1 the general path (kinds of
+ *      every block in LDS, candidates as R per thread, list and eligibility
+ *      by passes over the blocks), 2 for a pair of at most 256 candidates,
+ *      one candidate per thread (kinds, list places and eligibility bits
+ *      from per-thread flags and two counts). Both give the same
+ *      selections.
  * The per-pair arrival counters of the select and decode workspaces sit at
  * the start of each workspace whatever the launch shape, so a change
  * between calls never leaves them on non-zero bytes. */
 enum { NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT = 0, NOSA_TUNE_SELECT_SUBS = 1,
-       NOSA_TUNE_GATHER_VPT = 2, NOSA_NUM_TUNE };
+       NOSA_TUNE_GATHER_VPT = 2, NOSA_TUNE_SELECT_POOL = 3, NOSA_NUM_TUNE };
 int nosa_set_tuning(int knob, int32_t value);
 
 const char *nosa_strerror(int code);

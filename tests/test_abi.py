@@ -204,7 +204,8 @@ def test_tuning_knobs():
     for knob, bad in ((L.NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT, 3),
                       (L.NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT, 65),
                       (L.NOSA_TUNE_SELECT_SUBS, -1),
-                      (L.NOSA_TUNE_GATHER_VPT, 3), (7, 1), (-1, 0)):
+                      (L.NOSA_TUNE_GATHER_VPT, 3), (L.NOSA_TUNE_SELECT_POOL, 3),
+                      (7, 1), (-1, 0)):
         assert lib.nosa_set_tuning(knob, bad) == L.NOSA_ERR_INVALID, (knob, bad)
     default = lib.nosa_workspace_bytes(ctypes.byref(c), L.NOSA_WS_DECODE, 16640)
     with L.tuning(L.NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT, 64):

@@ -701,6 +701,45 @@ def test_select_splits_per_workgroup_do_not_change_results():
             assert torch.equal(sa[n], sb[n]), f"step {t}: state {n}"
 
 
+@pytest.mark.parametrize("case", ["g4_6k", "g8_boundary_17k", "tiny_candidates"])
+def test_select_pool_paths_agree(case):
+    """The selection's two finishing paths -- general (kinds of every block
+    in LDS, passes over the blocks) and one candidate per thread -- give the
+    same selection, kinds, block scores and state, bit for bit, step after
+    step. The first decoding step ranks stage 2 (every candidate still
+    eligible); the 17K case starts at 255 candidates and steps past 256,
+    where the library leaves the one-candidate-per-thread path; the last case
+    has fewer candidates than k_q, and a sequence with none."""
+    if case == "g4_6k":
+        wl = small_workload(231, context=6000, steps=20, k_blocks=12, k_q_blocks=4, k_e_blocks=8)
+        lengths = [6000, 5711]
+    elif case == "g8_boundary_17k":
+        wl = small_workload(232, batch=1, n_q_heads=16, n_kv_heads=2, context=17350, steps=140,
+                            window_tokens=1024, k_blocks=64, k_q_blocks=16, k_e_blocks=48,
+                            n_hot=8)
+        lengths = None
+    else:
+        wl = small_workload(233, context=300, steps=40, k_blocks=10, k_q_blocks=4, k_e_blocks=6,
+                            n_hot=1)
+        lengths = [300, 170]
+    runs = [Lockstep(wl, check_pairs=[], lengths=lengths, fused=True) for _ in range(2)]
+    for t in range(wl.steps):
+        kd, vd, qd = runs[0].inputs(t)
+        for ls, mode in zip(runs, (1, 2)):
+            with L.tuning(L.NOSA_TUNE_SELECT_POOL, mode):
+                ls.gpu.append_select(kd, vd, qd, want_kind=True, want_qscore=True)
+        torch.cuda.synchronize()
+        a = runs[0].gpu
+        for b in (r.gpu for r in runs[1:]):
+            for n in ("sel", "n_sel", "kind"):
+                assert torch.equal(getattr(a, n), getattr(b, n)), f"{case} step {t}: {n}"
+            assert torch.equal(torch.nan_to_num(a.dbg_q, nan=-7.0),
+                               torch.nan_to_num(b.dbg_q, nan=-7.0)), f"{case} step {t}: qscore"
+            sa, sb = _state_tensors(a), _state_tensors(b)
+            for n in sa:
+                assert torch.equal(sa[n], sb[n]), f"{case} step {t}: state {n}"
+
+
 def test_decode_one_split_per_pair():
     """A pair whose whole selection is one workgroup's run (one split: the
     output is normalised and written without the split merge) stays within

@@ -39,6 +39,7 @@ NOSA_OFFLOAD = 2
 
 NOSA_WS_SELECT, NOSA_WS_FETCH, NOSA_WS_DECODE = 1, 2, 3
 NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT, NOSA_TUNE_SELECT_SUBS, NOSA_TUNE_GATHER_VPT = 0, 1, 2
+NOSA_TUNE_SELECT_POOL = 3
 KIND_NONE, KIND_SINK, KIND_WINDOW, KIND_QUERY, KIND_AGNOSTIC = range(5)
 
 BUFFERS = ["seq_len", "arrive", "status", "ckey", "tok_s", "chunk_e", "blk_e",

@@ -69,6 +69,7 @@ int make_dims(const nosa_config *c, nosa::Dims *d) {
   d->k_e_dyn = c->k_e_blocks - c->n_sink_blocks - d->n_win;
   d->offload = (c->flags & NOSA_OFFLOAD) ? 1 : 0;
   d->bias = (c->flags & NOSA_EVICT_BIAS) ? 1 : 0;
+  d->pool_small = nosa::tuning(NOSA_TUNE_SELECT_POOL) == 1 ? 0 : 1;
   return NOSA_OK;
 }
 
@@ -117,6 +118,7 @@ int nosa_set_tuning(int knob, int32_t value) {
     case NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT: ok = value == 0 || (value >= 4 && value <= 64); break;
     case NOSA_TUNE_SELECT_SUBS: ok = value >= 0 && value <= 2048; break;
     case NOSA_TUNE_GATHER_VPT: ok = value == 0 || value == 1 || value == 2 || value == 4 || value == 8; break;
+    case NOSA_TUNE_SELECT_POOL: ok = value >= 0 && value <= 2; break;
     default: break;
   }
   if (!ok) return fail(NOSA_ERR_INVALID, "unknown tuning knob or value out of range");

@@ -234,6 +234,7 @@ struct Dims {
   int max_context, tok_stride, C_max, NB_max, elig_words;
   int n_sink, n_win, k, k_q, k_e_dyn;
   int offload, bias;
+  int pool_small;  // 1: a pair with at most 256 candidates finishes with one per thread
 };
 
 // This workgroup's (x, y) in a 2-D grid whose rows (one pair's workgroups,

@@ -105,11 +105,7 @@ __device__ __forceinline__ void pool_forecast(const Dims &d, const nosa_state &s
     el_sh[i] = st.eligible[(size_t)p * d.elig_words + i];
   for (int bb = t; bb < nb; bb += kTopkThreads)
     kind[bb] = bb < d.n_sink ? NOSA_KIND_SINK : (bb >= win_lo ? NOSA_KIND_WINDOW : NOSA_KIND_NONE);
-#pragma unroll
-  for (int i = 0; i < kTopkBins / kTopkThreads; ++i) {
-    tk.hist[0][t + kTopkThreads * i] = 0;
-    tk.hist[1][t + kTopkThreads * i] = 0;
-  }
+  topk_lds_init(tk);
   // 1. the logits into LDS (entries at and past C are never read)
   if (do_q) {
     const int n4 = (C + 3) / 4;

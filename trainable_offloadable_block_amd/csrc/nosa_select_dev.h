@@ -307,30 +307,46 @@ __device__ inline uint32_t wave_incl_scan(uint32_t x) {
 
 constexpr int kTopkBits = 8, kTopkBins = 1 << kTopkBits;   // bins per refinement round
 
+constexpr int kSmallWords = 16;   // eligibility words <= 256 consecutive candidates touch (<= 9)
+
 struct __align__(16) TopkLds {
   uint32_t hist[2][kTopkBins];
   uint64_t mn[2][kTopkThreads / 64], mx[2][kTopkThreads / 64];
   uint32_t cnt[2][kTopkThreads / 64];
+  uint32_t clr[kSmallWords];   // eligibility bits finish_select_small clears, zero at entry
 };
 
-// Marks kind[bb0 + t + NT r] = val for the k largest nonzero keys of the
-// NT-thread workgroup (thread t holds the keys of candidates t + NT r, r < R).
+// Zeroes a TopkLds's histograms and clear marks (thread t of kTopkThreads);
+// the caller's next barrier orders it before their use.
+__device__ inline void topk_lds_init(TopkLds &tk) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kTopkBins / kTopkThreads; ++i) {
+    tk.hist[0][t + kTopkThreads * i] = 0;
+    tk.hist[1][t + kTopkThreads * i] = 0;
+  }
+  if (t < kSmallWords) tk.clr[t] = 0;
+}
+
+// Calls mark(r) in thread t for each of the k largest nonzero keys of the
+// NT-thread workgroup (thread t holds the keys of candidates t + NT r, r < R;
+// a thread marks only its own keys) and returns the rounds it ran.
 // Exact selection by range refinement: each round histograms the active keys
 // into 256 bins over [min, max] (the top 8 bits of their spread), keeps every
 // key above the bin holding the k-th largest, drops those below it, and goes
 // on inside that bin; a bin whose keys are all wanted ends it. The spread
 // shrinks by 8 bits per round, so 64-bit keys need at most 8 rounds.
 // hist[0] must be zero on entry; both are zero again on return. Called by
-// all threads; the caller syncs before reading kind.
-template <int R, int NT = kTopkThreads>
-__device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0, uint8_t *kind, uint8_t val,
-                        TopkLds &sh, int clk_p = 0, int clk_slot = -1) {
+// all threads; the caller syncs before another thread reads a mark.
+template <int R, int NT = kTopkThreads, typename Mark>
+__device__ __forceinline__ int wg_topk_marks(const uint64_t (&key)[R], int k, Mark mark, TopkLds &sh,
+                                             int clk_p = 0, int clk_slot = -1) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   bool act[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) act[r] = key[r] != 0;
   int need = k;
-  [[maybe_unused]] int rounds = 0;
+  int rounds = 0;
   for (int round = 0; need > 0 && round < 9; ++round) {    // uniform; <= 8 refinements
     ++rounds;
     const int par = round & 1;
@@ -381,7 +397,7 @@ __device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0
     if (c <= static_cast<uint32_t>(need)) {                  // uniform: take them all
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        if (act[r]) kind[bb0 + t + NT * r] = val;
+        if (act[r]) mark(r);
       break;
     }
     const int span = mx > mn ? 64 - __builtin_clzll(mx - mn) : 0;   // c >= 2 distinct keys
@@ -436,7 +452,7 @@ __device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0
       if (act[r]) {
         const int bin = static_cast<int>((key[r] - mn) >> shift);
         if (bin > bstar || (bin == bstar && all_in)) {
-          kind[bb0 + t + NT * r] = val;
+          mark(r);
           act[r] = false;
         } else if (bin < bstar) {
           act[r] = false;
@@ -454,6 +470,16 @@ __device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0
     sh.hist[0][t + NT * i] = 0;
     sh.hist[1][t + NT * i] = 0;
   }
+  return rounds;
+}
+
+// wg_topk_marks that marks kind[bb0 + t + NT r] = val.
+template <int R, int NT = kTopkThreads>
+__device__ __forceinline__ void wg_topk(const uint64_t (&key)[R], int k, int bb0, uint8_t *kind,
+                                        uint8_t val, TopkLds &sh, int clk_p = 0,
+                                        int clk_slot = -1) {
+  wg_topk_marks<R, NT>(key, k, [&](int r) { kind[bb0 + threadIdx.x + NT * r] = val; }, sh, clk_p,
+                       clk_slot);
 }
 
 // Query-aware score of block bb: max over its overlapping chunks
@@ -531,6 +557,107 @@ __device__ __forceinline__ void select_stages(const Dims &d, int p, int n_cand, 
   }
 }
 
+// Both stages, the ascending selection list and the eligibility update of
+// pair p when it has at most kTopkThreads candidates: thread t owns candidate
+// t, block n_sink + t (none past n_cand), so a block's kind, its place in the
+// list and its eligibility bit need no LDS array of kinds and no pass over
+// the blocks. kq: its stage-1 key (0 unless stage 1 runs); e_raw: its
+// agnostic score; el_sh: the eligibility words as they stand; tk.clr zero
+// (topk_lds_init, then a barrier). Each stage is the exact top-k that
+// select_stages runs, so the sets are the same; stage 2 takes every eligible
+// candidate stage 1 left when they do not outnumber k_e', as there. The list
+// holds the sink blocks, the kept candidates, then the window blocks
+// (ascending block order), cut at k. Called by all threads.
+__device__ __forceinline__ void finish_select_small(const Dims &d, const nosa_state &st, int p,
+                                                    int nb, int win_lo, int n_cand, bool do_q,
+                                                    bool do_e, uint64_t kq, float e_raw,
+                                                    const uint32_t *el_sh, int32_t *sel,
+                                                    int32_t *n_sel, uint8_t *kind_out,
+                                                    TopkLds &tk) {
+  __shared__ int cnt_sh[2][kTopkThreads / 64];
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const int bb = d.n_sink + t;
+  const bool cand = t < n_cand;
+  // 1. stage 1: the k_q candidates of highest query-aware score
+  bool in_q = false;
+  if (do_q) {                                      // uniform
+    const uint64_t k1[1] = {kq};
+    wg_topk_marks<1>(k1, d.k_q, [&](int) { in_q = true; }, tk, p, 12);   // rounds -> slot 12
+  }
+  NOSA_PHASE(p, kPhasePoolRow, 7);
+  // 2. stage 2 over the eligible candidates stage 1 left; the candidates the
+  // list keeps and those it leaves out are counted and marked as if stage 2
+  // took them all (the usual case), completed below otherwise
+  const int w_lo = d.n_sink >> 5;
+  const bool e_cand = do_e && cand && !in_q && ((el_sh[bb >> 5] >> (bb & 31)) & 1u);
+  bool inc = in_q || e_cand;
+  if (cand && !inc) atomicOr(&tk.clr[(bb >> 5) - w_lo], 1u << (bb & 31));
+  const uint64_t m_e = __ballot(e_cand);
+  uint64_t m_in = __ballot(inc);
+  if (lane == 0) {
+    cnt_sh[0][w] = __popcll(m_e);
+    cnt_sh[1][w] = __popcll(m_in);
+  }
+  __syncthreads();
+  int n_rank = 0;
+#pragma unroll
+  for (int ww = 0; ww < kTopkThreads / 64; ++ww) n_rank += cnt_sh[0][ww];
+  NOSA_PHASE_VAL(p, kPhasePoolRow, 14, n_rank);
+  int row = 1;
+  if (n_rank > d.k_e_dyn) {                        // uniform: rank them by agnostic score
+    const uint64_t k1[1] = {e_cand ? compose_key(e_raw, bb) : 0};
+    bool in_e = false;
+    wg_topk_marks<1>(k1, d.k_e_dyn, [&](int) { in_e = true; }, tk, p, 13);   // ends with a barrier
+    // the marks so far leave out the candidates stage 2 could have taken;
+    // add those it drops (no one has read the marks yet)
+    if (e_cand && !in_e) atomicOr(&tk.clr[(bb >> 5) - w_lo], 1u << (bb & 31));
+    inc = in_q || in_e;
+    m_in = __ballot(inc);
+    if (lane == 0) cnt_sh[0][w] = __popcll(m_in);  // n_rank's reads ended before a barrier
+    __syncthreads();
+    row = 0;
+  } else {
+    NOSA_PHASE_VAL(p, kPhasePoolRow, 13, 0);
+  }
+  NOSA_PHASE(p, kPhasePoolRow, 8);
+  // 3. ascending selection list: sinks, kept candidates, window
+  const int n_s = min(d.n_sink, nb), n_w = max(0, nb - win_lo);
+  int off = __popcll(m_in & ((1ull << lane) - 1ull)), kept = 0;
+#pragma unroll
+  for (int ww = 0; ww < kTopkThreads / 64; ++ww) {
+    if (ww < w) off += cnt_sh[row][ww];
+    kept += cnt_sh[row][ww];
+  }
+  const int tot = n_s + kept + n_w;
+  int32_t *sp = sel + (size_t)p * d.k;
+  uint8_t *kp = kind_out ? kind_out + (size_t)p * d.k : nullptr;
+  if (inc && n_s + off < d.k) {
+    sp[n_s + off] = bb;
+    if (kp) kp[n_s + off] = in_q ? NOSA_KIND_QUERY : NOSA_KIND_AGNOSTIC;
+  }
+  for (int j = t; j < n_s + n_w; j += kTopkThreads) {   // the sink and window blocks
+    const bool sink = j < n_s;
+    const int pos = sink ? j : j + kept;
+    if (pos < d.k) {
+      sp[pos] = sink ? j : win_lo + (j - n_s);
+      if (kp) kp[pos] = sink ? NOSA_KIND_SINK : NOSA_KIND_WINDOW;
+    }
+  }
+  for (int j = tot + t; j < d.k; j += kTopkThreads) {
+    sp[j] = -1;
+    if (kp) kp[j] = NOSA_KIND_NONE;
+  }
+  if (t == 0) n_sel[p] = min(tot, d.k);
+  NOSA_PHASE(p, kPhasePoolRow, 9);
+  // 4. eligibility: a candidate outside the selection is out for good
+  if (n_cand > 0 && t < kSmallWords) {
+    const int wd = w_lo + t;
+    const uint32_t clear = tk.clr[t];
+    if (clear) st.eligible[(size_t)p * d.elig_words + wd] = el_sh[wd] & ~clear;
+  }
+  NOSA_PHASE(p, kPhasePoolRow, 10);
+}
+
 constexpr int kMaxCandPerThread = (kMaxContext / kBlock) / kTopkThreads;   // 16
 constexpr int kLoadBatch = 10;    // chunk-weight float4 loads in flight per thread
 constexpr int kStatBatches = 4;   // split statistics loaded early: 16 splits each
@@ -549,6 +676,19 @@ __device__ __forceinline__ void finish_select(const Dims &d, const nosa_state &s
   __shared__ int cnt_sh[2][kTopkThreads / 64];
   const int t = threadIdx.x;
   const int w = t >> 6, lane = t & 63;
+  if (d.pool_small && n_cand <= kTopkThreads) {     // uniform: a candidate per thread
+    const int bb = d.n_sink + t;
+    uint64_t kq = 0;
+    if (do_q && t < n_cand) {
+      const float qb = block_qscore(a_sh, bb, C);
+      kq = compose_key(qb, bb);
+      if (dbg) dbg[(size_t)p * d.NB_max + bb] = qb;
+    }
+    NOSA_PHASE(p, kPhasePoolRow, 0);
+    finish_select_small(d, st, p, nb, win_lo, n_cand, do_q, do_e, kq, e0, el_sh, sel, n_sel,
+                        kind_out, tk);
+    return;
+  }
   // 3. both stages, with as many candidate slots per thread as needed
   {
     const int m = (n_cand + kTopkThreads - 1) / kTopkThreads;   // <= kMaxCandPerThread
@@ -688,79 +828,16 @@ __device__ __forceinline__ void chunk_scores(const float4 (&eb)[kLoadBatch], int
   }
 }
 
-// Pooling and both stages for pair p, run by the pair's last score
-// workgroup once every split has published (so the chunk weights and split
-// statistics are read with device-coherent loads); the splits cover every
-// complete chunk. L is the pair's sequence length (after this step's append).
-__device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st, int L_in,
-                                            const float *ws_e, const float *ws_stats,
-                                            int c_pad, int n_splits, int32_t *sel,
-                                            int32_t *n_sel, uint8_t *kind_out, float *dbg,
-                                            int p) {
-  const int Gp = padded_group(d.G);
-  extern __shared__ __align__(16) uint8_t smem[];
-  float *f_sh = reinterpret_cast<float *>(smem);                            // [n_splits][Gp]
-  float *a_sh = f_sh + n_splits * Gp;                                       // [c_pad]
-  uint32_t *el_sh = reinterpret_cast<uint32_t *>(a_sh + c_pad);             // [elig_words]
-  uint8_t *kind = reinterpret_cast<uint8_t *>(el_sh + d.elig_words);        // [NB_max]
-  __shared__ TopkLds tk;
-
+// Pooling's first step: per-split factors exp(m_split - M) / Z of each
+// head's softmax over all complete chunks (0 for the padding heads), into
+// f_sh[split][Gp]. Thread (t / 16, t % 16) takes head t / 16's statistics
+// of splits t % 16 + 16 i; stv_raw holds the first kStatBatches of them,
+// loaded early. Ends with a barrier.
+__device__ __forceinline__ void pool_factors(const Dims &d, int Gp, int used, bool do_q,
+                                             __amdgpu_buffer_rsrc_t sr,
+                                             const float2 (&stv_raw)[kStatBatches], float *f_sh) {
   const int t = threadIdx.x;
-
-  // 0. issue the global loads together, bounded by the buffers' extents
-  // rather than the length (which is itself being loaded), so the kernel
-  // waits for one memory round trip: the first batch of chunk weights
-  // (coalesced float4s of the chunk-major [c][Gp] array), split statistics,
-  // the candidates' agnostic scores, eligibility
-  const int n4_ext = c_pad * Gp / 4;
-  const __amdgpu_buffer_rsrc_t er = make_rsrc(ws_e + (size_t)p * c_pad * Gp, (uint32_t)n4_ext * 16);
-  float4 eb[kLoadBatch];
-#pragma unroll
-  for (int u = 0; u < kLoadBatch; ++u) {
-    const int k4 = t + kTopkThreads * u;
-    eb[u] = k4 < n4_ext ? load4_coherent(er, 16 * k4) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  const float *be = st.blk_e + (size_t)p * d.NB_max;
-  const float e0_raw = d.n_sink + t < d.NB_max ? get(&be[d.n_sink + t]) : 0.0f;
   const int sh_h = t >> 4, sh_j = t & 15;
-  const __amdgpu_buffer_rsrc_t sr =
-      make_rsrc(ws_stats + (size_t)2 * p * n_splits * d.G, (uint32_t)n_splits * d.G * 8);
-  // thread (sh_h, sh_j): head sh_h's statistics of splits sh_j + 16 i
-  float2 stv_raw[kStatBatches];
-#pragma unroll
-  for (int i = 0; i < kStatBatches; ++i) {
-    const int s = sh_j + 16 * i;
-    stv_raw[i] = (sh_h < d.G && s < n_splits) ? load2_coherent(sr, 8 * (s * d.G + sh_h))
-                                              : make_float2(-INFINITY, 0.0f);
-  }
-
-  const int L = max(0, min(L_in, d.max_context));
-  int C = chunks_for(L);
-  if (C > c_pad) {                      // caller's length bound was too small
-    if (t == 0) atomicOr(st.status, NOSA_STATUS_LEN_HINT);
-    C = c_pad;
-  }
-  const int nb = blocks_for(L);
-  const int win_lo = max(d.n_sink, nb - d.n_win);
-  const int n_cand = max(0, win_lo - d.n_sink);
-  const int used = (C + kChunksPerSplit - 1) / kChunksPerSplit;
-  const bool do_q = d.k_q > 0 && n_cand > 0, do_e = d.k_e_dyn > 0 && n_cand > 0;
-  const int n4 = do_q ? C * Gp / 4 : 0;
-  const bool have0 = t < n_cand;
-  const float e0 = (do_e && have0) ? e0_raw : 0.0f;
-  for (int i = t; i < d.elig_words; i += kTopkThreads)
-    el_sh[i] = st.eligible[(size_t)p * d.elig_words + i];
-  for (int bb = t; bb < nb; bb += kTopkThreads)
-    kind[bb] = bb < d.n_sink ? NOSA_KIND_SINK : (bb >= win_lo ? NOSA_KIND_WINDOW : NOSA_KIND_NONE);
-#pragma unroll
-  for (int i = 0; i < kTopkBins / kTopkThreads; ++i) {
-    tk.hist[0][t + kTopkThreads * i] = 0;
-    tk.hist[1][t + kTopkThreads * i] = 0;
-  }
-
-  NOSA_PHASE(p, kPhasePoolRow, 4);
-  // 1. per-split factors exp(m_split - M) / Z of each head's softmax over
-  // all complete chunks (0 for the padding heads)
   if (do_q && sh_h < Gp) {
     const bool real = sh_h < d.G;
     constexpr int kPre = 16 * kStatBatches;          // splits held in registers
@@ -797,6 +874,74 @@ __device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st,
     }
   }
   __syncthreads();
+}
+
+// Pooling and both stages for pair p, run by the pair's last score
+// workgroup once every split has published (so the chunk weights and split
+// statistics are read with device-coherent loads); the splits cover every
+// complete chunk. L is the pair's sequence length (after this step's append).
+__device__ __forceinline__ void pool_select(const Dims &d, const nosa_state &st, int L_in,
+                                            const float *ws_e, const float *ws_stats,
+                                            int c_pad, int n_splits, int32_t *sel,
+                                            int32_t *n_sel, uint8_t *kind_out, float *dbg,
+                                            int p) {
+  const int Gp = padded_group(d.G);
+  extern __shared__ __align__(16) uint8_t smem[];
+  float *f_sh = reinterpret_cast<float *>(smem);                            // [n_splits][Gp]
+  float *a_sh = f_sh + n_splits * Gp;                                       // [c_pad]
+  uint32_t *el_sh = reinterpret_cast<uint32_t *>(a_sh + c_pad);             // [elig_words]
+  uint8_t *kind = reinterpret_cast<uint8_t *>(el_sh + d.elig_words);        // [NB_max]
+  __shared__ TopkLds tk;
+
+  const int t = threadIdx.x;
+
+  const int L = max(0, min(L_in, d.max_context));
+  int C = chunks_for(L);
+  if (C > c_pad) {                      // caller's length bound was too small
+    if (t == 0) atomicOr(st.status, NOSA_STATUS_LEN_HINT);
+    C = c_pad;
+  }
+  const int nb = blocks_for(L);
+  const int win_lo = max(d.n_sink, nb - d.n_win);
+  const int n_cand = max(0, win_lo - d.n_sink);
+  const int used = (C + kChunksPerSplit - 1) / kChunksPerSplit;
+  const bool do_q = d.k_q > 0 && n_cand > 0, do_e = d.k_e_dyn > 0 && n_cand > 0;
+  const int sh_h = t >> 4, sh_j = t & 15;
+  const __amdgpu_buffer_rsrc_t sr =
+      make_rsrc(ws_stats + (size_t)2 * p * n_splits * d.G, (uint32_t)n_splits * d.G * 8);
+  // thread (sh_h, sh_j): head sh_h's statistics of splits sh_j + 16 i
+  float2 stv_raw[kStatBatches];
+#pragma unroll
+  for (int i = 0; i < kStatBatches; ++i) {
+    const int s = sh_j + 16 * i;
+    stv_raw[i] = (sh_h < d.G && s < n_splits) ? load2_coherent(sr, 8 * (s * d.G + sh_h))
+                                              : make_float2(-INFINITY, 0.0f);
+  }
+  // 0. issue the global loads together, so the kernel waits for one memory
+  // round trip: the first batch of chunk weights (coalesced float4s of the
+  // chunk-major [c][Gp] array, bounded by the buffer's extent), the split
+  // statistics (above), the candidates' agnostic scores, eligibility
+  const int n4_ext = c_pad * Gp / 4;
+  const __amdgpu_buffer_rsrc_t er = make_rsrc(ws_e + (size_t)p * c_pad * Gp, (uint32_t)n4_ext * 16);
+  float4 eb[kLoadBatch];
+#pragma unroll
+  for (int u = 0; u < kLoadBatch; ++u) {
+    const int k4 = t + kTopkThreads * u;
+    eb[u] = k4 < n4_ext ? load4_coherent(er, 16 * k4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const float *be = st.blk_e + (size_t)p * d.NB_max;
+  const float e0_raw = d.n_sink + t < d.NB_max ? get(&be[d.n_sink + t]) : 0.0f;
+  const int n4 = do_q ? C * Gp / 4 : 0;
+  const bool have0 = t < n_cand;
+  const float e0 = (do_e && have0) ? e0_raw : 0.0f;
+  for (int i = t; i < d.elig_words; i += kTopkThreads)
+    el_sh[i] = st.eligible[(size_t)p * d.elig_words + i];
+  for (int bb = t; bb < nb; bb += kTopkThreads)
+    kind[bb] = bb < d.n_sink ? NOSA_KIND_SINK : (bb >= win_lo ? NOSA_KIND_WINDOW : NOSA_KIND_NONE);
+  topk_lds_init(tk);
+
+  NOSA_PHASE(p, kPhasePoolRow, 4);
+  pool_factors(d, Gp, used, do_q, sr, stv_raw, f_sh);
   NOSA_PHASE(p, kPhasePoolRow, 5);
 
   // 2. chunk scores a_c = sum over the group's heads of the head's softmax
