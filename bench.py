@@ -529,7 +529,8 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0, link_peak=None):
             layer.fetch()
             layer.decode(q, events=(events[0][i], events[1][i]))
             return
-        for li, layer in enumerate(layers):        # every layer's selection, then
+        events[2][i].record()                       # every layer's selection, then
+        for li, layer in enumerate(layers):
             q, kn, vn = inputs[li][0][t], inputs[li][1][t], inputs[li][2][t]
             layer.append_select(kn, vn, q, want_kind=False)
             layer.fetch()
@@ -557,7 +558,7 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0, link_peak=None):
     el = time.perf_counter() - t0
     # the decode's launch time: K more steps with each step's R decodes back
     # to back between two events (created, by a first record, beforehand)
-    ev = tuple([torch.cuda.Event(enable_timing=True) for _ in range(K)] for _ in range(2))
+    ev = tuple([torch.cuda.Event(enable_timing=True) for _ in range(K)] for _ in range(3))
     for lst in ev:
         for e in lst:
             e.record()
@@ -567,7 +568,9 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0, link_peak=None):
         run_step(t, ev)
     torch.cuda.synchronize()
     el_stamped = time.perf_counter() - t1
-    dec_ms = [a.elapsed_time(b) / R for a, b in zip(*ev)]      # per launch, step by step
+    dec_ms = [a.elapsed_time(b) / R for a, b in zip(ev[0], ev[1])]   # per launch, step by step
+    # the R selections (+ fetches) back to back before them, the same way
+    sel_ms = [a.elapsed_time(b) / R for a, b in zip(ev[2], ev[0])] if R > 1 else []
 
     # per-call breakdown on a few extra steps (untimed region); these steps
     # also give the exact number of attended tokens per decode launch (the
@@ -622,6 +625,12 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0, link_peak=None):
                              "launches": len(dec_us) * R,
                              "samples": ("per launch" if R == 1 else
                                          f"{len(dec_us)} step means of {R} launches")},
+           "sel_launch_us": ({"mean": round(float(np.mean(sel_ms)) * 1e3, 2),
+                              "median": pct([x * 1e3 for x in sel_ms], 50),
+                              "p90": pct([x * 1e3 for x in sel_ms], 90),
+                              "launches": len(sel_ms) * R,
+                              "samples": f"{len(sel_ms)} step means of {R} calls"}
+                             if sel_ms else None),
            "breakdown": {n: round(float(np.median(v)), 2) for n, v in bd.items()},
            "breakdown_p90": {n: pct(v, 90) for n, v in bd.items()},
            "layer_step_us": {"median": pct(layer_step, 50), "p90": pct(layer_step, 90),
@@ -1307,16 +1316,22 @@ def main():
         "locality": m["locality"],
     }
     # the selection against the same roofline: its algorithmic bytes over the
-    # fused append + select call's time (events around the call, so an upper
-    # bound on the selection's own time; the pool after the scoring splits is
-    # latency-bound)
+    # fused append + select launch's time, the step's 8 calls back to back
+    # between two events (as the decode; events around a single call add
+    # their own cost, kept as call_us_events_around); the pool after the
+    # scoring splits is latency-bound
     L_mid = wl.context + W + K
     sb = select_bytes(wl, L_mid)
+    sel_us = m["sel_launch_us"]["mean"]
     res["select_roofline"] = {
         "kernel": "nosa_append_select", "bound": "hbm", "bytes_per_launch": int(sb),
+        "avg_launch_us": sel_us,
+        "timing": "HIP events around each step's 8 append + select calls, run back to "
+                  "back before the step's decodes, over the same K steps as the decode's",
+        "launch_us": m["sel_launch_us"],
         "call_us_events_around": bd["append_select"],
-        "achieved": round(sb / (bd["append_select"] * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
-        "unit": "GB/s", "frac": round(sb / (bd["append_select"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        "achieved": round(sb / (sel_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+        "unit": "GB/s", "frac": round(sb / (sel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     if "graph" in m:
         res["graph_replay"] = m["graph"]
     pf = [ms for name, ms in PREFILL_MS if name == wl.name]
