@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--select-pool", type=int, default=0, choices=(0, 1, 2),
                     help="nosa_set_tuning NOSA_TUNE_SELECT_POOL for the whole run "
                          "(0: the library's choice)")
+    ap.add_argument("--decode-bps", type=int, default=0,
+                    help="nosa_set_tuning NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT for the whole "
+                         "run (0: the library's choice)")
     ap.add_argument("--fetch-wg", type=int, default=8,
                     help="workgroup budget of the layer-ahead fetch (8: the budget "
                          "of the fastest two-stream order in the sweep)")
@@ -1237,9 +1240,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     workers = min(16, len(os.sched_getaffinity(0)))
-    if args.select_pool:
-        from trainable_offloadable_block_amd import _lib as L
-        L.check(L.lib().nosa_set_tuning(L.NOSA_TUNE_SELECT_POOL, args.select_pool), "set_tuning")
+    from trainable_offloadable_block_amd import _lib as L
+    for knob, v in ((L.NOSA_TUNE_SELECT_POOL, args.select_pool),
+                    (L.NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT, args.decode_bps)):
+        if v:
+            L.check(L.lib().nosa_set_tuning(knob, v), "set_tuning")
     if args.phase_clocks:
         print(json.dumps(phase_clocks(dev, workers)), flush=True)
         return

@@ -244,13 +244,13 @@ __device__ void merge_splits(const Dims &d, int p, int b, int g, int n_splits,
 // t owns the float4s of outputs 4 (t + 256 j) .. + 3 below G * 128 (one head
 // each; at G = 4 the last two waves own none), read with unconditional
 // 16-byte device-coherent buffer loads (a split past n_splits reads zeros),
-// SB = 4 / NV splits per batch.
+// SB splits per batch: every batch is one memory round trip, so SB covers
+// the pair's splits in one batch up to 16 / NV of them.
 constexpr int kAgentCoherent = 16;   // buffer cache policy: sc1 (device scope)
 
-template <int NV>
+template <int NV, int SB>
 __device__ void merge_splits_v(const Dims &d, int p, int b, int g, int n_splits,
                                const float *mlf, const float *ws_o, float *sm, float *out) {
-  constexpr int SB = 4 / NV;
   const int t = threadIdx.x;
   const int n_out = d.G * kHeadDim;                   // 512, 1024 or 2048
   const float *mlp = mlf + (size_t)2 * p * n_splits * d.G;
@@ -538,11 +538,15 @@ __global__ __launch_bounds__(kDecThreads, NOSA_DECODE_MIN_WAVES) void decode_ker
   __syncthreads();
   NOSA_PHASE(p, split, 4);
   if (!sm_last) return;
-  if (d.G == 4 || d.G == 8)
-    merge_splits_v<1>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
+  constexpr int NV16 = (16 * 32 + kDecThreads - 1) / kDecThreads;   // 2
+  if ((d.G == 4 || d.G == 8) && n_splits <= 4)
+    merge_splits_v<1, 4>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
+  else if (d.G == 4 || d.G == 8)
+    merge_splits_v<1, 16>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
+  else if (d.G == 16 && n_splits <= 4 / NV16)
+    merge_splits_v<NV16, 4 / NV16>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
   else if (d.G == 16)
-    merge_splits_v<(16 * 32 + kDecThreads - 1) / kDecThreads>(d, p, b, g, n_splits, mlf, ws_o,
-                                                             &sm_o[0][0][0], out);
+    merge_splits_v<NV16, 16 / NV16>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
   else if (d.G <= 8)
     merge_splits<4>(d, p, b, g, n_splits, mlf, ws_o, &sm_o[0][0][0], out);
   else
@@ -573,11 +577,11 @@ DecodeLayout decode_layout(const Dims &d) {
   // per pair (at most kMaxSplits), each a run of bps >= 4 list entries
   // (256 workgroups of 16 blocks each at 64 pairs and k = 64)
   const int want = max(1, min(kMaxSplits, (256 + d.P - 1) / d.P));
+  // (the last workgroup reads all of a pair's partials in one batch of
+  // loads, so more splits cost the merge little: 32 pairs x 96 blocks at
+  // GQA 16, 8 KiB partials, ran 24.5 us in runs of 12, 24.8 us in runs of
+  // 16, 28.4 and 31.3 us in runs of 8 and 10, which overfill the chip)
   int bps = max(4, (d.k + want - 1) / want);
-  // runs of 16 when they still give 192+ workgroups: fewer partials for the
-  // merge (at GQA 16 a pair's partials are 8 KiB each; 32 pairs x 96 blocks
-  // measured 32.3 us at 16 per run against 33.3 us at 12)
-  if (bps < 16 && (long)d.P * ((d.k + 15) / 16) >= 192) bps = 16;
   if (const int v = tuning(NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT)) bps = v;
   while (bps < 64 && (d.k + bps - 1) / bps > kMaxSplits) bps *= 2;   // merge bound
   lay.blocks_per_split = bps;
