@@ -384,6 +384,42 @@ def host_link_peak(dev, nbytes=1 << 30, reps=5):
             "peak_from": "memcpy" if memcpy >= max(cu.values()) else "cu_read"}
 
 
+def hbm_read_ceiling(dev, nbytes=2 << 30, reps=3, launches=5):
+    """The practical HBM read rate of this GPU: nosa_hbm_read (a streaming
+    read that does nothing else) over nbytes of device memory at several
+    workgroup counts, the best of reps runs of `launches` back-to-back
+    launches between two events. Reported beside the published peak, which
+    stays the roofline's peak."""
+    import ctypes
+    import torch
+    from trainable_offloadable_block_amd import _lib as L
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+    buf.fill_(0x01010101)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    by_wg = {}
+    for n_wg in (256, 512, 1024):
+        sink = torch.empty(n_wg * 256 * 4, dtype=torch.int32, device=dev)
+        best = 0.0
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(launches):
+                L.check(L.lib().nosa_hbm_read(ctypes.c_void_p(buf.data_ptr()), nbytes, n_wg,
+                                              ctypes.c_void_p(sink.data_ptr()), stream),
+                        "hbm_read")
+            b.record()
+            torch.cuda.synchronize()
+            best = max(best, launches * nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+        by_wg[n_wg] = round(best, 1)
+        del sink
+    del buf
+    torch.cuda.empty_cache()
+    best_wg = max(by_wg, key=by_wg.get)
+    return {"GBps": by_wg[best_wg], "workgroups": best_wg, "bytes": nbytes,
+            "GBps_by_workgroups": {str(k): v for k, v in by_wg.items()},
+            "frac_of_peak": round(by_wg[best_wg] / HBM_PEAK_GBS, 4)}
+
+
 def fetch_stats(fetched, wl, link_peak):
     """Delta-fetch record of a leg: bytes and time summed over the calls
     (GB/s = total bytes / total time), per-call median and p90, and the time
@@ -1281,6 +1317,8 @@ def main():
     value, el, n_att, dec_avg_s, bd = m["value"], m["elapsed"], m["n_att"], m["dec_avg_s"], m["breakdown"]
     dbytes = decode_bytes(wl, n_att)
     achieved = dbytes / dec_avg_s / 1e9
+    log("HBM read ceiling")
+    ceiling = hbm_read_ceiling(dev)
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -1313,6 +1351,10 @@ def main():
             "launch_us": m["dec_launch_us"],
             "call_us_events_around": bd["decode"],
             "attended_tokens_per_pair": round(n_att, 2),
+            # beside the published peak: what a streaming read that does
+            # nothing else reaches on this GPU (nosa_hbm_read)
+            "practical_read_ceiling": ceiling,
+            "frac_of_practical_read_ceiling": round(achieved / ceiling["GBps"], 4),
         },
         "decode_timing_steps": m["decode_timing_steps"],
         "breakdown_us": bd,

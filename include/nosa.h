@@ -399,6 +399,21 @@ int nosa_host_alias(void *pinned_host_ptr, void **dev_alias);
 int nosa_link_copy(const void *src, void *dst, size_t bytes, int32_t n_workgroups,
                    hipStream_t stream);
 
+/* Reads `bytes` (a multiple of 16) of device memory at src with n_workgroups
+ * workgroups of 256 threads, grid-stride over 16-byte loads with 8 in flight
+ * per thread, and writes each thread's XOR of what it read as one 16-byte
+ * word to sink[workgroup * 256 + thread] (the caller's n_workgroups * 4 KiB
+ * of device memory; the XOR of all of them is the XOR of the buffer). The
+ * HBM read rate of a kernel that does nothing else: the practical ceiling
+ * beside the published peak that the decode's streaming (NOSA-1B 核心组件揭秘,
+ * 解码阶段如何只用 64 个 KV 块: the selected blocks' K and V read once per
+ * step) is reported against. src and sink 16-byte aligned;
+ * 1 <= n_workgroups <= NOSA_MAX_READ_WORKGROUPS; NOSA_ERR_INVALID otherwise,
+ * before any HIP call. */
+#define NOSA_MAX_READ_WORKGROUPS 65536
+int nosa_hbm_read(const void *src, size_t bytes, int32_t n_workgroups, void *sink,
+                  hipStream_t stream);
+
 /* ------------------------------------------------------------ tuning
  * Process-wide launch-shape overrides, for tests and tuning sweeps (host
  * state only; results do not depend on them). value 0 restores the

@@ -228,6 +228,18 @@ def test_link_copy_rejects_before_any_hip_call():
     assert lib.nosa_link_copy(256, 256, 0, 8, null) == L.NOSA_OK
 
 
+def test_hbm_read_rejects_before_any_hip_call():
+    lib = nosa.lib()
+    null = ctypes.c_void_p(0)
+    assert lib.nosa_hbm_read(None, 4096, 8, 256, null) == L.NOSA_ERR_INVALID
+    assert lib.nosa_hbm_read(256, 4096, 8, None, null) == L.NOSA_ERR_INVALID
+    assert lib.nosa_hbm_read(256, 4100, 8, 256, null) == L.NOSA_ERR_INVALID
+    assert lib.nosa_hbm_read(264, 4096, 8, 256, null) == L.NOSA_ERR_INVALID
+    assert lib.nosa_hbm_read(256, 4096, 8, 264, null) == L.NOSA_ERR_INVALID
+    for n_wg in (0, L.NOSA_MAX_READ_WORKGROUPS + 1):
+        assert lib.nosa_hbm_read(256, 4096, n_wg, 256, null) == L.NOSA_ERR_INVALID
+
+
 def test_static_decode_rejects_before_any_hip_call():
     """nosa_sparse_decode_static: NULL arguments, and a config whose decode
     workspace exceeds the static scratch, come back as errors before any HIP

@@ -32,6 +32,7 @@ NOSA_STATUS_LEN_HINT = 4
 NOSA_STATUS_SHORT_CONTEXT = 8
 
 NOSA_MAX_FETCH_WORKGROUPS = 4096
+NOSA_MAX_READ_WORKGROUPS = 65536
 NOSA_DECODE_STATIC_SCRATCH_BYTES = 8 << 20
 
 NOSA_EVICT_BIAS = 1
@@ -110,6 +111,7 @@ def lib():
         "nosa_prefill_attend": (ctypes.c_int, [cfgp, stp, _P, _I32, _I32, _P, _P, _P, _P]),
         "nosa_host_alias": (ctypes.c_int, [_P, ctypes.POINTER(_P)]),
         "nosa_link_copy": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _I32, _P]),
+        "nosa_hbm_read": (ctypes.c_int, [_P, ctypes.c_size_t, _I32, _P, _P]),
         "nosa_set_tuning": (ctypes.c_int, [ctypes.c_int, _I32]),
         "nosa_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "nosa_last_error": (ctypes.c_char_p, []),

@@ -125,6 +125,17 @@ int nosa_set_tuning(int knob, int32_t value) {
   return g_tuning[knob].exchange(value, std::memory_order_relaxed);
 }
 
+int nosa_hbm_read(const void *src, size_t bytes, int32_t n_workgroups, void *sink,
+                  hipStream_t stream) {
+  if (!src || !sink) return fail(NOSA_ERR_INVALID, "src / sink is NULL");
+  if (bytes % 16) return fail(NOSA_ERR_INVALID, "bytes must be a multiple of 16");
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(sink)) & 15u)
+    return fail(NOSA_ERR_INVALID, "src and sink must be 16-byte aligned");
+  if (n_workgroups < 1 || n_workgroups > NOSA_MAX_READ_WORKGROUPS)
+    return fail(NOSA_ERR_INVALID, "n_workgroups outside [1, NOSA_MAX_READ_WORKGROUPS]");
+  return hip_result(nosa::launch_hbm_read(src, bytes, n_workgroups, sink, stream));
+}
+
 int nosa_link_copy(const void *src, void *dst, size_t bytes, int32_t n_workgroups,
                    hipStream_t stream) {
   if (!src || !dst) return fail(NOSA_ERR_INVALID, "src / dst is NULL");

@@ -184,6 +184,38 @@ __global__ __launch_bounds__(256) void link_copy_kernel(const uint4 *__restrict_
   }
 }
 
+// grid (n_wg), block 256: a plain streaming read, grid-stride over 16-byte
+// loads with 8 of them in flight per thread, folded by XOR into one 16-byte
+// word per thread (so the loads cannot be dropped), for measuring how fast
+// the chip streams HBM with no other work.
+__global__ __launch_bounds__(256) void hbm_read_kernel(const uint4 *__restrict__ src,
+                                                       size_t n16, uint4 *__restrict__ sink) {
+  constexpr int kPer = 8;
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  uint4 acc = make_uint4(0, 0, 0, 0);
+  for (; i + (kPer - 1) * stride < n16; i += kPer * stride) {
+    uint4 v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) v[j] = src[i + j * stride];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      acc.x ^= v[j].x;
+      acc.y ^= v[j].y;
+      acc.z ^= v[j].z;
+      acc.w ^= v[j].w;
+    }
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = src[i];
+    acc.x ^= v.x;
+    acc.y ^= v.y;
+    acc.z ^= v.z;
+    acc.w ^= v.w;
+  }
+  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 // Resident KV: every selected block already sits in the device pool at its
 // own index, so phys = sel and nothing moves. grid (P), block 64.
 __global__ __launch_bounds__(64) void resident_phys_kernel(
@@ -207,6 +239,12 @@ hipError_t launch_link_copy(const void *src, void *dst, size_t bytes, int n_wg,
                             hipStream_t s) {
   link_copy_kernel<<<dim3(n_wg), 256, 0, s>>>(static_cast<const uint4 *>(src),
                                               static_cast<uint4 *>(dst), bytes / 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_hbm_read(const void *src, size_t bytes, int n_wg, void *sink, hipStream_t s) {
+  hbm_read_kernel<<<dim3(n_wg), 256, 0, s>>>(static_cast<const uint4 *>(src), bytes / 16,
+                                             static_cast<uint4 *>(sink));
   return hipGetLastError();
 }
 

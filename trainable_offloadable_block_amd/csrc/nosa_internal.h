@@ -69,6 +69,8 @@ hipError_t launch_prefill_attend(const Dims &d, const nosa_state &st,
                                  const uint16_t *q, int T, int pos0,
                                  const int32_t *sel, const int32_t *n_sel,
                                  float *out, hipStream_t s);
+hipError_t launch_hbm_read(const void *src, size_t bytes, int n_wg, void *sink,
+                           hipStream_t s);
 hipError_t launch_link_copy(const void *src, void *dst, size_t bytes, int n_wg,
                             hipStream_t s);
 // n_wg > 0: copy with that many looping workgroups; 0: one per list entry
