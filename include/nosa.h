@@ -429,11 +429,13 @@ int nosa_hbm_read(const void *src, size_t bytes, int32_t n_workgroups, void *sin
  *      workgroup moves at a time: 1, 2, 4 or 8.
  *  NOSA_TUNE_SELECT_POOL  how a selection's last workgroup finishes: 0 the
  *      library's choice (2 where it applies), 1 the general path (kinds of
- *      every block in LDS, candidates as R per thread, list and eligibility
- *      by passes over the blocks), 2 for a pair of at most 256 candidates,
- *      one candidate per thread (kinds, list places and eligibility bits
- *      from per-thread flags and two counts). Both give the same
- *      selections.
+ *      every block in LDS, candidates as R per thread, each stage an exact
+ *      histogram range refinement, list and eligibility by passes over the
+ *      blocks), 2 for a pair of at most 256 candidates, one candidate per
+ *      thread (each stage ranks the candidates: a bitonic sort per wave and
+ *      a binary search in each wave's run; kinds, list places and
+ *      eligibility bits from per-thread flags and two counts). Both give
+ *      the same selections.
  * The per-pair arrival counters of the select and decode workspaces sit at
  * the start of each workspace whatever the launch shape, so a change
  * between calls never leaves them on non-zero bytes. */

@@ -704,9 +704,10 @@ def test_select_splits_per_workgroup_do_not_change_results():
 @pytest.mark.parametrize("case", ["g4_6k", "g8_boundary_17k", "tiny_candidates"])
 def test_select_pool_paths_agree(case):
     """The selection's two finishing paths -- general (kinds of every block
-    in LDS, passes over the blocks) and one candidate per thread -- give the
-    same selection, kinds, block scores and state, bit for bit, step after
-    step. The first decoding step ranks stage 2 (every candidate still
+    in LDS, histogram range refinement, passes over the blocks) and one
+    candidate per thread (bitonic sort per wave and binary-search ranks) --
+    give the same selection, kinds, block scores and state, bit for bit,
+    step after step. The first decoding step ranks stage 2 (every candidate still
     eligible); the 17K case starts at 255 candidates and steps past 256,
     where the library leaves the one-candidate-per-thread path; the last case
     has fewer candidates than k_q, and a sequence with none."""

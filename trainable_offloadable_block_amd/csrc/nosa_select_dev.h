@@ -557,15 +557,115 @@ __device__ __forceinline__ void select_stages(const Dims &d, int p, int n_cand, 
   }
 }
 
+// 32-bit value of lane (lane ^ D) of the wave for D = 1, 2, 4, 8, on DPP:
+// quad permutations for 1 and 2; a row rotation by 8 (within a row of 16
+// lanes it is the xor); for 4, a shift by 4 either way within the row, each
+// lane taking the one that stays inside its group of 8.
+template <int D>
+__device__ inline uint32_t xor_lane_dpp(uint32_t v, int lane) {
+  const int x = static_cast<int>(v);
+  if constexpr (D == 4) {
+    const int up = __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0xF, true);    // row_shl:4, lane + 4
+    const int dn = __builtin_amdgcn_mov_dpp(x, 0x114, 0xF, 0xF, true);    // row_shr:4, lane - 4
+    return static_cast<uint32_t>((lane & 4) ? dn : up);
+  } else {
+    constexpr int ctrl = D == 1 ? 0xB1 : (D == 2 ? 0x4E : 0x128);        // quad_perm / row_ror:8
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(x, ctrl, 0xF, 0xF, true));
+  }
+}
+
+// One compare-exchange step of a bitonic network over the wave's lanes: the
+// lane keeps the larger of its key and lane (lane ^ D)'s when it is the
+// lower lane of a descending block of K lanes or the upper lane of an
+// ascending one. D = 16 and 32 use the permlane swaps, which hand each lane
+// both keys of its pair (the same pair order for both words of a key), so
+// the lane keeps their larger or smaller one.
+template <int K, int D>
+__device__ inline uint64_t bitonic_step(uint64_t v, int lane) {
+  const bool keep_larger = ((lane & D) == 0) == ((lane & K) == 0);
+  const uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  if constexpr (D <= 8) {
+    const uint64_t o = (static_cast<uint64_t>(xor_lane_dpp<D>(hi, lane)) << 32) |
+                       xor_lane_dpp<D>(lo, lane);
+    return (v > o) == keep_larger ? v : o;
+  } else {
+    const auto h = D == 16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                           : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const auto l = D == 16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                           : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const uint64_t a = (static_cast<uint64_t>(h[0]) << 32) | l[0];
+    const uint64_t b = (static_cast<uint64_t>(h[1]) << 32) | l[1];
+    return (a > b) == keep_larger ? a : b;
+  }
+}
+
+// Rank of thread t's key among the workgroup's kTopkThreads keys, one per
+// thread (distinct where nonzero; zero keys are below every other key): the
+// number of keys above it. Each wave sorts its 64 keys in descending order
+// with a bitonic network of 21 compare-exchange steps on cross-lane moves;
+// the four sorted runs go to srt (LDS, kTopkThreads entries); after one
+// barrier each thread counts the keys above its own in every run by binary
+// search (7 dependent reads, the four runs at once). A fixed cost whatever the keys,
+// where a range refinement's rounds depend on how they spread and tie. The
+// caller syncs before srt is written again. Called by all threads, with
+// every lane of each wave active (the network moves values between lanes).
+__device__ __forceinline__ uint32_t wg_rank256(uint64_t key, uint64_t *srt) {
+  const int t = threadIdx.x, lane = t & 63;
+  uint64_t v = key;
+  v = bitonic_step<2, 1>(v, lane);
+  v = bitonic_step<4, 2>(v, lane);
+  v = bitonic_step<4, 1>(v, lane);
+  v = bitonic_step<8, 4>(v, lane);
+  v = bitonic_step<8, 2>(v, lane);
+  v = bitonic_step<8, 1>(v, lane);
+  v = bitonic_step<16, 8>(v, lane);
+  v = bitonic_step<16, 4>(v, lane);
+  v = bitonic_step<16, 2>(v, lane);
+  v = bitonic_step<16, 1>(v, lane);
+  v = bitonic_step<32, 16>(v, lane);
+  v = bitonic_step<32, 8>(v, lane);
+  v = bitonic_step<32, 4>(v, lane);
+  v = bitonic_step<32, 2>(v, lane);
+  v = bitonic_step<32, 1>(v, lane);
+  v = bitonic_step<64, 32>(v, lane);
+  v = bitonic_step<64, 16>(v, lane);
+  v = bitonic_step<64, 8>(v, lane);
+  v = bitonic_step<64, 4>(v, lane);
+  v = bitonic_step<64, 2>(v, lane);
+  v = bitonic_step<64, 1>(v, lane);
+  srt[t] = v;                                      // run w: srt[64 w .. 64 w + 63], descending
+  __syncthreads();
+  // per run, the number of keys above `key` by binary lifting: pos grows by
+  // each power of two whose last key is still above (indices stay <= 62),
+  // then by one if the key at pos is (a run whose 64 keys are all above)
+  uint32_t pos[kTopkThreads / 64];
+#pragma unroll
+  for (int r = 0; r < kTopkThreads / 64; ++r) pos[r] = 0;
+#pragma unroll
+  for (int step = 32; step >= 1; step >>= 1) {
+    uint64_t m[kTopkThreads / 64];
+#pragma unroll
+    for (int r = 0; r < kTopkThreads / 64; ++r) m[r] = srt[64 * r + pos[r] + step - 1];
+#pragma unroll
+    for (int r = 0; r < kTopkThreads / 64; ++r) pos[r] += m[r] > key ? step : 0;
+  }
+  uint32_t above = 0;
+#pragma unroll
+  for (int r = 0; r < kTopkThreads / 64; ++r) above += pos[r] + (srt[64 * r + pos[r]] > key ? 1u : 0u);
+  return above;
+}
+
 // Both stages, the ascending selection list and the eligibility update of
 // pair p when it has at most kTopkThreads candidates: thread t owns candidate
 // t, block n_sink + t (none past n_cand), so a block's kind, its place in the
 // list and its eligibility bit need no LDS array of kinds and no pass over
 // the blocks. kq: its stage-1 key (0 unless stage 1 runs); e_raw: its
 // agnostic score; el_sh: the eligibility words as they stand; tk.clr zero
-// (topk_lds_init, then a barrier). Each stage is the exact top-k that
-// select_stages runs, so the sets are the same; stage 2 takes every eligible
-// candidate stage 1 left when they do not outnumber k_e', as there. The list
+// (topk_lds_init, then a barrier). Each stage keeps the candidates with fewer
+// than k keys above their own (wg_rank256: the keys are distinct, so these
+// are exactly the sets select_stages' range refinement keeps); stage 2 takes
+// every eligible candidate stage 1 left when they do not outnumber k_e', as
+// there. The list
 // holds the sink blocks, the kept candidates, then the window blocks
 // (ascending block order), cut at k. Called by all threads.
 __device__ __forceinline__ void finish_select_small(const Dims &d, const nosa_state &st, int p,
@@ -575,14 +675,15 @@ __device__ __forceinline__ void finish_select_small(const Dims &d, const nosa_st
                                                     int32_t *n_sel, uint8_t *kind_out,
                                                     TopkLds &tk) {
   __shared__ int cnt_sh[2][kTopkThreads / 64];
+  __shared__ uint64_t srt[kTopkThreads];
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   const int bb = d.n_sink + t;
   const bool cand = t < n_cand;
   // 1. stage 1: the k_q candidates of highest query-aware score
   bool in_q = false;
   if (do_q) {                                      // uniform
-    const uint64_t k1[1] = {kq};
-    wg_topk_marks<1>(k1, d.k_q, [&](int) { in_q = true; }, tk, p, 12);   // rounds -> slot 12
+    const uint32_t rank = wg_rank256(kq, srt);     // every thread takes part
+    in_q = kq != 0 && rank < static_cast<uint32_t>(d.k_q);
   }
   NOSA_PHASE(p, kPhasePoolRow, 7);
   // 2. stage 2 over the eligible candidates stage 1 left; the candidates the
@@ -605,9 +706,10 @@ __device__ __forceinline__ void finish_select_small(const Dims &d, const nosa_st
   NOSA_PHASE_VAL(p, kPhasePoolRow, 14, n_rank);
   int row = 1;
   if (n_rank > d.k_e_dyn) {                        // uniform: rank them by agnostic score
-    const uint64_t k1[1] = {e_cand ? compose_key(e_raw, bb) : 0};
-    bool in_e = false;
-    wg_topk_marks<1>(k1, d.k_e_dyn, [&](int) { in_e = true; }, tk, p, 13);   // ends with a barrier
+    const uint64_t ke = e_cand ? compose_key(e_raw, bb) : 0;
+    const uint32_t rank = wg_rank256(ke, srt);     // srt's reads ended before the barrier
+    const bool in_e = ke != 0 && rank < static_cast<uint32_t>(d.k_e_dyn);
+    NOSA_PHASE_VAL(p, kPhasePoolRow, 13, 1);
     // the marks so far leave out the candidates stage 2 could have taken;
     // add those it drops (no one has read the marks yet)
     if (e_cand && !in_e) atomicOr(&tk.clr[(bb >> 5) - w_lo], 1u << (bb & 31));
