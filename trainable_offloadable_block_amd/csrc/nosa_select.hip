@@ -5,8 +5,8 @@
 //  - every workgroup scores one split (or, at long contexts, several one
 //    after another): query-aware logits of the GQA group against the
 //    compressed keys on MFMA, l = q . c / sqrt(128) (kept in the log2 domain
-//    for the hardware exp2); per split and head, m = max l, Z =
-//    sum exp(l - m); it publishes e = exp(l - m) per
+//    for the hardware exp2); per split and head, m = max l (published in
+//    the log2 domain), Z = sum exp(l - m); it publishes e = exp(l - m) per
 //    chunk and (m, Z) with device-coherent stores and arrives on the pair's
 //    counter; the newest chunk is left to
 //  - the pair's last workgroup, which scores it, combines the split

@@ -217,7 +217,7 @@ __device__ __forceinline__ void score_compute(const Dims &d, int C, ScoreIn &in,
     const int hh = threadIdx.x;
     const float Mh = fmaxf(fmaxf(red_m[0][hh], red_m[1][hh]), fmaxf(red_m[2][hh], red_m[3][hh]));
     const float Zh = (red_z[0][hh] + red_z[1][hh]) + (red_z[2][hh] + red_z[3][hh]);
-    put(&stats[2 * hh], Mh * 0.6931471805599453f);   // back to the natural domain
+    put(&stats[2 * hh], Mh);                       // log2 domain, as the weights
     put(&stats[2 * hh + 1], Zh);
   }
 }
@@ -655,6 +655,23 @@ __device__ __forceinline__ uint32_t wg_rank256(uint64_t key, uint64_t *srt) {
   return above;
 }
 
+// ORs a wave's 64-lane mask of blocks base .. base + 63 into the eligibility
+// clear words clr[word - w_lo] (at most three words; lane 0 does it, one LDS
+// atomic per word touched).
+__device__ inline void mark_clear(uint64_t m, int base, int w_lo, uint32_t *clr) {
+  if ((threadIdx.x & 63) != 0 || m == 0) return;
+  const int wd0 = base >> 5, sh = base & 31;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    // bits of word wd0 + i: blocks 32 (wd0 + i) .. + 31, i.e. mask bits
+    // 32 i - sh .. 32 i - sh + 31
+    const int lo = 32 * i - sh;
+    const uint64_t part = lo >= 0 ? (lo < 64 ? m >> lo : 0ull) : m << (-lo);
+    const uint32_t bits = static_cast<uint32_t>(part);
+    if (bits) atomicOr(&clr[wd0 + i - w_lo], bits);
+  }
+}
+
 // Both stages, the ascending selection list and the eligibility update of
 // pair p when it has at most kTopkThreads candidates: thread t owns candidate
 // t, block n_sink + t (none past n_cand), so a block's kind, its place in the
@@ -692,7 +709,7 @@ __device__ __forceinline__ void finish_select_small(const Dims &d, const nosa_st
   const int w_lo = d.n_sink >> 5;
   const bool e_cand = do_e && cand && !in_q && ((el_sh[bb >> 5] >> (bb & 31)) & 1u);
   bool inc = in_q || e_cand;
-  if (cand && !inc) atomicOr(&tk.clr[(bb >> 5) - w_lo], 1u << (bb & 31));
+  mark_clear(__ballot(cand && !inc), d.n_sink + 64 * w, w_lo, tk.clr);
   const uint64_t m_e = __ballot(e_cand);
   uint64_t m_in = __ballot(inc);
   if (lane == 0) {
@@ -712,7 +729,7 @@ __device__ __forceinline__ void finish_select_small(const Dims &d, const nosa_st
     NOSA_PHASE_VAL(p, kPhasePoolRow, 13, 1);
     // the marks so far leave out the candidates stage 2 could have taken;
     // add those it drops (no one has read the marks yet)
-    if (e_cand && !in_e) atomicOr(&tk.clr[(bb >> 5) - w_lo], 1u << (bb & 31));
+    mark_clear(__ballot(e_cand && !in_e), d.n_sink + 64 * w, w_lo, tk.clr);
     inc = in_q || in_e;
     m_in = __ballot(inc);
     if (lane == 0) cnt_sh[0][w] = __popcll(m_in);  // n_rank's reads ended before a barrier
@@ -930,7 +947,8 @@ __device__ __forceinline__ void chunk_scores(const float4 (&eb)[kLoadBatch], int
   }
 }
 
-// Pooling's first step: per-split factors exp(m_split - M) / Z of each
+// Pooling's first step: per-split factors exp(m_split - M) / Z (the maxima
+// in the log2 domain, so one hardware exp2 each) of each
 // head's softmax over all complete chunks (0 for the padding heads), into
 // f_sh[split][Gp]. Thread (t / 16, t % 16) takes head t / 16's statistics
 // of splits t % 16 + 16 i; stv_raw holds the first kStatBatches of them,
@@ -957,13 +975,13 @@ __device__ __forceinline__ void pool_factors(const Dims &d, int Gp, int used, bo
     float z = 0.0f;
 #pragma unroll
     for (int i = 0; i < kStatBatches; ++i) {
-      es[i] = sv[i].y > 0.0f ? expf(sv[i].x - m) : 0.0f;
+      es[i] = sv[i].y > 0.0f ? __builtin_amdgcn_exp2f(sv[i].x - m) : 0.0f;
       z += sv[i].y * es[i];
     }
     if (real)
       for (int s = sh_j + kPre; s < used; s += 16) {
         const float2 v = load2_coherent(sr, 8 * (s * d.G + sh_h));
-        if (v.y > 0.0f) z += v.y * expf(v.x - m);
+        if (v.y > 0.0f) z += v.y * __builtin_amdgcn_exp2f(v.x - m);
       }
     z = row16_sum(z);
     const float rz = real ? 1.0f / z : 0.0f;
@@ -972,7 +990,7 @@ __device__ __forceinline__ void pool_factors(const Dims &d, int Gp, int used, bo
       if (sh_j + 16 * i < used) f_sh[(sh_j + 16 * i) * Gp + sh_h] = es[i] * rz;
     for (int s = sh_j + kPre; s < used; s += 16) {
       const float2 v = real ? load2_coherent(sr, 8 * (s * d.G + sh_h)) : make_float2(-INFINITY, 0.0f);
-      f_sh[s * Gp + sh_h] = v.y > 0.0f ? expf(v.x - m) * rz : 0.0f;
+      f_sh[s * Gp + sh_h] = v.y > 0.0f ? __builtin_amdgcn_exp2f(v.x - m) * rz : 0.0f;
     }
   }
   __syncthreads();
