@@ -55,6 +55,11 @@ def parse():
                     help="skip the many-query block-score (sparse prefill) leg")
     ap.add_argument("--only-next", action="store_true",
                     help="run only the GQA-16 96-block leg and print its JSON")
+    ap.add_argument("--phase-workload", type=int, default=2, choices=(1, 2, 3, 4, 5),
+                    help="with --phase-clocks: the workload (2: the 16K stack of 8 "
+                         "layers; others as stacks of 4)")
+    ap.add_argument("--only-32k", action="store_true",
+                    help="run only the offloaded 32K stack leg and print its JSON")
     ap.add_argument("--only-8b", action="store_true",
                     help="run only the offloaded 8B-shaped 64K leg and print its JSON")
     ap.add_argument("--only-prefill", action="store_true",
@@ -65,6 +70,9 @@ def parse():
                     help="run only the layer-ahead leg and print its JSON")
     ap.add_argument("--select-pool", type=int, default=0, choices=(0, 1, 2),
                     help="nosa_set_tuning NOSA_TUNE_SELECT_POOL for the whole run "
+                         "(0: the library's choice)")
+    ap.add_argument("--select-subs", type=int, default=0,
+                    help="nosa_set_tuning NOSA_TUNE_SELECT_SUBS for the whole run "
                          "(0: the library's choice)")
     ap.add_argument("--decode-bps", type=int, default=0,
                     help="nosa_set_tuning NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT for the whole "
@@ -1103,9 +1111,11 @@ def warm_leg(dev, workers, W=8, K=120):
             "breakdown_us": m["breakdown"]}
 
 
-def phase_clocks(dev, workers, R=8, W=12, samples=24):
+def phase_clocks(dev, workers, R=8, W=12, samples=24, wl_id=2):
     """Phase breakdown of the fused append + select and the decode launches
-    on the 16K stack, from the timing build's in-kernel clocks (load it with
+    on a stack of R layers of workload wl_id (the 16K stack by default; an
+    offloaded workload runs its delta fetch between the two), from the
+    timing build's in-kernel clocks (load it with
     NOSA_LIBRARY=trainable_offloadable_block_amd/libnosa_clocks.so). Every
     other sampled step stops after the last layer's append + select (its
     clocks copied out, the earlier launches having run back to back); the
@@ -1129,12 +1139,12 @@ def phase_clocks(dev, workers, R=8, W=12, samples=24):
         fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
         readers[name] = fn
     NP, ROWS, SLOTS = 512, 40, 16
-    wl = WORKLOADS[2]
+    wl = WORKLOADS[wl_id]
     P = wl.batch * wl.n_kv_heads
     n_tok = W + samples
     shape = LayerShape(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_sink_blocks,
                        wl.window_tokens, wl.k_blocks, wl.k_q_blocks, wl.k_e_blocks,
-                       wl.context + n_tok)
+                       wl.context + n_tok, offload=wl.offload)
     layers, inputs = [], []
     with cf.ThreadPoolExecutor(workers) as pool:
         for li in range(R):
@@ -1151,6 +1161,7 @@ def phase_clocks(dev, workers, R=8, W=12, samples=24):
         for li, ly in enumerate(layers):
             q, kn, vn = (x[t] for x in inputs[li])
             ly.append_select(kn, vn, q, want_kind=False)
+            ly.fetch()
             ly.decode(q)
     t_warm = time.perf_counter()
     while time.perf_counter() - t_warm < CLOCK_WARM_S:
@@ -1169,6 +1180,7 @@ def phase_clocks(dev, workers, R=8, W=12, samples=24):
             if li == R - 1 and sidx % 2 == 0:
                 torch.cuda.synchronize()
                 sel_runs.append(read("append_select"))
+            ly.fetch()
             ly.decode(q)
         torch.cuda.synchronize()
         if sidx % 2 == 1:
@@ -1278,11 +1290,13 @@ def main():
     workers = min(16, len(os.sched_getaffinity(0)))
     from trainable_offloadable_block_amd import _lib as L
     for knob, v in ((L.NOSA_TUNE_SELECT_POOL, args.select_pool),
-                    (L.NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT, args.decode_bps)):
+                    (L.NOSA_TUNE_DECODE_BLOCKS_PER_SPLIT, args.decode_bps),
+                    (L.NOSA_TUNE_SELECT_SUBS, args.select_subs)):
         if v:
             L.check(L.lib().nosa_set_tuning(knob, v), "set_tuning")
     if args.phase_clocks:
-        print(json.dumps(phase_clocks(dev, workers)), flush=True)
+        print(json.dumps(phase_clocks(dev, workers, R=8 if args.phase_workload == 2 else 4,
+                                      wl_id=args.phase_workload)), flush=True)
         return
     if args.only_host_link:
         link = host_link_peak(dev)
@@ -1303,6 +1317,10 @@ def main():
         return
     if args.only_prefill:
         print(json.dumps(prefill_scores_leg(dev, workers)), flush=True)
+        return
+    if args.only_32k:
+        link = host_link_peak(dev)
+        print(json.dumps(offload_32k_leg(dev, workers, link_peak=link["peak_GBps"])), flush=True)
         return
     if args.only_8b:
         print(json.dumps(offload_8b_64k_leg(dev, workers)), flush=True)

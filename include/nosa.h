@@ -431,11 +431,11 @@ int nosa_hbm_read(const void *src, size_t bytes, int32_t n_workgroups, void *sin
  *      library's choice (2 where it applies), 1 the general path (kinds of
  *      every block in LDS, candidates as R per thread, each stage an exact
  *      histogram range refinement, list and eligibility by passes over the
- *      blocks), 2 for a pair of at most 256 candidates, one candidate per
- *      thread (each stage ranks the candidates: a bitonic sort per wave and
- *      a binary search in each wave's run; kinds, list places and
- *      eligibility bits from per-thread flags and two counts). Both give
- *      the same selections.
+ *      blocks), 2 for a pair of at most 512 candidates, one or two per
+ *      thread (up to 256, each stage ranks them: a bitonic sort per wave and
+ *      a binary search in each wave's run; above, the range refinement;
+ *      kinds, list places and eligibility bits from per-thread flags and
+ *      per-wave counts). Both give the same selections.
  * The per-pair arrival counters of the select and decode workspaces sit at
  * the start of each workspace whatever the launch shape, so a change
  * between calls never leaves them on non-zero bytes. */

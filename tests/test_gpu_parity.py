@@ -701,21 +701,34 @@ def test_select_splits_per_workgroup_do_not_change_results():
             assert torch.equal(sa[n], sb[n]), f"step {t}: state {n}"
 
 
-@pytest.mark.parametrize("case", ["g4_6k", "g8_boundary_17k", "tiny_candidates"])
+@pytest.mark.parametrize("case", ["g4_6k", "g8_boundary_17k", "g8_30k", "g8_boundary_34k",
+                                  "tiny_candidates"])
 def test_select_pool_paths_agree(case):
     """The selection's two finishing paths -- general (kinds of every block
-    in LDS, histogram range refinement, passes over the blocks) and one
-    candidate per thread (bitonic sort per wave and binary-search ranks) --
-    give the same selection, kinds, block scores and state, bit for bit,
-    step after step. The first decoding step ranks stage 2 (every candidate still
-    eligible); the 17K case starts at 255 candidates and steps past 256,
-    where the library leaves the one-candidate-per-thread path; the last case
-    has fewer candidates than k_q, and a sequence with none."""
+    in LDS, histogram range refinement, passes over the blocks) and one or
+    two candidates per thread (bitonic sorts per wave and binary-search
+    ranks) -- give the same selection, kinds, block scores and state, bit
+    for bit, step after step. The first decoding step ranks stage 2 (every
+    candidate still eligible); the 17K case starts at 255 candidates and
+    steps past 256, where a thread takes two candidates; the 30K case has
+    about 450; the 34K case starts at 510 and steps past 512, where the
+    library leaves the per-thread path; the last case has fewer candidates
+    than k_q, and a sequence with none."""
     if case == "g4_6k":
         wl = small_workload(231, context=6000, steps=20, k_blocks=12, k_q_blocks=4, k_e_blocks=8)
         lengths = [6000, 5711]
     elif case == "g8_boundary_17k":
         wl = small_workload(232, batch=1, n_q_heads=16, n_kv_heads=2, context=17350, steps=140,
+                            window_tokens=1024, k_blocks=64, k_q_blocks=16, k_e_blocks=48,
+                            n_hot=8)
+        lengths = None
+    elif case == "g8_30k":
+        wl = small_workload(234, batch=2, n_q_heads=16, n_kv_heads=2, context=30000, steps=40,
+                            window_tokens=1024, k_blocks=64, k_q_blocks=16, k_e_blocks=48,
+                            n_hot=8)
+        lengths = [30000, 28100]
+    elif case == "g8_boundary_34k":
+        wl = small_workload(235, batch=1, n_q_heads=16, n_kv_heads=2, context=33700, steps=200,
                             window_tokens=1024, k_blocks=64, k_q_blocks=16, k_e_blocks=48,
                             n_hot=8)
         lengths = None

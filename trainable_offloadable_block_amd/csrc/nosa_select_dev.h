@@ -307,7 +307,7 @@ __device__ inline uint32_t wave_incl_scan(uint32_t x) {
 
 constexpr int kTopkBits = 8, kTopkBins = 1 << kTopkBits;   // bins per refinement round
 
-constexpr int kSmallWords = 16;   // eligibility words <= 256 consecutive candidates touch (<= 9)
+constexpr int kSmallWords = 32;   // eligibility words <= 512 consecutive candidates touch (<= 17)
 
 struct __align__(16) TopkLds {
   uint32_t hist[2][kTopkBins];
@@ -599,19 +599,9 @@ __device__ inline uint64_t bitonic_step(uint64_t v, int lane) {
   }
 }
 
-// Rank of thread t's key among the workgroup's kTopkThreads keys, one per
-// thread (distinct where nonzero; zero keys are below every other key): the
-// number of keys above it. Each wave sorts its 64 keys in descending order
-// with a bitonic network of 21 compare-exchange steps on cross-lane moves;
-// the four sorted runs go to srt (LDS, kTopkThreads entries); after one
-// barrier each thread counts the keys above its own in every run by binary
-// search (7 dependent reads, the four runs at once). A fixed cost whatever the keys,
-// where a range refinement's rounds depend on how they spread and tie. The
-// caller syncs before srt is written again. Called by all threads, with
-// every lane of each wave active (the network moves values between lanes).
-__device__ __forceinline__ uint32_t wg_rank256(uint64_t key, uint64_t *srt) {
-  const int t = threadIdx.x, lane = t & 63;
-  uint64_t v = key;
+// The wave's 64 keys (one per lane) in descending order: a bitonic network
+// of 21 compare-exchange steps on cross-lane moves.
+__device__ __forceinline__ uint64_t wave_sort64(uint64_t v, int lane) {
   v = bitonic_step<2, 1>(v, lane);
   v = bitonic_step<4, 2>(v, lane);
   v = bitonic_step<4, 1>(v, lane);
@@ -632,26 +622,43 @@ __device__ __forceinline__ uint32_t wg_rank256(uint64_t key, uint64_t *srt) {
   v = bitonic_step<64, 8>(v, lane);
   v = bitonic_step<64, 4>(v, lane);
   v = bitonic_step<64, 2>(v, lane);
-  v = bitonic_step<64, 1>(v, lane);
-  srt[t] = v;                                      // run w: srt[64 w .. 64 w + 63], descending
+  return bitonic_step<64, 1>(v, lane);
+}
+
+// Rank of thread t's key among the workgroup's kTopkThreads keys, one per
+// thread (distinct where nonzero; zero keys are below every other key): the
+// number of keys above it. Each wave sorts its 64 keys in descending order
+// (wave_sort64) and writes them to srt (LDS, kTopkThreads entries) as one
+// run; after one barrier each thread counts the keys above its own in every
+// run by binary lifting (7 dependent reads, the four runs at once). A fixed
+// cost whatever the keys, where a range refinement's rounds depend on how
+// they spread and tie (with two keys per thread, merging each wave's two
+// sorted runs and searching runs of 128 measured slower than the
+// refinement: 2.4 against 1.9 us at 32K). The caller syncs before srt is
+// written again. Called by all threads, with every lane of each wave active
+// (the network moves values between lanes).
+__device__ __forceinline__ uint32_t wg_rank256(uint64_t key, uint64_t *srt) {
+  constexpr int NR = kTopkThreads / 64;            // runs, one per wave
+  const int t = threadIdx.x, lane = t & 63;
+  srt[t] = wave_sort64(key, lane);                 // run w: srt[64 w .. 64 w + 63]
   __syncthreads();
   // per run, the number of keys above `key` by binary lifting: pos grows by
   // each power of two whose last key is still above (indices stay <= 62),
   // then by one if the key at pos is (a run whose 64 keys are all above)
-  uint32_t pos[kTopkThreads / 64];
+  uint32_t pos[NR];
 #pragma unroll
-  for (int r = 0; r < kTopkThreads / 64; ++r) pos[r] = 0;
+  for (int q = 0; q < NR; ++q) pos[q] = 0;
 #pragma unroll
   for (int step = 32; step >= 1; step >>= 1) {
-    uint64_t m[kTopkThreads / 64];
+    uint64_t m[NR];
 #pragma unroll
-    for (int r = 0; r < kTopkThreads / 64; ++r) m[r] = srt[64 * r + pos[r] + step - 1];
+    for (int q = 0; q < NR; ++q) m[q] = srt[64 * q + pos[q] + step - 1];
 #pragma unroll
-    for (int r = 0; r < kTopkThreads / 64; ++r) pos[r] += m[r] > key ? step : 0;
+    for (int q = 0; q < NR; ++q) pos[q] += m[q] > key ? step : 0;
   }
   uint32_t above = 0;
 #pragma unroll
-  for (int r = 0; r < kTopkThreads / 64; ++r) above += pos[r] + (srt[64 * r + pos[r]] > key ? 1u : 0u);
+  for (int q = 0; q < NR; ++q) above += pos[q] + (srt[64 * q + pos[q]] > key ? 1u : 0u);
   return above;
 }
 
@@ -673,66 +680,104 @@ __device__ inline void mark_clear(uint64_t m, int base, int w_lo, uint32_t *clr)
 }
 
 // Both stages, the ascending selection list and the eligibility update of
-// pair p when it has at most kTopkThreads candidates: thread t owns candidate
-// t, block n_sink + t (none past n_cand), so a block's kind, its place in the
-// list and its eligibility bit need no LDS array of kinds and no pass over
-// the blocks. kq: its stage-1 key (0 unless stage 1 runs); e_raw: its
-// agnostic score; el_sh: the eligibility words as they stand; tk.clr zero
-// (topk_lds_init, then a barrier). Each stage keeps the candidates with fewer
-// than k keys above their own (wg_rank256: the keys are distinct, so these
-// are exactly the sets select_stages' range refinement keeps); stage 2 takes
-// every eligible candidate stage 1 left when they do not outnumber k_e', as
-// there. The list
-// holds the sink blocks, the kept candidates, then the window blocks
-// (ascending block order), cut at k. Called by all threads.
+// pair p when it has at most R * kTopkThreads candidates (R = 1 or 2):
+// thread t owns candidates t + 256 r, blocks n_sink + t + 256 r (none past
+// n_cand), so a block's kind, its place in the list and its eligibility bit
+// need no LDS array of kinds and no pass over the blocks. kq: their stage-1
+// keys (0 unless stage 1 runs); e0: candidate t's agnostic score (the others'
+// are read from be if stage 2 ranks); el_sh: the eligibility words as they
+// stand; tk.clr zero (topk_lds_init, then a barrier). With one candidate per
+// thread each stage keeps the candidates with fewer than k keys above their
+// own (wg_rank256: the keys are distinct, so these are exactly the sets a
+// range refinement keeps); with two, each stage is that range refinement
+// (wg_topk_marks). Stage 2 takes every eligible candidate stage 1 left when
+// they do not outnumber k_e', as select_stages does. The list holds the sink blocks, the kept
+// candidates, then the window blocks (ascending block order), cut at k.
+// Called by all threads.
+template <int R>
 __device__ __forceinline__ void finish_select_small(const Dims &d, const nosa_state &st, int p,
                                                     int nb, int win_lo, int n_cand, bool do_q,
-                                                    bool do_e, uint64_t kq, float e_raw,
+                                                    bool do_e, const uint64_t (&kq)[R],
+                                                    float e0, const float *be,
                                                     const uint32_t *el_sh, int32_t *sel,
                                                     int32_t *n_sel, uint8_t *kind_out,
                                                     TopkLds &tk) {
-  __shared__ int cnt_sh[2][kTopkThreads / 64];
-  __shared__ uint64_t srt[kTopkThreads];
+  constexpr int NW = kTopkThreads / 64;
+  __shared__ int cnt_sh[2][R][NW];
+  __shared__ uint64_t srt[R == 1 ? kTopkThreads : 1];   // wg_rank256's runs
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-  const int bb = d.n_sink + t;
-  const bool cand = t < n_cand;
+  const int w_lo = d.n_sink >> 5;
+  int bb[R];
+  bool cand[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    bb[r] = d.n_sink + t + kTopkThreads * r;
+    cand[r] = t + kTopkThreads * r < n_cand;
+  }
   // 1. stage 1: the k_q candidates of highest query-aware score
-  bool in_q = false;
+  bool in_q[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) in_q[r] = false;
   if (do_q) {                                      // uniform
-    const uint32_t rank = wg_rank256(kq, srt);     // every thread takes part
-    in_q = kq != 0 && rank < static_cast<uint32_t>(d.k_q);
+    if constexpr (R == 1) {
+      const uint32_t rank = wg_rank256(kq[0], srt);   // every thread takes part
+      in_q[0] = kq[0] != 0 && rank < static_cast<uint32_t>(d.k_q);
+    } else {
+      wg_topk_marks<R>(kq, d.k_q, [&](int r) { in_q[r] = true; }, tk, p, 12);
+    }
   }
   NOSA_PHASE(p, kPhasePoolRow, 7);
   // 2. stage 2 over the eligible candidates stage 1 left; the candidates the
   // list keeps and those it leaves out are counted and marked as if stage 2
   // took them all (the usual case), completed below otherwise
-  const int w_lo = d.n_sink >> 5;
-  const bool e_cand = do_e && cand && !in_q && ((el_sh[bb >> 5] >> (bb & 31)) & 1u);
-  bool inc = in_q || e_cand;
-  mark_clear(__ballot(cand && !inc), d.n_sink + 64 * w, w_lo, tk.clr);
-  const uint64_t m_e = __ballot(e_cand);
-  uint64_t m_in = __ballot(inc);
-  if (lane == 0) {
-    cnt_sh[0][w] = __popcll(m_e);
-    cnt_sh[1][w] = __popcll(m_in);
+  bool e_cand[R], inc[R];
+  uint64_t m_in[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    e_cand[r] = do_e && cand[r] && !in_q[r] && ((el_sh[bb[r] >> 5] >> (bb[r] & 31)) & 1u);
+    inc[r] = in_q[r] || e_cand[r];
+    mark_clear(__ballot(cand[r] && !inc[r]), d.n_sink + kTopkThreads * r + 64 * w, w_lo, tk.clr);
+    const uint64_t m_e = __ballot(e_cand[r]);
+    m_in[r] = __ballot(inc[r]);
+    if (lane == 0) {
+      cnt_sh[0][r][w] = __popcll(m_e);
+      cnt_sh[1][r][w] = __popcll(m_in[r]);
+    }
   }
   __syncthreads();
   int n_rank = 0;
 #pragma unroll
-  for (int ww = 0; ww < kTopkThreads / 64; ++ww) n_rank += cnt_sh[0][ww];
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) n_rank += cnt_sh[0][r][ww];
   NOSA_PHASE_VAL(p, kPhasePoolRow, 14, n_rank);
   int row = 1;
   if (n_rank > d.k_e_dyn) {                        // uniform: rank them by agnostic score
-    const uint64_t ke = e_cand ? compose_key(e_raw, bb) : 0;
-    const uint32_t rank = wg_rank256(ke, srt);     // srt's reads ended before the barrier
-    const bool in_e = ke != 0 && rank < static_cast<uint32_t>(d.k_e_dyn);
+    uint64_t ke[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      ke[r] = e_cand[r] ? compose_key(r == 0 ? e0 : get(&be[bb[r]]), bb[r]) : 0;
+    bool sel_e[R];
+    if constexpr (R == 1) {
+      const uint32_t rank = wg_rank256(ke[0], srt);   // srt's reads ended before the barrier
+      sel_e[0] = ke[0] != 0 && rank < static_cast<uint32_t>(d.k_e_dyn);
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) sel_e[r] = false;
+      wg_topk_marks<R>(ke, d.k_e_dyn, [&](int r) { sel_e[r] = true; }, tk);
+    }
     NOSA_PHASE_VAL(p, kPhasePoolRow, 13, 1);
-    // the marks so far leave out the candidates stage 2 could have taken;
-    // add those it drops (no one has read the marks yet)
-    mark_clear(__ballot(e_cand && !in_e), d.n_sink + 64 * w, w_lo, tk.clr);
-    inc = in_q || in_e;
-    m_in = __ballot(inc);
-    if (lane == 0) cnt_sh[0][w] = __popcll(m_in);  // n_rank's reads ended before a barrier
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const bool in_e = sel_e[r];
+      // the marks so far leave out the candidates stage 2 could have taken;
+      // add those it drops (no one has read the marks yet)
+      mark_clear(__ballot(e_cand[r] && !in_e), d.n_sink + kTopkThreads * r + 64 * w, w_lo,
+                 tk.clr);
+      inc[r] = in_q[r] || in_e;
+      m_in[r] = __ballot(inc[r]);
+      if (lane == 0) cnt_sh[0][r][w] = __popcll(m_in[r]);   // n_rank's reads ended before a barrier
+    }
     __syncthreads();
     row = 0;
   } else {
@@ -741,19 +786,25 @@ __device__ __forceinline__ void finish_select_small(const Dims &d, const nosa_st
   NOSA_PHASE(p, kPhasePoolRow, 8);
   // 3. ascending selection list: sinks, kept candidates, window
   const int n_s = min(d.n_sink, nb), n_w = max(0, nb - win_lo);
-  int off = __popcll(m_in & ((1ull << lane) - 1ull)), kept = 0;
-#pragma unroll
-  for (int ww = 0; ww < kTopkThreads / 64; ++ww) {
-    if (ww < w) off += cnt_sh[row][ww];
-    kept += cnt_sh[row][ww];
-  }
-  const int tot = n_s + kept + n_w;
   int32_t *sp = sel + (size_t)p * d.k;
   uint8_t *kp = kind_out ? kind_out + (size_t)p * d.k : nullptr;
-  if (inc && n_s + off < d.k) {
-    sp[n_s + off] = bb;
-    if (kp) kp[n_s + off] = in_q ? NOSA_KIND_QUERY : NOSA_KIND_AGNOSTIC;
+  int kept = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int off = __popcll(m_in[r] & ((1ull << lane) - 1ull)), kept_r = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      if (ww < w) off += cnt_sh[row][r][ww];
+      kept_r += cnt_sh[row][r][ww];
+    }
+    const int pos = n_s + kept + off;
+    if (inc[r] && pos < d.k) {
+      sp[pos] = bb[r];
+      if (kp) kp[pos] = in_q[r] ? NOSA_KIND_QUERY : NOSA_KIND_AGNOSTIC;
+    }
+    kept += kept_r;
   }
+  const int tot = n_s + kept + n_w;
   for (int j = t; j < n_s + n_w; j += kTopkThreads) {   // the sink and window blocks
     const bool sink = j < n_s;
     const int pos = sink ? j : j + kept;
@@ -795,17 +846,26 @@ __device__ __forceinline__ void finish_select(const Dims &d, const nosa_state &s
   __shared__ int cnt_sh[2][kTopkThreads / 64];
   const int t = threadIdx.x;
   const int w = t >> 6, lane = t & 63;
-  if (d.pool_small && n_cand <= kTopkThreads) {     // uniform: a candidate per thread
-    const int bb = d.n_sink + t;
-    uint64_t kq = 0;
-    if (do_q && t < n_cand) {
-      const float qb = block_qscore(a_sh, bb, C);
-      kq = compose_key(qb, bb);
-      if (dbg) dbg[(size_t)p * d.NB_max + bb] = qb;
+  if (d.pool_small && n_cand <= 2 * kTopkThreads) {   // uniform: a candidate or two per thread
+    uint64_t kq[2] = {0, 0};
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int bb = d.n_sink + t + kTopkThreads * r;
+      if (do_q && t + kTopkThreads * r < n_cand) {
+        const float qb = block_qscore(a_sh, bb, C);
+        kq[r] = compose_key(qb, bb);
+        if (dbg) dbg[(size_t)p * d.NB_max + bb] = qb;
+      }
     }
     NOSA_PHASE(p, kPhasePoolRow, 0);
-    finish_select_small(d, st, p, nb, win_lo, n_cand, do_q, do_e, kq, e0, el_sh, sel, n_sel,
-                        kind_out, tk);
+    if (n_cand <= kTopkThreads) {
+      const uint64_t k1[1] = {kq[0]};
+      finish_select_small<1>(d, st, p, nb, win_lo, n_cand, do_q, do_e, k1, e0, be, el_sh, sel,
+                             n_sel, kind_out, tk);
+    } else {
+      finish_select_small<2>(d, st, p, nb, win_lo, n_cand, do_q, do_e, kq, e0, be, el_sh, sel,
+                             n_sel, kind_out, tk);
+    }
     return;
   }
   // 3. both stages, with as many candidate slots per thread as needed
