@@ -6,7 +6,8 @@
 //  - the last workgroup of a pair appends the token (K, V, ring, eviction
 //    score, and the compressed key, chunk score and block score the token
 //    completes);
-//  - the others score their splits (one or several each) as the select
+//  - the others score their splits (one each unless NOSA_TUNE_SELECT_SUBS
+//    asks for several) as the select
 //    kernel does, in parallel, and arrive on the pair's counter; the last of
 //    them pools and selects. The selection does not wait for the append:
 //    the only thing it needs from it is the key of a chunk the token

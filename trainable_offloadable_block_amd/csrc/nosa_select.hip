@@ -2,8 +2,8 @@
 // 核心组件揭秘, 核心组件三; l189 article, 2.1).
 //
 // select_kernel (chunk splits x pairs), one launch:
-//  - every workgroup scores one split (or, at long contexts, several one
-//    after another): query-aware logits of the GQA group against the
+//  - every workgroup scores one split (several one after another when
+//    NOSA_TUNE_SELECT_SUBS asks for it): query-aware logits of the GQA group against the
 //    compressed keys on MFMA, l = q . c / sqrt(128) (kept in the log2 domain
 //    for the hardware exp2); per split and head, m = max l (published in
 //    the log2 domain), Z = sum exp(l - m); it publishes e = exp(l - m) per
@@ -55,12 +55,13 @@ SelectLayout select_layout(const Dims &d, int max_len) {
   const int C = chunks_for(max_len);
   s.n_splits = C > 0 ? (C + kChunksPerSplit - 1) / kChunksPerSplit : 1;
   s.c_pad = s.n_splits * kChunksPerSplit;
-  // one round of workgroups where possible: several splits per workgroup
-  // once pairs x (splits + 1) passes the chip's resident count (4 per CU)
+  // one split per workgroup, however many rounds of workgroups that takes:
+  // scoring several splits one after another in one round (the grid kept
+  // to the chip's 4 resident workgroups per CU) measured slower on every
+  // workload that needs it (offloaded 32K stack 377.3 against 373.8 K
+  // tokens/s per layer with 3 splits per workgroup; 8B-shaped 64K layer
+  // 89.6 against 87.8 K with 11)
   s.subs = 1;
-  while (s.subs < s.n_splits &&
-         (long)d.P * ((s.n_splits + s.subs - 1) / s.subs + 1) > kSelectWgBudget)
-    ++s.subs;
   if (const int v = tuning(NOSA_TUNE_SELECT_SUBS)) s.subs = min(v, s.n_splits);
   s.n_wg = (s.n_splits + s.subs - 1) / s.subs;
   s.count_off = 0;

@@ -222,8 +222,6 @@ __device__ __forceinline__ void score_compute(const Dims &d, int C, ScoreIn &in,
   }
 }
 
-constexpr int kSelectWgBudget = 1024;   // resident workgroups of one round (4 per CU)
-
 // Splits ws * subs .. ws * subs + subs - 1 of pair p (those below n_splits),
 // one after another: the newest chunk left out (split_chunks). The first
 // split's loads go out before the length is used. MULTI = false compiles
