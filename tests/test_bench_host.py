@@ -98,3 +98,72 @@ def test_generator_rounds_float64_to_bf16_once():
     assert f64_to_bf16_bits(x).tolist() == want
     with pytest.raises(ValueError):
         f64_to_bf16_bits(np.array([2.0 ** -130]))
+
+
+def _oracle_records(wl, n):
+    """Selections, kinds and outputs of layer 0 of wl for n steps, computed
+    by the oracle itself: records a faultless GPU would produce."""
+    from synth import bf16_bits_to_f64, context_kv, eviction_weights, new_tokens, queries
+    from trainable_offloadable_block_amd import _lib as L
+    to_lib = {o.SINK: L.KIND_SINK, o.WINDOW: L.KIND_WINDOW, o.QUERY: L.KIND_QUERY,
+              o.AGNOSTIC: L.KIND_AGNOSTIC}
+    G, Hkv, k = wl.group, wl.n_kv_heads, wl.k_blocks
+    P = wl.batch * Hkv
+    n_w = wl.window_tokens // 64
+    sel = np.full((n, P, k), -1, np.int32)
+    nsel = np.zeros((n, P), np.int32)
+    kind = np.zeros((n, P, k), np.uint8)
+    out = np.zeros((n, wl.batch, wl.n_q_heads, 128), np.float32)
+    for p in range(P):
+        b, g = divmod(p, Hkv)
+        K, V = context_kv(wl, 0, b, g)
+        w1, w2 = eviction_weights(wl, 0, g)
+        Kf, Vf = np.zeros((wl.context + n, 128)), np.zeros((wl.context + n, 128))
+        Kf[:wl.context], Vf[:wl.context] = bf16_bits_to_f64(K), bf16_bits_to_f64(V)
+        orc = o.PairOracle(Kf, Vf, bf16_bits_to_f64(w1), bf16_bits_to_f64(w2), wl.context,
+                           wl.n_sink_blocks, n_w, wl.k_q_blocks,
+                           wl.k_e_blocks - wl.n_sink_blocks - n_w, 1.0)
+        kn, vn = new_tokens(wl, 0, b, g)
+        q = np.stack([queries(wl, 0, b, g * G + h) for h in range(G)])
+        for t in range(n):
+            r = orc.step(bf16_bits_to_f64(kn[t]), bf16_bits_to_f64(vn[t]),
+                         bf16_bits_to_f64(q[:, t]))
+            m = len(r.sel.blocks)
+            nsel[t, p] = m
+            sel[t, p, :m] = r.sel.blocks
+            kind[t, p, :m] = [to_lib[r.sel.kinds[x]] for x in r.sel.blocks]
+            out[t, b, g * G:(g + 1) * G] = r.out
+    return sel, nsel, kind, out
+
+
+def test_cpu_baseline_parity_check():
+    """The bench's full-size parity check (the CPU baseline's oracle run
+    against the GPU's records of the same steps): records equal to the
+    oracle's pass; a query-aware block swapped for a candidate far from the
+    boundary is an unexplained difference, and that pair is followed no
+    further; an output off by more than the bar fails the verdict."""
+    from trainable_offloadable_block_amd import _lib as L
+    wl = WORKLOADS[1]
+    n = 3
+    sel, nsel, kind, out = _oracle_records(wl, n)
+    par, cpu = bench.cpu_baseline(1, 2, n, (sel, nsel, kind, out))
+    assert par["verdict"] == "pass" and par["selections_identical"] == 2 * n
+    assert par["near_ties"] == 0 and par["unexplained_differences"] == 0
+    assert par["attention_max_abs"] < 1e-6 and cpu["cores"] >= 1
+    # a planted swap at step 1 of pair 0
+    sel2, kind2 = sel.copy(), kind.copy()
+    m = int(nsel[1, 0])
+    blocks = sel2[1, 0, :m].tolist()
+    kinds = kind2[1, 0, :m].tolist()
+    i = kinds.index(L.KIND_QUERY)
+    blocks[i] = next(x for x in range(wl.n_sink_blocks, 64) if x not in blocks)
+    order = np.argsort(blocks)
+    sel2[1, 0, :m] = np.array(blocks)[order]
+    kind2[1, 0, :m] = np.array(kinds)[order]
+    par2, _ = bench.cpu_baseline(1, 2, n, (sel2, nsel, kind2, out))
+    assert par2["verdict"] == "fail" and par2["unexplained_differences"] == 1
+    assert par2["pair_steps_compared"] == 2 * n - 1
+    out3 = out.copy()
+    out3[0, 0, 0, 0] += 0.05
+    par3, _ = bench.cpu_baseline(1, 2, n, (sel, nsel, kind, out3))
+    assert par3["verdict"] == "fail" and par3["unexplained_differences"] == 0
