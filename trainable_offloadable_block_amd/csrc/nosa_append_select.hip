@@ -2,7 +2,8 @@
 // of aiwiki "NOSA", How NOSA works, in order), for callers that run them
 // back to back: the separate append launch and its dispatch disappear.
 //
-// grid (scoring workgroups + 1, pairs), 256 threads:
+// grid (scoring workgroups + 1, pairs), 256 threads, a pair's workgroups on
+// one XCD and each XCD's dispatched split by split (grid_unit_x_major):
 //  - the last workgroup of a pair appends the token (K, V, ring, eviction
 //    score, and the compressed key, chunk score and block score the token
 //    completes);
@@ -30,7 +31,7 @@ __global__ __launch_bounds__(kScoreThreads, 4) void append_select_kernel(
     int n_splits, int subs, int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
     uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
   int wg, p;
-  grid_unit(wg, p);
+  grid_unit_x_major(wg, p);
   NOSA_PHASE(p, wg, 0);
   const int n_wg = gridDim.x - 1;
   const int b = p / d.Hkv, g = p % d.Hkv;

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kScoreThreads) void forecast_select_kernel(
     int c_pad, int n_splits, int subs, int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
     uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
   int wg, p;
-  grid_unit(wg, p);
+  grid_unit_x_major(wg, p);
   __shared__ int sm_last;
   Dims df = d;                       // f is [B][Hkv][128]: a group of one head
   df.G = 1;

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kScoreThreads, 4) void select_kernel(
     int32_t *ws_count, int c_pad, int n_splits, int subs, int32_t *__restrict__ sel,
     int32_t *__restrict__ n_sel, uint8_t *__restrict__ kind_out, float *__restrict__ dbg) {
   int wg, p;
-  grid_unit(wg, p);
+  grid_unit_x_major(wg, p);
   __shared__ int sm_last;
   const int L = st.seq_len[p / d.Hkv];
   score_splits<MULTI>(d, st, q, L, ws_e, ws_stats, c_pad, n_splits, subs, wg, p);
