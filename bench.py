@@ -535,7 +535,7 @@ def hbm_read_ceiling(dev, nbytes=2 << 30, reps=3, launches=5):
     buf.fill_(0x01010101)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     by_wg = {}
-    for n_wg in (256, 512, 1024):
+    for n_wg in (64, 128, 256, 512, 1024):     # 64, 128: what one workgroup streams
         sink = torch.empty(n_wg * 256 * 4, dtype=torch.int32, device=dev)
         best = 0.0
         for _ in range(reps):
@@ -555,6 +555,7 @@ def hbm_read_ceiling(dev, nbytes=2 << 30, reps=3, launches=5):
     best_wg = max(by_wg, key=by_wg.get)
     return {"GBps": by_wg[best_wg], "workgroups": best_wg, "bytes": nbytes,
             "GBps_by_workgroups": {str(k): v for k, v in by_wg.items()},
+            "GBps_per_workgroup_at_64": round(by_wg[64] / 64, 2),
             "frac_of_peak": round(by_wg[best_wg] / HBM_PEAK_GBS, 4)}
 
 
@@ -1360,7 +1361,8 @@ def phase_clocks(dev, workers, R=8, W=12, samples=24, wl_id=2):
         for k, slot in (("stage1_rounds", 12), ("stage2_rounds", 13), ("stage2_ranked", 14)):
             sel[k].append(float(a[:, ROWS - 1, slot].mean()))
     dec = {k: [] for k in ("start", "wave_loop_end_mean", "wave_loop_end_max", "lds_merge",
-                           "published", "last_arrival", "merge_end", "slowest_pair_vs_median")}
+                           "published", "last_arrival", "merge_end", "slowest_pair_vs_median",
+                           "wave_spread_in_wg", "wg_spread_in_xcd")}
     xcd_loop = []             # per launch: mean over each XCD's workgroups of their slowest wave
     for a in dec_runs:
         rows = np.nonzero((a[:, :, 0] > 0).any(axis=0))[0]
@@ -1382,6 +1384,11 @@ def phase_clocks(dev, workers, R=8, W=12, samples=24, wl_id=2):
         unit = np.arange(P)[:, None] * ns + np.arange(ns)[None, :]
         xcd = unit // max(1, (P * ns) // 8) if (P * ns) % 8 == 0 else unit % 8
         xcd_loop.append([float(wg_end[xcd == x].mean()) for x in range(8)])
+        # slowest minus fastest wave of a workgroup, and slowest minus fastest
+        # workgroup (by its slowest wave) of an XCD: means
+        dec["wave_spread_in_wg"].append(float((loops.max(axis=2) - loops.min(axis=2)).mean()))
+        dec["wg_spread_in_xcd"].append(float(np.mean(
+            [wg_end[xcd == x].max() - wg_end[xcd == x].min() for x in range(8)])))
     out = {"workload": wl.name, "layers": R, "sampled_launches": {"append_select": len(sel_runs),
                                                                  "decode": len(dec_runs)},
            "unit": "us from the launch's first workgroup start; mean over sampled launches",
