@@ -251,24 +251,4 @@ __device__ inline void grid_unit(int &x, int &y) {
   y = L / nx;
 }
 
-// grid_unit for a grid (units per pair, pairs) whose units differ in cost
-// by their x index (a pair's scoring splits, its lighter last split and its
-// append): each XCD still holds whole pairs, but its dispatch order runs
-// over x first (unit x of all its pairs, then unit x + 1), so the units the
-// dispatcher deals out together, one per CU, are of one kind, and every
-// CU takes the same number of the heavy ones. Pair counts that are not a
-// multiple of 8 keep grid_unit's order.
-__device__ inline void grid_unit_x_major(int &x, int &y) {
-  const int nx = gridDim.x, ny = gridDim.y;
-  if ((ny & 7) != 0) {
-    grid_unit(x, y);
-    return;
-  }
-  const int L = blockIdx.x + nx * blockIdx.y;
-  const int ppx = ny >> 3;                 // pairs per XCD
-  const int j = L >> 3;                    // place in XCD (L & 7)'s dispatch order
-  x = j / ppx;
-  y = (L & 7) * ppx + j % ppx;
-}
-
 }  // namespace nosa

@@ -11,6 +11,26 @@
 namespace nosa {
 namespace {
 
+// grid_unit for a grid (units per pair, pairs) whose units differ in cost
+// by their x index (a pair's scoring splits, its lighter last split and its
+// append): each XCD still holds whole pairs, but its dispatch order runs
+// over x first (unit x of all its pairs, then unit x + 1): the heavy units
+// lead the order and spread over the XCD's CUs before the light ones, where
+// the pair-major order stacked up to three scoring splits on some CUs and
+// one on others. Pair counts that are not a multiple of 8 keep grid_unit's
+// order.
+__device__ inline void grid_unit_x_major(int &x, int &y) {
+  const int nx = gridDim.x, ny = gridDim.y;
+  if ((ny & 7) != 0) {
+    grid_unit(x, y);
+    return;
+  }
+  const int L = blockIdx.x + nx * blockIdx.y;
+  const int ppx = ny >> 3;                 // pairs per XCD
+  const int j = L >> 3;                    // place in XCD (L & 7)'s dispatch order
+  x = j / ppx;
+  y = (L & 7) * ppx + j % ppx;
+}
 
 constexpr int kScoreThreads = 256;
 constexpr int kTopkThreads = 256;
