@@ -400,9 +400,10 @@ int nosa_link_copy(const void *src, void *dst, size_t bytes, int32_t n_workgroup
                    hipStream_t stream);
 
 /* Reads `bytes` (a multiple of 16) of device memory at src with n_workgroups
- * workgroups of 256 threads, grid-stride over 16-byte loads with 8 in flight
- * per thread, and writes each thread's XOR of what it read as one 16-byte
- * word to sink[workgroup * 256 + thread] (the caller's n_workgroups * 4 KiB
+ * workgroups of 256 threads, each over its own contiguous span (the bytes
+ * split evenly, the last spans shorter or empty), with non-temporal 16-byte loads, 8
+ * in flight per thread, and writes each thread's XOR of what it read as one
+ * 16-byte word to sink[workgroup * 256 + thread] (the caller's n_workgroups * 4 KiB
  * of device memory; the XOR of all of them is the XOR of the buffer). The
  * HBM read rate of a kernel that does nothing else: the practical ceiling
  * beside the published peak that the decode's streaming (NOSA-1B 核心组件揭秘,

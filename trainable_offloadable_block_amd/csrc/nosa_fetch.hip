@@ -184,35 +184,42 @@ __global__ __launch_bounds__(256) void link_copy_kernel(const uint4 *__restrict_
   }
 }
 
-// grid (n_wg), block 256: a plain streaming read, grid-stride over 16-byte
-// loads with 8 of them in flight per thread, folded by XOR into one 16-byte
-// word per thread (so the loads cannot be dropped), for measuring how fast
-// the chip streams HBM with no other work.
+// grid (n_wg), block 256: a plain streaming read, folded by XOR into one
+// 16-byte word per thread (so the loads cannot be dropped), for measuring
+// how fast the chip streams HBM with no other work. Workgroup i reads its
+// own contiguous span of the buffer (as a decode wave reads its blocks),
+// 4 KiB per round of 16-byte non-temporal loads (the policy of the decode's
+// KV stream), 8 rounds in flight per thread.
+typedef unsigned int u32x4n __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void hbm_read_kernel(const uint4 *__restrict__ src,
                                                        size_t n16, uint4 *__restrict__ sink) {
   constexpr int kPer = 8;
-  const size_t stride = (size_t)gridDim.x * 256;
-  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = (size_t)blockIdx.x * per;
+  const size_t hi = lo + per < n16 ? lo + per : n16;
+  size_t i = lo + threadIdx.x;
   uint4 acc = make_uint4(0, 0, 0, 0);
-  for (; i + (kPer - 1) * stride < n16; i += kPer * stride) {
-    uint4 v[kPer];
+  auto fold = [&](size_t at) {
+    const u32x4n v = __builtin_nontemporal_load(reinterpret_cast<const u32x4n *>(src + at));
+    acc.x ^= v[0];
+    acc.y ^= v[1];
+    acc.z ^= v[2];
+    acc.w ^= v[3];
+  };
+  for (; i + (kPer - 1) * 256 < hi; i += kPer * 256) {
+    u32x4n v[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) v[j] = src[i + j * stride];
+    for (int j = 0; j < kPer; ++j)
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4n *>(src + i + j * 256));
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      acc.x ^= v[j].x;
-      acc.y ^= v[j].y;
-      acc.z ^= v[j].z;
-      acc.w ^= v[j].w;
+      acc.x ^= v[j][0];
+      acc.y ^= v[j][1];
+      acc.z ^= v[j][2];
+      acc.w ^= v[j][3];
     }
   }
-  for (; i < n16; i += stride) {
-    const uint4 v = src[i];
-    acc.x ^= v.x;
-    acc.y ^= v.y;
-    acc.z ^= v.z;
-    acc.w ^= v.w;
-  }
+  for (; i < hi; i += 256) fold(i);
   sink[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 

@@ -95,7 +95,9 @@ __device__ __forceinline__ void score_load_keys(const Dims &d, const uint16_t *_
     if (chunk < d.C_max) {
       const uint16_t *src = ckey + ((size_t)p * d.C_max + chunk) * kHeadDim + 8 * lg;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) in.kv[t][s] = *reinterpret_cast<const uint4 *>(src + 32 * s);
+      for (int s = 0; s < 4; ++s)   // read once per step: non-temporal
+        in.kv[t][s] = __builtin_bit_cast(
+            uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(src + 32 * s)));
     }
   }
 }
