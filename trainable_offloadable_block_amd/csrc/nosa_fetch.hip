@@ -194,33 +194,27 @@ typedef unsigned int u32x4n __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void hbm_read_kernel(const uint4 *__restrict__ src,
                                                        size_t n16, uint4 *__restrict__ sink) {
   constexpr int kPer = 8;
+  constexpr size_t kWindow = size_t(1) << 26;   // 16-byte words per buffer window (1 GiB)
   const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
   const size_t lo = (size_t)blockIdx.x * per;
   const size_t hi = lo + per < n16 ? lo + per : n16;
-  size_t i = lo + threadIdx.x;
-  uint4 acc = make_uint4(0, 0, 0, 0);
-  auto fold = [&](size_t at) {
-    const u32x4n v = __builtin_nontemporal_load(reinterpret_cast<const u32x4n *>(src + at));
-    acc.x ^= v[0];
-    acc.y ^= v[1];
-    acc.z ^= v[2];
-    acc.w ^= v[3];
-  };
-  for (; i + (kPer - 1) * 256 < hi; i += kPer * 256) {
-    u32x4n v[kPer];
+  u32x4n acc = {0u, 0u, 0u, 0u};
+  for (size_t w0 = lo; w0 < hi; w0 += kWindow) {
+    const uint32_t n = (uint32_t)(hi - w0 < kWindow ? hi - w0 : kWindow);   // words in the window
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint4 *>(src + w0), (short)0, (int)(n * 16u), 0x00020000);
+    uint32_t i = threadIdx.x;
+    for (; i + (kPer - 1) * 256 < n; i += kPer * 256) {
+      u32x4n v[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4n *>(src + i + j * 256));
+      for (int j = 0; j < kPer; ++j)
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (i + j * 256) * 16, 0, 2);   // nt
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      acc.x ^= v[j][0];
-      acc.y ^= v[j][1];
-      acc.z ^= v[j][2];
-      acc.w ^= v[j][3];
+      for (int j = 0; j < kPer; ++j) acc ^= v[j];
     }
+    for (; i < n; i += 256) acc ^= __builtin_amdgcn_raw_buffer_load_b128(r, i * 16, 0, 2);
   }
-  for (; i < hi; i += 256) fold(i);
-  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = make_uint4(acc[0], acc[1], acc[2], acc[3]);
 }
 
 // Resident KV: every selected block already sits in the device pool at its
