@@ -17,6 +17,8 @@
 //    highest agnostic score, under the never-reselect rule. Every candidate
 //    block's chunks exist before the append (the window holds at least two
 //    blocks), so nothing waits for the coming token.
+#include <algorithm>
+
 #include "nosa_select_dev.h"
 
 namespace nosa {
@@ -31,13 +33,19 @@ __device__ __forceinline__ void forecast_score(int C, const ScoreIn &in, float *
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int h = l & 15, lg = l >> 4;
   const int cg = c0 + 32 * w;
+  extern __shared__ __align__(16) uint8_t score_keys[];
+  uint4 *ks = reinterpret_cast<uint4 *>(score_keys);
+  keys_to_lds(in, ks, -1);
+  __syncthreads();
+  uint4 kv[2][4];
+  keys_from_lds(ks, kv);
   f32x4 acc[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      acc[t] = mfma16x16x32(as_bf16x8(in.kv[t][s]), as_bf16x8(in.qv[s]), acc[t]);
+      acc[t] = mfma16x16x32(as_bf16x8(kv[t][s]), as_bf16x8(in.qv[s]), acc[t]);
   }
   // lane (0, lg) holds the forecast head against chunks cg + 8*lg + m: two
   // runs of 4 contiguous logits, each one 16-byte device-coherent store when
@@ -144,6 +152,7 @@ __global__ __launch_bounds__(kScoreThreads) void forecast_select_kernel(
   for (int j = 0; j < subs; ++j) {                 // uniform: this workgroup's splits
     const int split = wg * subs + j;
     if (split >= n_splits) break;
+    if (j > 0) __syncthreads();                    // the last split's staged keys are read
     ScoreIn in;
     score_load(df, st.ckey, f, split, p, in);
     forecast_score(C, in, ws_l, c_pad, split, p);
@@ -167,8 +176,9 @@ hipError_t launch_select_forecast(const Dims &d, const nosa_state &st, const uin
   char *base = static_cast<char *>(ws);
   float *ws_l = reinterpret_cast<float *>(base + lay.e_off);
   int32_t *ws_count = reinterpret_cast<int32_t *>(base + lay.count_off);
-  const size_t lds = (size_t)lay.c_pad * sizeof(float) + (size_t)d.elig_words * sizeof(uint32_t) +
-                     (size_t)d.NB_max;
+  const size_t lds = std::max((size_t)lay.c_pad * sizeof(float) +
+                                   (size_t)d.elig_words * sizeof(uint32_t) + (size_t)d.NB_max,
+                               kScoreLdsBytes);
   forecast_select_kernel<<<dim3(lay.n_wg, d.P), kScoreThreads, lds, s>>>(
       d, st, f, ws_l, ws_count, lay.c_pad, lay.n_splits, lay.subs, sel, n_sel, kind, dbg);
   return hipGetLastError();

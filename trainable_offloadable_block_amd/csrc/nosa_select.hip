@@ -77,7 +77,7 @@ size_t select_dyn_lds(const Dims &d, const SelectLayout &lay) {
   // workgroup pools only after its scoring is done)
   return std::max(((size_t)lay.n_splits * padded_group(d.G) + lay.c_pad) * sizeof(float) +
                       (size_t)d.elig_words * sizeof(uint32_t) + (size_t)d.NB_max,
-                  kScoreTrBytes);
+                  kScoreLdsBytes);
 }
 
 hipError_t launch_select(const Dims &d, const nosa_state &st, const uint16_t *q,

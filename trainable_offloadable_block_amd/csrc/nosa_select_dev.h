@@ -64,6 +64,11 @@ typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 // 32 chunks x 16 heads
 constexpr int kScoreTrFloats = 32 * 16;
 constexpr size_t kScoreTrBytes = 4 * kScoreTrFloats * sizeof(float);   // 4 waves
+// A split's compressed keys staged in the dynamic LDS region on their way
+// from coalesced loads to the MFMA operand layout: 128 rows x 256 B (the
+// transposes above reuse the region once the products are taken)
+constexpr size_t kScoreKeyBytes = (size_t)kChunksPerSplit * kHeadDim * 2;
+constexpr size_t kScoreLdsBytes = kScoreKeyBytes > kScoreTrBytes ? kScoreKeyBytes : kScoreTrBytes;
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                            0x00020000);
@@ -75,31 +80,61 @@ __device__ inline float2 load2_coherent(__amdgpu_buffer_rsrc_t r, int byte_off) 
   return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kCoherent));
 }
 
-// Operands of one split's scoring: the group's query rows and the split's
-// stored compressed keys, as this lane's MFMA operands.
+// Operands of one split's scoring: the group's query rows as this lane's
+// MFMA operands, and the split's stored compressed keys as loaded: thread t
+// holds 16-byte words t + 256 j (j < 8) of the split's 128 rows of 256 B.
 struct ScoreIn {
-  uint4 qv[4], kv[2][4];
+  uint4 qv[4], kr[8];
 };
 
-// Issues the loads of split `split`'s compressed keys of pair p.
+// Issues the loads of split `split`'s compressed keys of pair p: each
+// instruction reads 4 whole rows (4 KiB over the workgroup), where loads in
+// the MFMA layout would read 64 B of each of 16 rows (a streaming read in
+// that pattern measured 5.6 against 7.3 TB/s for whole rows). Read once per
+// step: non-temporal.
 __device__ __forceinline__ void score_load_keys(const Dims &d, const uint16_t *__restrict__ ckey,
                                                 int split, int p, ScoreIn &in) {
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int lg = l >> 4;
-  const int cg = split * kChunksPerSplit + 32 * w;
+  const int t = threadIdx.x;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int chunk = cg + tile_row(l & 15, t);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) in.kv[t][s] = make_uint4(0, 0, 0, 0);
-    if (chunk < d.C_max) {
-      const uint16_t *src = ckey + ((size_t)p * d.C_max + chunk) * kHeadDim + 8 * lg;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)   // read once per step: non-temporal
-        in.kv[t][s] = __builtin_bit_cast(
-            uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(src + 32 * s)));
-    }
+  for (int j = 0; j < 8; ++j) {
+    const int g = t + kScoreThreads * j, row = g >> 4, col = g & 15;
+    const int chunk = split * kChunksPerSplit + row;
+    in.kr[j] = make_uint4(0, 0, 0, 0);
+    if (chunk < d.C_max)
+      in.kr[j] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(
+                                               ckey + ((size_t)p * d.C_max + chunk) * kHeadDim + 8 * col)));
   }
+}
+
+// 16-byte slot of (row, column col) of the staged keys: the column is
+// XOR-swizzled by a function of the row that is distinct over the 16 rows an
+// MFMA operand read touches at once (rows 8 (i / 4) + 4 t + i % 4 of a
+// wave's 32), so neither the row-wise writes nor those reads conflict on
+// LDS banks.
+__device__ inline int key_slot(int row, int col) {
+  return row * 16 + (col ^ (((row >> 1) & 12) | (row & 3)));
+}
+
+// The loaded keys into the staging area (ks: the dynamic LDS region); row
+// skip_row (-1: none) is left to the caller.
+__device__ __forceinline__ void keys_to_lds(const ScoreIn &in, uint4 *ks, int skip_row) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int g = t + kScoreThreads * j, row = g >> 4;
+    if (row != skip_row) ks[key_slot(row, g & 15)] = in.kr[j];
+  }
+}
+
+// This lane's MFMA operands of its wave's 32 rows, from the staging area
+// (after a barrier): tile t, k-step s.
+__device__ __forceinline__ void keys_from_lds(const uint4 *ks, uint4 (&kv)[2][4]) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int h = l & 15, lg = l >> 4;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kv[t][s] = ks[key_slot(32 * w + tile_row(h, t), 4 * s + lg)];
 }
 
 // Issues the loads of split `split` of pair p. They do not depend on the
@@ -164,20 +199,19 @@ __device__ __forceinline__ void score_compute(const Dims &d, int C, ScoreIn &in,
     }
     return;
   }
-  if (fresh_ring && C - 1 < c0 + kChunksPerSplit) {               // uniform: this split holds it
-    __shared__ __align__(16) uint16_t fresh_sh[kHeadDim];
-    if (threadIdx.x < kHeadDim) fresh_sh[threadIdx.x] = fresh_key_dim(fresh_ring, fresh_k, pos, threadIdx.x);
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-      if (cg + tile_row(l & 15, t) == C - 1) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          in.kv[t][s] = *reinterpret_cast<const uint4 *>(&fresh_sh[8 * lg + 32 * s]);
-      }
+  extern __shared__ __align__(16) uint8_t score_tr[];
+  uint4 *ks = reinterpret_cast<uint4 *>(score_tr);
+  const bool fresh_here = fresh_ring && C - 1 < c0 + kChunksPerSplit;   // uniform
+  keys_to_lds(in, ks, fresh_here ? C - 1 - c0 : -1);
+  if (fresh_here && threadIdx.x < kHeadDim) {
+    const int r = C - 1 - c0, dim = threadIdx.x;
+    reinterpret_cast<uint16_t *>(&ks[key_slot(r, dim >> 3)])[dim & 7] =
+        fresh_key_dim(fresh_ring, fresh_k, pos, dim);
   }
+  __syncthreads();
+  uint4 kv[2][4];
+  keys_from_lds(ks, kv);
   const uint4 (&qv)[4] = in.qv;
-  const uint4 (&kv)[2][4] = in.kv;
   // logits on MFMA; a row past the length only feeds its own (masked) output
   f32x4 acc[2];
 #pragma unroll
@@ -217,8 +251,7 @@ __device__ __forceinline__ void score_compute(const Dims &d, int C, ScoreIn &in,
     // the wave's 32 chunks x Gp heads (chunk-major [c][Gp], pad = 0) are one
     // contiguous run of ws_e: transposed through this wave's part of the
     // dynamic LDS, then written as 16-byte device-coherent stores
-    extern __shared__ __align__(16) uint8_t score_tr[];
-    float *tr = reinterpret_cast<float *>(score_tr) + w * kScoreTrFloats;
+    float *tr = reinterpret_cast<float *>(score_tr) + w * kScoreTrFloats;   // keys no longer read
     if (h < Gp) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) tr[(8 * lg + m) * Gp + h] = h < d.G ? ev[m] : 0.0f;
