@@ -17,7 +17,8 @@
 //    score the append may finalise belongs to a window block, which is
 //    never a candidate;
 //  - every pool and every append of a sequence arrive on the sequence's
-//    counter once they have read its length; the last of them advances it.
+//    counter once they have read its length (a pool as it starts pooling,
+//    an append when done); the last of them advances it.
 #include "nosa_append_dev.h"
 #include "nosa_select_dev.h"
 
@@ -43,9 +44,21 @@ __global__ __launch_bounds__(kScoreThreads, 4) void append_select_kernel(
   const int pos = st.seq_len[b];
   const bool ok = pos >= 0 && pos < d.max_context;
   const int L = ok ? pos + 1 : pos;
+  // the last of the sequence's pools and appends to arrive on its counter
+  // (each after reading the length) advances the length and leaves the
+  // counter at zero
+  auto advance = [&](int old) {
+    if (old == 2 * d.Hkv - 1) {
+      __hip_atomic_store(&st.arrive[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (ok) __hip_atomic_store(&st.seq_len[b], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else atomicOr(st.status, NOSA_STATUS_CAPACITY);
+    }
+  };
   if (wg == n_wg) {                                       // uniform
     append_pair<kScoreThreads>(d, st, k_new, v_new, b, g, pos, true, ash);
     NOSA_PHASE(p, wg, 1);
+    if (threadIdx.x == 0)
+      advance(__hip_atomic_fetch_add(&st.arrive[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   } else {
     score_splits<MULTI>(d, st, q, L, ws_e, ws_stats, c_pad, n_splits, subs, wg, p,
                         ok ? k_new : nullptr);
@@ -59,20 +72,17 @@ __global__ __launch_bounds__(kScoreThreads, 4) void append_select_kernel(
     __syncthreads();
     NOSA_PHASE(p, wg, 3);
     if (!sm_last) return;
-    pool_select(d, st, L, ws_e, ws_stats, c_pad, n_splits, sel, n_sel, kind_out, dbg, p);
+    // the pool arrives on the sequence's counter before pooling (it and its
+    // scoring peers have read the length): the round trip runs under the
+    // pooling instead of after its last step (issued behind the pooling's
+    // first loads instead, it measured slower)
+    int old = 0;
     if (threadIdx.x == 0)
+      old = __hip_atomic_fetch_add(&st.arrive[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    pool_select(d, st, L, ws_e, ws_stats, c_pad, n_splits, sel, n_sel, kind_out, dbg, p);
+    if (threadIdx.x == 0) {
       __hip_atomic_store(&ws_count[p], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (threadIdx.x == 0) {
-    // every workgroup of this pair that reads the length has read it (the
-    // pool's scoring peers arrived before it); the last of the sequence's
-    // pools and appends advances it (and leaves the counter at zero)
-    const int old = __hip_atomic_fetch_add(&st.arrive[b], 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    if (old == 2 * d.Hkv - 1) {
-      __hip_atomic_store(&st.arrive[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (ok) __hip_atomic_store(&st.seq_len[b], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else atomicOr(st.status, NOSA_STATUS_CAPACITY);
+      advance(old);
     }
   }
   if (wg == n_wg) NOSA_PHASE(p, wg, 2);
