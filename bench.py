@@ -91,6 +91,10 @@ def parse():
                     help="skip the GQA-16, 96-block leg (beyond the five configs)")
     ap.add_argument("--no-tiny", action="store_true",
                     help="skip the tiny 4K single-layer leg")
+    ap.add_argument("--no-microbatch", action="store_true",
+                    help="skip the headline stack run as two micro-batches on two streams")
+    ap.add_argument("--only-microbatch", action="store_true",
+                    help="run only the two-micro-batch leg and print its JSON")
     ap.add_argument("--clock-warm", type=float, default=CLOCK_WARM_S, metavar="S",
                     help="seconds of untimed decode launches before each timed region")
     ap.add_argument("--phase-clocks", action="store_true",
@@ -110,22 +114,24 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def build_layer(wl, li, shape, pool):
+def build_layer(wl, li, shape, pool, b0=0):
+    """Layer li of workload wl holding sequences b0 .. b0 + shape.batch - 1."""
     import numpy as np
     from synth import context_kv, eviction_weights
     from trainable_offloadable_block_amd import NosaLayer
     layer = NosaLayer(shape)
     w = [eviction_weights(wl, li, g) for g in range(wl.n_kv_heads)]
     layer.set_weights(np.stack([x[0] for x in w]), np.stack([x[1] for x in w]))
-    P = wl.batch * wl.n_kv_heads
-    ctx = list(pool.map(lambda p: context_kv(wl, li, *divmod(p, wl.n_kv_heads)), range(P)))
+    P = shape.batch * wl.n_kv_heads
+    ctx = list(pool.map(lambda p: context_kv(wl, li, b0 + p // wl.n_kv_heads, p % wl.n_kv_heads),
+                        range(P)))
     for p, (K, V) in enumerate(ctx):
         layer.load_pair_context(p, K, V)
     import torch
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    layer.prefill([wl.context] * wl.batch)
+    layer.prefill([wl.context] * shape.batch)
     e1.record()
     torch.cuda.synchronize()
     PREFILL_MS.append((wl.name, e0.elapsed_time(e1)))
@@ -135,17 +141,18 @@ def build_layer(wl, li, shape, pool):
 PREFILL_MS = []          # (workload, ms) of every nosa_prefill_init call
 
 
-def step_inputs(wl, li, n, pool, device):
-    """Per-step q, k_new, v_new for one layer, resident on the device:
-    [n][B][Hq][128], [n][B][Hkv][128] x2 (bf16 bits as int16)."""
+def step_inputs(wl, li, n, pool, device, b0=0, nb=None):
+    """Per-step q, k_new, v_new for one layer (sequences b0 .. b0 + nb - 1,
+    all of them by default), resident on the device: [n][B][Hq][128],
+    [n][B][Hkv][128] x2 (bf16 bits as int16)."""
     import numpy as np
     import torch
     from synth import new_tokens, queries
-    B, Hq, Hkv = wl.batch, wl.n_q_heads, wl.n_kv_heads
+    B, Hq, Hkv = (wl.batch if nb is None else nb), wl.n_q_heads, wl.n_kv_heads
     wl = wl.replace(steps=max(wl.steps, n))     # the same streams, drawn further
-    qs = list(pool.map(lambda bh: queries(wl, li, *divmod(bh, Hq))[:n], range(B * Hq)))
+    qs = list(pool.map(lambda bh: queries(wl, li, b0 + bh // Hq, bh % Hq)[:n], range(B * Hq)))
     q = np.stack(qs).reshape(B, Hq, n, 128).transpose(2, 0, 1, 3)
-    toks = list(pool.map(lambda bg: new_tokens(wl, li, *divmod(bg, Hkv)), range(B * Hkv)))
+    toks = list(pool.map(lambda bg: new_tokens(wl, li, b0 + bg // Hkv, bg % Hkv), range(B * Hkv)))
     k = np.stack([t[0][:n] for t in toks]).reshape(B, Hkv, n, 128).transpose(2, 0, 1, 3)
     v = np.stack([t[1][:n] for t in toks]).reshape(B, Hkv, n, 128).transpose(2, 0, 1, 3)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)  # noqa: E731
@@ -1203,6 +1210,61 @@ def next_leg(dev, workers, R=4, W=8, K=48):
             "breakdown_us": m["breakdown"], "locality": m["locality"]}
 
 
+def microbatch_leg(dev, workers, R=8, W=12, K=120, n_mb=2):
+    """The headline stack (the 16K workload's 32 sequences, R layers) run as
+    n_mb micro-batches of 32 / n_mb sequences, each on its own HIP stream
+    (default priority) and its own layers, a step issuing every
+    micro-batch's whole R-layer step in turn: the sequences are independent,
+    so one micro-batch's latency-bound selection runs beside another's
+    HBM-bound decode. Every sequence still goes through every layer in order
+    (append + select, then decode), as in the headline's single stream.
+    value = decode tokens/s per layer over K timed steps."""
+    import torch
+    from synth import WORKLOADS
+    from trainable_offloadable_block_amd import LayerShape
+    wl = WORKLOADS[2]
+    nb = wl.batch // n_mb
+    n_tok = W + K
+    shape = LayerShape(nb, wl.n_q_heads, wl.n_kv_heads, wl.n_sink_blocks, wl.window_tokens,
+                       wl.k_blocks, wl.k_q_blocks, wl.k_e_blocks, wl.context + n_tok,
+                       offload=wl.offload)
+    mbs = []
+    with cf.ThreadPoolExecutor(workers) as pool:
+        for m in range(n_mb):
+            layers = [build_layer(wl, li, shape, pool, b0=m * nb) for li in range(R)]
+            inputs = [step_inputs(wl, li, n_tok, pool, dev, b0=m * nb, nb=nb) for li in range(R)]
+            mbs.append((layers, inputs))
+    streams = [torch.cuda.Stream(dev) for _ in range(n_mb)]
+    torch.cuda.synchronize()
+
+    def step(t):
+        for (layers, inputs), s in zip(mbs, streams):
+            with torch.cuda.stream(s):
+                for li, layer in enumerate(layers):
+                    q, kn, vn = inputs[li][0][t], inputs[li][1][t], inputs[li][2][t]
+                    layer.append_select(kn, vn, q, want_kind=False)
+                    layer.fetch()
+                    layer.decode(q)
+
+    for t in range(W):
+        step(t)
+    torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < CLOCK_WARM_S:
+        for layers, inputs in mbs:
+            for li, layer in enumerate(layers):
+                layer.decode(inputs[li][0][W - 1])
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(W, W + K):
+        step(t)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    return {"workload": wl.name, "micro_batches": n_mb, "sequences_each": nb, "streams": n_mb,
+            "layers_per_step": R, "steps": K, "unit": "tokens/s/layer",
+            "value": round(wl.batch * R * K / el, 1), "ms_per_step": round(el * 1e3 / K, 4)}
+
+
 def tiny_leg(dev, workers, W=4, K=32):
     """The tiny single-layer 4K workload (batch 1, 16/2 heads, k = 16 blocks:
     4 query-aware + 12 agnostic, window 256): its 32 decode steps, a
@@ -1465,6 +1527,9 @@ def main():
     if args.only_next:
         print(json.dumps(next_leg(dev, workers)), flush=True)
         return
+    if args.only_microbatch:
+        print(json.dumps(microbatch_leg(dev, workers)), flush=True)
+        return
     wl = WORKLOADS[2]
     R, W, K = args.layers, args.warmup, args.steps
     m = time_stack(wl, R, W, K, args.breakdown_steps, dev, workers,
@@ -1544,6 +1609,9 @@ def main():
         res["state_build"] = {"call": "nosa_prefill_init", "ms_per_layer": round(ms, 3),
                               "context_tokens_per_s": round(wl.batch * wl.context / (ms * 1e-3), 1),
                               "kv_GBps": round(byt / (ms * 1e-3) / 1e9, 1)}
+    if not args.no_microbatch:
+        log("two micro-batches on two streams")
+        res["microbatch_2x16"] = microbatch_leg(dev, workers)
     log("warm single-layer leg")
     res["warm_1layer"] = warm_leg(dev, workers)
     if not args.no_tiny:
