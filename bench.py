@@ -94,7 +94,14 @@ def parse():
     ap.add_argument("--no-microbatch", action="store_true",
                     help="skip the headline stack run as two micro-batches on two streams")
     ap.add_argument("--only-microbatch", action="store_true",
-                    help="run only the two-micro-batch leg and print its JSON")
+                    help="run only the micro-batch leg and print its JSON")
+    ap.add_argument("--mb-workload", type=int, default=2, choices=(2, 3),
+                    help="with --only-microbatch: 2 the 16K stack, 3 the offloaded 32K stack")
+    ap.add_argument("--mb-count", type=int, default=2, choices=(1, 2, 4),
+                    help="with --only-microbatch: micro-batches (1: the plain one-stream run)")
+    ap.add_argument("--mb-fetch-wg", type=int, default=0,
+                    help="with --only-microbatch and an offloaded workload: looping fetch "
+                         "workgroups (0: one workgroup per block)")
     ap.add_argument("--clock-warm", type=float, default=CLOCK_WARM_S, metavar="S",
                     help="seconds of untimed decode launches before each timed region")
     ap.add_argument("--phase-clocks", action="store_true",
@@ -1210,19 +1217,23 @@ def next_leg(dev, workers, R=4, W=8, K=48):
             "breakdown_us": m["breakdown"], "locality": m["locality"]}
 
 
-def microbatch_leg(dev, workers, R=8, W=12, K=120, n_mb=2):
-    """The headline stack (the 16K workload's 32 sequences, R layers) run as
-    n_mb micro-batches of 32 / n_mb sequences, each on its own HIP stream
+def microbatch_leg(dev, workers, R=8, W=12, K=120, n_mb=2, wl_id=2, fetch_wg=None):
+    """A stack of R layers of workload wl_id (by default the headline: the
+    16K workload's 32 sequences, 8 layers) run as n_mb micro-batches of
+    batch / n_mb sequences, each on its own HIP stream
     (default priority) and its own layers, a step issuing every
     micro-batch's whole R-layer step in turn: the sequences are independent,
     so one micro-batch's latency-bound selection runs beside another's
     HBM-bound decode. Every sequence still goes through every layer in order
-    (append + select, then decode), as in the headline's single stream.
+    (append + select, then decode), as in the headline's single stream. An
+    offloaded workload fetches each layer's missing blocks between the two
+    (with fetch_wg, by that many looping workgroups, which leave the CUs to
+    the other stream's kernels, instead of one workgroup per block).
     value = decode tokens/s per layer over K timed steps."""
     import torch
     from synth import WORKLOADS
     from trainable_offloadable_block_amd import LayerShape
-    wl = WORKLOADS[2]
+    wl = WORKLOADS[wl_id]
     nb = wl.batch // n_mb
     n_tok = W + K
     shape = LayerShape(nb, wl.n_q_heads, wl.n_kv_heads, wl.n_sink_blocks, wl.window_tokens,
@@ -1243,7 +1254,10 @@ def microbatch_leg(dev, workers, R=8, W=12, K=120, n_mb=2):
                 for li, layer in enumerate(layers):
                     q, kn, vn = inputs[li][0][t], inputs[li][1][t], inputs[li][2][t]
                     layer.append_select(kn, vn, q, want_kind=False)
-                    layer.fetch()
+                    if fetch_wg:
+                        layer.fetch_wg(fetch_wg)
+                    else:
+                        layer.fetch()
                     layer.decode(q)
 
     for t in range(W):
@@ -1261,7 +1275,7 @@ def microbatch_leg(dev, workers, R=8, W=12, K=120, n_mb=2):
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     return {"workload": wl.name, "micro_batches": n_mb, "sequences_each": nb, "streams": n_mb,
-            "layers_per_step": R, "steps": K, "unit": "tokens/s/layer",
+            "fetch_workgroups": fetch_wg, "layers_per_step": R, "steps": K, "unit": "tokens/s/layer",
             "value": round(wl.batch * R * K / el, 1), "ms_per_step": round(el * 1e3 / K, 4)}
 
 
@@ -1528,7 +1542,12 @@ def main():
         print(json.dumps(next_leg(dev, workers)), flush=True)
         return
     if args.only_microbatch:
-        print(json.dumps(microbatch_leg(dev, workers)), flush=True)
+        if args.mb_workload == 3:        # the offloaded 32K stack: 4 of its layers
+            leg = microbatch_leg(dev, workers, R=4, W=4, K=24, n_mb=args.mb_count, wl_id=3,
+                                 fetch_wg=args.mb_fetch_wg or None)
+        else:
+            leg = microbatch_leg(dev, workers, n_mb=args.mb_count)
+        print(json.dumps(leg), flush=True)
         return
     wl = WORKLOADS[2]
     R, W, K = args.layers, args.warmup, args.steps
