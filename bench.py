@@ -34,7 +34,9 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA, MI355X
 
 
-CLOCK_WARM_S = 0.5      # untimed decode launches before each timed region
+CLOCK_WARM_S = 0.5      # untimed decode launches before each timed region (at least)
+CLOCK_WARM_MAX_S = 12.0  # ... and at most, while their launch time has not settled
+WARMUPS = []             # what each warm-up took (reported in the JSON line)
 
 
 def parse():
@@ -103,7 +105,8 @@ def parse():
                     help="with --only-microbatch and an offloaded workload: looping fetch "
                          "workgroups (0: one workgroup per block)")
     ap.add_argument("--clock-warm", type=float, default=CLOCK_WARM_S, metavar="S",
-                    help="seconds of untimed decode launches before each timed region")
+                    help="least seconds of untimed decode launches before each timed region "
+                         "(more while their launch time has not settled)")
     ap.add_argument("--phase-clocks", action="store_true",
                     help="phase breakdown of the append + select and decode launches from the "
                          "timing build's in-kernel clocks (NOSA_LIBRARY=.../libnosa_clocks.so)")
@@ -146,6 +149,37 @@ def build_layer(wl, li, shape, pool, b0=0):
 
 
 PREFILL_MS = []          # (workload, ms) of every nosa_prefill_init call
+
+
+def warm_until_steady(launch_round, label):
+    """Untimed rounds of decode launches (launch_round() enqueues one) before
+    a timed region: at least CLOCK_WARM_S seconds, then until the last three
+    rounds each ran within 2 % of the fastest round so far, at most
+    CLOCK_WARM_MAX_S. The GPU idles while the layers are built on the host;
+    on a freshly leased box the first seconds of launches have also run
+    10-15 % slower than a minute later in the same process (decode 30.7
+    against 26.9 us), so a fixed warm-up left some timed regions in that
+    state. Returns the record appended to WARMUPS."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rounds = []
+    t0 = time.perf_counter()
+    while True:
+        e0.record()
+        launch_round()
+        e1.record()
+        torch.cuda.synchronize()
+        rounds.append(e0.elapsed_time(e1))
+        el = time.perf_counter() - t0
+        best = min(rounds)
+        settled = len(rounds) >= 3 and max(rounds[-3:]) <= 1.02 * best
+        if el >= CLOCK_WARM_MAX_S or (el >= CLOCK_WARM_S and settled):
+            break
+    rec = {"leg": label, "s": round(el, 2), "rounds": len(rounds),
+           "first_round_ms": round(rounds[0], 3), "last_round_ms": round(rounds[-1], 3),
+           "settled": bool(settled)}
+    WARMUPS.append(rec)
+    return rec
 
 
 def step_inputs(wl, li, n, pool, device, b0=0, nb=None):
@@ -733,15 +767,15 @@ def time_stack(wl, R, W, K, n_bd, dev, workers, graph_steps=0, link_peak=None):
 
     for t in range(W):
         run_step(t)
-    # the GPU idles while the layers are built on the host and its clocks
-    # drop; repeated decode launches (they read the state and rewrite only
-    # the output and workspace) bring it back to speed before the timed steps
-    t_warm = time.perf_counter()
-    while time.perf_counter() - t_warm < CLOCK_WARM_S:
+    # repeated decode launches (they read the state and rewrite only the
+    # output and workspace) bring the GPU to a steady speed before the timed
+    # steps
+
+    def warm_round():
         for _ in range(16):
             for li, layer in enumerate(layers):
                 layer.decode(inputs[li][0][W - 1] if W > 0 else inputs[li][0][0])
-        torch.cuda.synchronize()
+    warm_until_steady(warm_round, wl.name)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for t in range(W, W + K):
@@ -1263,12 +1297,13 @@ def microbatch_leg(dev, workers, R=8, W=12, K=120, n_mb=2, wl_id=2, fetch_wg=Non
     for t in range(W):
         step(t)
     torch.cuda.synchronize()
-    t_warm = time.perf_counter()
-    while time.perf_counter() - t_warm < CLOCK_WARM_S:
-        for layers, inputs in mbs:
-            for li, layer in enumerate(layers):
-                layer.decode(inputs[li][0][W - 1])
-        torch.cuda.synchronize()
+
+    def warm_round():
+        for _ in range(4):
+            for layers, inputs in mbs:
+                for li, layer in enumerate(layers):
+                    layer.decode(inputs[li][0][W - 1])
+    warm_until_steady(warm_round, f"microbatch-{wl.name}")
     t0 = time.perf_counter()
     for t in range(W, W + K):
         step(t)
@@ -1370,12 +1405,11 @@ def phase_clocks(dev, workers, R=8, W=12, samples=24, wl_id=2):
             ly.append_select(kn, vn, q, want_kind=False)
             ly.fetch()
             ly.decode(q)
-    t_warm = time.perf_counter()
-    while time.perf_counter() - t_warm < CLOCK_WARM_S:
+    def warm_round():
         for _ in range(16):
             for li, ly in enumerate(layers):
                 ly.decode(inputs[li][0][W - 1])
-        torch.cuda.synchronize()
+    warm_until_steady(warm_round, f"phase-clocks-{wl.name}")
     sel_runs, dec_runs = [], []
     for sidx in range(samples):
         t = W + sidx
@@ -1663,6 +1697,7 @@ def main():
         res["parity"], res["cpu_baseline"] = cpu_baseline(2, args.cpu_pairs, args.cpu_steps, gpu)
     else:
         res["cpu_baseline"] = None
+    res["clock_warm"] = WARMUPS
     print(json.dumps(res), flush=True)
 
 

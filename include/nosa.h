@@ -100,7 +100,11 @@ typedef struct nosa_config {
 /* ------------------------------------------------------------ state
  * One layer's decode state. Sizes (in elements) come from nosa_state_bytes;
  * write C_max = (max_context - 32) / 16 + 1 chunks, NB_max =
- * ceil(max_context / 64) blocks, P = batch * n_kv_heads pairs.
+ * ceil(max_context / 64) blocks, P = batch * n_kv_heads pairs, and NB_kv
+ * = NB_max, or NB_max + 1 when NB_max is a multiple of 129, for the
+ * per-pair stride of the KV pool, the host store and the token scores (a
+ * stride of 258 blocks put the decode's reads of many pairs on a part of
+ * the HBM channels: 13 % slower on MI355X; the extra block is never used).
  *
  * KV block layout (device pool, device cache and host store alike): one
  * block of one pair is 32 KiB = K then V, bf16:
@@ -120,15 +124,15 @@ typedef struct nosa_state {
   int32_t *arrive;        /* dev [B]: zero; append's per-sequence counter   */
   uint32_t *status;       /* dev [1]: NOSA_STATUS_* bits (sticky)           */
   uint16_t *ckey;         /* dev [P][C_max][128] bf16 compressed keys       */
-  float *tok_s;           /* dev [P][NB_max*64] eviction score per token    */
+  float *tok_s;           /* dev [P][NB_kv*64] eviction score per token     */
   float *chunk_e;         /* dev [P][C_max] mean eviction score per chunk   */
   float *blk_e;           /* dev [P][NB_max] query-agnostic block score     */
   uint32_t *eligible;     /* dev [P][ceil(NB_max/32)] never-reselect bits   */
   uint16_t *tail_keys;    /* dev [P][32][128] last 32 keys (ring by pos%32) */
-  uint16_t *kv_dev;       /* dev: resident pool [P][NB_max][32 KiB block] or
+  uint16_t *kv_dev;       /* dev: resident pool [P][NB_kv][32 KiB block] or
                              offload cache [P][k_blocks+1][32 KiB block]    */
   uint16_t *kv_host;      /* device-usable alias of the pinned host store
-                             [P][NB_max][32 KiB block]; NULL when resident  */
+                             [P][NB_kv][32 KiB block]; NULL when resident   */
   int32_t *slot_of_block; /* dev [P][NB_max] cache slot or -1 (offload)     */
   int32_t *block_of_slot; /* dev [P][k_blocks+1] block id or -1 (offload)   */
   const uint16_t *w1;     /* dev [Hkv][128 in][128 hidden] bf16 eviction W1 */

@@ -370,7 +370,7 @@ class Lockstep:
         nsel = g.n_sel.cpu().numpy()
         seq = g.seq_len.cpu().numpy()
         cache = g.kv_dev.view(self.P, k + 1, 2, 64, 128)
-        host = g.kv_host.view(self.P, self.shape.nb_max, 2, 64, 128)
+        host = g.kv_host.view(self.P, g.nb_kv, 2, 64, 128)
         for p in self.check:
             Lb = int(seq[p // self.wl.n_kv_heads])
             o = self.oracles.get(p)

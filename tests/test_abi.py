@@ -95,6 +95,22 @@ def test_state_bytes_layout():
     assert s["kv_dev"] == P * 65 * 32768          # k + 1 cache slots
     assert s["kv_host"] == P * NB * 32768
     assert s["block_of_slot"] == P * 65 * 4
+    # a block count that is a multiple of 129 gets one more block of stride
+    # in the pool, the host store and the token scores (not elsewhere)
+    for nb, nb_kv in ((258, 259), (257, 257), (387, 388), (516, 517)):
+        c = _cfg(max_context=64 * nb)
+        for flags in (0, L.NOSA_OFFLOAD):
+            c.flags = flags
+            assert lib.nosa_state_bytes(ctypes.byref(c), sizes) == 0
+            s = dict(zip(L.BUFFERS, sizes))
+            assert s["tok_s"] == P * nb_kv * 64 * 4
+            assert s["blk_e"] == P * nb * 4
+            assert s["eligible"] == P * ((nb + 31) // 32) * 4
+            if flags:
+                assert s["kv_host"] == P * nb_kv * 32768
+                assert s["slot_of_block"] == P * nb * 4
+            else:
+                assert s["kv_dev"] == P * nb_kv * 32768
 
 
 def test_workspace_sizes():

@@ -144,7 +144,7 @@ def test_chunk_mean_exact_for_any_span():
     Kall = np.concatenate([ctx, new.transpose(1, 2, 0, 3).reshape(P, steps, 128)], axis=1)
 
     def plant(ls):
-        pool = ls.gpu.kv_dev.view(ls.P, ls.shape.nb_max, 2, 64, 128)
+        pool = ls.gpu.kv_dev.view(ls.P, ls.gpu.nb_kv, 2, 64, 128)
         for p in range(P):
             kb = np.zeros((7, 64, 128), dtype=np.uint16)
             kb.reshape(-1, 128)[:400] = ctx[p]
@@ -204,7 +204,7 @@ def test_nan_bytes_past_length_are_ignored():
     nan = int(np.array([0x7FC0], dtype=np.uint16).view(np.int16)[0])
 
     def plant(ls):
-        pool = ls.gpu.kv_dev.view(ls.P, ls.shape.nb_max, 2, 64, 128)
+        pool = ls.gpu.kv_dev.view(ls.P, ls.gpu.nb_kv, 2, 64, 128)
         for p in range(ls.P):
             Lb = int(ls.lengths[p // wl.n_kv_heads])
             blk, r = divmod(Lb, 64)

@@ -59,7 +59,8 @@ int make_dims(const nosa_config *c, nosa::Dims *d) {
   d->P = c->batch * c->n_kv_heads;
   d->max_context = c->max_context;
   d->NB_max = nosa::blocks_for(c->max_context);
-  d->tok_stride = d->NB_max * nosa::kBlock;
+  d->NB_kv = nosa::kv_blocks_per_pair(d->NB_max);
+  d->tok_stride = d->NB_kv * nosa::kBlock;
   d->C_max = nosa::chunks_for(c->max_context);
   d->elig_words = (d->NB_max + 31) / 32;
   d->n_sink = c->n_sink_blocks;
@@ -165,8 +166,8 @@ int nosa_state_bytes(const nosa_config *cfg, size_t out[NOSA_NUM_BUFFERS]) {
   out[NOSA_BUF_BLK_E] = P * d.NB_max * 4;
   out[NOSA_BUF_ELIGIBLE] = P * d.elig_words * 4;
   out[NOSA_BUF_TAIL_KEYS] = P * nosa::kPoolKernel * nosa::kHeadDim * 2;
-  out[NOSA_BUF_KV_DEV] = P * (d.offload ? (size_t)d.k + 1 : (size_t)d.NB_max) * blk;
-  out[NOSA_BUF_KV_HOST] = d.offload ? P * d.NB_max * blk : 0;
+  out[NOSA_BUF_KV_DEV] = P * (d.offload ? (size_t)d.k + 1 : (size_t)d.NB_kv) * blk;
+  out[NOSA_BUF_KV_HOST] = d.offload ? P * d.NB_kv * blk : 0;
   out[NOSA_BUF_SLOT_OF_BLOCK] = d.offload ? P * d.NB_max * 4 : 0;
   out[NOSA_BUF_BLOCK_OF_SLOT] = d.offload ? P * (d.k + 1) * 4 : 0;
   out[NOSA_BUF_W1] = (size_t)d.Hkv * nosa::kHeadDim * nosa::kHeadDim * 2;

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(Dims d, nosa_state 
     __syncthreads();                         // W1 staged / previous block's vs consumed
     {   // V part, tile order -> vs[token][dim]
       const uint4 *src = reinterpret_cast<const uint4 *>(
-          kvb + ((size_t)p * d.NB_max + blk) * kBlockElems + kBlock * kHeadDim);
+          kvb + ((size_t)p * d.NB_kv + blk) * kBlockElems + kBlock * kHeadDim);
 #pragma unroll
       for (int j = 0; j < kBlock * kHeadDim / 8 / 256; ++j) {
         const int gi = t + 256 * j;           // 8 tokens of one dim
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(128) void prefill_chunks_kernel(Dims d, nosa_state 
     if (i >= C) return;
     st.ckey[((size_t)p * d.C_max + i) * kHeadDim + t] = mean32_bf16([&](int j) -> uint16_t {
       const int tok = i * kPoolStride + j;
-      return kvb[((size_t)p * d.NB_max + tok / kBlock) * kBlockElems +
+      return kvb[((size_t)p * d.NB_kv + tok / kBlock) * kBlockElems +
                  (tok % kBlock) * kHeadDim + t];
     });
     if (t < 64) {
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(128) void prefill_finish_kernel(Dims d, nosa_state 
   if (L % kBlock) {
     // tail of the last, partial block: K and V of the positions past L read 0
     uint16_t *base = (d.offload ? st.kv_host : st.kv_dev) +
-                     ((size_t)p * d.NB_max + L / kBlock) * kBlockElems;
+                     ((size_t)p * d.NB_kv + L / kBlock) * kBlockElems;
     const int r0 = L % kBlock, n = (kBlock - r0) * kHeadDim;
     for (int i = idx; i < n; i += gridDim.x * blockDim.x) {
       const int tok = r0 + i / kHeadDim, dim = i % kHeadDim;
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(128) void prefill_finish_kernel(Dims d, nosa_state 
     for (int j = 0; j < kPoolKernel; ++j) {
       const int tok = L - kPoolKernel + j;
       if (tok < 0) continue;
-      const uint16_t *row = kvb + ((size_t)p * d.NB_max + tok / kBlock) * kBlockElems +
+      const uint16_t *row = kvb + ((size_t)p * d.NB_kv + tok / kBlock) * kBlockElems +
                             (tok % kBlock) * kHeadDim;
       ring[(tok % kPoolKernel) * kHeadDim + t] = row[t];
     }

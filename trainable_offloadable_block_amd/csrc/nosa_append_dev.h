@@ -116,7 +116,7 @@ __device__ __forceinline__ int append_pair(const Dims &d, const nosa_state &st, 
 
   // 1. store K, V (K row-major, V in the block's tile order)
   if (!d.offload) {
-    uint16_t *base = st.kv_dev + ((size_t)p * d.NB_max + blk) * kBlockElems;
+    uint16_t *base = st.kv_dev + ((size_t)p * d.NB_kv + blk) * kBlockElems;
     if (r == 0) clear_block(base);
     if (dim) {
       base[r * kHeadDim + t] = kb;
@@ -128,7 +128,7 @@ __device__ __forceinline__ int append_pair(const Dims &d, const nosa_state &st, 
     // arrives (a block stays cached until then: the window holds it). A token
     // whose block is not cached (before the first fetch) goes to the host
     // store directly.
-    uint16_t *hb = st.kv_host + ((size_t)p * d.NB_max + blk) * kBlockElems;
+    uint16_t *hb = st.kv_host + ((size_t)p * d.NB_kv + blk) * kBlockElems;
     int32_t *sob = st.slot_of_block + (size_t)p * d.NB_max;
     int32_t *bos = st.block_of_slot + (size_t)p * (d.k + 1);
     if (t == 0) sh.slot_sh = sob[blk];

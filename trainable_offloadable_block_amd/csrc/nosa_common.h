@@ -228,10 +228,24 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
+// Blocks per pair in the KV pool, the host store and the token-score rows:
+// NB_max, or NB_max + 1 when NB_max is a multiple of 129. Every pair's
+// region starts at p times this stride, and the decode's workgroups read
+// the same block offsets of many pairs at once. At strides of 258 and 516
+// blocks (2^23 + 2^16 and 2^24 + 2^17 bytes) those reads crowded part of
+// the HBM channels: the 16K decode launch (4 layers, 64 pairs) ran 29.7 and
+// 29.2 us, against 26.1-26.6 us at 257, 259-288, 320, 321, 384, 385, 513 and
+// 514 blocks, and 26.4 and 27.2 us with the extra block (387 and 645 blocks
+// ran 27.1 and 27.0 us, 388 blocks 26.4 us).
+__host__ __device__ inline int kv_blocks_per_pair(int nb_max) {
+  return nb_max % 129 == 0 ? nb_max + 1 : nb_max;
+}
+
 // Device-side launch parameters shared by the kernels.
 struct Dims {
   int B, Hq, Hkv, G, P;           // P = B * Hkv pairs
   int max_context, tok_stride, C_max, NB_max, elig_words;
+  int NB_kv;       // blocks per pair in the KV pool and host store (kv_blocks_per_pair)
   int n_sink, n_win, k, k_q, k_e_dyn;
   int offload, bias;
   int pool_small;  // 1: a pair with at most 256 candidates finishes with one per thread

@@ -606,7 +606,7 @@ hipError_t launch_decode(const Dims &d, const nosa_state &st, const uint16_t *q,
   float *ws_o = reinterpret_cast<float *>(base + lay.o_off);
   float2 *ws_ml = reinterpret_cast<float2 *>(base + lay.ml_off);
   int32_t *ws_count = reinterpret_cast<int32_t *>(base + lay.count_off);
-  const int slots = d.offload ? d.k + 1 : d.NB_max;
+  const int slots = d.offload ? d.k + 1 : d.NB_kv;
   if (ev_start || ev_stop) {
     hipExtLaunchKernelGGL(decode_kernel, dim3(lay.n_splits, d.P), dim3(kDecThreads), 0, s,
                           ev_start, ev_stop, 0, d, st.seq_len, q, sel, phys, n_sel, st.kv_dev,

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
   if (r >= n_miss[p]) return;
   const int2 e = list[(size_t)p * d.k + r];
   const uint4 *src = reinterpret_cast<const uint4 *>(
-      host + ((size_t)p * d.NB_max + e.x) * kBlockElems);
+      host + ((size_t)p * d.NB_kv + e.x) * kBlockElems);
   uint4 *dst = reinterpret_cast<uint4 *>(cache + ((size_t)p * (d.k + 1) + e.y) * kBlockElems);
   constexpr int kVec = kBlockElems * 2 / 16;   // 2048 uint4 per block
   uint4 v[kVec / 256];
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void gather_wg_kernel(
     if (r >= n_miss[p]) continue;
     const int2 e = list[(size_t)p * d.k + r];
     const uint4 *src = reinterpret_cast<const uint4 *>(
-        host + ((size_t)p * d.NB_max + e.x) * kBlockElems);
+        host + ((size_t)p * d.NB_kv + e.x) * kBlockElems);
     uint4 *dst = reinterpret_cast<uint4 *>(cache + ((size_t)p * (d.k + 1) + e.y) * kBlockElems);
 #pragma unroll
     for (int j0 = 0; j0 < kVec / 256; j0 += VPT) {

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kPaWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   }
   const float qscale = 0.08838834764831845f * 1.4426950408889634f;
   const float bscale = d.bias ? 1.4426950408889634f : 0.0f;
-  const uint4 *kvg = reinterpret_cast<const uint4 *>(st.kv_dev + (size_t)p * d.NB_max * kBlockElems);
+  const uint4 *kvg = reinterpret_cast<const uint4 *>(st.kv_dev + (size_t)p * d.NB_kv * kBlockElems);
   const float *tsp = st.tok_s + (size_t)p * d.tok_stride;
   const int koff0 = pa_tile_row(h, 0) * kPaKPitch + 16 * lg;
   const int koff1 = pa_tile_row(h, 1) * kPaKPitch + 16 * lg;

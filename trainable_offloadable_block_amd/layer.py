@@ -126,6 +126,10 @@ class NosaLayer:
         sizes = (ctypes.c_size_t * len(L.BUFFERS))()
         L.check(lib.nosa_state_bytes(ctypes.byref(self.cfg), sizes), "state_bytes")
         self.sizes = dict(zip(L.BUFFERS, list(sizes)))
+        # blocks per pair in the KV pool / host store (NB_max, or one more
+        # where that stride would crowd the HBM channels): tok_s holds one
+        # row of nb_kv * 64 scores per pair
+        self.nb_kv = self.sizes["tok_s"] // (shape.pairs * BLOCK * 4)
         dev = self.device
         P, nbm = shape.pairs, shape.nb_max
 
@@ -203,11 +207,10 @@ class NosaLayer:
     def load_pair_context(self, p: int, K: np.ndarray, V: np.ndarray):
         """Writes pair p's prefilled K, V (token-major uint16 bf16 bits) into
         the pool (resident) or the pinned host store (offload)."""
-        nbm = self.shape.nb_max
         blocks = to_block_layout(K, V, -(-K.shape[0] // BLOCK)).view(np.int16)
         nb = blocks.shape[0]
         flat = blocks.reshape(-1)
-        base = p * nbm * BLOCK_ELEMS
+        base = p * self.nb_kv * BLOCK_ELEMS
         if self.shape.offload:
             self.kv_host.numpy()[base:base + flat.size] = flat
         else:
