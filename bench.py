@@ -155,11 +155,11 @@ def warm_until_steady(launch_round, label):
     """Untimed rounds of decode launches (launch_round() enqueues one) before
     a timed region: at least CLOCK_WARM_S seconds, then until the last three
     rounds each ran within 2 % of the fastest round so far, at most
-    CLOCK_WARM_MAX_S. The GPU idles while the layers are built on the host;
-    on a freshly leased box the first seconds of launches have also run
-    10-15 % slower than a minute later in the same process (decode 30.7
-    against 26.9 us), so a fixed warm-up left some timed regions in that
-    state. Returns the record appended to WARMUPS."""
+    CLOCK_WARM_MAX_S. The GPU idles while the layers are built on the host,
+    and its first launches after that run slower; a fixed warm-up cannot
+    tell whether they have come back to speed, this one measures it (most
+    legs settle within the minimum; the tiny 4K leg, whose rounds last
+    0.12 ms, takes about 3 s). Returns the record appended to WARMUPS."""
     import torch
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     rounds = []
