@@ -35,7 +35,7 @@ BF16_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA, MI355X
 
 
 CLOCK_WARM_S = 0.5      # untimed decode launches before each timed region (at least)
-CLOCK_WARM_MAX_S = 12.0  # ... and at most, while their launch time has not settled
+CLOCK_WARM_MAX_S = 5.0   # ... and at most, while their launch time has not settled
 WARMUPS = []             # what each warm-up took (reported in the JSON line)
 
 
