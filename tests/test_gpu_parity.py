@@ -220,6 +220,30 @@ def test_nan_bytes_past_length_are_ignored():
     ls.run()
 
 
+@pytest.mark.parametrize("offload", [False, True])
+def test_kv_stride_with_extra_block(offload):
+    """A length bound of 129 blocks (a multiple of 129): the pool, the host
+    store and the token scores get one block more of stride per pair. Steps
+    still match the oracle, and NaN planted in every pair's extra block and
+    extra token scores is never read."""
+    wl = small_workload(115, context=8190, steps=12, offload=offload)
+    nan16 = int(np.array([0x7FC0], dtype=np.uint16).view(np.int16)[0])
+
+    def plant(ls):
+        g = ls.gpu
+        assert ls.shape.nb_max == 129 and g.nb_kv == 130
+        store = g.kv_host if offload else g.kv_dev
+        store.view(ls.P, g.nb_kv, 2, 64, 128)[:, 129] = nan16
+        g.tok_s.view(ls.P, g.nb_kv * 64)[:, 129 * 64:] = float("nan")
+        torch.cuda.synchronize()
+
+    ls = Lockstep(wl, before_prefill=plant)
+    ls.check_prefill()
+    ls.run(cache_every=4 if offload else 0)
+    if offload:
+        ls.check_cache()
+
+
 def test_resident_fetch_is_identity():
     """With resident KV, nosa_fetch_delta only sets phys = sel, n_miss = 0."""
     wl = small_workload(114)
